@@ -1,0 +1,528 @@
+/*
+ * moe_oracle.c -- plain, slow, obviously-correct CPU oracle for one
+ * DeepSeekMoE feed-forward layer forward pass and its per-step bias update.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This library is the reference the GPU library is
+ * checked against.  Only the test-suite, the smoke check and the CPU-baseline
+ * leg of the benchmark may load it.  It shares no code, header, table or
+ * constant generator with the HIP library, and it never touches a GPU.
+ *
+ * Sources (the pages are web copies of material about the DeepSeek-V3
+ * technical report, arXiv:2412.19437):
+ *  [P4]  "DeepSeek-V3 Technischer Bericht" reading guide (xyznot.com/de),
+ *        section "Methode", item 2 "DeepSeekMoE mit Auxiliary-Loss-Free
+ *        Balancing": the layer output h'_t, the sigmoid affinity s_{i,t},
+ *        the biased Topk definition of g'_{i,t}, the normalisation of g',
+ *        and the end-of-step bias rule with gamma = 0.001.
+ *  [P4k] same page, "Kernideen", FP8 bullet: E4M3 for all tensors, 1x128
+ *        activation tiles, 128x128 weight blocks, FP32 promotion every
+ *        N_c = 128 accumulation steps.
+ *  [P1]  "DeepSeek-V3 技術報告書：MLAと極小スパースMoE..." (singularity-lens.com),
+ *        its formula paragraph: bias rule b <- b + gamma*sign(mean_load - load),
+ *        and FP8 scaling S = max|X|/448, X_fp8 = clip(round(X/S), -448, 448).
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *  - logits are a fixed-order fp32 FMA chain over the hidden dimension
+ *    (index ascending, starting from +0.0f); the pages give only u^T e_i;
+ *  - sigmoid is evaluated in double and rounded once to fp32;
+ *  - ties in the Topk are broken toward the lower expert index; -0 == +0;
+ *  - group-limited routing: G contiguous groups of N/G experts; a group's
+ *    score is the fp32 sum of its two largest biased keys; the TG best
+ *    groups (ties to the lower group) are kept; the pages do not define it
+ *    (parity unpinned by the pages; pinned only by brute force against this
+ *    reading);
+ *  - gates: g_j = s_j / sum of the selected s, no extra scaling factor;
+ *  - the FFN is SwiGLU without biases: W2 (silu(W1 u) * (W3 u)); the pages
+ *    only write FFN_i (parity unpinned by the pages; pinned by the dense
+ *    textbook reduction against an independent library matmul);
+ *  - permutation: stable counting sort of (token, slot) pairs by expert;
+ *  - the bias update compares load_i * N with T*k exactly in integers;
+ *    gamma is the fp32 value nearest 0.001; sign(0) = 0;
+ *  - FP8 is OCP E4M3FN (largest finite 448); scale = amax/448 as an fp32
+ *    divide; x/scale is an fp32 divide, clamped to +-448, then rounded to the
+ *    nearest E4M3 value, ties to even; an all-zero tile has scale 0 and all
+ *    codes 0.
+ *
+ * Build: gcc -O2 -fno-fast-math -ffp-contract=off -fopenmp -shared -fPIC.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_F32 0
+#define ORC_BF16 1
+
+/* ---------------------------------------------------------------------- */
+/* scalar helpers                                                         */
+/* ---------------------------------------------------------------------- */
+
+static float bf16_bits_to_float(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* Round a double to bfloat16 with a single rounding, nearest-even.  bf16
+ * keeps 8 significant bits; below 2^-126 the grid step is fixed at 2^-133. */
+static uint16_t double_to_bf16_bits(double v) {
+    if (isnan(v)) return 0x7fc0;
+    double a = fabs(v), r = 0.0;
+    if (a != 0.0 && !isinf(a)) {
+        int ex;
+        frexp(a, &ex); /* a in [2^(ex-1), 2^ex) */
+        int step = ex - 8;
+        if (step < -133) step = -133;
+        r = ldexp(nearbyint(ldexp(a, -step)), step); /* exact in double */
+    } else if (isinf(a)) {
+        r = a;
+    }
+    float f = (float)r; /* exact, or +inf past the largest finite bf16 */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    u >>= 16;
+    if (signbit(v)) u |= 0x8000u;
+    return (uint16_t)u;
+}
+
+static float load_elem(const void* p, int dtype, int64_t i) {
+    if (dtype == ORC_BF16) return bf16_bits_to_float(((const uint16_t*)p)[i]);
+    return ((const float*)p)[i];
+}
+
+static void store_elem_from_double(void* p, int dtype, int64_t i, double v) {
+    if (dtype == ORC_BF16)
+        ((uint16_t*)p)[i] = double_to_bf16_bits(v);
+    else
+        ((float*)p)[i] = (float)v;
+}
+
+/* Exposed for the pins: round doubles to the storage dtype. */
+void orc_round_to_dtype(int64_t n, int dtype, const double* v, void* out) {
+    for (int64_t i = 0; i < n; ++i) store_elem_from_double(out, dtype, i, v[i]);
+}
+
+/* ---------------------------------------------------------------------- */
+/* routing: affinity, biased selection, gates   [P4] Methode 2            */
+/* ---------------------------------------------------------------------- */
+
+/* z[t,i] = u_t . e_i as the chain acc = fma(x[t,j], e[i,j], acc), j = 0..d-1,
+ * starting from +0.0f.  The loop runs over j outermost so that several
+ * independent chains advance together; each output's own order is the
+ * definition above. */
+void orc_logits(int64_t T, int64_t d, int64_t N, int x_dtype, const void* x,
+                const float* centroids, float* z) {
+    float* et = (float*)malloc((size_t)(d * N) * sizeof(float));
+    for (int64_t i = 0; i < N; ++i)
+        for (int64_t j = 0; j < d; ++j) et[j * N + i] = centroids[i * d + j];
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        float* zt = z + t * N;
+        for (int64_t i = 0; i < N; ++i) zt[i] = 0.0f;
+        for (int64_t j = 0; j < d; ++j) {
+            float xv = load_elem(x, x_dtype, t * d + j);
+            const float* ej = et + j * N;
+            for (int64_t i = 0; i < N; ++i) zt[i] = fmaf(xv, ej[i], zt[i]);
+        }
+    }
+    free(et);
+}
+
+/* s = Sigmoid(z), in double, rounded once to fp32.   [P4] s_{i,t} */
+void orc_sigmoid(int64_t n, const float* z, float* s) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) s[i] = (float)(1.0 / (1.0 + exp(-(double)z[i])));
+}
+
+/* total order used for every selection: larger key first, lower index on ties */
+static int beats(float ra, int64_t a, float rb, int64_t b) {
+    return ra > rb || (ra == rb && a < b);
+}
+
+/* For one token: scores s[N], bias b[N] -> idx[k] (selection order), gate[k].
+ * [P4]: g'_{i,t} = s_{i,t} if s_{i,t}+b_i is among the K_r largest of
+ * {s_{j,t}+b_j}; gates are the g' normalised over the chosen experts; the bias
+ * only enters the key. */
+static void select_one(int64_t N, int64_t k, int64_t G, int64_t TG, const float* s,
+                       const float* b, int32_t* idx, float* gate, float* r,
+                       unsigned char* allowed) {
+    for (int64_t i = 0; i < N; ++i) {
+        float v = s[i] + b[i];
+        if (v == 0.0f) v = 0.0f; /* -0 -> +0 */
+        r[i] = v;
+        allowed[i] = 1;
+    }
+    if (G > 1) {
+        int64_t gs = N / G;
+        float gscore[1024];
+        unsigned char gkeep[1024];
+        for (int64_t g = 0; g < G; ++g) {
+            /* two largest keys of the group under the total order */
+            int64_t i1 = -1, i2 = -1;
+            for (int64_t i = g * gs; i < (g + 1) * gs; ++i) {
+                if (i1 < 0 || beats(r[i], i, r[i1], i1)) {
+                    i2 = i1;
+                    i1 = i;
+                } else if (i2 < 0 || beats(r[i], i, r[i2], i2)) {
+                    i2 = i;
+                }
+            }
+            float sc = r[i1] + r[i2];
+            if (sc == 0.0f) sc = 0.0f;
+            gscore[g] = sc;
+            gkeep[g] = 0;
+        }
+        for (int64_t pick = 0; pick < TG; ++pick) {
+            int64_t best = -1;
+            for (int64_t g = 0; g < G; ++g) {
+                if (gkeep[g]) continue;
+                if (best < 0 || beats(gscore[g], g, gscore[best], best)) best = g;
+            }
+            gkeep[best] = 1;
+        }
+        for (int64_t i = 0; i < N; ++i) allowed[i] = gkeep[i / gs];
+    }
+    for (int64_t j = 0; j < k; ++j) {
+        int64_t best = -1;
+        for (int64_t i = 0; i < N; ++i) {
+            if (!allowed[i]) continue;
+            if (best < 0 || beats(r[i], i, r[best], best)) best = i;
+        }
+        idx[j] = (int32_t)best;
+        allowed[best] = 0;
+    }
+    double S = 0.0;
+    for (int64_t j = 0; j < k; ++j) S += (double)s[idx[j]];
+    for (int64_t j = 0; j < k; ++j) gate[j] = (float)((double)s[idx[j]] / S);
+}
+
+void orc_select(int64_t T, int64_t N, int64_t k, int64_t G, int64_t TG, const float* s,
+                const float* bias, int32_t* idx, float* gate) {
+#pragma omp parallel
+    {
+        float* r = (float*)malloc((size_t)N * sizeof(float));
+        unsigned char* allowed = (unsigned char*)malloc((size_t)N);
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < T; ++t)
+            select_one(N, k, G, TG, s + t * N, bias, idx + t * k, gate + t * k, r, allowed);
+        free(r);
+        free(allowed);
+    }
+}
+
+/* counts[e] = number of (token, slot) pairs routed to e (the step's load) */
+void orc_histogram(int64_t T, int64_t k, int64_t N, const int32_t* idx, int32_t* counts) {
+    for (int64_t e = 0; e < N; ++e) counts[e] = 0;
+    for (int64_t p = 0; p < T * k; ++p) counts[idx[p]] += 1;
+}
+
+/* Whole routing step: logits, sigmoid, biased selection, gates, counts.
+ * scores may be NULL. */
+void orc_route(int64_t T, int64_t d, int64_t N, int64_t k, int64_t G, int64_t TG,
+               int x_dtype, const void* x, const float* centroids, const float* bias,
+               float* scores, int32_t* idx, float* gate, int32_t* counts) {
+    float* z = (float*)malloc((size_t)(T * N) * sizeof(float));
+    float* s = scores ? scores : (float*)malloc((size_t)(T * N) * sizeof(float));
+    orc_logits(T, d, N, x_dtype, x, centroids, z);
+    orc_sigmoid(T * N, z, s);
+    orc_select(T, N, k, G, TG, s, bias, idx, gate);
+    orc_histogram(T, k, N, idx, counts);
+    if (!scores) free(s);
+    free(z);
+}
+
+/* ---------------------------------------------------------------------- */
+/* permutation by expert (stable counting sort)                           */
+/* ---------------------------------------------------------------------- */
+
+/* offsets[N+1] = exclusive prefix sum of the per-expert counts; rows are
+ * handed out scanning tokens t ascending, then slots j ascending:
+ * row = offsets[e] + (rows of e handed out so far). */
+void orc_permute(int64_t T, int64_t k, int64_t N, const int32_t* idx, int32_t* offsets,
+                 int32_t* src_token, int32_t* dst_row) {
+    int32_t* counts = (int32_t*)calloc((size_t)N, sizeof(int32_t));
+    int32_t* cursor = (int32_t*)calloc((size_t)N, sizeof(int32_t));
+    orc_histogram(T, k, N, idx, counts);
+    offsets[0] = 0;
+    for (int64_t e = 0; e < N; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t j = 0; j < k; ++j) {
+            int32_t e = idx[t * k + j];
+            int32_t row = offsets[e] + cursor[e]++;
+            src_token[row] = (int32_t)t;
+            dst_row[t * k + j] = row;
+        }
+    free(counts);
+    free(cursor);
+}
+
+/* out[r] = in[src[r]], rows of row_bytes bytes, bit for bit */
+void orc_gather_rows(int64_t rows, int64_t row_bytes, const int32_t* src, const void* in,
+                     void* out) {
+    for (int64_t r = 0; r < rows; ++r)
+        memcpy((char*)out + r * row_bytes, (const char*)in + (int64_t)src[r] * row_bytes,
+               (size_t)row_bytes);
+}
+
+/* ---------------------------------------------------------------------- */
+/* expert FFN (SwiGLU) in double accumulation                              */
+/* ---------------------------------------------------------------------- */
+
+static double silu_d(double a) { return a / (1.0 + exp(-a)); }
+
+/* A [M,d] rows of one expert; w13 [2I,d]: rows 0..I-1 are W1 (gate), rows
+ * I..2I-1 are W3 (up); w2 [d,I].  y[m,:] = W2 (silu(W1 a_m) * (W3 a_m)).
+ * a, b: double sums rounded to fp32; h: double, rounded to the storage dtype;
+ * y: double sum rounded to the storage dtype. */
+void orc_swiglu_ffn(int64_t M, int64_t d, int64_t I, int dtype, const void* A,
+                    const void* w13, const void* w2, void* y) {
+#pragma omp parallel
+    {
+        double* hrow = (double*)malloc((size_t)I * sizeof(double));
+        double* arow = (double*)malloc((size_t)d * sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t m = 0; m < M; ++m) {
+            for (int64_t j = 0; j < d; ++j) arow[j] = (double)load_elem(A, dtype, m * d + j);
+            for (int64_t n = 0; n < I; ++n) {
+                double sa = 0.0, sb = 0.0;
+                for (int64_t j = 0; j < d; ++j) {
+                    sa += arow[j] * (double)load_elem(w13, dtype, n * d + j);
+                    sb += arow[j] * (double)load_elem(w13, dtype, (I + n) * d + j);
+                }
+                double a = (double)(float)sa, b = (double)(float)sb;
+                double h = silu_d(a) * b;
+                /* round h to the storage dtype */
+                if (dtype == ORC_BF16) {
+                    uint16_t hb = double_to_bf16_bits(h);
+                    hrow[n] = (double)bf16_bits_to_float(hb);
+                } else {
+                    hrow[n] = (double)(float)h;
+                }
+            }
+            for (int64_t c = 0; c < d; ++c) {
+                double acc = 0.0;
+                for (int64_t n = 0; n < I; ++n)
+                    acc += hrow[n] * (double)load_elem(w2, dtype, c * I + n);
+                store_elem_from_double(y, dtype, m * d + c, acc);
+            }
+        }
+        free(hrow);
+        free(arow);
+    }
+}
+
+/* ---------------------------------------------------------------------- */
+/* FP8 E4M3FN   [P4k] tiles/blocks, [P1] scale rule                        */
+/* ---------------------------------------------------------------------- */
+
+/* E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits; no infinities;
+ * S.1111.111 is NaN; largest finite 448 = 1.75 * 2^8; smallest normal 2^-6;
+ * subnormals m * 2^-9, m = 1..7. */
+float orc_e4m3_decode(uint8_t c) {
+    int s = c >> 7, e = (c >> 3) & 0xf, m = c & 7;
+    double v;
+    if (e == 0xf && m == 7) return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(1.0 + m / 8.0, e - 7);
+    return (float)(s ? -v : v);
+}
+
+/* nearest E4M3FN code, ties to even; |v| must be <= 448 (callers clamp) */
+uint8_t orc_e4m3_encode(float v) {
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal grid step 2^-9; a result of 8 steps is the smallest
+         * normal, whose code is also 8 (exponent field 1, mantissa 0) */
+        double q = nearbyint(ldexp(a, 9)); /* default rounding: nearest-even */
+        return (uint8_t)(sign | (uint8_t)q);
+    }
+    int ex;
+    frexp(a, &ex);      /* a = f * 2^ex, f in [0.5, 1) */
+    int e = ex - 1;     /* a = 1.xxx * 2^e, e in [-6, 8] */
+    double q = nearbyint(ldexp(a, 3 - e)); /* 8..16 : 1.mmm scaled by 8 */
+    if (q == 16.0) {
+        q = 8.0;
+        e += 1;
+    }
+    int mant = (int)q - 8;
+    return (uint8_t)(sign | (uint8_t)(((e + 7) << 3) | mant));
+}
+
+void orc_e4m3_encode_array(int64_t n, const float* v, uint8_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_encode(v[i]);
+}
+
+void orc_e4m3_decode_array(int64_t n, const uint8_t* c, float* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_decode(c[i]);
+}
+
+/* quantise a group of values that share one scale: scale = amax/448 (fp32
+ * divide); q = E4M3(clamp(v/scale, -448, 448)); all-zero -> scale 0, codes 0 */
+static float quant_scale(float amax) { return amax / 448.0f; }
+
+static uint8_t quant_one(float v, float scale) {
+    if (scale == 0.0f) return 0;
+    float t = v / scale;
+    if (t > 448.0f) t = 448.0f;
+    if (t < -448.0f) t = -448.0f;
+    return orc_e4m3_encode(t);
+}
+
+/* activations: rows x cols (cols % 128 == 0), one scale per row per 128
+ * consecutive columns (a 1x128 tile along the contraction dimension).
+ * scales: [rows, cols/128] */
+void orc_quant_act_fp8(int64_t rows, int64_t cols, int dtype, const void* x, uint8_t* q,
+                       float* scales) {
+    int64_t nt = cols / 128;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < nt; ++c) {
+            float amax = 0.0f;
+            for (int64_t j = 0; j < 128; ++j) {
+                float a = fabsf(load_elem(x, dtype, r * cols + c * 128 + j));
+                if (a > amax) amax = a;
+            }
+            float sc = quant_scale(amax);
+            scales[r * nt + c] = sc;
+            for (int64_t j = 0; j < 128; ++j)
+                q[r * cols + c * 128 + j] = quant_one(load_elem(x, dtype, r * cols + c * 128 + j), sc);
+        }
+}
+
+/* weights: n_mats matrices of rows x cols (both % 128 == 0), one scale per
+ * 128x128 block.  scales: [n_mats, rows/128, cols/128] */
+void orc_quant_weight_fp8(int64_t n_mats, int64_t rows, int64_t cols, int dtype, const void* w,
+                          uint8_t* q, float* scales) {
+    int64_t br = rows / 128, bc = cols / 128;
+#pragma omp parallel for schedule(static)
+    for (int64_t mb = 0; mb < n_mats * br; ++mb) {
+        int64_t mat = mb / br, rb = mb % br;
+        for (int64_t cb = 0; cb < bc; ++cb) {
+            float amax = 0.0f;
+            for (int64_t i = 0; i < 128; ++i)
+                for (int64_t j = 0; j < 128; ++j) {
+                    int64_t off = mat * rows * cols + (rb * 128 + i) * cols + cb * 128 + j;
+                    float a = fabsf(load_elem(w, dtype, off));
+                    if (a > amax) amax = a;
+                }
+            float sc = quant_scale(amax);
+            scales[(mat * br + rb) * bc + cb] = sc;
+            for (int64_t i = 0; i < 128; ++i)
+                for (int64_t j = 0; j < 128; ++j) {
+                    int64_t off = mat * rows * cols + (rb * 128 + i) * cols + cb * 128 + j;
+                    q[off] = quant_one(load_elem(w, dtype, off), sc);
+                }
+        }
+    }
+}
+
+/* sum over one 128-wide contraction block of decoded code products; exact in
+ * double (each product has at most 8 significant bits, 128 terms) */
+static double block_dot(const uint8_t* a, const uint8_t* b, const double* lut) {
+    double s = 0.0;
+    for (int j = 0; j < 128; ++j) s += lut[a[j]] * lut[b[j]];
+    return s;
+}
+
+/* FP8 SwiGLU expert:  A_q [M,d] codes with A_s [M,d/128];  w13_q [2I,d] with
+ * w13_s [2I/128, d/128]; w2_q [d,I] with w2_s [d/128, I/128].
+ * Each contraction is sum over 128-blocks kb of (s_a[m,kb]*s_w[nb,kb]) times
+ * the block's exact code-product sum (the "promotion every 128" of [P4k]).
+ * a, b rounded to fp32; h = silu(a)*b rounded to fp32, then quantised per
+ * 1x128 tile exactly like the activations; y rounded to bf16. */
+void orc_swiglu_ffn_fp8(int64_t M, int64_t d, int64_t I, const uint8_t* Aq, const float* As,
+                        const uint8_t* w13q, const float* w13s, const uint8_t* w2q,
+                        const float* w2s, uint16_t* y_bf16) {
+    double lut[256];
+    for (int c = 0; c < 256; ++c) {
+        float v = orc_e4m3_decode((uint8_t)c);
+        lut[c] = isnan(v) ? 0.0 : (double)v;
+    }
+    int64_t kd = d / 128, ki = I / 128;
+#pragma omp parallel
+    {
+        float* hrow = (float*)malloc((size_t)I * sizeof(float));
+        uint8_t* hq = (uint8_t*)malloc((size_t)I);
+        float* hs = (float*)malloc((size_t)ki * sizeof(float));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t m = 0; m < M; ++m) {
+            const uint8_t* am = Aq + m * d;
+            for (int64_t n = 0; n < I; ++n) {
+                double sa = 0.0, sb = 0.0;
+                for (int64_t kb = 0; kb < kd; ++kb) {
+                    double pa = block_dot(am + kb * 128, w13q + n * d + kb * 128, lut);
+                    double pb = block_dot(am + kb * 128, w13q + (I + n) * d + kb * 128, lut);
+                    double xs = (double)As[m * kd + kb];
+                    sa += xs * (double)w13s[(n / 128) * kd + kb] * pa;
+                    sb += xs * (double)w13s[((I + n) / 128) * kd + kb] * pb;
+                }
+                double a = (double)(float)sa, b = (double)(float)sb;
+                hrow[n] = (float)(silu_d(a) * b);
+            }
+            for (int64_t c = 0; c < ki; ++c) {
+                float amax = 0.0f;
+                for (int64_t j = 0; j < 128; ++j) {
+                    float v = fabsf(hrow[c * 128 + j]);
+                    if (v > amax) amax = v;
+                }
+                float sc = quant_scale(amax);
+                hs[c] = sc;
+                for (int64_t j = 0; j < 128; ++j) hq[c * 128 + j] = quant_one(hrow[c * 128 + j], sc);
+            }
+            for (int64_t c = 0; c < d; ++c) {
+                double acc = 0.0;
+                for (int64_t kb = 0; kb < ki; ++kb) {
+                    double p = block_dot(hq + kb * 128, w2q + c * I + kb * 128, lut);
+                    acc += (double)hs[kb] * (double)w2s[(c / 128) * ki + kb] * p;
+                }
+                y_bf16[m * d + c] = double_to_bf16_bits(acc);
+            }
+        }
+        free(hrow);
+        free(hq);
+        free(hs);
+    }
+}
+
+/* ---------------------------------------------------------------------- */
+/* combine   [P4] h'_t = u_t + sum shared FFN + sum_i g_{i,t} FFN_i        */
+/* ---------------------------------------------------------------------- */
+
+/* out[t,:] = x[t,:] (if x != NULL) + y_shared[t,:] + sum_j gate[t,j] *
+ * y_perm[dst_row[t,j], :], summed in double, rounded to the dtype. */
+void orc_combine(int64_t T, int64_t d, int64_t k, int dtype, const void* x,
+                 const void* y_shared, const void* y_perm, const float* gate,
+                 const int32_t* dst_row, void* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t c = 0; c < d; ++c) {
+            double acc = 0.0;
+            if (x) acc += (double)load_elem(x, dtype, t * d + c);
+            if (y_shared) acc += (double)load_elem(y_shared, dtype, t * d + c);
+            for (int64_t j = 0; j < k; ++j)
+                acc += (double)gate[t * k + j] *
+                       (double)load_elem(y_perm, dtype, (int64_t)dst_row[t * k + j] * d + c);
+            store_elem_from_double(out, dtype, t * d + c, acc);
+        }
+}
+
+/* ---------------------------------------------------------------------- */
+/* bias update   [P4] end-of-step rule, [P1] sign form                     */
+/* ---------------------------------------------------------------------- */
+
+/* expert i is overloaded when its load exceeds the mean load T*k/N, i.e.
+ * counts[i]*N > T*k: b_i <- b_i - gamma; underloaded: b_i <- b_i + gamma;
+ * exactly at the mean: unchanged.  fp32 arithmetic. */
+void orc_bias_update(int64_t N, int64_t TK, const int32_t* counts, float gamma, float* bias) {
+    for (int64_t i = 0; i < N; ++i) {
+        int64_t lhs = (int64_t)counts[i] * N;
+        if (lhs > TK)
+            bias[i] = bias[i] - gamma;
+        else if (lhs < TK)
+            bias[i] = bias[i] + gamma;
+    }
+}
