@@ -277,39 +277,34 @@ static double silu_d(double a) { return a / (1.0 + exp(-a)); }
  * y: double sum rounded to the storage dtype. */
 void orc_swiglu_ffn(int64_t M, int64_t d, int64_t I, int dtype, const void* A,
                     const void* w13, const void* w2, void* y) {
-#pragma omp parallel
-    {
-        double* hrow = (double*)malloc((size_t)I * sizeof(double));
-        double* arow = (double*)malloc((size_t)d * sizeof(double));
-#pragma omp for schedule(dynamic, 1)
-        for (int64_t m = 0; m < M; ++m) {
-            for (int64_t j = 0; j < d; ++j) arow[j] = (double)load_elem(A, dtype, m * d + j);
-            for (int64_t n = 0; n < I; ++n) {
-                double sa = 0.0, sb = 0.0;
-                for (int64_t j = 0; j < d; ++j) {
-                    sa += arow[j] * (double)load_elem(w13, dtype, n * d + j);
-                    sb += arow[j] * (double)load_elem(w13, dtype, (I + n) * d + j);
-                }
-                double a = (double)(float)sa, b = (double)(float)sb;
-                double h = silu_d(a) * b;
-                /* round h to the storage dtype */
-                if (dtype == ORC_BF16) {
-                    uint16_t hb = double_to_bf16_bits(h);
-                    hrow[n] = (double)bf16_bits_to_float(hb);
-                } else {
-                    hrow[n] = (double)(float)h;
-                }
+    double* h = (double*)malloc((size_t)(M * I) * sizeof(double));
+    /* h[m,n]: one (row, column) per iteration; parallel over both */
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < I; ++n) {
+            double sa = 0.0, sb = 0.0;
+            for (int64_t j = 0; j < d; ++j) {
+                double av = (double)load_elem(A, dtype, m * d + j);
+                sa += av * (double)load_elem(w13, dtype, n * d + j);
+                sb += av * (double)load_elem(w13, dtype, (I + n) * d + j);
             }
-            for (int64_t c = 0; c < d; ++c) {
-                double acc = 0.0;
-                for (int64_t n = 0; n < I; ++n)
-                    acc += hrow[n] * (double)load_elem(w2, dtype, c * I + n);
-                store_elem_from_double(y, dtype, m * d + c, acc);
-            }
+            double a = (double)(float)sa, b = (double)(float)sb;
+            double hv = silu_d(a) * b;
+            /* h is stored in the storage dtype between the two projections */
+            if (dtype == ORC_BF16)
+                h[m * I + n] = (double)bf16_bits_to_float(double_to_bf16_bits(hv));
+            else
+                h[m * I + n] = (double)(float)hv;
         }
-        free(hrow);
-        free(arow);
-    }
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (int64_t n = 0; n < I; ++n)
+                acc += h[m * I + n] * (double)load_elem(w2, dtype, c * I + n);
+            store_elem_from_double(y, dtype, m * d + c, acc);
+        }
+    free(h);
 }
 
 /* ---------------------------------------------------------------------- */
@@ -443,49 +438,39 @@ void orc_swiglu_ffn_fp8(int64_t M, int64_t d, int64_t I, const uint8_t* Aq, cons
         lut[c] = isnan(v) ? 0.0 : (double)v;
     }
     int64_t kd = d / 128, ki = I / 128;
-#pragma omp parallel
-    {
-        float* hrow = (float*)malloc((size_t)I * sizeof(float));
-        uint8_t* hq = (uint8_t*)malloc((size_t)I);
-        float* hs = (float*)malloc((size_t)ki * sizeof(float));
-#pragma omp for schedule(dynamic, 1)
-        for (int64_t m = 0; m < M; ++m) {
+    float* h = (float*)malloc((size_t)(M * I) * sizeof(float));
+    uint8_t* hq = (uint8_t*)malloc((size_t)(M * I));
+    float* hs = (float*)malloc((size_t)(M * ki) * sizeof(float));
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < I; ++n) {
             const uint8_t* am = Aq + m * d;
-            for (int64_t n = 0; n < I; ++n) {
-                double sa = 0.0, sb = 0.0;
-                for (int64_t kb = 0; kb < kd; ++kb) {
-                    double pa = block_dot(am + kb * 128, w13q + n * d + kb * 128, lut);
-                    double pb = block_dot(am + kb * 128, w13q + (I + n) * d + kb * 128, lut);
-                    double xs = (double)As[m * kd + kb];
-                    sa += xs * (double)w13s[(n / 128) * kd + kb] * pa;
-                    sb += xs * (double)w13s[((I + n) / 128) * kd + kb] * pb;
-                }
-                double a = (double)(float)sa, b = (double)(float)sb;
-                hrow[n] = (float)(silu_d(a) * b);
+            double sa = 0.0, sb = 0.0;
+            for (int64_t kb = 0; kb < kd; ++kb) {
+                double pa = block_dot(am + kb * 128, w13q + n * d + kb * 128, lut);
+                double pb = block_dot(am + kb * 128, w13q + (I + n) * d + kb * 128, lut);
+                double xs = (double)As[m * kd + kb];
+                sa += xs * (double)w13s[(n / 128) * kd + kb] * pa;
+                sb += xs * (double)w13s[((I + n) / 128) * kd + kb] * pb;
             }
-            for (int64_t c = 0; c < ki; ++c) {
-                float amax = 0.0f;
-                for (int64_t j = 0; j < 128; ++j) {
-                    float v = fabsf(hrow[c * 128 + j]);
-                    if (v > amax) amax = v;
-                }
-                float sc = quant_scale(amax);
-                hs[c] = sc;
-                for (int64_t j = 0; j < 128; ++j) hq[c * 128 + j] = quant_one(hrow[c * 128 + j], sc);
-            }
-            for (int64_t c = 0; c < d; ++c) {
-                double acc = 0.0;
-                for (int64_t kb = 0; kb < ki; ++kb) {
-                    double p = block_dot(hq + kb * 128, w2q + c * I + kb * 128, lut);
-                    acc += (double)hs[kb] * (double)w2s[(c / 128) * ki + kb] * p;
-                }
-                y_bf16[m * d + c] = double_to_bf16_bits(acc);
-            }
+            double a = (double)(float)sa, b = (double)(float)sb;
+            h[m * I + n] = (float)(silu_d(a) * b);
         }
-        free(hrow);
-        free(hq);
-        free(hs);
-    }
+    /* re-quantise h per 1x128 tile, exactly like the activations */
+    orc_quant_act_fp8(M, I, ORC_F32, h, hq, hs);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (int64_t kb = 0; kb < ki; ++kb) {
+                double p = block_dot(hq + m * I + kb * 128, w2q + c * I + kb * 128, lut);
+                acc += (double)hs[m * ki + kb] * (double)w2s[(c / 128) * ki + kb] * p;
+            }
+            y_bf16[m * d + c] = double_to_bf16_bits(acc);
+        }
+    free(h);
+    free(hq);
+    free(hs);
 }
 
 /* ---------------------------------------------------------------------- */
