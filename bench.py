@@ -1,0 +1,207 @@
+"""Benchmark: one DeepSeekMoE layer step at DeepSeek-V3 shape on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v3_bf16|v3_fp8|mid_bf16]
+                    [--no-cpu-baseline]
+
+A step is the whole hot path on one batch already resident in HBM:
+route -> permute -> expert FFN (routed + shared) -> combine -> bias update.
+Prints ONE JSON line.  `value` is tokens per second of the whole step;
+`roofline` describes the dominant stage, the grouped expert GEMMs (gate/up
+with fused SwiGLU, then down), timed live with HIP events on the stream they
+run on; `cpu_baseline` is the CPU oracle timed on a bounded sample of the same
+workload on this host.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"bf16": 2516.6e12, "fp8": 5033.2e12, "hbm": 8.0e12}
+
+METRIC = "MoE-layer fwd tokens/s at V3 shape; grouped-GEMM % of MFMA peak"
+
+
+def ffn_flops(c):
+    T, k, d, I, Is = c["T"], c["k"], c["d"], c["I"], c["Is"]
+    return 6.0 * T * k * d * I + 6.0 * T * d * Is
+
+
+def ffn_weight_bytes(c):
+    eb = 1 if c.get("fp8") else 2
+    return eb * (3.0 * c["N"] * c["d"] * c["I"] + 3.0 * c["d"] * c["Is"])
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="v3_bf16")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(cfg, dev, log):
+    """Time the oracle (untuned) on a bounded sample of the workload and scale
+    to tokens/s: route, permute and combine on S tokens; the SwiGLU expert on S
+    rows of expert 0, counted k+1 times per token (k routed rows + the shared
+    expert row)."""
+    import numpy as np
+
+    import moe_inputs
+    from oracle import oracle as orc
+
+    S = 64
+    xs = moe_inputs.to_host(dev["x"][:S])
+    E = moe_inputs.to_host(dev["centroids"])
+    b = moe_inputs.to_host(dev["bias"])
+    w13 = moe_inputs.to_host(dev["w13"][0])
+    w2 = moe_inputs.to_host(dev["w2"][0])
+    orc.lib()
+    t0 = time.perf_counter()
+    r = orc.route(xs, E, b, cfg["k"], cfg["G"], cfg["TG"])
+    t1 = time.perf_counter()
+    off, src, dst = orc.permute(r["idx"], cfg["N"])
+    xp = orc.gather_rows(xs, src)
+    t2 = time.perf_counter()
+    if cfg.get("fp8"):
+        xq, xsc = orc.quant_act_fp8(xs)
+        q13, s13 = orc.quant_weight_fp8(w13)
+        q2, s2 = orc.quant_weight_fp8(w2)
+        t3a = time.perf_counter()
+        y = orc.swiglu_ffn_fp8(xq, xsc, q13, s13, q2, s2)
+        t3 = time.perf_counter()
+        ffn_s = t3 - t3a
+    else:
+        t3a = time.perf_counter()
+        y = orc.swiglu_ffn(xs, w13, w2)
+        t3 = time.perf_counter()
+        ffn_s = t3 - t3a
+    yp = np.repeat(y, cfg["k"], axis=0)[: S * cfg["k"]]
+    t4 = time.perf_counter()
+    orc.combine(xs, y, yp, r["gate"], dst, cfg["dtype"])
+    orc.bias_update(r["counts"], S * cfg["k"], b)
+    t5 = time.perf_counter()
+    per_token = ((t1 - t0) + (t2 - t1) + (t5 - t4)) / S + ffn_s / S * (cfg["k"] + 1)
+    cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    log("cpu oracle: route %.2fs permute %.3fs ffn(%d rows) %.2fs combine %.3fs -> %.3f s/token"
+        % (t1 - t0, t2 - t1, S, ffn_s, t5 - t4, per_token))
+    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "%d tokens of the batch: route, permute, combine, bias update on them; "
+                      "the SwiGLU expert on %d rows of expert 0, counted k+1=%d times per "
+                      "token" % (S, S, cfg["k"] + 1)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(no collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import moe_inputs
+    import sparse_moe_layer_bias_amd as moe
+    from sparse_moe_layer_bias_amd.layer import MoeLayer
+
+    def log(*a):
+        print(*a, file=sys.stderr, flush=True)
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    moe.lib()
+    cfg = dict(moe_inputs.CONFIGS[args.workload])
+    T = cfg["T"]
+    log("generating inputs for", args.workload, cfg)
+    dev = moe_inputs.make_layer_inputs(cfg, args.seed, "cuda")
+    layer = MoeLayer(cfg, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"])
+    x, E = dev["x"], dev["centroids"]
+    bias = dev["bias"].clone()
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        layer.forward(x, E, bias)
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    # timed region: K whole steps; events bracket each stage on the stream
+    stages = ["route", "permute", "expert_ffn", "combine", "bias_update"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+          for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for s in range(args.steps):
+        e = ev[s]
+        e[0].record(stream)
+        layer.route(x, E, bias)
+        e[1].record(stream)
+        layer.permute(x)
+        e[2].record(stream)
+        layer.expert_ffn(x)
+        e[3].record(stream)
+        layer.combine(x)
+        e[4].record(stream)
+        layer.bias_update(bias)
+        e[5].record(stream)
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_stop)
+    ms_per_step = total_ms / args.steps
+    stage_ms = {st: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps))
+                / args.steps for i, st in enumerate(stages)}
+    log("stages ms:", json.dumps({k: round(v, 4) for k, v in stage_ms.items()}))
+
+    fp8 = bool(cfg.get("fp8"))
+    flops = ffn_flops(cfg)
+    ffn_s = stage_ms["expert_ffn"] / 1e3
+    achieved = flops / ffn_s
+    peak = PEAK["fp8" if fp8 else "bf16"]
+    wbytes = ffn_weight_bytes(cfg)
+    result = {
+        "metric": METRIC,
+        "value": T / (ms_per_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8" if fp8 else cfg["dtype"],
+        "data": "synthetic",
+        "config": {"workload": "%s: T=%d d=%d, %d routed experts top-%d%s + %d shared, "
+                               "SwiGLU I=%d, %s expert GEMMs" %
+                               (args.workload, T, cfg["d"], cfg["N"], cfg["k"],
+                                (" (%d groups, top-%d)" % (cfg["G"], cfg["TG"]))
+                                if cfg["G"] > 1 else "", 1, cfg["I"],
+                                "FP8 E4M3" if fp8 else cfg["dtype"]),
+                   "global_batch": T, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": "grouped expert GEMMs (gate/up+SwiGLU, down)",
+                     "achieved": achieved / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": None,
+                     "weight_stream_frac_of_hbm": wbytes / ffn_s / PEAK["hbm"]},
+        "stages_ms": stage_ms,
+        "layer_tflops": (flops + 2.0 * T * cfg["d"] * cfg["N"]) / (ms_per_step / 1e3) / 1e12,
+    }
+    if not args.no_cpu_baseline:
+        try:
+            result["cpu_baseline"] = cpu_baseline(cfg, dev, log)
+        except Exception as ex:  # report, never hide
+            log("cpu baseline failed:", repr(ex))
+            result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

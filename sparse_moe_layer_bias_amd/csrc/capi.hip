@@ -1,0 +1,266 @@
+// capi.cpp -- the C ABI of libmoe (include/moe.h): argument validation, error
+// reporting and dispatch to the kernel launchers.  Validation runs on the host
+// before anything is enqueued, so a rejected call has no effect on the device.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "moe_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = 0;
+    return MOE_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define REQ_PTR(p)                                                                   \
+    do {                                                                             \
+        if (!(p)) return fail(MOE_ERR_ARG, "%s: %s is NULL", fn, #p);                \
+        if (!aligned16(p)) return fail(MOE_ERR_ARG, "%s: %s is not 16-byte aligned", \
+                                       fn, #p);                                      \
+    } while (0)
+
+#define OPT_PTR(p)                                                                   \
+    do {                                                                             \
+        if ((p) && !aligned16(p))                                                    \
+            return fail(MOE_ERR_ARG, "%s: %s is not 16-byte aligned", fn, #p);       \
+    } while (0)
+
+int check_cfg(const char* fn, const moe_cfg* c) {
+    if (!c) return fail(MOE_ERR_ARG, "%s: cfg is NULL", fn);
+    if (c->tokens < 0 || c->tokens > (int64_t)1 << 26)
+        return fail(MOE_ERR_ARG, "%s: tokens=%lld out of range", fn, (long long)c->tokens);
+    if (c->hidden <= 0) return fail(MOE_ERR_ARG, "%s: hidden must be > 0", fn);
+    if (c->n_experts < 1 || c->n_experts > 1024)
+        return fail(MOE_ERR_ARG, "%s: n_experts=%lld must be in 1..1024", fn,
+                    (long long)c->n_experts);
+    if (c->top_k < 1 || c->top_k > c->n_experts || c->top_k > 64)
+        return fail(MOE_ERR_ARG, "%s: top_k=%lld must be in 1..min(n_experts, 64)", fn,
+                    (long long)c->top_k);
+    if (c->n_group < 1) return fail(MOE_ERR_ARG, "%s: n_group must be >= 1", fn);
+    if (c->n_group > 1) {
+        if (c->n_group > 64 || c->n_experts % c->n_group)
+            return fail(MOE_ERR_ARG, "%s: n_group must divide n_experts and be <= 64", fn);
+        if (c->n_experts / c->n_group < 2)
+            return fail(MOE_ERR_ARG, "%s: groups need at least 2 experts", fn);
+        if (c->topk_group < 1 || c->topk_group > c->n_group)
+            return fail(MOE_ERR_ARG, "%s: topk_group must be in 1..n_group", fn);
+        if (c->top_k > c->topk_group * (c->n_experts / c->n_group))
+            return fail(MOE_ERR_ARG, "%s: top_k exceeds the experts of the kept groups", fn);
+    }
+    if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: act_dtype must be MOE_F32 or MOE_BF16", fn);
+    if (c->gemm_dtype != c->act_dtype && c->gemm_dtype != MOE_FP8_E4M3)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: gemm_dtype must equal act_dtype or be FP8", fn);
+    if (c->gemm_dtype == MOE_FP8_E4M3 && c->act_dtype != MOE_BF16)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: FP8 expert GEMMs need bf16 activations", fn);
+    if (c->act_dtype == MOE_BF16 && c->hidden % 8)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 needs hidden %% 8 == 0", fn);
+    if (c->act_dtype == MOE_F32 && c->hidden % 4)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: fp32 needs hidden %% 4 == 0", fn);
+    if ((int64_t)c->tokens * c->top_k > INT32_MAX)
+        return fail(MOE_ERR_ARG, "%s: tokens*top_k exceeds int32 row indices", fn);
+    return MOE_OK;
+}
+
+int check_ffn_shape(const char* fn, const moe_cfg* c) {
+    if (c->inter <= 0) return fail(MOE_ERR_ARG, "%s: inter must be > 0", fn);
+    if (c->inter_shared < 0) return fail(MOE_ERR_ARG, "%s: inter_shared must be >= 0", fn);
+    if (c->act_dtype == MOE_BF16 || c->gemm_dtype == MOE_FP8_E4M3) {
+        if (c->hidden % 128 || c->inter % 128 || c->inter_shared % 128)
+            return fail(MOE_ERR_UNSUPPORTED,
+                        "%s: bf16/FP8 expert GEMMs need hidden, inter, inter_shared %% 128 == 0",
+                        fn);
+    }
+    return MOE_OK;
+}
+
+int hip_status(const char* fn, hipError_t e) {
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return 1; }
+
+const char* moe_last_error(void) { return g_err; }
+
+size_t moe_route_workspace_size(const moe_cfg* cfg) {
+    if (!cfg) return 0;
+    return (size_t)(cfg->tokens * cfg->n_experts * 4);
+}
+
+int moe_route(const moe_cfg* cfg, const void* x, const float* centroids, const float* bias,
+              float* scores, int32_t* idx, float* gate, int32_t* counts, void* workspace,
+              size_t workspace_bytes, void* stream) {
+    const char* fn = "moe_route";
+    if (int r = check_cfg(fn, cfg)) return r;
+    REQ_PTR(centroids);
+    REQ_PTR(bias);
+    REQ_PTR(counts);
+    if (cfg->tokens > 0) {
+        REQ_PTR(x);
+        REQ_PTR(idx);
+        REQ_PTR(gate);
+    }
+    OPT_PTR(scores);
+    if (!scores && cfg->tokens > 0) {
+        REQ_PTR(workspace);
+        if (workspace_bytes < moe_route_workspace_size(cfg))
+            return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes,
+                        moe_route_workspace_size(cfg));
+        scores = (float*)workspace;
+    }
+    return hip_status(fn, moe::launch_route(*cfg, x, centroids, bias, scores, idx, gate, counts,
+                                            (hipStream_t)stream));
+}
+
+size_t moe_permute_workspace_size(const moe_cfg* cfg) {
+    if (!cfg) return 0;
+    return moe::permute_workspace_bytes(*cfg);
+}
+
+int moe_permute(const moe_cfg* cfg, const void* x, const int32_t* idx, int32_t* offsets,
+                int32_t* src_token, int32_t* dst_row, void* x_perm, float* x_perm_scale,
+                uint8_t* x_q, float* x_s, void* workspace, size_t workspace_bytes,
+                void* stream) {
+    const char* fn = "moe_permute";
+    if (int r = check_cfg(fn, cfg)) return r;
+    REQ_PTR(offsets);
+    REQ_PTR(workspace);
+    if (cfg->tokens > 0) {
+        REQ_PTR(x);
+        REQ_PTR(idx);
+        REQ_PTR(src_token);
+        REQ_PTR(dst_row);
+        REQ_PTR(x_perm);
+        if (cfg->gemm_dtype == MOE_FP8_E4M3) {
+            if (cfg->hidden % 128)
+                return fail(MOE_ERR_UNSUPPORTED, "%s: FP8 needs hidden %% 128 == 0", fn);
+            REQ_PTR(x_perm_scale);
+            REQ_PTR(x_q);
+            REQ_PTR(x_s);
+        }
+    }
+    if (workspace_bytes < moe_permute_workspace_size(cfg))
+        return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes,
+                    moe_permute_workspace_size(cfg));
+    return hip_status(fn, moe::launch_permute(*cfg, x, idx, offsets, src_token, dst_row, x_perm,
+                                              x_perm_scale, x_q, x_s, workspace,
+                                              (hipStream_t)stream));
+}
+
+size_t moe_expert_ffn_workspace_size(const moe_cfg* cfg) {
+    if (!cfg) return 0;
+    return moe::ffn_workspace_bytes(*cfg);
+}
+
+int moe_expert_ffn(const moe_cfg* cfg, const void* x_perm, const float* x_perm_scale,
+                   const int32_t* offsets, const void* w13, const float* w13_scale,
+                   const void* w2, const float* w2_scale, void* y_perm, const void* x_sh,
+                   const float* x_sh_scale, const void* ws13, const float* ws13_scale,
+                   const void* ws2, const float* ws2_scale, void* y_shared, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+    const char* fn = "moe_expert_ffn";
+    if (int r = check_cfg(fn, cfg)) return r;
+    if (int r = check_ffn_shape(fn, cfg)) return r;
+    const bool fp8 = cfg->gemm_dtype == MOE_FP8_E4M3;
+    if (cfg->tokens > 0) {
+        REQ_PTR(x_perm);
+        REQ_PTR(offsets);
+        REQ_PTR(w13);
+        REQ_PTR(w2);
+        REQ_PTR(y_perm);
+        REQ_PTR(workspace);
+        if (fp8) {
+            REQ_PTR(x_perm_scale);
+            REQ_PTR(w13_scale);
+            REQ_PTR(w2_scale);
+        }
+        if (cfg->inter_shared > 0) {
+            REQ_PTR(x_sh);
+            REQ_PTR(ws13);
+            REQ_PTR(ws2);
+            REQ_PTR(y_shared);
+            if (fp8) {
+                REQ_PTR(x_sh_scale);
+                REQ_PTR(ws13_scale);
+                REQ_PTR(ws2_scale);
+            }
+        }
+        if (workspace_bytes < moe_expert_ffn_workspace_size(cfg))
+            return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes,
+                        moe_expert_ffn_workspace_size(cfg));
+    }
+    moe::FfnArgs a{x_perm, x_perm_scale, offsets, w13, w13_scale, w2, w2_scale, y_perm,
+                   x_sh,   x_sh_scale,   ws13,    ws13_scale, ws2, ws2_scale, y_shared};
+    return hip_status(fn, moe::launch_expert_ffn(*cfg, a, workspace, (hipStream_t)stream));
+}
+
+int moe_combine(const moe_cfg* cfg, const void* x_residual, const void* y_shared,
+                const void* y_perm, const float* gate, const int32_t* dst_row, void* out,
+                void* stream) {
+    const char* fn = "moe_combine";
+    if (int r = check_cfg(fn, cfg)) return r;
+    if (cfg->tokens > 0) {
+        REQ_PTR(y_perm);
+        REQ_PTR(gate);
+        REQ_PTR(dst_row);
+        REQ_PTR(out);
+        OPT_PTR(x_residual);
+        OPT_PTR(y_shared);
+        if (out == x_residual || out == y_shared || out == y_perm)
+            return fail(MOE_ERR_ARG, "%s: out must not alias an input", fn);
+    }
+    return hip_status(fn, moe::launch_combine(*cfg, x_residual, y_shared, y_perm, gate, dst_row,
+                                              out, (hipStream_t)stream));
+}
+
+int moe_bias_update(int64_t n_experts, int64_t tokens_times_k, const int32_t* counts,
+                    float gamma, float* bias, void* stream) {
+    const char* fn = "moe_bias_update";
+    if (n_experts < 1 || n_experts > (int64_t)1 << 20)
+        return fail(MOE_ERR_ARG, "%s: n_experts out of range", fn);
+    if (tokens_times_k < 0) return fail(MOE_ERR_ARG, "%s: tokens_times_k < 0", fn);
+    if (!(gamma == gamma)) return fail(MOE_ERR_ARG, "%s: gamma is NaN", fn);
+    REQ_PTR(counts);
+    REQ_PTR(bias);
+    return hip_status(fn, moe::launch_bias_update(n_experts, tokens_times_k, counts, gamma, bias,
+                                                  (hipStream_t)stream));
+}
+
+int moe_quantize_weights_fp8(int64_t n_mats, int64_t rows, int64_t cols, const void* w_bf16,
+                             uint8_t* w_q, float* w_scale, void* stream) {
+    const char* fn = "moe_quantize_weights_fp8";
+    if (n_mats < 0 || rows <= 0 || cols <= 0 || rows % 128 || cols % 128)
+        return fail(MOE_ERR_ARG, "%s: rows and cols must be positive multiples of 128", fn);
+    if (n_mats * (rows / 128) * (cols / 128) > INT32_MAX)
+        return fail(MOE_ERR_ARG, "%s: too many blocks", fn);
+    if (n_mats > 0) {
+        REQ_PTR(w_bf16);
+        REQ_PTR(w_q);
+        REQ_PTR(w_scale);
+    }
+    return hip_status(fn, moe::launch_quantize_weights(n_mats, rows, cols, w_bf16, w_q, w_scale,
+                                                       (hipStream_t)stream));
+}
+
+}  // extern "C"

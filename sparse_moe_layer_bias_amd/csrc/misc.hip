@@ -1,0 +1,171 @@
+// misc.hip -- combine (un-permute), end-of-step bias update, and the FP8
+// weight block quantiser used as preparation.
+#include "moe_internal.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- combine
+// h'_t = u_t + y_shared[t] + sum_j g_{t,j} * y_perm[dst_row[t,j]]
+// (DeepSeek-V3 report reading guide, xyznot.com/de, "Methode" item 2).
+// A gather: each output row is produced by one block reading its k rows, so no
+// atomics and a fixed fp32 summation order (residual, shared, slots 0..k-1).
+
+template <bool BF16>
+__global__ void __launch_bounds__(128) combine_kernel(const uint4* __restrict__ x,
+                                                      const uint4* __restrict__ ys,
+                                                      const uint4* __restrict__ yp,
+                                                      const float* __restrict__ gate,
+                                                      const int32_t* __restrict__ dst_row,
+                                                      uint4* __restrict__ out, int k,
+                                                      int64_t row_vecs) {
+    __shared__ int32_t rows[64];
+    __shared__ float g[64];
+    const int64_t t = blockIdx.x;
+    if (threadIdx.x < k) {
+        rows[threadIdx.x] = dst_row[t * k + threadIdx.x];
+        g[threadIdx.x] = gate[t * k + threadIdx.x];
+    }
+    __syncthreads();
+    constexpr int E = BF16 ? 8 : 4;
+    for (int64_t v = threadIdx.x; v < row_vecs; v += blockDim.x) {
+        float acc[E];
+#pragma unroll
+        for (int i = 0; i < E; ++i) acc[i] = 0.0f;
+        auto add = [&](const uint4 q, float s) {
+            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+            if constexpr (BF16) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[2 * i] = __builtin_fmaf(s, __uint_as_float(w[i] << 16), acc[2 * i]);
+                    acc[2 * i + 1] =
+                        __builtin_fmaf(s, __uint_as_float(w[i] & 0xffff0000u), acc[2 * i + 1]);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(s, __uint_as_float(w[i]), acc[i]);
+            }
+        };
+        if (x) add(x[t * row_vecs + v], 1.0f);
+        if (ys) add(ys[t * row_vecs + v], 1.0f);
+        for (int j = 0; j < k; ++j) add(yp[(int64_t)rows[j] * row_vecs + v], g[j]);
+        uint4 o;
+        if constexpr (BF16) {
+            o.x = pack_bf16x2(acc[0], acc[1]);
+            o.y = pack_bf16x2(acc[2], acc[3]);
+            o.z = pack_bf16x2(acc[4], acc[5]);
+            o.w = pack_bf16x2(acc[6], acc[7]);
+        } else {
+            o.x = __float_as_uint(acc[0]);
+            o.y = __float_as_uint(acc[1]);
+            o.z = __float_as_uint(acc[2]);
+            o.w = __float_as_uint(acc[3]);
+        }
+        out[t * row_vecs + v] = o;
+    }
+}
+
+hipError_t launch_combine(const moe_cfg& c, const void* x, const void* y_shared,
+                          const void* y_perm, const float* gate, const int32_t* dst_row,
+                          void* out, hipStream_t st) {
+    const int64_t T = c.tokens;
+    if (T == 0) return hipSuccess;
+    const int64_t esz = c.act_dtype == MOE_BF16 ? 2 : 4;
+    const int64_t row_vecs = c.hidden * esz / 16;
+    if (c.act_dtype == MOE_BF16)
+        combine_kernel<true><<<dim3((unsigned)T), 128, 0, st>>>(
+            (const uint4*)x, (const uint4*)y_shared, (const uint4*)y_perm, gate, dst_row,
+            (uint4*)out, (int)c.top_k, row_vecs);
+    else
+        combine_kernel<false><<<dim3((unsigned)T), 128, 0, st>>>(
+            (const uint4*)x, (const uint4*)y_shared, (const uint4*)y_perm, gate, dst_row,
+            (uint4*)out, (int)c.top_k, row_vecs);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- bias update
+// End-of-step rule (reading guide "Methode" item 2; singularity-lens formula
+// paragraph: b_i += gamma * sign(mean_load - load_i)).  Overload is decided
+// exactly in integers: counts[i] * N versus T*k.
+
+__global__ void bias_update_kernel(const int32_t* __restrict__ counts, float gamma,
+                                   float* __restrict__ bias, int64_t N, int64_t TK) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= N) return;
+    const int64_t lhs = (int64_t)counts[i] * N;
+    const float b = bias[i];
+    if (lhs > TK)
+        bias[i] = b - gamma;
+    else if (lhs < TK)
+        bias[i] = b + gamma;
+}
+
+hipError_t launch_bias_update(int64_t N, int64_t TK, const int32_t* counts, float gamma,
+                              float* bias, hipStream_t st) {
+    bias_update_kernel<<<dim3((unsigned)cdiv(N, 256)), 256, 0, st>>>(counts, gamma, bias, N, TK);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- weight FP8
+// One 256-thread block per 128x128 block (reading guide "Kernideen", FP8
+// bullet: block-wise weight scaling): amax -> scale = amax/448 -> E4M3 codes.
+
+__global__ void __launch_bounds__(256) quant_weight_kernel(const uint4* __restrict__ w,
+                                                           uint2* __restrict__ q,
+                                                           float* __restrict__ s, int64_t rows,
+                                                           int64_t cols) {
+    __shared__ float sh[4];
+    const int64_t br = rows / 128, bc = cols / 128;
+    const int64_t blk = blockIdx.x;
+    const int64_t mat = blk / (br * bc), rb = (blk / bc) % br, cb = blk % bc;
+    const int64_t vec_cols = cols / 8;
+    // 128 rows x 16 vectors of 8 bf16; thread handles 8 of the 2048 vectors
+    uint4 v[8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        const int64_t r = rb * 128 + (c >> 4);
+        const int64_t vc = cb * 16 + (c & 15);
+        v[i] = w[(mat * rows + r) * vec_cols + vc];
+        const uint32_t ww[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            amax = fmaxf(amax, fabsf(__uint_as_float(ww[j] << 16)));
+            amax = fmaxf(amax, fabsf(__uint_as_float(ww[j] & 0xffff0000u)));
+        }
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+    const float scale = amax / 448.0f;
+    if (threadIdx.x == 0) s[blk] = scale;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        const int64_t r = rb * 128 + (c >> 4);
+        const int64_t vc = cb * 16 + (c & 15);
+        const uint32_t ww[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            lo |= quant_e4m3(__uint_as_float(ww[j] << 16), scale) << (16 * j);
+            lo |= quant_e4m3(__uint_as_float(ww[j] & 0xffff0000u), scale) << (16 * j + 8);
+            hi |= quant_e4m3(__uint_as_float(ww[2 + j] << 16), scale) << (16 * j);
+            hi |= quant_e4m3(__uint_as_float(ww[2 + j] & 0xffff0000u), scale) << (16 * j + 8);
+        }
+        q[(mat * rows + r) * vec_cols + vc] = make_uint2(lo, hi);
+    }
+}
+
+hipError_t launch_quantize_weights(int64_t n_mats, int64_t rows, int64_t cols, const void* w,
+                                   uint8_t* q, float* s, hipStream_t st) {
+    const int64_t nblk = n_mats * (rows / 128) * (cols / 128);
+    if (nblk == 0) return hipSuccess;
+    quant_weight_kernel<<<dim3((unsigned)nblk), 256, 0, st>>>((const uint4*)w, (uint2*)q, s, rows,
+                                                              cols);
+    return hipGetLastError();
+}
+
+}  // namespace moe

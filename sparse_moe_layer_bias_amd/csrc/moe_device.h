@@ -1,0 +1,111 @@
+// moe_device.h -- device-side helpers shared by the libmoe kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------- bf16 bits
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (finite values; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// ---------------------------------------------------------------- E4M3FN
+//
+// OCP E4M3FN: sign, 4 exponent bits (bias 7), 3 mantissa bits; largest finite
+// 448; smallest normal 2^-6; subnormals m * 2^-9.  Encoding of a value already
+// clamped to [-448, 448], nearest-even, done on the fp32 bit pattern with
+// integer operations only (no dependence on conversion instructions).
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+    uint32_t u = __float_as_uint(v);
+    uint32_t sign = (u >> 24) & 0x80u;
+    uint32_t a = u & 0x7fffffffu;          // |v| bits
+    uint32_t exp = a >> 23;                 // biased fp32 exponent
+    uint32_t code;
+    if (exp < 121) {                        // |v| < 2^-6: subnormal grid 2^-9
+        // q = rne(|v| * 2^9).  Below 2^-10 (fp32 exponent field < 117) the
+        // product is under one half (or exactly one half, a tie to even 0).
+        if (exp < 117) {
+            code = 0;
+        } else {
+            uint32_t mant = (a & 0x7fffffu) | 0x800000u;   // 24-bit significand
+            // |v| * 2^9 = mant * 2^(exp - 127 - 23 + 9) = mant >> (141 - exp)
+            uint32_t sh = 141 - exp;                         // 21..24
+            uint32_t q = mant >> sh;
+            uint32_t rem = mant & ((1u << sh) - 1u);
+            uint32_t half = 1u << (sh - 1);
+            if (rem > half || (rem == half && (q & 1u))) q += 1;
+            code = q;                       // 0..8 (8 == smallest normal, code 0x08)
+        }
+    } else {
+        // normal: keep 3 mantissa bits, round the dropped 20 bits
+        uint32_t e = exp - 120;             // E4M3 biased exponent (exp-127+7), >= 1
+        uint32_t mant = a & 0x7fffffu;
+        uint32_t q = mant >> 20;
+        uint32_t rem = mant & 0xfffffu;
+        if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) q += 1;
+        code = (e << 3) + q;                // a mantissa carry bumps the exponent
+    }
+    return sign | code;
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+    uint32_t e = (c >> 3) & 0xfu, m = c & 7u;
+    float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+    return (c & 0x80u) ? -v : v;
+}
+
+// quantise one value with its tile scale: clamp(v/scale) to +-448, nearest-even
+__device__ __forceinline__ uint32_t quant_e4m3(float v, float scale) {
+    if (scale == 0.0f) return 0u;
+    float t = v / scale;                    // IEEE fp32 divide
+    t = fminf(fmaxf(t, -448.0f), 448.0f);
+    return e4m3_encode(t);
+}
+
+// ---------------------------------------------------------------- misc
+
+__host__ __device__ constexpr int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace moe
+
+namespace moe {
+
+// inclusive prefix sum over a 256-thread block; every thread must call it
+__device__ __forceinline__ int32_t block_incl_scan_256(int32_t v, int32_t* sh_wave4) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int32_t u = __shfl_up(v, o, 64);
+        if (lane >= o) v += u;
+    }
+    if (lane == 63) sh_wave4[w] = v;
+    __syncthreads();
+    int32_t add = 0;
+    for (int i = 0; i < w; ++i) add += sh_wave4[i];
+    __syncthreads();
+    return v + add;
+}
+
+}  // namespace moe

@@ -1,0 +1,52 @@
+// moe_internal.h -- launchers shared between the kernel files and the C ABI.
+#pragma once
+
+#include "moe_device.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- route
+hipError_t launch_route(const moe_cfg& c, const void* x, const float* centroids,
+                        const float* bias, float* scores, int32_t* idx, float* gate,
+                        int32_t* counts, hipStream_t st);
+
+// ---------------------------------------------------------------- permute
+// tokens per block of the stable rank; workspace layout in permute.hip
+constexpr int PERM_TB = 64;
+size_t permute_workspace_bytes(const moe_cfg& c);
+hipError_t launch_permute(const moe_cfg& c, const void* x, const int32_t* idx,
+                          int32_t* offsets, int32_t* src_token, int32_t* dst_row, void* x_perm,
+                          float* x_perm_scale, uint8_t* x_q, float* x_s, void* ws,
+                          hipStream_t st);
+
+// ---------------------------------------------------------------- expert FFN
+struct FfnArgs {
+    const void* x_perm;
+    const float* x_perm_scale;
+    const int32_t* offsets;
+    const void* w13;
+    const float* w13_scale;
+    const void* w2;
+    const float* w2_scale;
+    void* y_perm;
+    const void* x_sh;
+    const float* x_sh_scale;
+    const void* ws13;
+    const float* ws13_scale;
+    const void* ws2;
+    const float* ws2_scale;
+    void* y_shared;
+};
+size_t ffn_workspace_bytes(const moe_cfg& c);
+hipError_t launch_expert_ffn(const moe_cfg& c, const FfnArgs& a, void* ws, hipStream_t st);
+
+// ---------------------------------------------------------------- combine / bias / prep
+hipError_t launch_combine(const moe_cfg& c, const void* x, const void* y_shared,
+                          const void* y_perm, const float* gate, const int32_t* dst_row,
+                          void* out, hipStream_t st);
+hipError_t launch_bias_update(int64_t N, int64_t TK, const int32_t* counts, float gamma,
+                              float* bias, hipStream_t st);
+hipError_t launch_quantize_weights(int64_t n_mats, int64_t rows, int64_t cols, const void* w,
+                                   uint8_t* q, float* s, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,307 @@
+// route.hip -- affinity, biased (group-limited) top-k, gates and per-expert
+// load for the DeepSeekMoE router.
+//
+// DeepSeek-V3 report reading guide (xyznot.com/de), "Methode" item 2:
+// s_{i,t} = Sigmoid(u_t^T e_i); g'_{i,t} = s_{i,t} when s_{i,t} + b_i is in the
+// Topk of {s_{j,t} + b_j}, else 0; g = normalised g'.  The bias only decides
+// membership of the Topk.
+//
+// Two kernels:
+//  router_logits: z = x E^T as a fixed-order fp32 FMA chain per output (k
+//    ascending from +0), so that the chosen indices are reproducible bit for
+//    bit; the chain runs on the VALU (MFMA has no defined summation order).
+//    Epilogue: s = fp32(1 / (1 + exp(-(double)z))).
+//  router_select: one wavefront per token; keys s+b; optional group limit;
+//    k rounds of a wave-wide argmax under the total order (key desc, index
+//    asc); gates in double; per-expert load via integer atomics (order-free).
+#include "moe_internal.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------ logits
+
+// Tile: 128 tokens x 64 experts per 256-thread workgroup; each thread owns
+// 8 tokens x 4 experts (32 independent FMA chains).  BK = 16 hidden
+// elements per LDS stage, double buffered.
+constexpr int RL_TM = 128, RL_TN = 64, RL_BK = 16;
+
+template <typename XT>
+__device__ __forceinline__ void rl_load_x(const XT* __restrict__ x, int64_t T, int64_t d,
+                                          int64_t t0, int64_t k0, int tid, float (&xr)[8]) {
+    // thread -> token t0 + tid/2, hidden k0 + 8*(tid%2) .. +7
+    int64_t t = t0 + (tid >> 1);
+    if (t >= T) t = T - 1;  // clamp: a valid row, the result is never stored
+    int64_t kk = k0 + 8 * (tid & 1);
+    const XT* row = x + t * d;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        int64_t j = kk + i;
+        float v = 0.0f;
+        if (j < d) {
+            if constexpr (sizeof(XT) == 2)
+                v = bf16_to_f32(row[j]);
+            else
+                v = row[j];
+        }
+        xr[i] = v;
+    }
+}
+
+__device__ __forceinline__ void rl_load_e(const float* __restrict__ E, int64_t N, int64_t d,
+                                          int64_t n0, int64_t k0, int tid, float (&er)[4]) {
+    // thread -> expert n0 + tid/4, hidden k0 + 4*(tid%4) .. +3
+    int64_t n = n0 + (tid >> 2);
+    int64_t kk = k0 + 4 * (tid & 3);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int64_t j = kk + i;
+        er[i] = (n < N && j < d) ? E[n * d + j] : 0.0f;
+    }
+}
+
+template <typename XT>
+__global__ void __launch_bounds__(256) router_logits_kernel(const XT* __restrict__ x,
+                                                            const float* __restrict__ E,
+                                                            float* __restrict__ s_out,
+                                                            int64_t T, int64_t d, int64_t N) {
+    __shared__ float xs[2][RL_BK][RL_TM + 4];
+    __shared__ float es[2][RL_BK][RL_TN + 4];
+    const int tid = threadIdx.x;
+    const int64_t n0 = (int64_t)blockIdx.x * RL_TN;
+    const int64_t t0 = (int64_t)blockIdx.y * RL_TM;
+    const int ty = tid >> 4;  // 0..15 -> tokens ty*8 .. +7
+    const int tx = tid & 15;  // 0..15 -> experts tx*4 .. +3
+
+    float acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+
+    float xr[8], er[4];
+    const int64_t nk = cdiv(d, RL_BK);
+    rl_load_x(x, T, d, t0, 0, tid, xr);
+    rl_load_e(E, N, d, n0, 0, tid, er);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xs[0][8 * (tid & 1) + i][tid >> 1] = xr[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) es[0][4 * (tid & 3) + i][tid >> 2] = er[i];
+    __syncthreads();
+
+    for (int64_t kb = 0; kb < nk; ++kb) {
+        const int buf = kb & 1;
+        const bool more = kb + 1 < nk;
+        if (more) {
+            rl_load_x(x, T, d, t0, (kb + 1) * RL_BK, tid, xr);
+            rl_load_e(E, N, d, n0, (kb + 1) * RL_BK, tid, er);
+        }
+#pragma unroll
+        for (int k = 0; k < RL_BK; ++k) {
+            const float4 xa = *reinterpret_cast<const float4*>(&xs[buf][k][ty * 8]);
+            const float4 xb = *reinterpret_cast<const float4*>(&xs[buf][k][ty * 8 + 4]);
+            const float4 eb = *reinterpret_cast<const float4*>(&es[buf][k][tx * 4]);
+            const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+            const float ev[4] = {eb.x, eb.y, eb.z, eb.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(xv[i], ev[j], acc[i][j]);
+        }
+        if (more) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xs[buf ^ 1][8 * (tid & 1) + i][tid >> 1] = xr[i];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) es[buf ^ 1][4 * (tid & 3) + i][tid >> 2] = er[i];
+        }
+        __syncthreads();
+    }
+
+    // epilogue: affinity s = Sigmoid(z), evaluated in double, rounded once
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t t = t0 + ty * 8 + i;
+        if (t >= T) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t n = n0 + tx * 4 + j;
+            if (n < N) s_out[t * N + n] = (float)(1.0 / (1.0 + exp(-(double)acc[i][j])));
+        }
+    }
+}
+
+// ------------------------------------------------------------------ select
+
+// "a beats b": larger key, or equal key and lower index
+__device__ __forceinline__ bool beats(float ra, int ia, float rb, int ib) {
+    return ra > rb || (ra == rb && ia < ib);
+}
+
+template <typename T>
+__device__ __forceinline__ T shfl_xor(T v, int m) {
+    return __shfl_xor(v, m, 64);
+}
+
+// Each lane holds up to SEL_RK keys of one token: experts lane + 64*r
+// (SEL_RK = 16 covers N <= 1024).
+template <int SEL_RK>
+__global__ void __launch_bounds__(256) router_select_kernel(
+    const float* __restrict__ s, const float* __restrict__ bias, int32_t* __restrict__ idx_out,
+    float* __restrict__ gate_out, int32_t* __restrict__ counts, int64_t T, int N, int k, int G,
+    int TG) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const float* st = s + t * N;
+
+    float sv[SEL_RK], rv[SEL_RK];
+    bool ok[SEL_RK];
+#pragma unroll
+    for (int r = 0; r < SEL_RK; ++r) {
+        const int i = lane + 64 * r;
+        if (i < N) {
+            sv[r] = st[i];
+            float key = sv[r] + bias[i];
+            if (key == 0.0f) key = 0.0f;  // -0 -> +0
+            rv[r] = key;
+            ok[r] = true;
+        } else {
+            sv[r] = 0.0f;
+            rv[r] = -__builtin_inff();
+            ok[r] = false;
+        }
+    }
+
+    if (G > 1) {
+        // group g = experts [g*gs, (g+1)*gs); score = sum of its two best keys;
+        // lane g ends up holding group g's score
+        const int gs = N / G;
+        float my_gscore = -__builtin_inff();
+        for (int g = 0; g < G; ++g) {
+            float r1 = -__builtin_inff(), r2 = -__builtin_inff();
+            int i1 = 0x7fffffff, i2 = 0x7fffffff;
+#pragma unroll
+            for (int r = 0; r < SEL_RK; ++r) {
+                const int i = lane + 64 * r;
+                if (!ok[r] || i / gs != g) continue;
+                if (beats(rv[r], i, r1, i1)) {
+                    r2 = r1; i2 = i1; r1 = rv[r]; i1 = i;
+                } else if (beats(rv[r], i, r2, i2)) {
+                    r2 = rv[r]; i2 = i;
+                }
+            }
+#pragma unroll
+            for (int m = 1; m < 64; m <<= 1) {
+                const float p1 = shfl_xor(r1, m), p2 = shfl_xor(r2, m);
+                const int q1 = shfl_xor(i1, m), q2 = shfl_xor(i2, m);
+                // merge two sorted pairs, keep the best two
+                if (beats(p1, q1, r1, i1)) {
+                    // partner's first wins; second is the better of (r1, p2)
+                    if (beats(r1, i1, p2, q2)) { r2 = r1; i2 = i1; } else { r2 = p2; i2 = q2; }
+                    r1 = p1; i1 = q1;
+                } else {
+                    if (beats(p1, q1, r2, i2)) { r2 = p1; i2 = q1; }
+                }
+            }
+            float sc = r1 + r2;
+            if (sc == 0.0f) sc = 0.0f;
+            if (lane == g) my_gscore = sc;
+        }
+        // keep the TG best groups: TG rounds of argmax over lanes 0..G-1
+        bool kept = false;
+        bool cand = lane < G;
+        for (int p = 0; p < TG; ++p) {
+            float bv = cand ? my_gscore : -__builtin_inff();
+            int bi = cand ? lane : 0x7fffffff;
+#pragma unroll
+            for (int m = 1; m < 64; m <<= 1) {
+                const float ov = shfl_xor(bv, m);
+                const int oi = shfl_xor(bi, m);
+                if (beats(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+            }
+            if (lane == bi) { kept = true; cand = false; }
+        }
+        // experts outside the kept groups are not eligible
+#pragma unroll
+        for (int r = 0; r < SEL_RK; ++r) {
+            const int i = lane + 64 * r;
+            const int g = ok[r] ? i / gs : 0;
+            const bool gk = __shfl(kept, g, 64);
+            if (ok[r] && !gk) ok[r] = false;
+        }
+    }
+
+    // k rounds of wave argmax; lane j records the j-th winner
+    int my_idx = 0;
+    float my_s = 0.0f;
+    for (int j = 0; j < k; ++j) {
+        float bv = -__builtin_inff();
+        int bi = 0x7fffffff;
+        float bs = 0.0f;
+#pragma unroll
+        for (int r = 0; r < SEL_RK; ++r) {
+            const int i = lane + 64 * r;
+            if (ok[r] && beats(rv[r], i, bv, bi)) { bv = rv[r]; bi = i; bs = sv[r]; }
+        }
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) {
+            const float ov = shfl_xor(bv, m);
+            const int oi = shfl_xor(bi, m);
+            const float os = shfl_xor(bs, m);
+            if (beats(ov, oi, bv, bi)) { bv = ov; bi = oi; bs = os; }
+        }
+        // the owner lane drops the winner from its candidates
+#pragma unroll
+        for (int r = 0; r < SEL_RK; ++r)
+            if (lane + 64 * r == bi) ok[r] = false;
+        if (lane == j) { my_idx = bi; my_s = bs; }
+    }
+    // gates: g_j = s_j / sum_j' s_j', the sum in double in selection order
+    double S = 0.0;
+    for (int j = 0; j < k; ++j) S += (double)__shfl(my_s, j, 64);
+    if (lane < k) {
+        idx_out[t * k + lane] = my_idx;
+        gate_out[t * k + lane] = (float)((double)my_s / S);
+        atomicAdd(&counts[my_idx], 1);
+    }
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+// ------------------------------------------------------------------ launch
+
+hipError_t launch_route(const moe_cfg& c, const void* x, const float* centroids,
+                        const float* bias, float* scores, int32_t* idx, float* gate,
+                        int32_t* counts, hipStream_t st) {
+    const int64_t T = c.tokens, d = c.hidden, N = c.n_experts;
+    if (T == 0) {
+        fill_i32_kernel<<<dim3((unsigned)cdiv(N, 256)), 256, 0, st>>>(counts, N, 0);
+        return hipGetLastError();
+    }
+    dim3 g1((unsigned)cdiv(N, RL_TN), (unsigned)cdiv(T, RL_TM));
+    if (c.act_dtype == MOE_BF16)
+        router_logits_kernel<uint16_t><<<g1, 256, 0, st>>>((const uint16_t*)x, centroids, scores,
+                                                           T, d, N);
+    else
+        router_logits_kernel<float><<<g1, 256, 0, st>>>((const float*)x, centroids, scores, T, d,
+                                                        N);
+    fill_i32_kernel<<<dim3((unsigned)cdiv(N, 256)), 256, 0, st>>>(counts, N, 0);
+    const int G = c.n_group > 1 ? (int)c.n_group : 1;
+    const dim3 gs((unsigned)cdiv(T, 4));
+    const int K = (int)c.top_k, TG = (int)c.topk_group, NN = (int)N;
+    if (N <= 64)
+        router_select_kernel<1><<<gs, 256, 0, st>>>(scores, bias, idx, gate, counts, T, NN, K, G, TG);
+    else if (N <= 128)
+        router_select_kernel<2><<<gs, 256, 0, st>>>(scores, bias, idx, gate, counts, T, NN, K, G, TG);
+    else if (N <= 256)
+        router_select_kernel<4><<<gs, 256, 0, st>>>(scores, bias, idx, gate, counts, T, NN, K, G, TG);
+    else if (N <= 512)
+        router_select_kernel<8><<<gs, 256, 0, st>>>(scores, bias, idx, gate, counts, T, NN, K, G, TG);
+    else
+        router_select_kernel<16><<<gs, 256, 0, st>>>(scores, bias, idx, gate, counts, T, NN, K, G, TG);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,114 @@
+"""One DeepSeekMoE layer step through libmoe: buffers (torch device memory) and
+the five calls in order on one stream.
+
+    route -> permute -> expert_ffn (routed + shared) -> combine -> bias_update
+
+(DeepSeek-V3 report reading guide, xyznot.com/de, "Methode" item 2: the layer
+output h'_t, the biased Topk routing and the end-of-step bias rule.)
+"""
+import torch
+
+from . import (MoeCfg, cfg_from_dict, moe_bias_update, moe_combine, moe_expert_ffn,
+               moe_expert_ffn_workspace_size, moe_permute, moe_permute_workspace_size,
+               moe_quantize_weights_fp8, moe_route, moe_route_workspace_size)
+
+GAMMA = 0.001  # end-of-step bias step (reading guide, "Methode" item 2)
+
+
+def quantize_weights_fp8(w, stream=None):
+    """128x128 block E4M3 codes and scales of a bf16 weight stack [..., rows, cols]."""
+    rows, cols = w.shape[-2:]
+    n = w.numel() // (rows * cols)
+    q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    s = torch.empty(w.shape[:-2] + (rows // 128, cols // 128), dtype=torch.float32,
+                    device=w.device)
+    moe_quantize_weights_fp8(n, rows, cols, w, q, s, stream)
+    return q, s
+
+
+class MoeLayer:
+    """Holds the expert weights (and their FP8 form when the config asks for it)
+    and every per-step buffer for a batch of T tokens."""
+
+    def __init__(self, cfg, w13, w2, ws13=None, ws2=None, T=None, device="cuda"):
+        self.c = dict(cfg)
+        if T is not None:
+            self.c["T"] = T
+        c = self.c
+        self.cfg: MoeCfg = cfg_from_dict(c)
+        self.fp8 = bool(c.get("fp8", False))
+        T, d, N, k = c["T"], c["d"], c["N"], c["k"]
+        TK = T * k
+        act = torch.bfloat16 if c["dtype"] == "bf16" else torch.float32
+        dev = torch.device(device)
+        if self.fp8:
+            self.w13, self.w13_s = quantize_weights_fp8(w13)
+            self.w2, self.w2_s = quantize_weights_fp8(w2)
+            if ws13 is not None:
+                self.ws13, self.ws13_s = quantize_weights_fp8(ws13)
+                self.ws2, self.ws2_s = quantize_weights_fp8(ws2)
+            else:
+                self.ws13 = self.ws13_s = self.ws2 = self.ws2_s = None
+        else:
+            self.w13, self.w2, self.ws13, self.ws2 = w13, w2, ws13, ws2
+            self.w13_s = self.w2_s = self.ws13_s = self.ws2_s = None
+        has_shared = ws13 is not None and c["Is"] > 0
+        if not has_shared:
+            self.cfg.inter_shared = 0
+        i32 = dict(dtype=torch.int32, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.scores = torch.empty((T, N), **f32)
+        self.idx = torch.empty((T, k), **i32)
+        self.gate = torch.empty((T, k), **f32)
+        self.counts = torch.empty((N,), **i32)
+        self.offsets = torch.empty((N + 1,), **i32)
+        self.src_token = torch.empty((TK,), **i32)
+        self.dst_row = torch.empty((T, k), **i32)
+        if self.fp8:
+            self.x_perm = torch.empty((TK, d), dtype=torch.uint8, device=dev)
+            self.x_perm_s = torch.empty((TK, d // 128), **f32)
+            self.x_q = torch.empty((T, d), dtype=torch.uint8, device=dev)
+            self.x_s = torch.empty((T, d // 128), **f32)
+        else:
+            self.x_perm = torch.empty((TK, d), dtype=act, device=dev)
+            self.x_perm_s = self.x_q = self.x_s = None
+        self.y_perm = torch.empty((TK, d), dtype=act, device=dev)
+        self.y_shared = torch.empty((T, d), dtype=act, device=dev) if has_shared else None
+        self.out = torch.empty((T, d), dtype=act, device=dev)
+        ws = max(moe_route_workspace_size(self.cfg), moe_permute_workspace_size(self.cfg),
+                 moe_expert_ffn_workspace_size(self.cfg), 256)
+        self.workspace = torch.empty((ws,), dtype=torch.uint8, device=dev)
+
+    # the five calls -------------------------------------------------------
+    def route(self, x, centroids, bias, stream=None):
+        moe_route(self.cfg, x, centroids, bias, self.scores, self.idx, self.gate, self.counts,
+                  None, stream)
+
+    def permute(self, x, stream=None):
+        moe_permute(self.cfg, x, self.idx, self.offsets, self.src_token, self.dst_row,
+                    self.x_perm, self.x_perm_s, self.x_q, self.x_s, self.workspace, stream)
+
+    def expert_ffn(self, x, stream=None):
+        shared_in = self.x_q if self.fp8 else x
+        moe_expert_ffn(self.cfg, self.x_perm, self.x_perm_s, self.offsets, self.w13, self.w13_s,
+                       self.w2, self.w2_s, self.y_perm, shared_in if self.y_shared is not None
+                       else None, self.x_s if self.y_shared is not None else None, self.ws13,
+                       self.ws13_s, self.ws2, self.ws2_s, self.y_shared, self.workspace, stream)
+
+    def combine(self, x, residual=True, stream=None):
+        moe_combine(self.cfg, x if residual else None, self.y_shared, self.y_perm, self.gate,
+                    self.dst_row, self.out, stream)
+
+    def bias_update(self, bias, stream=None):
+        moe_bias_update(self.c["N"], self.c["T"] * self.c["k"], self.counts, GAMMA, bias, stream)
+
+    def forward(self, x, centroids, bias, residual=True, update_bias=True, stream=None):
+        """One step; returns ``self.out``.  ``bias`` is updated in place at the
+        end when ``update_bias`` (the routing of this step used the old value)."""
+        self.route(x, centroids, bias, stream)
+        self.permute(x, stream)
+        self.expert_ffn(x, stream)
+        self.combine(x, residual, stream)
+        if update_bias:
+            self.bias_update(bias, stream)
+        return self.out

@@ -1,0 +1,74 @@
+"""Helpers shared by the GPU parity tests: input preparation on both sides and
+the tolerance rule.
+
+Tolerance (floating outputs): |gpu - ref| <= rtol * (|ref| + rms(ref row)),
+elementwise, with rtol 1e-5 (fp32), 2e-2 (bf16), 6e-2 (FP8 GEMMs).
+Integer, index and byte outputs are compared bit for bit.
+"""
+import sys
+
+import numpy as np
+import torch
+
+import moe_inputs
+from moe_inputs import to_host
+
+RTOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_f64(a):
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def assert_close(got, ref, rtol, what=""):
+    g, r = to_f64(got), to_f64(ref)
+    assert g.shape == r.shape, (what, g.shape, r.shape)
+    if r.size == 0:
+        return
+    r2 = r.reshape(-1, r.shape[-1]) if r.ndim > 1 else r.reshape(1, -1)
+    g2 = g.reshape(r2.shape)
+    rms = np.sqrt(np.mean(r2 ** 2, axis=1, keepdims=True))
+    bound = rtol * (np.abs(r2) + rms)
+    err = np.abs(g2 - r2)
+    bad = ~(err <= bound)
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError("%s: %d/%d elements out of tolerance %g; first at %s: gpu=%r ref=%r"
+                             " (max rel err %.3g)" % (what, bad.sum(), bad.size, rtol, tuple(i),
+                                                      g2[tuple(i)], r2[tuple(i)],
+                                                      float(np.max(err / (np.abs(r2) + rms)))))
+
+
+def assert_bits(got, ref, what=""):
+    g, r = np.asarray(got), np.asarray(ref)
+    assert g.shape == r.shape, (what, g.shape, r.shape)
+    if g.dtype != r.dtype:
+        g = g.view(r.dtype) if g.itemsize == r.itemsize else g.astype(r.dtype)
+    neq = g != r
+    if neq.any():
+        i = np.argwhere(neq)[0]
+        raise AssertionError("%s: %d/%d mismatches; first at %s: gpu=%r ref=%r" %
+                             (what, neq.sum(), neq.size, tuple(i), g[tuple(i)], r[tuple(i)]))
+
+
+def host_inputs(inp):
+    """torch dict -> numpy dict in the oracle's conventions"""
+    return {k: (to_host(v) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+
+
+def small_layer_inputs(cfg, seed=0, T=None):
+    """generate on the host (so CPU and GPU tests see the same bytes), copy to GPU"""
+    c = dict(cfg)
+    if T is not None:
+        c["T"] = T
+    inp = moe_inputs.make_layer_inputs(c, seed, "cpu")
+    dev = {k: v.cuda() for k, v in inp.items()}
+    return c, inp, dev
