@@ -4,7 +4,7 @@
 namespace moe {
 
 hipError_t launch_expert_ffn_fp8(const moe_cfg&, const FfnArgs&, const int2*, const int32_t*,
-                                 void*, void*, float*, float*, int64_t, hipStream_t) {
+                                 void*, void*, float*, float*, int64_t, int64_t, hipStream_t) {
     return hipErrorNotSupported;
 }
 
