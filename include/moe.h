@@ -136,15 +136,16 @@ size_t moe_expert_ffn_workspace_size(const moe_cfg* cfg);
  *  x_perm      [T*k, d]   routed rows (act_dtype, or E4M3 codes for FP8)
  *  x_perm_scale[T*k, d/128] FP8 tile scales (FP8 only, else NULL)
  *  offsets     [N+1]      from moe_permute (device)
- *  w13         [N, 2I, d] per expert: rows 0..I-1 = W1 (gate), I..2I-1 = W3 (up)
+ *  w13         routed gate/up weights, PACKED by moe_pack_weights(which = 0) from
+ *              [N, 2I, d] (per expert rows 0..I-1 = W1 (gate), I..2I-1 = W3 (up))
  *  w13_scale   [N, 2I/128, d/128]  FP8 block scales (FP8 only)
- *  w2          [N, d, I]  down projection
+ *  w2          routed down weights, PACKED (which = 1) from [N, d, I]
  *  w2_scale    [N, d/128, I/128]   FP8 block scales (FP8 only)
  *  y_perm      [T*k, d]   act_dtype out, expert output per row (unweighted)
  *  x_sh        [T, d]     shared-expert input: x (act_dtype) or x_q (FP8); NULL if Is == 0
  *  x_sh_scale  [T, d/128] FP8 only
- *  ws13        [2Is, d], ws13_scale [2Is/128, d/128] (FP8)
- *  ws2         [d, Is],  ws2_scale  [d/128, Is/128] (FP8)
+ *  ws13        shared gate/up, PACKED (which = 2) from [2Is, d]; ws13_scale (FP8)
+ *  ws2         shared down, PACKED (which = 3) from [d, Is]; ws2_scale (FP8)
  *  y_shared    [T, d]     act_dtype out (NULL if Is == 0)
  * Accumulation is fp32.  bf16: h = silu(a)*b is rounded to bf16 between the
  * two GEMMs.  FP8 ("Kernideen": promotion every N_c = 128): each 128-wide
@@ -157,6 +158,19 @@ int moe_expert_ffn(const moe_cfg* cfg, const void* x_perm, const float* x_perm_s
                    const float* x_sh_scale, const void* ws13, const float* ws13_scale,
                    const void* ws2, const float* ws2_scale, void* y_shared, void* workspace,
                    size_t workspace_bytes, void* stream);
+
+/* Weight preparation, off the per-step path (weights are constant across
+ * steps).  Rearranges one weight stack into the order the expert GEMM streams
+ * it: tiles of 256 output rows, 32-wide contraction blocks, 16-byte chunks in
+ * the kernel's shared-memory order, so each pipeline stage reads one
+ * contiguous block.  Gate/up tiles interleave 32 W1 rows with the matching 32
+ * W3 rows.  fp32 layers keep the plain layout (a copy).
+ *  which: 0 = routed W13 [N, 2I, d], 1 = routed W2 [N, d, I],
+ *         2 = shared W13 [2Is, d],   3 = shared W2 [d, Is]
+ *  w: act_dtype, row-major; w_packed: moe_packed_weights_size(cfg, which) bytes.
+ * FP8 weights are not packed by this call. */
+size_t moe_packed_weights_size(const moe_cfg* cfg, int which);
+int moe_pack_weights(const moe_cfg* cfg, int which, const void* w, void* w_packed, void* stream);
 
 /* ---------------------------------------------------------------- combine */
 

@@ -67,6 +67,8 @@ def lib():
             "moe_expert_ffn_workspace_size": ([C], SZ),
             "moe_expert_ffn": ([C] + [P] * 15 + [P, SZ, P], ctypes.c_int),
             "moe_combine": ([C, P, P, P, P, P, P, P], ctypes.c_int),
+            "moe_packed_weights_size": ([C, ctypes.c_int], SZ),
+            "moe_pack_weights": ([C, ctypes.c_int, P, P, P], ctypes.c_int),
             "moe_bias_update": ([I64, I64, P, F, P, P], ctypes.c_int),
             "moe_quantize_weights_fp8": ([I64, I64, I64, P, P, P, P], ctypes.c_int),
             "moe_last_error": ([], ctypes.c_char_p),
@@ -140,6 +142,15 @@ def moe_expert_ffn(cfg, x_perm, x_perm_scale, offsets, w13, w13_scale, w2, w2_sc
                                 _p(x_sh), _p(x_sh_scale), _p(ws13), _p(ws13_scale), _p(ws2),
                                 _p(ws2_scale), _p(y_shared), _p(workspace), _nbytes(workspace),
                                 _stream(stream)))
+
+
+def moe_packed_weights_size(cfg, which):
+    return lib().moe_packed_weights_size(ctypes.byref(cfg), int(which))
+
+
+def moe_pack_weights(cfg, which, w, w_packed, stream=None):
+    _check(lib().moe_pack_weights(ctypes.byref(cfg), int(which), _p(w), _p(w_packed),
+                                  _stream(stream)))
 
 
 def moe_combine(cfg, x_residual, y_shared, y_perm, gate, dst_row, out, stream=None):

@@ -99,7 +99,7 @@ int hip_status(const char* fn, hipError_t e) {
 
 extern "C" {
 
-int moe_abi_version(void) { return 1; }
+int moe_abi_version(void) { return 2; }
 
 const char* moe_last_error(void) { return g_err; }
 
@@ -213,6 +213,27 @@ int moe_expert_ffn(const moe_cfg* cfg, const void* x_perm, const float* x_perm_s
     moe::FfnArgs a{x_perm, x_perm_scale, offsets, w13, w13_scale, w2, w2_scale, y_perm,
                    x_sh,   x_sh_scale,   ws13,    ws13_scale, ws2, ws2_scale, y_shared};
     return hip_status(fn, moe::launch_expert_ffn(*cfg, a, workspace, (hipStream_t)stream));
+}
+
+size_t moe_packed_weights_size(const moe_cfg* cfg, int which) {
+    if (!cfg || which < 0 || which > 3) return 0;
+    return moe::packed_weight_bytes(*cfg, which);
+}
+
+int moe_pack_weights(const moe_cfg* cfg, int which, const void* w, void* w_packed,
+                     void* stream) {
+    const char* fn = "moe_pack_weights";
+    if (int r = check_cfg(fn, cfg)) return r;
+    if (int r = check_ffn_shape(fn, cfg)) return r;
+    if (which < 0 || which > 3) return fail(MOE_ERR_ARG, "%s: which must be 0..3", fn);
+    if (which >= 2 && cfg->inter_shared == 0)
+        return fail(MOE_ERR_ARG, "%s: no shared expert (inter_shared == 0)", fn);
+    if (cfg->gemm_dtype == MOE_FP8_E4M3)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: FP8 weights are packed by moe_quantize_weights_fp8", fn);
+    REQ_PTR(w);
+    REQ_PTR(w_packed);
+    if (w == w_packed) return fail(MOE_ERR_ARG, "%s: packing cannot run in place", fn);
+    return hip_status(fn, moe::launch_pack_weights(*cfg, which, w, w_packed, (hipStream_t)stream));
 }
 
 int moe_combine(const moe_cfg* cfg, const void* x_residual, const void* y_shared,

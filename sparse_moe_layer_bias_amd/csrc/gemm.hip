@@ -19,8 +19,9 @@ namespace moe {
 
 static int64_t align256(int64_t b) { return (b + 255) & ~int64_t(255); }
 
-constexpr int BF_BM = 320;   // token rows per tile, bf16 / FP8 MFMA kernels
-constexpr int F32_BM = 64;   // fp32 path
+constexpr int BF_BM = 320;      // token rows per tile, bf16 / FP8 MFMA kernels
+constexpr int G_WR_PACK = 256;  // rows per packed weight tile (bf16)
+constexpr int F32_BM = 64;      // token rows per tile, fp32 path
 
 // ---------------------------------------------------------------- tile map
 
@@ -56,32 +57,7 @@ __global__ void __launch_bounds__(256) ffn_tile_map_kernel(const int32_t* __rest
     }
 }
 
-// ---------------------------------------------------------------- bf16 MFMA
-//
-// Workgroup = 8 wavefronts; tile = 256 weight rows x up to 320 token rows,
-// i.e. one weight panel against ALL rows of an expert (routed experts get
-// ~T*k/N rows), so every weight byte streams from HBM exactly once and the
-// MFMA work follows the expert's real row count in steps of 32.
-// MFMA v_mfma_f32_32x32x16_bf16 with the weight rows as the A operand:
-// D[w][t] = sum_k W[w][k] X[t][k].  Wave (wg = wave%4, tg = wave/4) owns weight
-// rows wg*64..+63 (two 32-row blocks) and token rows tg*160..+159 (five blocks).
-// K step 64; the next step's operands are copied global -> LDS directly
-// (global_load_lds_dwordx4) while the current step is multiplied; two LDS
-// stages (2 x 72 KB).  LDS rows are 128 B (8 chunks of 16 B); chunk c of row r
-// sits at slot c ^ (r & 7), so the 32 lanes reading one chunk of 32
-// consecutive rows hit distinct banks.
-// gate/up: the 64 weight rows of a wave are W1 rows n..n+31 (block 0) and W3
-// rows n..n+31 (block 1): a and b of one (token, column) share a register slot
-// and SwiGLU is applied in registers.
-
-constexpr int G_WR = 256;      // weight rows per tile
-constexpr int G_TR = 320;      // token rows per tile
-constexpr int G_BK = 64;       // contraction step
-constexpr int G_THREADS = 512;
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ lds_void* to_lds(void* p) { return (lds_void*)p; }
+// ---------------------------------------------------------------- work units
 
 struct GemmParamsV2 {
     const int2* tiles;     // routed tiles [0, n_r), shared tiles [n_r, n_r + n_s)
@@ -139,7 +115,10 @@ __device__ __forceinline__ bool decode_v2(const GemmParamsV2& p, int mode, WorkV
         w.K = p.K_r;
         w.Nout = p.Nout_r;
         w.X = (const char*)p.A_r + rowbase * w.K * ESZ;
-        const int64_t wrows = mode == 0 ? 2 * w.Nout : w.Nout;
+        // weights of one expert: ntn_r packed tiles of G_WR_PACK rows (bf16)
+        // or the plain [rows][K] matrix (fp32)
+        const int64_t wrows = ESZ == 2 ? (int64_t)p.ntn_r * G_WR_PACK
+                                       : (mode == 0 ? 2 * w.Nout : w.Nout);
         w.W = (const char*)p.B_r + (int64_t)g * wrows * w.K * ESZ;
         w.C = (char*)p.C_r + rowbase * w.Nout * ESZ;
     } else {
@@ -155,145 +134,285 @@ __device__ __forceinline__ bool decode_v2(const GemmParamsV2& p, int mode, WorkV
 
 __device__ __forceinline__ float silu_f(float a) { return a / (1.0f + __expf(-a)); }
 
+// ---------------------------------------------------------------- bf16 MFMA
+//
+// Workgroup = 8 wavefronts; tile = 256 weight rows x up to 320 token rows,
+// i.e. one weight panel against ALL rows of an expert (routed experts get
+// ~T*k/N rows), so every weight byte streams from HBM exactly once and the
+// MFMA work follows the expert's real row count in steps of 32.
+// MFMA v_mfma_f32_32x32x16_bf16 with the weight rows as the A operand:
+// D[w][t] = sum_k W[w][k] X[t][k].  Wave (wg = wave%4, tg = wave/4) owns weight
+// rows wg*64..+63 (two 32-row blocks) and token rows tg*160..+159 (five blocks);
+// only the blocks that hold real token rows are multiplied (the main loop is
+// specialised on that count, so it is straight-line code).
+// LDS holds NS stages of BK contraction elements; a stage is a sequence of
+// 32-wide sub-tiles, each [rows][4 chunks of 16 B] with chunk c of row r at
+// slot c ^ ((r >> 2) & 3), so that the 16 lanes served together by a
+// ds_read_b128 hit distinct banks.  Stages are filled by
+// global_load_lds_dwordx4 copies issued NS-1 stages ahead.  The weights are
+// pre-packed (pack_weights_kernel) in exactly this LDS image order, so a
+// stage's weight copy is one contiguous 256*BK*2-byte read.
+// gate/up: the 64 weight rows of a wave are W1 rows n..n+31 (block 0) and W3
+// rows n..n+31 (block 1): a and b of one (token, column) share a register slot
+// and SwiGLU is applied in registers.
+
+constexpr int G_WR = 256;      // weight rows per tile
+constexpr int G_TR = 320;      // token rows per tile
+// wavefronts per workgroup: 8 (4 weight-row groups of 64 x 2 token halves) or
+// 4 (2 weight-row groups of 128 x 2 token halves)
+#ifndef MOE_GEMM_WAVES
+#define MOE_GEMM_WAVES 8
+#endif
+constexpr int G_WAVES = MOE_GEMM_WAVES;
+constexpr int G_THREADS = 64 * G_WAVES;
+constexpr int G_WRG = G_WAVES / 2;        // weight-row groups
+constexpr int G_WRB = 256 / 32 / G_WRG;   // 32-row weight blocks per wave
+constexpr int G_SUB = 32;      // contraction elements per LDS sub-tile (64-byte rows)
+// contraction step and number of LDS stages in the copy pipeline
+#ifndef MOE_GEMM_BK
+#define MOE_GEMM_BK 64
+#endif
+#ifndef MOE_GEMM_NS
+#define MOE_GEMM_NS 2
+#endif
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ lds_void* to_lds(const void* p) { return (lds_void*)p; }
+
+// physical chunk of logical chunk c in row r of a 64-byte-row sub-tile (an
+// involution).  A ds_read_b128 is served 16 lanes (256 bytes, the 64 banks)
+// at a time; those lanes read one chunk of 16 consecutive rows, i.e. 4 rows
+// for each of the 4 row positions within a 256-byte bank line, and the XOR
+// with (r >> 2) & 3 gives those 4 rows 4 distinct chunk slots.
+__device__ __forceinline__ int sub_chunk(int r, int c) { return c ^ ((r >> 2) & 3); }
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// s_waitcnt vmcnt(n) for a wave-uniform n in 0..23 (the counter field takes
+// an immediate, hence the switch)
+__device__ __forceinline__ void vm_wait_n(int n) {
+    switch (n) {
+#define MOE_VMW(i) \
+    case i: vm_wait<i>(); break;
+        MOE_VMW(0) MOE_VMW(1) MOE_VMW(2) MOE_VMW(3) MOE_VMW(4) MOE_VMW(5) MOE_VMW(6) MOE_VMW(7)
+        MOE_VMW(8) MOE_VMW(9) MOE_VMW(10) MOE_VMW(11) MOE_VMW(12) MOE_VMW(13) MOE_VMW(14)
+        MOE_VMW(15) MOE_VMW(16) MOE_VMW(17) MOE_VMW(18) MOE_VMW(19) MOE_VMW(20) MOE_VMW(21)
+        MOE_VMW(22) MOE_VMW(23)
+#undef MOE_VMW
+        default: vm_wait<0>(); break;
+    }
+}
+
+// weight row (of the [2*Nout or Nout][K] expert matrix) held in packed row r of
+// weight tile wt; -1 for padding rows past the end (down projection only)
 template <int MODE>
-__global__ void __launch_bounds__(G_THREADS, 1) ffn_gemm_bf16_kernel(GemmParamsV2 p) {
-    WorkV2 w;
-    if (!decode_v2<2>(p, MODE, w)) return;
-    const uint16_t* Wp = (const uint16_t*)w.W;
-    const uint16_t* Xp = (const uint16_t*)w.X;
+__device__ __forceinline__ int64_t packed_row_source(int64_t wt, int r, int64_t Nout) {
+    if (MODE == 0) {
+        const int g4 = r >> 6, half = (r >> 5) & 1, j = r & 31;
+        return (half ? Nout : 0) + wt * 128 + g4 * 32 + j;
+    }
+    const int64_t wr = wt * 256 + r;
+    return wr < Nout ? wr : -1;
+}
 
-    __shared__ __attribute__((aligned(1024))) uint16_t Aw0[G_WR * G_BK];
-    __shared__ __attribute__((aligned(1024))) uint16_t Xt0[G_TR * G_BK];
-    __shared__ __attribute__((aligned(1024))) uint16_t Aw1[G_WR * G_BK];
-    __shared__ __attribute__((aligned(1024))) uint16_t Xt1[G_TR * G_BK];
+// Pack a stack of n_mats expert matrices into the GEMM's LDS image order:
+// out[mat][wt][kc][slot] (16-byte chunks), kc = 32-wide contraction block,
+// slot = r*4 + pc holding logical chunk sub_chunk(r, pc) of packed row r.
+template <int MODE>
+__global__ void __launch_bounds__(256) pack_weights_kernel(const uint4* __restrict__ w,
+                                                           uint4* __restrict__ out,
+                                                           int64_t n_mats, int64_t Nout,
+                                                           int64_t K, int64_t ntn) {
+    const int64_t nkc = K / G_SUB;
+    const int64_t per_mat = ntn * nkc * G_WR * 4;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n_mats * per_mat) return;
+    const int64_t mat = i / per_mat;
+    int64_t rem = i % per_mat;
+    const int64_t wt = rem / (nkc * G_WR * 4);
+    rem %= nkc * G_WR * 4;
+    const int64_t kc = rem / (G_WR * 4);
+    const int slot = (int)(rem % (G_WR * 4));
+    const int r = slot >> 2, c = sub_chunk(r, slot & 3);
+    const int64_t src = packed_row_source<MODE>(wt, r, Nout);
+    const int64_t rows = MODE == 0 ? 2 * Nout : Nout;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (src >= 0) v = w[((mat * rows + src) * K + kc * G_SUB + c * 8) / 8];
+    out[i] = v;
+}
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wg = wave & 3, tg = wave >> 2;
+template <int MODE, int BK, int NS, int NB>
+__device__ __forceinline__ void gemm_bf16_body(const WorkV2& w, uint16_t* smem) {
+    constexpr int NSUB = BK / G_SUB;
+    constexpr int A_EL = G_WR * BK, X_EL = G_TR * BK;
+    constexpr int NA = A_EL * 2 / 1024;         // 1 KB copies per stage (weights)
+    constexpr int NX = X_EL * 2 / 1024;         // 1 KB copies per stage (tokens, at most)
+    constexpr int PA = NA / G_WAVES, PX = (NX + G_WAVES - 1) / G_WAVES;
+    constexpr int NBB = NB > 0 ? NB : 1;
+    static_assert(NA % G_WAVES == 0, "weight copies split evenly over the waves");
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wr = wave % G_WRG, tg = wave / G_WRG;  // weight-row group, token half
     const int64_t K = w.K;
-    const int64_t mc = w.M - w.m0 < G_TR ? w.M - w.m0 : G_TR;  // token rows in this tile, >= 1
+    const int64_t mc = w.M - w.m0 < G_TR ? w.M - w.m0 : G_TR;
+    const int nk = (int)(K / BK);
+    // uniform bases + 32-bit per-lane byte offsets (scalar-base addressing)
+    const char* wstage0 = w.W + (w.wt * (int64_t)nk * A_EL) * 2;
+    const uint32_t woff = lane * 16;
+    const char* xbase = w.X + w.m0 * K * 2;  // the tile's first token row
 
-    // weight rows of this tile that exist (MODE 1 may end inside a tile)
-    const int64_t wbase = MODE == 0 ? w.wt * 128 : w.wt * 256;
-    // per-lane global sources for the 4 weight-chunk and 5 token-chunk copies
-    const uint16_t* wsrc[4];
-    const uint16_t* xsrc[5];
+    // Token copies: block b = 16 rows (rb = b / NSUB) of sub-tile q = b % NSUB,
+    // so the blocks holding real rows are the prefix b < nxe.  Rows past the
+    // tile's last real row are never copied (their LDS is never stored from).
+    const int nxe = NSUB * (int)((mc + 15) / 16);
+    int cnt = PA;  // copies this wave issues per stage
+    uint32_t xoff[PX];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int slot = (wave * 4 + i) * 64 + lane;
-        const int r = slot >> 3, c = (slot & 7) ^ (r & 7);
-        int64_t wr;
-        if (MODE == 0) {
-            const int g4 = r >> 6, half = (r >> 5) & 1, j = r & 31;
-            wr = (half ? w.Nout : 0) + wbase + g4 * 32 + j;
-        } else {
-            wr = wbase + r;
-            if (wr >= w.Nout) wr = w.Nout - 1;  // clamp; never stored
+    for (int j = 0; j < PX; ++j) {
+        const int b = wave + G_WAVES * j;
+        if (b < nxe) ++cnt;
+        const int q = b % NSUB, rb = b / NSUB;
+        const int r = rb * 16 + (lane >> 2), c = sub_chunk(r, lane & 3);
+        const int64_t tr = r < mc ? r : mc - 1;  // clamp inside a partial block
+        xoff[j] = (uint32_t)((tr * K + q * G_SUB + c * 8) * 2);
+    }
+
+    auto stage_a = [&](int s) { return smem + s * (A_EL + X_EL); };
+    auto stage_x = [&](int s) { return smem + s * (A_EL + X_EL) + A_EL; };
+    auto issue = [&](int kt, int s) {
+        uint16_t* As = stage_a(s);
+        uint16_t* Xs = stage_x(s);
+        const char* wsrc = wstage0 + (int64_t)kt * A_EL * 2;
+        const char* xsrc = xbase + (int64_t)kt * BK * 2;
+#pragma unroll
+        for (int j = 0; j < PA; ++j) {
+            const int b = wave + G_WAVES * j;
+            __builtin_amdgcn_global_load_lds((const void*)(wsrc + b * 1024 + woff),
+                                             to_lds(As + b * 512), 16, 0, 0);
         }
-        wsrc[i] = Wp + wr * K + c * 8;
-    }
 #pragma unroll
-    for (int i = 0; i < 5; ++i) {
-        const int slot = (wave * 5 + i) * 64 + lane;
-        const int r = slot >> 3, c = (slot & 7) ^ (r & 7);
-        int64_t tr = w.m0 + (r < mc ? r : mc - 1);  // clamp; never stored
-        xsrc[i] = Xp + tr * K + c * 8;
-    }
-
-    auto issue = [&](int64_t k0, uint16_t* Aw, uint16_t* Xt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_global_load_lds((const void*)(wsrc[i] + k0),
-                                             to_lds(Aw + (wave * 4 + i) * 512), 16, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 5; ++i)
-            __builtin_amdgcn_global_load_lds((const void*)(xsrc[i] + k0),
-                                             to_lds(Xt + (wave * 5 + i) * 512), 16, 0, 0);
+        for (int j = 0; j < PX; ++j) {
+            const int b = wave + G_WAVES * j;
+            if (b < nxe)
+                __builtin_amdgcn_global_load_lds(
+                    (const void*)(xsrc + xoff[j]),
+                    to_lds(Xs + (b % NSUB) * G_TR * G_SUB + (b / NSUB) * 512), 16, 0, 0);
+        }
     };
 
-    f32x16_t acc[2][5];
+    f32x16_t acc[G_WRB][NBB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < G_WRB; ++i)
 #pragma unroll
-        for (int j = 0; j < 5; ++j)
+        for (int j = 0; j < NBB; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    // which 32-row blocks of this wave carry real rows (wave-uniform)
-    bool t_on[5];
 #pragma unroll
-    for (int j = 0; j < 5; ++j) t_on[j] = tg * 160 + j * 32 < mc;
-    const bool w_on = MODE == 0 ? true : (wbase + wg * 64 < w.Nout);
-
-    const int nk = (int)(K / G_BK);
-    issue(0, Aw0, Xt0);
+    for (int s = 0; s < NS - 1; ++s)
+        if (s < nk) issue(s, s);
     for (int kt = 0; kt < nk; ++kt) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();  // stage kt is in LDS; everyone is done with stage kt-1
-        uint16_t* Aw = (kt & 1) ? Aw1 : Aw0;
-        uint16_t* Xt = (kt & 1) ? Xt1 : Xt0;
-        if (kt + 1 < nk) {
-            if (kt & 1)
-                issue((int64_t)(kt + 1) * G_BK, Aw0, Xt0);
-            else
-                issue((int64_t)(kt + 1) * G_BK, Aw1, Xt1);
-        }
-        if (w_on) {
+        // copies of later stages already issued by this wave may stay in flight
+        const int after = nk - 1 - kt < NS - 2 ? nk - 1 - kt : NS - 2;
+        vm_wait_n(after * cnt);
+        __syncthreads();  // stage kt landed for every wave; stage kt-1 is free
+        if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
+        if constexpr (NB > 0) {
+            const uint16_t* As = stage_a(kt % NS);
+            const uint16_t* Xs = stage_x(kt % NS);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int ch = 2 * s + (lane >> 5);
-                bf16x8_t af[2];
+            for (int s = 0; s < BK / 16; ++s) {
+                const int q = s >> 1, c = 2 * (s & 1) + (lane >> 5);
+                bf16x8_t af[G_WRB], xf[NB];
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int r = wg * 64 + i * 32 + (lane & 31);
+                for (int i = 0; i < G_WRB; ++i) {
+                    const int r = (wr * G_WRB + i) * 32 + (lane & 31);
                     af[i] = __builtin_bit_cast(
-                        bf16x8_t, *(const uint4*)(Aw + r * 64 + ((ch ^ (r & 7)) << 3)));
+                        bf16x8_t,
+                        *(const uint4*)(As + q * G_WR * G_SUB + r * G_SUB + sub_chunk(r, c) * 8));
                 }
 #pragma unroll
-                for (int j = 0; j < 5; ++j) {
-                    if (!t_on[j]) continue;
+                for (int j = 0; j < NB; ++j) {
                     const int r = tg * 160 + j * 32 + (lane & 31);
-                    const bf16x8_t xf = __builtin_bit_cast(
-                        bf16x8_t, *(const uint4*)(Xt + r * 64 + ((ch ^ (r & 7)) << 3)));
-#pragma unroll
-                    for (int i = 0; i < 2; ++i)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], xf, acc[i][j],
-                                                                             0, 0, 0);
+                    xf[j] = __builtin_bit_cast(
+                        bf16x8_t,
+                        *(const uint4*)(Xs + q * G_TR * G_SUB + r * G_SUB + sub_chunk(r, c) * 8));
                 }
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+#pragma unroll
+                    for (int i = 0; i < G_WRB; ++i)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], xf[j], acc[i][j],
+                                                                             0, 0, 0);
             }
         }
     }
 
     // epilogue.  32x32 accumulator layout: lane l holds column (token) l%32 and
-    // rows (weight rows) 8*(v/4) + 4*(l/32) + v%4, v = 0..15.
-    if (!w_on) return;
+    // rows (weight rows) 8*(v/4) + 4*(l/32) + v%4, v = 0..15.  gate/up: weight
+    // blocks (0, 1) and (2, 3) are the W1 and W3 rows of the same 32 columns.
+    if constexpr (NB > 0) {
+        const int64_t wbase = MODE == 0 ? w.wt * 128 : w.wt * 256;
 #pragma unroll
-    for (int j = 0; j < 5; ++j) {
-        if (!t_on[j]) continue;
-        const int64_t t = w.m0 + tg * 160 + j * 32 + (lane & 31);
-        if (t >= w.M) continue;
-        uint16_t* crow = (uint16_t*)w.C + t * w.Nout;
+        for (int j = 0; j < NB; ++j) {
+            const int64_t t = w.m0 + tg * 160 + j * 32 + (lane & 31);
+            if (t >= w.M) continue;
+            uint16_t* crow = (uint16_t*)w.C + t * w.Nout;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int rr = 8 * g + 4 * (lane >> 5);
-            if (MODE == 0) {
-                const int64_t n = wbase + wg * 32 + rr;
-                float h[4];
+            for (int g = 0; g < 4; ++g) {
+                const int rr = 8 * g + 4 * (lane >> 5);
+                if (MODE == 0) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    h[q] = silu_f(acc[0][j][4 * g + q]) * acc[1][j][4 * g + q];
-                *(uint2*)(crow + n) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
-            } else {
+                    for (int pr = 0; pr < G_WRB / 2; ++pr) {
+                        const int64_t n = wbase + (wr * G_WRB / 2 + pr) * 32 + rr;
+                        float h[4];
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int64_t n = wbase + wg * 64 + i * 32 + rr;
-                    *(uint2*)(crow + n) =
-                        make_uint2(pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]),
-                                   pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]));
+                        for (int qq = 0; qq < 4; ++qq)
+                            h[qq] = silu_f(acc[2 * pr][j][4 * g + qq]) * acc[2 * pr + 1][j][4 * g + qq];
+                        *(uint2*)(crow + n) =
+                            make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < G_WRB; ++i) {
+                        const int64_t n = wbase + (wr * G_WRB + i) * 32 + rr;
+                        if (n >= w.Nout) continue;
+                        *(uint2*)(crow + n) =
+                            make_uint2(pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]),
+                                       pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]));
+                    }
                 }
             }
         }
+    }
+}
+
+template <int MODE, int BK, int NS>
+__global__ void __launch_bounds__(G_THREADS, 1) ffn_gemm_bf16_kernel(GemmParamsV2 p) {
+    WorkV2 w;
+    if (!decode_v2<2>(p, MODE, w)) return;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * (G_WR + G_TR) * BK];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wr = wave % G_WRG, tg = wave / G_WRG;
+    const int64_t mc = w.M - w.m0 < G_TR ? w.M - w.m0 : G_TR;
+    // token blocks of this wave that hold real rows; none if all its weight rows
+    // are past the end of the matrix (last tile of the down projection)
+    int64_t nb = (mc - tg * 160 + 31) / 32;
+    nb = nb < 0 ? 0 : (nb > 5 ? 5 : nb);
+    const int64_t wbase = MODE == 0 ? w.wt * 128 : w.wt * 256;
+    if (MODE == 1 && wbase + wr * G_WRB * 32 >= w.Nout) nb = 0;
+    switch (nb) {
+        case 5: gemm_bf16_body<MODE, BK, NS, 5>(w, smem); break;
+        case 4: gemm_bf16_body<MODE, BK, NS, 4>(w, smem); break;
+        case 3: gemm_bf16_body<MODE, BK, NS, 3>(w, smem); break;
+        case 2: gemm_bf16_body<MODE, BK, NS, 2>(w, smem); break;
+        case 1: gemm_bf16_body<MODE, BK, NS, 1>(w, smem); break;
+        default: gemm_bf16_body<MODE, BK, NS, 0>(w, smem); break;
     }
 }
 
@@ -385,6 +504,47 @@ static FfnWs carve_ffn(const moe_cfg& c, void* ws) {
     return w;
 }
 
+// ---------------------------------------------------------------- weight packing
+
+struct PackShape {
+    int mode;
+    int64_t n_mats, Nout, K, ntn;
+};
+
+static PackShape pack_shape(const moe_cfg& c, int which) {
+    const bool routed = which == 0 || which == 1;
+    const int64_t n = routed ? c.n_experts : 1;
+    const int64_t I = routed ? c.inter : c.inter_shared;
+    if (which == 0 || which == 2) return {0, n, I, c.hidden, cdiv(I, 128)};
+    return {1, n, c.hidden, I, cdiv(c.hidden, 256)};
+}
+
+size_t packed_weight_bytes(const moe_cfg& c, int which) {
+    const PackShape s = pack_shape(c, which);
+    if (c.act_dtype == MOE_F32 && c.gemm_dtype == MOE_F32)
+        return (size_t)(s.n_mats * (s.mode == 0 ? 2 * s.Nout : s.Nout) * s.K * 4);
+    if (c.gemm_dtype == MOE_FP8_E4M3) return packed_weight_bytes_fp8(c, which);
+    return (size_t)(s.n_mats * s.ntn * G_WR * s.K * 2);
+}
+
+hipError_t launch_pack_weights(const moe_cfg& c, int which, const void* w, void* out,
+                               hipStream_t st) {
+    const PackShape s = pack_shape(c, which);
+    if (s.n_mats == 0 || s.Nout == 0) return hipSuccess;
+    if (c.act_dtype == MOE_F32 && c.gemm_dtype == MOE_F32)
+        return hipMemcpyAsync(out, w, packed_weight_bytes(c, which), hipMemcpyDeviceToDevice, st);
+    if (c.gemm_dtype == MOE_FP8_E4M3) return launch_pack_weights_fp8(c, which, w, out, st);
+    const int64_t n = s.n_mats * s.ntn * (s.K / G_SUB) * G_WR * 4;
+    const unsigned blocks = (unsigned)cdiv(n, 256);
+    if (s.mode == 0)
+        pack_weights_kernel<0><<<blocks, 256, 0, st>>>((const uint4*)w, (uint4*)out, s.n_mats,
+                                                       s.Nout, s.K, s.ntn);
+    else
+        pack_weights_kernel<1><<<blocks, 256, 0, st>>>((const uint4*)w, (uint4*)out, s.n_mats,
+                                                       s.Nout, s.K, s.ntn);
+    return hipGetLastError();
+}
+
 hipError_t launch_expert_ffn_fp8(const moe_cfg& c, const FfnArgs& a, const int2* tiles,
                                  const int32_t* counts, void* h_r, void* h_s, float* hs_r,
                                  float* hs_s, int64_t max_r, int64_t max_s, hipStream_t st);
@@ -429,7 +589,7 @@ hipError_t launch_expert_ffn(const moe_cfg& c, const FfnArgs& a, void* ws, hipSt
     // the bound on units up to a multiple of 8
     unsigned grid = (unsigned)(8 * cdiv(max_r * p.ntn_r + max_s * p.ntn_s, 8));
     if (bf)
-        ffn_gemm_bf16_kernel<0><<<grid, G_THREADS, 0, st>>>(p);
+        ffn_gemm_bf16_kernel<0, MOE_GEMM_BK, MOE_GEMM_NS><<<grid, G_THREADS, 0, st>>>(p);
     else
         ffn_gemm_f32_kernel<0><<<grid, 256, 0, st>>>(p);
 
@@ -449,7 +609,7 @@ hipError_t launch_expert_ffn(const moe_cfg& c, const FfnArgs& a, void* ws, hipSt
     p.ntn_s = has_shared ? (int)cdiv(c.hidden, cols1) : 0;
     grid = (unsigned)(8 * cdiv(max_r * p.ntn_r + max_s * p.ntn_s, 8));
     if (bf)
-        ffn_gemm_bf16_kernel<1><<<grid, G_THREADS, 0, st>>>(p);
+        ffn_gemm_bf16_kernel<1, MOE_GEMM_BK, MOE_GEMM_NS><<<grid, G_THREADS, 0, st>>>(p);
     else
         ffn_gemm_f32_kernel<1><<<grid, 256, 0, st>>>(p);
     return hipGetLastError();

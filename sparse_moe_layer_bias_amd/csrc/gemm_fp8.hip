@@ -8,4 +8,10 @@ hipError_t launch_expert_ffn_fp8(const moe_cfg&, const FfnArgs&, const int2*, co
     return hipErrorNotSupported;
 }
 
+size_t packed_weight_bytes_fp8(const moe_cfg&, int) { return 0; }
+
+hipError_t launch_pack_weights_fp8(const moe_cfg&, int, const void*, void*, hipStream_t) {
+    return hipErrorNotSupported;
+}
+
 }  // namespace moe

@@ -38,6 +38,13 @@ struct FfnArgs {
     void* y_shared;
 };
 size_t ffn_workspace_bytes(const moe_cfg& c);
+// which: 0 = routed W13, 1 = routed W2, 2 = shared W13, 3 = shared W2
+size_t packed_weight_bytes(const moe_cfg& c, int which);
+hipError_t launch_pack_weights(const moe_cfg& c, int which, const void* w, void* out,
+                               hipStream_t st);
+size_t packed_weight_bytes_fp8(const moe_cfg& c, int which);
+hipError_t launch_pack_weights_fp8(const moe_cfg& c, int which, const void* w, void* out,
+                                   hipStream_t st);
 hipError_t launch_expert_ffn(const moe_cfg& c, const FfnArgs& a, void* ws, hipStream_t st);
 
 // ---------------------------------------------------------------- combine / bias / prep

@@ -9,10 +9,19 @@ output h'_t, the biased Topk routing and the end-of-step bias rule.)
 import torch
 
 from . import (MoeCfg, cfg_from_dict, moe_bias_update, moe_combine, moe_expert_ffn,
-               moe_expert_ffn_workspace_size, moe_permute, moe_permute_workspace_size,
-               moe_quantize_weights_fp8, moe_route, moe_route_workspace_size)
+               moe_expert_ffn_workspace_size, moe_pack_weights, moe_packed_weights_size,
+               moe_permute, moe_permute_workspace_size, moe_quantize_weights_fp8, moe_route,
+               moe_route_workspace_size)
 
 GAMMA = 0.001  # end-of-step bias step (reading guide, "Methode" item 2)
+
+
+def pack_weights(cfg, which, w, stream=None):
+    """The expert GEMM's streaming layout of one weight stack (moe_pack_weights)."""
+    out = torch.empty((moe_packed_weights_size(cfg, which),), dtype=torch.uint8,
+                      device=w.device)
+    moe_pack_weights(cfg, which, w, out, stream)
+    return out
 
 
 def quantize_weights_fp8(w, stream=None):
@@ -49,12 +58,15 @@ class MoeLayer:
                 self.ws2, self.ws2_s = quantize_weights_fp8(ws2)
             else:
                 self.ws13 = self.ws13_s = self.ws2 = self.ws2_s = None
-        else:
-            self.w13, self.w2, self.ws13, self.ws2 = w13, w2, ws13, ws2
-            self.w13_s = self.w2_s = self.ws13_s = self.ws2_s = None
         has_shared = ws13 is not None and c["Is"] > 0
         if not has_shared:
             self.cfg.inter_shared = 0
+        if not self.fp8:
+            self.w13 = pack_weights(self.cfg, 0, w13)
+            self.w2 = pack_weights(self.cfg, 1, w2)
+            self.ws13 = pack_weights(self.cfg, 2, ws13) if has_shared else None
+            self.ws2 = pack_weights(self.cfg, 3, ws2) if has_shared else None
+            self.w13_s = self.w2_s = self.ws13_s = self.ws2_s = None
         i32 = dict(dtype=torch.int32, device=dev)
         f32 = dict(dtype=torch.float32, device=dev)
         self.scores = torch.empty((T, N), **f32)

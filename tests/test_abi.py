@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
             "moe_bias_update"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert moe.moe_abi_version() == 1
+    assert moe.moe_abi_version() == 2
 
 
 def _cfg(**kw):
