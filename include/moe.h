@@ -167,8 +167,9 @@ int moe_expert_ffn(const moe_cfg* cfg, const void* x_perm, const float* x_perm_s
  * W3 rows.  fp32 layers keep the plain layout (a copy).
  *  which: 0 = routed W13 [N, 2I, d], 1 = routed W2 [N, d, I],
  *         2 = shared W13 [2Is, d],   3 = shared W2 [d, Is]
- *  w: act_dtype, row-major; w_packed: moe_packed_weights_size(cfg, which) bytes.
- * FP8 weights are not packed by this call. */
+ *  w: act_dtype, row-major (FP8 layers: the E4M3 codes from
+ *     moe_quantize_weights_fp8, same shape; their scales are passed to
+ *     moe_expert_ffn unchanged); w_packed: moe_packed_weights_size(cfg, which) bytes. */
 size_t moe_packed_weights_size(const moe_cfg* cfg, int which);
 int moe_pack_weights(const moe_cfg* cfg, int which, const void* w, void* w_packed, void* stream);
 

@@ -228,8 +228,6 @@ int moe_pack_weights(const moe_cfg* cfg, int which, const void* w, void* w_packe
     if (which < 0 || which > 3) return fail(MOE_ERR_ARG, "%s: which must be 0..3", fn);
     if (which >= 2 && cfg->inter_shared == 0)
         return fail(MOE_ERR_ARG, "%s: no shared expert (inter_shared == 0)", fn);
-    if (cfg->gemm_dtype == MOE_FP8_E4M3)
-        return fail(MOE_ERR_UNSUPPORTED, "%s: FP8 weights are packed by moe_quantize_weights_fp8", fn);
     REQ_PTR(w);
     REQ_PTR(w_packed);
     if (w == w_packed) return fail(MOE_ERR_ARG, "%s: packing cannot run in place", fn);

@@ -13,14 +13,14 @@
 //
 // Tile order is XCD-aware (see decode_v2): consecutive work units of one
 // expert land on one XCD so its token rows or weight panel are shared in L2.
-#include "moe_internal.h"
+#include "gemm_common.h"
 
 namespace moe {
 
 static int64_t align256(int64_t b) { return (b + 255) & ~int64_t(255); }
 
-constexpr int BF_BM = 320;      // token rows per tile, bf16 / FP8 MFMA kernels
-constexpr int G_WR_PACK = 256;  // rows per packed weight tile (bf16)
+constexpr int BF_BM = 320;      // token rows per tile, bf16 MFMA kernel
+constexpr int FP8_BM = 256;     // token rows per tile, FP8 MFMA kernel
 constexpr int F32_BM = 64;      // token rows per tile, fp32 path
 
 // ---------------------------------------------------------------- tile map
@@ -56,83 +56,6 @@ __global__ void __launch_bounds__(256) ffn_tile_map_kernel(const int32_t* __rest
         counts[1] = ns;
     }
 }
-
-// ---------------------------------------------------------------- work units
-
-struct GemmParamsV2 {
-    const int2* tiles;     // routed tiles [0, n_r), shared tiles [n_r, n_r + n_s)
-    const int32_t* counts; // [0] = routed tiles, [1] = shared tiles
-    const int32_t* offsets;
-    int N;
-    int ntn_r, ntn_s;      // weight tiles per token tile, routed / shared
-    int64_t T;
-    int64_t K_r, K_s;
-    int64_t Nout_r, Nout_s;
-    const void* A_r;       // token rows
-    const void* A_s;
-    const void* B_r;       // weights
-    const void* B_s;
-    void* C_r;
-    void* C_s;
-};
-
-struct WorkV2 {
-    int64_t m0, M, K, Nout, wt;
-    const char* X;   // token rows of the group
-    const char* W;   // weights of the group
-    char* C;         // output rows of the group
-};
-
-// Units: routed (tile, wt) tile-major -- the weight tiles of one expert run
-// next to each other and share its token rows in L2; shared (wt, tile)
-// wt-major -- the token chunks of one weight panel run next to each other and
-// share it.  Unit u runs on blockIdx (u % per) * 8 + u / per, per = ceil(units/8),
-// so each XCD (blockIdx x, x+8, ...) gets a contiguous unit range.
-template <int ESZ>
-__device__ __forceinline__ bool decode_v2(const GemmParamsV2& p, int mode, WorkV2& w) {
-    const int64_t nr = p.counts[0], ns = p.counts[1];
-    const int64_t ur = nr * p.ntn_r, units = ur + ns * p.ntn_s;
-    const int64_t per = (units + 7) / 8;
-    const int64_t L = blockIdx.x;
-    if (L >= 8 * per) return false;
-    const int64_t u = (L % 8) * per + L / 8;
-    if (u >= units) return false;
-    int64_t tile;
-    if (u < ur) {
-        tile = u / p.ntn_r;
-        w.wt = u % p.ntn_r;
-    } else {
-        const int64_t v = u - ur;
-        w.wt = v / ns;
-        tile = nr + v % ns;
-    }
-    const int2 t = p.tiles[tile];
-    const int g = t.x;
-    w.m0 = t.y;
-    if (g < p.N) {
-        const int64_t rowbase = p.offsets[g];
-        w.M = p.offsets[g + 1] - rowbase;
-        w.K = p.K_r;
-        w.Nout = p.Nout_r;
-        w.X = (const char*)p.A_r + rowbase * w.K * ESZ;
-        // weights of one expert: ntn_r packed tiles of G_WR_PACK rows (bf16)
-        // or the plain [rows][K] matrix (fp32)
-        const int64_t wrows = ESZ == 2 ? (int64_t)p.ntn_r * G_WR_PACK
-                                       : (mode == 0 ? 2 * w.Nout : w.Nout);
-        w.W = (const char*)p.B_r + (int64_t)g * wrows * w.K * ESZ;
-        w.C = (char*)p.C_r + rowbase * w.Nout * ESZ;
-    } else {
-        w.M = p.T;
-        w.K = p.K_s;
-        w.Nout = p.Nout_s;
-        w.X = (const char*)p.A_s;
-        w.W = (const char*)p.B_s;
-        w.C = (char*)p.C_s;
-    }
-    return true;
-}
-
-__device__ __forceinline__ float silu_f(float a) { return a / (1.0f + __expf(-a)); }
 
 // ---------------------------------------------------------------- bf16 MFMA
 //
@@ -175,49 +98,6 @@ constexpr int G_SUB = 32;      // contraction elements per LDS sub-tile (64-byte
 #ifndef MOE_GEMM_NS
 #define MOE_GEMM_NS 2
 #endif
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ lds_void* to_lds(const void* p) { return (lds_void*)p; }
-
-// physical chunk of logical chunk c in row r of a 64-byte-row sub-tile (an
-// involution).  A ds_read_b128 is served 16 lanes (256 bytes, the 64 banks)
-// at a time; those lanes read one chunk of 16 consecutive rows, i.e. 4 rows
-// for each of the 4 row positions within a 256-byte bank line, and the XOR
-// with (r >> 2) & 3 gives those 4 rows 4 distinct chunk slots.
-__device__ __forceinline__ int sub_chunk(int r, int c) { return c ^ ((r >> 2) & 3); }
-
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// s_waitcnt vmcnt(n) for a wave-uniform n in 0..23 (the counter field takes
-// an immediate, hence the switch)
-__device__ __forceinline__ void vm_wait_n(int n) {
-    switch (n) {
-#define MOE_VMW(i) \
-    case i: vm_wait<i>(); break;
-        MOE_VMW(0) MOE_VMW(1) MOE_VMW(2) MOE_VMW(3) MOE_VMW(4) MOE_VMW(5) MOE_VMW(6) MOE_VMW(7)
-        MOE_VMW(8) MOE_VMW(9) MOE_VMW(10) MOE_VMW(11) MOE_VMW(12) MOE_VMW(13) MOE_VMW(14)
-        MOE_VMW(15) MOE_VMW(16) MOE_VMW(17) MOE_VMW(18) MOE_VMW(19) MOE_VMW(20) MOE_VMW(21)
-        MOE_VMW(22) MOE_VMW(23)
-#undef MOE_VMW
-        default: vm_wait<0>(); break;
-    }
-}
-
-// weight row (of the [2*Nout or Nout][K] expert matrix) held in packed row r of
-// weight tile wt; -1 for padding rows past the end (down projection only)
-template <int MODE>
-__device__ __forceinline__ int64_t packed_row_source(int64_t wt, int r, int64_t Nout) {
-    if (MODE == 0) {
-        const int g4 = r >> 6, half = (r >> 5) & 1, j = r & 31;
-        return (half ? Nout : 0) + wt * 128 + g4 * 32 + j;
-    }
-    const int64_t wr = wt * 256 + r;
-    return wr < Nout ? wr : -1;
-}
 
 // Pack a stack of n_mats expert matrices into the GEMM's LDS image order:
 // out[mat][wt][kc][slot] (16-byte chunks), kc = 32-wide contraction block,
@@ -462,7 +342,10 @@ struct FfnWs {
     float* hs_s;      // FP8 scales [T, Is/128]
 };
 
-static int ffn_bm(const moe_cfg& c) { return c.act_dtype == MOE_F32 ? F32_BM : BF_BM; }
+static int ffn_bm(const moe_cfg& c) {
+    if (c.gemm_dtype == MOE_FP8_E4M3) return FP8_BM;
+    return c.act_dtype == MOE_F32 ? F32_BM : BF_BM;
+}
 
 static int64_t ffn_max_routed_tiles(const moe_cfg& c) {
     return c.tokens * c.top_k / ffn_bm(c) + c.n_experts;

@@ -50,18 +50,23 @@ class MoeLayer:
         TK = T * k
         act = torch.bfloat16 if c["dtype"] == "bf16" else torch.float32
         dev = torch.device(device)
-        if self.fp8:
-            self.w13, self.w13_s = quantize_weights_fp8(w13)
-            self.w2, self.w2_s = quantize_weights_fp8(w2)
-            if ws13 is not None:
-                self.ws13, self.ws13_s = quantize_weights_fp8(ws13)
-                self.ws2, self.ws2_s = quantize_weights_fp8(ws2)
-            else:
-                self.ws13 = self.ws13_s = self.ws2 = self.ws2_s = None
         has_shared = ws13 is not None and c["Is"] > 0
         if not has_shared:
             self.cfg.inter_shared = 0
-        if not self.fp8:
+        if self.fp8:
+            # 128x128 block quantisation, then the GEMM's streaming order
+            q13, self.w13_s = quantize_weights_fp8(w13)
+            q2, self.w2_s = quantize_weights_fp8(w2)
+            self.w13 = pack_weights(self.cfg, 0, q13)
+            self.w2 = pack_weights(self.cfg, 1, q2)
+            del q13, q2
+            self.ws13 = self.ws13_s = self.ws2 = self.ws2_s = None
+            if has_shared:
+                qs13, self.ws13_s = quantize_weights_fp8(ws13)
+                qs2, self.ws2_s = quantize_weights_fp8(ws2)
+                self.ws13 = pack_weights(self.cfg, 2, qs13)
+                self.ws2 = pack_weights(self.cfg, 3, qs2)
+        else:
             self.w13 = pack_weights(self.cfg, 0, w13)
             self.w2 = pack_weights(self.cfg, 1, w2)
             self.ws13 = pack_weights(self.cfg, 2, ws13) if has_shared else None

@@ -15,7 +15,7 @@ import torch
 
 import moe_inputs
 import sparse_moe_layer_bias_amd as moe
-from parity_util import (RTOL, assert_bits, assert_close, host_inputs, log,
+from parity_util import (RTOL, assert_bits, assert_close, assert_close_fp8, host_inputs, log,
                          small_layer_inputs)
 from sparse_moe_layer_bias_amd.layer import MoeLayer
 
@@ -76,6 +76,35 @@ def test_layer_parity_small(orc, name, over):
     assert_close(moe_inputs.to_host(layer.y_perm), ref["y_perm"], rtol, "y_perm")
     assert_close(moe_inputs.to_host(layer.y_shared), ref["y_shared"], rtol, "y_shared")
     assert_close(moe_inputs.to_host(out), ref["out"], rtol, "out")
+    assert_bits(moe_inputs.to_host(bias), ref["new_bias"], "bias after update")
+
+
+FP8_CASES = [
+    ("mid_bf16", dict(T=256)),
+    ("mid_bf16", dict()),                                  # full mid size, T=2048
+    ("mid_bf16", dict(T=77)),                              # ragged, empty experts
+    ("mid_bf16", dict(T=300, G=8, TG=3)),                  # group-limited
+    ("mid_bf16", dict(T=64, d=256, I=128, Is=256)),        # Is != I
+    ("mid_bf16", dict(T=700, d=384, N=4, k=2, I=256, Is=128)),  # >256 rows/expert, d%256 != 0
+]
+
+
+@pytest.mark.parametrize("name,over", FP8_CASES)
+def test_layer_parity_fp8_small(orc, name, over):
+    """FP8 E4M3 expert GEMMs (1x128 activation tiles, 128x128 weight blocks,
+    fp32 promotion per 128-K block) against the oracle's FP8 path."""
+    over = dict(over)
+    T = over.pop("T", None)
+    c, layer, out, bias, ref = _run_small(name, orc, T=T, fp8=True, **over)
+    rtol = RTOL["fp8"]
+    assert_bits(moe_inputs.to_host(layer.idx), ref["idx"], "idx")
+    assert_bits(moe_inputs.to_host(layer.x_q), ref["x_q"], "x codes")
+    assert_bits(moe_inputs.to_host(layer.x_s).view(np.uint32), ref["x_s"].view(np.uint32),
+                "x scales")
+    assert_bits(moe_inputs.to_host(layer.x_perm), ref["x_q_perm"], "permuted codes")
+    assert_close_fp8(moe_inputs.to_host(layer.y_perm), ref["y_perm"], "y_perm")
+    assert_close_fp8(moe_inputs.to_host(layer.y_shared), ref["y_shared"], "y_shared")
+    assert_close_fp8(moe_inputs.to_host(out), ref["out"], "out")
     assert_bits(moe_inputs.to_host(bias), ref["new_bias"], "bias after update")
 
 
@@ -268,6 +297,54 @@ def v3_run():
     torch.cuda.synchronize()
     log("V3 forward done")
     return cfg, dev, layer, bias0, bias
+
+
+@pytest.fixture(scope="module")
+def v3_fp8_run():
+    cfg = dict(moe_inputs.CONFIGS["v3_fp8"])
+    log("generating V3-shaped inputs on the GPU (FP8 layer)")
+    dev = moe_inputs.make_layer_inputs(cfg, 0, "cuda")
+    layer = MoeLayer(cfg, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"])
+    bias0 = dev["bias"].clone()
+    bias = dev["bias"].clone()
+    layer.forward(dev["x"], dev["centroids"], bias)
+    torch.cuda.synchronize()
+    log("V3 FP8 forward done")
+    yield cfg, dev, layer, bias0, bias
+    del layer, dev
+    torch.cuda.empty_cache()
+
+
+def test_v3_fp8_layer_output_sampled_tokens(orc, v3_fp8_run):
+    cfg, dev, layer, bias0, bias = v3_fp8_run
+    rng = np.random.default_rng(3)
+    tok = np.unique(np.concatenate([rng.choice(cfg["T"], 6, replace=False), [cfg["T"] - 1]]))
+    ti = torch.from_numpy(tok).cuda()
+    xh = moe_inputs.to_host(dev["x"][ti])
+    r = orc.route(xh, moe_inputs.to_host(dev["centroids"]), moe_inputs.to_host(bias0),
+                  cfg["k"], cfg["G"], cfg["TG"])
+    assert_bits(moe_inputs.to_host(layer.idx)[tok], r["idx"], "idx (sampled)")
+    xq, xs = orc.quant_act_fp8(xh)
+    assert_bits(moe_inputs.to_host(layer.x_q[ti]), xq, "x codes (sampled)")
+    q13, s13 = orc.quant_weight_fp8(moe_inputs.to_host(dev["ws13"]))
+    q2, s2 = orc.quant_weight_fp8(moe_inputs.to_host(dev["ws2"]))
+    ys = orc.swiglu_ffn_fp8(xq, xs, q13, s13, q2, s2)
+    assert_close_fp8(moe_inputs.to_host(layer.y_shared[ti]), ys, "y_shared (sampled)")
+    yp_ref = np.zeros((len(tok), cfg["k"], cfg["d"]), np.uint16)
+    for e in np.unique(r["idx"]):
+        sel = np.argwhere(r["idx"] == e)
+        q13, s13 = orc.quant_weight_fp8(moe_inputs.to_host(dev["w13"][int(e)]))
+        q2, s2 = orc.quant_weight_fp8(moe_inputs.to_host(dev["w2"][int(e)]))
+        yp_ref[sel[:, 0], sel[:, 1]] = orc.swiglu_ffn_fp8(xq[sel[:, 0]], xs[sel[:, 0]], q13, s13,
+                                                          q2, s2)
+    dst = moe_inputs.to_host(layer.dst_row)[tok]
+    yp_gpu = moe_inputs.to_host(layer.y_perm[torch.from_numpy(dst.ravel()).long().cuda()])
+    assert_close_fp8(yp_gpu.reshape(-1, cfg["d"]), yp_ref.reshape(-1, cfg["d"]),
+                     "y_perm (sampled)")
+    k = cfg["k"]
+    fake_dst = np.arange(len(tok) * k, dtype=np.int32).reshape(len(tok), k)
+    out_ref = orc.combine(xh, ys, yp_ref.reshape(-1, cfg["d"]), r["gate"], fake_dst, "bf16")
+    assert_close_fp8(moe_inputs.to_host(layer.out[ti]), out_ref, "out (sampled)")
 
 
 def test_v3_routing_sampled_tokens(orc, v3_run):
