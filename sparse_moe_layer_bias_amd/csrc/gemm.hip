@@ -90,7 +90,8 @@ constexpr int G_WAVES = MOE_GEMM_WAVES;
 constexpr int G_THREADS = 64 * G_WAVES;
 constexpr int G_WRG = G_WAVES / 2;        // weight-row groups
 constexpr int G_WRB = 256 / 32 / G_WRG;   // 32-row weight blocks per wave
-constexpr int G_SUB = 32;      // contraction elements per LDS sub-tile (64-byte rows)
+constexpr int G_SUB = 64;      // contraction elements per LDS sub-tile (128-byte rows)
+constexpr int G_CPR = G_SUB / 8;  // 16-byte chunks per LDS row
 // contraction step and number of LDS stages in the copy pipeline
 #ifndef MOE_GEMM_BK
 #define MOE_GEMM_BK 64
@@ -98,26 +99,37 @@ constexpr int G_SUB = 32;      // contraction elements per LDS sub-tile (64-byte
 #ifndef MOE_GEMM_NS
 #define MOE_GEMM_NS 2
 #endif
+// L2 prefetch of the weight stage after the one being copied (two-stage
+// pipeline only): copies it into a 1 KB throwaway LDS slot so that its later
+// real copy hits L2 instead of waiting on HBM
+#ifndef MOE_GEMM_PF
+#define MOE_GEMM_PF 0
+#endif
+// operand copies: 0 = global -> LDS directly (global_load_lds), 1 = through
+// registers (global_load_dwordx4, then ds_write_b128 after the stage's MFMAs)
+#ifndef MOE_GEMM_LOADER
+#define MOE_GEMM_LOADER 0
+#endif
 
 // Pack a stack of n_mats expert matrices into the GEMM's LDS image order:
-// out[mat][wt][kc][slot] (16-byte chunks), kc = 32-wide contraction block,
-// slot = r*4 + pc holding logical chunk sub_chunk(r, pc) of packed row r.
+// out[mat][wt][kc][slot] (16-byte chunks), kc = 64-wide contraction block,
+// slot = r*8 + pc holding logical chunk sub_chunk8(r, pc) of packed row r.
 template <int MODE>
 __global__ void __launch_bounds__(256) pack_weights_kernel(const uint4* __restrict__ w,
                                                            uint4* __restrict__ out,
                                                            int64_t n_mats, int64_t Nout,
                                                            int64_t K, int64_t ntn) {
     const int64_t nkc = K / G_SUB;
-    const int64_t per_mat = ntn * nkc * G_WR * 4;
+    const int64_t per_mat = ntn * nkc * G_WR * G_CPR;
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n_mats * per_mat) return;
     const int64_t mat = i / per_mat;
     int64_t rem = i % per_mat;
-    const int64_t wt = rem / (nkc * G_WR * 4);
-    rem %= nkc * G_WR * 4;
-    const int64_t kc = rem / (G_WR * 4);
-    const int slot = (int)(rem % (G_WR * 4));
-    const int r = slot >> 2, c = sub_chunk(r, slot & 3);
+    const int64_t wt = rem / (nkc * G_WR * G_CPR);
+    rem %= nkc * G_WR * G_CPR;
+    const int64_t kc = rem / (G_WR * G_CPR);
+    const int slot = (int)(rem % (G_WR * G_CPR));
+    const int r = slot / G_CPR, c = sub_chunk8(r, slot % G_CPR);
     const int64_t src = packed_row_source<MODE>(wt, r, Nout);
     const int64_t rows = MODE == 0 ? 2 * Nout : Nout;
     uint4 v = make_uint4(0, 0, 0, 0);
@@ -134,6 +146,7 @@ __device__ __forceinline__ void gemm_bf16_body(const WorkV2& w, uint16_t* smem) 
     constexpr int PA = NA / G_WAVES, PX = (NX + G_WAVES - 1) / G_WAVES;
     constexpr int NBB = NB > 0 ? NB : 1;
     static_assert(NA % G_WAVES == 0, "weight copies split evenly over the waves");
+    static_assert(BK % G_SUB == 0, "contraction step is a whole number of LDS sub-tiles");
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -146,10 +159,11 @@ __device__ __forceinline__ void gemm_bf16_body(const WorkV2& w, uint16_t* smem) 
     const uint32_t woff = lane * 16;
     const char* xbase = w.X + w.m0 * K * 2;  // the tile's first token row
 
-    // Token copies: block b = 16 rows (rb = b / NSUB) of sub-tile q = b % NSUB,
-    // so the blocks holding real rows are the prefix b < nxe.  Rows past the
-    // tile's last real row are never copied (their LDS is never stored from).
-    const int nxe = NSUB * (int)((mc + 15) / 16);
+    // Token copies: block b = 8 rows (rb = b / NSUB) of sub-tile q = b % NSUB,
+    // each row one full 128-byte line; the blocks holding real rows are the
+    // prefix b < nxe.  Rows past the tile's last real row are never copied
+    // (their LDS is never stored from).
+    const int nxe = NSUB * (int)((mc + 7) / 8);
     int cnt = PA;  // copies this wave issues per stage
     uint32_t xoff[PX];
 #pragma unroll
@@ -157,7 +171,7 @@ __device__ __forceinline__ void gemm_bf16_body(const WorkV2& w, uint16_t* smem) 
         const int b = wave + G_WAVES * j;
         if (b < nxe) ++cnt;
         const int q = b % NSUB, rb = b / NSUB;
-        const int r = rb * 16 + (lane >> 2), c = sub_chunk(r, lane & 3);
+        const int r = rb * 8 + (lane >> 3), c = sub_chunk8(r, lane & 7);
         const int64_t tr = r < mc ? r : mc - 1;  // clamp inside a partial block
         xoff[j] = (uint32_t)((tr * K + q * G_SUB + c * 8) * 2);
     }
@@ -185,6 +199,18 @@ __device__ __forceinline__ void gemm_bf16_body(const WorkV2& w, uint16_t* smem) 
         }
     };
 
+    constexpr bool PF = MOE_GEMM_PF != 0 && NS == 2;
+    uint16_t* pf_slot = smem + NS * (A_EL + X_EL);  // 1 KB, never read
+    auto prefetch = [&](int kt) {
+        const char* wsrc = wstage0 + (int64_t)kt * A_EL * 2;
+#pragma unroll
+        for (int j = 0; j < PA; ++j) {
+            const int b = wave + G_WAVES * j;
+            __builtin_amdgcn_global_load_lds((const void*)(wsrc + b * 1024 + woff), to_lds(pf_slot),
+                                             16, 0, 0);
+        }
+    };
+
     f32x16_t acc[G_WRB][NBB];
 #pragma unroll
     for (int i = 0; i < G_WRB; ++i)
@@ -193,35 +219,27 @@ __device__ __forceinline__ void gemm_bf16_body(const WorkV2& w, uint16_t* smem) 
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-#pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
-        if (s < nk) issue(s, s);
-    for (int kt = 0; kt < nk; ++kt) {
-        // copies of later stages already issued by this wave may stay in flight
-        const int after = nk - 1 - kt < NS - 2 ? nk - 1 - kt : NS - 2;
-        vm_wait_n(after * cnt);
-        __syncthreads();  // stage kt landed for every wave; stage kt-1 is free
-        if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
+    auto compute = [&](int sidx) {
         if constexpr (NB > 0) {
-            const uint16_t* As = stage_a(kt % NS);
-            const uint16_t* Xs = stage_x(kt % NS);
+            const uint16_t* As = stage_a(sidx);
+            const uint16_t* Xs = stage_x(sidx);
 #pragma unroll
             for (int s = 0; s < BK / 16; ++s) {
-                const int q = s >> 1, c = 2 * (s & 1) + (lane >> 5);
+                const int q = s / (G_SUB / 16), c = 2 * (s % (G_SUB / 16)) + (lane >> 5);
                 bf16x8_t af[G_WRB], xf[NB];
 #pragma unroll
                 for (int i = 0; i < G_WRB; ++i) {
                     const int r = (wr * G_WRB + i) * 32 + (lane & 31);
                     af[i] = __builtin_bit_cast(
                         bf16x8_t,
-                        *(const uint4*)(As + q * G_WR * G_SUB + r * G_SUB + sub_chunk(r, c) * 8));
+                        *(const uint4*)(As + q * G_WR * G_SUB + r * G_SUB + sub_chunk8(r, c) * 8));
                 }
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
                     const int r = tg * 160 + j * 32 + (lane & 31);
                     xf[j] = __builtin_bit_cast(
                         bf16x8_t,
-                        *(const uint4*)(Xs + q * G_TR * G_SUB + r * G_SUB + sub_chunk(r, c) * 8));
+                        *(const uint4*)(Xs + q * G_TR * G_SUB + r * G_SUB + sub_chunk8(r, c) * 8));
                 }
 #pragma unroll
                 for (int j = 0; j < NB; ++j)
@@ -230,6 +248,61 @@ __device__ __forceinline__ void gemm_bf16_body(const WorkV2& w, uint16_t* smem) 
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], xf[j], acc[i][j],
                                                                              0, 0, 0);
             }
+        }
+    };
+
+    if constexpr (MOE_GEMM_LOADER == 1 && NS == 2) {
+        uint4 ra[PA], rx[PX];
+        auto gload = [&](int kt) {
+            const char* wsrc = wstage0 + (int64_t)kt * A_EL * 2;
+            const char* xsrc = xbase + (int64_t)kt * BK * 2;
+#pragma unroll
+            for (int j = 0; j < PA; ++j)
+                ra[j] = *(const uint4*)(wsrc + (wave + G_WAVES * j) * 1024 + woff);
+#pragma unroll
+            for (int j = 0; j < PX; ++j)
+                if (wave + G_WAVES * j < nxe) rx[j] = *(const uint4*)(xsrc + xoff[j]);
+        };
+        auto lstore = [&](int s) {
+            uint16_t* As = stage_a(s);
+            uint16_t* Xs = stage_x(s);
+#pragma unroll
+            for (int j = 0; j < PA; ++j)
+                *(uint4*)(As + (wave + G_WAVES * j) * 512 + lane * 8) = ra[j];
+#pragma unroll
+            for (int j = 0; j < PX; ++j) {
+                const int b = wave + G_WAVES * j;
+                if (b < nxe)
+                    *(uint4*)(Xs + (b % NSUB) * G_TR * G_SUB + (b / NSUB) * 512 + lane * 8) = rx[j];
+            }
+        };
+        gload(0);
+        lstore(0);
+        if (1 < nk) gload(1);
+        __syncthreads();
+        for (int kt = 0; kt < nk; ++kt) {
+            compute(kt & 1);
+            if (kt + 1 < nk) lstore((kt + 1) & 1);  // registers hold stage kt+1
+            if (kt + 2 < nk) gload(kt + 2);
+            __syncthreads();
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < NS - 1; ++s)
+            if (s < nk) issue(s, s);
+        if (PF && 1 < nk) prefetch(1);
+        for (int kt = 0; kt < nk; ++kt) {
+            // copies issued by this wave after stage kt's may stay in flight: later
+            // stages (cnt each) or, two-stage + prefetch, the prefetch of kt+1
+            const int after = nk - 1 - kt < NS - 2 ? nk - 1 - kt : NS - 2;
+            if (PF)
+                vm_wait_n(kt + 1 < nk ? PA : 0);
+            else
+                vm_wait_n(after * cnt);
+            __syncthreads();  // stage kt landed for every wave; stage kt-1 is free
+            if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
+            if (PF && kt + NS < nk) prefetch(kt + NS);
+            compute(kt % NS);
         }
     }
 
@@ -276,7 +349,7 @@ template <int MODE, int BK, int NS>
 __global__ void __launch_bounds__(G_THREADS, 1) ffn_gemm_bf16_kernel(GemmParamsV2 p) {
     WorkV2 w;
     if (!decode_v2<2>(p, MODE, w)) return;
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * (G_WR + G_TR) * BK];
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * (G_WR + G_TR) * BK + 512];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wr = wave % G_WRG, tg = wave / G_WRG;
     const int64_t mc = w.M - w.m0 < G_TR ? w.M - w.m0 : G_TR;
@@ -417,7 +490,7 @@ hipError_t launch_pack_weights(const moe_cfg& c, int which, const void* w, void*
     if (c.act_dtype == MOE_F32 && c.gemm_dtype == MOE_F32)
         return hipMemcpyAsync(out, w, packed_weight_bytes(c, which), hipMemcpyDeviceToDevice, st);
     if (c.gemm_dtype == MOE_FP8_E4M3) return launch_pack_weights_fp8(c, which, w, out, st);
-    const int64_t n = s.n_mats * s.ntn * (s.K / G_SUB) * G_WR * 4;
+    const int64_t n = s.n_mats * s.ntn * (s.K / G_SUB) * G_WR * G_CPR;
     const unsigned blocks = (unsigned)cdiv(n, 256);
     if (s.mode == 0)
         pack_weights_kernel<0><<<blocks, 256, 0, st>>>((const uint4*)w, (uint4*)out, s.n_mats,

@@ -102,6 +102,10 @@ __device__ __forceinline__ lds_void* to_lds(const void* p) { return (lds_void*)p
 // with (r >> 2) & 3 gives those 4 rows 4 distinct chunk slots.
 __device__ __forceinline__ int sub_chunk(int r, int c) { return c ^ ((r >> 2) & 3); }
 
+// the same for 128-byte rows (8 chunks, two rows per 256-byte bank line):
+// the 16 lanes reading one chunk of 16 consecutive rows get 16 distinct slots
+__device__ __forceinline__ int sub_chunk8(int r, int c) { return c ^ ((r >> 1) & 7); }
+
 template <int N>
 __device__ __forceinline__ void vm_wait() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");

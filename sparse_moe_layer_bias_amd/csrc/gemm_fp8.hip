@@ -188,22 +188,35 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
                     af[q][i] = ld_frag32(As + q * (G_WR_PACK * F8_SUB) + r * F8_SUB, r,
                                          2 * (lane >> 5));
                 }
-#pragma unroll
-            for (int j = 0; j < NB; ++j) {
+            // partials of token block j are promoted while the MFMAs of block
+            // j+1 run: two sets of partial registers, used alternately
+            f32x16_t pp[2][2];
+            float sxv[2];
+            auto mma = [&](int j, int buf) {
                 const int r = tg * 128 + j * 32 + (lane & 31);
                 const i32x8_t x0 = ld_frag32(Xs + r * F8_SUB, r, 2 * (lane >> 5));
                 const i32x8_t x1 = ld_frag32(Xs + F8_TR * F8_SUB + r * F8_SUB, r, 2 * (lane >> 5));
-                const float sx = Ss[r];
+                sxv[buf] = Ss[r];
+                const f32x16_t z = {};
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    pp[buf][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[0][i], x0, z, 0,
+                                                                                 0, 0, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    pp[buf][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        af[1][i], x1, pp[buf][i], 0, 0, 0, 0, 0, 0);
+            };
+            mma(0, 0);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                if (j + 1 < NB) mma(j + 1, (j + 1) & 1);
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
-                    f32x16_t p = {};
-                    p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[0][i], x0, p, 0, 0, 0,
-                                                                        0, 0, 0);
-                    p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[1][i], x1, p, 0, 0, 0,
-                                                                        0, 0, 0);
-                    const float sc = sw[i] * sx;
+                    const float sc = sw[i] * sxv[j & 1];
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(p[v], sc, acc[i][j][v]);
+                    for (int v = 0; v < 16; ++v)
+                        acc[i][j][v] = __builtin_fmaf(pp[j & 1][i][v], sc, acc[i][j][v]);
                 }
             }
         }
