@@ -20,106 +20,133 @@ namespace moe {
 
 // ------------------------------------------------------------------ logits
 
-// Tile: 128 tokens x 64 experts per 256-thread workgroup; each thread owns
-// 8 tokens x 4 experts (32 independent FMA chains).  BK = 16 hidden
-// elements per LDS stage, double buffered.
-constexpr int RL_TM = 128, RL_TN = 64, RL_BK = 16;
+// Tile: TM = 16*TY tokens x 64 experts per 256-thread workgroup; each thread
+// owns TY tokens x 4 experts (4*TY independent FMA chains).  BK = 32 hidden
+// elements per LDS stage, double buffered, held transposed ([k][token],
+// [k][expert]) so each thread reads its tokens and experts as float4s.
+// Global loads are 16-byte vectors; FULL = (d % BK == 0) drops every
+// per-element bound check, the other instance pads the last stage with zeros
+// (an fma with two zero operands leaves a chain unchanged: the chain starts
+// at +0 and never holds -0).
+constexpr int RL_TN = 64, RL_BK = 32;
 
-template <typename XT>
-__device__ __forceinline__ void rl_load_x(const XT* __restrict__ x, int64_t T, int64_t d,
-                                          int64_t t0, int64_t k0, int tid, float (&xr)[8]) {
-    // thread -> token t0 + tid/2, hidden k0 + 8*(tid%2) .. +7
-    int64_t t = t0 + (tid >> 1);
+template <int TY>
+struct RlRegs {
+    static constexpr int XE = 16 * TY * RL_BK / 256;  // x elements per thread per stage
+    float x[XE];
+    float e[8];   // expert tid/4, hidden (tid&3)*8 .. +7
+};
+
+template <typename XT, bool FULL, int TY>
+__device__ __forceinline__ void rl_load(const XT* __restrict__ x, const float* __restrict__ E,
+                                        int64_t T, int64_t d, int64_t N, int64_t t0, int64_t n0,
+                                        int64_t k0, int tid, RlRegs<TY>& r) {
+    constexpr int XE = RlRegs<TY>::XE, TPT = RL_BK / XE;  // threads per token row
+    int64_t t = t0 + tid / TPT;
     if (t >= T) t = T - 1;  // clamp: a valid row, the result is never stored
-    int64_t kk = k0 + 8 * (tid & 1);
-    const XT* row = x + t * d;
+    const int64_t kx = k0 + XE * (tid % TPT);
+    const XT* xrow = x + t * d + kx;
+    if (FULL) {
+        // XE consecutive elements: one vector load of XE * sizeof(XT) bytes
+        XT raw[XE];
+        __builtin_memcpy(raw, xrow, sizeof(raw));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        int64_t j = kk + i;
-        float v = 0.0f;
-        if (j < d) {
+        for (int i = 0; i < XE; ++i) {
             if constexpr (sizeof(XT) == 2)
-                v = bf16_to_f32(row[j]);
+                r.x[i] = bf16_to_f32(raw[i]);
             else
-                v = row[j];
+                r.x[i] = raw[i];
         }
-        xr[i] = v;
-    }
-}
-
-__device__ __forceinline__ void rl_load_e(const float* __restrict__ E, int64_t N, int64_t d,
-                                          int64_t n0, int64_t k0, int tid, float (&er)[4]) {
-    // thread -> expert n0 + tid/4, hidden k0 + 4*(tid%4) .. +3
-    int64_t n = n0 + (tid >> 2);
-    int64_t kk = k0 + 4 * (tid & 3);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int64_t j = kk + i;
-        er[i] = (n < N && j < d) ? E[n * d + j] : 0.0f;
+        for (int i = 0; i < XE; ++i) {
+            float v = 0.0f;
+            if (kx + i < d) {
+                if constexpr (sizeof(XT) == 2)
+                    v = bf16_to_f32(xrow[i]);
+                else
+                    v = xrow[i];
+            }
+            r.x[i] = v;
+        }
+    }
+    const int64_t n = n0 + (tid >> 2);
+    const int64_t ke = k0 + 8 * (tid & 3);
+    if (n < N) {
+        const float* erow = E + n * d + ke;
+        if (FULL) {
+            const float4 a = *(const float4*)erow;
+            const float4 b = *(const float4*)(erow + 4);
+            r.e[0] = a.x; r.e[1] = a.y; r.e[2] = a.z; r.e[3] = a.w;
+            r.e[4] = b.x; r.e[5] = b.y; r.e[6] = b.z; r.e[7] = b.w;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) r.e[i] = ke + i < d ? erow[i] : 0.0f;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r.e[i] = 0.0f;
     }
 }
 
-template <typename XT>
+template <typename XT, bool FULL, int TY>
 __global__ void __launch_bounds__(256) router_logits_kernel(const XT* __restrict__ x,
                                                             const float* __restrict__ E,
                                                             float* __restrict__ s_out,
                                                             int64_t T, int64_t d, int64_t N) {
-    __shared__ float xs[2][RL_BK][RL_TM + 4];
-    __shared__ float es[2][RL_BK][RL_TN + 4];
+    constexpr int TM = 16 * TY;
+    constexpr int XE = RlRegs<TY>::XE, TPT = RL_BK / XE;
+    __shared__ __attribute__((aligned(16))) float xs[2][RL_BK][TM + 4];
+    __shared__ __attribute__((aligned(16))) float es[2][RL_BK][RL_TN + 4];
     const int tid = threadIdx.x;
     const int64_t n0 = (int64_t)blockIdx.x * RL_TN;
-    const int64_t t0 = (int64_t)blockIdx.y * RL_TM;
-    const int ty = tid >> 4;  // 0..15 -> tokens ty*8 .. +7
+    const int64_t t0 = (int64_t)blockIdx.y * TM;
+    const int ty = tid >> 4;  // 0..15 -> tokens ty*TY .. +TY-1
     const int tx = tid & 15;  // 0..15 -> experts tx*4 .. +3
 
-    float acc[8][4];
+    float acc[TY][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < TY; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
 
-    float xr[8], er[4];
+    auto store = [&](int buf, const RlRegs<TY>& r) {
+#pragma unroll
+        for (int i = 0; i < XE; ++i) xs[buf][XE * (tid % TPT) + i][tid / TPT] = r.x[i];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) es[buf][8 * (tid & 3) + i][tid >> 2] = r.e[i];
+    };
+
+    RlRegs<TY> r;
     const int64_t nk = cdiv(d, RL_BK);
-    rl_load_x(x, T, d, t0, 0, tid, xr);
-    rl_load_e(E, N, d, n0, 0, tid, er);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) xs[0][8 * (tid & 1) + i][tid >> 1] = xr[i];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) es[0][4 * (tid & 3) + i][tid >> 2] = er[i];
+    rl_load<XT, FULL, TY>(x, E, T, d, N, t0, n0, 0, tid, r);
+    store(0, r);
     __syncthreads();
 
     for (int64_t kb = 0; kb < nk; ++kb) {
         const int buf = kb & 1;
         const bool more = kb + 1 < nk;
-        if (more) {
-            rl_load_x(x, T, d, t0, (kb + 1) * RL_BK, tid, xr);
-            rl_load_e(E, N, d, n0, (kb + 1) * RL_BK, tid, er);
-        }
+        if (more) rl_load<XT, FULL, TY>(x, E, T, d, N, t0, n0, (kb + 1) * RL_BK, tid, r);
 #pragma unroll
         for (int k = 0; k < RL_BK; ++k) {
-            const float4 xa = *reinterpret_cast<const float4*>(&xs[buf][k][ty * 8]);
-            const float4 xb = *reinterpret_cast<const float4*>(&xs[buf][k][ty * 8 + 4]);
+            float xv[TY];
+#pragma unroll
+            for (int i = 0; i < TY; ++i) xv[i] = xs[buf][k][ty * TY + i];
             const float4 eb = *reinterpret_cast<const float4*>(&es[buf][k][tx * 4]);
-            const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
             const float ev[4] = {eb.x, eb.y, eb.z, eb.w};
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < TY; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(xv[i], ev[j], acc[i][j]);
         }
-        if (more) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) xs[buf ^ 1][8 * (tid & 1) + i][tid >> 1] = xr[i];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) es[buf ^ 1][4 * (tid & 3) + i][tid >> 2] = er[i];
-        }
+        if (more) store(buf ^ 1, r);
         __syncthreads();
     }
 
     // epilogue: affinity s = Sigmoid(z), evaluated in double, rounded once
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t t = t0 + ty * 8 + i;
+    for (int i = 0; i < TY; ++i) {
+        const int64_t t = t0 + ty * TY + i;
         if (t >= T) continue;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -272,6 +299,27 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
 
 // ------------------------------------------------------------------ launch
 
+template <int TY>
+static void launch_logits(int32_t act_dtype, bool full, const void* x, const float* centroids,
+                          float* scores, int64_t T, int64_t d, int64_t N, hipStream_t st) {
+    const dim3 g1((unsigned)cdiv(N, RL_TN), (unsigned)cdiv(T, 16 * TY));
+    if (act_dtype == MOE_BF16) {
+        if (full)
+            router_logits_kernel<uint16_t, true, TY><<<g1, 256, 0, st>>>(
+                (const uint16_t*)x, centroids, scores, T, d, N);
+        else
+            router_logits_kernel<uint16_t, false, TY><<<g1, 256, 0, st>>>(
+                (const uint16_t*)x, centroids, scores, T, d, N);
+    } else {
+        if (full)
+            router_logits_kernel<float, true, TY><<<g1, 256, 0, st>>>((const float*)x, centroids,
+                                                                      scores, T, d, N);
+        else
+            router_logits_kernel<float, false, TY><<<g1, 256, 0, st>>>(
+                (const float*)x, centroids, scores, T, d, N);
+    }
+}
+
 hipError_t launch_route(const moe_cfg& c, const void* x, const float* centroids,
                         const float* bias, float* scores, int32_t* idx, float* gate,
                         int32_t* counts, hipStream_t st) {
@@ -280,13 +328,17 @@ hipError_t launch_route(const moe_cfg& c, const void* x, const float* centroids,
         fill_i32_kernel<<<dim3((unsigned)cdiv(N, 256)), 256, 0, st>>>(counts, N, 0);
         return hipGetLastError();
     }
-    dim3 g1((unsigned)cdiv(N, RL_TN), (unsigned)cdiv(T, RL_TM));
-    if (c.act_dtype == MOE_BF16)
-        router_logits_kernel<uint16_t><<<g1, 256, 0, st>>>((const uint16_t*)x, centroids, scores,
-                                                           T, d, N);
+    // Each (token, expert) logit is one serial chain over d, so the tile per
+    // thread trades chains (latency hiding) against workgroups (parallelism):
+    // 8 tokens per thread for large batches, 1 for decode-sized ones.
+    const bool full = d % RL_BK == 0;
+    const int64_t wgs8 = cdiv(N, RL_TN) * cdiv(T, 16 * 8);
+    if (wgs8 >= 192)
+        launch_logits<8>(c.act_dtype, full, x, centroids, scores, T, d, N, st);
+    else if (cdiv(N, RL_TN) * cdiv(T, 16 * 2) >= 192)
+        launch_logits<2>(c.act_dtype, full, x, centroids, scores, T, d, N, st);
     else
-        router_logits_kernel<float><<<g1, 256, 0, st>>>((const float*)x, centroids, scores, T, d,
-                                                        N);
+        launch_logits<1>(c.act_dtype, full, x, centroids, scores, T, d, N, st);
     fill_i32_kernel<<<dim3((unsigned)cdiv(N, 256)), 256, 0, st>>>(counts, N, 0);
     const int G = c.n_group > 1 ? (int)c.n_group : 1;
     const dim3 gs((unsigned)cdiv(T, 4));
