@@ -43,7 +43,121 @@ def parse():
     ap.add_argument("--workload", default="v3_bf16")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-run", action="store_true",
+                    help="run the expert FFN 3 times and a 1 GiB copy 3 times (for rocprofv3 "
+                         "--pmc FETCH_SIZE / WRITE_SIZE passes), then exit")
+    ap.add_argument("--stats-summary", metavar="KERNEL_STATS_CSV",
+                    help="print the per-kernel table of a rocprofv3 --stats run, then exit")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise the two counter CSVs of a --traffic-run into the text "
+                         "that profiles/ keeps, then exit")
     return ap.parse_args()
+
+
+GEMM_SOURCES = ("gemm.hip", "gemm_common.h", "gemm_fp8.hip")
+COPY_BYTES = 1 << 30
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def gemm_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "sparse_moe_layer_bias_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(workload):
+    return os.path.join(PROFILE_DIR, "expert_ffn_%s_traffic.txt" % workload)
+
+
+def recorded_traffic(workload):
+    """HBM bytes per expert-FFN call recorded under profiles/, or None when
+    absent or taken on GEMM sources other than the current ones."""
+    path = traffic_file(workload)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("gemm_source_hash") != gemm_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def traffic_summary(fetch_csv, write_csv, workload):
+    import csv
+    import collections
+
+    def per_kernel(path, counter):
+        acc = collections.defaultdict(list)
+        with open(path) as f:
+            rows = [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        for r in rows:
+            acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return acc
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    # the calibration copies are the last 3 dispatches of the copy kernel
+    copy_k = [k for k in fetch if "copybuffer" in k.lower()]
+    if not copy_k or len(fetch[copy_k[0]]) < 3:
+        raise SystemExit("no calibration copy found")
+    cf = sum(fetch[copy_k[0]][-3:]) / 3 * 1024.0
+    cw = sum(write[copy_k[0]][-3:]) / 3 * 1024.0
+    f_scale = COPY_BYTES / cf
+    w_scale = COPY_BYTES / cw
+    lines = []
+    ffn = [k for k in fetch if "ffn_" in k]
+    total = 0.0
+    for k in ffn:
+        fb = sum(fetch[k]) / len(fetch[k]) * 1024.0 * f_scale
+        wb = (sum(write[k]) / len(write[k]) * 1024.0 * w_scale) if k in write else 0.0
+        total += fb + wb
+        lines.append("kernel: %s | fetch %.4g B | write %.4g B | dispatches %d" %
+                     (k[:90], fb, wb, len(fetch[k])))
+    out = ["workload: %s" % workload,
+           "calibration_copy_kernel: %s" % copy_k[0][:90],
+           "calibration_fetch_scale: %.5f" % f_scale,
+           "calibration_write_scale: %.5f" % w_scale]
+    out += lines
+    out += ["hbm_bytes_per_launch: %.6g" % total,
+            "gemm_source_hash: %s" % gemm_source_hash()]
+    return "\n".join(out)
+
+
+def stats_summary(path):
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    out = ["%-72s %6s %12s %12s %7s" % ("kernel", "calls", "avg_us", "total_us", "pct")]
+    for r in rows:
+        out.append("%-72s %6s %12.1f %12.1f %7.2f" % (
+            r["Name"][:72], r["Calls"], float(r["AverageNs"]) / 1e3,
+            float(r["TotalDurationNs"]) / 1e3, float(r["Percentage"])))
+    return "\n".join(out)
+
+
+def traffic_run(cfg, layer, dev):
+    import torch
+    x = dev["x"]
+    layer.route(x, dev["centroids"], dev["bias"])
+    layer.permute(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        layer.expert_ffn(x)
+    a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
 
 
 def cpu_baseline(cfg, dev, log):
@@ -102,6 +216,12 @@ def cpu_baseline(cfg, dev, log):
 
 def main():
     args = parse()
+    if args.stats_summary:
+        print(stats_summary(args.stats_summary))
+        return
+    if args.traffic_summary:
+        print(traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.workload))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(no collectives); run with --gpus 1", file=sys.stderr)
@@ -129,6 +249,10 @@ def main():
     bias = dev["bias"].clone()
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
+    if args.traffic_run:
+        traffic_run(cfg, layer, dev)
+        log("traffic run done")
+        return
 
     for _ in range(args.warmup):
         layer.forward(x, E, bias)
@@ -192,7 +316,7 @@ def main():
                    "global_batch": T, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "kernel": "grouped expert GEMMs (gate/up+SwiGLU, down)",
                      "achieved": achieved / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": None,
+                     "frac": achieved / peak, "traffic": recorded_traffic(args.workload),
                      "weight_stream_frac_of_hbm": wbytes / ffn_s / PEAK["hbm"]},
         "stages_ms": stage_ms,
         "layer_tflops": (flops + 2.0 * T * cfg["d"] * cfg["N"]) / (ms_per_step / 1e3) / 1e12,
