@@ -20,7 +20,7 @@ namespace moe {
 static int64_t align256(int64_t b) { return (b + 255) & ~int64_t(255); }
 
 constexpr int BF_BM = 320;      // token rows per tile, bf16 MFMA kernel
-constexpr int FP8_BM = 256;     // token rows per tile, FP8 MFMA kernel
+constexpr int FP8_BM = 320;     // token rows per tile, FP8 MFMA kernel
 constexpr int F32_BM = 64;      // token rows per tile, fp32 path
 
 // ---------------------------------------------------------------- tile map
@@ -221,6 +221,7 @@ __device__ __forceinline__ void gemm_bf16_body(const WorkV2& w, uint16_t* smem) 
 
     auto compute = [&](int sidx) {
         if constexpr (NB > 0) {
+            __builtin_amdgcn_iglp_opt(1);  // interleave the LDS reads with the MFMAs
             const uint16_t* As = stage_a(sidx);
             const uint16_t* Xs = stage_x(sidx);
 #pragma unroll
@@ -306,41 +307,78 @@ __device__ __forceinline__ void gemm_bf16_body(const WorkV2& w, uint16_t* smem) 
         }
     }
 
-    // epilogue.  32x32 accumulator layout: lane l holds column (token) l%32 and
+    // Epilogue.  32x32 accumulator layout: lane l holds column (token) l%32 and
     // rows (weight rows) 8*(v/4) + 4*(l/32) + v%4, v = 0..15.  gate/up: weight
     // blocks (0, 1) and (2, 3) are the W1 and W3 rows of the same 32 columns.
-    if constexpr (NB > 0) {
-        const int64_t wbase = MODE == 0 ? w.wt * 128 : w.wt * 256;
+    // The output tile goes through LDS so that global stores are whole
+    // 16-byte row chunks: gate/up writes 128 h columns of every row at once;
+    // down writes 256 y columns in two passes (token halves).  LDS rows are
+    // padded by 16 bytes so the 16 rows written by a half-wave hit distinct banks.
+    __syncthreads();  // every wave is done with the stage buffers
+    constexpr int OCOLS = MODE == 0 ? 128 : 256;
+    constexpr int OSTR = OCOLS + 8;  // padded LDS row (elements)
+    uint16_t* ot = smem;
+    const int64_t wbase = MODE == 0 ? w.wt * 128 : w.wt * 256;
+    auto put = [&](int row, int col, float a0, float a1, float a2, float a3) {
+        *(uint2*)(ot + row * OSTR + col) = make_uint2(pack_bf16x2(a0, a1), pack_bf16x2(a2, a3));
+    };
+    auto flush_rows = [&](int r0, int nrows) {
+        // tile rows r0 .. r0+nrows-1 (held in LDS rows 0 ..) -> global,
+        // 16 bytes per thread
+        constexpr int CH = OCOLS / 8;
+        uint16_t* C = (uint16_t*)w.C;
+        for (int q = threadIdx.x; q < nrows * CH; q += G_THREADS) {
+            const int rr = q / CH, ch = q % CH;
+            const int64_t t = w.m0 + r0 + rr;
+            const int64_t col = wbase + ch * 8;
+            if (r0 + rr < mc && col < w.Nout)
+                *(uint4*)(C + t * w.Nout + col) = *(const uint4*)(ot + rr * OSTR + ch * 8);
+        }
+    };
+    if (MODE == 0) {
+        if constexpr (NB > 0) {
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const int64_t t = w.m0 + tg * 160 + j * 32 + (lane & 31);
-            if (t >= w.M) continue;
-            uint16_t* crow = (uint16_t*)w.C + t * w.Nout;
+            for (int j = 0; j < NB; ++j) {
+                const int row = tg * 160 + j * 32 + (lane & 31);
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int rr = 8 * g + 4 * (lane >> 5);
-                if (MODE == 0) {
+                for (int g = 0; g < 4; ++g) {
+                    const int rr = 8 * g + 4 * (lane >> 5);
 #pragma unroll
                     for (int pr = 0; pr < G_WRB / 2; ++pr) {
-                        const int64_t n = wbase + (wr * G_WRB / 2 + pr) * 32 + rr;
                         float h[4];
 #pragma unroll
                         for (int qq = 0; qq < 4; ++qq)
                             h[qq] = silu_f(acc[2 * pr][j][4 * g + qq]) * acc[2 * pr + 1][j][4 * g + qq];
-                        *(uint2*)(crow + n) =
-                            make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
-                    }
-                } else {
-#pragma unroll
-                    for (int i = 0; i < G_WRB; ++i) {
-                        const int64_t n = wbase + (wr * G_WRB + i) * 32 + rr;
-                        if (n >= w.Nout) continue;
-                        *(uint2*)(crow + n) =
-                            make_uint2(pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]),
-                                       pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]));
+                        put(row, (wr * G_WRB / 2 + pr) * 32 + rr, h[0], h[1], h[2], h[3]);
                     }
                 }
             }
+        }
+        __syncthreads();
+        flush_rows(0, (int)mc);
+    } else {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            if (half == 1) __syncthreads();  // the first half's rows are stored
+            if constexpr (NB > 0) {
+                if (tg == half) {
+#pragma unroll
+                    for (int j = 0; j < NB; ++j) {
+                        const int row = j * 32 + (lane & 31);
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const int rr = 8 * g + 4 * (lane >> 5);
+#pragma unroll
+                            for (int i = 0; i < G_WRB; ++i)
+                                put(row, (wr * G_WRB + i) * 32 + rr, acc[i][j][4 * g],
+                                    acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+            const int nrows = (int)(mc - half * 160 < 160 ? mc - half * 160 : 160);
+            if (nrows > 0) flush_rows(half * 160, nrows);
         }
     }
 }
@@ -349,7 +387,9 @@ template <int MODE, int BK, int NS>
 __global__ void __launch_bounds__(G_THREADS, 1) ffn_gemm_bf16_kernel(GemmParamsV2 p) {
     WorkV2 w;
     if (!decode_v2<2>(p, MODE, w)) return;
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * (G_WR + G_TR) * BK + 512];
+    constexpr int STAGES_EL = NS * (G_WR + G_TR) * BK + 512;
+    constexpr int EPI_EL = MODE == 0 ? G_TR * (128 + 8) : 160 * (256 + 8);
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES_EL > EPI_EL ? STAGES_EL : EPI_EL];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wr = wave % G_WRG, tg = wave / G_WRG;
     const int64_t mc = w.M - w.m0 < G_TR ? w.M - w.m0 : G_TR;

@@ -3,31 +3,37 @@
 //
 // DeepSeek-V3 report reading guide (xyznot.com/de), "Kernideen", FP8 bullet:
 // E4M3 operands with 1x128 activation tiles and 128x128 weight blocks, and the
-// partial sums moved to FP32 every N_c = 128 accumulation steps.  Here: every
-// 128-wide contraction block k_b gives a partial P_b = sum_{k in k_b} qx*qw
-// from two v_mfma_f32_32x32x64_f8f6f4 (fresh fp32 accumulator), and the running
-// fp32 accumulator takes acc += P_b * (s_x[row, k_b] * s_w[block, k_b]) on the
-// VALU -- the block scales are arbitrary fp32 values (amax/448), which the
+// partial sums moved to FP32 every N_c = 128 accumulation steps.  Here every
+// 128-wide contraction block k_b contributes P_b = sum_{k in k_b} qx*qw from
+// two v_mfma_f32_32x32x64_f8f6f4, scaled by s_x[row, k_b] * s_w[block, k_b] in
+// fp32 -- the block scales are arbitrary fp32 values (amax/448), which the
 // hardware's power-of-two block scales cannot express.
 // gate/up: h = silu(a) * b is quantised in the epilogue per 1x128 tile: a
 // workgroup computes exactly 128 h columns (one tile) for each of its rows, so
 // the tile amax is a reduction over the workgroup's 4 weight-row waves.
 //
-// Tiles: 256 weight rows x up to 256 token rows, 8 wavefronts (wg = wave%4
-// owns 64 weight rows = two 32-row blocks, tg = wave/4 owns 128 token rows =
-// four blocks).  K step 128 (one scale block), two LDS stages of 32 KB weight
-// codes + 32 KB token codes + 1 KB token scales, copied global -> LDS directly.
-// LDS rows are 64 bytes (64 codes) in sub-tiles with the same chunk swizzle
-// as the bf16 kernel; weights are pre-packed in that order.
+// Tiles: 256 weight rows x up to 320 token rows -- one weight panel against
+// all rows of an expert, as in the bf16 kernel -- with 8 wavefronts (wg =
+// wave%4 owns 64 weight rows = two 32-row blocks, tg = wave/4 owns 160 token
+// rows = five blocks).  K step 128 = one scale block; two LDS stages of
+// 32 KB weight codes + 40 KB token codes + 1.25 KB token scales, copied
+// global -> LDS directly.  LDS rows are 128 bytes (the 128 codes of a K step)
+// with the bf16 kernel's chunk swizzle; weights are pre-packed in that order.
+//
+// Promotion in place: with sc_b = s_x[row, b] * s_w[block, b] the accumulator
+// holds R_b = S_b / sc_b, i.e. R_b = R_{b-1} * (sc_{b-1} / sc_b) + P_b, where the
+// MFMAs add P_b directly into R.  The result is S = R_last * sc_last.  A zero
+// scale (an all-zero tile or block, whose codes are all zero, so P_b = 0)
+// keeps the previous scale.  This keeps one register set per output block
+// (no separate partials), which is what lets a wave hold 5 token blocks.
 #include "gemm_common.h"
 
 namespace moe {
 
-constexpr int F8_TR = 256;                 // token rows per tile
-constexpr int F8_BK = 128;                 // contraction step = scale block
+constexpr int F8_TR = 320;                 // token rows per tile
+constexpr int F8_BK = 128;                 // contraction step = scale block = LDS row (bytes)
 constexpr int F8_WAVES = 8;
 constexpr int F8_THREADS = 64 * F8_WAVES;
-constexpr int F8_SUB = 64;                 // codes per LDS row (one k-half)
 constexpr int F8_A = G_WR_PACK * F8_BK;    // bytes per stage: weight codes
 constexpr int F8_X = F8_TR * F8_BK;        // token codes
 constexpr int F8_S = F8_TR * 4;            // token scales
@@ -44,35 +50,35 @@ struct Fp8Params {
 };
 
 // Pack FP8 weight codes [n_mats][rows][K] into the kernel's LDS image order:
-// out[mat][wt][kc][slot] (16-byte chunks), kc = 64-wide contraction block,
-// slot = r*4 + pc holding logical chunk sub_chunk(r, pc) of packed row r.
+// out[mat][wt][kt][slot] (16-byte chunks), kt = 128-wide contraction step,
+// slot = r*8 + pc holding logical chunk sub_chunk8(r, pc) of packed row r.
 template <int MODE>
 __global__ void __launch_bounds__(256) pack_weights_fp8_kernel(const uint4* __restrict__ w,
                                                                uint4* __restrict__ out,
                                                                int64_t n_mats, int64_t Nout,
                                                                int64_t K, int64_t ntn) {
-    const int64_t nkc = K / F8_SUB;
-    const int64_t per_mat = ntn * nkc * G_WR_PACK * 4;
+    const int64_t nkt = K / F8_BK;
+    const int64_t per_mat = ntn * nkt * G_WR_PACK * 8;
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n_mats * per_mat) return;
     const int64_t mat = i / per_mat;
     int64_t rem = i % per_mat;
-    const int64_t wt = rem / (nkc * G_WR_PACK * 4);
-    rem %= nkc * G_WR_PACK * 4;
-    const int64_t kc = rem / (G_WR_PACK * 4);
-    const int slot = (int)(rem % (G_WR_PACK * 4));
-    const int r = slot >> 2, c = sub_chunk(r, slot & 3);
+    const int64_t wt = rem / (nkt * G_WR_PACK * 8);
+    rem %= nkt * G_WR_PACK * 8;
+    const int64_t kt = rem / (G_WR_PACK * 8);
+    const int slot = (int)(rem % (G_WR_PACK * 8));
+    const int r = slot >> 3, c = sub_chunk8(r, slot & 7);
     const int64_t src = packed_row_source<MODE>(wt, r, Nout);
     const int64_t rows = MODE == 0 ? 2 * Nout : Nout;
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (src >= 0) v = w[((mat * rows + src) * K + kc * F8_SUB + c * 16) / 16];
+    if (src >= 0) v = w[((mat * rows + src) * K + kt * F8_BK + c * 16) / 16];
     out[i] = v;
 }
 
+// 32 codes of one 128-byte LDS row for k-half q: logical chunks 4q + 2*(lane/32), +1
 __device__ __forceinline__ i32x8_t ld_frag32(const uint8_t* rowp, int r, int c0) {
-    // 32 codes = logical chunks c0, c0+1 of one 64-byte LDS row
-    const uint4 lo = *(const uint4*)(rowp + sub_chunk(r, c0) * 16);
-    const uint4 hi = *(const uint4*)(rowp + sub_chunk(r, c0 + 1) * 16);
+    const uint4 lo = *(const uint4*)(rowp + sub_chunk8(r, c0) * 16);
+    const uint4 hi = *(const uint4*)(rowp + sub_chunk8(r, c0 + 1) * 16);
     i32x8_t v;
     v[0] = (int)lo.x; v[1] = (int)lo.y; v[2] = (int)lo.z; v[3] = (int)lo.w;
     v[4] = (int)hi.x; v[5] = (int)hi.y; v[6] = (int)hi.z; v[7] = (int)hi.w;
@@ -83,7 +89,8 @@ template <int MODE, int NB>
 __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& w,
                                               uint8_t* smem) {
     constexpr int NA = F8_A / 1024, NX = F8_X / 1024;  // 1 KB copies per stage
-    constexpr int PA = NA / F8_WAVES, PX = NX / F8_WAVES;
+    constexpr int PA = NA / F8_WAVES, PX = (NX + F8_WAVES - 1) / F8_WAVES;
+    constexpr int NSC = F8_TR / 64;                      // dword copies for the scales
     constexpr int NBB = NB > 0 ? NB : 1;
 
     const int lane = threadIdx.x & 63;
@@ -104,21 +111,18 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
     const uint32_t woff = lane * 16;
     const char* xbase = w.X + w.m0 * K;
 
-    // token code copies: block b = 16 rows (rb = b/2) of k-half q = b%2; the
-    // blocks with real rows are the prefix b < nxe
-    const int nxe = 2 * (int)((mc + 15) / 16);
-    int cnt = PA + (wave < F8_TR / 64 ? 1 : 0);  // + one scale copy for waves 0..3
+    // token code copies: block b = 8 rows (one 128-byte line each); the blocks
+    // holding real rows are the prefix b < nxe
+    const int nxe = (int)((mc + 7) / 8);
     uint32_t xoff[PX];
 #pragma unroll
     for (int j = 0; j < PX; ++j) {
         const int b = wave + F8_WAVES * j;
-        if (b < nxe) ++cnt;
-        const int q = b & 1, rb = b >> 1;
-        const int r = rb * 16 + (lane >> 2), c = sub_chunk(r, lane & 3);
+        const int r = b * 8 + (lane >> 3), c = sub_chunk8(r, lane & 7);
         const int64_t tr = r < mc ? r : mc - 1;
-        xoff[j] = (uint32_t)(tr * K + q * F8_SUB + c * 16);
+        xoff[j] = (uint32_t)(tr * K + c * 16);
     }
-    // token scale copies (dwords): wave s < 4 copies rows s*64 .. +63
+    // token scale copies (dwords): wave s < NSC copies rows s*64 .. +63
     const int64_t srow = wave * 64 + lane < mc ? wave * 64 + lane : mc - 1;
     const float* ssrc0 = xs + srow * nkb;
 
@@ -140,22 +144,23 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
             const int b = wave + F8_WAVES * j;
             if (b < nxe)
                 __builtin_amdgcn_global_load_lds((const void*)(xsrc + xoff[j]),
-                                                 to_lds(Xs + (b & 1) * (F8_TR * F8_SUB) +
-                                                        (b >> 1) * 1024),
-                                                 16, 0, 0);
+                                                 to_lds(Xs + b * 1024), 16, 0, 0);
         }
-        if (wave < F8_TR / 64)
+        if (wave < NSC)
             __builtin_amdgcn_global_load_lds((const void*)(ssrc0 + kt), to_lds(Ss + wave * 256),
                                              4, 0, 0);
     };
 
     f32x16_t acc[2][NBB];
+    float cur[2][NBB];  // the scale the accumulator is currently expressed in
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < NBB; ++j)
+        for (int j = 0; j < NBB; ++j) {
+            cur[i][j] = 1.0f;
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+        }
 
     // weight-scale block of each of this wave's two 32-row blocks
     int64_t wblk[2];
@@ -173,6 +178,7 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
         __syncthreads();  // stage kt landed for every wave; stage kt-1 is free
         if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
         if constexpr (NB > 0) {
+            __builtin_amdgcn_iglp_opt(1);
             const uint8_t* As = stage(kt & 1);
             const uint8_t* Xs = As + F8_A;
             const float* Ss = (const float*)(Xs + F8_X);
@@ -185,49 +191,46 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
                     const int r = (wg * 2 + i) * 32 + (lane & 31);
-                    af[q][i] = ld_frag32(As + q * (G_WR_PACK * F8_SUB) + r * F8_SUB, r,
-                                         2 * (lane >> 5));
+                    af[q][i] = ld_frag32(As + r * F8_BK, r, 4 * q + 2 * (lane >> 5));
                 }
-            // partials of token block j are promoted while the MFMAs of block
-            // j+1 run: two sets of partial registers, used alternately
-            f32x16_t pp[2][2];
-            float sxv[2];
-            auto mma = [&](int j, int buf) {
-                const int r = tg * 128 + j * 32 + (lane & 31);
-                const i32x8_t x0 = ld_frag32(Xs + r * F8_SUB, r, 2 * (lane >> 5));
-                const i32x8_t x1 = ld_frag32(Xs + F8_TR * F8_SUB + r * F8_SUB, r, 2 * (lane >> 5));
-                sxv[buf] = Ss[r];
-                const f32x16_t z = {};
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    pp[buf][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[0][i], x0, z, 0,
-                                                                                 0, 0, 0, 0, 0);
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    pp[buf][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        af[1][i], x1, pp[buf][i], 0, 0, 0, 0, 0, 0);
-            };
-            mma(0, 0);
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
-                if (j + 1 < NB) mma(j + 1, (j + 1) & 1);
+                const int r = tg * 160 + j * 32 + (lane & 31);
+                const i32x8_t x0 = ld_frag32(Xs + r * F8_BK, r, 2 * (lane >> 5));
+                const i32x8_t x1 = ld_frag32(Xs + r * F8_BK, r, 4 + 2 * (lane >> 5));
+                const float sx = Ss[r];
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
-                    const float sc = sw[i] * sxv[j & 1];
+                    const float sc = sw[i] * sx;
+                    const float nw = sc == 0.0f ? cur[i][j] : sc;
+                    const float ratio = cur[i][j] / nw;
+                    cur[i][j] = nw;
 #pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        acc[i][j][v] = __builtin_fmaf(pp[j & 1][i][v], sc, acc[i][j][v]);
+                    for (int v = 0; v < 16; ++v) acc[i][j][v] *= ratio;
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[0][i], x0, acc[i][j],
+                                                                                0, 0, 0, 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[1][i], x1, acc[i][j],
+                                                                                0, 0, 0, 0, 0, 0);
                 }
             }
         }
     }
+    // back to absolute values
+    if constexpr (NB > 0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] *= cur[i][j];
+    }
 
     // epilogue.  32x32 accumulator layout: lane l holds column (token) l%32 and
     // rows (weight rows) 8*(v/4) + 4*(l/32) + v%4, v = 0..15.
+    __syncthreads();  // every wave is done with the stage buffers
     if (MODE == 0) {
         // h = silu(a) * b for the tile's 128 columns, then 1x128 quantisation:
         // amax over the 4 weight-row waves through LDS
-        __syncthreads();  // every wave is done with the stage buffers
         float* red = (float*)smem;  // [F8_TR rows][4 waves]
         float hv[NBB][16];
 #pragma unroll
@@ -239,7 +242,7 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
                 m = fmaxf(m, fabsf(hv[j][v]));
             }
             m = fmaxf(m, __shfl_xor(m, 32, 64));
-            if (NB > 0 && lane < 32) red[(tg * 128 + j * 32 + lane) * 4 + wg] = m;
+            if (NB > 0 && lane < 32) red[(tg * 160 + j * 32 + lane) * 4 + wg] = m;
         }
         __syncthreads();
         if constexpr (NB > 0) {
@@ -248,7 +251,7 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
             const int64_t ntile = w.Nout / 128;
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
-                const int rr = tg * 128 + j * 32 + (lane & 31);
+                const int rr = tg * 160 + j * 32 + (lane & 31);
                 const int64_t t = w.m0 + rr;
                 if (t >= w.M) continue;
                 const float4 mm = *(const float4*)(red + rr * 4);
@@ -266,25 +269,40 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
                 if (wg == 0 && lane < 32) hsc[row * ntile + w.wt] = scale;
             }
         }
-    } else if constexpr (NB > 0) {
-        uint16_t* y = (uint16_t*)(shared ? P.g.C_s : P.g.C_r);
+    } else {
+        // y (bf16) through LDS in two token halves, stored as 16-byte row chunks
+        constexpr int OSTR = 256 + 8;  // padded row (elements)
+        uint16_t* ot = (uint16_t*)smem;
+        uint16_t* y = (uint16_t*)(shared ? P.g.C_s : P.g.C_r) + w.rowbase * w.Nout;
         const int64_t wbase = w.wt * 256;
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const int64_t t = w.m0 + tg * 128 + j * 32 + (lane & 31);
-            if (t >= w.M) continue;
-            uint16_t* crow = y + (w.rowbase + t) * w.Nout;
+        for (int half = 0; half < 2; ++half) {
+            if (half == 1) __syncthreads();
+            if constexpr (NB > 0) {
+                if (tg == half) {
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int rr = 8 * g4 + 4 * (lane >> 5);
+                    for (int j = 0; j < NB; ++j) {
+                        const int row = j * 32 + (lane & 31);
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int64_t n = wbase + (wg * 2 + i) * 32 + rr;
-                    if (n >= w.Nout) continue;
-                    *(uint2*)(crow + n) =
-                        make_uint2(pack_bf16x2(acc[i][j][4 * g4], acc[i][j][4 * g4 + 1]),
-                                   pack_bf16x2(acc[i][j][4 * g4 + 2], acc[i][j][4 * g4 + 3]));
+                        for (int g4 = 0; g4 < 4; ++g4) {
+                            const int rr = 8 * g4 + 4 * (lane >> 5);
+#pragma unroll
+                            for (int i = 0; i < 2; ++i)
+                                *(uint2*)(ot + row * OSTR + (wg * 2 + i) * 32 + rr) = make_uint2(
+                                    pack_bf16x2(acc[i][j][4 * g4], acc[i][j][4 * g4 + 1]),
+                                    pack_bf16x2(acc[i][j][4 * g4 + 2], acc[i][j][4 * g4 + 3]));
+                        }
+                    }
                 }
+            }
+            __syncthreads();
+            const int nrows = (int)(mc - half * 160 < 160 ? mc - half * 160 : 160);
+            for (int q = threadIdx.x; q < nrows * 32; q += F8_THREADS) {
+                const int rr = q / 32, ch = q % 32;
+                const int64_t col = wbase + ch * 8;
+                if (col < w.Nout)
+                    *(uint4*)(y + (w.m0 + half * 160 + rr) * w.Nout + col) =
+                        *(const uint4*)(ot + rr * OSTR + ch * 8);
             }
         }
     }
@@ -298,10 +316,11 @@ __global__ void __launch_bounds__(F8_THREADS, 1) ffn_gemm_fp8_kernel(Fp8Params P
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wg = wave & 3, tg = wave >> 2;
     const int64_t mc = w.M - w.m0 < F8_TR ? w.M - w.m0 : F8_TR;
-    int64_t nb = (mc - tg * 128 + 31) / 32;
-    nb = nb < 0 ? 0 : (nb > 4 ? 4 : nb);
+    int64_t nb = (mc - tg * 160 + 31) / 32;
+    nb = nb < 0 ? 0 : (nb > 5 ? 5 : nb);
     if (MODE == 1 && w.wt * 256 + wg * 64 >= w.Nout) nb = 0;
     switch (nb) {
+        case 5: gemm_fp8_body<MODE, 5>(P, w, smem); break;
         case 4: gemm_fp8_body<MODE, 4>(P, w, smem); break;
         case 3: gemm_fp8_body<MODE, 3>(P, w, smem); break;
         case 2: gemm_fp8_body<MODE, 2>(P, w, smem); break;
@@ -328,7 +347,7 @@ hipError_t launch_pack_weights_fp8(const moe_cfg& c, int which, const void* w, v
     const bool up = which == 0 || which == 2;
     const int64_t Nout = up ? I : c.hidden, K = up ? c.hidden : I;
     const int64_t ntn = up ? cdiv(I, 128) : cdiv(c.hidden, 256);
-    const int64_t total = n * ntn * (K / F8_SUB) * G_WR_PACK * 4;
+    const int64_t total = n * ntn * (K / F8_BK) * G_WR_PACK * 8;
     if (total == 0) return hipSuccess;
     const unsigned blocks = (unsigned)cdiv(total, 256);
     if (up)
