@@ -87,6 +87,13 @@ int check_ffn_shape(const char* fn, const moe_cfg* c) {
                         "%s: bf16/FP8 expert GEMMs need hidden, inter, inter_shared %% 128 == 0",
                         fn);
     }
+    if (c->gemm_dtype == MOE_FP8_E4M3) {
+        const int64_t kmax = 128 * (int64_t)moe::FP8_MAX_KB;
+        if (c->hidden > kmax || c->inter > kmax || c->inter_shared > kmax)
+            return fail(MOE_ERR_UNSUPPORTED,
+                        "%s: FP8 expert GEMMs need hidden, inter, inter_shared <= %lld", fn,
+                        (long long)kmax);
+    }
     return MOE_OK;
 }
 

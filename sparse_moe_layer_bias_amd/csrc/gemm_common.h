@@ -95,6 +95,40 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ lds_void* to_lds(const void* p) { return (lds_void*)p; }
 
+// Raw buffer descriptor over [base, base + bytes) (wave-uniform, in SGPRs):
+// loads at offsets past the end return zero.  bytes must stay below 2^32.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, int64_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    i32x4_t r;
+    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)) & 0xffff;  // stride 0
+    r.z = __builtin_amdgcn_readfirstlane((int)(uint32_t)bytes);
+    r.w = 0x00020000;  // raw 32-bit data format
+    return r;
+}
+
+// Global -> LDS copy through a buffer descriptor: lane l copies SIZE (16 or 4)
+// bytes from rsrc + voff + soff to LDS address lds + l*SIZE.  Written as
+// inline asm on purpose: for the compiler's own LDS-DMA instructions its
+// waitcnt pass makes every later LDS read wait for all copies in flight
+// (vmcnt(0)), which would serialise the next stage's copies with the MFMAs of
+// the current one.  The caller orders copies and reads itself (s_waitcnt
+// vmcnt + barrier).  The s_nop covers the M0-write -> LDS-DMA hazard.
+template <int SIZE>
+__device__ __forceinline__ void dma_to_lds(i32x4_t rsrc, const void* lds, uint32_t voff,
+                                           uint32_t soff) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)lds;
+    if constexpr (SIZE == 16)
+        asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc),
+                     "s"(soff), "{m0}"(m0)
+                     : "memory");
+    else
+        asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc),
+                     "s"(soff), "{m0}"(m0)
+                     : "memory");
+}
+
 // physical chunk of logical chunk c in row r of a 64-byte-row sub-tile (an
 // involution).  A ds_read_b128 is served 16 lanes (256 bytes, the 64 banks)
 // at a time; those lanes read one chunk of 16 consecutive rows, i.e. 4 rows

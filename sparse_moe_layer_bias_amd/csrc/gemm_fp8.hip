@@ -5,9 +5,10 @@
 // E4M3 operands with 1x128 activation tiles and 128x128 weight blocks, and the
 // partial sums moved to FP32 every N_c = 128 accumulation steps.  Here every
 // 128-wide contraction block k_b contributes P_b = sum_{k in k_b} qx*qw from
-// two v_mfma_f32_32x32x64_f8f6f4, scaled by s_x[row, k_b] * s_w[block, k_b] in
-// fp32 -- the block scales are arbitrary fp32 values (amax/448), which the
-// hardware's power-of-two block scales cannot express.
+// two v_mfma_scale_f32_32x32x64_f8f6f4, scaled by s_x[row, k_b] *
+// s_w[block, k_b] in fp32.  The block scales are arbitrary fp32 values
+// (amax/448): the MFMA's power-of-two block-scale operands take their
+// exponents and the VALU their significands (promotion, below).
 // gate/up: h = silu(a) * b is quantised in the epilogue per 1x128 tile: a
 // workgroup computes exactly 128 h columns (one tile) for each of its rows, so
 // the tile amax is a reduction over the workgroup's 4 weight-row waves.
@@ -15,28 +16,36 @@
 // Tiles: 256 weight rows x up to 320 token rows -- one weight panel against
 // all rows of an expert, as in the bf16 kernel -- with 8 wavefronts (wg =
 // wave%4 owns 64 weight rows = two 32-row blocks, tg = wave/4 owns 160 token
-// rows = five blocks).  K step 128 = one scale block; two LDS stages of
-// 32 KB weight codes + 40 KB token codes + 1.25 KB token scales, copied
-// global -> LDS directly.  LDS rows are 128 bytes (the 128 codes of a K step)
-// with the bf16 kernel's chunk swizzle; weights are pre-packed in that order.
+// rows = five blocks).  The contraction runs in steps of 128 (one scale
+// block) through two LDS stages of 32 KB weight codes + 40 KB token codes +
+// 1.25 KB token scales, copied global -> LDS directly.  LDS rows are 128 bytes
+// with the chunk swizzle c ^ ((r >> 1) & 7); the weights are pre-packed in that
+// order.
 //
-// Promotion in place: with sc_b = s_x[row, b] * s_w[block, b] the accumulator
-// holds R_b = S_b / sc_b, i.e. R_b = R_{b-1} * (sc_{b-1} / sc_b) + P_b, where the
-// MFMAs add P_b directly into R.  The result is S = R_last * sc_last.  A zero
-// scale (an all-zero tile or block, whose codes are all zero, so P_b = 0)
-// keeps the previous scale.  This keeps one register set per output block
-// (no separate partials), which is what lets a wave hold 5 token blocks.
+// Promotion: with the K block's scale split as sc_b = s_x * s_w =
+// 2^(E_b) * m_b (E_b from the E8M0 codes of s_x and s_w, m_b the product of
+// their significands, in [1, 4)), the accumulator holds R_b = S_b / m_b:
+// R_b = R_{b-1} * (m_{b-1} / m_b) + 2^(E_b) * P_b.  The MFMA applies 2^(E_b)
+// through its block-scale operands and adds into R directly; the VALU only
+// rescales by the mantissa ratio, which stays within [1/4, 4], so no range is
+// lost whatever the spread of the block scales.  S = R_last * m_last.  A zero
+// scale (an all-zero tile or block: its codes are all zero) keeps the unit.
+// One register set per output block (no separate partials) lets a wave hold
+// five token blocks.
 #include "gemm_common.h"
 
 namespace moe {
 
 constexpr int F8_TR = 320;                 // token rows per tile
-constexpr int F8_BK = 128;                 // contraction step = scale block = LDS row (bytes)
+constexpr int F8_KB = 128;                 // scale block along the contraction
+constexpr int F8_BK = 128;                 // contraction step per stage = LDS row (bytes)
+constexpr int F8_NS = 2;                   // LDS stages
 constexpr int F8_WAVES = 8;
 constexpr int F8_THREADS = 64 * F8_WAVES;
 constexpr int F8_A = G_WR_PACK * F8_BK;    // bytes per stage: weight codes
 constexpr int F8_X = F8_TR * F8_BK;        // token codes
-constexpr int F8_S = F8_TR * 4;            // token scales
+constexpr int F8_S = F8_TR * 4;            // token scales of the step's scale block
+static_assert(F8_BK == F8_KB, "one scale block per step");
 constexpr int F8_STAGE = F8_A + F8_X + F8_S;
 
 struct Fp8Params {
@@ -75,14 +84,24 @@ __global__ void __launch_bounds__(256) pack_weights_fp8_kernel(const uint4* __re
     out[i] = v;
 }
 
-// 32 codes of one 128-byte LDS row for k-half q: logical chunks 4q + 2*(lane/32), +1
-__device__ __forceinline__ i32x8_t ld_frag32(const uint8_t* rowp, int r, int c0) {
-    const uint4 lo = *(const uint4*)(rowp + sub_chunk8(r, c0) * 16);
-    const uint4 hi = *(const uint4*)(rowp + sub_chunk8(r, c0 + 1) * 16);
+// The 32 codes of a 128-byte LDS row that lane half h (= lane/32) feeds the
+// 32x32x64 MFMA for the K half q: logical chunks 4q + 2h and 4q + 2h + 1
+__device__ __forceinline__ i32x8_t ld_frag32(const uint8_t* rowp, int r, int q, int h) {
+    const uint4 lo = *(const uint4*)(rowp + sub_chunk8(r, 4 * q + 2 * h) * 16);
+    const uint4 hi = *(const uint4*)(rowp + sub_chunk8(r, 4 * q + 2 * h + 1) * 16);
     i32x8_t v;
     v[0] = (int)lo.x; v[1] = (int)lo.y; v[2] = (int)lo.z; v[3] = (int)lo.w;
     v[4] = (int)hi.x; v[5] = (int)hi.y; v[6] = (int)hi.z; v[7] = (int)hi.w;
     return v;
+}
+
+// A non-negative scale s as m * 2^(e8 - 127): e8 is s's biased exponent (the
+// E8M0 code) and m in [1, 2) its significand; for s below 2^-126 (zero or
+// subnormal) e8 = 0 and m = s * 2^127 in [0, 2), exact.
+__device__ __forceinline__ void split_scale(float s, int& e8, float& m) {
+    const uint32_t b = __float_as_uint(s);
+    e8 = (int)(b >> 23);
+    m = e8 ? __uint_as_float((b & 0x7fffffu) | 0x3f800000u) : s * 0x1p127f;
 }
 
 template <int MODE, int NB>
@@ -92,14 +111,15 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
     constexpr int PA = NA / F8_WAVES, PX = (NX + F8_WAVES - 1) / F8_WAVES;
     constexpr int NSC = F8_TR / 64;                      // dword copies for the scales
     constexpr int NBB = NB > 0 ? NB : 1;
+    static_assert(NA % F8_WAVES == 0, "weight copies split evenly over the waves");
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wg = wave & 3, tg = wave >> 2;
     const int64_t K = w.K;
-    const int64_t nkb = K / F8_BK;
+    const int64_t nkb = K / F8_KB;  // scale blocks
+    const int nk = (int)(K / F8_BK);  // steps
     const int64_t mc = w.M - w.m0 < F8_TR ? w.M - w.m0 : F8_TR;
-    const int nk = (int)nkb;
     const bool shared = w.g >= P.g.N;
     const int64_t gi = shared ? 0 : w.g;
     const float* xs = (shared ? P.xs_s : P.xs_r) + (w.rowbase + w.m0) * nkb;
@@ -107,12 +127,17 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
     const int64_t wrows = MODE == 0 ? 2 * w.Nout : w.Nout;
     const int64_t wrb = wrows / 128;  // 128-row scale blocks per expert matrix
 
-    const char* wstage0 = w.W + w.wt * (int64_t)nk * F8_A;
-    const uint32_t woff = lane * 16;
+    // Copies go through buffer descriptors (base in SGPRs, 32-bit lane offsets,
+    // out-of-range lanes read as zero): the tile's weight panel, the expert's
+    // token rows and their scales.
+    const char* wpanel = w.W + w.wt * (int64_t)nk * F8_A;
     const char* xbase = w.X + w.m0 * K;
+    const i32x4_t rw = make_rsrc(wpanel, (int64_t)nk * F8_A);
+    const i32x4_t rx = make_rsrc(xbase, mc * K);
+    const i32x4_t rs = make_rsrc(xs, mc * nkb * 4);
 
-    // token code copies: block b = 8 rows (one 128-byte line each); the blocks
-    // holding real rows are the prefix b < nxe
+    // token code copies: block b = 8 rows (128-byte lines); the blocks holding
+    // real rows are the prefix b < nxe; rows past the last one repeat it
     const int nxe = (int)((mc + 7) / 8);
     uint32_t xoff[PX];
 #pragma unroll
@@ -124,35 +149,31 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
     }
     // token scale copies (dwords): wave s < NSC copies rows s*64 .. +63
     const int64_t srow = wave * 64 + lane < mc ? wave * 64 + lane : mc - 1;
-    const float* ssrc0 = xs + srow * nkb;
+    const uint32_t soff = (uint32_t)(srow * nkb * 4);
 
     auto stage = [&](int s) { return smem + s * F8_STAGE; };
+    // this wave's copies for step kt into buffer s: weight blocks, token
+    // blocks, then the token scales of the step's scale block
     auto issue = [&](int kt, int s) {
         uint8_t* As = stage(s);
         uint8_t* Xs = As + F8_A;
         uint8_t* Ss = Xs + F8_X;
-        const char* wsrc = wstage0 + (int64_t)kt * F8_A;
-        const char* xsrc = xbase + (int64_t)kt * F8_BK;
 #pragma unroll
-        for (int j = 0; j < PA; ++j) {
-            const int b = wave + F8_WAVES * j;
-            __builtin_amdgcn_global_load_lds((const void*)(wsrc + b * 1024 + woff),
-                                             to_lds(As + b * 1024), 16, 0, 0);
+        for (int c = 0; c < PA; ++c) {
+            const int b = wave + F8_WAVES * c;
+            dma_to_lds<16>(rw, As + b * 1024, lane * 16, kt * F8_A + b * 1024);
         }
 #pragma unroll
         for (int j = 0; j < PX; ++j) {
             const int b = wave + F8_WAVES * j;
-            if (b < nxe)
-                __builtin_amdgcn_global_load_lds((const void*)(xsrc + xoff[j]),
-                                                 to_lds(Xs + b * 1024), 16, 0, 0);
+            if (b < nxe) dma_to_lds<16>(rx, Xs + b * 1024, xoff[j], kt * F8_BK);
         }
-        if (wave < NSC)
-            __builtin_amdgcn_global_load_lds((const void*)(ssrc0 + kt), to_lds(Ss + wave * 256),
-                                             4, 0, 0);
+        if (wave < NSC) dma_to_lds<4>(rs, Ss + wave * 256, soff, kt * 4);
     };
 
     f32x16_t acc[2][NBB];
-    float cur[2][NBB];  // the scale the accumulator is currently expressed in
+    float cur[2][NBB];  // the significand unit the accumulator is expressed in
+    int ew[2], ex[NBB];  // E8M0 codes of the current scale block (weights, tokens)
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -162,14 +183,19 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
         }
 
-    // weight-scale block of each of this wave's two 32-row blocks
-    int64_t wblk[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        if (MODE == 0)
-            wblk[i] = (i ? w.Nout / 128 : 0) + w.wt;  // W1 rows, then the W3 rows
-        else
-            wblk[i] = w.wt * 2 + (wg >> 1);
+    // The weight block scales of the tile's two 128-row blocks for every K
+    // block, staged in LDS once per tile.  (A global load per step would make
+    // the step wait for the next stage's copies as well: vmcnt counts both.)
+    // gate/up: block 0 = the W1 rows, block 1 = the W3 rows; down: the tile's
+    // rows 0..127 and 128..255 (a wave's 64 rows lie in block wg/2).
+    float* swl = (float*)(smem + F8_NS * F8_STAGE);
+    {
+        const int64_t b0 = MODE == 0 ? w.wt : 2 * w.wt;
+        const int64_t b1 = MODE == 0 ? w.Nout / 128 + w.wt : 2 * w.wt + 1;
+        for (int t = threadIdx.x; t < 2 * nkb; t += F8_THREADS) {
+            const int64_t blk = t < nkb ? b0 : b1;
+            swl[t] = blk < wrb ? wsc[(gi * wrb + blk) * nkb + (t < nkb ? t : t - nkb)] : 0.0f;
+        }
     }
 
     issue(0, 0);
@@ -178,39 +204,43 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
         __syncthreads();  // stage kt landed for every wave; stage kt-1 is free
         if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
         if constexpr (NB > 0) {
-            __builtin_amdgcn_iglp_opt(1);
             const uint8_t* As = stage(kt & 1);
             const uint8_t* Xs = As + F8_A;
             const float* Ss = (const float*)(Xs + F8_X);
-            float sw[2];
+            const int h = lane >> 5;
+            // the two 64-wide K halves one after the other; the rescale to this
+            // block's unit comes before the first half's MFMA
 #pragma unroll
-            for (int i = 0; i < 2; ++i) sw[i] = wsc[(gi * wrb + wblk[i]) * nkb + kt];
-            i32x8_t af[2][2];
-#pragma unroll
-            for (int q = 0; q < 2; ++q)
+            for (int q = 0; q < 2; ++q) {
+                i32x8_t af[2];
+                float mw[2];
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
                     const int r = (wg * 2 + i) * 32 + (lane & 31);
-                    af[q][i] = ld_frag32(As + r * F8_BK, r, 4 * q + 2 * (lane >> 5));
+                    af[i] = ld_frag32(As + r * F8_BK, r, q, h);
+                    if (q == 0) split_scale(swl[(MODE == 0 ? i : wg >> 1) * nkb + kt], ew[i], mw[i]);
                 }
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                const int r = tg * 160 + j * 32 + (lane & 31);
-                const i32x8_t x0 = ld_frag32(Xs + r * F8_BK, r, 2 * (lane >> 5));
-                const i32x8_t x1 = ld_frag32(Xs + r * F8_BK, r, 4 + 2 * (lane >> 5));
-                const float sx = Ss[r];
+                for (int j = 0; j < NB; ++j) {
+                    const int r = tg * 160 + j * 32 + (lane & 31);
+                    const i32x8_t xf = ld_frag32(Xs + r * F8_BK, r, q, h);
+                    if (q == 0) {
+                        float mx;
+                        split_scale(Ss[r], ex[j], mx);
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const float sc = sw[i] * sx;
-                    const float nw = sc == 0.0f ? cur[i][j] : sc;
-                    const float ratio = cur[i][j] / nw;
-                    cur[i][j] = nw;
+                        for (int i = 0; i < 2; ++i) {
+                            const float mn = mw[i] * mx;
+                            const float nw = mn == 0.0f ? cur[i][j] : mn;
+                            const float ratio = cur[i][j] * __builtin_amdgcn_rcpf(nw);
+                            cur[i][j] = nw;
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) acc[i][j][v] *= ratio;
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[0][i], x0, acc[i][j],
-                                                                                0, 0, 0, 0, 0, 0);
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[1][i], x1, acc[i][j],
-                                                                                0, 0, 0, 0, 0, 0);
+                            for (int v = 0; v < 16; ++v) acc[i][j][v] *= ratio;
+                        }
+                    }
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            af[i], xf, acc[i][j], 0, 0, 0, ew[i], 0, ex[j]);
                 }
             }
         }
@@ -312,7 +342,7 @@ template <int MODE>
 __global__ void __launch_bounds__(F8_THREADS, 1) ffn_gemm_fp8_kernel(Fp8Params P) {
     WorkV2 w;
     if (!decode_v2<1>(P.g, MODE, w)) return;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * F8_STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[F8_NS * F8_STAGE + 2 * 4 * FP8_MAX_KB];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wg = wave & 3, tg = wave >> 2;
     const int64_t mc = w.M - w.m0 < F8_TR ? w.M - w.m0 : F8_TR;
@@ -347,7 +377,7 @@ hipError_t launch_pack_weights_fp8(const moe_cfg& c, int which, const void* w, v
     const bool up = which == 0 || which == 2;
     const int64_t Nout = up ? I : c.hidden, K = up ? c.hidden : I;
     const int64_t ntn = up ? cdiv(I, 128) : cdiv(c.hidden, 256);
-    const int64_t total = n * ntn * (K / F8_BK) * G_WR_PACK * 8;
+    const int64_t total = n * ntn * (K / F8_BK) * G_WR_PACK * (F8_BK / 16);
     if (total == 0) return hipSuccess;
     const unsigned blocks = (unsigned)cdiv(total, 256);
     if (up)

@@ -38,6 +38,9 @@ struct FfnArgs {
     void* y_shared;
 };
 size_t ffn_workspace_bytes(const moe_cfg& c);
+// FP8 expert GEMM: contraction blocks of 128 per tile whose weight scales it
+// stages in LDS, i.e. hidden, inter and inter_shared <= 128 * FP8_MAX_KB
+constexpr int FP8_MAX_KB = 512;
 // which: 0 = routed W13, 1 = routed W2, 2 = shared W13, 3 = shared W2
 size_t packed_weight_bytes(const moe_cfg& c, int which);
 hipError_t launch_pack_weights(const moe_cfg& c, int which, const void* w, void* out,

@@ -108,6 +108,47 @@ def test_layer_parity_fp8_small(orc, name, over):
     assert_bits(moe_inputs.to_host(bias), ref["new_bias"], "bias after update")
 
 
+def test_fp8_block_scales_far_apart(orc):
+    """FP8 promotion with block scales that jump by 2^60 from one 128-wide K
+    block to the next, all-zero blocks (scale 0) in activations and weights,
+    and a block scale at the bottom of the normal fp32 range.  The exact
+    block sums scaled by s_x * s_w (oracle) must survive the kernel's
+    accumulation order."""
+    cfg = dict(moe_inputs.CONFIGS["mid_bf16"], T=160, fp8=True)
+    c = dict(cfg)
+    inp = moe_inputs.make_layer_inputs(c, 5, "cpu")
+    x, w13, w2 = inp["x"].float(), inp["w13"].float(), inp["w2"].float()
+    ws13, ws2 = inp["ws13"].float(), inp["ws2"].float()
+    d = c["d"]
+    # activations: K blocks of very different magnitude, per row pattern
+    x[:, 0:128] *= 2.0 ** 30
+    x[:, 128:256] *= 2.0 ** -30
+    x[::3, 256:384] = 0
+    x[1::4, 384:512] *= 2.0 ** -100
+    # weights: W1/W3 and W2 blocks scaled the other way, some all-zero blocks
+    for w in (w13, ws13):
+        w[..., 0:128] *= 2.0 ** -30
+        w[..., 128:256] *= 2.0 ** 30
+        w[..., :128, 256:384] = 0
+    for w in (w2, ws2):
+        w[..., :, 0:128] *= 2.0 ** 20
+        w[..., :128, 128:256] = 0
+    inp.update(x=x.to(torch.bfloat16), w13=w13.to(torch.bfloat16), w2=w2.to(torch.bfloat16),
+               ws13=ws13.to(torch.bfloat16), ws2=ws2.to(torch.bfloat16))
+    dev = {k: v.cuda() for k, v in inp.items()}
+    log("case fp8 far-apart block scales T=%d" % c["T"])
+    layer = MoeLayer(c, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"])
+    out = layer.forward(dev["x"], dev["centroids"], dev["bias"].clone())
+    torch.cuda.synchronize()
+    ref = orc.layer_forward(host_inputs(inp), c, residual=True)
+    assert np.all(np.isfinite(ref["y_perm"].astype(np.float64))), "oracle overflowed"
+    assert_bits(moe_inputs.to_host(layer.idx), ref["idx"], "idx")
+    assert_bits(moe_inputs.to_host(layer.x_perm), ref["x_q_perm"], "permuted codes")
+    assert_close_fp8(moe_inputs.to_host(layer.y_perm), ref["y_perm"], "y_perm")
+    assert_close_fp8(moe_inputs.to_host(layer.y_shared), ref["y_shared"], "y_shared")
+    assert_close_fp8(moe_inputs.to_host(out), ref["out"], "out")
+
+
 def test_layer_without_residual(orc):
     c, layer, out, bias, ref = _run_small("tiny_fp32", orc, residual=False)
     assert_close(moe_inputs.to_host(out), ref["out"], RTOL["f32"], "out (no residual)")
