@@ -329,10 +329,9 @@ __device__ __forceinline__ void gemm_bf16_body(const WorkV2& w, uint16_t* smem) 
         uint16_t* C = (uint16_t*)w.C;
         for (int q = threadIdx.x; q < nrows * CH; q += G_THREADS) {
             const int rr = q / CH, ch = q % CH;
-            const int64_t t = w.m0 + r0 + rr;
             const int64_t col = wbase + ch * 8;
             if (r0 + rr < mc && col < w.Nout)
-                *(uint4*)(C + t * w.Nout + col) = *(const uint4*)(ot + rr * OSTR + ch * 8);
+                *(uint4*)(C + (w.m0 + r0 + rr) * w.Nout + col) = *(const uint4*)(ot + rr * OSTR + ch * 8);
         }
     };
     if (MODE == 0) {
@@ -359,7 +358,7 @@ __device__ __forceinline__ void gemm_bf16_body(const WorkV2& w, uint16_t* smem) 
     } else {
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-            if (half == 1) __syncthreads();  // the first half's rows are stored
+            if (half == 1) lds_barrier();  // the first half's rows are read out of LDS
             if constexpr (NB > 0) {
                 if (tg == half) {
 #pragma unroll
@@ -376,7 +375,7 @@ __device__ __forceinline__ void gemm_bf16_body(const WorkV2& w, uint16_t* smem) 
                     }
                 }
             }
-            __syncthreads();
+            lds_barrier();
             const int nrows = (int)(mc - half * 160 < 160 ? mc - half * 160 : 160);
             if (nrows > 0) flush_rows(half * 160, nrows);
         }

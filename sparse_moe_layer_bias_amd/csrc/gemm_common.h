@@ -95,6 +95,14 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ lds_void* to_lds(const void* p) { return (lds_void*)p; }
 
+// Workgroup barrier for LDS reuse: waits for this wave's LDS (and scalar)
+// operations only.  __syncthreads also waits for the wave's global stores to
+// complete (its fence covers global memory), which an epilogue that stores
+// one part of a tile and then reuses the LDS for the next does not need.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Raw buffer descriptor over [base, base + bytes) (wave-uniform, in SGPRs):
 // loads at offsets past the end return zero.  bytes must stay below 2^32.
 typedef int i32x4_t __attribute__((ext_vector_type(4)));

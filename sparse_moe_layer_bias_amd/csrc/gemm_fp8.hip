@@ -260,8 +260,11 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
     __syncthreads();  // every wave is done with the stage buffers
     if (MODE == 0) {
         // h = silu(a) * b for the tile's 128 columns, then 1x128 quantisation:
-        // amax over the 4 weight-row waves through LDS
-        float* red = (float*)smem;  // [F8_TR rows][4 waves]
+        // the tile amax is reduced over the 4 weight-row waves through LDS;
+        // codes are staged in LDS and stored as whole 128-byte rows
+        float* red = (float*)smem;          // [F8_TR rows][4 waves]
+        constexpr int HST = 128 + 16;       // padded code row (bytes)
+        uint8_t* hcodes = smem + F8_TR * 16;  // [F8_TR rows][HST]
         float hv[NBB][16];
 #pragma unroll
         for (int j = 0; j < NBB; ++j) {
@@ -275,29 +278,33 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
             if (NB > 0 && lane < 32) red[(tg * 160 + j * 32 + lane) * 4 + wg] = m;
         }
         __syncthreads();
+        float* hsc = shared ? P.hs_s : P.hs_r;
+        const int64_t ntile = w.Nout / 128;
         if constexpr (NB > 0) {
-            uint8_t* hq = (uint8_t*)(shared ? P.g.C_s : P.g.C_r);
-            float* hsc = shared ? P.hs_s : P.hs_r;
-            const int64_t ntile = w.Nout / 128;
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 const int rr = tg * 160 + j * 32 + (lane & 31);
-                const int64_t t = w.m0 + rr;
-                if (t >= w.M) continue;
                 const float4 mm = *(const float4*)(red + rr * 4);
                 const float amax = fmaxf(fmaxf(mm.x, mm.y), fmaxf(mm.z, mm.w));
                 const float scale = amax / 448.0f;
-                const int64_t row = w.rowbase + t;
-                uint8_t* hrow = hq + row * w.Nout + w.wt * 128 + wg * 32;
+                // codes of h / scale, computed as h * (1 / scale): the quotient
+                // may differ from the division in its last bit
+                const float inv = scale > 0.0f ? 1.0f / scale : 0.0f;
+                float t[16];
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    uint32_t q = 0;
+                for (int v = 0; v < 16; ++v) t[v] = fminf(fmaxf(hv[j][v] * inv, -448.0f), 448.0f);
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) q |= quant_e4m3(hv[j][4 * g4 + u], scale) << (8 * u);
-                    *(uint32_t*)(hrow + 8 * g4 + 4 * (lane >> 5)) = q;
-                }
-                if (wg == 0 && lane < 32) hsc[row * ntile + w.wt] = scale;
+                for (int g4 = 0; g4 < 4; ++g4)
+                    *(uint32_t*)(hcodes + rr * HST + wg * 32 + 8 * g4 + 4 * (lane >> 5)) =
+                        e4m3_encode4(t[4 * g4], t[4 * g4 + 1], t[4 * g4 + 2], t[4 * g4 + 3]);
+                if (wg == 0 && lane < 32 && rr < mc) hsc[(w.rowbase + w.m0 + rr) * ntile + w.wt] = scale;
             }
+        }
+        __syncthreads();
+        uint8_t* hq = (uint8_t*)(shared ? P.g.C_s : P.g.C_r) + (w.rowbase + w.m0) * w.Nout + w.wt * 128;
+        for (int q = threadIdx.x; q < mc * 8; q += F8_THREADS) {
+            const int rr = q >> 3, ch = q & 7;
+            *(uint4*)(hq + rr * w.Nout + ch * 16) = *(const uint4*)(hcodes + rr * HST + ch * 16);
         }
     } else {
         // y (bf16) through LDS in two token halves, stored as 16-byte row chunks
@@ -307,7 +314,7 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
         const int64_t wbase = w.wt * 256;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-            if (half == 1) __syncthreads();
+            if (half == 1) lds_barrier();  // the first half is read out of LDS
             if constexpr (NB > 0) {
                 if (tg == half) {
 #pragma unroll
@@ -325,7 +332,7 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
                     }
                 }
             }
-            __syncthreads();
+            lds_barrier();
             const int nrows = (int)(mc - half * 160 < 160 ? mc - half * 160 : 160);
             for (int q = threadIdx.x; q < nrows * 32; q += F8_THREADS) {
                 const int rr = q / 32, ch = q % 32;

@@ -34,40 +34,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // ---------------------------------------------------------------- E4M3FN
 //
 // OCP E4M3FN: sign, 4 exponent bits (bias 7), 3 mantissa bits; largest finite
-// 448; smallest normal 2^-6; subnormals m * 2^-9.  Encoding of a value already
-// clamped to [-448, 448], nearest-even, done on the fp32 bit pattern with
-// integer operations only (no dependence on conversion instructions).
+// 448; smallest normal 2^-6; subnormals m * 2^-9.  Encoding of values already
+// clamped to [-448, 448] with gfx950's converter (v_cvt_pk_fp8_f32: OCP
+// E4M3, round to nearest even, subnormals kept, the sign kept on zero).
+__device__ __forceinline__ uint32_t e4m3_encode4(float a, float b, float c, float d) {
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+    return (uint32_t)r;
+}
 __device__ __forceinline__ uint32_t e4m3_encode(float v) {
-    uint32_t u = __float_as_uint(v);
-    uint32_t sign = (u >> 24) & 0x80u;
-    uint32_t a = u & 0x7fffffffu;          // |v| bits
-    uint32_t exp = a >> 23;                 // biased fp32 exponent
-    uint32_t code;
-    if (exp < 121) {                        // |v| < 2^-6: subnormal grid 2^-9
-        // q = rne(|v| * 2^9).  Below 2^-10 (fp32 exponent field < 117) the
-        // product is under one half (or exactly one half, a tie to even 0).
-        if (exp < 117) {
-            code = 0;
-        } else {
-            uint32_t mant = (a & 0x7fffffu) | 0x800000u;   // 24-bit significand
-            // |v| * 2^9 = mant * 2^(exp - 127 - 23 + 9) = mant >> (141 - exp)
-            uint32_t sh = 141 - exp;                         // 21..24
-            uint32_t q = mant >> sh;
-            uint32_t rem = mant & ((1u << sh) - 1u);
-            uint32_t half = 1u << (sh - 1);
-            if (rem > half || (rem == half && (q & 1u))) q += 1;
-            code = q;                       // 0..8 (8 == smallest normal, code 0x08)
-        }
-    } else {
-        // normal: keep 3 mantissa bits, round the dropped 20 bits
-        uint32_t e = exp - 120;             // E4M3 biased exponent (exp-127+7), >= 1
-        uint32_t mant = a & 0x7fffffu;
-        uint32_t q = mant >> 20;
-        uint32_t rem = mant & 0xfffffu;
-        if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) q += 1;
-        code = (e << 3) + q;                // a mantissa carry bumps the exponent
-    }
-    return sign | code;
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xffu;
 }
 
 __device__ __forceinline__ float e4m3_decode(uint32_t c) {
