@@ -28,47 +28,37 @@ namespace moe {
 // per-element bound check, the other instance pads the last stage with zeros
 // (an fma with two zero operands leaves a chain unchanged: the chain starts
 // at +0 and never holds -0).
-constexpr int RL_TN = 64, RL_BK = 32;
+constexpr int RL_TN = 64, RL_BK = 32, RL_KG = 2;
+static_assert(RL_TN * RL_BK / 256 == 8, "each thread copies 8 centroid values per stage");
 
-template <int TY>
+// one stage's global loads, held in registers until the stage's FMAs are done
+// (x stays in its input type: converting at load time would make the wait
+// for the loads come right after issuing them)
+template <typename XT, int TY>
 struct RlRegs {
     static constexpr int XE = 16 * TY * RL_BK / 256;  // x elements per thread per stage
-    float x[XE];
+    static constexpr int XW = XE * (int)sizeof(XT) / 4;  // as 32-bit words
+    uint32_t xw[XW];
     float e[8];   // expert tid/4, hidden (tid&3)*8 .. +7
 };
 
 template <typename XT, bool FULL, int TY>
 __device__ __forceinline__ void rl_load(const XT* __restrict__ x, const float* __restrict__ E,
                                         int64_t T, int64_t d, int64_t N, int64_t t0, int64_t n0,
-                                        int64_t k0, int tid, RlRegs<TY>& r) {
-    constexpr int XE = RlRegs<TY>::XE, TPT = RL_BK / XE;  // threads per token row
+                                        int64_t k0, int tid, RlRegs<XT, TY>& r) {
+    constexpr int XE = RlRegs<XT, TY>::XE, TPT = RL_BK / XE;  // threads per token row
     int64_t t = t0 + tid / TPT;
     if (t >= T) t = T - 1;  // clamp: a valid row, the result is never stored
     const int64_t kx = k0 + XE * (tid % TPT);
     const XT* xrow = x + t * d + kx;
     if (FULL) {
         // XE consecutive elements: one vector load of XE * sizeof(XT) bytes
-        XT raw[XE];
-        __builtin_memcpy(raw, xrow, sizeof(raw));
-#pragma unroll
-        for (int i = 0; i < XE; ++i) {
-            if constexpr (sizeof(XT) == 2)
-                r.x[i] = bf16_to_f32(raw[i]);
-            else
-                r.x[i] = raw[i];
-        }
+        __builtin_memcpy(r.xw, xrow, sizeof(r.xw));
     } else {
+        XT v[XE];
 #pragma unroll
-        for (int i = 0; i < XE; ++i) {
-            float v = 0.0f;
-            if (kx + i < d) {
-                if constexpr (sizeof(XT) == 2)
-                    v = bf16_to_f32(xrow[i]);
-                else
-                    v = xrow[i];
-            }
-            r.x[i] = v;
-        }
+        for (int i = 0; i < XE; ++i) v[i] = kx + i < d ? xrow[i] : XT(0);  // +0 in either type
+        __builtin_memcpy(r.xw, v, sizeof(r.xw));
     }
     const int64_t n = n0 + (tid >> 2);
     const int64_t ke = k0 + 8 * (tid & 3);
@@ -95,7 +85,7 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const XT* __restrict
                                                             float* __restrict__ s_out,
                                                             int64_t T, int64_t d, int64_t N) {
     constexpr int TM = 16 * TY;
-    constexpr int XE = RlRegs<TY>::XE, TPT = RL_BK / XE;
+    constexpr int XE = RlRegs<XT, TY>::XE, TPT = RL_BK / XE;
     __shared__ __attribute__((aligned(16))) float xs[2][RL_BK][TM + 4];
     __shared__ __attribute__((aligned(16))) float es[2][RL_BK][RL_TN + 4];
     const int tid = threadIdx.x;
@@ -110,14 +100,21 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const XT* __restrict
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
 
-    auto store = [&](int buf, const RlRegs<TY>& r) {
+    auto store = [&](int buf, const RlRegs<XT, TY>& r) {
 #pragma unroll
-        for (int i = 0; i < XE; ++i) xs[buf][XE * (tid % TPT) + i][tid / TPT] = r.x[i];
+        for (int i = 0; i < XE; ++i) {
+            float v;
+            if constexpr (sizeof(XT) == 2)  // bf16: element i is half i%2 of word i/2
+                v = __uint_as_float(i & 1 ? r.xw[i / 2] & 0xffff0000u : r.xw[i / 2] << 16);
+            else
+                v = __uint_as_float(r.xw[i]);
+            xs[buf][XE * (tid % TPT) + i][tid / TPT] = v;
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) es[buf][8 * (tid & 3) + i][tid >> 2] = r.e[i];
     };
 
-    RlRegs<TY> r;
+    RlRegs<XT, TY> r;
     const int64_t nk = cdiv(d, RL_BK);
     rl_load<XT, FULL, TY>(x, E, T, d, N, t0, n0, 0, tid, r);
     store(0, r);
@@ -127,24 +124,48 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const XT* __restrict
         const int buf = kb & 1;
         const bool more = kb + 1 < nk;
         if (more) rl_load<XT, FULL, TY>(x, E, T, d, N, t0, n0, (kb + 1) * RL_BK, tid, r);
+        // groups of RL_KG steps, the LDS operands of group g+1 read while group
+        // g's FMAs run; a fence per group keeps the compiler from hoisting every
+        // read of the stage ahead of the FMAs (it runs out of registers)
+        float xv[2][RL_KG][TY];
+        float ev[2][RL_KG][4];
+        auto ld = [&](int g, int slot) {
 #pragma unroll
-        for (int k = 0; k < RL_BK; ++k) {
-            float xv[TY];
+            for (int kk = 0; kk < RL_KG; ++kk) {
+                const int k = g * RL_KG + kk;
 #pragma unroll
-            for (int i = 0; i < TY; ++i) xv[i] = xs[buf][k][ty * TY + i];
-            const float4 eb = *reinterpret_cast<const float4*>(&es[buf][k][tx * 4]);
-            const float ev[4] = {eb.x, eb.y, eb.z, eb.w};
+                for (int i = 0; i < TY; ++i) xv[slot][kk][i] = xs[buf][k][ty * TY + i];
+                const float4 eb = *reinterpret_cast<const float4*>(&es[buf][k][tx * 4]);
+                ev[slot][kk][0] = eb.x; ev[slot][kk][1] = eb.y;
+                ev[slot][kk][2] = eb.z; ev[slot][kk][3] = eb.w;
+            }
+        };
+        ld(0, 0);
+#pragma unroll
+        for (int g = 0; g < RL_BK / RL_KG; ++g) {
+            if (g + 1 < RL_BK / RL_KG) ld(g + 1, (g + 1) & 1);
+            // fence: the reads above stay above, the FMAs below (they consume
+            // the accumulators this empty asm passes through) stay below
 #pragma unroll
             for (int i = 0; i < TY; ++i)
+                asm volatile("" : "+v"(acc[i][0]), "+v"(acc[i][1]), "+v"(acc[i][2]), "+v"(acc[i][3])
+                             :: "memory");
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(xv[i], ev[j], acc[i][j]);
+            for (int kk = 0; kk < RL_KG; ++kk)
+#pragma unroll
+                for (int i = 0; i < TY; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_fmaf(xv[g & 1][kk][i], ev[g & 1][kk][j], acc[i][j]);
         }
         if (more) store(buf ^ 1, r);
         __syncthreads();
     }
 
     // epilogue: affinity s = Sigmoid(z), evaluated in double, rounded once
-#pragma unroll
+    // (one value at a time: the double-precision exp unrolled over all
+    // outputs would claim registers the main loop then goes without)
+#pragma unroll 1
     for (int i = 0; i < TY; ++i) {
         const int64_t t = t0 + ty * TY + i;
         if (t >= T) continue;
@@ -330,11 +351,11 @@ hipError_t launch_route(const moe_cfg& c, const void* x, const float* centroids,
     }
     // Each (token, expert) logit is one serial chain over d, so the tile per
     // thread trades chains (latency hiding) against workgroups (parallelism):
-    // 8 tokens per thread for large batches, 1 for decode-sized ones.
+    // 4 tokens per thread for large batches (two workgroups per CU at
+    // 8192 x 256), 1 for decode-sized ones.
     const bool full = d % RL_BK == 0;
-    const int64_t wgs8 = cdiv(N, RL_TN) * cdiv(T, 16 * 8);
-    if (wgs8 >= 192)
-        launch_logits<8>(c.act_dtype, full, x, centroids, scores, T, d, N, st);
+    if (cdiv(N, RL_TN) * cdiv(T, 16 * 4) >= 384)
+        launch_logits<4>(c.act_dtype, full, x, centroids, scores, T, d, N, st);
     else if (cdiv(N, RL_TN) * cdiv(T, 16 * 2) >= 192)
         launch_logits<2>(c.act_dtype, full, x, centroids, scores, T, d, N, st);
     else
