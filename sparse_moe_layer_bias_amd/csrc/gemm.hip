@@ -11,8 +11,9 @@
 // Each launch walks a device-side tile list built from the expert offsets
 // (ffn_tile_map), so the ragged per-expert row counts never reach the host.
 //
-// Tile order is XCD-aware (see decode_v2): consecutive work units of one
-// expert land on one XCD so its token rows or weight panel are shared in L2.
+// Tile order is XCD-aware (see decode_v2): the units of one tile run on one
+// XCD, back to back, so its token rows are shared in L2; tiles go to the XCDs
+// round-robin so each gets an even share of routed and shared work.
 #include "gemm_common.h"
 
 namespace moe {
@@ -580,9 +581,8 @@ hipError_t launch_expert_ffn(const moe_cfg& c, const FfnArgs& a, void* ws, hipSt
     const int cols0 = bf ? 128 : 64;
     p.ntn_r = (int)cdiv(c.inter, cols0);
     p.ntn_s = has_shared ? (int)cdiv(c.inter_shared, cols0) : 0;
-    // every unit index the XCD mapping can produce must have a block: round
-    // the bound on units up to a multiple of 8
-    unsigned grid = (unsigned)(8 * cdiv(max_r * p.ntn_r + max_s * p.ntn_s, 8));
+    // a block for every (XCD, slot) the mapping can produce
+    unsigned grid = (unsigned)ffn_grid_blocks(max_r, p.ntn_r, max_s, p.ntn_s);
     if (bf)
         ffn_gemm_bf16_kernel<0, MOE_GEMM_BK, MOE_GEMM_NS><<<grid, G_THREADS, 0, st>>>(p);
     else
@@ -602,7 +602,7 @@ hipError_t launch_expert_ffn(const moe_cfg& c, const FfnArgs& a, void* ws, hipSt
     const int cols1 = bf ? 256 : 64;
     p.ntn_r = (int)cdiv(c.hidden, cols1);
     p.ntn_s = has_shared ? (int)cdiv(c.hidden, cols1) : 0;
-    grid = (unsigned)(8 * cdiv(max_r * p.ntn_r + max_s * p.ntn_s, 8));
+    grid = (unsigned)ffn_grid_blocks(max_r, p.ntn_r, max_s, p.ntn_s);
     if (bf)
         ffn_gemm_bf16_kernel<1, MOE_GEMM_BK, MOE_GEMM_NS><<<grid, G_THREADS, 0, st>>>(p);
     else

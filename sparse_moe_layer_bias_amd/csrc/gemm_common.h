@@ -42,23 +42,32 @@ struct WorkV2 {
 // wt-major -- the token chunks of one weight panel run next to each other and
 // share it.  Unit u runs on blockIdx (u % per) * 8 + u / per, per = ceil(units/8),
 // so each XCD (blockIdx x, x+8, ...) gets a contiguous unit range.
+// grid of a decode_v2 launch: 8 XCD slots x the most units one XCD can get
+// (at most max_r routed and max_s shared tiles in all)
+inline int64_t ffn_grid_blocks(int64_t max_r, int64_t ntn_r, int64_t max_s, int64_t ntn_s) {
+    return 8 * (cdiv(max_r, 8) * ntn_r + cdiv(max_s, 8) * ntn_s);
+}
+
 template <int ESZ>
 __device__ __forceinline__ bool decode_v2(const GemmParamsV2& p, int mode, WorkV2& w) {
     const int64_t nr = p.counts[0], ns = p.counts[1];
-    const int64_t ur = nr * p.ntn_r, units = ur + ns * p.ntn_s;
-    const int64_t per = (units + 7) / 8;
-    const int64_t L = blockIdx.x;
-    if (L >= 8 * per) return false;
-    const int64_t u = (L % 8) * per + L / 8;
-    if (u >= units) return false;
+    // Tiles go to the 8 XCDs round-robin (tile t to XCD t % 8; block L runs on
+    // XCD L % 8).  An XCD runs the units of its tiles tile by tile, the weight
+    // panels of one tile back to back, so a tile's token rows are shared in
+    // that XCD's L2 and every XCD gets an even share of routed and shared work.
+    const int64_t x = blockIdx.x % 8, i = blockIdx.x / 8;
+    const int64_t rx = nr > x ? (nr - x + 7) / 8 : 0;  // routed tiles of this XCD
     int64_t tile;
-    if (u < ur) {
-        tile = u / p.ntn_r;
-        w.wt = u % p.ntn_r;
+    if (i < rx * p.ntn_r) {
+        tile = x + 8 * (i / p.ntn_r);
+        w.wt = i % p.ntn_r;
     } else {
-        const int64_t v = u - ur;
-        w.wt = v / ns;
-        tile = nr + v % ns;
+        if (p.ntn_s == 0) return false;
+        const int64_t i2 = i - rx * p.ntn_r;
+        const int64_t t0 = nr + (x - nr % 8 + 8) % 8;  // first shared tile of this XCD
+        tile = t0 + 8 * (i2 / p.ntn_s);
+        if (tile >= nr + ns) return false;
+        w.wt = i2 % p.ntn_s;
     }
     const int2 t = p.tiles[tile];
     const int g = t.x;

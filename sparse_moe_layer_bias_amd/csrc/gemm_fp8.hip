@@ -427,7 +427,7 @@ hipError_t launch_expert_ffn_fp8(const moe_cfg& c, const FfnArgs& a, const int2*
     P.hs_s = hs_s;
     P.g.ntn_r = (int)(c.inter / 128);
     P.g.ntn_s = has_shared ? (int)(c.inter_shared / 128) : 0;
-    unsigned grid = (unsigned)(8 * cdiv(max_r * P.g.ntn_r + max_s * P.g.ntn_s, 8));
+    unsigned grid = (unsigned)ffn_grid_blocks(max_r, P.g.ntn_r, max_s, P.g.ntn_s);
     ffn_gemm_fp8_kernel<0><<<grid, F8_THREADS, 0, st>>>(P);
 
     // down: h codes x W2 codes -> y (bf16)
@@ -449,7 +449,7 @@ hipError_t launch_expert_ffn_fp8(const moe_cfg& c, const FfnArgs& a, const int2*
     P.hs_s = nullptr;
     P.g.ntn_r = (int)cdiv(c.hidden, 256);
     P.g.ntn_s = has_shared ? (int)cdiv(c.hidden, 256) : 0;
-    grid = (unsigned)(8 * cdiv(max_r * P.g.ntn_r + max_s * P.g.ntn_s, 8));
+    grid = (unsigned)ffn_grid_blocks(max_r, P.g.ntn_r, max_s, P.g.ntn_s);
     ffn_gemm_fp8_kernel<1><<<grid, F8_THREADS, 0, st>>>(P);
     return hipGetLastError();
 }

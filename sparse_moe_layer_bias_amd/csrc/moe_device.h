@@ -19,16 +19,17 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __uint_as_float(((uint32_t)h) << 16);
 }
 
-// fp32 -> bf16, round to nearest even (finite values; NaN stays NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+// fp32 -> bf16 with gfx950's converter (v_cvt_pk_bf16_f32, two values per
+// instruction): round to nearest even, NaN stays NaN.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    return (uint16_t)(pack_bf16x2(f, 0.0f) & 0xffffu);
 }
 
 // ---------------------------------------------------------------- E4M3FN
