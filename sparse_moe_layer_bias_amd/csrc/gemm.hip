@@ -30,12 +30,22 @@ constexpr int F32_BM = 64;      // token rows per tile, fp32 path
 // ceil(M_g / BM) tiles, written first; the shared expert (rows 0..T-1) gets
 // ceil(T / BM) tiles after them.  tiles[i] = (group, first row); group N is
 // the shared expert.  counts[0] = routed tiles, counts[1] = shared tiles.
+// Tile list and order.  Routed tiles (expert g, first row m0) come expert by
+// expert, then the shared expert's tiles.  `order` lists the routed tiles by
+// row count, largest first (counting sort on the count; tiles with equal
+// counts in any order -- the order only decides where a tile runs, never what
+// it computes).  BM <= TM_MAXBM.
+constexpr int TM_MAXBM = 512;
 __global__ void __launch_bounds__(256) ffn_tile_map_kernel(const int32_t* __restrict__ offsets,
                                                            int N, int64_t T, int has_shared,
                                                            int BM, int2* __restrict__ tiles,
-                                                           int32_t* __restrict__ counts) {
+                                                           int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ order,
+                                                           int32_t* __restrict__ keys) {
     __shared__ int32_t sh_wave[4];
     __shared__ int32_t sh_carry;
+    __shared__ int32_t hist[TM_MAXBM + 1];
+    for (int k = threadIdx.x; k <= BM; k += blockDim.x) hist[k] = 0;
     if (threadIdx.x == 0) sh_carry = 0;
     __syncthreads();
     for (int g0 = 0; g0 < N; g0 += 256) {
@@ -44,12 +54,32 @@ __global__ void __launch_bounds__(256) ffn_tile_map_kernel(const int32_t* __rest
         const int32_t nt = (int32_t)((M + BM - 1) / BM);
         const int32_t incl = block_incl_scan_256(nt, sh_wave);
         const int32_t start = sh_carry + incl - nt;
-        for (int32_t i = 0; i < nt; ++i) tiles[start + i] = make_int2(g, i * BM);
+        for (int32_t i = 0; i < nt; ++i) {
+            const int32_t rows = (int32_t)(M - (int64_t)i * BM < BM ? M - (int64_t)i * BM : BM);
+            tiles[start + i] = make_int2(g, i * BM);
+            keys[start + i] = rows;
+            atomicAdd(&hist[rows], 1);
+        }
         __syncthreads();
         if (threadIdx.x == 255) sh_carry = sh_carry + incl;
         __syncthreads();
     }
     const int32_t nr = sh_carry;
+    // first position of each row count in `order`, largest count first
+    __syncthreads();
+    if (threadIdx.x == 0) sh_carry = 0;
+    __syncthreads();
+    for (int k0 = 0; k0 <= BM; k0 += 256) {
+        const int k = BM - (k0 + (int)threadIdx.x);  // descending counts
+        const int32_t h = k >= 0 ? hist[k] : 0;
+        const int32_t incl = block_incl_scan_256(h, sh_wave);
+        const int32_t base = sh_carry;
+        __syncthreads();
+        if (k >= 0) hist[k] = base + incl - h;
+        if (threadIdx.x == 255) sh_carry = base + incl;
+        __syncthreads();
+    }
+    for (int32_t t = threadIdx.x; t < nr; t += blockDim.x) order[atomicAdd(&hist[keys[t]], 1)] = t;
     const int32_t ns = has_shared ? (int32_t)((T + BM - 1) / BM) : 0;
     for (int32_t i = threadIdx.x; i < ns; i += blockDim.x) tiles[nr + i] = make_int2(N, i * BM);
     if (threadIdx.x == 0) {
@@ -449,6 +479,8 @@ __global__ void __launch_bounds__(256) ffn_gemm_f32_kernel(GemmParamsV2 p) {
 struct FfnWs {
     int2* tiles;
     int32_t* counts;  // [2]
+    int32_t* order;   // routed tiles, largest first [max routed tiles]
+    int32_t* keys;    // row count of each routed tile [max routed tiles]
     void* h_r;        // [TK, I]
     void* h_s;        // [T, Is]
     float* hs_r;      // FP8 scales [TK, I/128]
@@ -473,6 +505,7 @@ size_t ffn_workspace_bytes(const moe_cfg& c) {
     const int64_t TK = c.tokens * c.top_k, T = c.tokens;
     const int64_t eb = h_elem_bytes(c);
     int64_t b = align256((ffn_max_routed_tiles(c) + ffn_max_shared_tiles(c)) * 8) + 256;
+    b += 2 * align256(ffn_max_routed_tiles(c) * 4);
     b += align256(TK * c.inter * eb) + align256(T * c.inter_shared * eb);
     if (c.gemm_dtype == MOE_FP8_E4M3)
         b += align256(TK * (c.inter / 128) * 4) + align256(T * (c.inter_shared / 128) * 4);
@@ -488,6 +521,10 @@ static FfnWs carve_ffn(const moe_cfg& c, void* ws) {
     p += align256((ffn_max_routed_tiles(c) + ffn_max_shared_tiles(c)) * 8);
     w.counts = (int32_t*)p;
     p += 256;
+    w.order = (int32_t*)p;
+    p += align256(ffn_max_routed_tiles(c) * 4);
+    w.keys = (int32_t*)p;
+    p += align256(ffn_max_routed_tiles(c) * 4);
     w.h_r = p;
     p += align256(TK * c.inter * eb);
     w.h_s = p;
@@ -542,8 +579,9 @@ hipError_t launch_pack_weights(const moe_cfg& c, int which, const void* w, void*
 }
 
 hipError_t launch_expert_ffn_fp8(const moe_cfg& c, const FfnArgs& a, const int2* tiles,
-                                 const int32_t* counts, void* h_r, void* h_s, float* hs_r,
-                                 float* hs_s, int64_t max_r, int64_t max_s, hipStream_t st);
+                                 const int32_t* counts, const int32_t* order, void* h_r,
+                                 void* h_s, float* hs_r, float* hs_s, int64_t max_r,
+                                 int64_t max_s, hipStream_t st);
 
 hipError_t launch_expert_ffn(const moe_cfg& c, const FfnArgs& a, void* ws, hipStream_t st) {
     const int64_t T = c.tokens, TK = T * c.top_k;
@@ -554,14 +592,15 @@ hipError_t launch_expert_ffn(const moe_cfg& c, const FfnArgs& a, void* ws, hipSt
     const int64_t max_r = ffn_max_routed_tiles(c);
     const int64_t max_s = has_shared ? ffn_max_shared_tiles(c) : 0;
     ffn_tile_map_kernel<<<1, 256, 0, st>>>(a.offsets, (int)c.n_experts, T, has_shared ? 1 : 0,
-                                           BM, w.tiles, w.counts);
+                                           BM, w.tiles, w.counts, w.order, w.keys);
     if (c.gemm_dtype == MOE_FP8_E4M3)
-        return launch_expert_ffn_fp8(c, a, w.tiles, w.counts, w.h_r, w.h_s, w.hs_r, w.hs_s,
+        return launch_expert_ffn_fp8(c, a, w.tiles, w.counts, w.order, w.h_r, w.h_s, w.hs_r, w.hs_s,
                                      max_r, max_s, st);
 
     GemmParamsV2 p{};
     p.tiles = w.tiles;
     p.counts = w.counts;
+    p.order = w.order;
     p.offsets = a.offsets;
     p.N = (int)c.n_experts;
     p.T = has_shared ? T : 0;

@@ -14,6 +14,7 @@ constexpr int G_WR_PACK = 256;  // rows per packed weight tile
 struct GemmParamsV2 {
     const int2* tiles;     // routed tiles [0, n_r), shared tiles [n_r, n_r + n_s)
     const int32_t* counts; // [0] = routed tiles, [1] = shared tiles
+    const int32_t* order;  // routed tiles, largest first
     const int32_t* offsets;
     int N;
     int ntn_r, ntn_s;      // weight tiles per token tile, routed / shared
@@ -45,29 +46,33 @@ struct WorkV2 {
 // grid of a decode_v2 launch: 8 XCD slots x the most units one XCD can get
 // (at most max_r routed and max_s shared tiles in all)
 inline int64_t ffn_grid_blocks(int64_t max_r, int64_t ntn_r, int64_t max_s, int64_t ntn_s) {
-    return 8 * (cdiv(max_r, 8) * ntn_r + cdiv(max_s, 8) * ntn_s);
+    return 8 * cdiv(max_r + max_s, 8) * (ntn_r > ntn_s ? ntn_r : ntn_s);
 }
 
 template <int ESZ>
 __device__ __forceinline__ bool decode_v2(const GemmParamsV2& p, int mode, WorkV2& w) {
     const int64_t nr = p.counts[0], ns = p.counts[1];
-    // Tiles go to the 8 XCDs round-robin (tile t to XCD t % 8; block L runs on
-    // XCD L % 8).  An XCD runs the units of its tiles tile by tile, the weight
-    // panels of one tile back to back, so a tile's token rows are shared in
-    // that XCD's L2 and every XCD gets an even share of routed and shared work.
+    // Tiles are dealt to the 8 XCDs (block L runs on XCD L % 8) in rounds of 8
+    // along the sequence [shared tiles, routed tiles largest first], the
+    // direction reversed every round: position q goes to XCD q % 8 or 7 - q % 8.
+    // That evens out each XCD's work, and each XCD starts with its largest
+    // tiles.  An XCD runs its tiles in order, the weight panels of one tile back
+    // to back, so a tile's token rows are shared in that XCD's L2.
     const int64_t x = blockIdx.x % 8, i = blockIdx.x / 8;
-    const int64_t rx = nr > x ? (nr - x + 7) / 8 : 0;  // routed tiles of this XCD
+    const int64_t rf = ns / 8, rem = ns % 8;
+    const int64_t sx = rf + ((rf % 2 == 0) ? (x < rem) : (x >= 8 - rem));  // shared tiles here
     int64_t tile;
-    if (i < rx * p.ntn_r) {
-        tile = x + 8 * (i / p.ntn_r);
-        w.wt = i % p.ntn_r;
+    if (i < sx * p.ntn_s) {
+        const int64_t j = i / p.ntn_s;
+        tile = nr + j * 8 + (j % 2 == 0 ? x : 7 - x);
+        w.wt = i % p.ntn_s;
     } else {
-        if (p.ntn_s == 0) return false;
-        const int64_t i2 = i - rx * p.ntn_r;
-        const int64_t t0 = nr + (x - nr % 8 + 8) % 8;  // first shared tile of this XCD
-        tile = t0 + 8 * (i2 / p.ntn_s);
-        if (tile >= nr + ns) return false;
-        w.wt = i2 % p.ntn_s;
+        const int64_t i2 = i - sx * p.ntn_s;
+        const int64_t j = sx + i2 / p.ntn_r;
+        const int64_t k = j * 8 + (j % 2 == 0 ? x : 7 - x) - ns;
+        if (k < 0 || k >= nr) return false;
+        tile = p.order[k];
+        w.wt = i2 % p.ntn_r;
     }
     const int2 t = p.tiles[tile];
     const int g = t.x;

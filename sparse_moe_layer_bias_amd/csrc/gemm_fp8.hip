@@ -397,13 +397,14 @@ hipError_t launch_pack_weights_fp8(const moe_cfg& c, int which, const void* w, v
 }
 
 hipError_t launch_expert_ffn_fp8(const moe_cfg& c, const FfnArgs& a, const int2* tiles,
-                                 const int32_t* counts, void* h_r, void* h_s, float* hs_r,
+                                 const int32_t* counts, const int32_t* order, void* h_r, void* h_s, float* hs_r,
                                  float* hs_s, int64_t max_r, int64_t max_s, hipStream_t st) {
     const int64_t T = c.tokens;
     const bool has_shared = c.inter_shared > 0 && T > 0;
     Fp8Params P{};
     P.g.tiles = tiles;
     P.g.counts = counts;
+    P.g.order = order;
     P.g.offsets = a.offsets;
     P.g.N = (int)c.n_experts;
     P.g.T = has_shared ? T : 0;
