@@ -136,17 +136,21 @@ __device__ __forceinline__ i32x4_t make_rsrc(const void* base, int64_t bytes) {
 // waitcnt pass makes every later LDS read wait for all copies in flight
 // (vmcnt(0)), which would serialise the next stage's copies with the MFMAs of
 // the current one.  The caller orders copies and reads itself (s_waitcnt
-// vmcnt + barrier).  The s_nop covers the M0-write -> LDS-DMA hazard.
+// vmcnt + barrier).  The compiler does not check hazards against the asm's
+// operands, so the asm waits for them itself: s_nop 4 gives the 5 wait states
+// a VMEM instruction needs after a VALU write of an SGPR it reads (the
+// descriptor and offset SGPRs can come straight from v_readlane /
+// v_readfirstlane), which also covers the 1 after an M0 write.
 template <int SIZE>
 __device__ __forceinline__ void dma_to_lds(i32x4_t rsrc, const void* lds, uint32_t voff,
                                            uint32_t soff) {
     const uint32_t m0 = (uint32_t)(uintptr_t)lds;
     if constexpr (SIZE == 16)
-        asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc),
+        asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc),
                      "s"(soff), "{m0}"(m0)
                      : "memory");
     else
-        asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc),
+        asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc),
                      "s"(soff), "{m0}"(m0)
                      : "memory");
 }
