@@ -103,7 +103,9 @@ __device__ __forceinline__ bool decode_v2(const GemmParamsV2& p, int mode, WorkV
     return true;
 }
 
-__device__ __forceinline__ float silu_f(float a) { return a / (1.0f + __expf(-a)); }
+// silu(a) = a / (1 + e^-a), with the hardware reciprocal (1 ulp) instead of a
+// division: it feeds bf16 / E4M3 outputs
+__device__ __forceinline__ float silu_f(float a) { return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 

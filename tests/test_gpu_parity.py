@@ -55,6 +55,8 @@ LAYER_CASES = [
     ("mid_bf16", dict(T=130, N=1, k=1)),             # one expert: gate 1
     ("mid_bf16", dict(T=64, d=256, I=128, Is=256)),  # Is != I
     ("mid_bf16", dict(T=64, d=256, I=256, Is=128)),
+    ("mid_bf16", dict(T=100, d=384, I=256, Is=128)),  # d % 256 != 0: half a down tile
+    ("mid_bf16", dict(T=1000, N=2, k=1)),             # >320 rows per expert: several tiles
 ]
 
 
@@ -86,6 +88,8 @@ FP8_CASES = [
     ("mid_bf16", dict(T=300, G=8, TG=3)),                  # group-limited
     ("mid_bf16", dict(T=64, d=256, I=128, Is=256)),        # Is != I
     ("mid_bf16", dict(T=700, d=384, N=4, k=2, I=256, Is=128)),  # >256 rows/expert, d%256 != 0
+    ("mid_bf16", dict(T=1)),                               # one token: 8 one-row tiles
+    ("mid_bf16", dict(T=1000, N=2, k=1)),                  # >320 rows/expert: several tiles
 ]
 
 
@@ -322,6 +326,35 @@ def test_skew_balance_trajectory(orc):
         if step % 20 == 0:
             log("step", step, "max/mean load %.2f" % imb[-1])
     assert np.mean(imb[-10:]) < np.mean(imb[:10])
+
+
+def test_bias_state_resumes_exactly():
+    """The bias is the layer's only state across steps: 30 steps in one go and
+    15 + 15 steps with the bias saved to host memory and restored into a
+    fresh buffer in between end with the same bias bits."""
+    cfg = dict(moe_inputs.CONFIGS["skew_balance"])
+    E = moe_inputs.make_skew_centroids(cfg, 0, "cpu").cuda()
+    c = moe.cfg_from_dict(cfg)
+    T, N, k = cfg["T"], cfg["N"], cfg["k"]
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gate = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    counts = torch.empty((N,), dtype=torch.int32, device="cuda")
+    scores = torch.empty((T, N), dtype=torch.float32, device="cuda")
+
+    def run(bias, steps):
+        for step in steps:
+            x = moe_inputs.make_skew_tokens(cfg, step, 0, "cpu").cuda()
+            moe.moe_route(c, x, E, bias, scores, idx, gate, counts)
+            moe.moe_bias_update(N, T * k, counts, 0.001, bias)
+        torch.cuda.synchronize()
+        return bias
+
+    straight = run(torch.zeros(N, device="cuda"), range(30))
+    saved = moe_inputs.to_host(run(torch.zeros(N, device="cuda"), range(15))).copy()
+    resumed = run(torch.from_numpy(saved).cuda(), range(15, 30))
+    assert_bits(moe_inputs.to_host(resumed).view(np.uint32),
+                moe_inputs.to_host(straight).view(np.uint32), "bias after resume")
+    assert np.any(moe_inputs.to_host(straight) != 0)
 
 
 # ------------------------------------------------------------------ V3 shape, sampled
