@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--workload", default="v3_bf16")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the measured-peak probes (HBM read, MFMA loop)")
     ap.add_argument("--traffic-run", action="store_true",
                     help="run the expert FFN 3 times and a 1 GiB copy 3 times (for rocprofv3 "
                          "--pmc FETCH_SIZE / WRITE_SIZE passes), then exit")
@@ -327,6 +329,19 @@ def main():
                  "traffic": recorded_traffic(args.workload),
                  "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
                  "mfma_tflops": achieved / 1e12, "mfma_frac": achieved / peak})
+    if not args.no_probes:
+        # the same ceilings measured on this GPU, after the timed region: the
+        # HBM read rate of the GEMMs' global -> LDS copies alone, and the rate
+        # of a register-resident loop of their MFMA instruction (its clock is
+        # the rate over the published flop per cycle)
+        from sparse_moe_layer_bias_amd import probe
+        rd = probe.hbm_read_rate()
+        mf = probe.mfma_rate("fp8" if fp8 else "bf16")
+        roof["measured_peak"] = {"hbm_read_GBps": rd / 1e9, "mfma_tflops": mf / 1e12,
+                                 "mfma_clock_GHz": mf / (peak / 2.4e9) / 1e9}
+        roof["frac_of_measured"] = (nbytes / ffn_s / rd) if hbm_bound else (achieved / mf)
+        roof["mfma_frac_of_measured"] = achieved / mf
+        log("measured peaks:", json.dumps(roof["measured_peak"]))
     result = {
         "metric": METRIC,
         "value": T / (ms_per_step / 1e3),

@@ -104,6 +104,16 @@ int hip_status(const char* fn, hipError_t e) {
 
 }  // namespace
 
+namespace moe {
+int set_error(int code, const char* msg) {
+    if (code == MOE_OK)
+        g_err[0] = 0;
+    else
+        snprintf(g_err, sizeof(g_err), "%s", msg);
+    return code;
+}
+}  // namespace moe
+
 extern "C" {
 
 int moe_abi_version(void) { return 2; }

@@ -5,6 +5,9 @@
 
 namespace moe {
 
+// sets the thread's moe_last_error() text (cleared for MOE_OK); returns code
+int set_error(int code, const char* msg);
+
 // ---------------------------------------------------------------- route
 hipError_t launch_route(const moe_cfg& c, const void* x, const float* centroids,
                         const float* bias, float* scores, int32_t* idx, float* gate,

@@ -21,9 +21,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared():
-    src = open(os.path.join(ROOT, "include", "moe.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", src)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", h)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(moe_\w+)\s*\(", src))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
@@ -31,9 +35,28 @@ def test_library_exports_every_declared_symbol():
     names = _declared()
     assert {"moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
             "moe_bias_update"} <= set(names)
+    assert {"moe_probe_hbm_read", "moe_probe_mfma"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert moe.moe_abi_version() == 2
+
+
+@host_only
+@pytest.mark.parametrize("call,code", [
+    (lambda L: L.moe_probe_hbm_read(None, 1 << 20, 16, ctypes.c_void_p(FAKE), None), 1),
+    (lambda L: L.moe_probe_hbm_read(ctypes.c_void_p(FAKE), 1000, 16, ctypes.c_void_p(FAKE), None), 1),
+    (lambda L: L.moe_probe_hbm_read(ctypes.c_void_p(FAKE), 1 << 20, 0, ctypes.c_void_p(FAKE), None), 1),
+    (lambda L: L.moe_probe_hbm_read(ctypes.c_void_p(FAKE + 8), 1 << 20, 16, ctypes.c_void_p(FAKE), None), 1),
+    (lambda L: L.moe_probe_mfma(0, 10, 1, ctypes.c_void_p(FAKE), None), 1),
+    (lambda L: L.moe_probe_mfma(1, 0, 1, ctypes.c_void_p(FAKE), None), 1),
+    (lambda L: L.moe_probe_mfma(2, 10, 0, ctypes.c_void_p(FAKE), None), 1),
+    (lambda L: L.moe_probe_mfma(1, 10, 1, None, None), 1),
+])
+def test_probes_reject_bad_arguments(call, code):
+    from sparse_moe_layer_bias_amd import probe
+    L = probe._lib()
+    assert call(L) == code
+    assert moe.lib().moe_last_error()
 
 
 def _cfg(**kw):
