@@ -68,6 +68,11 @@ def parse():
     ap.add_argument("--traffic-run", action="store_true",
                     help="run the expert FFN 3 times and a 1 GiB copy 3 times (for rocprofv3 "
                          "--pmc FETCH_SIZE / WRITE_SIZE passes), then exit")
+    ap.add_argument("--counter-run", action="store_true",
+                    help="run 1 + 2 layer steps, the bf16 and FP8 MFMA probes and a 1 GiB copy "
+                         "3 times (for rocprofv3 --pmc passes over the whole step), then exit")
+    ap.add_argument("--counter-summary", nargs=3, metavar=("MFMA_CSV", "FETCH_CSV", "WRITE_CSV"),
+                    help="per-kernel MFMA busy share and HBM bytes of a --counter-run, then exit")
     ap.add_argument("--stats-summary", metavar="KERNEL_STATS_CSV",
                     help="print the per-kernel table of a rocprofv3 --stats run, then exit")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -167,6 +172,92 @@ def stats_summary(path):
     return "\n".join(out)
 
 
+def counter_run(cfg, layer, dev):
+    """One warm step, two counted steps, then the calibration kernels: the MFMA
+    probes (a register-resident MFMA loop keeps the MFMA pipe busy all the
+    time) and a 1 GiB device copy (known bytes)."""
+    import torch
+    from sparse_moe_layer_bias_amd import probe
+    x, E = dev["x"], dev["centroids"]
+    bias = dev["bias"].clone()
+    layer.forward(x, E, bias)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        layer.forward(x, E, bias)
+    torch.cuda.synchronize()
+    probe.mfma_rate("bf16", iters=2000, blocks=256, reps=1)
+    probe.mfma_rate("fp8", iters=1000, blocks=256, reps=1)
+    a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+
+
+def counter_summary(mfma_csv, fetch_csv, write_csv, workload):
+    """Per libmoe kernel of a --counter-run: average duration, MFMA busy share
+    and HBM bytes.  SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE is expressed
+    relative to the MFMA probe of the same dtype (busy every cycle: 100%);
+    FETCH_SIZE / WRITE_SIZE are scaled so that the 1 GiB copy reads / writes
+    1 GiB."""
+    import csv
+    import collections
+
+    def load(path, counters):
+        per = collections.defaultdict(lambda: collections.defaultdict(list))
+        dur = collections.defaultdict(list)
+        seen = set()
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] not in counters:
+                    continue
+                per[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+                key = (r["Kernel_Name"], r["Dispatch_Id"])
+                if key not in seen:
+                    seen.add(key)
+                    dur[r["Kernel_Name"]].append(
+                        (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+        return per, dur
+
+    m, mdur = load(mfma_csv, ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"))
+    fe, _ = load(fetch_csv, ("FETCH_SIZE",))
+    wr, _ = load(write_csv, ("WRITE_SIZE",))
+
+    def busy(k):
+        b = sum(m[k]["SQ_VALU_MFMA_BUSY_CYCLES"])
+        g = sum(m[k]["GRBM_GUI_ACTIVE"])
+        return b / g if g else 0.0
+
+    probes = {dt: [k for k in m if "probe_mfma_kernel<%d>" % code in k]
+              for dt, code in (("bf16", 1), ("fp8", 2))}
+    ref = {dt: busy(ks[0]) for dt, ks in probes.items() if ks}
+    copy_k = [k for k in fe if "copybuffer" in k.lower()]
+    if not copy_k or not ref:
+        raise SystemExit("calibration kernels missing")
+    f_scale = COPY_BYTES / (sum(fe[copy_k[0]]["FETCH_SIZE"][-3:]) / 3 * 1024.0)
+    w_scale = COPY_BYTES / (sum(wr[copy_k[0]]["WRITE_SIZE"][-3:]) / 3 * 1024.0)
+    fp8 = "fp8" in workload
+    out = ["workload: %s" % workload,
+           "calibration: MFMA busy/active of the probes = bf16 %.4g, fp8 %.4g (= 100%%); "
+           "byte scales fetch %.5f, write %.5f (1 GiB copy)" % (ref.get("bf16", 0), ref.get("fp8", 0),
+                                                              f_scale, w_scale),
+           "%-58s %5s %10s %9s %10s %10s %9s %7s" % ("kernel", "disp", "avg_us", "mfma_busy",
+                                                    "read_MB", "write_MB", "GB/s", "%8TB/s")]
+    for k in m:
+        if "moe::" not in k or "probe" in k:
+            continue
+        n = len(mdur[k])
+        d = sum(mdur[k]) / n
+        bz = busy(k) / ref["fp8" if ("fp8" in k or fp8 and "gemm" in k) else "bf16"]
+        rb = sum(fe[k]["FETCH_SIZE"]) / max(len(fe[k]["FETCH_SIZE"]), 1) * 1024.0 * f_scale
+        wb = sum(wr[k]["WRITE_SIZE"]) / max(len(wr[k]["WRITE_SIZE"]), 1) * 1024.0 * w_scale
+        gbs = (rb + wb) / d / 1e9 if d > 0 else 0.0
+        out.append("%-58s %5d %10.1f %8.1f%% %10.1f %10.1f %9.0f %6.1f%%" % (
+            k.replace("moe::", "")[:58], n, d * 1e6, 100 * bz, rb / 1e6, wb / 1e6, gbs,
+            100 * gbs / (PEAK["hbm"] / 1e9)))
+    return "\n".join(out)
+
+
 def traffic_run(cfg, layer, dev):
     import torch
     x = dev["x"]
@@ -244,6 +335,9 @@ def main():
     if args.traffic_summary:
         print(traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.workload))
         return
+    if args.counter_summary:
+        print(counter_summary(*args.counter_summary, args.workload))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(no collectives); run with --gpus 1", file=sys.stderr)
@@ -274,6 +368,10 @@ def main():
     if args.traffic_run:
         traffic_run(cfg, layer, dev)
         log("traffic run done")
+        return
+    if args.counter_run:
+        counter_run(cfg, layer, dev)
+        log("counter run done")
         return
 
     for _ in range(args.warmup):
