@@ -57,6 +57,10 @@ LAYER_CASES = [
     ("mid_bf16", dict(T=64, d=256, I=256, Is=128)),
     ("mid_bf16", dict(T=100, d=384, I=256, Is=128)),  # d % 256 != 0: half a down tile
     ("mid_bf16", dict(T=1000, N=2, k=1)),             # >320 rows per expert: several tiles
+    ("mid_bf16", dict(T=96, N=1024, k=64, d=256, I=128, Is=128)),  # largest N and top_k accepted
+    ("mid_bf16", dict(T=64, N=100, k=6)),             # N % 64 != 0: a partial router tile
+    ("mid_bf16", dict(T=50, N=16, k=16)),             # k = N: every expert chosen
+    ("mid_bf16", dict(T=200, N=128, k=8, G=64, TG=4)),  # 64 groups of 2 experts
 ]
 
 
@@ -90,6 +94,7 @@ FP8_CASES = [
     ("mid_bf16", dict(T=700, d=384, N=4, k=2, I=256, Is=128)),  # >256 rows/expert, d%256 != 0
     ("mid_bf16", dict(T=1)),                               # one token: 8 one-row tiles
     ("mid_bf16", dict(T=1000, N=2, k=1)),                  # >320 rows/expert: several tiles
+    ("mid_bf16", dict(T=40, d=65536, N=2, k=1, I=128, Is=128)),  # K at the FP8 limit: 512 scale blocks
 ]
 
 
