@@ -127,17 +127,6 @@ constexpr int G_CPR = G_SUB / 8;  // 16-byte chunks per LDS row
 #ifndef MOE_GEMM_NS
 #define MOE_GEMM_NS 2
 #endif
-// L2 prefetch of the weight stage after the one being copied (two-stage
-// pipeline only): copies it into a 1 KB throwaway LDS slot so that its later
-// real copy hits L2 instead of waiting on HBM
-#ifndef MOE_GEMM_PF
-#define MOE_GEMM_PF 0
-#endif
-// operand copies: 0 = global -> LDS directly (global_load_lds), 1 = through
-// registers (global_load_dwordx4, then ds_write_b128 after the stage's MFMAs)
-#ifndef MOE_GEMM_LOADER
-#define MOE_GEMM_LOADER 0
-#endif
 
 // Pack a stack of n_mats expert matrices into the GEMM's LDS image order:
 // out[mat][wt][kc][slot] (16-byte chunks), kc = 64-wide contraction block,
@@ -227,18 +216,6 @@ __device__ __forceinline__ void gemm_bf16_body(const WorkV2& w, uint16_t* smem) 
         }
     };
 
-    constexpr bool PF = MOE_GEMM_PF != 0 && NS == 2;
-    uint16_t* pf_slot = smem + NS * (A_EL + X_EL);  // 1 KB, never read
-    auto prefetch = [&](int kt) {
-        const char* wsrc = wstage0 + (int64_t)kt * A_EL * 2;
-#pragma unroll
-        for (int j = 0; j < PA; ++j) {
-            const int b = wave + G_WAVES * j;
-            __builtin_amdgcn_global_load_lds((const void*)(wsrc + b * 1024 + woff), to_lds(pf_slot),
-                                             16, 0, 0);
-        }
-    };
-
     // 16x16x32 MFMAs: wave (wr, tg) owns weight rows wr*64 + 16i + 0..15
     // (i = 0..3) and token rows tg*160 + 16j + 0..15 (j < NB)
     f32x4_t acc[4][NBB];
@@ -277,59 +254,17 @@ __device__ __forceinline__ void gemm_bf16_body(const WorkV2& w, uint16_t* smem) 
         }
     };
 
-    if constexpr (MOE_GEMM_LOADER == 1 && NS == 2) {
-        uint4 ra[PA], rx[PX];
-        auto gload = [&](int kt) {
-            const char* wsrc = wstage0 + (int64_t)kt * A_EL * 2;
-            const char* xsrc = xbase + (int64_t)kt * BK * 2;
 #pragma unroll
-            for (int j = 0; j < PA; ++j)
-                ra[j] = *(const uint4*)(wsrc + (wave + G_WAVES * j) * 1024 + woff);
-#pragma unroll
-            for (int j = 0; j < PX; ++j)
-                if (wave + G_WAVES * j < nxe) rx[j] = *(const uint4*)(xsrc + xoff[j]);
-        };
-        auto lstore = [&](int s) {
-            uint16_t* As = stage_a(s);
-            uint16_t* Xs = stage_x(s);
-#pragma unroll
-            for (int j = 0; j < PA; ++j)
-                *(uint4*)(As + (wave + G_WAVES * j) * 512 + lane * 8) = ra[j];
-#pragma unroll
-            for (int j = 0; j < PX; ++j) {
-                const int b = wave + G_WAVES * j;
-                if (b < nxe)
-                    *(uint4*)(Xs + (b % NSUB) * G_TR * G_SUB + (b / NSUB) * 512 + lane * 8) = rx[j];
-            }
-        };
-        gload(0);
-        lstore(0);
-        if (1 < nk) gload(1);
-        __syncthreads();
-        for (int kt = 0; kt < nk; ++kt) {
-            compute(kt & 1);
-            if (kt + 1 < nk) lstore((kt + 1) & 1);  // registers hold stage kt+1
-            if (kt + 2 < nk) gload(kt + 2);
-            __syncthreads();
-        }
-    } else {
-#pragma unroll
-        for (int s = 0; s < NS - 1; ++s)
-            if (s < nk) issue(s, s);
-        if (PF && 1 < nk) prefetch(1);
-        for (int kt = 0; kt < nk; ++kt) {
-            // copies issued by this wave after stage kt's may stay in flight: later
-            // stages (cnt each) or, two-stage + prefetch, the prefetch of kt+1
-            const int after = nk - 1 - kt < NS - 2 ? nk - 1 - kt : NS - 2;
-            if (PF)
-                vm_wait_n(kt + 1 < nk ? PA : 0);
-            else
-                vm_wait_n(after * cnt);
-            __syncthreads();  // stage kt landed for every wave; stage kt-1 is free
-            if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
-            if (PF && kt + NS < nk) prefetch(kt + NS);
-            compute(kt % NS);
-        }
+    for (int s = 0; s < NS - 1; ++s)
+        if (s < nk) issue(s, s);
+    for (int kt = 0; kt < nk; ++kt) {
+        // copies issued by this wave after stage kt's may stay in flight:
+        // later stages, cnt each
+        const int after = nk - 1 - kt < NS - 2 ? nk - 1 - kt : NS - 2;
+        vm_wait_n(after * cnt);
+        __syncthreads();  // stage kt landed for every wave; stage kt-1 is free
+        if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
+        compute(kt % NS);
     }
 
     // Epilogue.  The output tile goes through LDS so that global stores are
@@ -403,7 +338,7 @@ template <int MODE, int BK, int NS>
 __global__ void __launch_bounds__(G_THREADS, 1) ffn_gemm_bf16_kernel(GemmParamsV2 p) {
     WorkV2 w;
     if (!decode_v2<2>(p, MODE, w)) return;
-    constexpr int STAGES_EL = NS * (G_WR + G_TR) * BK + 512;
+    constexpr int STAGES_EL = NS * (G_WR + G_TR) * BK;
     constexpr int EPI_EL = MODE == 0 ? G_TR * (128 + 8) : 160 * (256 + 8);
     __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES_EL > EPI_EL ? STAGES_EL : EPI_EL];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
