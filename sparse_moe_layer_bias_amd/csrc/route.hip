@@ -177,6 +177,110 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const XT* __restrict
     }
 }
 
+// Small batches: the tiled kernel above would leave most CUs idle (each of
+// its threads runs 4*TY chains), so here every lane runs one chain.  A
+// workgroup of 8 waves covers 8 tokens x 64 experts: wave w owns token t0+w,
+// lane l expert n0+l.  The centroid tile [64 experts][RR_BK] is staged in LDS
+// once per workgroup and read by lane l as float4s along k (rows padded by 4
+// floats, so the 16 lanes served together hit distinct banks); the token tile
+// [8][RR_BK] is read by all lanes of a wave at one address.  Same chain as
+// above: k ascending from +0, fma(x, e, acc); zero padding past d.
+constexpr int RR_BK = 256, RR_TM = 8;
+constexpr int RR_EQ = RL_TN * RR_BK / 4 / 512;  // centroid float4s per thread and stage
+constexpr int RR_XE = RR_TM * RR_BK / 512;       // token elements per thread and stage
+
+template <typename XT, bool FULL>
+__global__ void __launch_bounds__(512) router_logits_rows_kernel(const XT* __restrict__ x,
+                                                                const float* __restrict__ E,
+                                                                float* __restrict__ s_out,
+                                                                int64_t T, int64_t d, int64_t N) {
+    __shared__ __attribute__((aligned(16))) float es[2][RL_TN][RR_BK + 4];
+    __shared__ __attribute__((aligned(16))) float xs[2][RR_TM][RR_BK];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t n0 = (int64_t)blockIdx.x * RL_TN, t0 = (int64_t)blockIdx.y * RR_TM;
+
+    // stage loads, held in registers while the previous stage is multiplied:
+    // centroids 64 rows x RR_BK/4 float4s, tokens 8 rows x RR_BK elements
+    constexpr int Q4 = RR_BK / 4;  // float4s per centroid row
+    float4 er[RR_EQ];
+    float xr[RR_XE];
+    auto load = [&](int64_t k0) {
+#pragma unroll
+        for (int c = 0; c < RR_EQ; ++c) {
+            const int q = tid + 512 * c, row = q / Q4, c4 = q % Q4;
+            const int64_t n = n0 + row, k = k0 + 4 * c4;
+            float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (n < N) {
+                const float* e = E + n * d + k;
+                if (FULL) {
+                    v = *(const float4*)e;
+                } else {
+                    v.x = k < d ? e[0] : 0.0f;
+                    v.y = k + 1 < d ? e[1] : 0.0f;
+                    v.z = k + 2 < d ? e[2] : 0.0f;
+                    v.w = k + 3 < d ? e[3] : 0.0f;
+                }
+            }
+            er[c] = v;
+        }
+        {
+            constexpr int TPR = RR_BK / RR_XE;  // threads per token row
+            int64_t t = t0 + tid / TPR;
+            if (t >= T) t = T - 1;  // clamp: a valid row, the result is never stored
+            const int64_t k = k0 + RR_XE * (tid % TPR);
+            const XT* xp = x + t * d + k;
+#pragma unroll
+            for (int i = 0; i < RR_XE; ++i) {
+                float v = 0.0f;
+                if (FULL || k + i < d) {
+                    if constexpr (sizeof(XT) == 2)
+                        v = __uint_as_float((uint32_t)xp[i] << 16);
+                    else
+                        v = (float)xp[i];
+                }
+                xr[i] = v;
+            }
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int c = 0; c < RR_EQ; ++c) {
+            const int q = tid + 512 * c;
+            *(float4*)&es[buf][q / Q4][4 * (q % Q4)] = er[c];
+        }
+        constexpr int TPR = RR_BK / RR_XE;
+        float* xp = &xs[buf][tid / TPR][RR_XE * (tid % TPR)];
+#pragma unroll
+        for (int i = 0; i < RR_XE; i += 4) *(float4*)(xp + i) = make_float4(xr[i], xr[i + 1], xr[i + 2], xr[i + 3]);
+    };
+
+    float acc = 0.0f;
+    const int64_t nk = cdiv(d, RR_BK);
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int64_t kb = 0; kb < nk; ++kb) {
+        const int buf = kb & 1;
+        const bool more = kb + 1 < nk;
+        if (more) load((kb + 1) * RR_BK);
+        const float* erow = &es[buf][lane][0];
+        const float* xrow = &xs[buf][wave][0];
+#pragma unroll 8
+        for (int k = 0; k < RR_BK; k += 4) {
+            const float4 ev = *(const float4*)(erow + k);
+            const float4 xv = *(const float4*)(xrow + k);
+            acc = __builtin_fmaf(xv.x, ev.x, acc);
+            acc = __builtin_fmaf(xv.y, ev.y, acc);
+            acc = __builtin_fmaf(xv.z, ev.z, acc);
+            acc = __builtin_fmaf(xv.w, ev.w, acc);
+        }
+        if (more) store(buf ^ 1);
+        __syncthreads();
+    }
+    const int64_t t = t0 + wave, n = n0 + lane;
+    if (t < T && n < N) s_out[t * N + n] = (float)(1.0 / (1.0 + exp(-(double)acc)));
+}
+
 // ------------------------------------------------------------------ select
 
 // "a beats b": larger key, or equal key and lower index
@@ -352,9 +456,29 @@ hipError_t launch_route(const moe_cfg& c, const void* x, const float* centroids,
     // Each (token, expert) logit is one serial chain over d, so the tile per
     // thread trades chains (latency hiding) against workgroups (parallelism):
     // 4 tokens per thread for large batches (two workgroups per CU at
-    // 8192 x 256), 1 for decode-sized ones.
+    // 8192 x 256), fewer for smaller ones, and one chain per lane for
+    // decode-sized batches.
     const bool full = d % RL_BK == 0;
-    if (cdiv(N, RL_TN) * cdiv(T, 16 * 4) >= 384)
+    if (cdiv(N, RL_TN) * cdiv(T, 64) < 64) {
+        // decode-sized batch: one chain per lane
+        const dim3 g1((unsigned)cdiv(N, RL_TN), (unsigned)cdiv(T, RR_TM));
+        const bool fr = d % RR_BK == 0;
+        if (c.act_dtype == MOE_BF16) {
+            if (fr)
+                router_logits_rows_kernel<uint16_t, true><<<g1, 512, 0, st>>>(
+                    (const uint16_t*)x, centroids, scores, T, d, N);
+            else
+                router_logits_rows_kernel<uint16_t, false><<<g1, 512, 0, st>>>(
+                    (const uint16_t*)x, centroids, scores, T, d, N);
+        } else {
+            if (fr)
+                router_logits_rows_kernel<float, true><<<g1, 512, 0, st>>>(
+                    (const float*)x, centroids, scores, T, d, N);
+            else
+                router_logits_rows_kernel<float, false><<<g1, 512, 0, st>>>(
+                    (const float*)x, centroids, scores, T, d, N);
+        }
+    } else if (cdiv(N, RL_TN) * cdiv(T, 16 * 4) >= 384)
         launch_logits<4>(c.act_dtype, full, x, centroids, scores, T, d, N, st);
     else if (cdiv(N, RL_TN) * cdiv(T, 16 * 2) >= 192)
         launch_logits<2>(c.act_dtype, full, x, centroids, scores, T, d, N, st);
