@@ -1,6 +1,7 @@
 /*
  * moe_oracle.c -- plain, slow, obviously-correct CPU oracle for one
- * DeepSeekMoE feed-forward layer forward pass and its per-step bias update.
+ * DeepSeekMoE feed-forward layer: its forward pass, its per-step bias update,
+ * and the gradients of the forward (bf16 / fp32 storage).
  *
  * TEST INFRASTRUCTURE ONLY.  This library is the reference the GPU library is
  * checked against.  Only the test-suite, the smoke check and the CPU-baseline
@@ -510,4 +511,174 @@ void orc_bias_update(int64_t N, int64_t TK, const int32_t* counts, float gamma, 
         else if (lhs < TK)
             bias[i] = bias[i] + gamma;
     }
+}
+
+/* ====================================================================== */
+/* backward pass of the layer                                              */
+/* ====================================================================== */
+/*
+ * The gradient of the layer statement ([P4] "Methode" item 2) with respect to
+ * its inputs and parameters, by the chain rule, given the upstream gradient
+ * dout = dL/dh'_t.  The selection (idx) is piecewise constant and the bias
+ * enters only the selection key, so neither carries a gradient; gates carry
+ * one through s_{i,t} = sigmoid(u_t^T e_i) into u_t and the centroids e_i.
+ *
+ * Storage points mirror the forward: a, b are fp32 sums; h = silu(a)*b is
+ * stored in the storage dtype; the backward also reads a and b back from
+ * storage (rounded to the dtype) and stores da, db in the dtype.  Every sum is
+ * a double sum; each output is rounded once.
+ */
+
+/* combine backward.  out[t] = x[t] + y_s[t] + sum_j gate[t,j] y_perm[dst[t,j]]:
+ *   dy_perm[dst[t,j], c] = gate[t,j] * dout[t,c]       (rounded to the dtype)
+ *   dgate[t,j] = sum_c dout[t,c] * y_perm[dst[t,j], c]  (fp32)
+ * The residual and shared-expert gradients are dout itself. */
+void orc_combine_backward(int64_t T, int64_t d, int64_t k, int dtype, const void* dout,
+                          const void* y_perm, const float* gate, const int32_t* dst_row,
+                          void* dy_perm, float* dgate) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t j = 0; j < k; ++j) {
+            const int64_t row = dst_row[t * k + j];
+            double acc = 0.0;
+            for (int64_t c = 0; c < d; ++c) {
+                const double g = (double)load_elem(dout, dtype, t * d + c);
+                acc += g * (double)load_elem(y_perm, dtype, row * d + c);
+                store_elem_from_double(dy_perm, dtype, row * d + c, (double)gate[t * k + j] * g);
+            }
+            dgate[t * k + j] = (float)acc;
+        }
+}
+
+static double sigmoid_d(double a) { return 1.0 / (1.0 + exp(-a)); }
+
+static double round_dtype(int dtype, double v) {
+    if (dtype == ORC_BF16) return (double)bf16_bits_to_float(double_to_bf16_bits(v));
+    return (double)(float)v;
+}
+
+/* SwiGLU expert backward over the M rows A [M,d] of one expert, with
+ * w13 [2I,d] (W1 rows, then W3 rows), w2 [d,I] and the gradient dY [M,d] of
+ * its output y = W2 (silu(W1 a) * (W3 a)):
+ *   a, b = W1 A, W3 A (fp32); h = silu(a)*b (dtype)           -- forward values
+ *   dh[m,n] = sum_c dY[m,c] w2[c,n]
+ *   da = dh * b * silu'(a),  silu'(a) = sig(a) (1 + a (1 - sig(a)));  db = dh * silu(a)
+ *       (a, b read back in the dtype; da, db stored in the dtype)
+ *   dA[m,c]   = sum_n da[m,n] w13[n,c] + db[m,n] w13[I+n,c]
+ *   dw2[c,n]  = sum_m dY[m,c] h[m,n]
+ *   dw13[n,c] = sum_m da[m,n] A[m,c];  dw13[I+n,c] = sum_m db[m,n] A[m,c]
+ * M may be 0 (dA empty, weight gradients zero). */
+void orc_swiglu_ffn_backward(int64_t M, int64_t d, int64_t I, int dtype, const void* A,
+                             const void* w13, const void* w2, const void* dY, void* dA,
+                             void* dw13, void* dw2) {
+    double* h = (double*)malloc((size_t)(M * I + 1) * sizeof(double));
+    double* da = (double*)malloc((size_t)(M * I + 1) * sizeof(double));
+    double* db = (double*)malloc((size_t)(M * I + 1) * sizeof(double));
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < I; ++n) {
+            double sa = 0.0, sb = 0.0, sh = 0.0;
+            for (int64_t c = 0; c < d; ++c) {
+                const double av = (double)load_elem(A, dtype, m * d + c);
+                sa += av * (double)load_elem(w13, dtype, n * d + c);
+                sb += av * (double)load_elem(w13, dtype, (I + n) * d + c);
+                sh += (double)load_elem(dY, dtype, m * d + c) *
+                      (double)load_elem(w2, dtype, c * I + n);
+            }
+            const double a = (double)(float)sa, b = (double)(float)sb;
+            h[m * I + n] = round_dtype(dtype, a / (1.0 + exp(-a)) * b);
+            const double ar = round_dtype(dtype, a), br = round_dtype(dtype, b);
+            const double sg = sigmoid_d(ar);
+            da[m * I + n] = round_dtype(dtype, sh * br * sg * (1.0 + ar * (1.0 - sg)));
+            db[m * I + n] = round_dtype(dtype, sh * ar * sg);
+        }
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (int64_t n = 0; n < I; ++n)
+                acc += da[m * I + n] * (double)load_elem(w13, dtype, n * d + c) +
+                       db[m * I + n] * (double)load_elem(w13, dtype, (I + n) * d + c);
+            store_elem_from_double(dA, dtype, m * d + c, acc);
+        }
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t c = 0; c < d; ++c)
+        for (int64_t n = 0; n < I; ++n) {
+            double acc = 0.0;
+            for (int64_t m = 0; m < M; ++m)
+                acc += (double)load_elem(dY, dtype, m * d + c) * h[m * I + n];
+            store_elem_from_double(dw2, dtype, c * I + n, acc);
+        }
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t n = 0; n < I; ++n)
+        for (int64_t c = 0; c < d; ++c) {
+            double ga = 0.0, gb = 0.0;
+            for (int64_t m = 0; m < M; ++m) {
+                const double av = (double)load_elem(A, dtype, m * d + c);
+                ga += da[m * I + n] * av;
+                gb += db[m * I + n] * av;
+            }
+            store_elem_from_double(dw13, dtype, n * d + c, ga);
+            store_elem_from_double(dw13, dtype, (I + n) * d + c, gb);
+        }
+    free(h);
+    free(da);
+    free(db);
+}
+
+/* gate backward.  g_j = s_j / S with S the sum of the chosen s (j < k):
+ * dg_j/ds_m = (delta_jm - g_j) / S, so ds_m = (dgate_m - sum_j dgate_j g_j) / S,
+ * with g_j = s_j / S in double; then through the sigmoid, ds/dz = s (1 - s):
+ *   dz[t,m] = ds_m * s_m * (1 - s_m)   (fp32), s_m = scores[t, idx[t,m]]. */
+void orc_route_backward(int64_t T, int64_t N, int64_t k, const float* scores,
+                        const int32_t* idx, const float* dgate, float* dz) {
+    for (int64_t t = 0; t < T; ++t) {
+        double S = 0.0, gd = 0.0;
+        for (int64_t j = 0; j < k; ++j) S += (double)scores[t * N + idx[t * k + j]];
+        for (int64_t j = 0; j < k; ++j)
+            gd += (double)dgate[t * k + j] * ((double)scores[t * N + idx[t * k + j]] / S);
+        for (int64_t j = 0; j < k; ++j) {
+            const double s = (double)scores[t * N + idx[t * k + j]];
+            dz[t * k + j] = (float)(((double)dgate[t * k + j] - gd) / S * s * (1.0 - s));
+        }
+    }
+}
+
+/* centroid gradient.  z[t,i] = u_t . e_i, so
+ *   dcentroids[i, c] = sum over (t, j) with idx[t,j] = i of dz[t,j] * x[t,c]  (fp32);
+ * rows of experts nobody chose are zero. */
+void orc_centroid_grad(int64_t T, int64_t d, int64_t N, int64_t k, int dtype, const void* x,
+                       const int32_t* idx, const float* dz, float* dcentroids) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < N; ++i)
+        for (int64_t c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (int64_t t = 0; t < T; ++t)
+                for (int64_t j = 0; j < k; ++j)
+                    if (idx[t * k + j] == i)
+                        acc += (double)dz[t * k + j] * (double)load_elem(x, dtype, t * d + c);
+            dcentroids[i * d + c] = (float)acc;
+        }
+}
+
+/* input gradient.  u_t reaches the output through the residual, the shared
+ * expert, each chosen routed expert's rows, and each chosen logit:
+ *   dx[t,c] = dout[t,c] + dx_shared[t,c] + sum_j dx_perm[dst[t,j], c]
+ *             + sum_j dz[t,j] * centroids[idx[t,j], c]          (rounded to the dtype)
+ * dout (no residual) and dx_shared (no shared expert) may be NULL. */
+void orc_input_grad(int64_t T, int64_t d, int64_t k, int dtype, const void* dout,
+                    const void* dx_shared, const void* dx_perm, const int32_t* dst_row,
+                    const float* dz, const int32_t* idx, const float* centroids, void* dx) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t c = 0; c < d; ++c) {
+            double acc = 0.0;
+            if (dout) acc += (double)load_elem(dout, dtype, t * d + c);
+            if (dx_shared) acc += (double)load_elem(dx_shared, dtype, t * d + c);
+            for (int64_t j = 0; j < k; ++j) {
+                acc += (double)load_elem(dx_perm, dtype, (int64_t)dst_row[t * k + j] * d + c);
+                acc += (double)dz[t * k + j] * (double)centroids[(int64_t)idx[t * k + j] * d + c];
+            }
+            store_elem_from_double(dx, dtype, t * d + c, acc);
+        }
 }

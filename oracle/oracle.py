@@ -65,6 +65,11 @@ def _declare(L):
         "orc_combine": [I64, I64, I64, I, P, P, P, P, P, P],
         "orc_bias_update": [I64, I64, P, F, P],
         "orc_round_to_dtype": [I64, I, P, P],
+        "orc_combine_backward": [I64, I64, I64, I, P, P, P, P, P, P],
+        "orc_swiglu_ffn_backward": [I64, I64, I64, I, P, P, P, P, P, P, P],
+        "orc_route_backward": [I64, I64, I64, P, P, P, P],
+        "orc_centroid_grad": [I64, I64, I64, I64, I, P, P, P, P],
+        "orc_input_grad": [I64, I64, I64, I, P, P, P, P, P, P, P, P],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -336,3 +341,117 @@ def layer_forward(inp, cfg, residual=True):
     if fp8:
         res.update(x_q=xq, x_s=xs, x_q_perm=xq_perm, x_s_perm=xs_perm)
     return res
+
+
+# ---------------------------------------------------------------- backward
+
+def combine_backward(dout, y_perm, gate, dst_row):
+    """dy_perm[dst[t,j]] = gate[t,j] * dout[t] (dtype), dgate[t,j] = dout[t] . y_perm[dst[t,j]]."""
+    dout = np.ascontiguousarray(dout)
+    y_perm = _c(y_perm, dout.dtype)
+    gate = _c(gate, np.float32)
+    dst = _c(dst_row, np.int32)
+    T, k = gate.shape
+    d = dout.shape[1]
+    dy_perm = np.empty((T * k, d), dout.dtype)
+    dgate = np.empty((T, k), np.float32)
+    lib().orc_combine_backward(T, d, k, dtype_code(dout), _p(dout), _p(y_perm), _p(gate),
+                               _p(dst), _p(dy_perm), _p(dgate))
+    return dy_perm, dgate
+
+
+def swiglu_ffn_backward(A, w13, w2, dY):
+    """One expert's backward: (dA [M,d], dw13 [2I,d], dw2 [d,I]) for the rows A
+    and the output gradient dY."""
+    A = np.ascontiguousarray(A)
+    dt = dtype_code(A)
+    w13 = _c(w13, A.dtype)
+    w2 = _c(w2, A.dtype)
+    dY = _c(dY, A.dtype)
+    M, d = A.shape
+    I = w13.shape[0] // 2
+    assert w13.shape == (2 * I, d) and w2.shape == (d, I) and dY.shape == (M, d)
+    dA = np.empty((M, d), A.dtype)
+    dw13 = np.empty((2 * I, d), A.dtype)
+    dw2 = np.empty((d, I), A.dtype)
+    lib().orc_swiglu_ffn_backward(M, d, I, dt, _p(A), _p(w13), _p(w2), _p(dY), _p(dA),
+                                  _p(dw13), _p(dw2))
+    return dA, dw13, dw2
+
+
+def route_backward(scores, idx, dgate):
+    """dz[t,j]: gradient of the chosen logits from the gate gradient."""
+    scores = _c(scores, np.float32)
+    idx = _c(idx, np.int32)
+    dgate = _c(dgate, np.float32)
+    T, N = scores.shape
+    k = idx.shape[1]
+    dz = np.empty((T, k), np.float32)
+    lib().orc_route_backward(T, N, k, _p(scores), _p(idx), _p(dgate), _p(dz))
+    return dz
+
+
+def centroid_grad(x, idx, dz, N):
+    x = np.ascontiguousarray(x)
+    idx = _c(idx, np.int32)
+    dz = _c(dz, np.float32)
+    T, d = x.shape
+    k = idx.shape[1]
+    dE = np.empty((N, d), np.float32)
+    lib().orc_centroid_grad(T, d, N, k, dtype_code(x), _p(x), _p(idx), _p(dz), _p(dE))
+    return dE
+
+
+def input_grad(dout, dx_shared, dx_perm, dst_row, dz, idx, centroids):
+    """dx = dout (residual; None = no residual) + dx_shared (None = no shared
+    expert) + the routed rows' gradients + the logits' gradients."""
+    dx_perm = np.ascontiguousarray(dx_perm)
+    dt = dtype_code(dx_perm)
+    dst = _c(dst_row, np.int32)
+    dz = _c(dz, np.float32)
+    idx = _c(idx, np.int32)
+    E = _c(centroids, np.float32)
+    T, k = dst.shape
+    d = dx_perm.shape[1]
+    if dout is not None:
+        dout = _c(dout, dx_perm.dtype)
+    if dx_shared is not None:
+        dx_shared = _c(dx_shared, dx_perm.dtype)
+    dx = np.empty((T, d), dx_perm.dtype)
+    lib().orc_input_grad(T, d, k, dt, _p(dout), _p(dx_shared), _p(dx_perm), _p(dst), _p(dz),
+                         _p(idx), _p(E), _p(dx))
+    return dx
+
+
+def layer_backward(inp, cfg, fwd, dout, residual=True):
+    """Gradients of the layer (bf16 or fp32 storage, no FP8) for the upstream
+    gradient ``dout`` [T,d], given the inputs ``inp`` and the forward's results
+    ``fwd`` (from layer_forward).  Returns dx, dcentroids, dw13 [N,2I,d],
+    dw2 [N,d,I], dws13, dws2 and the intermediates dy_perm, dgate, dz, dx_perm,
+    dx_shared."""
+    assert not cfg.get("fp8", False), "the backward covers bf16 and fp32 storage"
+    N = cfg["N"]
+    x = inp["x"]
+    T, d = x.shape
+    dout = _c(dout, x.dtype)
+    offsets = fwd["offsets"]
+    dy_perm, dgate = combine_backward(dout, fwd["y_perm"], fwd["gate"], fwd["dst_row"])
+    x_perm = fwd["x_perm"]
+    dx_perm = np.empty_like(x_perm)
+    dw13 = np.empty_like(inp["w13"])
+    dw2 = np.empty_like(inp["w2"])
+    for e in range(N):
+        a, b = offsets[e], offsets[e + 1]
+        dA, dw13[e], dw2[e] = swiglu_ffn_backward(x_perm[a:b], inp["w13"][e], inp["w2"][e],
+                                                  dy_perm[a:b])
+        dx_perm[a:b] = dA
+    has_shared = inp.get("ws13") is not None and fwd.get("y_shared") is not None
+    dx_shared = dws13 = dws2 = None
+    if has_shared:
+        dx_shared, dws13, dws2 = swiglu_ffn_backward(x, inp["ws13"], inp["ws2"], dout)
+    dz = route_backward(fwd["scores"], fwd["idx"], dgate)
+    dE = centroid_grad(x, fwd["idx"], dz, N)
+    dx = input_grad(dout if residual else None, dx_shared, dx_perm, fwd["dst_row"], dz,
+                    fwd["idx"], inp["centroids"])
+    return dict(dx=dx, dcentroids=dE, dw13=dw13, dw2=dw2, dws13=dws13, dws2=dws2,
+                dy_perm=dy_perm, dgate=dgate, dz=dz, dx_perm=dx_perm, dx_shared=dx_shared)
