@@ -1,0 +1,110 @@
+/*
+ * moe_backward.h -- C ABI of libmoe, backward pass: the gradients of the layer
+ * forward declared in moe.h, for bf16 and fp32 storage (gemm_dtype ==
+ * act_dtype; FP8 expert GEMMs have no backward here yet).
+ *
+ * The layer, from the DeepSeek-V3 report reading guide (xyznot.com/de),
+ * "Methode", item 2:
+ *   h'_t = u_t + FFN^(s)(u_t) + sum_j g_{t,j} FFN^(r)_{idx_j}(u_t)
+ *   s_{i,t} = Sigmoid(u_t^T e_i),  g_{t,j} = s_{t,idx_j} / sum_j' s_{t,idx_j'}
+ * with FFN read as SwiGLU without biases, W2 (silu(W1 u) * (W3 u)).  The
+ * selection idx is piecewise constant and the balancing bias b_i only enters
+ * the selection key, so neither has a gradient.  Given dout = dL/dh' the chain
+ * rule splits into four calls, run in this order after a forward step whose
+ * buffers (scores, idx, gate, offsets, src_token, dst_row, x_perm, y_perm)
+ * are kept:
+ *   moe_combine_backward     dout -> routed-row gradients dy_perm and dgate
+ *   moe_expert_ffn_backward  dy_perm, dout -> dx_perm, dx_shared and every
+ *                            expert's weight gradients
+ *   moe_route_backward       dgate -> logit gradients dz and the centroid
+ *                            gradient
+ *   moe_input_grad           dout + dx_shared + routed rows + dz e -> dx
+ * The shared expert's output gradient and the residual's are dout itself.
+ *
+ * The common rules of moe.h hold: device pointers owned by the caller
+ * (cfg on the host), dense row-major 16-byte-aligned tensors, asynchronous on
+ * `stream`, no allocation, arguments validated before anything is enqueued,
+ * MOE_OK or an error code with moe_last_error(), bitwise deterministic.
+ * Accumulation is fp32; each output is rounded once to its dtype.
+ */
+#ifndef MOE_BACKWARD_H
+#define MOE_BACKWARD_H
+
+#include "moe.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Backward of moe_combine.  out[t] = x[t] + y_shared[t] + sum_j gate[t,j] y_perm[dst_row[t,j]]:
+ *  dout    [T, d]    act_dtype  upstream gradient dL/dh'
+ *  y_perm  [T*k, d]  act_dtype  the forward's routed expert outputs
+ *  gate, dst_row [T, k]          the forward's gates and rows
+ *  dy_perm [T*k, d]  act_dtype  out, dy_perm[dst_row[t,j]] = gate[t,j] * dout[t]
+ *  dgate   [T, k]    fp32       out, dgate[t,j] = dout[t] . y_perm[dst_row[t,j]]
+ * dy_perm must not alias dout or y_perm. */
+int moe_combine_backward(const moe_cfg* cfg, const void* dout, const void* y_perm,
+                         const float* gate, const int32_t* dst_row, void* dy_perm, float* dgate,
+                         void* stream);
+
+/* Bytes of workspace moe_expert_ffn_backward needs: the recomputed a, b, h and
+ * the gradients da, db of every row (bf16 V3 shape: about 1.5 GB). */
+size_t moe_expert_ffn_backward_workspace_size(const moe_cfg* cfg);
+
+/* Backward of the grouped SwiGLU experts (routed experts over their rows of
+ * x_perm, the shared expert over all T rows).  For one expert with rows X:
+ *   a = X W1^T, b = X W3^T, h = silu(a) b   (recomputed; h and a, b stored in act_dtype)
+ *   dh = dY W2;  da = dh b silu'(a), db = dh silu(a)   (stored in act_dtype)
+ *   dX = da W1 + db W3;  dW2 = dY^T h;  dW1 = da^T X;  dW3 = db^T X
+ * with silu'(a) = sig(a) (1 + a (1 - sig(a))).
+ *  x_perm    [T*k, d]      the forward's routed rows
+ *  offsets   [N+1]         the forward's expert row offsets
+ *  w13       [N, 2I, d]    routed gate/up weights, PLAIN row-major (not packed)
+ *  w2        [N, d, I]     routed down weights, plain
+ *  dy_perm   [T*k, d]      from moe_combine_backward
+ *  x_sh      [T, d]        shared-expert input x (NULL if inter_shared == 0)
+ *  ws13 [2Is, d], ws2 [d, Is]  shared weights, plain
+ *  dy_shared [T, d]        gradient of the shared output: dout
+ *  dx_perm   [T*k, d]      out, gradient of each routed row
+ *  dx_shared [T, d]        out, gradient of x through the shared expert
+ *  dw13, dw2, dws13, dws2  out, same shapes as the weights; an expert without
+ *                          rows gets zeros
+ * All in act_dtype.  bf16 needs hidden, inter, inter_shared % 128 == 0. */
+int moe_expert_ffn_backward(const moe_cfg* cfg, const void* x_perm, const int32_t* offsets,
+                            const void* w13, const void* w2, const void* dy_perm,
+                            const void* x_sh, const void* ws13, const void* ws2,
+                            const void* dy_shared, void* dx_perm, void* dx_shared, void* dw13,
+                            void* dw2, void* dws13, void* dws2, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace moe_route_backward needs (T*k fp32). */
+size_t moe_route_backward_workspace_size(const moe_cfg* cfg);
+
+/* Backward of the gates and the affinity.  With S the sum of the chosen s:
+ *   dz[t,j] = (dgate[t,j] - sum_j' dgate[t,j'] s_j'/S) / S * s_j (1 - s_j),
+ *   s_j = scores[t, idx[t,j]]  (S and the weighted sum in double, dz rounded to fp32)
+ *   dcentroids[i] = sum over the rows r of expert i of dz[r] x[src_token[r]]
+ *                   (fp32, rows in order; zero for experts nobody chose)
+ *  x [T, d] act_dtype; scores [T, N] fp32 (the forward's, required here);
+ *  idx, dgate, dst_row [T, k]; offsets [N+1]; src_token [T*k];
+ *  dz [T, k] fp32 out; dcentroids [N, d] fp32 out. */
+int moe_route_backward(const moe_cfg* cfg, const void* x, const float* scores,
+                       const int32_t* idx, const float* dgate, const int32_t* offsets,
+                       const int32_t* src_token, const int32_t* dst_row, float* dz,
+                       float* dcentroids, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Gradient of the layer input:
+ *   dx[t] = dout[t] + dx_shared[t] + sum_j (dx_perm[dst_row[t,j]] + dz[t,j] e_{idx[t,j]})
+ * summed in fp32 in that order, rounded once to act_dtype.  dout may be NULL
+ * (the forward had no residual), dx_shared NULL (no shared expert).
+ * centroids [N, d] fp32; dx [T, d] out, must not alias an input. */
+int moe_input_grad(const moe_cfg* cfg, const void* dout, const void* dx_shared,
+                   const void* dx_perm, const int32_t* dst_row, const float* dz,
+                   const int32_t* idx, const float* centroids, void* dx, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_BACKWARD_H */

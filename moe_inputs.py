@@ -107,6 +107,12 @@ def make_layer_inputs(cfg, seed=0, device="cpu"):
     return inp
 
 
+def make_upstream_grad(cfg, seed=0, device="cpu", T=None):
+    """dL/dh' [T, d] for the backward: N(0, 1) in the storage dtype."""
+    T = cfg["T"] if T is None else T
+    return storage(normal((T, cfg["d"]), 1.0, device, seed, "dout"), cfg["dtype"])
+
+
 # ------------------------------------------------------------------ skewed routing
 
 def make_skew_centroids(cfg, seed=0, device="cpu", c=1.0):

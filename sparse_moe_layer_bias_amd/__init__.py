@@ -7,8 +7,10 @@ for device memory and streams only.  There is no fallback: if ``libmoe.so`` is
 missing, importing the functions fails loudly.
 
 The functions carry the C names: moe_route, moe_permute, moe_expert_ffn,
-moe_combine, moe_bias_update, moe_quantize_weights_fp8, plus the workspace
-size queries.  ``MoeLayer`` (in layer.py) strings them together for one step.
+moe_combine, moe_bias_update, moe_quantize_weights_fp8, the backward calls of
+include/moe_backward.h (moe_combine_backward, moe_expert_ffn_backward,
+moe_route_backward, moe_input_grad), plus the workspace size queries.
+``MoeLayer`` (in layer.py) strings them together for one step.
 """
 import ctypes
 import os
@@ -71,6 +73,12 @@ def lib():
             "moe_pack_weights": ([C, ctypes.c_int, P, P, P], ctypes.c_int),
             "moe_bias_update": ([I64, I64, P, F, P, P], ctypes.c_int),
             "moe_quantize_weights_fp8": ([I64, I64, I64, P, P, P, P], ctypes.c_int),
+            "moe_combine_backward": ([C, P, P, P, P, P, P, P], ctypes.c_int),
+            "moe_expert_ffn_backward_workspace_size": ([C], SZ),
+            "moe_expert_ffn_backward": ([C] + [P] * 16 + [SZ, P], ctypes.c_int),
+            "moe_route_backward_workspace_size": ([C], SZ),
+            "moe_route_backward": ([C] + [P] * 10 + [SZ, P], ctypes.c_int),
+            "moe_input_grad": ([C] + [P] * 8 + [P], ctypes.c_int),
             "moe_last_error": ([], ctypes.c_char_p),
             "moe_abi_version": ([], ctypes.c_int),
         }
@@ -166,6 +174,43 @@ def moe_bias_update(n_experts, tokens_times_k, counts, gamma, bias, stream=None)
 def moe_quantize_weights_fp8(n_mats, rows, cols, w_bf16, w_q, w_scale, stream=None):
     _check(lib().moe_quantize_weights_fp8(int(n_mats), int(rows), int(cols), _p(w_bf16), _p(w_q),
                                           _p(w_scale), _stream(stream)))
+
+
+# ------------------------------------------------------------------ backward
+
+def moe_combine_backward(cfg, dout, y_perm, gate, dst_row, dy_perm, dgate, stream=None):
+    _check(lib().moe_combine_backward(ctypes.byref(cfg), _p(dout), _p(y_perm), _p(gate),
+                                      _p(dst_row), _p(dy_perm), _p(dgate), _stream(stream)))
+
+
+def moe_expert_ffn_backward_workspace_size(cfg):
+    return lib().moe_expert_ffn_backward_workspace_size(ctypes.byref(cfg))
+
+
+def moe_expert_ffn_backward(cfg, x_perm, offsets, w13, w2, dy_perm, x_sh, ws13, ws2, dy_shared,
+                            dx_perm, dx_shared, dw13, dw2, dws13, dws2, workspace, stream=None):
+    _check(lib().moe_expert_ffn_backward(
+        ctypes.byref(cfg), _p(x_perm), _p(offsets), _p(w13), _p(w2), _p(dy_perm), _p(x_sh),
+        _p(ws13), _p(ws2), _p(dy_shared), _p(dx_perm), _p(dx_shared), _p(dw13), _p(dw2),
+        _p(dws13), _p(dws2), _p(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def moe_route_backward_workspace_size(cfg):
+    return lib().moe_route_backward_workspace_size(ctypes.byref(cfg))
+
+
+def moe_route_backward(cfg, x, scores, idx, dgate, offsets, src_token, dst_row, dz, dcentroids,
+                       workspace, stream=None):
+    _check(lib().moe_route_backward(ctypes.byref(cfg), _p(x), _p(scores), _p(idx), _p(dgate),
+                                    _p(offsets), _p(src_token), _p(dst_row), _p(dz),
+                                    _p(dcentroids), _p(workspace), _nbytes(workspace),
+                                    _stream(stream)))
+
+
+def moe_input_grad(cfg, dout, dx_shared, dx_perm, dst_row, dz, idx, centroids, dx, stream=None):
+    _check(lib().moe_input_grad(ctypes.byref(cfg), _p(dout), _p(dx_shared), _p(dx_perm),
+                                _p(dst_row), _p(dz), _p(idx), _p(centroids), _p(dx),
+                                _stream(stream)))
 
 
 def moe_abi_version():

@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstring>
 
+#include "moe_backward.h"
 #include "moe_internal.h"
 
 namespace {
@@ -116,7 +117,7 @@ int set_error(int code, const char* msg) {
 
 extern "C" {
 
-int moe_abi_version(void) { return 2; }
+int moe_abi_version(void) { return 3; }
 
 const char* moe_last_error(void) { return g_err; }
 
@@ -297,6 +298,136 @@ int moe_quantize_weights_fp8(int64_t n_mats, int64_t rows, int64_t cols, const v
     }
     return hip_status(fn, moe::launch_quantize_weights(n_mats, rows, cols, w_bf16, w_q, w_scale,
                                                        (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ backward
+
+extern "C" {
+
+int moe_combine_backward(const moe_cfg* cfg, const void* dout, const void* y_perm,
+                         const float* gate, const int32_t* dst_row, void* dy_perm, float* dgate,
+                         void* stream) {
+    const char* fn = "moe_combine_backward";
+    if (int r = check_cfg(fn, cfg)) return r;
+    if (cfg->tokens > 0) {
+        REQ_PTR(dout);
+        REQ_PTR(y_perm);
+        REQ_PTR(gate);
+        REQ_PTR(dst_row);
+        REQ_PTR(dy_perm);
+        REQ_PTR(dgate);
+        if (dy_perm == dout || dy_perm == y_perm)
+            return fail(MOE_ERR_ARG, "%s: dy_perm must not alias an input", fn);
+    }
+    return hip_status(fn, moe::launch_combine_backward(*cfg, dout, y_perm, gate, dst_row, dy_perm,
+                                                       dgate, (hipStream_t)stream));
+}
+
+size_t moe_expert_ffn_backward_workspace_size(const moe_cfg* cfg) {
+    if (!cfg) return 0;
+    return moe::ffn_backward_workspace_bytes(*cfg);
+}
+
+int moe_expert_ffn_backward(const moe_cfg* cfg, const void* x_perm, const int32_t* offsets,
+                            const void* w13, const void* w2, const void* dy_perm,
+                            const void* x_sh, const void* ws13, const void* ws2,
+                            const void* dy_shared, void* dx_perm, void* dx_shared, void* dw13,
+                            void* dw2, void* dws13, void* dws2, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    const char* fn = "moe_expert_ffn_backward";
+    if (int r = check_cfg(fn, cfg)) return r;
+    if (int r = check_ffn_shape(fn, cfg)) return r;
+    if (cfg->gemm_dtype != cfg->act_dtype)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: the backward covers bf16 and fp32 storage only", fn);
+    // every routed weight gradient is written, also with no tokens (zeros)
+    REQ_PTR(w13);
+    REQ_PTR(w2);
+    REQ_PTR(dw13);
+    REQ_PTR(dw2);
+    REQ_PTR(offsets);
+    REQ_PTR(workspace);
+    if (cfg->tokens > 0) {
+        REQ_PTR(x_perm);
+        REQ_PTR(dy_perm);
+        REQ_PTR(dx_perm);
+        if (cfg->inter_shared > 0) {
+            REQ_PTR(x_sh);
+            REQ_PTR(ws13);
+            REQ_PTR(ws2);
+            REQ_PTR(dy_shared);
+            REQ_PTR(dx_shared);
+            REQ_PTR(dws13);
+            REQ_PTR(dws2);
+        }
+    }
+    if (cfg->act_dtype == MOE_F32) {
+        // one thread per output element
+        const int64_t T = cfg->tokens, I = cfg->inter, Is = cfg->inter_shared, d = cfg->hidden;
+        const int64_t big = (T * cfg->top_k + T) * (I > Is ? I : Is) + cfg->n_experts * 2 * I * d;
+        if (big > (int64_t)1 << 38)
+            return fail(MOE_ERR_UNSUPPORTED, "%s: fp32 layer too large for the VALU path", fn);
+    }
+    if (workspace_bytes < moe_expert_ffn_backward_workspace_size(cfg))
+        return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes,
+                    moe_expert_ffn_backward_workspace_size(cfg));
+    moe::FfnBwdArgs a{x_perm, offsets, w13, w2, dy_perm, x_sh, ws13, ws2, dy_shared,
+                      dx_perm, dx_shared, dw13, dw2, dws13, dws2};
+    return hip_status(fn, moe::launch_expert_ffn_backward(*cfg, a, workspace, (hipStream_t)stream));
+}
+
+size_t moe_route_backward_workspace_size(const moe_cfg* cfg) {
+    if (!cfg) return 0;
+    return (size_t)(cfg->tokens * cfg->top_k * 4);
+}
+
+int moe_route_backward(const moe_cfg* cfg, const void* x, const float* scores,
+                       const int32_t* idx, const float* dgate, const int32_t* offsets,
+                       const int32_t* src_token, const int32_t* dst_row, float* dz,
+                       float* dcentroids, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    const char* fn = "moe_route_backward";
+    if (int r = check_cfg(fn, cfg)) return r;
+    REQ_PTR(offsets);
+    REQ_PTR(dcentroids);
+    if (cfg->tokens > 0) {
+        REQ_PTR(x);
+        REQ_PTR(scores);
+        REQ_PTR(idx);
+        REQ_PTR(dgate);
+        REQ_PTR(src_token);
+        REQ_PTR(dst_row);
+        REQ_PTR(dz);
+        REQ_PTR(workspace);
+        if (workspace_bytes < moe_route_backward_workspace_size(cfg))
+            return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes,
+                        moe_route_backward_workspace_size(cfg));
+    }
+    return hip_status(fn, moe::launch_route_backward(*cfg, x, scores, idx, dgate, offsets,
+                                                     src_token, dst_row, dz, (float*)workspace,
+                                                     dcentroids, (hipStream_t)stream));
+}
+
+int moe_input_grad(const moe_cfg* cfg, const void* dout, const void* dx_shared,
+                   const void* dx_perm, const int32_t* dst_row, const float* dz,
+                   const int32_t* idx, const float* centroids, void* dx, void* stream) {
+    const char* fn = "moe_input_grad";
+    if (int r = check_cfg(fn, cfg)) return r;
+    if (cfg->tokens > 0) {
+        REQ_PTR(dx_perm);
+        REQ_PTR(dst_row);
+        REQ_PTR(dz);
+        REQ_PTR(idx);
+        REQ_PTR(centroids);
+        REQ_PTR(dx);
+        OPT_PTR(dout);
+        OPT_PTR(dx_shared);
+        if (dx == dout || dx == dx_shared || dx == dx_perm)
+            return fail(MOE_ERR_ARG, "%s: dx must not alias an input", fn);
+    }
+    return hip_status(fn, moe::launch_input_grad(*cfg, dout, dx_shared, dx_perm, dst_row, dz, idx,
+                                                 centroids, dx, (hipStream_t)stream));
 }
 
 }  // extern "C"

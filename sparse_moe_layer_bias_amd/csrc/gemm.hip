@@ -504,6 +504,12 @@ hipError_t launch_pack_weights(const moe_cfg& c, int which, const void* w, void*
     return hipGetLastError();
 }
 
+void launch_tile_map(const int32_t* offsets, int N, int64_t T, bool has_shared, int BM,
+                     int2* tiles, int32_t* counts, int32_t* order, int32_t* keys, hipStream_t st) {
+    ffn_tile_map_kernel<<<1, 256, 0, st>>>(offsets, N, T, has_shared ? 1 : 0, BM, tiles, counts,
+                                           order, keys);
+}
+
 hipError_t launch_expert_ffn_fp8(const moe_cfg& c, const FfnArgs& a, const int2* tiles,
                                  const int32_t* counts, const int32_t* order, void* h_r,
                                  void* h_s, float* hs_r, float* hs_s, int64_t max_r,
@@ -517,8 +523,8 @@ hipError_t launch_expert_ffn(const moe_cfg& c, const FfnArgs& a, void* ws, hipSt
     const int BM = ffn_bm(c);
     const int64_t max_r = ffn_max_routed_tiles(c);
     const int64_t max_s = has_shared ? ffn_max_shared_tiles(c) : 0;
-    ffn_tile_map_kernel<<<1, 256, 0, st>>>(a.offsets, (int)c.n_experts, T, has_shared ? 1 : 0,
-                                           BM, w.tiles, w.counts, w.order, w.keys);
+    launch_tile_map(a.offsets, (int)c.n_experts, T, has_shared, BM, w.tiles, w.counts, w.order,
+                    w.keys, st);
     if (c.gemm_dtype == MOE_FP8_E4M3)
         return launch_expert_ffn_fp8(c, a, w.tiles, w.counts, w.order, w.h_r, w.h_s, w.hs_r, w.hs_s,
                                      max_r, max_s, st);

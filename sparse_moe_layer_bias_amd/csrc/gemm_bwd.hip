@@ -1,0 +1,606 @@
+// gemm_bwd.hip -- backward of the grouped SwiGLU expert FFN (routed experts and
+// the shared expert), bf16 and fp32 storage.
+//
+// Forward (DeepSeek-V3 report reading guide, xyznot.com/de, "Methode" item 2,
+// FFN read as SwiGLU without biases): for the rows X of one expert,
+//   a = X W1^T, b = X W3^T, h = silu(a) * b, y = h W2^T.
+// Given dY = dL/dy, the chain rule gives five grouped GEMMs:
+//   recompute  a, b (stored), h (stored)       X [M,d]    x W13 [2I,d]^T
+//   dgrad down dh = dY W2, then in the epilogue da = dh b silu'(a), db = dh silu(a)
+//                                              dY [M,d]   x W2 [d,I]
+//   dgrad up   dX = [da db] W13                [M,2I]     x W13 [2I,d]
+//   wgrad down dW2 = dY^T h                    contraction over the M rows
+//   wgrad up   dW13 = [da db]^T X              contraction over the M rows
+// silu'(a) = sig(a) (1 + a (1 - sig(a))).
+//
+// Every GEMM here computes C[m][n] = sum_k A(m,k) B(n,k) for one 128 x 128 tile
+// of C with 4 wavefronts of 64 x 64 each, on v_mfma_f32_16x16x32_bf16.  An
+// operand is either stored K-contiguous ("direct": rows of A or B are rows in
+// memory) or K-strided ("transposed": the weight matrices read against their
+// storage order, and the token rows of the weight gradients, whose contraction
+// runs over tokens).  Both land in LDS in one layout -- [row][64 contraction
+// elements], 16-byte chunks swizzled as in the forward kernels -- so the MFMA
+// loop is the same for every GEMM: transposed operands are loaded as 4 x 16
+// bytes (4 consecutive k of 8 consecutive rows) per thread and transposed in
+// registers before the LDS store.  Two LDS stages; global loads for stage k+1
+// are in flight while stage k is multiplied.
+#include "gemm_common.h"
+
+namespace moe {
+
+enum BwdOp { OP_RECOMP = 0, OP_DGRAD_DOWN = 1, OP_DGRAD_UP = 2, OP_WGRAD_DOWN = 3, OP_WGRAD_UP = 4 };
+
+struct BwdParams {
+    const int2* tiles;      // row tiles (group, first row): routed, then shared
+    const int32_t* counts;  // [0] routed row tiles, [1] shared row tiles
+    const int32_t* offsets;
+    int N;
+    int has_shared;
+    int64_t ntn;  // units per row tile (row-tiled GEMMs) or per group (weight gradients)
+    int64_t ntc;  // weight gradients: column tiles per row of tiles
+    int64_t T, TK, d, I_r, I_s;
+    const void* x_perm;
+    const void* x;
+    const void* dy_perm;
+    const void* dy_s;
+    const void* w13;
+    const void* w2;
+    const void* ws13;
+    const void* ws2;
+    void* ab_r;
+    void* ab_s;
+    void* h_r;
+    void* h_s;
+    void* dab_r;
+    void* dab_s;
+    void* dx_perm;
+    void* dx_s;
+    void* dw13;
+    void* dw2;
+    void* dws13;
+    void* dws2;
+};
+
+// One group's view: routed expert g < N over its rows of the permuted arrays,
+// or the shared expert (g == N) over all T tokens.
+template <typename E>
+struct Grp {
+    int64_t M, I;
+    const E* X;
+    const E* dY;
+    const E* W13;
+    const E* W2;
+    E* ab;    // [M][2I]: a in columns 0..I-1, b in I..2I-1
+    E* h;     // [M][I]
+    E* dab;   // [M][2I]: da, db
+    E* dX;    // [M][d]
+    E* dW13;  // [2I][d]
+    E* dW2;   // [d][I]
+};
+
+template <typename E>
+__device__ __forceinline__ void group_view(const BwdParams& p, int g, Grp<E>& v) {
+    const int64_t d = p.d;
+    if (g < p.N) {
+        const int64_t rb = p.offsets[g];
+        const int64_t I = p.I_r;
+        v.M = p.offsets[g + 1] - rb;
+        v.I = I;
+        v.X = (const E*)p.x_perm + rb * d;
+        v.dY = (const E*)p.dy_perm + rb * d;
+        v.W13 = (const E*)p.w13 + (int64_t)g * 2 * I * d;
+        v.W2 = (const E*)p.w2 + (int64_t)g * d * I;
+        v.ab = (E*)p.ab_r + rb * 2 * I;
+        v.h = (E*)p.h_r + rb * I;
+        v.dab = (E*)p.dab_r + rb * 2 * I;
+        v.dX = (E*)p.dx_perm + rb * d;
+        v.dW13 = (E*)p.dw13 + (int64_t)g * 2 * I * d;
+        v.dW2 = (E*)p.dw2 + (int64_t)g * d * I;
+    } else {
+        v.M = p.T;
+        v.I = p.I_s;
+        v.X = (const E*)p.x;
+        v.dY = (const E*)p.dy_s;
+        v.W13 = (const E*)p.ws13;
+        v.W2 = (const E*)p.ws2;
+        v.ab = (E*)p.ab_s;
+        v.h = (E*)p.h_s;
+        v.dab = (E*)p.dab_s;
+        v.dX = (E*)p.dx_s;
+        v.dW13 = (E*)p.dws13;
+        v.dW2 = (E*)p.dws2;
+    }
+}
+
+// extents of C (rows, columns) and of the contraction for one group
+template <int OP>
+__device__ __forceinline__ void op_extents(int64_t M, int64_t I, int64_t d, int64_t& R,
+                                           int64_t& C, int64_t& K) {
+    if (OP == OP_RECOMP) { R = M; C = I; K = d; }             // C columns = h columns
+    else if (OP == OP_DGRAD_DOWN) { R = M; C = I; K = d; }
+    else if (OP == OP_DGRAD_UP) { R = M; C = d; K = 2 * I; }
+    else if (OP == OP_WGRAD_DOWN) { R = d; C = I; K = M; }
+    else { R = 2 * I; C = d; K = M; }
+}
+
+// Unit of a launch -> (group, first C row, first C column); false = no work.
+// Row-tiled GEMMs walk the tile list (ntn column tiles per row tile); weight
+// gradients walk groups x (row tile, column tile), shared expert first: its
+// contraction runs over all T tokens, the longest units of the launch.
+template <int OP>
+__device__ __forceinline__ bool bwd_unit(const BwdParams& p, int64_t u, int& g, int64_t& r0,
+                                         int64_t& c0, int CT) {
+    if (OP <= OP_DGRAD_UP) {
+        const int64_t ti = u / p.ntn, nt = u % p.ntn;
+        if (ti >= (int64_t)p.counts[0] + p.counts[1]) return false;
+        const int2 t = p.tiles[ti];
+        g = t.x;
+        r0 = t.y;
+        c0 = nt * CT;
+    } else {
+        const int64_t gi = u / p.ntn, rem = u % p.ntn;
+        if (p.has_shared)
+            g = gi == 0 ? p.N : (int)gi - 1;
+        else
+            g = (int)gi;
+        if (g > p.N || (g == p.N && !p.has_shared)) return false;
+        r0 = (rem / p.ntc) * CT;
+        c0 = (rem % p.ntc) * CT;
+    }
+    return true;
+}
+
+// ---------------------------------------------------------------- bf16 MFMA
+
+constexpr int BT = 128;   // C tile rows and columns (recompute: 64 h columns)
+constexpr int BBK = 64;   // contraction elements per LDS stage
+constexpr int BW_THREADS = 256;
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <int OP>
+__global__ void __launch_bounds__(BW_THREADS) bwd_gemm_bf16_kernel(BwdParams p) {
+    constexpr bool A_T = OP >= OP_WGRAD_DOWN;  // A stored [K][rows]
+    constexpr bool B_T = OP != OP_RECOMP;      // B stored [K][rows]
+    constexpr int CT = OP == OP_RECOMP ? 64 : BT;
+    int g;
+    int64_t r0, c0;
+    if (!bwd_unit<OP>(p, blockIdx.x, g, r0, c0, CT)) return;
+    Grp<uint16_t> v;
+    group_view(p, g, v);
+    const int64_t d = p.d, I = v.I;
+    int64_t R, C, K;
+    op_extents<OP>(v.M, I, d, R, C, K);
+    if (r0 >= R || c0 >= C) return;
+
+    // operands: base of the tile, row stride, rows present from the tile start
+    const uint16_t* a_base;
+    const uint16_t* b_base;
+    int64_t a_ld, b_ld, a_rows, b_rows;
+    if (OP == OP_RECOMP) {
+        a_base = v.X + r0 * d; a_ld = d; a_rows = R - r0;
+        b_base = v.W13; b_ld = d; b_rows = 0;  // row map below
+    } else if (OP == OP_DGRAD_DOWN) {
+        a_base = v.dY + r0 * d; a_ld = d; a_rows = R - r0;
+        b_base = v.W2 + c0; b_ld = I; b_rows = I - c0;
+    } else if (OP == OP_DGRAD_UP) {
+        a_base = v.dab + r0 * 2 * I; a_ld = 2 * I; a_rows = R - r0;
+        b_base = v.W13 + c0; b_ld = d; b_rows = d - c0;
+    } else if (OP == OP_WGRAD_DOWN) {
+        a_base = v.dY + r0; a_ld = d; a_rows = d - r0;
+        b_base = v.h + c0; b_ld = I; b_rows = I - c0;
+    } else {
+        a_base = v.dab + r0; a_ld = 2 * I; a_rows = 2 * I - r0;
+        b_base = v.X + c0; b_ld = d; b_rows = d - c0;
+    }
+
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[2][2][BT * BBK];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1, wn = wave >> 1;
+    const int l16 = lane & 15, gq = lane >> 4;
+    const int nk = (int)((K + BBK - 1) / BBK);
+
+    // ---- loaders (registers), then LDS stores
+    uint4 ra[4], rb[4];
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+    // direct: 128 rows x 8 chunks; thread q = tid + 256 i -> row q/8, chunk q%8
+    auto load_direct = [&](uint4* r, const uint16_t* base, int64_t ld, int64_t rows, int64_t kb,
+                           bool recomp_map) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = tid + BW_THREADS * i;
+            const int row = q >> 3, ch = q & 7;
+            const int64_t kk = kb + ch * 8;
+            int64_t src;
+            bool ok;
+            if (recomp_map) {
+                // rows 0..63: W1 rows c0.., rows 64..127: the matching W3 rows
+                const int64_t hc = c0 + (row & 63);
+                src = (row < 64 ? 0 : I) + hc;
+                ok = hc < I;
+            } else {
+                src = row;
+                ok = row < rows;
+            }
+            r[i] = (ok && kk < K) ? *(const uint4*)(base + src * ld + kk) : zero;
+        }
+    };
+    auto store_direct = [&](uint16_t* s, const uint4* r) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = tid + BW_THREADS * i;
+            const int row = q >> 3, ch = q & 7;
+            *(uint4*)(s + row * BBK + sub_chunk8(row, ch) * 8) = r[i];
+        }
+    };
+    // transposed: thread (rq = tid%16, kq = tid/16) loads k = 4kq..4kq+3 of
+    // rows 8rq..8rq+7 (16 bytes each)
+    const int rq = tid & 15, kq = tid >> 4;
+    auto load_trans = [&](uint4* r, const uint16_t* base, int64_t ld, int64_t rows, int64_t kb) {
+        const bool rok = 8 * rq < rows;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t kr = kb + 4 * kq + j;
+            r[j] = (rok && kr < K) ? *(const uint4*)(base + kr * ld + 8 * rq) : zero;
+        }
+    };
+    auto store_trans = [&](uint16_t* s, const uint4* r) {
+        const uint32_t w0[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
+        const uint32_t w1[4] = {r[1].x, r[1].y, r[1].z, r[1].w};
+        const uint32_t w2[4] = {r[2].x, r[2].y, r[2].z, r[2].w};
+        const uint32_t w3[4] = {r[3].x, r[3].y, r[3].z, r[3].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = 8 * rq + i;
+            const int wi = i >> 1;
+            uint2 o;
+            if ((i & 1) == 0) {
+                o.x = (w0[wi] & 0xffffu) | (w1[wi] << 16);
+                o.y = (w2[wi] & 0xffffu) | (w3[wi] << 16);
+            } else {
+                o.x = (w0[wi] >> 16) | (w1[wi] & 0xffff0000u);
+                o.y = (w2[wi] >> 16) | (w3[wi] & 0xffff0000u);
+            }
+            *(uint2*)(s + row * BBK + sub_chunk8(row, kq >> 1) * 8 + (kq & 1) * 4) = o;
+        }
+    };
+    auto load = [&](int kt) {
+        const int64_t kb = (int64_t)kt * BBK;
+        if (A_T)
+            load_trans(ra, a_base, a_ld, a_rows, kb);
+        else
+            load_direct(ra, a_base, a_ld, a_rows, kb, false);
+        if (B_T)
+            load_trans(rb, b_base, b_ld, b_rows, kb);
+        else
+            load_direct(rb, b_base, b_ld, b_rows, kb, OP == OP_RECOMP);
+    };
+    auto store = [&](int s) {
+        if (A_T) store_trans(smem[s][0], ra); else store_direct(smem[s][0], ra);
+        if (B_T) store_trans(smem[s][1], rb); else store_direct(smem[s][1], rb);
+    };
+
+    // ---- MFMA: D rows = B rows (n), D columns = A rows (m); lane holds
+    // C[m = 16-row block + l16][n = 16-column block + 4 gq + 0..3]
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[j][i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    auto brow = [&](int j) {
+        if (OP == OP_RECOMP) return j < 2 ? wn * 32 + j * 16 : 64 + wn * 32 + (j - 2) * 16;
+        return wn * 64 + j * 16;
+    };
+    uint32_t coff[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) coff[s] = sub_chunk8(l16, 4 * s + gq) * 8;
+    auto compute = [&](int st) {
+        const uint16_t* As = smem[st][0];
+        const uint16_t* Bs = smem[st][1];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            bf16x8_t af[4], bfr[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                af[i] = __builtin_bit_cast(bf16x8_t,
+                                           *(const uint4*)(As + (wm * 64 + i * 16 + l16) * BBK + coff[s]));
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                bfr[j] = __builtin_bit_cast(bf16x8_t,
+                                            *(const uint4*)(Bs + (brow(j) + l16) * BBK + coff[s]));
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[j][i], 0, 0, 0);
+        }
+    };
+
+    if (nk > 0) {
+        load(0);
+        store(0);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        if (kt + 1 < nk) load(kt + 1);
+        compute(kt & 1);
+        if (kt + 1 < nk) store((kt + 1) & 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: direct 8-byte stores (4 consecutive columns per lane)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t m = r0 + wm * 64 + i * 16 + l16;  // C row (group-relative)
+        if (m >= R) continue;
+        if (OP == OP_RECOMP) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int64_t hc = c0 + wn * 32 + j * 16 + 4 * gq;
+                if (hc >= I) continue;
+                float hv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hv[e] = silu_f(acc[j][i][e]) * acc[j + 2][i][e];
+                uint16_t* abr = v.ab + m * 2 * I;
+                *(uint2*)(abr + hc) = make_uint2(pack_bf16x2(acc[j][i][0], acc[j][i][1]),
+                                                 pack_bf16x2(acc[j][i][2], acc[j][i][3]));
+                *(uint2*)(abr + I + hc) = make_uint2(pack_bf16x2(acc[j + 2][i][0], acc[j + 2][i][1]),
+                                                     pack_bf16x2(acc[j + 2][i][2], acc[j + 2][i][3]));
+                *(uint2*)(v.h + m * I + hc) = make_uint2(pack_bf16x2(hv[0], hv[1]),
+                                                         pack_bf16x2(hv[2], hv[3]));
+            }
+        } else if (OP == OP_DGRAD_DOWN) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t n = c0 + wn * 64 + j * 16 + 4 * gq;
+                if (n >= I) continue;
+                const uint16_t* abr = v.ab + m * 2 * I;
+                const uint2 qa = *(const uint2*)(abr + n);
+                const uint2 qb = *(const uint2*)(abr + I + n);
+                const float a[4] = {bf_lo(qa.x), bf_hi(qa.x), bf_lo(qa.y), bf_hi(qa.y)};
+                const float b[4] = {bf_lo(qb.x), bf_hi(qb.x), bf_lo(qb.y), bf_hi(qb.y)};
+                float da[4], db[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-a[e]));
+                    const float dh = acc[j][i][e];
+                    da[e] = dh * b[e] * sg * (1.0f + a[e] * (1.0f - sg));
+                    db[e] = dh * a[e] * sg;
+                }
+                uint16_t* dr = v.dab + m * 2 * I;
+                *(uint2*)(dr + n) = make_uint2(pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3]));
+                *(uint2*)(dr + I + n) = make_uint2(pack_bf16x2(db[0], db[1]), pack_bf16x2(db[2], db[3]));
+            }
+        } else {
+            uint16_t* Cp;
+            int64_t ldc;
+            if (OP == OP_DGRAD_UP) { Cp = v.dX; ldc = d; }
+            else if (OP == OP_WGRAD_DOWN) { Cp = v.dW2; ldc = I; }
+            else { Cp = v.dW13; ldc = d; }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t n = c0 + wn * 64 + j * 16 + 4 * gq;
+                if (n >= C) continue;
+                *(uint2*)(Cp + m * ldc + n) = make_uint2(pack_bf16x2(acc[j][i][0], acc[j][i][1]),
+                                                         pack_bf16x2(acc[j][i][2], acc[j][i][3]));
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- fp32 path
+// Plain VALU kernels for fp32 storage (small layers): one thread per output
+// element, contraction in ascending order with fp32 FMAs.  Row-tiled GEMMs
+// enumerate the TK routed rows then the T shared rows; weight gradients
+// enumerate each group's R x C outputs.
+template <int OP>
+__global__ void __launch_bounds__(256) bwd_f32_kernel(BwdParams p, int64_t cols,
+                                                      int64_t per_r, int64_t total) {
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= total) return;
+    int g;
+    int64_t m, n;
+    if (OP <= OP_DGRAD_UP) {
+        const int64_t row = e / cols;
+        n = e % cols;
+        if (row < p.TK) {
+            int lo = 0, hi = p.N;  // largest g with offsets[g] <= row
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (p.offsets[mid] <= row) lo = mid; else hi = mid;
+            }
+            g = lo;
+            m = row - p.offsets[g];
+        } else {
+            g = p.N;
+            m = row - p.TK;
+        }
+    } else {
+        if (e < (int64_t)p.N * per_r) {
+            g = (int)(e / per_r);
+            m = (e % per_r) / cols;
+            n = (e % per_r) % cols;
+        } else {
+            g = p.N;
+            const int64_t r = e - (int64_t)p.N * per_r;
+            const int64_t cs = OP == OP_WGRAD_DOWN ? p.I_s : p.d;
+            m = r / cs;
+            n = r % cs;
+        }
+    }
+    Grp<float> v;
+    group_view(p, g, v);
+    const int64_t d = p.d, I = v.I;
+    int64_t R, C, K;
+    op_extents<OP>(v.M, I, d, R, C, K);
+    if (m >= R || n >= C) return;
+    if (OP == OP_RECOMP) {
+        float sa = 0.0f, sb = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            const float xv = v.X[m * d + k];
+            sa = __builtin_fmaf(xv, v.W13[n * d + k], sa);
+            sb = __builtin_fmaf(xv, v.W13[(I + n) * d + k], sb);
+        }
+        v.ab[m * 2 * I + n] = sa;
+        v.ab[m * 2 * I + I + n] = sb;
+        v.h[m * I + n] = sa / (1.0f + expf(-sa)) * sb;
+    } else if (OP == OP_DGRAD_DOWN) {
+        float dh = 0.0f;
+        for (int64_t k = 0; k < K; ++k) dh = __builtin_fmaf(v.dY[m * d + k], v.W2[k * I + n], dh);
+        const float a = v.ab[m * 2 * I + n], b = v.ab[m * 2 * I + I + n];
+        const float sg = 1.0f / (1.0f + expf(-a));
+        v.dab[m * 2 * I + n] = dh * b * sg * (1.0f + a * (1.0f - sg));
+        v.dab[m * 2 * I + I + n] = dh * a * sg;
+    } else if (OP == OP_DGRAD_UP) {
+        float s = 0.0f;
+        for (int64_t k = 0; k < K; ++k) s = __builtin_fmaf(v.dab[m * 2 * I + k], v.W13[k * d + n], s);
+        v.dX[m * d + n] = s;
+    } else if (OP == OP_WGRAD_DOWN) {
+        float s = 0.0f;
+        for (int64_t k = 0; k < K; ++k) s = __builtin_fmaf(v.dY[k * d + m], v.h[k * I + n], s);
+        v.dW2[m * I + n] = s;
+    } else {
+        float s = 0.0f;
+        for (int64_t k = 0; k < K; ++k) s = __builtin_fmaf(v.dab[k * 2 * I + m], v.X[k * d + n], s);
+        v.dW13[m * d + n] = s;
+    }
+}
+
+// ---------------------------------------------------------------- launch
+
+struct BwdWs {
+    int2* tiles;
+    int32_t* counts;
+    int32_t* order;
+    int32_t* keys;
+    void *ab_r, *ab_s, *h_r, *h_s, *dab_r, *dab_s;
+};
+
+static int64_t align256(int64_t b) { return (b + 255) & ~int64_t(255); }
+static int64_t bwd_max_routed_tiles(const moe_cfg& c) { return c.tokens * c.top_k / BT + c.n_experts; }
+static int64_t bwd_max_shared_tiles(const moe_cfg& c) { return cdiv(c.tokens, BT); }
+static int64_t bwd_esz(const moe_cfg& c) { return c.act_dtype == MOE_BF16 ? 2 : 4; }
+
+size_t ffn_backward_workspace_bytes(const moe_cfg& c) {
+    const int64_t TK = c.tokens * c.top_k, T = c.tokens, eb = bwd_esz(c);
+    const int64_t I = c.inter, Is = c.inter_shared;
+    int64_t b = align256((bwd_max_routed_tiles(c) + bwd_max_shared_tiles(c)) * 8) + 256;
+    b += 2 * align256(bwd_max_routed_tiles(c) * 4);
+    b += 2 * align256(TK * 2 * I * eb) + align256(TK * I * eb);       // ab, dab, h routed
+    b += 2 * align256(T * 2 * Is * eb) + align256(T * Is * eb);       // shared
+    return (size_t)b;
+}
+
+static BwdWs carve_bwd(const moe_cfg& c, void* ws) {
+    const int64_t TK = c.tokens * c.top_k, T = c.tokens, eb = bwd_esz(c);
+    const int64_t I = c.inter, Is = c.inter_shared;
+    char* q = (char*)ws;
+    BwdWs w{};
+    w.tiles = (int2*)q;
+    q += align256((bwd_max_routed_tiles(c) + bwd_max_shared_tiles(c)) * 8);
+    w.counts = (int32_t*)q;
+    q += 256;
+    w.order = (int32_t*)q;
+    q += align256(bwd_max_routed_tiles(c) * 4);
+    w.keys = (int32_t*)q;
+    q += align256(bwd_max_routed_tiles(c) * 4);
+    w.ab_r = q; q += align256(TK * 2 * I * eb);
+    w.dab_r = q; q += align256(TK * 2 * I * eb);
+    w.h_r = q; q += align256(TK * I * eb);
+    w.ab_s = q; q += align256(T * 2 * Is * eb);
+    w.dab_s = q; q += align256(T * 2 * Is * eb);
+    w.h_s = q;
+    return w;
+}
+
+template <int OP>
+static void launch_bwd_bf16(const BwdParams& p, int64_t units, hipStream_t st) {
+    if (units > 0) bwd_gemm_bf16_kernel<OP><<<dim3((unsigned)units), BW_THREADS, 0, st>>>(p);
+}
+
+template <int OP>
+static void launch_bwd_f32(const BwdParams& p, int64_t cols, int64_t per_r, int64_t total,
+                           hipStream_t st) {
+    if (total > 0)
+        bwd_f32_kernel<OP><<<dim3((unsigned)cdiv(total, 256)), 256, 0, st>>>(p, cols, per_r, total);
+}
+
+static int64_t imax(int64_t a, int64_t b) { return a > b ? a : b; }
+
+hipError_t launch_expert_ffn_backward(const moe_cfg& c, const FfnBwdArgs& a, void* ws,
+                                      hipStream_t st) {
+    const int64_t T = c.tokens, TK = T * c.top_k, d = c.hidden, N = c.n_experts;
+    const int64_t I = c.inter, Is = c.inter_shared;
+    const bool has_shared = Is > 0 && T > 0;
+    BwdWs w = carve_bwd(c, ws);
+    BwdParams p{};
+    p.offsets = a.offsets;
+    p.N = (int)N;
+    p.has_shared = has_shared ? 1 : 0;
+    p.T = has_shared ? T : 0;
+    p.TK = TK;
+    p.d = d;
+    p.I_r = I;
+    p.I_s = has_shared ? Is : 0;
+    p.x_perm = a.x_perm;
+    p.x = a.x_sh;
+    p.dy_perm = a.dy_perm;
+    p.dy_s = a.dy_sh;
+    p.w13 = a.w13;
+    p.w2 = a.w2;
+    p.ws13 = a.ws13;
+    p.ws2 = a.ws2;
+    p.ab_r = w.ab_r;
+    p.ab_s = w.ab_s;
+    p.h_r = w.h_r;
+    p.h_s = w.h_s;
+    p.dab_r = w.dab_r;
+    p.dab_s = w.dab_s;
+    p.dx_perm = a.dx_perm;
+    p.dx_s = a.dx_sh;
+    p.dw13 = a.dw13;
+    p.dw2 = a.dw2;
+    p.dws13 = a.dws13;
+    p.dws2 = a.dws2;
+    const int64_t Ish = p.I_s;
+    const int64_t ng = N + (has_shared ? 1 : 0);
+
+    if (c.act_dtype == MOE_BF16) {
+        if (TK > 0) {
+            const int64_t max_r = bwd_max_routed_tiles(c);
+            const int64_t max_s = has_shared ? bwd_max_shared_tiles(c) : 0;
+            launch_tile_map(a.offsets, (int)N, T, has_shared, BT, w.tiles, w.counts, w.order,
+                            w.keys, st);
+            p.tiles = w.tiles;
+            p.counts = w.counts;
+            // recompute a, b, h (64 h columns per tile)
+            p.ntn = imax(cdiv(I, 64), cdiv(Ish, 64));
+            launch_bwd_bf16<OP_RECOMP>(p, (max_r + max_s) * p.ntn, st);
+            p.ntn = imax(cdiv(I, BT), cdiv(Ish, BT));
+            launch_bwd_bf16<OP_DGRAD_DOWN>(p, (max_r + max_s) * p.ntn, st);
+            p.ntn = cdiv(d, BT);
+            launch_bwd_bf16<OP_DGRAD_UP>(p, (max_r + max_s) * p.ntn, st);
+        }
+        // weight gradients: every group, including experts without rows (zeros)
+        p.ntc = imax(cdiv(I, BT), cdiv(Ish, BT));
+        p.ntn = cdiv(d, BT) * p.ntc;
+        launch_bwd_bf16<OP_WGRAD_DOWN>(p, ng * p.ntn, st);
+        p.ntc = cdiv(d, BT);
+        p.ntn = imax(cdiv(2 * I, BT), cdiv(2 * Ish, BT)) * p.ntc;
+        launch_bwd_bf16<OP_WGRAD_UP>(p, ng * p.ntn, st);
+    } else {
+        const int64_t rows = TK + p.T;
+        const int64_t hcols = imax(I, Ish);
+        launch_bwd_f32<OP_RECOMP>(p, hcols, 0, rows * hcols, st);
+        launch_bwd_f32<OP_DGRAD_DOWN>(p, hcols, 0, rows * hcols, st);
+        launch_bwd_f32<OP_DGRAD_UP>(p, d, 0, rows * d, st);
+        launch_bwd_f32<OP_WGRAD_DOWN>(p, I, d * I, N * d * I + (has_shared ? d * Is : 0), st);
+        launch_bwd_f32<OP_WGRAD_UP>(p, d, 2 * I * d, N * 2 * I * d + (has_shared ? 2 * Is * d : 0), st);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

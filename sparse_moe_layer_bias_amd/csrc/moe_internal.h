@@ -52,6 +52,44 @@ size_t packed_weight_bytes_fp8(const moe_cfg& c, int which);
 hipError_t launch_pack_weights_fp8(const moe_cfg& c, int which, const void* w, void* out,
                                    hipStream_t st);
 hipError_t launch_expert_ffn(const moe_cfg& c, const FfnArgs& a, void* ws, hipStream_t st);
+// device tile list of the grouped GEMMs: routed expert g gets ceil(M_g / BM)
+// tiles (group, first row), then the shared expert's ceil(T / BM); counts[0],
+// counts[1] = their numbers; order = routed tiles by row count, largest first
+void launch_tile_map(const int32_t* offsets, int N, int64_t T, bool has_shared, int BM,
+                     int2* tiles, int32_t* counts, int32_t* order, int32_t* keys, hipStream_t st);
+
+// ---------------------------------------------------------------- backward
+struct FfnBwdArgs {
+    const void* x_perm;
+    const int32_t* offsets;
+    const void* w13;
+    const void* w2;
+    const void* dy_perm;
+    const void* x_sh;
+    const void* ws13;
+    const void* ws2;
+    const void* dy_sh;
+    void* dx_perm;
+    void* dx_sh;
+    void* dw13;
+    void* dw2;
+    void* dws13;
+    void* dws2;
+};
+size_t ffn_backward_workspace_bytes(const moe_cfg& c);
+hipError_t launch_expert_ffn_backward(const moe_cfg& c, const FfnBwdArgs& a, void* ws,
+                                      hipStream_t st);
+hipError_t launch_combine_backward(const moe_cfg& c, const void* dout, const void* y_perm,
+                                   const float* gate, const int32_t* dst_row, void* dy_perm,
+                                   float* dgate, hipStream_t st);
+hipError_t launch_route_backward(const moe_cfg& c, const void* x, const float* scores,
+                                 const int32_t* idx, const float* dgate, const int32_t* offsets,
+                                 const int32_t* src_token, const int32_t* dst_row, float* dz,
+                                 float* dz_perm, float* dcentroids, hipStream_t st);
+hipError_t launch_input_grad(const moe_cfg& c, const void* dout, const void* dx_shared,
+                             const void* dx_perm, const int32_t* dst_row, const float* dz,
+                             const int32_t* idx, const float* centroids, void* dx,
+                             hipStream_t st);
 
 // ---------------------------------------------------------------- combine / bias / prep
 hipError_t launch_combine(const moe_cfg& c, const void* x, const void* y_shared,

@@ -3,15 +3,22 @@ the five calls in order on one stream.
 
     route -> permute -> expert_ffn (routed + shared) -> combine -> bias_update
 
+and, for bf16 / fp32 layers built with ``keep_plain=True``, the backward calls
+of include/moe_backward.h:
+
+    combine_backward -> expert_ffn_backward -> route_backward -> input_grad
+
 (DeepSeek-V3 report reading guide, xyznot.com/de, "Methode" item 2: the layer
 output h'_t, the biased Topk routing and the end-of-step bias rule.)
 """
 import torch
 
-from . import (MoeCfg, cfg_from_dict, moe_bias_update, moe_combine, moe_expert_ffn,
-               moe_expert_ffn_workspace_size, moe_pack_weights, moe_packed_weights_size,
-               moe_permute, moe_permute_workspace_size, moe_quantize_weights_fp8, moe_route,
-               moe_route_workspace_size)
+from . import (MoeCfg, cfg_from_dict, moe_bias_update, moe_combine, moe_combine_backward,
+               moe_expert_ffn, moe_expert_ffn_backward, moe_expert_ffn_backward_workspace_size,
+               moe_expert_ffn_workspace_size, moe_input_grad, moe_pack_weights,
+               moe_packed_weights_size, moe_permute, moe_permute_workspace_size,
+               moe_quantize_weights_fp8, moe_route, moe_route_backward,
+               moe_route_backward_workspace_size, moe_route_workspace_size)
 
 GAMMA = 0.001  # end-of-step bias step (reading guide, "Methode" item 2)
 
@@ -39,7 +46,8 @@ class MoeLayer:
     """Holds the expert weights (and their FP8 form when the config asks for it)
     and every per-step buffer for a batch of T tokens."""
 
-    def __init__(self, cfg, w13, w2, ws13=None, ws2=None, T=None, device="cuda"):
+    def __init__(self, cfg, w13, w2, ws13=None, ws2=None, T=None, device="cuda",
+                 keep_plain=False):
         self.c = dict(cfg)
         if T is not None:
             self.c["T"] = T
@@ -95,6 +103,10 @@ class MoeLayer:
         ws = max(moe_route_workspace_size(self.cfg), moe_permute_workspace_size(self.cfg),
                  moe_expert_ffn_workspace_size(self.cfg), 256)
         self.workspace = torch.empty((ws,), dtype=torch.uint8, device=dev)
+        # the backward reads the plain (unpacked) weights
+        self.plain = (w13, w2, ws13 if has_shared else None, ws2 if has_shared else None) \
+            if keep_plain else None
+        self.grads = None
 
     # the five calls -------------------------------------------------------
     def route(self, x, centroids, bias, stream=None):
@@ -129,3 +141,53 @@ class MoeLayer:
         if update_bias:
             self.bias_update(bias, stream)
         return self.out
+
+    # the backward ------------------------------------------------------------
+    def _grad_buffers(self, centroids):
+        c = self.c
+        T, d, N, k = c["T"], c["d"], c["N"], c["k"]
+        dev = self.out.device
+        act = self.out.dtype
+        w13, w2, ws13, ws2 = self.plain
+        f32 = dict(dtype=torch.float32, device=dev)
+        g = dict(dy_perm=torch.empty((T * k, d), dtype=act, device=dev),
+                 dgate=torch.empty((T, k), **f32),
+                 dx_perm=torch.empty((T * k, d), dtype=act, device=dev),
+                 dx_shared=torch.empty((T, d), dtype=act, device=dev) if ws13 is not None
+                 else None,
+                 dw13=torch.empty_like(w13), dw2=torch.empty_like(w2),
+                 dws13=torch.empty_like(ws13) if ws13 is not None else None,
+                 dws2=torch.empty_like(ws2) if ws2 is not None else None,
+                 dz=torch.empty((T, k), **f32),
+                 dcentroids=torch.empty_like(centroids),
+                 dx=torch.empty((T, d), dtype=act, device=dev))
+        wsb = max(moe_expert_ffn_backward_workspace_size(self.cfg),
+                  moe_route_backward_workspace_size(self.cfg), 256)
+        g["workspace"] = torch.empty((wsb,), dtype=torch.uint8, device=dev)
+        return g
+
+    def backward(self, dout, x, centroids, residual=True, stream=None):
+        """Gradients of the last forward step for the upstream gradient ``dout``
+        [T, d]: returns a dict with dx, dcentroids, dw13, dw2, dws13, dws2 (plus
+        the intermediates dy_perm, dgate, dx_perm, dx_shared, dz).  The buffers
+        are reused across calls."""
+        if self.plain is None:
+            raise RuntimeError("the backward needs the plain weights: build the layer with "
+                               "keep_plain=True")
+        if self.grads is None:
+            self.grads = self._grad_buffers(centroids)
+        g = self.grads
+        w13, w2, ws13, ws2 = self.plain
+        moe_combine_backward(self.cfg, dout, self.y_perm, self.gate, self.dst_row, g["dy_perm"],
+                             g["dgate"], stream)
+        moe_expert_ffn_backward(self.cfg, self.x_perm, self.offsets, w13, w2, g["dy_perm"],
+                                x if ws13 is not None else None, ws13, ws2,
+                                dout if ws13 is not None else None, g["dx_perm"],
+                                g["dx_shared"], g["dw13"], g["dw2"], g["dws13"], g["dws2"],
+                                g["workspace"], stream)
+        moe_route_backward(self.cfg, x, self.scores, self.idx, g["dgate"], self.offsets,
+                           self.src_token, self.dst_row, g["dz"], g["dcentroids"],
+                           g["workspace"], stream)
+        moe_input_grad(self.cfg, dout if residual else None, g["dx_shared"], g["dx_perm"],
+                       self.dst_row, g["dz"], self.idx, centroids, g["dx"], stream)
+        return g

@@ -4,6 +4,15 @@ the tolerance rule.
 Tolerance (floating outputs): |gpu - ref| <= rtol * (|ref| + rms(ref row)),
 elementwise, with rtol 1e-5 (fp32), 2e-2 (bf16), 6e-2 (FP8 GEMMs).
 Integer, index and byte outputs are compared bit for bit.
+
+Gradients of fp32 layers use the same rtol against the RMS of the whole
+tensor instead of the row: |gpu - ref| <= rtol * (|ref| + rms(ref)).  Their
+entries are differences and cancelling sums (silu' vanishes near a = -1.28,
+dL/dz = (dg_j - sum_i dg_i g_i) s (1-s) / S, dot products with small
+results); fp32 evaluation of such a quantity errs by about eps times the size
+of its terms, which is the tensor's typical magnitude, not by eps times the
+result.  With one token the weight gradient rows are single products
+da[n] * x, so a row is one such quantity and the row RMS gives no scale.
 """
 import sys
 
@@ -44,7 +53,22 @@ def assert_close(got, ref, rtol, what=""):
         raise AssertionError("%s: %d/%d elements out of tolerance %g; first at %s: gpu=%r ref=%r"
                              " (max rel err %.3g)" % (what, bad.sum(), bad.size, rtol, tuple(i),
                                                       g2[tuple(i)], r2[tuple(i)],
-                                                      float(np.max(err / (np.abs(r2) + rms)))))
+                                                      float(np.nanmax(err / (np.abs(r2) + rms)))))
+
+
+def assert_close_tensor(got, ref, rtol, what=""):
+    g, r = to_f64(got), to_f64(ref)
+    assert g.shape == r.shape, (what, g.shape, r.shape)
+    if r.size == 0:
+        return
+    rms = float(np.sqrt(np.mean(r ** 2)))
+    err = np.abs(g - r)
+    bad = ~(err <= rtol * (np.abs(r) + rms))
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError("%s: %d/%d elements out of tolerance %g (tensor rms %.3g); first at "
+                             "%s: gpu=%r ref=%r" % (what, bad.sum(), bad.size, rtol, rms, tuple(i),
+                                                    g[tuple(i)], r[tuple(i)]))
 
 
 def assert_close_fp8(got, ref, what="", rtol=RTOL["fp8"]):

@@ -36,9 +36,11 @@ def test_library_exports_every_declared_symbol():
     assert {"moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
             "moe_bias_update"} <= set(names)
     assert {"moe_probe_hbm_read", "moe_probe_mfma"} <= set(names)
+    assert {"moe_combine_backward", "moe_expert_ffn_backward", "moe_route_backward",
+            "moe_input_grad"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert moe.moe_abi_version() == 2
+    assert moe.moe_abi_version() == 3
 
 
 @host_only
@@ -160,4 +162,58 @@ def test_bias_update_and_quantize_validation():
     assert L.moe_bias_update(8, 10, P(FAKE), ctypes.c_float(float("nan")), P(FAKE), None) == \
         moe.MOE_ERR_ARG
     assert L.moe_quantize_weights_fp8(1, 100, 128, P(FAKE), P(FAKE), P(FAKE), None) == \
+        moe.MOE_ERR_ARG
+
+
+# ------------------------------------------------------------------ backward
+
+def _ffn_bwd(cfg, ws_bytes=1 << 40, **over):
+    names = ("x_perm", "offsets", "w13", "w2", "dy_perm", "x_sh", "ws13", "ws2", "dy_shared",
+             "dx_perm", "dx_shared", "dw13", "dw2", "dws13", "dws2", "workspace")
+    args = {n: FAKE for n in names}
+    args.update(over)
+    P = ctypes.c_void_p
+    return moe.lib().moe_expert_ffn_backward(
+        ctypes.byref(cfg), *(P(args[n]) if args[n] else None for n in names), ws_bytes, None)
+
+
+@host_only
+def test_expert_ffn_backward_validation():
+    assert _ffn_bwd(_cfg(dtype="bf16", fp8=True, d=256, I=128, Is=128)) == \
+        moe.MOE_ERR_UNSUPPORTED                        # no FP8 backward
+    assert _ffn_bwd(_cfg(dtype="bf16", d=256, I=96, Is=128)) == moe.MOE_ERR_UNSUPPORTED
+    assert _ffn_bwd(_cfg(), dw13=0) == moe.MOE_ERR_ARG
+    assert _ffn_bwd(_cfg(), dx_shared=0) == moe.MOE_ERR_ARG    # shared expert present
+    assert _ffn_bwd(_cfg(Is=0), dx_shared=0, x_sh=0, ws13=0, ws2=0, dy_shared=0, dws13=0,
+                    dws2=0, ws_bytes=0) == moe.MOE_ERR_WORKSPACE
+    c = _cfg(dtype="bf16", d=256, I=128, Is=128)
+    need = moe.moe_expert_ffn_backward_workspace_size(c)
+    # a, b, h and da, db of T*k routed and T shared rows, bf16
+    assert need >= 2 * (64 * 2 * 2 * 128 * 2 + 64 * 128) + 2 * (64 * 2 * 128 * 2 + 64 * 128)
+    assert _ffn_bwd(c, ws_bytes=need - 1) == moe.MOE_ERR_WORKSPACE
+    assert moe.lib().moe_last_error().decode().startswith("moe_expert_ffn_backward")
+
+
+@host_only
+def test_backward_calls_reject_bad_arguments():
+    L = moe.lib()
+    P = ctypes.c_void_p
+    c = _cfg()
+    # combine backward: dy_perm aliasing dout
+    assert L.moe_combine_backward(ctypes.byref(c), P(FAKE), P(FAKE * 2), P(FAKE * 3),
+                                  P(FAKE * 4), P(FAKE), P(FAKE * 5), None) == moe.MOE_ERR_ARG
+    assert L.moe_combine_backward(ctypes.byref(c), P(FAKE), P(FAKE * 2), None, P(FAKE * 4),
+                                  P(FAKE * 6), P(FAKE * 5), None) == moe.MOE_ERR_ARG
+    # route backward: scores required, workspace of T*k floats
+    rb = lambda **o: L.moe_route_backward(
+        ctypes.byref(c), *(P(o.get(n, FAKE)) if o.get(n, FAKE) else None for n in
+                           ("x", "scores", "idx", "dgate", "offsets", "src_token", "dst_row",
+                            "dz", "dcentroids", "workspace")), o.get("ws", 1 << 20), None)
+    assert rb(scores=0) == moe.MOE_ERR_ARG
+    assert rb(dcentroids=FAKE + 4) == moe.MOE_ERR_ARG
+    assert rb(ws=64 * 2 * 4 - 1) == moe.MOE_ERR_WORKSPACE
+    assert moe.moe_route_backward_workspace_size(c) == 64 * 2 * 4
+    # input gradient: dx aliasing an input
+    assert L.moe_input_grad(ctypes.byref(c), P(FAKE), P(FAKE * 2), P(FAKE * 3), P(FAKE * 4),
+                            P(FAKE * 5), P(FAKE * 6), P(FAKE * 7), P(FAKE * 3), None) == \
         moe.MOE_ERR_ARG
