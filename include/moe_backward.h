@@ -59,23 +59,28 @@ size_t moe_expert_ffn_backward_workspace_size(const moe_cfg* cfg);
  * with silu'(a) = sig(a) (1 + a (1 - sig(a))).
  *  x_perm    [T*k, d]      the forward's routed rows
  *  offsets   [N+1]         the forward's expert row offsets
- *  w13       [N, 2I, d]    routed gate/up weights, PLAIN row-major (not packed)
- *  w2        [N, d, I]     routed down weights, plain
+ *  w13       routed gate/up weights packed as for the forward (moe_pack_weights
+ *            which = 0), used to recompute a, b, h
+ *  w13t      the same weights [N, 2I, d] packed transposed (which = 4), for dX
+ *  w2t       routed down weights [N, d, I] packed transposed (which = 5), for dh
  *  dy_perm   [T*k, d]      from moe_combine_backward
  *  x_sh      [T, d]        shared-expert input x (NULL if inter_shared == 0)
- *  ws13 [2Is, d], ws2 [d, Is]  shared weights, plain
+ *  ws13, ws13t, ws2t       the shared expert's weights packed the same way
+ *                          (which = 2, 6, 7)
  *  dy_shared [T, d]        gradient of the shared output: dout
  *  dx_perm   [T*k, d]      out, gradient of each routed row
  *  dx_shared [T, d]        out, gradient of x through the shared expert
- *  dw13, dw2, dws13, dws2  out, same shapes as the weights; an expert without
- *                          rows gets zeros
- * All in act_dtype.  bf16 needs hidden, inter, inter_shared % 128 == 0. */
+ *  dw13 [N, 2I, d], dw2 [N, d, I], dws13 [2Is, d], dws2 [d, Is]
+ *                          out, plain row-major like the weights; an expert
+ *                          without rows gets zeros
+ * Activations and gradients in act_dtype.  fp32 layers: every packed form is
+ * a plain copy.  bf16 needs hidden, inter, inter_shared % 128 == 0. */
 int moe_expert_ffn_backward(const moe_cfg* cfg, const void* x_perm, const int32_t* offsets,
-                            const void* w13, const void* w2, const void* dy_perm,
-                            const void* x_sh, const void* ws13, const void* ws2,
-                            const void* dy_shared, void* dx_perm, void* dx_shared, void* dw13,
-                            void* dw2, void* dws13, void* dws2, void* workspace,
-                            size_t workspace_bytes, void* stream);
+                            const void* w13, const void* w13t, const void* w2t,
+                            const void* dy_perm, const void* x_sh, const void* ws13,
+                            const void* ws13t, const void* ws2t, const void* dy_shared,
+                            void* dx_perm, void* dx_shared, void* dw13, void* dw2, void* dws13,
+                            void* dws2, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace moe_route_backward needs (T*k fp32). */
 size_t moe_route_backward_workspace_size(const moe_cfg* cfg);

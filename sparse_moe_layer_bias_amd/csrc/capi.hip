@@ -234,7 +234,7 @@ int moe_expert_ffn(const moe_cfg* cfg, const void* x_perm, const float* x_perm_s
 }
 
 size_t moe_packed_weights_size(const moe_cfg* cfg, int which) {
-    if (!cfg || which < 0 || which > 3) return 0;
+    if (!cfg || which < 0 || which > 7) return 0;
     return moe::packed_weight_bytes(*cfg, which);
 }
 
@@ -243,8 +243,10 @@ int moe_pack_weights(const moe_cfg* cfg, int which, const void* w, void* w_packe
     const char* fn = "moe_pack_weights";
     if (int r = check_cfg(fn, cfg)) return r;
     if (int r = check_ffn_shape(fn, cfg)) return r;
-    if (which < 0 || which > 3) return fail(MOE_ERR_ARG, "%s: which must be 0..3", fn);
-    if (which >= 2 && cfg->inter_shared == 0)
+    if (which < 0 || which > 7) return fail(MOE_ERR_ARG, "%s: which must be 0..7", fn);
+    if (which >= 4 && cfg->gemm_dtype == MOE_FP8_E4M3)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: transposed packs are for bf16 / fp32 layers", fn);
+    if ((which == 2 || which == 3 || which == 6 || which == 7) && cfg->inter_shared == 0)
         return fail(MOE_ERR_ARG, "%s: no shared expert (inter_shared == 0)", fn);
     REQ_PTR(w);
     REQ_PTR(w_packed);
@@ -331,31 +333,33 @@ size_t moe_expert_ffn_backward_workspace_size(const moe_cfg* cfg) {
 }
 
 int moe_expert_ffn_backward(const moe_cfg* cfg, const void* x_perm, const int32_t* offsets,
-                            const void* w13, const void* w2, const void* dy_perm,
-                            const void* x_sh, const void* ws13, const void* ws2,
-                            const void* dy_shared, void* dx_perm, void* dx_shared, void* dw13,
-                            void* dw2, void* dws13, void* dws2, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+                            const void* w13, const void* w13t, const void* w2t,
+                            const void* dy_perm, const void* x_sh, const void* ws13,
+                            const void* ws13t, const void* ws2t, const void* dy_shared,
+                            void* dx_perm, void* dx_shared, void* dw13, void* dw2, void* dws13,
+                            void* dws2, void* workspace, size_t workspace_bytes, void* stream) {
     const char* fn = "moe_expert_ffn_backward";
     if (int r = check_cfg(fn, cfg)) return r;
     if (int r = check_ffn_shape(fn, cfg)) return r;
     if (cfg->gemm_dtype != cfg->act_dtype)
         return fail(MOE_ERR_UNSUPPORTED, "%s: the backward covers bf16 and fp32 storage only", fn);
     // every routed weight gradient is written, also with no tokens (zeros)
-    REQ_PTR(w13);
-    REQ_PTR(w2);
     REQ_PTR(dw13);
     REQ_PTR(dw2);
     REQ_PTR(offsets);
     REQ_PTR(workspace);
     if (cfg->tokens > 0) {
         REQ_PTR(x_perm);
+        REQ_PTR(w13);
+        REQ_PTR(w13t);
+        REQ_PTR(w2t);
         REQ_PTR(dy_perm);
         REQ_PTR(dx_perm);
         if (cfg->inter_shared > 0) {
             REQ_PTR(x_sh);
             REQ_PTR(ws13);
-            REQ_PTR(ws2);
+            REQ_PTR(ws13t);
+            REQ_PTR(ws2t);
             REQ_PTR(dy_shared);
             REQ_PTR(dx_shared);
             REQ_PTR(dws13);
@@ -372,8 +376,8 @@ int moe_expert_ffn_backward(const moe_cfg* cfg, const void* x_perm, const int32_
     if (workspace_bytes < moe_expert_ffn_backward_workspace_size(cfg))
         return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes,
                     moe_expert_ffn_backward_workspace_size(cfg));
-    moe::FfnBwdArgs a{x_perm, offsets, w13, w2, dy_perm, x_sh, ws13, ws2, dy_shared,
-                      dx_perm, dx_shared, dw13, dw2, dws13, dws2};
+    moe::FfnBwdArgs a{x_perm,  offsets, w13,     w13t,      w2t,  dy_perm, x_sh, ws13,  ws13t,
+                      ws2t,    dy_shared, dx_perm, dx_shared, dw13, dw2,     dws13, dws2};
     return hip_status(fn, moe::launch_expert_ffn_backward(*cfg, a, workspace, (hipStream_t)stream));
 }
 

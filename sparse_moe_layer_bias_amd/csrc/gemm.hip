@@ -14,6 +14,14 @@
 // Tile order is XCD-aware (see decode_v2): the units of one tile run on one
 // XCD, back to back, so its token rows are shared in L2; tiles go to the XCDs
 // round-robin so each gets an even share of routed and shared work.
+//
+// The same kernel serves three GEMMs of the backward (gemm_bwd.hip), by mode:
+//   0  gate/up            h = silu(x W1^T) * (x W3^T)
+//   1  down               y = h W2^T  (also the up-projection dgrad dX = [da db] W13,
+//                         with the transposed W13 packed as the weights)
+//   2  gate/up recompute  mode 0, also storing a and b for the backward
+//   3  down dgrad         dh = dY W2 (transposed W2 packed as the weights), and
+//                         in the epilogue da = dh b silu'(a), db = dh silu(a)
 #include "gemm_common.h"
 
 namespace moe {
@@ -154,6 +162,35 @@ __global__ void __launch_bounds__(256) pack_weights_kernel(const uint4* __restri
     out[i] = v;
 }
 
+// Transposed packing, for the backward's dgrad GEMMs: packed row r of weight
+// tile wt is column wt*256 + r of a matrix stored [K][Nout] (zero past Nout),
+// in the same LDS image order as above.
+__global__ void __launch_bounds__(256) pack_weights_t_kernel(const uint16_t* __restrict__ w,
+                                                             uint4* __restrict__ out,
+                                                             int64_t n_mats, int64_t Nout,
+                                                             int64_t K, int64_t ntn) {
+    const int64_t nkc = K / G_SUB;
+    const int64_t per_mat = ntn * nkc * G_WR * G_CPR;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n_mats * per_mat) return;
+    const int64_t mat = i / per_mat;
+    int64_t rem = i % per_mat;
+    const int64_t wt = rem / (nkc * G_WR * G_CPR);
+    rem %= nkc * G_WR * G_CPR;
+    const int64_t kc = rem / (G_WR * G_CPR);
+    const int slot = (int)(rem % (G_WR * G_CPR));
+    const int r = slot / G_CPR, c = sub_chunk8(r, slot % G_CPR);
+    const int64_t col = wt * G_WR + r;
+    uint32_t v[4] = {0, 0, 0, 0};
+    if (col < Nout) {
+        const uint16_t* src = w + (mat * K + kc * G_SUB + c * 8) * Nout + col;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            v[e] = (uint32_t)src[(2 * e) * Nout] | ((uint32_t)src[(2 * e + 1) * Nout] << 16);
+    }
+    out[i] = make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 template <int MODE, int BK, int NS, int NB>
 __device__ __forceinline__ void gemm_bf16_body(const WorkV2& w, uint16_t* smem) {
     constexpr int NSUB = BK / G_SUB;
@@ -273,10 +310,11 @@ __device__ __forceinline__ void gemm_bf16_body(const WorkV2& w, uint16_t* smem) 
     // are padded by 16 bytes so the 16 rows written by a lane group hit
     // distinct banks.
     __syncthreads();  // every wave is done with the stage buffers
-    constexpr int OCOLS = MODE == 0 ? 128 : 256;
+    constexpr bool GU = MODE == 0 || MODE == 2;  // gate/up-shaped tile
+    constexpr int OCOLS = GU ? 128 : 256;
     constexpr int OSTR = OCOLS + 8;  // padded LDS row (elements)
     uint16_t* ot = smem;
-    const int64_t wbase = MODE == 0 ? w.wt * 128 : w.wt * 256;
+    const int64_t wbase = GU ? w.wt * 128 : w.wt * 256;
     auto put = [&](int row, int col, float a0, float a1, float a2, float a3) {
         *(uint2*)(ot + row * OSTR + col) = make_uint2(pack_bf16x2(a0, a1), pack_bf16x2(a2, a3));
     };
@@ -295,7 +333,7 @@ __device__ __forceinline__ void gemm_bf16_body(const WorkV2& w, uint16_t* smem) 
     // 16x16 layout: lane l holds column (token) l%16 and rows 4*(l/16) + v of
     // its block.  gate/up: blocks 0, 1 are the W1 rows and 2, 3 the W3 rows of
     // the wave's h columns 32*wr + 16*i + 4*g + v.
-    if (MODE == 0) {
+    if (GU) {
         if constexpr (NB > 0) {
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
@@ -306,11 +344,55 @@ __device__ __forceinline__ void gemm_bf16_body(const WorkV2& w, uint16_t* smem) 
 #pragma unroll
                     for (int v = 0; v < 4; ++v) h[v] = silu_f(acc[i][j][v]) * acc[i + 2][j][v];
                     put(row, wr * 32 + i * 16 + 4 * g, h[0], h[1], h[2], h[3]);
+                    if (MODE == 2 && row < mc) {
+                        // a and b (rounded to bf16) for the backward: row of E is [a | b]
+                        uint16_t* e = (uint16_t*)w.E + (w.m0 + row) * 2 * w.Nout + wbase +
+                                      wr * 32 + i * 16 + 4 * g;
+                        *(uint2*)e = make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]),
+                                                pack_bf16x2(acc[i][j][2], acc[i][j][3]));
+                        *(uint2*)(e + w.Nout) =
+                            make_uint2(pack_bf16x2(acc[i + 2][j][0], acc[i + 2][j][1]),
+                                       pack_bf16x2(acc[i + 2][j][2], acc[i + 2][j][3]));
+                    }
                 }
             }
         }
         __syncthreads();
         flush_rows(0, (int)mc);
+    } else if (MODE == 3) {
+        // dh of token row m, columns n..n+3 -> da, db (direct 8-byte stores);
+        // a, b are read back from E, the recompute's bf16 copy
+        if constexpr (NB > 0) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const int row = tg * 160 + j * 16 + l16;
+                if (row >= mc) continue;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t n = wbase + wr * 64 + i * 16 + 4 * g;
+                    if (n >= w.Nout) continue;
+                    const uint16_t* e = (const uint16_t*)w.E + (w.m0 + row) * 2 * w.Nout + n;
+                    const uint2 qa = *(const uint2*)e;
+                    const uint2 qb = *(const uint2*)(e + w.Nout);
+                    const float a[4] = {__uint_as_float(qa.x << 16), __uint_as_float(qa.x & 0xffff0000u),
+                                        __uint_as_float(qa.y << 16), __uint_as_float(qa.y & 0xffff0000u)};
+                    const float b[4] = {__uint_as_float(qb.x << 16), __uint_as_float(qb.x & 0xffff0000u),
+                                        __uint_as_float(qb.y << 16), __uint_as_float(qb.y & 0xffff0000u)};
+                    float da[4], db[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-a[v]));
+                        const float dh = acc[i][j][v];
+                        da[v] = dh * b[v] * sg * (1.0f + a[v] * (1.0f - sg));
+                        db[v] = dh * a[v] * sg;
+                    }
+                    uint16_t* o = (uint16_t*)w.C + (w.m0 + row) * 2 * w.Nout + n;
+                    *(uint2*)o = make_uint2(pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3]));
+                    *(uint2*)(o + w.Nout) = make_uint2(pack_bf16x2(db[0], db[1]),
+                                                       pack_bf16x2(db[2], db[3]));
+                }
+            }
+        }
     } else {
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -339,7 +421,8 @@ __global__ void __launch_bounds__(G_THREADS, 1) ffn_gemm_bf16_kernel(GemmParamsV
     WorkV2 w;
     if (!decode_v2<2>(p, MODE, w)) return;
     constexpr int STAGES_EL = NS * (G_WR + G_TR) * BK;
-    constexpr int EPI_EL = MODE == 0 ? G_TR * (128 + 8) : 160 * (256 + 8);
+    constexpr bool GU = MODE == 0 || MODE == 2;
+    constexpr int EPI_EL = GU ? G_TR * (128 + 8) : 160 * (256 + 8);
     __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES_EL > EPI_EL ? STAGES_EL : EPI_EL];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wr = wave % G_WRG, tg = wave / G_WRG;
@@ -348,8 +431,8 @@ __global__ void __launch_bounds__(G_THREADS, 1) ffn_gemm_bf16_kernel(GemmParamsV
     // are past the end of the matrix (last tile of the down projection)
     int64_t nb = (mc - tg * 160 + 15) / 16;
     nb = nb < 0 ? 0 : (nb > 10 ? 10 : nb);
-    const int64_t wbase = MODE == 0 ? w.wt * 128 : w.wt * 256;
-    if (MODE == 1 && wbase + wr * 64 >= w.Nout) nb = 0;
+    const int64_t wbase = GU ? w.wt * 128 : w.wt * 256;
+    if (!GU && wbase + wr * 64 >= w.Nout) nb = 0;
     switch (nb) {
         case 10: gemm_bf16_body<MODE, BK, NS, 10>(w, smem); break;
         case 9: gemm_bf16_body<MODE, BK, NS, 9>(w, smem); break;
@@ -466,22 +549,27 @@ static FfnWs carve_ffn(const moe_cfg& c, void* ws) {
 // ---------------------------------------------------------------- weight packing
 
 struct PackShape {
-    int mode;
+    int mode;  // 0 gate/up, 1 plain rows, 2 transposed (source [K][Nout])
     int64_t n_mats, Nout, K, ntn;
 };
 
+// which: 0/2 W13 (routed/shared), 1/3 W2, and for the backward's dgrad
+// GEMMs 4/6 W13 transposed (rows = d, K = 2I), 5/7 W2 transposed (rows = I, K = d)
 static PackShape pack_shape(const moe_cfg& c, int which) {
-    const bool routed = which == 0 || which == 1;
+    const bool routed = which == 0 || which == 1 || which == 4 || which == 5;
     const int64_t n = routed ? c.n_experts : 1;
     const int64_t I = routed ? c.inter : c.inter_shared;
     if (which == 0 || which == 2) return {0, n, I, c.hidden, cdiv(I, 128)};
-    return {1, n, c.hidden, I, cdiv(c.hidden, 256)};
+    if (which == 1 || which == 3) return {1, n, c.hidden, I, cdiv(c.hidden, 256)};
+    if (which == 4 || which == 6) return {2, n, c.hidden, 2 * I, cdiv(c.hidden, 256)};
+    return {2, n, I, c.hidden, cdiv(I, 256)};
 }
 
 size_t packed_weight_bytes(const moe_cfg& c, int which) {
     const PackShape s = pack_shape(c, which);
     if (c.act_dtype == MOE_F32 && c.gemm_dtype == MOE_F32)
         return (size_t)(s.n_mats * (s.mode == 0 ? 2 * s.Nout : s.Nout) * s.K * 4);
+    if (s.mode == 2 && c.gemm_dtype == MOE_FP8_E4M3) return 0;  // no FP8 backward
     if (c.gemm_dtype == MOE_FP8_E4M3) return packed_weight_bytes_fp8(c, which);
     return (size_t)(s.n_mats * s.ntn * G_WR * s.K * 2);
 }
@@ -495,7 +583,10 @@ hipError_t launch_pack_weights(const moe_cfg& c, int which, const void* w, void*
     if (c.gemm_dtype == MOE_FP8_E4M3) return launch_pack_weights_fp8(c, which, w, out, st);
     const int64_t n = s.n_mats * s.ntn * (s.K / G_SUB) * G_WR * G_CPR;
     const unsigned blocks = (unsigned)cdiv(n, 256);
-    if (s.mode == 0)
+    if (s.mode == 2)
+        pack_weights_t_kernel<<<blocks, 256, 0, st>>>((const uint16_t*)w, (uint4*)out, s.n_mats,
+                                                      s.Nout, s.K, s.ntn);
+    else if (s.mode == 0)
         pack_weights_kernel<0><<<blocks, 256, 0, st>>>((const uint4*)w, (uint4*)out, s.n_mats,
                                                        s.Nout, s.K, s.ntn);
     else
@@ -578,6 +669,90 @@ hipError_t launch_expert_ffn(const moe_cfg& c, const FfnArgs& a, void* ws, hipSt
         ffn_gemm_bf16_kernel<1, MOE_GEMM_BK, MOE_GEMM_NS><<<grid, G_THREADS, 0, st>>>(p);
     else
         ffn_gemm_f32_kernel<1><<<grid, 256, 0, st>>>(p);
+    return hipGetLastError();
+}
+
+}  // namespace moe
+
+namespace moe {
+
+// ---------------------------------------------------------------- backward GEMMs
+// Recompute, down-projection dgrad and up-projection dgrad of the backward,
+// on the forward's kernel (modes 2, 3 and 1).  The tile list is built here with
+// the forward's row tile.
+size_t ffn_bwd_tile_ws_bytes(const moe_cfg& c) {
+    return (size_t)(align256((ffn_max_routed_tiles(c) + ffn_max_shared_tiles(c)) * 8) + 256 +
+                    2 * align256(ffn_max_routed_tiles(c) * 4));
+}
+
+hipError_t launch_ffn_bwd_dgrad_bf16(const moe_cfg& c, const FfnBwdArgs& a, void* tile_ws,
+                                     void* ab_r, void* ab_s, void* h_r, void* h_s, void* dab_r,
+                                     void* dab_s, hipStream_t st) {
+    const int64_t T = c.tokens, d = c.hidden, I = c.inter, Is = c.inter_shared;
+    const bool has_shared = Is > 0 && T > 0;
+    char* q = (char*)tile_ws;
+    int2* tiles = (int2*)q;
+    q += align256((ffn_max_routed_tiles(c) + ffn_max_shared_tiles(c)) * 8);
+    int32_t* counts = (int32_t*)q;
+    q += 256;
+    int32_t* order = (int32_t*)q;
+    q += align256(ffn_max_routed_tiles(c) * 4);
+    int32_t* keys = (int32_t*)q;
+    const int64_t max_r = ffn_max_routed_tiles(c);
+    const int64_t max_s = has_shared ? ffn_max_shared_tiles(c) : 0;
+    launch_tile_map(a.offsets, (int)c.n_experts, T, has_shared, BF_BM, tiles, counts, order, keys,
+                    st);
+    GemmParamsV2 p{};
+    p.tiles = tiles;
+    p.counts = counts;
+    p.order = order;
+    p.offsets = a.offsets;
+    p.N = (int)c.n_experts;
+    p.T = has_shared ? T : 0;
+    // recompute: a, b (E) and h (C) from x and the forward-packed W13
+    p.K_r = p.K_s = d;
+    p.Nout_r = I;
+    p.Nout_s = Is;
+    p.A_r = a.x_perm;
+    p.A_s = a.x_sh;
+    p.B_r = a.w13;
+    p.B_s = a.ws13;
+    p.C_r = h_r;
+    p.C_s = h_s;
+    p.E_r = ab_r;
+    p.E_s = ab_s;
+    p.ntn_r = (int)cdiv(I, 128);
+    p.ntn_s = has_shared ? (int)cdiv(Is, 128) : 0;
+    unsigned grid = (unsigned)ffn_grid_blocks(max_r, p.ntn_r, max_s, p.ntn_s);
+    ffn_gemm_bf16_kernel<2, MOE_GEMM_BK, MOE_GEMM_NS><<<grid, G_THREADS, 0, st>>>(p);
+    // down dgrad: dh = dY W2 (W2 transposed and packed), epilogue -> da, db
+    p.A_r = a.dy_perm;
+    p.A_s = a.dy_sh;
+    p.B_r = a.w2t;
+    p.B_s = a.ws2t;
+    p.C_r = dab_r;
+    p.C_s = dab_s;
+    p.c_stride2 = 1;
+    p.ntn_r = (int)cdiv(I, 256);
+    p.ntn_s = has_shared ? (int)cdiv(Is, 256) : 0;
+    grid = (unsigned)ffn_grid_blocks(max_r, p.ntn_r, max_s, p.ntn_s);
+    ffn_gemm_bf16_kernel<3, MOE_GEMM_BK, MOE_GEMM_NS><<<grid, G_THREADS, 0, st>>>(p);
+    // up dgrad: dX = [da db] W13 (W13 transposed and packed), K = 2I
+    p.K_r = 2 * I;
+    p.K_s = 2 * Is;
+    p.Nout_r = p.Nout_s = d;
+    p.A_r = dab_r;
+    p.A_s = dab_s;
+    p.B_r = a.w13t;
+    p.B_s = a.ws13t;
+    p.C_r = a.dx_perm;
+    p.C_s = a.dx_sh;
+    p.E_r = p.E_s = nullptr;
+    p.c_stride2 = 0;
+    p.ntn_r = (int)cdiv(d, 256);
+    p.ntn_s = has_shared ? (int)cdiv(d, 256) : 0;
+    grid = (unsigned)ffn_grid_blocks(max_r, p.ntn_r, max_s, p.ntn_s);
+    ffn_gemm_bf16_kernel<1, MOE_GEMM_BK, MOE_GEMM_NS><<<grid, G_THREADS, 0, st>>>(p);
     return hipGetLastError();
 }
 

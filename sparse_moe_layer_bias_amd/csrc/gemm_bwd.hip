@@ -13,17 +13,17 @@
 //   wgrad up   dW13 = [da db]^T X              contraction over the M rows
 // silu'(a) = sig(a) (1 + a (1 - sig(a))).
 //
-// Every GEMM here computes C[m][n] = sum_k A(m,k) B(n,k) for one 128 x 128 tile
-// of C with 4 wavefronts of 64 x 64 each, on v_mfma_f32_16x16x32_bf16.  An
-// operand is either stored K-contiguous ("direct": rows of A or B are rows in
-// memory) or K-strided ("transposed": the weight matrices read against their
-// storage order, and the token rows of the weight gradients, whose contraction
-// runs over tokens).  Both land in LDS in one layout -- [row][64 contraction
-// elements], 16-byte chunks swizzled as in the forward kernels -- so the MFMA
-// loop is the same for every GEMM: transposed operands are loaded as 4 x 16
-// bytes (4 consecutive k of 8 consecutive rows) per thread and transposed in
-// registers before the LDS store.  Two LDS stages; global loads for stage k+1
-// are in flight while stage k is multiplied.
+// bf16: the first three run on the forward's streaming kernel (gemm.hip, modes
+// 2, 3 and 1) with the weights packed for it -- W13 as in the forward, W13 and
+// W2 transposed for the dgrads.  The weight gradients contract over token rows,
+// so both operands are read against their storage order; they run here: one
+// 128 x 128 tile of dW per workgroup, 4 wavefronts of 64 x 64 on
+// v_mfma_f32_16x16x32_bf16.  Each thread loads 4 consecutive rows x 8
+// consecutive columns (4 x 16 bytes) and transposes them in registers, so LDS
+// holds [output row][64 contraction elements] with the forward's 16-byte chunk
+// swizzle and the MFMA loop reads whole chunks.  Two LDS stages; the global
+// loads of stage k+1 are in flight while stage k is multiplied.
+// fp32: plain VALU kernels for all five (small layers).
 #include "gemm_common.h"
 
 namespace moe {
@@ -31,12 +31,10 @@ namespace moe {
 enum BwdOp { OP_RECOMP = 0, OP_DGRAD_DOWN = 1, OP_DGRAD_UP = 2, OP_WGRAD_DOWN = 3, OP_WGRAD_UP = 4 };
 
 struct BwdParams {
-    const int2* tiles;      // row tiles (group, first row): routed, then shared
-    const int32_t* counts;  // [0] routed row tiles, [1] shared row tiles
     const int32_t* offsets;
     int N;
     int has_shared;
-    int64_t ntn;  // units per row tile (row-tiled GEMMs) or per group (weight gradients)
+    int64_t ntn;  // weight gradients: tiles per group
     int64_t ntc;  // weight gradients: column tiles per row of tiles
     int64_t T, TK, d, I_r, I_s;
     const void* x_perm;
@@ -123,50 +121,34 @@ __device__ __forceinline__ void op_extents(int64_t M, int64_t I, int64_t d, int6
     else { R = 2 * I; C = d; K = M; }
 }
 
-// Unit of a launch -> (group, first C row, first C column); false = no work.
-// Row-tiled GEMMs walk the tile list (ntn column tiles per row tile); weight
-// gradients walk groups x (row tile, column tile), shared expert first: its
-// contraction runs over all T tokens, the longest units of the launch.
-template <int OP>
-__device__ __forceinline__ bool bwd_unit(const BwdParams& p, int64_t u, int& g, int64_t& r0,
-                                         int64_t& c0, int CT) {
-    if (OP <= OP_DGRAD_UP) {
-        const int64_t ti = u / p.ntn, nt = u % p.ntn;
-        if (ti >= (int64_t)p.counts[0] + p.counts[1]) return false;
-        const int2 t = p.tiles[ti];
-        g = t.x;
-        r0 = t.y;
-        c0 = nt * CT;
-    } else {
-        const int64_t gi = u / p.ntn, rem = u % p.ntn;
-        if (p.has_shared)
-            g = gi == 0 ? p.N : (int)gi - 1;
-        else
-            g = (int)gi;
-        if (g > p.N || (g == p.N && !p.has_shared)) return false;
-        r0 = (rem / p.ntc) * CT;
-        c0 = (rem % p.ntc) * CT;
-    }
+// Weight-gradient unit -> (group, first dW row, first dW column); false = no
+// work.  Units walk groups x (row tile, column tile), the shared expert first:
+// its contraction runs over all T tokens, the longest units of the launch.
+__device__ __forceinline__ bool wgrad_unit(const BwdParams& p, int64_t u, int& g, int64_t& r0,
+                                           int64_t& c0, int CT) {
+    const int64_t gi = u / p.ntn, rem = u % p.ntn;
+    if (p.has_shared)
+        g = gi == 0 ? p.N : (int)gi - 1;
+    else
+        g = (int)gi;
+    if (g > p.N || (g == p.N && !p.has_shared)) return false;
+    r0 = (rem / p.ntc) * CT;
+    c0 = (rem % p.ntc) * CT;
     return true;
 }
 
 // ---------------------------------------------------------------- bf16 MFMA
 
-constexpr int BT = 128;   // C tile rows and columns (recompute: 64 h columns)
-constexpr int BBK = 64;   // contraction elements per LDS stage
+constexpr int BT = 128;   // dW tile rows and columns
+constexpr int BBK = 64;   // contraction elements (token rows) per LDS stage
 constexpr int BW_THREADS = 256;
 
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
 template <int OP>
-__global__ void __launch_bounds__(BW_THREADS) bwd_gemm_bf16_kernel(BwdParams p) {
-    constexpr bool A_T = OP >= OP_WGRAD_DOWN;  // A stored [K][rows]
-    constexpr bool B_T = OP != OP_RECOMP;      // B stored [K][rows]
-    constexpr int CT = OP == OP_RECOMP ? 64 : BT;
+__global__ void __launch_bounds__(BW_THREADS) wgrad_bf16_kernel(BwdParams p) {
+    static_assert(OP == OP_WGRAD_DOWN || OP == OP_WGRAD_UP, "weight gradients only");
     int g;
     int64_t r0, c0;
-    if (!bwd_unit<OP>(p, blockIdx.x, g, r0, c0, CT)) return;
+    if (!wgrad_unit(p, blockIdx.x, g, r0, c0, BT)) return;
     Grp<uint16_t> v;
     group_view(p, g, v);
     const int64_t d = p.d, I = v.I;
@@ -174,26 +156,23 @@ __global__ void __launch_bounds__(BW_THREADS) bwd_gemm_bf16_kernel(BwdParams p) 
     op_extents<OP>(v.M, I, d, R, C, K);
     if (r0 >= R || c0 >= C) return;
 
-    // operands: base of the tile, row stride, rows present from the tile start
+    // C[r][c] = sum_m A[m][r0 + r] B[m][c0 + c]: base of the tile's columns,
+    // row stride, columns present from the tile start
     const uint16_t* a_base;
     const uint16_t* b_base;
-    int64_t a_ld, b_ld, a_rows, b_rows;
-    if (OP == OP_RECOMP) {
-        a_base = v.X + r0 * d; a_ld = d; a_rows = R - r0;
-        b_base = v.W13; b_ld = d; b_rows = 0;  // row map below
-    } else if (OP == OP_DGRAD_DOWN) {
-        a_base = v.dY + r0 * d; a_ld = d; a_rows = R - r0;
-        b_base = v.W2 + c0; b_ld = I; b_rows = I - c0;
-    } else if (OP == OP_DGRAD_UP) {
-        a_base = v.dab + r0 * 2 * I; a_ld = 2 * I; a_rows = R - r0;
-        b_base = v.W13 + c0; b_ld = d; b_rows = d - c0;
-    } else if (OP == OP_WGRAD_DOWN) {
-        a_base = v.dY + r0; a_ld = d; a_rows = d - r0;
-        b_base = v.h + c0; b_ld = I; b_rows = I - c0;
-    } else {
-        a_base = v.dab + r0; a_ld = 2 * I; a_rows = 2 * I - r0;
-        b_base = v.X + c0; b_ld = d; b_rows = d - c0;
+    int64_t a_ld, b_ld;
+    uint16_t* Cp;
+    int64_t ldc;
+    if (OP == OP_WGRAD_DOWN) {  // dW2 [d][I] = dY^T h
+        a_base = v.dY + r0; a_ld = d;
+        b_base = v.h + c0; b_ld = I;
+        Cp = v.dW2; ldc = I;
+    } else {                    // dW13 [2I][d] = [da db]^T X
+        a_base = v.dab + r0; a_ld = 2 * I;
+        b_base = v.X + c0; b_ld = d;
+        Cp = v.dW13; ldc = d;
     }
+    const int64_t a_rows = R - r0, b_rows = C - c0;
 
     __shared__ __attribute__((aligned(1024))) uint16_t smem[2][2][BT * BBK];
     const int tid = threadIdx.x;
@@ -203,43 +182,12 @@ __global__ void __launch_bounds__(BW_THREADS) bwd_gemm_bf16_kernel(BwdParams p) 
     const int l16 = lane & 15, gq = lane >> 4;
     const int nk = (int)((K + BBK - 1) / BBK);
 
-    // ---- loaders (registers), then LDS stores
+    // thread (rq = tid%16, kq = tid/16): contraction rows 4kq..4kq+3 of tile
+    // rows (= columns in memory) 8rq..8rq+7, 16 bytes per contraction row
     uint4 ra[4], rb[4];
     const uint4 zero = make_uint4(0, 0, 0, 0);
-    // direct: 128 rows x 8 chunks; thread q = tid + 256 i -> row q/8, chunk q%8
-    auto load_direct = [&](uint4* r, const uint16_t* base, int64_t ld, int64_t rows, int64_t kb,
-                           bool recomp_map) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = tid + BW_THREADS * i;
-            const int row = q >> 3, ch = q & 7;
-            const int64_t kk = kb + ch * 8;
-            int64_t src;
-            bool ok;
-            if (recomp_map) {
-                // rows 0..63: W1 rows c0.., rows 64..127: the matching W3 rows
-                const int64_t hc = c0 + (row & 63);
-                src = (row < 64 ? 0 : I) + hc;
-                ok = hc < I;
-            } else {
-                src = row;
-                ok = row < rows;
-            }
-            r[i] = (ok && kk < K) ? *(const uint4*)(base + src * ld + kk) : zero;
-        }
-    };
-    auto store_direct = [&](uint16_t* s, const uint4* r) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = tid + BW_THREADS * i;
-            const int row = q >> 3, ch = q & 7;
-            *(uint4*)(s + row * BBK + sub_chunk8(row, ch) * 8) = r[i];
-        }
-    };
-    // transposed: thread (rq = tid%16, kq = tid/16) loads k = 4kq..4kq+3 of
-    // rows 8rq..8rq+7 (16 bytes each)
     const int rq = tid & 15, kq = tid >> 4;
-    auto load_trans = [&](uint4* r, const uint16_t* base, int64_t ld, int64_t rows, int64_t kb) {
+    auto load_t = [&](uint4* r, const uint16_t* base, int64_t ld, int64_t rows, int64_t kb) {
         const bool rok = 8 * rq < rows;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -247,7 +195,9 @@ __global__ void __launch_bounds__(BW_THREADS) bwd_gemm_bf16_kernel(BwdParams p) 
             r[j] = (rok && kr < K) ? *(const uint4*)(base + kr * ld + 8 * rq) : zero;
         }
     };
-    auto store_trans = [&](uint16_t* s, const uint4* r) {
+    // transpose: tile row 8rq+i gets the 4 contraction values (8 bytes) at
+    // chunk kq/2, half kq%2
+    auto store_t = [&](uint16_t* s, const uint4* r) {
         const uint32_t w0[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
         const uint32_t w1[4] = {r[1].x, r[1].y, r[1].z, r[1].w};
         const uint32_t w2[4] = {r[2].x, r[2].y, r[2].z, r[2].w};
@@ -269,31 +219,21 @@ __global__ void __launch_bounds__(BW_THREADS) bwd_gemm_bf16_kernel(BwdParams p) 
     };
     auto load = [&](int kt) {
         const int64_t kb = (int64_t)kt * BBK;
-        if (A_T)
-            load_trans(ra, a_base, a_ld, a_rows, kb);
-        else
-            load_direct(ra, a_base, a_ld, a_rows, kb, false);
-        if (B_T)
-            load_trans(rb, b_base, b_ld, b_rows, kb);
-        else
-            load_direct(rb, b_base, b_ld, b_rows, kb, OP == OP_RECOMP);
+        load_t(ra, a_base, a_ld, a_rows, kb);
+        load_t(rb, b_base, b_ld, b_rows, kb);
     };
     auto store = [&](int s) {
-        if (A_T) store_trans(smem[s][0], ra); else store_direct(smem[s][0], ra);
-        if (B_T) store_trans(smem[s][1], rb); else store_direct(smem[s][1], rb);
+        store_t(smem[s][0], ra);
+        store_t(smem[s][1], rb);
     };
 
-    // ---- MFMA: D rows = B rows (n), D columns = A rows (m); lane holds
-    // C[m = 16-row block + l16][n = 16-column block + 4 gq + 0..3]
+    // MFMA: D rows = B tile rows (output columns), D columns = A tile rows
+    // (output rows); lane holds C[16-row block + l16][16-column block + 4 gq + 0..3]
     f32x4_t acc[4][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[j][i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    auto brow = [&](int j) {
-        if (OP == OP_RECOMP) return j < 2 ? wn * 32 + j * 16 : 64 + wn * 32 + (j - 2) * 16;
-        return wn * 64 + j * 16;
-    };
     uint32_t coff[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) coff[s] = sub_chunk8(l16, 4 * s + gq) * 8;
@@ -310,7 +250,7 @@ __global__ void __launch_bounds__(BW_THREADS) bwd_gemm_bf16_kernel(BwdParams p) 
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 bfr[j] = __builtin_bit_cast(bf16x8_t,
-                                            *(const uint4*)(Bs + (brow(j) + l16) * BBK + coff[s]));
+                                            *(const uint4*)(Bs + (wn * 64 + j * 16 + l16) * BBK + coff[s]));
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -331,62 +271,18 @@ __global__ void __launch_bounds__(BW_THREADS) bwd_gemm_bf16_kernel(BwdParams p) 
         __syncthreads();
     }
 
-    // ---- epilogue: direct 8-byte stores (4 consecutive columns per lane)
+    // epilogue: 8-byte stores of 4 consecutive columns; a group without rows
+    // (K = 0) writes zeros
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int64_t m = r0 + wm * 64 + i * 16 + l16;  // C row (group-relative)
+        const int64_t m = r0 + wm * 64 + i * 16 + l16;
         if (m >= R) continue;
-        if (OP == OP_RECOMP) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int64_t hc = c0 + wn * 32 + j * 16 + 4 * gq;
-                if (hc >= I) continue;
-                float hv[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) hv[e] = silu_f(acc[j][i][e]) * acc[j + 2][i][e];
-                uint16_t* abr = v.ab + m * 2 * I;
-                *(uint2*)(abr + hc) = make_uint2(pack_bf16x2(acc[j][i][0], acc[j][i][1]),
-                                                 pack_bf16x2(acc[j][i][2], acc[j][i][3]));
-                *(uint2*)(abr + I + hc) = make_uint2(pack_bf16x2(acc[j + 2][i][0], acc[j + 2][i][1]),
-                                                     pack_bf16x2(acc[j + 2][i][2], acc[j + 2][i][3]));
-                *(uint2*)(v.h + m * I + hc) = make_uint2(pack_bf16x2(hv[0], hv[1]),
-                                                         pack_bf16x2(hv[2], hv[3]));
-            }
-        } else if (OP == OP_DGRAD_DOWN) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t n = c0 + wn * 64 + j * 16 + 4 * gq;
-                if (n >= I) continue;
-                const uint16_t* abr = v.ab + m * 2 * I;
-                const uint2 qa = *(const uint2*)(abr + n);
-                const uint2 qb = *(const uint2*)(abr + I + n);
-                const float a[4] = {bf_lo(qa.x), bf_hi(qa.x), bf_lo(qa.y), bf_hi(qa.y)};
-                const float b[4] = {bf_lo(qb.x), bf_hi(qb.x), bf_lo(qb.y), bf_hi(qb.y)};
-                float da[4], db[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-a[e]));
-                    const float dh = acc[j][i][e];
-                    da[e] = dh * b[e] * sg * (1.0f + a[e] * (1.0f - sg));
-                    db[e] = dh * a[e] * sg;
-                }
-                uint16_t* dr = v.dab + m * 2 * I;
-                *(uint2*)(dr + n) = make_uint2(pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3]));
-                *(uint2*)(dr + I + n) = make_uint2(pack_bf16x2(db[0], db[1]), pack_bf16x2(db[2], db[3]));
-            }
-        } else {
-            uint16_t* Cp;
-            int64_t ldc;
-            if (OP == OP_DGRAD_UP) { Cp = v.dX; ldc = d; }
-            else if (OP == OP_WGRAD_DOWN) { Cp = v.dW2; ldc = I; }
-            else { Cp = v.dW13; ldc = d; }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t n = c0 + wn * 64 + j * 16 + 4 * gq;
-                if (n >= C) continue;
-                *(uint2*)(Cp + m * ldc + n) = make_uint2(pack_bf16x2(acc[j][i][0], acc[j][i][1]),
-                                                         pack_bf16x2(acc[j][i][2], acc[j][i][3]));
-            }
+        for (int j = 0; j < 4; ++j) {
+            const int64_t n = c0 + wn * 64 + j * 16 + 4 * gq;
+            if (n >= C) continue;
+            *(uint2*)(Cp + m * ldc + n) = make_uint2(pack_bf16x2(acc[j][i][0], acc[j][i][1]),
+                                                     pack_bf16x2(acc[j][i][2], acc[j][i][3]));
         }
     }
 }
@@ -472,25 +368,20 @@ __global__ void __launch_bounds__(256) bwd_f32_kernel(BwdParams p, int64_t cols,
 // ---------------------------------------------------------------- launch
 
 struct BwdWs {
-    int2* tiles;
-    int32_t* counts;
-    int32_t* order;
-    int32_t* keys;
+    void* tile_ws;
     void *ab_r, *ab_s, *h_r, *h_s, *dab_r, *dab_s;
 };
 
 static int64_t align256(int64_t b) { return (b + 255) & ~int64_t(255); }
-static int64_t bwd_max_routed_tiles(const moe_cfg& c) { return c.tokens * c.top_k / BT + c.n_experts; }
-static int64_t bwd_max_shared_tiles(const moe_cfg& c) { return cdiv(c.tokens, BT); }
 static int64_t bwd_esz(const moe_cfg& c) { return c.act_dtype == MOE_BF16 ? 2 : 4; }
+static int64_t imax(int64_t a, int64_t b) { return a > b ? a : b; }
 
 size_t ffn_backward_workspace_bytes(const moe_cfg& c) {
     const int64_t TK = c.tokens * c.top_k, T = c.tokens, eb = bwd_esz(c);
     const int64_t I = c.inter, Is = c.inter_shared;
-    int64_t b = align256((bwd_max_routed_tiles(c) + bwd_max_shared_tiles(c)) * 8) + 256;
-    b += 2 * align256(bwd_max_routed_tiles(c) * 4);
-    b += 2 * align256(TK * 2 * I * eb) + align256(TK * I * eb);       // ab, dab, h routed
-    b += 2 * align256(T * 2 * Is * eb) + align256(T * Is * eb);       // shared
+    int64_t b = align256((int64_t)ffn_bwd_tile_ws_bytes(c));
+    b += 2 * align256(TK * 2 * I * eb) + align256(TK * I * eb);  // ab, dab, h routed
+    b += 2 * align256(T * 2 * Is * eb) + align256(T * Is * eb);  // shared
     return (size_t)b;
 }
 
@@ -499,14 +390,8 @@ static BwdWs carve_bwd(const moe_cfg& c, void* ws) {
     const int64_t I = c.inter, Is = c.inter_shared;
     char* q = (char*)ws;
     BwdWs w{};
-    w.tiles = (int2*)q;
-    q += align256((bwd_max_routed_tiles(c) + bwd_max_shared_tiles(c)) * 8);
-    w.counts = (int32_t*)q;
-    q += 256;
-    w.order = (int32_t*)q;
-    q += align256(bwd_max_routed_tiles(c) * 4);
-    w.keys = (int32_t*)q;
-    q += align256(bwd_max_routed_tiles(c) * 4);
+    w.tile_ws = q;
+    q += align256((int64_t)ffn_bwd_tile_ws_bytes(c));
     w.ab_r = q; q += align256(TK * 2 * I * eb);
     w.dab_r = q; q += align256(TK * 2 * I * eb);
     w.h_r = q; q += align256(TK * I * eb);
@@ -517,8 +402,8 @@ static BwdWs carve_bwd(const moe_cfg& c, void* ws) {
 }
 
 template <int OP>
-static void launch_bwd_bf16(const BwdParams& p, int64_t units, hipStream_t st) {
-    if (units > 0) bwd_gemm_bf16_kernel<OP><<<dim3((unsigned)units), BW_THREADS, 0, st>>>(p);
+static void launch_wgrad_bf16(const BwdParams& p, int64_t units, hipStream_t st) {
+    if (units > 0) wgrad_bf16_kernel<OP><<<dim3((unsigned)units), BW_THREADS, 0, st>>>(p);
 }
 
 template <int OP>
@@ -527,8 +412,6 @@ static void launch_bwd_f32(const BwdParams& p, int64_t cols, int64_t per_r, int6
     if (total > 0)
         bwd_f32_kernel<OP><<<dim3((unsigned)cdiv(total, 256)), 256, 0, st>>>(p, cols, per_r, total);
 }
-
-static int64_t imax(int64_t a, int64_t b) { return a > b ? a : b; }
 
 hipError_t launch_expert_ffn_backward(const moe_cfg& c, const FfnBwdArgs& a, void* ws,
                                       hipStream_t st) {
@@ -549,10 +432,11 @@ hipError_t launch_expert_ffn_backward(const moe_cfg& c, const FfnBwdArgs& a, voi
     p.x = a.x_sh;
     p.dy_perm = a.dy_perm;
     p.dy_s = a.dy_sh;
+    // fp32 layers: the "packed" weights are plain copies (W13 [2I][d], W2 [d][I])
     p.w13 = a.w13;
-    p.w2 = a.w2;
+    p.w2 = a.w2t;
     p.ws13 = a.ws13;
-    p.ws2 = a.ws2;
+    p.ws2 = a.ws2t;
     p.ab_r = w.ab_r;
     p.ab_s = w.ab_s;
     p.h_r = w.h_r;
@@ -570,27 +454,17 @@ hipError_t launch_expert_ffn_backward(const moe_cfg& c, const FfnBwdArgs& a, voi
 
     if (c.act_dtype == MOE_BF16) {
         if (TK > 0) {
-            const int64_t max_r = bwd_max_routed_tiles(c);
-            const int64_t max_s = has_shared ? bwd_max_shared_tiles(c) : 0;
-            launch_tile_map(a.offsets, (int)N, T, has_shared, BT, w.tiles, w.counts, w.order,
-                            w.keys, st);
-            p.tiles = w.tiles;
-            p.counts = w.counts;
-            // recompute a, b, h (64 h columns per tile)
-            p.ntn = imax(cdiv(I, 64), cdiv(Ish, 64));
-            launch_bwd_bf16<OP_RECOMP>(p, (max_r + max_s) * p.ntn, st);
-            p.ntn = imax(cdiv(I, BT), cdiv(Ish, BT));
-            launch_bwd_bf16<OP_DGRAD_DOWN>(p, (max_r + max_s) * p.ntn, st);
-            p.ntn = cdiv(d, BT);
-            launch_bwd_bf16<OP_DGRAD_UP>(p, (max_r + max_s) * p.ntn, st);
+            const hipError_t e = launch_ffn_bwd_dgrad_bf16(c, a, w.tile_ws, w.ab_r, w.ab_s, w.h_r,
+                                                           w.h_s, w.dab_r, w.dab_s, st);
+            if (e != hipSuccess) return e;
         }
         // weight gradients: every group, including experts without rows (zeros)
         p.ntc = imax(cdiv(I, BT), cdiv(Ish, BT));
         p.ntn = cdiv(d, BT) * p.ntc;
-        launch_bwd_bf16<OP_WGRAD_DOWN>(p, ng * p.ntn, st);
+        launch_wgrad_bf16<OP_WGRAD_DOWN>(p, ng * p.ntn, st);
         p.ntc = cdiv(d, BT);
         p.ntn = imax(cdiv(2 * I, BT), cdiv(2 * Ish, BT)) * p.ntc;
-        launch_bwd_bf16<OP_WGRAD_UP>(p, ng * p.ntn, st);
+        launch_wgrad_bf16<OP_WGRAD_UP>(p, ng * p.ntn, st);
     } else {
         const int64_t rows = TK + p.T;
         const int64_t hcols = imax(I, Ish);

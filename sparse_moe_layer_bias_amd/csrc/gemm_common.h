@@ -27,6 +27,11 @@ struct GemmParamsV2 {
     const void* B_s;
     void* C_r;
     void* C_s;
+    // backward launches only: [rows][2 Nout] side array of the epilogue -- the
+    // stored a, b (written by the recompute, read by the down-projection dgrad)
+    void* E_r;
+    void* E_s;
+    int c_stride2;         // output rows are 2 Nout wide (down-projection dgrad: da, db)
 };
 
 struct WorkV2 {
@@ -36,6 +41,7 @@ struct WorkV2 {
     const char* X;   // token rows of the group
     const char* W;   // weights of the group
     char* C;         // output rows of the group
+    char* E;         // side array rows of the group (backward launches)
 };
 
 // Units: routed (tile, wt) tile-major -- the weight tiles of one expert run
@@ -91,7 +97,8 @@ __device__ __forceinline__ bool decode_v2(const GemmParamsV2& p, int mode, WorkV
         const int64_t wrows = ESZ != 4 ? (int64_t)p.ntn_r * G_WR_PACK
                                        : (mode == 0 ? 2 * w.Nout : w.Nout);
         w.W = (const char*)p.B_r + (int64_t)g * wrows * w.K * ESZ;
-        w.C = (char*)p.C_r + rowbase * w.Nout * ESZ;
+        w.C = (char*)p.C_r + rowbase * w.Nout * (p.c_stride2 ? 2 : 1) * ESZ;
+        w.E = p.E_r ? (char*)p.E_r + rowbase * 2 * w.Nout * ESZ : nullptr;
     } else {
         w.M = p.T;
         w.K = p.K_s;
@@ -99,6 +106,7 @@ __device__ __forceinline__ bool decode_v2(const GemmParamsV2& p, int mode, WorkV
         w.X = (const char*)p.A_s;
         w.W = (const char*)p.B_s;
         w.C = (char*)p.C_s;
+        w.E = (char*)p.E_s;
     }
     return true;
 }

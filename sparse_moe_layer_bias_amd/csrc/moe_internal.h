@@ -59,15 +59,19 @@ void launch_tile_map(const int32_t* offsets, int N, int64_t T, bool has_shared, 
                      int2* tiles, int32_t* counts, int32_t* order, int32_t* keys, hipStream_t st);
 
 // ---------------------------------------------------------------- backward
+// weights as moe_pack_weights lays them out: w13 / ws13 forward-packed
+// (which 0 / 2), w13t / ws13t and w2t / ws2t transposed (which 4 / 6, 5 / 7)
 struct FfnBwdArgs {
     const void* x_perm;
     const int32_t* offsets;
     const void* w13;
-    const void* w2;
+    const void* w13t;
+    const void* w2t;
     const void* dy_perm;
     const void* x_sh;
     const void* ws13;
-    const void* ws2;
+    const void* ws13t;
+    const void* ws2t;
     const void* dy_sh;
     void* dx_perm;
     void* dx_sh;
@@ -77,6 +81,11 @@ struct FfnBwdArgs {
     void* dws2;
 };
 size_t ffn_backward_workspace_bytes(const moe_cfg& c);
+// recompute and both dgrad GEMMs on the forward's bf16 kernel (gemm.hip)
+size_t ffn_bwd_tile_ws_bytes(const moe_cfg& c);
+hipError_t launch_ffn_bwd_dgrad_bf16(const moe_cfg& c, const FfnBwdArgs& a, void* tile_ws,
+                                     void* ab_r, void* ab_s, void* h_r, void* h_s, void* dab_r,
+                                     void* dab_s, hipStream_t st);
 hipError_t launch_expert_ffn_backward(const moe_cfg& c, const FfnBwdArgs& a, void* ws,
                                       hipStream_t st);
 hipError_t launch_combine_backward(const moe_cfg& c, const void* dout, const void* y_perm,

@@ -3,8 +3,8 @@ the five calls in order on one stream.
 
     route -> permute -> expert_ffn (routed + shared) -> combine -> bias_update
 
-and, for bf16 / fp32 layers built with ``keep_plain=True``, the backward calls
-of include/moe_backward.h:
+and, for bf16 / fp32 layers built with ``train=True``, the backward calls of
+include/moe_backward.h:
 
     combine_backward -> expert_ffn_backward -> route_backward -> input_grad
 
@@ -47,7 +47,7 @@ class MoeLayer:
     and every per-step buffer for a batch of T tokens."""
 
     def __init__(self, cfg, w13, w2, ws13=None, ws2=None, T=None, device="cuda",
-                 keep_plain=False):
+                 train=False):
         self.c = dict(cfg)
         if T is not None:
             self.c["T"] = T
@@ -103,9 +103,20 @@ class MoeLayer:
         ws = max(moe_route_workspace_size(self.cfg), moe_permute_workspace_size(self.cfg),
                  moe_expert_ffn_workspace_size(self.cfg), 256)
         self.workspace = torch.empty((ws,), dtype=torch.uint8, device=dev)
-        # the backward reads the plain (unpacked) weights
-        self.plain = (w13, w2, ws13 if has_shared else None, ws2 if has_shared else None) \
-            if keep_plain else None
+        # the backward's dgrad GEMMs stream the weights transposed
+        self.train = bool(train)
+        self.w_shapes = (tuple(w13.shape), tuple(w2.shape),
+                         tuple(ws13.shape) if has_shared else None,
+                         tuple(ws2.shape) if has_shared else None)
+        self.w13t = self.w2t = self.ws13t = self.ws2t = None
+        if self.train:
+            if self.fp8:
+                raise ValueError("the backward covers bf16 and fp32 layers")
+            self.w13t = pack_weights(self.cfg, 4, w13)
+            self.w2t = pack_weights(self.cfg, 5, w2)
+            if has_shared:
+                self.ws13t = pack_weights(self.cfg, 6, ws13)
+                self.ws2t = pack_weights(self.cfg, 7, ws2)
         self.grads = None
 
     # the five calls -------------------------------------------------------
@@ -145,22 +156,22 @@ class MoeLayer:
     # the backward ------------------------------------------------------------
     def _grad_buffers(self, centroids):
         c = self.c
-        T, d, N, k = c["T"], c["d"], c["N"], c["k"]
+        T, d, k = c["T"], c["d"], c["k"]
         dev = self.out.device
         act = self.out.dtype
-        w13, w2, ws13, ws2 = self.plain
+        s13, s2, ss13, ss2 = self.w_shapes
         f32 = dict(dtype=torch.float32, device=dev)
-        g = dict(dy_perm=torch.empty((T * k, d), dtype=act, device=dev),
+        a = dict(dtype=act, device=dev)
+        g = dict(dy_perm=torch.empty((T * k, d), **a),
                  dgate=torch.empty((T, k), **f32),
-                 dx_perm=torch.empty((T * k, d), dtype=act, device=dev),
-                 dx_shared=torch.empty((T, d), dtype=act, device=dev) if ws13 is not None
-                 else None,
-                 dw13=torch.empty_like(w13), dw2=torch.empty_like(w2),
-                 dws13=torch.empty_like(ws13) if ws13 is not None else None,
-                 dws2=torch.empty_like(ws2) if ws2 is not None else None,
+                 dx_perm=torch.empty((T * k, d), **a),
+                 dx_shared=torch.empty((T, d), **a) if ss13 is not None else None,
+                 dw13=torch.empty(s13, **a), dw2=torch.empty(s2, **a),
+                 dws13=torch.empty(ss13, **a) if ss13 is not None else None,
+                 dws2=torch.empty(ss2, **a) if ss2 is not None else None,
                  dz=torch.empty((T, k), **f32),
                  dcentroids=torch.empty_like(centroids),
-                 dx=torch.empty((T, d), dtype=act, device=dev))
+                 dx=torch.empty((T, d), **a))
         wsb = max(moe_expert_ffn_backward_workspace_size(self.cfg),
                   moe_route_backward_workspace_size(self.cfg), 256)
         g["workspace"] = torch.empty((wsb,), dtype=torch.uint8, device=dev)
@@ -171,18 +182,18 @@ class MoeLayer:
         [T, d]: returns a dict with dx, dcentroids, dw13, dw2, dws13, dws2 (plus
         the intermediates dy_perm, dgate, dx_perm, dx_shared, dz).  The buffers
         are reused across calls."""
-        if self.plain is None:
-            raise RuntimeError("the backward needs the plain weights: build the layer with "
-                               "keep_plain=True")
+        if not self.train:
+            raise RuntimeError("the backward needs the transposed weight packs: build the "
+                               "layer with train=True")
         if self.grads is None:
             self.grads = self._grad_buffers(centroids)
         g = self.grads
-        w13, w2, ws13, ws2 = self.plain
+        shared = self.ws13t is not None
         moe_combine_backward(self.cfg, dout, self.y_perm, self.gate, self.dst_row, g["dy_perm"],
                              g["dgate"], stream)
-        moe_expert_ffn_backward(self.cfg, self.x_perm, self.offsets, w13, w2, g["dy_perm"],
-                                x if ws13 is not None else None, ws13, ws2,
-                                dout if ws13 is not None else None, g["dx_perm"],
+        moe_expert_ffn_backward(self.cfg, self.x_perm, self.offsets, self.w13, self.w13t,
+                                self.w2t, g["dy_perm"], x if shared else None, self.ws13,
+                                self.ws13t, self.ws2t, dout if shared else None, g["dx_perm"],
                                 g["dx_shared"], g["dw13"], g["dw2"], g["dws13"], g["dws2"],
                                 g["workspace"], stream)
         moe_route_backward(self.cfg, x, self.scores, self.idx, g["dgate"], self.offsets,

@@ -168,8 +168,9 @@ def test_bias_update_and_quantize_validation():
 # ------------------------------------------------------------------ backward
 
 def _ffn_bwd(cfg, ws_bytes=1 << 40, **over):
-    names = ("x_perm", "offsets", "w13", "w2", "dy_perm", "x_sh", "ws13", "ws2", "dy_shared",
-             "dx_perm", "dx_shared", "dw13", "dw2", "dws13", "dws2", "workspace")
+    names = ("x_perm", "offsets", "w13", "w13t", "w2t", "dy_perm", "x_sh", "ws13", "ws13t",
+             "ws2t", "dy_shared", "dx_perm", "dx_shared", "dw13", "dw2", "dws13", "dws2",
+             "workspace")
     args = {n: FAKE for n in names}
     args.update(over)
     P = ctypes.c_void_p
@@ -184,8 +185,8 @@ def test_expert_ffn_backward_validation():
     assert _ffn_bwd(_cfg(dtype="bf16", d=256, I=96, Is=128)) == moe.MOE_ERR_UNSUPPORTED
     assert _ffn_bwd(_cfg(), dw13=0) == moe.MOE_ERR_ARG
     assert _ffn_bwd(_cfg(), dx_shared=0) == moe.MOE_ERR_ARG    # shared expert present
-    assert _ffn_bwd(_cfg(Is=0), dx_shared=0, x_sh=0, ws13=0, ws2=0, dy_shared=0, dws13=0,
-                    dws2=0, ws_bytes=0) == moe.MOE_ERR_WORKSPACE
+    assert _ffn_bwd(_cfg(Is=0), dx_shared=0, x_sh=0, ws13=0, ws13t=0, ws2t=0, dy_shared=0,
+                    dws13=0, dws2=0, ws_bytes=0) == moe.MOE_ERR_WORKSPACE
     c = _cfg(dtype="bf16", d=256, I=128, Is=128)
     need = moe.moe_expert_ffn_backward_workspace_size(c)
     # a, b, h and da, db of T*k routed and T shared rows, bf16

@@ -37,7 +37,7 @@ def _run(name, orc, seed=0, residual=True, **over):
     c, inp, dev = small_layer_inputs(cfg, seed, T)
     log("backward case", name, "T=%d" % c["T"], over, "seed", seed, "residual", residual)
     dout = moe_inputs.make_upstream_grad(c, seed, "cpu")
-    layer = MoeLayer(c, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"], keep_plain=True)
+    layer = MoeLayer(c, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"], train=True)
     layer.forward(dev["x"], dev["centroids"], dev["bias"].clone(), residual=residual)
     g = layer.backward(dout.cuda(), dev["x"], dev["centroids"], residual=residual)
     torch.cuda.synchronize()
@@ -94,7 +94,7 @@ def test_backward_deterministic_bytes(orc):
     dout = moe_inputs.make_upstream_grad(c, 4, "cuda")
     runs = []
     for _ in range(2):
-        layer = MoeLayer(c, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"], keep_plain=True)
+        layer = MoeLayer(c, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"], train=True)
         layer.forward(dev["x"], dev["centroids"], dev["bias"].clone())
         g = layer.backward(dout, dev["x"], dev["centroids"])
         torch.cuda.synchronize()
@@ -108,7 +108,7 @@ def test_backward_zero_tokens_gives_zero_weight_gradients():
     cfg = dict(moe_inputs.CONFIGS["mid_bf16"])
     c, inp, dev = small_layer_inputs(cfg, 0, 1)
     c0 = dict(c, T=0)
-    layer = MoeLayer(c0, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"], keep_plain=True)
+    layer = MoeLayer(c0, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"], train=True)
     x = torch.empty((0, c["d"]), dtype=torch.bfloat16, device="cuda")
     layer.forward(x, dev["centroids"], dev["bias"].clone())
     g = layer.backward(torch.empty_like(x), x, dev["centroids"])
@@ -128,7 +128,7 @@ def test_v3_backward_one_expert_and_sampled_tokens(orc):
     log("generating V3-shaped inputs on the GPU")
     dev = moe_inputs.make_layer_inputs(cfg, 0, "cuda")
     dout = moe_inputs.make_upstream_grad(cfg, 0, "cuda")
-    layer = MoeLayer(cfg, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"], keep_plain=True)
+    layer = MoeLayer(cfg, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"], train=True)
     layer.forward(dev["x"], dev["centroids"], dev["bias"].clone())
     g = layer.backward(dout, dev["x"], dev["centroids"])
     torch.cuda.synchronize()
