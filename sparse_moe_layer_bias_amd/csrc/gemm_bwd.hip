@@ -17,12 +17,14 @@
 // 2, 3 and 1) with the weights packed for it -- W13 as in the forward, W13 and
 // W2 transposed for the dgrads.  The weight gradients contract over token rows,
 // so both operands are read against their storage order; they run here: one
-// 128 x 128 tile of dW per workgroup, 4 wavefronts of 64 x 64 on
-// v_mfma_f32_16x16x32_bf16.  Each thread loads 4 consecutive rows x 8
-// consecutive columns (4 x 16 bytes) and transposes them in registers, so LDS
-// holds [output row][64 contraction elements] with the forward's 16-byte chunk
-// swizzle and the MFMA loop reads whole chunks.  Two LDS stages; the global
-// loads of stage k+1 are in flight while stage k is multiplied.
+// 256 x 256 tile of dW per workgroup, 8 wavefronts of 64 x 128 on
+// v_mfma_f32_16x16x32_bf16 (a tile contracts over only ~T*k/N rows, so a big
+// tile gets the most MFMA work out of each round trip to memory).  Each thread
+// loads 4 consecutive rows x 8 consecutive columns (4 x 16 bytes) and
+// transposes them in registers, so LDS holds [output row][64 contraction
+// elements] with the forward's 16-byte chunk swizzle and the MFMA loop reads
+// whole chunks.  Two LDS stages; the global loads of stage k+1 are in flight
+// while stage k is multiplied.
 // fp32: plain VALU kernels for all five (small layers).
 #include "gemm_common.h"
 
@@ -34,8 +36,9 @@ struct BwdParams {
     const int32_t* offsets;
     int N;
     int has_shared;
-    int64_t ntn;  // weight gradients: tiles per group
-    int64_t ntc;  // weight gradients: column tiles per row of tiles
+    // weight gradients: tiles per group and column tiles per row of tiles,
+    // routed experts and the shared expert
+    int64_t ntn_r, ntc_r, ntn_s, ntc_s;
     int64_t T, TK, d, I_r, I_s;
     const void* x_perm;
     const void* x;
@@ -122,29 +125,48 @@ __device__ __forceinline__ void op_extents(int64_t M, int64_t I, int64_t d, int6
 }
 
 // Weight-gradient unit -> (group, first dW row, first dW column); false = no
-// work.  Units walk groups x (row tile, column tile), the shared expert first:
-// its contraction runs over all T tokens, the longest units of the launch.
-__device__ __forceinline__ bool wgrad_unit(const BwdParams& p, int64_t u, int& g, int64_t& r0,
+// work.  The shared expert's tiles come first, dealt round-robin over the
+// XCDs (block L runs on XCD L % 8): each contracts over all T tokens, so they
+// are the longest units and are spread evenly.  Then XCD x takes the routed
+// experts x, x+8, x+16, ... one after the other, so the ~M rows of the expert
+// its CUs are working on stay in that XCD's L2.
+__device__ __forceinline__ bool wgrad_unit(const BwdParams& p, int64_t L, int& g, int64_t& r0,
                                            int64_t& c0, int CT) {
-    const int64_t gi = u / p.ntn, rem = u % p.ntn;
-    if (p.has_shared)
-        g = gi == 0 ? p.N : (int)gi - 1;
-    else
+    const int64_t S = p.has_shared ? p.ntn_s : 0;
+    int64_t rem, ntc;
+    if (L < S) {
+        g = p.N;
+        rem = L;
+        ntc = p.ntc_s;
+    } else {
+        const int64_t Lp = L - S, x = Lp % 8, i = Lp / 8;
+        const int64_t gi = (i / p.ntn_r) * 8 + x;
+        if (gi >= p.N) return false;
         g = (int)gi;
-    if (g > p.N || (g == p.N && !p.has_shared)) return false;
-    r0 = (rem / p.ntc) * CT;
-    c0 = (rem % p.ntc) * CT;
+        rem = i % p.ntn_r;
+        ntc = p.ntc_r;
+    }
+    r0 = (rem / ntc) * CT;
+    c0 = (rem % ntc) * CT;
     return true;
 }
 
 // ---------------------------------------------------------------- bf16 MFMA
 
-constexpr int BT = 128;   // dW tile rows and columns
+constexpr int BT = 256;   // dW tile rows and columns
+
+// 16-byte chunk slot of logical chunk c in LDS row r (64 contraction elements,
+// 128 bytes): the forward's XOR with (r >> 1) & 7 keeps the 16 consecutive
+// rows an MFMA operand read touches on distinct banks; the extra (r >> 4) & 7
+// (constant over such 16 rows) also spreads the transposing stores, whose
+// lanes write rows 8 apart.
+__device__ __forceinline__ int wg_chunk(int r, int c) { return c ^ ((r >> 1) & 7) ^ ((r >> 4) & 7); }
 constexpr int BBK = 64;   // contraction elements (token rows) per LDS stage
-constexpr int BW_THREADS = 256;
+constexpr int BW_WAVES = 8;  // 4 x 2 wavefronts of 64 x 128
+constexpr int BW_THREADS = 64 * BW_WAVES;
 
 template <int OP>
-__global__ void __launch_bounds__(BW_THREADS) wgrad_bf16_kernel(BwdParams p) {
+__global__ void __launch_bounds__(BW_THREADS, 1) wgrad_bf16_kernel(BwdParams p) {
     static_assert(OP == OP_WGRAD_DOWN || OP == OP_WGRAD_UP, "weight gradients only");
     int g;
     int64_t r0, c0;
@@ -156,8 +178,7 @@ __global__ void __launch_bounds__(BW_THREADS) wgrad_bf16_kernel(BwdParams p) {
     op_extents<OP>(v.M, I, d, R, C, K);
     if (r0 >= R || c0 >= C) return;
 
-    // C[r][c] = sum_m A[m][r0 + r] B[m][c0 + c]: base of the tile's columns,
-    // row stride, columns present from the tile start
+    // C[r][c] = sum_m A[m][r0 + r] B[m][c0 + c]
     const uint16_t* a_base;
     const uint16_t* b_base;
     int64_t a_ld, b_ld;
@@ -172,36 +193,38 @@ __global__ void __launch_bounds__(BW_THREADS) wgrad_bf16_kernel(BwdParams p) {
         b_base = v.X + c0; b_ld = d;
         Cp = v.dW13; ldc = d;
     }
-    const int64_t a_rows = R - r0, b_rows = C - c0;
 
     __shared__ __attribute__((aligned(1024))) uint16_t smem[2][2][BT * BBK];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave & 3, wn = wave >> 2;
     const int l16 = lane & 15, gq = lane >> 4;
     const int nk = (int)((K + BBK - 1) / BBK);
 
-    // thread (rq = tid%16, kq = tid/16): contraction rows 4kq..4kq+3 of tile
-    // rows (= columns in memory) 8rq..8rq+7, 16 bytes per contraction row
-    uint4 ra[4], rb[4];
+    // Loads: thread (rq = t%32, kq = t/32) fetches, for A and for B,
+    // contraction rows 4kq..4kq+3 of tile rows (= columns in memory)
+    // 8rq..8rq+7, 16 bytes per contraction row: 8 loads per stage.
+    const int rq = tid & 31, kq = tid >> 5;
+    const bool aok = 8 * rq < R - r0, bok = 8 * rq < C - c0;
     const uint4 zero = make_uint4(0, 0, 0, 0);
-    const int rq = tid & 15, kq = tid >> 4;
-    auto load_t = [&](uint4* r, const uint16_t* base, int64_t ld, int64_t rows, int64_t kb) {
-        const bool rok = 8 * rq < rows;
+    uint4 r[8];
+    auto load = [&](int kt) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int64_t kr = kb + 4 * kq + j;
-            r[j] = (rok && kr < K) ? *(const uint4*)(base + kr * ld + 8 * rq) : zero;
+            const int64_t kr = (int64_t)kt * BBK + 4 * kq + j;
+            const bool kok = kr < K;
+            r[j] = (aok && kok) ? *(const uint4*)(a_base + kr * a_ld + 8 * rq) : zero;
+            r[4 + j] = (bok && kok) ? *(const uint4*)(b_base + kr * b_ld + 8 * rq) : zero;
         }
     };
-    // transpose: tile row 8rq+i gets the 4 contraction values (8 bytes) at
-    // chunk kq/2, half kq%2
-    auto store_t = [&](uint16_t* s, const uint4* r) {
-        const uint32_t w0[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
-        const uint32_t w1[4] = {r[1].x, r[1].y, r[1].z, r[1].w};
-        const uint32_t w2[4] = {r[2].x, r[2].y, r[2].z, r[2].w};
-        const uint32_t w3[4] = {r[3].x, r[3].y, r[3].z, r[3].w};
+    // transpose into LDS: tile row 8rq+i gets the 4 contraction values
+    // (8 bytes) at chunk kq/2, half kq%2
+    auto store1 = [&](uint16_t* sm, const uint4* q) {
+        const uint32_t w0[4] = {q[0].x, q[0].y, q[0].z, q[0].w};
+        const uint32_t w1[4] = {q[1].x, q[1].y, q[1].z, q[1].w};
+        const uint32_t w2[4] = {q[2].x, q[2].y, q[2].z, q[2].w};
+        const uint32_t w3[4] = {q[3].x, q[3].y, q[3].z, q[3].w};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int row = 8 * rq + i;
@@ -214,51 +237,49 @@ __global__ void __launch_bounds__(BW_THREADS) wgrad_bf16_kernel(BwdParams p) {
                 o.x = (w0[wi] >> 16) | (w1[wi] & 0xffff0000u);
                 o.y = (w2[wi] >> 16) | (w3[wi] & 0xffff0000u);
             }
-            *(uint2*)(s + row * BBK + sub_chunk8(row, kq >> 1) * 8 + (kq & 1) * 4) = o;
+            *(uint2*)(sm + row * BBK + wg_chunk(row, kq >> 1) * 8 + (kq & 1) * 4) = o;
         }
     };
-    auto load = [&](int kt) {
-        const int64_t kb = (int64_t)kt * BBK;
-        load_t(ra, a_base, a_ld, a_rows, kb);
-        load_t(rb, b_base, b_ld, b_rows, kb);
-    };
     auto store = [&](int s) {
-        store_t(smem[s][0], ra);
-        store_t(smem[s][1], rb);
+        store1(smem[s][0], r);
+        store1(smem[s][1], r + 4);
     };
 
     // MFMA: D rows = B tile rows (output columns), D columns = A tile rows
-    // (output rows); lane holds C[16-row block + l16][16-column block + 4 gq + 0..3]
-    f32x4_t acc[4][4];
+    // (output rows); wave (wm, wn) owns output rows wm*64 + 16i + 0..15 (i < 4)
+    // and columns wn*128 + 16j + 0..15 (j < 8); lane holds
+    // C[16-row block + l16][16-column block + 4 gq + 0..3]
+    f32x4_t acc[8][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[j][i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    uint32_t coff[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) coff[s] = sub_chunk8(l16, 4 * s + gq) * 8;
     auto compute = [&](int st) {
         const uint16_t* As = smem[st][0];
         const uint16_t* Bs = smem[st][1];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            bf16x8_t af[4], bfr[4];
+            bf16x8_t af[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                af[i] = __builtin_bit_cast(bf16x8_t,
-                                           *(const uint4*)(As + (wm * 64 + i * 16 + l16) * BBK + coff[s]));
+            for (int i = 0; i < 4; ++i) {
+                const int row = wm * 64 + i * 16 + l16;
+                af[i] = __builtin_bit_cast(
+                    bf16x8_t, *(const uint4*)(As + row * BBK + wg_chunk(row, 4 * s + gq) * 8));
+            }
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bfr[j] = __builtin_bit_cast(bf16x8_t,
-                                            *(const uint4*)(Bs + (wn * 64 + j * 16 + l16) * BBK + coff[s]));
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 8; ++j) {
+                const int row = wn * 128 + j * 16 + l16;
+                const bf16x8_t bf = __builtin_bit_cast(
+                    bf16x8_t, *(const uint4*)(Bs + row * BBK + wg_chunk(row, 4 * s + gq) * 8));
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[j][i], 0, 0, 0);
+                    acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf, af[i], acc[j][i], 0, 0, 0);
+            }
         }
     };
 
+    // two LDS stages; the global loads of stage kt+1 are in flight while
+    // stage kt is multiplied
     if (nk > 0) {
         load(0);
         store(0);
@@ -271,19 +292,30 @@ __global__ void __launch_bounds__(BW_THREADS) wgrad_bf16_kernel(BwdParams p) {
         __syncthreads();
     }
 
-    // epilogue: 8-byte stores of 4 consecutive columns; a group without rows
-    // (K = 0) writes zeros
+    // Epilogue through LDS (the stage buffers are free after the loop's last
+    // barrier): the 256 x 256 bf16 tile, 16-byte chunk c of row r at slot
+    // c ^ (r & 15), then whole 512-byte rows to global memory, 16 bytes per
+    // thread.  A group without rows (K = 0) writes zeros.
+    uint16_t* ot = &smem[0][0][0];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int64_t m = r0 + wm * 64 + i * 16 + l16;
-        if (m >= R) continue;
+        const int row = wm * 64 + i * 16 + l16;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t n = c0 + wn * 64 + j * 16 + 4 * gq;
-            if (n >= C) continue;
-            *(uint2*)(Cp + m * ldc + n) = make_uint2(pack_bf16x2(acc[j][i][0], acc[j][i][1]),
-                                                     pack_bf16x2(acc[j][i][2], acc[j][i][3]));
+        for (int j = 0; j < 8; ++j) {
+            const int col = wn * 128 + j * 16 + 4 * gq;
+            *(uint2*)(ot + row * BT + (((col >> 3) ^ (row & 15)) << 3) + (col & 7)) =
+                make_uint2(pack_bf16x2(acc[j][i][0], acc[j][i][1]),
+                           pack_bf16x2(acc[j][i][2], acc[j][i][3]));
         }
+    }
+    __syncthreads();
+    const int64_t rows = R - r0 < BT ? R - r0 : BT;
+    const int64_t chunks = (C - c0 < BT ? C - c0 : BT) / 8;
+    for (int q = tid; q < BT * (BT / 8); q += BW_THREADS) {
+        const int row = q >> 5, c = q & 31;
+        if (row < rows && c < chunks)
+            *(uint4*)(Cp + (r0 + row) * ldc + c0 + c * 8) =
+                *(const uint4*)(ot + row * BT + ((c ^ (row & 15)) << 3));
     }
 }
 
@@ -450,7 +482,6 @@ hipError_t launch_expert_ffn_backward(const moe_cfg& c, const FfnBwdArgs& a, voi
     p.dws13 = a.dws13;
     p.dws2 = a.dws2;
     const int64_t Ish = p.I_s;
-    const int64_t ng = N + (has_shared ? 1 : 0);
 
     if (c.act_dtype == MOE_BF16) {
         if (TK > 0) {
@@ -459,12 +490,18 @@ hipError_t launch_expert_ffn_backward(const moe_cfg& c, const FfnBwdArgs& a, voi
             if (e != hipSuccess) return e;
         }
         // weight gradients: every group, including experts without rows (zeros)
-        p.ntc = imax(cdiv(I, BT), cdiv(Ish, BT));
-        p.ntn = cdiv(d, BT) * p.ntc;
-        launch_wgrad_bf16<OP_WGRAD_DOWN>(p, ng * p.ntn, st);
-        p.ntc = cdiv(d, BT);
-        p.ntn = imax(cdiv(2 * I, BT), cdiv(2 * Ish, BT)) * p.ntc;
-        launch_wgrad_bf16<OP_WGRAD_UP>(p, ng * p.ntn, st);
+        auto units = [&]() {
+            return (has_shared ? p.ntn_s : 0) + 8 * cdiv(N, 8) * p.ntn_r;
+        };
+        p.ntc_r = cdiv(I, BT);
+        p.ntn_r = cdiv(d, BT) * p.ntc_r;
+        p.ntc_s = cdiv(Ish, BT);
+        p.ntn_s = cdiv(d, BT) * p.ntc_s;
+        launch_wgrad_bf16<OP_WGRAD_DOWN>(p, units(), st);
+        p.ntc_r = p.ntc_s = cdiv(d, BT);
+        p.ntn_r = cdiv(2 * I, BT) * p.ntc_r;
+        p.ntn_s = cdiv(2 * Ish, BT) * p.ntc_s;
+        launch_wgrad_bf16<OP_WGRAD_UP>(p, units(), st);
     } else {
         const int64_t rows = TK + p.T;
         const int64_t hcols = imax(I, Ish);
