@@ -205,17 +205,25 @@ __global__ void __launch_bounds__(BW_THREADS, 1) wgrad_bf16_kernel(BwdParams p) 
     // Loads: thread (rq = t%32, kq = t/32) fetches, for A and for B,
     // contraction rows 4kq..4kq+3 of tile rows (= columns in memory)
     // 8rq..8rq+7, 16 bytes per contraction row: 8 loads per stage.
+    // Rows past the tile or the contraction are read from a clamped address
+    // (always inside the operand) and zeroed afterwards: a load that is
+    // skipped by a condition lets the compiler turn it into a flat load from
+    // a select of pointers.
     const int rq = tid & 31, kq = tid >> 5;
     const bool aok = 8 * rq < R - r0, bok = 8 * rq < C - c0;
-    const uint4 zero = make_uint4(0, 0, 0, 0);
+    const int64_t acol = aok ? 8 * rq : 0, bcol = bok ? 8 * rq : 0;
     uint4 r[8];
     auto load = [&](int kt) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int64_t kr = (int64_t)kt * BBK + 4 * kq + j;
             const bool kok = kr < K;
-            r[j] = (aok && kok) ? *(const uint4*)(a_base + kr * a_ld + 8 * rq) : zero;
-            r[4 + j] = (bok && kok) ? *(const uint4*)(b_base + kr * b_ld + 8 * rq) : zero;
+            const int64_t krc = kok ? kr : K - 1;
+            const uint4 va = *(const uint4*)(a_base + krc * a_ld + acol);
+            const uint4 vb = *(const uint4*)(b_base + krc * b_ld + bcol);
+            const bool ka = aok && kok, kb = bok && kok;
+            r[j] = make_uint4(ka ? va.x : 0u, ka ? va.y : 0u, ka ? va.z : 0u, ka ? va.w : 0u);
+            r[4 + j] = make_uint4(kb ? vb.x : 0u, kb ? vb.y : 0u, kb ? vb.z : 0u, kb ? vb.w : 0u);
         }
     };
     // transpose into LDS: tile row 8rq+i gets the 4 contraction values
@@ -295,7 +303,9 @@ __global__ void __launch_bounds__(BW_THREADS, 1) wgrad_bf16_kernel(BwdParams p) 
     // Epilogue through LDS (the stage buffers are free after the loop's last
     // barrier): the 256 x 256 bf16 tile, 16-byte chunk c of row r at slot
     // c ^ (r & 15), then whole 512-byte rows to global memory, 16 bytes per
-    // thread.  A group without rows (K = 0) writes zeros.
+    // thread, as non-temporal stores (dW is written once and not read back
+    // here; keeping it out of L2 leaves room for the operands; measured
+    // faster).  A group without rows (K = 0) writes zeros.
     uint16_t* ot = &smem[0][0][0];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -313,9 +323,11 @@ __global__ void __launch_bounds__(BW_THREADS, 1) wgrad_bf16_kernel(BwdParams p) 
     const int64_t chunks = (C - c0 < BT ? C - c0 : BT) / 8;
     for (int q = tid; q < BT * (BT / 8); q += BW_THREADS) {
         const int row = q >> 5, c = q & 31;
-        if (row < rows && c < chunks)
-            *(uint4*)(Cp + (r0 + row) * ldc + c0 + c * 8) =
-                *(const uint4*)(ot + row * BT + ((c ^ (row & 15)) << 3));
+        if (row < rows && c < chunks) {
+            const uint4 q4 = *(const uint4*)(ot + row * BT + ((c ^ (row & 15)) << 3));
+            __builtin_nontemporal_store(u32x4_t{q4.x, q4.y, q4.z, q4.w},
+                                        (u32x4_t*)(Cp + (r0 + row) * ldc + c0 + c * 8));
+        }
     }
 }
 
