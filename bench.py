@@ -1,7 +1,7 @@
 """Benchmark: one DeepSeekMoE layer step at DeepSeek-V3 shape on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v3_bf16|v3_fp8|mid_bf16]
-                    [--no-cpu-baseline]
+                    [--no-cpu-baseline] [--backward]
 
 A step is the whole hot path on one batch already resident in HBM:
 route -> permute -> expert FFN (routed + shared) -> combine -> bias update.
@@ -10,6 +10,11 @@ Prints ONE JSON line.  `value` is tokens per second of the whole step;
 with fused SwiGLU, then down), timed live with HIP events on the stream they
 run on, against the roofline (HBM or MFMA) that bounds its algorithmic work; `cpu_baseline` is the CPU oracle timed on a bounded sample of the same
 workload on this host.
+
+--backward measures the layer's backward instead (bf16 / fp32 workloads): a
+step is the four backward calls -- combine backward, expert FFN backward
+(recompute, two dgrad and two wgrad GEMMs), gate/centroid backward, input
+gradient -- on the state of one forward step, reported as its own metric.
 """
 import argparse
 import json
@@ -23,6 +28,7 @@ sys.path.insert(0, ROOT)
 PEAK = {"bf16": 2516.6e12, "fp8": 5033.2e12, "hbm": 8.0e12}
 
 METRIC = "MoE-layer fwd tokens/s at V3 shape; grouped-GEMM % of MFMA peak"
+METRIC_BWD = "MoE-layer bwd tokens/s at V3 shape; expert-backward GEMM % of MFMA peak"
 
 
 def ffn_flops(c):
@@ -55,6 +61,31 @@ def ffn_bytes(c):
     return w + acts
 
 
+def ffn_bwd_flops(c):
+    """recompute a, b (4 M d I), dgrad down (2 M d I), dgrad up (4 M d I),
+    wgrad down (2 M d I), wgrad up (4 M d I) for M = T*k routed rows, and the
+    same for the shared expert over T rows"""
+    T, k, d, I, Is = c["T"], c["k"], c["d"], c["I"], c["Is"]
+    return 16.0 * T * k * d * I + 16.0 * T * d * Is
+
+
+def ffn_bwd_bytes(c):
+    """Algorithmic HBM bytes of one moe_expert_ffn_backward call (bf16), each
+    GEMM reading its operands and writing its result once: weights W13 (the
+    recompute), W2^T and W13^T (the dgrads); x_perm, dY, a/b, h, da/db, dX and
+    the weight gradients as each GEMM reads or writes them."""
+    T, k, d, I, Is, N = c["T"], c["k"], c["d"], c["I"], c["Is"], c["N"]
+    def one(M, I, n):
+        w = 2.0 * n * (2 * I * d + d * I + 2 * I * d)            # W13, W2^T, W13^T read
+        rec = 2.0 * (M * d + M * 2 * I + M * I)                  # x in; a, b and h out
+        dgd = 2.0 * (M * d + M * 2 * I + M * 2 * I)              # dY, a/b in; da/db out
+        dgu = 2.0 * (M * 2 * I + M * d)                          # da/db in; dX out
+        wgd = 2.0 * (M * d + M * I) + 2.0 * n * d * I            # dY, h in; dW2 out
+        wgu = 2.0 * (M * 2 * I + M * d) + 2.0 * n * 2 * I * d    # da/db, x in; dW13 out
+        return w + rec + dgd + dgu + wgd + wgu
+    return one(T * k, I, N) + (one(T, Is, 1) if Is > 0 else 0.0)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -63,6 +94,8 @@ def parse():
     ap.add_argument("--workload", default="v3_bf16")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the layer's backward (four calls) instead of the forward step")
     ap.add_argument("--no-probes", action="store_true",
                     help="skip the measured-peak probes (HBM read, MFMA loop)")
     ap.add_argument("--traffic-run", action="store_true",
@@ -86,23 +119,25 @@ COPY_BYTES = 1 << 30
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
-def gemm_source_hash():
+def gemm_source_hash(backward=False):
     import hashlib
     h = hashlib.sha256()
-    for f in GEMM_SOURCES:
+    for f in GEMM_SOURCES + (("gemm_bwd.hip",) if backward else ()):
         with open(os.path.join(ROOT, "sparse_moe_layer_bias_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_file(workload):
-    return os.path.join(PROFILE_DIR, "expert_ffn_%s_traffic.txt" % workload)
+def traffic_file(workload, backward=False):
+    return os.path.join(PROFILE_DIR, "expert_ffn%s_%s_traffic.txt" %
+                        ("_backward" if backward else "", workload))
 
 
-def recorded_traffic(workload):
-    """HBM bytes per expert-FFN call recorded under profiles/, or None when
-    absent or taken on GEMM sources other than the current ones."""
-    path = traffic_file(workload)
+def recorded_traffic(workload, backward=False):
+    """HBM bytes per expert-FFN (or expert-FFN backward) call recorded under
+    profiles/, or None when absent or taken on GEMM sources other than the
+    current ones."""
+    path = traffic_file(workload, backward)
     if not os.path.exists(path):
         return None
     vals = {}
@@ -111,7 +146,7 @@ def recorded_traffic(workload):
             if ":" in line:
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("gemm_source_hash") != gemm_source_hash():
+    if vals.get("gemm_source_hash") != gemm_source_hash(backward):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -119,7 +154,7 @@ def recorded_traffic(workload):
         return None
 
 
-def traffic_summary(fetch_csv, write_csv, workload):
+def traffic_summary(fetch_csv, write_csv, workload, backward=False):
     import csv
     import collections
 
@@ -143,21 +178,28 @@ def traffic_summary(fetch_csv, write_csv, workload):
     f_scale = COPY_BYTES / cf
     w_scale = COPY_BYTES / cw
     lines = []
-    ffn = [k for k in fetch if "ffn_" in k]
+    # the kernels of one call; each averaged over its last 3 dispatches, the
+    # 3 measured calls (the backward's setup also runs forward kernels)
+    if backward:
+        ffn = [k for k in fetch if "wgrad" in k or "ffn_tile_map" in k or
+               any("ffn_gemm_bf16_kernel<%d," % m in k for m in (1, 2, 3))]
+    else:
+        ffn = [k for k in fetch if "ffn_" in k]
     total = 0.0
     for k in ffn:
-        fb = sum(fetch[k]) / len(fetch[k]) * 1024.0 * f_scale
-        wb = (sum(write[k]) / len(write[k]) * 1024.0 * w_scale) if k in write else 0.0
+        fl, wl = fetch[k][-3:], write.get(k, [0.0])[-3:]
+        fb = sum(fl) / len(fl) * 1024.0 * f_scale
+        wb = sum(wl) / len(wl) * 1024.0 * w_scale
         total += fb + wb
-        lines.append("kernel: %s | fetch %.4g B | write %.4g B | dispatches %d" %
-                     (k[:90], fb, wb, len(fetch[k])))
+        lines.append("kernel: %s | fetch %.4g B | write %.4g B | dispatches averaged %d" %
+                     (k[:90], fb, wb, len(fl)))
     out = ["workload: %s" % workload,
            "calibration_copy_kernel: %s" % copy_k[0][:90],
            "calibration_fetch_scale: %.5f" % f_scale,
            "calibration_write_scale: %.5f" % w_scale]
     out += lines
     out += ["hbm_bytes_per_launch: %.6g" % total,
-            "gemm_source_hash: %s" % gemm_source_hash()]
+            "gemm_source_hash: %s" % gemm_source_hash(backward)]
     return "\n".join(out)
 
 
@@ -258,14 +300,24 @@ def counter_summary(mfma_csv, fetch_csv, write_csv, workload):
     return "\n".join(out)
 
 
-def traffic_run(cfg, layer, dev):
+def traffic_run(cfg, layer, dev, backward=False):
     import torch
     x = dev["x"]
     layer.route(x, dev["centroids"], dev["bias"])
     layer.permute(x)
     torch.cuda.synchronize()
-    for _ in range(3):
+    if backward:
+        import moe_inputs
+        dout = moe_inputs.make_upstream_grad(cfg, 0, "cuda")
         layer.expert_ffn(x)
+        layer.combine(x)
+        layer.backward(dout, x, dev["centroids"])  # buffers, and the dy_perm the FFN reads
+        torch.cuda.synchronize()
+        for _ in range(3):
+            layer.expert_ffn_backward(dout, x)
+    else:
+        for _ in range(3):
+            layer.expert_ffn(x)
     a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     b = torch.empty_like(a)
     for _ in range(3):
@@ -327,13 +379,139 @@ def cpu_baseline(cfg, dev, log):
                       % (S, R, cfg["k"] + 1)}
 
 
+def cpu_baseline_backward(cfg, dev, log):
+    """Time the oracle's backward (untuned) on a bounded sample and scale to
+    tokens/s: the combine, gate/logit, centroid and input gradients on all T
+    tokens; the SwiGLU expert backward on R rows of expert 0, its per-row time
+    counted k+1 times per token (k routed rows + the shared row)."""
+    import numpy as np
+
+    import moe_inputs
+    from oracle import oracle as orc
+
+    S = cfg["T"]
+    R = min(128, S)
+    k, N = cfg["k"], cfg["N"]
+    xs = moe_inputs.to_host(dev["x"][:S])
+    E = moe_inputs.to_host(dev["centroids"])
+    b = moe_inputs.to_host(dev["bias"])
+    w13 = moe_inputs.to_host(dev["w13"][0])
+    w2 = moe_inputs.to_host(dev["w2"][0])
+    dout = moe_inputs.to_host(moe_inputs.make_upstream_grad(cfg, 0, "cpu", T=S))
+    orc.lib()
+    r = orc.route(xs, E, b, k, cfg["G"], cfg["TG"], want_scores=True)
+    off, src, dst = orc.permute(r["idx"], N)
+    yp = np.resize(dout, (S * k, dout.shape[1]))  # stand-in expert outputs (timing only)
+    t0 = time.perf_counter()
+    dyp, dg = orc.combine_backward(dout, yp, r["gate"], dst)
+    t1 = time.perf_counter()
+    dA, _, _ = orc.swiglu_ffn_backward(xs[:R], w13, w2, dout[:R])
+    t2 = time.perf_counter()
+    dz = orc.route_backward(r["scores"], r["idx"], dg)
+    orc.centroid_grad(xs, r["idx"], dz, N)
+    dxp = np.resize(dA, (S * k, dA.shape[1]))
+    dxs = np.resize(dA, (S, dA.shape[1]))
+    orc.input_grad(dout, dxs, dxp, dst, dz, r["idx"], E)
+    t3 = time.perf_counter()
+    per_token = ((t1 - t0) + (t3 - t2)) / S + (t2 - t1) / R * (k + 1)
+    cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    log("cpu oracle backward: combine %.2fs expert(%d rows) %.2fs route+input %.2fs -> %.4f "
+        "s/token" % (t1 - t0, R, t2 - t1, t3 - t2, per_token))
+    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "combine, gate/logit, centroid and input gradients on all %d tokens; "
+                      "the SwiGLU expert backward (recompute, dgrads, weight gradients) on %d "
+                      "rows of expert 0, its per-row time counted k+1=%d times per token"
+                      % (S, R, k + 1)}
+
+
+def run_backward(args, cfg, dev, log):
+    """Time K backward steps on the state of one forward step; one JSON line."""
+    import torch
+
+    import moe_inputs
+    from sparse_moe_layer_bias_amd.layer import MoeLayer
+
+    T = cfg["T"]
+    layer = MoeLayer(cfg, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"], train=True)
+    x, E = dev["x"], dev["centroids"]
+    dout = moe_inputs.make_upstream_grad(cfg, args.seed, "cuda")
+    stream = torch.cuda.current_stream()
+    layer.forward(x, E, dev["bias"].clone(), update_bias=False)
+    for _ in range(args.warmup):
+        layer.backward(dout, x, E)
+    torch.cuda.synchronize()
+    log("warmup done")
+    stages = ["combine_backward", "expert_ffn_backward", "route_backward", "input_grad"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+          for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for s in range(args.steps):
+        layer.backward(dout, x, E, events=ev[s])
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_stop) / args.steps
+    stage_ms = {st: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps))
+                / args.steps for i, st in enumerate(stages)}
+    log("stages ms:", json.dumps({k: round(v, 4) for k, v in stage_ms.items()}))
+    flops = ffn_bwd_flops(cfg)
+    nbytes = ffn_bwd_bytes(cfg)
+    ffn_s = stage_ms["expert_ffn_backward"] / 1e3
+    achieved = flops / ffn_s
+    peak = PEAK["bf16"]
+    hbm_bound = nbytes / PEAK["hbm"] > flops / peak
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": nbytes / ffn_s / 1e9, "peak": PEAK["hbm"] / 1e9,
+                "unit": "GB/s", "frac": nbytes / ffn_s / PEAK["hbm"]}
+    else:
+        roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12,
+                "unit": "TFLOP/s", "frac": achieved / peak}
+    roof.update({"kernel": "expert FFN backward GEMMs (recompute, dgrad down+SwiGLU', "
+                           "dgrad up, wgrad down, wgrad up)",
+                 "traffic": recorded_traffic(args.workload, backward=True),
+                 "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+                 "mfma_tflops": achieved / 1e12, "mfma_frac": achieved / peak})
+    result = {
+        "metric": METRIC_BWD,
+        "value": T / (ms_per_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic",
+        "config": {"workload": "%s backward: T=%d d=%d, %d routed experts top-%d%s + 1 "
+                               "shared, SwiGLU I=%d, %s" %
+                               (args.workload, T, cfg["d"], cfg["N"], cfg["k"],
+                                (" (%d groups, top-%d)" % (cfg["G"], cfg["TG"]))
+                                if cfg["G"] > 1 else "", cfg["I"], cfg["dtype"]),
+                   "global_batch": T, "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "stages_ms": stage_ms,
+    }
+    if not args.no_cpu_baseline:
+        try:
+            result["cpu_baseline"] = cpu_baseline_backward(cfg, dev, log)
+        except Exception as ex:  # report, never hide
+            log("cpu baseline failed:", repr(ex))
+            result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.stats_summary:
         print(stats_summary(args.stats_summary))
         return
     if args.traffic_summary:
-        print(traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.workload))
+        print(traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.workload,
+                              args.backward))
         return
     if args.counter_summary:
         print(counter_summary(*args.counter_summary, args.workload))
@@ -360,13 +538,19 @@ def main():
     T = cfg["T"]
     log("generating inputs for", args.workload, cfg)
     dev = moe_inputs.make_layer_inputs(cfg, args.seed, "cuda")
-    layer = MoeLayer(cfg, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"])
+    if args.backward and cfg.get("fp8"):
+        log("the backward covers bf16 and fp32 layers")
+        sys.exit(2)
+    if args.backward and not args.traffic_run:
+        run_backward(args, cfg, dev, log)
+        return
+    layer = MoeLayer(cfg, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"], train=args.backward)
     x, E = dev["x"], dev["centroids"]
     bias = dev["bias"].clone()
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
     if args.traffic_run:
-        traffic_run(cfg, layer, dev)
+        traffic_run(cfg, layer, dev, args.backward)
         log("traffic run done")
         return
     if args.counter_run:

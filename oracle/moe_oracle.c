@@ -649,16 +649,22 @@ void orc_route_backward(int64_t T, int64_t N, int64_t k, const float* scores,
  * rows of experts nobody chose are zero. */
 void orc_centroid_grad(int64_t T, int64_t d, int64_t N, int64_t k, int dtype, const void* x,
                        const int32_t* idx, const float* dz, float* dcentroids) {
-#pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < N; ++i)
-        for (int64_t c = 0; c < d; ++c) {
-            double acc = 0.0;
+    /* one expert per iteration; each column's terms are added in (t, j) order */
+#pragma omp parallel
+    {
+        double* acc = (double*)malloc((size_t)(d + 1) * sizeof(double));
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < N; ++i) {
+            for (int64_t c = 0; c < d; ++c) acc[c] = 0.0;
             for (int64_t t = 0; t < T; ++t)
                 for (int64_t j = 0; j < k; ++j)
                     if (idx[t * k + j] == i)
-                        acc += (double)dz[t * k + j] * (double)load_elem(x, dtype, t * d + c);
-            dcentroids[i * d + c] = (float)acc;
+                        for (int64_t c = 0; c < d; ++c)
+                            acc[c] += (double)dz[t * k + j] * (double)load_elem(x, dtype, t * d + c);
+            for (int64_t c = 0; c < d; ++c) dcentroids[i * d + c] = (float)acc[c];
         }
+        free(acc);
+    }
 }
 
 /* input gradient.  u_t reaches the output through the residual, the shared

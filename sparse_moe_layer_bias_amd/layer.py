@@ -177,28 +177,41 @@ class MoeLayer:
         g["workspace"] = torch.empty((wsb,), dtype=torch.uint8, device=dev)
         return g
 
-    def backward(self, dout, x, centroids, residual=True, stream=None):
+    def expert_ffn_backward(self, dout, x, stream=None):
+        """moe_expert_ffn_backward on the buffers of the last backward call
+        (dy_perm from its combine backward)."""
+        g = self.grads
+        shared = self.ws13t is not None
+        moe_expert_ffn_backward(self.cfg, self.x_perm, self.offsets, self.w13, self.w13t,
+                                self.w2t, g["dy_perm"], x if shared else None, self.ws13,
+                                self.ws13t, self.ws2t, dout if shared else None, g["dx_perm"],
+                                g["dx_shared"], g["dw13"], g["dw2"], g["dws13"], g["dws2"],
+                                g["workspace"], stream)
+
+    def backward(self, dout, x, centroids, residual=True, stream=None, events=None):
         """Gradients of the last forward step for the upstream gradient ``dout``
         [T, d]: returns a dict with dx, dcentroids, dw13, dw2, dws13, dws2 (plus
         the intermediates dy_perm, dgate, dx_perm, dx_shared, dz).  The buffers
-        are reused across calls."""
+        are reused across calls.  ``events``: 5 torch.cuda.Events recorded
+        around the four calls (on the current stream)."""
         if not self.train:
             raise RuntimeError("the backward needs the transposed weight packs: build the "
                                "layer with train=True")
         if self.grads is None:
             self.grads = self._grad_buffers(centroids)
         g = self.grads
-        shared = self.ws13t is not None
+        mark = (lambda i: events[i].record()) if events is not None else (lambda i: None)
+        mark(0)
         moe_combine_backward(self.cfg, dout, self.y_perm, self.gate, self.dst_row, g["dy_perm"],
                              g["dgate"], stream)
-        moe_expert_ffn_backward(self.cfg, self.x_perm, self.offsets, self.w13, self.w13t,
-                                self.w2t, g["dy_perm"], x if shared else None, self.ws13,
-                                self.ws13t, self.ws2t, dout if shared else None, g["dx_perm"],
-                                g["dx_shared"], g["dw13"], g["dw2"], g["dws13"], g["dws2"],
-                                g["workspace"], stream)
+        mark(1)
+        self.expert_ffn_backward(dout, x, stream)
+        mark(2)
         moe_route_backward(self.cfg, x, self.scores, self.idx, g["dgate"], self.offsets,
                            self.src_token, self.dst_row, g["dz"], g["dcentroids"],
                            g["workspace"], stream)
+        mark(3)
         moe_input_grad(self.cfg, dout if residual else None, g["dx_shared"], g["dx_perm"],
                        self.dst_row, g["dz"], self.idx, centroids, g["dx"], stream)
+        mark(4)
         return g
