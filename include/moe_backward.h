@@ -13,6 +13,9 @@
  * rule splits into four calls, run in this order after a forward step whose
  * buffers (scores, idx, gate, offsets, src_token, dst_row, x_perm, y_perm)
  * are kept:
+ * The forward's expert call may be moe_expert_ffn_train, which also keeps the
+ * SwiGLU inputs a, b and its output h for the backward (else the backward
+ * recomputes them).
  *   moe_combine_backward     dout -> routed-row gradients dy_perm and dgate
  *   moe_expert_ffn_backward  dy_perm, dout -> dx_perm, dx_shared and every
  *                            expert's weight gradients
@@ -47,20 +50,37 @@ int moe_combine_backward(const moe_cfg* cfg, const void* dout, const void* y_per
                          const float* gate, const int32_t* dst_row, void* dy_perm, float* dgate,
                          void* stream);
 
+/* Bytes of the activations a training forward keeps: a, b and h of every
+ * routed row and every shared-expert row, in act_dtype. */
+size_t moe_expert_ffn_saved_size(const moe_cfg* cfg);
+
+/* Training forward of the grouped SwiGLU experts: the same results as
+ * moe_expert_ffn (bitwise), and it also stores into `saved`
+ * (moe_expert_ffn_saved_size bytes, caller-owned, device) the activations
+ * a = X W1^T and b = X W3^T (rounded to act_dtype) and h = silu(a) * b of
+ * every row, for moe_expert_ffn_backward.  bf16 and fp32 layers only
+ * (gemm_dtype == act_dtype); weights packed as for moe_expert_ffn; the other
+ * arguments as there. */
+int moe_expert_ffn_train(const moe_cfg* cfg, const void* x_perm, const int32_t* offsets,
+                         const void* w13, const void* w2, void* y_perm, const void* x_sh,
+                         const void* ws13, const void* ws2, void* y_shared, void* saved,
+                         size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
 /* Bytes of workspace moe_expert_ffn_backward needs: the recomputed a, b, h and
  * the gradients da, db of every row (bf16 V3 shape: about 1.5 GB). */
 size_t moe_expert_ffn_backward_workspace_size(const moe_cfg* cfg);
 
 /* Backward of the grouped SwiGLU experts (routed experts over their rows of
  * x_perm, the shared expert over all T rows).  For one expert with rows X:
- *   a = X W1^T, b = X W3^T, h = silu(a) b   (recomputed; h and a, b stored in act_dtype)
+ *   a = X W1^T, b = X W3^T, h = silu(a) b   (read from `saved`, or recomputed)
  *   dh = dY W2;  da = dh b silu'(a), db = dh silu(a)   (stored in act_dtype)
  *   dX = da W1 + db W3;  dW2 = dY^T h;  dW1 = da^T X;  dW3 = db^T X
  * with silu'(a) = sig(a) (1 + a (1 - sig(a))).
  *  x_perm    [T*k, d]      the forward's routed rows
  *  offsets   [N+1]         the forward's expert row offsets
  *  w13       routed gate/up weights packed as for the forward (moe_pack_weights
- *            which = 0), used to recompute a, b, h
+ *            which = 0), used to recompute a, b, h; may be NULL with `saved`
  *  w13t      the same weights [N, 2I, d] packed transposed (which = 4), for dX
  *  w2t       routed down weights [N, d, I] packed transposed (which = 5), for dh
  *  dy_perm   [T*k, d]      from moe_combine_backward
@@ -73,6 +93,8 @@ size_t moe_expert_ffn_backward_workspace_size(const moe_cfg* cfg);
  *  dw13 [N, 2I, d], dw2 [N, d, I], dws13 [2Is, d], dws2 [d, Is]
  *                          out, plain row-major like the weights; an expert
  *                          without rows gets zeros
+ *  saved     the activations kept by moe_expert_ffn_train for this step
+ *            (saved_bytes >= moe_expert_ffn_saved_size), or NULL: recompute
  * Activations and gradients in act_dtype.  fp32 layers: every packed form is
  * a plain copy.  bf16 needs hidden, inter, inter_shared % 128 == 0. */
 int moe_expert_ffn_backward(const moe_cfg* cfg, const void* x_perm, const int32_t* offsets,
@@ -80,7 +102,8 @@ int moe_expert_ffn_backward(const moe_cfg* cfg, const void* x_perm, const int32_
                             const void* dy_perm, const void* x_sh, const void* ws13,
                             const void* ws13t, const void* ws2t, const void* dy_shared,
                             void* dx_perm, void* dx_shared, void* dw13, void* dw2, void* dws13,
-                            void* dws2, void* workspace, size_t workspace_bytes, void* stream);
+                            void* dws2, const void* saved, size_t saved_bytes, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace moe_route_backward needs (T*k fp32). */
 size_t moe_route_backward_workspace_size(const moe_cfg* cfg);

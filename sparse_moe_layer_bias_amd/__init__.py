@@ -8,8 +8,9 @@ missing, importing the functions fails loudly.
 
 The functions carry the C names: moe_route, moe_permute, moe_expert_ffn,
 moe_combine, moe_bias_update, moe_quantize_weights_fp8, the backward calls of
-include/moe_backward.h (moe_combine_backward, moe_expert_ffn_backward,
-moe_route_backward, moe_input_grad), plus the workspace size queries.
+include/moe_backward.h (moe_expert_ffn_train, moe_combine_backward,
+moe_expert_ffn_backward, moe_route_backward, moe_input_grad), plus the workspace
+size queries.
 ``MoeLayer`` (in layer.py) strings them together for one step.
 """
 import ctypes
@@ -75,7 +76,9 @@ def lib():
             "moe_quantize_weights_fp8": ([I64, I64, I64, P, P, P, P], ctypes.c_int),
             "moe_combine_backward": ([C, P, P, P, P, P, P, P], ctypes.c_int),
             "moe_expert_ffn_backward_workspace_size": ([C], SZ),
-            "moe_expert_ffn_backward": ([C] + [P] * 18 + [SZ, P], ctypes.c_int),
+            "moe_expert_ffn_backward": ([C] + [P] * 18 + [SZ, P, SZ, P], ctypes.c_int),
+            "moe_expert_ffn_saved_size": ([C], SZ),
+            "moe_expert_ffn_train": ([C] + [P] * 10 + [SZ, P, SZ, P], ctypes.c_int),
             "moe_route_backward_workspace_size": ([C], SZ),
             "moe_route_backward": ([C] + [P] * 10 + [SZ, P], ctypes.c_int),
             "moe_input_grad": ([C] + [P] * 8 + [P], ctypes.c_int),
@@ -187,14 +190,26 @@ def moe_expert_ffn_backward_workspace_size(cfg):
     return lib().moe_expert_ffn_backward_workspace_size(ctypes.byref(cfg))
 
 
+def moe_expert_ffn_saved_size(cfg):
+    return lib().moe_expert_ffn_saved_size(ctypes.byref(cfg))
+
+
+def moe_expert_ffn_train(cfg, x_perm, offsets, w13, w2, y_perm, x_sh, ws13, ws2, y_shared, saved,
+                         workspace, stream=None):
+    _check(lib().moe_expert_ffn_train(ctypes.byref(cfg), _p(x_perm), _p(offsets), _p(w13),
+                                      _p(w2), _p(y_perm), _p(x_sh), _p(ws13), _p(ws2),
+                                      _p(y_shared), _p(saved), _nbytes(saved), _p(workspace),
+                                      _nbytes(workspace), _stream(stream)))
+
+
 def moe_expert_ffn_backward(cfg, x_perm, offsets, w13, w13t, w2t, dy_perm, x_sh, ws13, ws13t,
-                            ws2t, dy_shared, dx_perm, dx_shared, dw13, dw2, dws13, dws2, workspace,
-                            stream=None):
+                            ws2t, dy_shared, dx_perm, dx_shared, dw13, dw2, dws13, dws2, saved,
+                            workspace, stream=None):
     _check(lib().moe_expert_ffn_backward(
         ctypes.byref(cfg), _p(x_perm), _p(offsets), _p(w13), _p(w13t), _p(w2t), _p(dy_perm),
         _p(x_sh), _p(ws13), _p(ws13t), _p(ws2t), _p(dy_shared), _p(dx_perm), _p(dx_shared),
-        _p(dw13), _p(dw2), _p(dws13), _p(dws2), _p(workspace), _nbytes(workspace),
-        _stream(stream)))
+        _p(dw13), _p(dw2), _p(dws13), _p(dws2), _p(saved), _nbytes(saved), _p(workspace),
+        _nbytes(workspace), _stream(stream)))
 
 
 def moe_route_backward_workspace_size(cfg):

@@ -117,7 +117,7 @@ int set_error(int code, const char* msg) {
 
 extern "C" {
 
-int moe_abi_version(void) { return 3; }
+int moe_abi_version(void) { return 4; }
 
 const char* moe_last_error(void) { return g_err; }
 
@@ -191,13 +191,15 @@ size_t moe_expert_ffn_workspace_size(const moe_cfg* cfg) {
     return moe::ffn_workspace_bytes(*cfg);
 }
 
-int moe_expert_ffn(const moe_cfg* cfg, const void* x_perm, const float* x_perm_scale,
-                   const int32_t* offsets, const void* w13, const float* w13_scale,
-                   const void* w2, const float* w2_scale, void* y_perm, const void* x_sh,
-                   const float* x_sh_scale, const void* ws13, const float* ws13_scale,
-                   const void* ws2, const float* ws2_scale, void* y_shared, void* workspace,
-                   size_t workspace_bytes, void* stream) {
-    const char* fn = "moe_expert_ffn";
+}  // extern "C"
+
+static int expert_ffn_impl(const char* fn, const moe_cfg* cfg, const void* x_perm,
+                           const float* x_perm_scale, const int32_t* offsets, const void* w13,
+                           const float* w13_scale, const void* w2, const float* w2_scale,
+                           void* y_perm, const void* x_sh, const float* x_sh_scale,
+                           const void* ws13, const float* ws13_scale, const void* ws2,
+                           const float* ws2_scale, void* y_shared, void* saved,
+                           void* workspace, size_t workspace_bytes, void* stream) {
     if (int r = check_cfg(fn, cfg)) return r;
     if (int r = check_ffn_shape(fn, cfg)) return r;
     const bool fp8 = cfg->gemm_dtype == MOE_FP8_E4M3;
@@ -230,8 +232,51 @@ int moe_expert_ffn(const moe_cfg* cfg, const void* x_perm, const float* x_perm_s
     }
     moe::FfnArgs a{x_perm, x_perm_scale, offsets, w13, w13_scale, w2, w2_scale, y_perm,
                    x_sh,   x_sh_scale,   ws13,    ws13_scale, ws2, ws2_scale, y_shared};
-    return hip_status(fn, moe::launch_expert_ffn(*cfg, a, workspace, (hipStream_t)stream));
+    return hip_status(fn, moe::launch_expert_ffn(*cfg, a, workspace, (hipStream_t)stream, saved));
 }
+
+extern "C" {
+
+int moe_expert_ffn(const moe_cfg* cfg, const void* x_perm, const float* x_perm_scale,
+                   const int32_t* offsets, const void* w13, const float* w13_scale,
+                   const void* w2, const float* w2_scale, void* y_perm, const void* x_sh,
+                   const float* x_sh_scale, const void* ws13, const float* ws13_scale,
+                   const void* ws2, const float* ws2_scale, void* y_shared, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+    return expert_ffn_impl("moe_expert_ffn", cfg, x_perm, x_perm_scale, offsets, w13, w13_scale,
+                           w2, w2_scale, y_perm, x_sh, x_sh_scale, ws13, ws13_scale, ws2,
+                           ws2_scale, y_shared, nullptr, workspace, workspace_bytes, stream);
+}
+
+size_t moe_expert_ffn_saved_size(const moe_cfg* cfg) {
+    if (!cfg) return 0;
+    return moe::ffn_saved_bytes(*cfg);
+}
+
+int moe_expert_ffn_train(const moe_cfg* cfg, const void* x_perm, const int32_t* offsets,
+                         const void* w13, const void* w2, void* y_perm, const void* x_sh,
+                         const void* ws13, const void* ws2, void* y_shared, void* saved,
+                         size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    const char* fn = "moe_expert_ffn_train";
+    if (int r = check_cfg(fn, cfg)) return r;
+    if (cfg->gemm_dtype != cfg->act_dtype)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: the training forward covers bf16 and fp32 storage",
+                    fn);
+    if (cfg->tokens > 0) {
+        REQ_PTR(saved);
+        if (saved_bytes < moe_expert_ffn_saved_size(cfg))
+            return fail(MOE_ERR_WORKSPACE, "%s: saved %zu < %zu bytes", fn, saved_bytes,
+                        moe_expert_ffn_saved_size(cfg));
+    }
+    return expert_ffn_impl(fn, cfg, x_perm, nullptr, offsets, w13, nullptr, w2, nullptr, y_perm,
+                           x_sh, nullptr, ws13, nullptr, ws2, nullptr, y_shared,
+                           cfg->tokens > 0 ? saved : nullptr, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+extern "C" {
 
 size_t moe_packed_weights_size(const moe_cfg* cfg, int which) {
     if (!cfg || which < 0 || which > 7) return 0;
@@ -337,7 +382,8 @@ int moe_expert_ffn_backward(const moe_cfg* cfg, const void* x_perm, const int32_
                             const void* dy_perm, const void* x_sh, const void* ws13,
                             const void* ws13t, const void* ws2t, const void* dy_shared,
                             void* dx_perm, void* dx_shared, void* dw13, void* dw2, void* dws13,
-                            void* dws2, void* workspace, size_t workspace_bytes, void* stream) {
+                            void* dws2, const void* saved, size_t saved_bytes, void* workspace,
+                            size_t workspace_bytes, void* stream) {
     const char* fn = "moe_expert_ffn_backward";
     if (int r = check_cfg(fn, cfg)) return r;
     if (int r = check_ffn_shape(fn, cfg)) return r;
@@ -350,14 +396,14 @@ int moe_expert_ffn_backward(const moe_cfg* cfg, const void* x_perm, const int32_
     REQ_PTR(workspace);
     if (cfg->tokens > 0) {
         REQ_PTR(x_perm);
-        REQ_PTR(w13);
+        OPT_PTR(w13);
         REQ_PTR(w13t);
         REQ_PTR(w2t);
         REQ_PTR(dy_perm);
         REQ_PTR(dx_perm);
         if (cfg->inter_shared > 0) {
             REQ_PTR(x_sh);
-            REQ_PTR(ws13);
+            if (!saved) REQ_PTR(ws13);
             REQ_PTR(ws13t);
             REQ_PTR(ws2t);
             REQ_PTR(dy_shared);
@@ -376,9 +422,16 @@ int moe_expert_ffn_backward(const moe_cfg* cfg, const void* x_perm, const int32_
     if (workspace_bytes < moe_expert_ffn_backward_workspace_size(cfg))
         return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes,
                     moe_expert_ffn_backward_workspace_size(cfg));
+    OPT_PTR(saved);
+    if (saved && saved_bytes < moe_expert_ffn_saved_size(cfg))
+        return fail(MOE_ERR_WORKSPACE, "%s: saved %zu < %zu bytes", fn, saved_bytes,
+                    moe_expert_ffn_saved_size(cfg));
+    if (!saved && cfg->tokens > 0 && !w13)
+        return fail(MOE_ERR_ARG, "%s: w13 is needed to recompute without saved activations", fn);
     moe::FfnBwdArgs a{x_perm,  offsets, w13,     w13t,      w2t,  dy_perm, x_sh, ws13,  ws13t,
                       ws2t,    dy_shared, dx_perm, dx_shared, dw13, dw2,     dws13, dws2};
-    return hip_status(fn, moe::launch_expert_ffn_backward(*cfg, a, workspace, (hipStream_t)stream));
+    return hip_status(fn, moe::launch_expert_ffn_backward(*cfg, a, workspace, (hipStream_t)stream,
+                                                          saved));
 }
 
 size_t moe_route_backward_workspace_size(const moe_cfg* cfg) {

@@ -606,11 +606,19 @@ hipError_t launch_expert_ffn_fp8(const moe_cfg& c, const FfnArgs& a, const int2*
                                  void* h_s, float* hs_r, float* hs_s, int64_t max_r,
                                  int64_t max_s, hipStream_t st);
 
-hipError_t launch_expert_ffn(const moe_cfg& c, const FfnArgs& a, void* ws, hipStream_t st) {
+hipError_t launch_expert_ffn(const moe_cfg& c, const FfnArgs& a, void* ws, hipStream_t st,
+                             void* saved) {
     const int64_t T = c.tokens, TK = T * c.top_k;
     const bool has_shared = c.inter_shared > 0 && T > 0;
     if (TK == 0) return hipSuccess;
     FfnWs w = carve_ffn(c, ws);
+    SavedActs sv{};
+    if (saved) {
+        // training forward: h lives in the saved activations (with a, b)
+        sv = carve_saved(c, saved);
+        w.h_r = sv.h_r;
+        w.h_s = sv.h_s;
+    }
     const int BM = ffn_bm(c);
     const int64_t max_r = ffn_max_routed_tiles(c);
     const int64_t max_s = has_shared ? ffn_max_shared_tiles(c) : 0;
@@ -645,10 +653,20 @@ hipError_t launch_expert_ffn(const moe_cfg& c, const FfnArgs& a, void* ws, hipSt
     p.ntn_s = has_shared ? (int)cdiv(c.inter_shared, cols0) : 0;
     // a block for every (XCD, slot) the mapping can produce
     unsigned grid = (unsigned)ffn_grid_blocks(max_r, p.ntn_r, max_s, p.ntn_s);
-    if (bf)
+    if (bf && saved) {
+        p.E_r = sv.ab_r;  // mode 2: also a and b
+        p.E_s = sv.ab_s;
+        ffn_gemm_bf16_kernel<2, MOE_GEMM_BK, MOE_GEMM_NS><<<grid, G_THREADS, 0, st>>>(p);
+        p.E_r = p.E_s = nullptr;
+    } else if (bf) {
         ffn_gemm_bf16_kernel<0, MOE_GEMM_BK, MOE_GEMM_NS><<<grid, G_THREADS, 0, st>>>(p);
-    else
+    } else if (saved) {
+        const hipError_t e = launch_ffn_save_f32(c, a.x_perm, a.x_sh, a.offsets, a.w13, a.ws13,
+                                                 saved, st);
+        if (e != hipSuccess) return e;
+    } else {
         ffn_gemm_f32_kernel<0><<<grid, 256, 0, st>>>(p);
+    }
 
     // down: h x W2 -> y  (bf16: 256 output columns per weight tile)
     p.K_r = c.inter;
@@ -677,9 +695,9 @@ hipError_t launch_expert_ffn(const moe_cfg& c, const FfnArgs& a, void* ws, hipSt
 namespace moe {
 
 // ---------------------------------------------------------------- backward GEMMs
-// Recompute, down-projection dgrad and up-projection dgrad of the backward,
-// on the forward's kernel (modes 2, 3 and 1).  The tile list is built here with
-// the forward's row tile.
+// Recompute (unless a training forward saved a, b and h), down-projection dgrad
+// and up-projection dgrad of the backward, on the forward's kernel (modes 2, 3
+// and 1).  The tile list is built here with the forward's row tile.
 size_t ffn_bwd_tile_ws_bytes(const moe_cfg& c) {
     return (size_t)(align256((ffn_max_routed_tiles(c) + ffn_max_shared_tiles(c)) * 8) + 256 +
                     2 * align256(ffn_max_routed_tiles(c) * 4));
@@ -687,7 +705,7 @@ size_t ffn_bwd_tile_ws_bytes(const moe_cfg& c) {
 
 hipError_t launch_ffn_bwd_dgrad_bf16(const moe_cfg& c, const FfnBwdArgs& a, void* tile_ws,
                                      void* ab_r, void* ab_s, void* h_r, void* h_s, void* dab_r,
-                                     void* dab_s, hipStream_t st) {
+                                     void* dab_s, bool recompute, hipStream_t st) {
     const int64_t T = c.tokens, d = c.hidden, I = c.inter, Is = c.inter_shared;
     const bool has_shared = Is > 0 && T > 0;
     char* q = (char*)tile_ws;
@@ -724,7 +742,7 @@ hipError_t launch_ffn_bwd_dgrad_bf16(const moe_cfg& c, const FfnBwdArgs& a, void
     p.ntn_r = (int)cdiv(I, 128);
     p.ntn_s = has_shared ? (int)cdiv(Is, 128) : 0;
     unsigned grid = (unsigned)ffn_grid_blocks(max_r, p.ntn_r, max_s, p.ntn_s);
-    ffn_gemm_bf16_kernel<2, MOE_GEMM_BK, MOE_GEMM_NS><<<grid, G_THREADS, 0, st>>>(p);
+    if (recompute) ffn_gemm_bf16_kernel<2, MOE_GEMM_BK, MOE_GEMM_NS><<<grid, G_THREADS, 0, st>>>(p);
     // down dgrad: dh = dY W2 (W2 transposed and packed), epilogue -> da, db
     p.A_r = a.dy_perm;
     p.A_s = a.dy_sh;

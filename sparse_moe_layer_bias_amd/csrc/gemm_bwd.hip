@@ -420,6 +420,25 @@ static int64_t align256(int64_t b) { return (b + 255) & ~int64_t(255); }
 static int64_t bwd_esz(const moe_cfg& c) { return c.act_dtype == MOE_BF16 ? 2 : 4; }
 static int64_t imax(int64_t a, int64_t b) { return a > b ? a : b; }
 
+size_t ffn_saved_bytes(const moe_cfg& c) {
+    const int64_t TK = c.tokens * c.top_k, T = c.tokens, eb = bwd_esz(c);
+    const int64_t I = c.inter, Is = c.inter_shared;
+    return (size_t)(align256(TK * 2 * I * eb) + align256(TK * I * eb) +
+                    align256(T * 2 * Is * eb) + align256(T * Is * eb));
+}
+
+SavedActs carve_saved(const moe_cfg& c, void* saved) {
+    const int64_t TK = c.tokens * c.top_k, T = c.tokens, eb = bwd_esz(c);
+    const int64_t I = c.inter, Is = c.inter_shared;
+    char* q = (char*)saved;
+    SavedActs s{};
+    s.ab_r = q; q += align256(TK * 2 * I * eb);
+    s.h_r = q; q += align256(TK * I * eb);
+    s.ab_s = q; q += align256(T * 2 * Is * eb);
+    s.h_s = q;
+    return s;
+}
+
 size_t ffn_backward_workspace_bytes(const moe_cfg& c) {
     const int64_t TK = c.tokens * c.top_k, T = c.tokens, eb = bwd_esz(c);
     const int64_t I = c.inter, Is = c.inter_shared;
@@ -457,21 +476,55 @@ static void launch_bwd_f32(const BwdParams& p, int64_t cols, int64_t per_r, int6
         bwd_f32_kernel<OP><<<dim3((unsigned)cdiv(total, 256)), 256, 0, st>>>(p, cols, per_r, total);
 }
 
+static BwdParams bwd_params(const moe_cfg& c) {
+    const int64_t T = c.tokens;
+    const bool has_shared = c.inter_shared > 0 && T > 0;
+    BwdParams p{};
+    p.N = (int)c.n_experts;
+    p.has_shared = has_shared ? 1 : 0;
+    p.T = has_shared ? T : 0;
+    p.TK = T * c.top_k;
+    p.d = c.hidden;
+    p.I_r = c.inter;
+    p.I_s = has_shared ? c.inter_shared : 0;
+    return p;
+}
+
+hipError_t launch_ffn_save_f32(const moe_cfg& c, const void* x_perm, const void* x_sh,
+                               const int32_t* offsets, const void* w13, const void* ws13,
+                               void* saved, hipStream_t st) {
+    BwdParams p = bwd_params(c);
+    const SavedActs sv = carve_saved(c, saved);
+    p.offsets = offsets;
+    p.x_perm = x_perm;
+    p.x = x_sh;
+    p.w13 = w13;
+    p.ws13 = ws13;
+    p.ab_r = sv.ab_r;
+    p.ab_s = sv.ab_s;
+    p.h_r = sv.h_r;
+    p.h_s = sv.h_s;
+    const int64_t hcols = p.I_r > p.I_s ? p.I_r : p.I_s;
+    launch_bwd_f32<OP_RECOMP>(p, hcols, 0, (p.TK + p.T) * hcols, st);
+    return hipGetLastError();
+}
+
 hipError_t launch_expert_ffn_backward(const moe_cfg& c, const FfnBwdArgs& a, void* ws,
-                                      hipStream_t st) {
+                                      hipStream_t st, const void* saved) {
     const int64_t T = c.tokens, TK = T * c.top_k, d = c.hidden, N = c.n_experts;
     const int64_t I = c.inter, Is = c.inter_shared;
     const bool has_shared = Is > 0 && T > 0;
     BwdWs w = carve_bwd(c, ws);
-    BwdParams p{};
+    if (saved) {
+        // a, b and h from the training forward
+        const SavedActs sv = carve_saved(c, (void*)saved);
+        w.ab_r = sv.ab_r;
+        w.ab_s = sv.ab_s;
+        w.h_r = sv.h_r;
+        w.h_s = sv.h_s;
+    }
+    BwdParams p = bwd_params(c);
     p.offsets = a.offsets;
-    p.N = (int)N;
-    p.has_shared = has_shared ? 1 : 0;
-    p.T = has_shared ? T : 0;
-    p.TK = TK;
-    p.d = d;
-    p.I_r = I;
-    p.I_s = has_shared ? Is : 0;
     p.x_perm = a.x_perm;
     p.x = a.x_sh;
     p.dy_perm = a.dy_perm;
@@ -498,7 +551,7 @@ hipError_t launch_expert_ffn_backward(const moe_cfg& c, const FfnBwdArgs& a, voi
     if (c.act_dtype == MOE_BF16) {
         if (TK > 0) {
             const hipError_t e = launch_ffn_bwd_dgrad_bf16(c, a, w.tile_ws, w.ab_r, w.ab_s, w.h_r,
-                                                           w.h_s, w.dab_r, w.dab_s, st);
+                                                           w.h_s, w.dab_r, w.dab_s, !saved, st);
             if (e != hipSuccess) return e;
         }
         // weight gradients: every group, including experts without rows (zeros)
@@ -517,7 +570,7 @@ hipError_t launch_expert_ffn_backward(const moe_cfg& c, const FfnBwdArgs& a, voi
     } else {
         const int64_t rows = TK + p.T;
         const int64_t hcols = imax(I, Ish);
-        launch_bwd_f32<OP_RECOMP>(p, hcols, 0, rows * hcols, st);
+        if (!saved) launch_bwd_f32<OP_RECOMP>(p, hcols, 0, rows * hcols, st);
         launch_bwd_f32<OP_DGRAD_DOWN>(p, hcols, 0, rows * hcols, st);
         launch_bwd_f32<OP_DGRAD_UP>(p, d, 0, rows * d, st);
         launch_bwd_f32<OP_WGRAD_DOWN>(p, I, d * I, N * d * I + (has_shared ? d * Is : 0), st);

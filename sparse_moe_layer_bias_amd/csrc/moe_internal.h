@@ -51,7 +51,20 @@ hipError_t launch_pack_weights(const moe_cfg& c, int which, const void* w, void*
 size_t packed_weight_bytes_fp8(const moe_cfg& c, int which);
 hipError_t launch_pack_weights_fp8(const moe_cfg& c, int which, const void* w, void* out,
                                    hipStream_t st);
-hipError_t launch_expert_ffn(const moe_cfg& c, const FfnArgs& a, void* ws, hipStream_t st);
+// Activations a training forward keeps for the backward (act_dtype):
+// ab [T*k][2I] (a, then b, of each routed row), h [T*k][I], and the same for
+// the shared expert's T rows.
+struct SavedActs {
+    void* ab_r;
+    void* h_r;
+    void* ab_s;
+    void* h_s;
+};
+size_t ffn_saved_bytes(const moe_cfg& c);
+SavedActs carve_saved(const moe_cfg& c, void* saved);
+// saved == nullptr: inference forward; else also store a, b and h there
+hipError_t launch_expert_ffn(const moe_cfg& c, const FfnArgs& a, void* ws, hipStream_t st,
+                             void* saved = nullptr);
 // device tile list of the grouped GEMMs: routed expert g gets ceil(M_g / BM)
 // tiles (group, first row), then the shared expert's ceil(T / BM); counts[0],
 // counts[1] = their numbers; order = routed tiles by row count, largest first
@@ -85,9 +98,14 @@ size_t ffn_backward_workspace_bytes(const moe_cfg& c);
 size_t ffn_bwd_tile_ws_bytes(const moe_cfg& c);
 hipError_t launch_ffn_bwd_dgrad_bf16(const moe_cfg& c, const FfnBwdArgs& a, void* tile_ws,
                                      void* ab_r, void* ab_s, void* h_r, void* h_s, void* dab_r,
-                                     void* dab_s, hipStream_t st);
+                                     void* dab_s, bool recompute, hipStream_t st);
+// saved == nullptr: recompute a, b, h; else read them from a training forward
 hipError_t launch_expert_ffn_backward(const moe_cfg& c, const FfnBwdArgs& a, void* ws,
-                                      hipStream_t st);
+                                      hipStream_t st, const void* saved = nullptr);
+// fp32 layers: a, b and h of every row into `saved` (the training forward)
+hipError_t launch_ffn_save_f32(const moe_cfg& c, const void* x_perm, const void* x_sh,
+                               const int32_t* offsets, const void* w13, const void* ws13,
+                               void* saved, hipStream_t st);
 hipError_t launch_combine_backward(const moe_cfg& c, const void* dout, const void* y_perm,
                                    const float* gate, const int32_t* dst_row, void* dy_perm,
                                    float* dgate, hipStream_t st);

@@ -15,6 +15,7 @@ import torch
 
 from . import (MoeCfg, cfg_from_dict, moe_bias_update, moe_combine, moe_combine_backward,
                moe_expert_ffn, moe_expert_ffn_backward, moe_expert_ffn_backward_workspace_size,
+               moe_expert_ffn_saved_size, moe_expert_ffn_train,
                moe_expert_ffn_workspace_size, moe_input_grad, moe_pack_weights,
                moe_packed_weights_size, moe_permute, moe_permute_workspace_size,
                moe_quantize_weights_fp8, moe_route, moe_route_backward,
@@ -47,7 +48,7 @@ class MoeLayer:
     and every per-step buffer for a batch of T tokens."""
 
     def __init__(self, cfg, w13, w2, ws13=None, ws2=None, T=None, device="cuda",
-                 train=False):
+                 train=False, save_activations=True):
         self.c = dict(cfg)
         if T is not None:
             self.c["T"] = T
@@ -118,6 +119,11 @@ class MoeLayer:
                 self.ws13t = pack_weights(self.cfg, 6, ws13)
                 self.ws2t = pack_weights(self.cfg, 7, ws2)
         self.grads = None
+        # a training forward keeps a, b and h for the backward (else recomputed)
+        self.saved = None
+        if self.train and save_activations:
+            self.saved = torch.empty((moe_expert_ffn_saved_size(self.cfg),), dtype=torch.uint8,
+                                     device=dev)
 
     # the five calls -------------------------------------------------------
     def route(self, x, centroids, bias, stream=None):
@@ -129,6 +135,12 @@ class MoeLayer:
                     self.x_perm, self.x_perm_s, self.x_q, self.x_s, self.workspace, stream)
 
     def expert_ffn(self, x, stream=None):
+        if self.saved is not None:
+            shared = self.y_shared is not None
+            moe_expert_ffn_train(self.cfg, self.x_perm, self.offsets, self.w13, self.w2,
+                                 self.y_perm, x if shared else None, self.ws13, self.ws2,
+                                 self.y_shared, self.saved, self.workspace, stream)
+            return
         shared_in = self.x_q if self.fp8 else x
         moe_expert_ffn(self.cfg, self.x_perm, self.x_perm_s, self.offsets, self.w13, self.w13_s,
                        self.w2, self.w2_s, self.y_perm, shared_in if self.y_shared is not None
@@ -186,7 +198,7 @@ class MoeLayer:
                                 self.w2t, g["dy_perm"], x if shared else None, self.ws13,
                                 self.ws13t, self.ws2t, dout if shared else None, g["dx_perm"],
                                 g["dx_shared"], g["dw13"], g["dw2"], g["dws13"], g["dws2"],
-                                g["workspace"], stream)
+                                self.saved, g["workspace"], stream)
 
     def backward(self, dout, x, centroids, residual=True, stream=None, events=None):
         """Gradients of the last forward step for the upstream gradient ``dout``

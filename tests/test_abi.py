@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
             "moe_input_grad"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert moe.moe_abi_version() == 3
+    assert moe.moe_abi_version() == 4
 
 
 @host_only
@@ -169,13 +169,14 @@ def test_bias_update_and_quantize_validation():
 
 def _ffn_bwd(cfg, ws_bytes=1 << 40, **over):
     names = ("x_perm", "offsets", "w13", "w13t", "w2t", "dy_perm", "x_sh", "ws13", "ws13t",
-             "ws2t", "dy_shared", "dx_perm", "dx_shared", "dw13", "dw2", "dws13", "dws2",
-             "workspace")
+             "ws2t", "dy_shared", "dx_perm", "dx_shared", "dw13", "dw2", "dws13", "dws2")
     args = {n: FAKE for n in names}
     args.update(over)
     P = ctypes.c_void_p
+    saved = over.get("saved", 0)
     return moe.lib().moe_expert_ffn_backward(
-        ctypes.byref(cfg), *(P(args[n]) if args[n] else None for n in names), ws_bytes, None)
+        ctypes.byref(cfg), *(P(args[n]) if args[n] else None for n in names),
+        P(saved) if saved else None, over.get("saved_bytes", 0), P(FAKE), ws_bytes, None)
 
 
 @host_only
@@ -193,6 +194,24 @@ def test_expert_ffn_backward_validation():
     assert need >= 2 * (64 * 2 * 2 * 128 * 2 + 64 * 128) + 2 * (64 * 2 * 128 * 2 + 64 * 128)
     assert _ffn_bwd(c, ws_bytes=need - 1) == moe.MOE_ERR_WORKSPACE
     assert moe.lib().moe_last_error().decode().startswith("moe_expert_ffn_backward")
+    # saved activations: too small is rejected; with them, w13 may be NULL
+    sv = moe.moe_expert_ffn_saved_size(c)
+    assert sv == (64 * 2 * 2 * 128 + 64 * 2 * 128) * 2 + (64 * 2 * 128 + 64 * 128) * 2
+    assert _ffn_bwd(c, saved=FAKE, saved_bytes=sv - 1) == moe.MOE_ERR_WORKSPACE
+    assert _ffn_bwd(c, w13=0) == moe.MOE_ERR_ARG
+
+
+@host_only
+def test_training_forward_validation():
+    L = moe.lib()
+    P = ctypes.c_void_p
+    c = _cfg(dtype="bf16", d=256, I=128, Is=128)
+    sv = moe.moe_expert_ffn_saved_size(c)
+    ws = moe.moe_expert_ffn_workspace_size(c)
+    call = lambda cfg, saved_bytes: L.moe_expert_ffn_train(
+        ctypes.byref(cfg), *([P(FAKE)] * 10), saved_bytes, P(FAKE), ws, None)
+    assert call(c, sv - 1) == moe.MOE_ERR_WORKSPACE
+    assert call(_cfg(dtype="bf16", fp8=True, d=256, I=128, Is=128), sv) == moe.MOE_ERR_UNSUPPORTED
 
 
 @host_only

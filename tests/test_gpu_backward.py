@@ -30,14 +30,16 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def _run(name, orc, seed=0, residual=True, **over):
+def _run(name, orc, seed=0, residual=True, save=True, **over):
     cfg = dict(moe_inputs.CONFIGS[name])
     T = over.pop("T", None)
     cfg.update(over)
     c, inp, dev = small_layer_inputs(cfg, seed, T)
-    log("backward case", name, "T=%d" % c["T"], over, "seed", seed, "residual", residual)
+    log("backward case", name, "T=%d" % c["T"], over, "seed", seed, "residual", residual,
+        "saved activations" if save else "recompute")
     dout = moe_inputs.make_upstream_grad(c, seed, "cpu")
-    layer = MoeLayer(c, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"], train=True)
+    layer = MoeLayer(c, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"], train=True,
+                     save_activations=save)
     layer.forward(dev["x"], dev["centroids"], dev["bias"].clone(), residual=residual)
     g = layer.backward(dout.cuda(), dev["x"], dev["centroids"], residual=residual)
     torch.cuda.synchronize()
@@ -79,6 +81,36 @@ def test_backward_parity_small(orc, name, over):
     c, layer, g, ref = _run(name, orc, **dict(over))
     _cmp(g, ref, ("dy_perm", "dgate", "dz", "dcentroids", "dx_perm", "dx_shared", "dw13", "dw2",
                   "dws13", "dws2", "dx"), c["dtype"])
+
+
+RECOMPUTE_CASES = [
+    ("tiny_fp32", {}),
+    ("mid_bf16", dict(T=77)),
+    ("mid_bf16", dict(T=700, d=384, N=2, k=1, I=256, Is=128)),
+    ("mid_bf16", dict(T=64, d=256, I=256, Is=128)),
+]
+
+
+@pytest.mark.parametrize("name,over", RECOMPUTE_CASES)
+def test_backward_parity_recompute(orc, name, over):
+    """Without saved activations the backward recomputes a, b and h."""
+    c, layer, g, ref = _run(name, orc, save=False, **dict(over))
+    _cmp(g, ref, ("dx_perm", "dx_shared", "dw13", "dw2", "dws13", "dws2", "dx"), c["dtype"])
+
+
+@pytest.mark.parametrize("name,T", [("tiny_fp32", 200), ("mid_bf16", 300)])
+def test_training_forward_is_bitwise_the_inference_forward(name, T):
+    cfg = dict(moe_inputs.CONFIGS[name])
+    c, inp, dev = small_layer_inputs(cfg, 9, T)
+    outs = []
+    for train in (False, True):
+        layer = MoeLayer(c, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"], train=train)
+        o = layer.forward(dev["x"], dev["centroids"], dev["bias"].clone()).clone()
+        torch.cuda.synchronize()
+        outs.append((moe_inputs.to_host(o), moe_inputs.to_host(layer.y_perm),
+                     moe_inputs.to_host(layer.y_shared)))
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
 def test_backward_without_residual(orc):
