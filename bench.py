@@ -12,9 +12,10 @@ run on, against the roofline (HBM or MFMA) that bounds its algorithmic work; `cp
 workload on this host.
 
 --backward measures the layer's backward instead (bf16 / fp32 workloads): a
-step is the four backward calls -- combine backward, expert FFN backward
-(recompute, two dgrad and two wgrad GEMMs), gate/centroid backward, input
-gradient -- on the state of one forward step, reported as its own metric.
+step is the four backward calls -- combine backward, expert FFN backward (two
+dgrad and two wgrad GEMMs, reading the a, b, h the training forward kept),
+gate/centroid backward, input gradient -- on the state of one training forward
+step, reported as its own metric.
 """
 import argparse
 import json
@@ -61,23 +62,27 @@ def ffn_bytes(c):
     return w + acts
 
 
-def ffn_bwd_flops(c):
-    """recompute a, b (4 M d I), dgrad down (2 M d I), dgrad up (4 M d I),
-    wgrad down (2 M d I), wgrad up (4 M d I) for M = T*k routed rows, and the
-    same for the shared expert over T rows"""
+def ffn_bwd_flops(c, recompute=False):
+    """dgrad down (2 M d I), dgrad up (4 M d I), wgrad down (2 M d I), wgrad up
+    (4 M d I) for M = T*k routed rows, the same for the shared expert over T
+    rows, and with recompute also a, b (4 M d I)"""
     T, k, d, I, Is = c["T"], c["k"], c["d"], c["I"], c["Is"]
-    return 16.0 * T * k * d * I + 16.0 * T * d * Is
+    f = 16.0 if recompute else 12.0
+    return f * T * k * d * I + f * T * d * Is
 
 
-def ffn_bwd_bytes(c):
+def ffn_bwd_bytes(c, recompute=False):
     """Algorithmic HBM bytes of one moe_expert_ffn_backward call (bf16), each
-    GEMM reading its operands and writing its result once: weights W13 (the
-    recompute), W2^T and W13^T (the dgrads); x_perm, dY, a/b, h, da/db, dX and
-    the weight gradients as each GEMM reads or writes them."""
+    GEMM reading its operands and writing its result once: weights W2^T and
+    W13^T (the dgrads), and W13 with recompute; x_perm, dY, a/b, h, da/db, dX
+    and the weight gradients as each GEMM reads or writes them."""
     T, k, d, I, Is, N = c["T"], c["k"], c["d"], c["I"], c["Is"], c["N"]
     def one(M, I, n):
-        w = 2.0 * n * (2 * I * d + d * I + 2 * I * d)            # W13, W2^T, W13^T read
-        rec = 2.0 * (M * d + M * 2 * I + M * I)                  # x in; a, b and h out
+        w = 2.0 * n * (d * I + 2 * I * d)                        # W2^T, W13^T read
+        rec = 0.0
+        if recompute:
+            w += 2.0 * n * 2 * I * d                             # W13 read
+            rec = 2.0 * (M * d + M * 2 * I + M * I)              # x in; a, b and h out
         dgd = 2.0 * (M * d + M * 2 * I + M * 2 * I)              # dY, a/b in; da/db out
         dgu = 2.0 * (M * 2 * I + M * d)                          # da/db in; dX out
         wgd = 2.0 * (M * d + M * I) + 2.0 * n * d * I            # dY, h in; dW2 out
@@ -180,9 +185,9 @@ def traffic_summary(fetch_csv, write_csv, workload, backward=False):
     lines = []
     # the kernels of one call; each averaged over its last 3 dispatches, the
     # 3 measured calls (the backward's setup also runs forward kernels)
-    if backward:
+    if backward:  # with the training forward's saved activations: no recompute (mode 2)
         ffn = [k for k in fetch if "wgrad" in k or "ffn_tile_map" in k or
-               any("ffn_gemm_bf16_kernel<%d," % m in k for m in (1, 2, 3))]
+               any("ffn_gemm_bf16_kernel<%d," % m in k for m in (1, 3))]
     else:
         ffn = [k for k in fetch if "ffn_" in k]
     total = 0.0
@@ -468,8 +473,8 @@ def run_backward(args, cfg, dev, log):
     else:
         roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12,
                 "unit": "TFLOP/s", "frac": achieved / peak}
-    roof.update({"kernel": "expert FFN backward GEMMs (recompute, dgrad down+SwiGLU', "
-                           "dgrad up, wgrad down, wgrad up)",
+    roof.update({"kernel": "expert FFN backward GEMMs (dgrad down+SwiGLU', dgrad up, wgrad "
+                           "down, wgrad up; a, b, h saved by the training forward)",
                  "traffic": recorded_traffic(args.workload, backward=True),
                  "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
                  "mfma_tflops": achieved / 1e12, "mfma_frac": achieved / peak})
