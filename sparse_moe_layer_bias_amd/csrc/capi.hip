@@ -412,6 +412,14 @@ int moe_expert_ffn_backward(const moe_cfg* cfg, const void* x_perm, const int32_
             REQ_PTR(dws2);
         }
     }
+    if (cfg->act_dtype == MOE_BF16) {
+        // weight-gradient copies address an expert's rows with 32-bit byte offsets
+        const int64_t w = cfg->hidden > 2 * cfg->inter ? cfg->hidden : 2 * cfg->inter;
+        const int64_t ws = 2 * cfg->inter_shared > w ? 2 * cfg->inter_shared : w;
+        if ((cfg->tokens + 32) * ws * 2 >= ((int64_t)1 << 32))
+            return fail(MOE_ERR_UNSUPPORTED, "%s: tokens * width exceeds the 32-bit row offsets",
+                        fn);
+    }
     if (cfg->act_dtype == MOE_F32) {
         // one thread per output element
         const int64_t T = cfg->tokens, I = cfg->inter, Is = cfg->inter_shared, d = cfg->hidden;

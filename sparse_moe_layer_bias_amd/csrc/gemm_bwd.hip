@@ -16,15 +16,13 @@
 // bf16: the first three run on the forward's streaming kernel (gemm.hip, modes
 // 2, 3 and 1) with the weights packed for it -- W13 as in the forward, W13 and
 // W2 transposed for the dgrads.  The weight gradients contract over token rows,
-// so both operands are read against their storage order; they run here: one
-// 256 x 256 tile of dW per workgroup, 8 wavefronts of 64 x 128 on
+// so both operands are stored against the MFMA's operand order; they run
+// here: one 256 x 256 tile of dW per workgroup, 8 wavefronts of 64 x 128 on
 // v_mfma_f32_16x16x32_bf16 (a tile contracts over only ~T*k/N rows, so a big
-// tile gets the most MFMA work out of each round trip to memory).  Each thread
-// loads 4 consecutive rows x 8 consecutive columns (4 x 16 bytes) and
-// transposes them in registers, so LDS holds [output row][64 contraction
-// elements] with the forward's 16-byte chunk swizzle and the MFMA loop reads
-// whole chunks.  Two LDS stages; the global loads of stage k+1 are in flight
-// while stage k is multiplied.
+// tile gets the most MFMA work out of each round trip to memory).  The rows
+// are copied global -> LDS as they are stored (4 stages of 32 rows, copies
+// 3 stages ahead, no staging registers), and gfx950's transposing LDS load
+// turns them into MFMA operands.
 // fp32: plain VALU kernels for all five (small layers).
 #include "gemm_common.h"
 
@@ -153,17 +151,26 @@ __device__ __forceinline__ bool wgrad_unit(const BwdParams& p, int64_t L, int& g
 
 // ---------------------------------------------------------------- bf16 MFMA
 
-constexpr int BT = 256;   // dW tile rows and columns
-
-// 16-byte chunk slot of logical chunk c in LDS row r (64 contraction elements,
-// 128 bytes): the forward's XOR with (r >> 1) & 7 keeps the 16 consecutive
-// rows an MFMA operand read touches on distinct banks; the extra (r >> 4) & 7
-// (constant over such 16 rows) also spreads the transposing stores, whose
-// lanes write rows 8 apart.
-__device__ __forceinline__ int wg_chunk(int r, int c) { return c ^ ((r >> 1) & 7) ^ ((r >> 4) & 7); }
-constexpr int BBK = 64;   // contraction elements (token rows) per LDS stage
-constexpr int BW_WAVES = 8;  // 4 x 2 wavefronts of 64 x 128
+constexpr int BT = 256;       // dW tile rows and columns
+constexpr int BBK = 32;       // contraction rows (token rows) per LDS stage
+constexpr int NSTG = 4;       // LDS stages: loads run 3 stages ahead
+constexpr int BW_WAVES = 8;   // 4 x 2 wavefronts of 64 x 128
 constexpr int BW_THREADS = 64 * BW_WAVES;
+constexpr int WG_DMA = 4;     // global -> LDS copies per wavefront per stage
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// LDS holds each operand stage in its memory order, [32 contraction rows][256
+// columns], 512-byte rows of 16 segments of 32 bytes; segment s of row k is
+// stored at slot s ^ wg_seg(k).  The MFMA operands are read with the
+// transposing LDS load (ds_read_b64_tr_b16): a group of 16 lanes names 16
+// pieces of 8 bytes, pieces 4e..4e+3 form row e of a 4 x 16 block, and lane i
+// receives element i of each of the 4 rows -- here one column and 4
+// consecutive contraction rows.  One such read touches rows 8g + e (+4) for
+// g, e < 4 in a single segment; wg_seg gives those 16 rows 8 distinct bank
+// groups (2 passes for 512 bytes, the minimum).
+__device__ __forceinline__ int wg_seg(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
 
 template <int OP>
 __global__ void __launch_bounds__(BW_THREADS, 1) wgrad_bf16_kernel(BwdParams p) {
@@ -194,118 +201,88 @@ __global__ void __launch_bounds__(BW_THREADS, 1) wgrad_bf16_kernel(BwdParams p) 
         Cp = v.dW13; ldc = d;
     }
 
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[2][2][BT * BBK];
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[NSTG][2][BBK * BT];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 3, wn = wave >> 2;
-    const int l16 = lane & 15, gq = lane >> 4;
     const int nk = (int)((K + BBK - 1) / BBK);
 
-    // Loads: thread (rq = t%32, kq = t/32) fetches, for A and for B,
-    // contraction rows 4kq..4kq+3 of tile rows (= columns in memory)
-    // 8rq..8rq+7, 16 bytes per contraction row: 8 loads per stage.
-    // Rows past the tile or the contraction are read from a clamped address
-    // (always inside the operand) and zeroed afterwards: a load that is
-    // skipped by a condition lets the compiler turn it into a flat load from
-    // a select of pointers.
-    const int rq = tid & 31, kq = tid >> 5;
-    const bool aok = 8 * rq < R - r0, bok = 8 * rq < C - c0;
-    const int64_t acol = aok ? 8 * rq : 0, bcol = bok ? 8 * rq : 0;
-    uint4 r[8];
-    auto load = [&](int kt) {
+    // Copies: buffer descriptors over the operand rows 0..K-1 of the tile's
+    // columns (range-checked: rows past K, and columns past the operand in its
+    // last row, read as zeros).  Copy q (0..15) of a stage covers rows 2q,
+    // 2q+1; wavefront w issues q = w and w + 8 for A and for B.  Lane l
+    // fills LDS bytes 16l..16l+15 of the two rows: row 2q + l/32, slot
+    // (l%32)/2, half l%2, which holds logical segment slot ^ wg_seg(row).
+    const int64_t acols = R - r0 < BT ? R - r0 : BT, bcols = C - c0 < BT ? C - c0 : BT;
+    const i32x4_t ra = make_rsrc(a_base, K > 0 ? ((K - 1) * a_ld + acols) * 2 : 0);
+    const i32x4_t rb = make_rsrc(b_base, K > 0 ? ((K - 1) * b_ld + bcols) * 2 : 0);
+    auto issue = [&](int kt, int s) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t kr = (int64_t)kt * BBK + 4 * kq + j;
-            const bool kok = kr < K;
-            const int64_t krc = kok ? kr : K - 1;
-            const uint4 va = *(const uint4*)(a_base + krc * a_ld + acol);
-            const uint4 vb = *(const uint4*)(b_base + krc * b_ld + bcol);
-            const bool ka = aok && kok, kb = bok && kok;
-            r[j] = make_uint4(ka ? va.x : 0u, ka ? va.y : 0u, ka ? va.z : 0u, ka ? va.w : 0u);
-            r[4 + j] = make_uint4(kb ? vb.x : 0u, kb ? vb.y : 0u, kb ? vb.z : 0u, kb ? vb.w : 0u);
+        for (int h = 0; h < 2; ++h) {
+            const int q = wave + 8 * h;
+            const int row = 2 * q + (lane >> 5);
+            const int col = (((lane & 31) >> 1) ^ wg_seg(row)) * 16 + (lane & 1) * 8;
+            const int64_t grow = (int64_t)kt * BBK + row;
+            dma_to_lds<16>(ra, smem[s][0] + 2 * q * BT, (uint32_t)((grow * a_ld + col) * 2), 0);
+            dma_to_lds<16>(rb, smem[s][1] + 2 * q * BT, (uint32_t)((grow * b_ld + col) * 2), 0);
         }
-    };
-    // transpose into LDS: tile row 8rq+i gets the 4 contraction values
-    // (8 bytes) at chunk kq/2, half kq%2
-    auto store1 = [&](uint16_t* sm, const uint4* q) {
-        const uint32_t w0[4] = {q[0].x, q[0].y, q[0].z, q[0].w};
-        const uint32_t w1[4] = {q[1].x, q[1].y, q[1].z, q[1].w};
-        const uint32_t w2[4] = {q[2].x, q[2].y, q[2].z, q[2].w};
-        const uint32_t w3[4] = {q[3].x, q[3].y, q[3].z, q[3].w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int row = 8 * rq + i;
-            const int wi = i >> 1;
-            uint2 o;
-            if ((i & 1) == 0) {
-                o.x = (w0[wi] & 0xffffu) | (w1[wi] << 16);
-                o.y = (w2[wi] & 0xffffu) | (w3[wi] << 16);
-            } else {
-                o.x = (w0[wi] >> 16) | (w1[wi] & 0xffff0000u);
-                o.y = (w2[wi] >> 16) | (w3[wi] & 0xffff0000u);
-            }
-            *(uint2*)(sm + row * BBK + wg_chunk(row, kq >> 1) * 8 + (kq & 1) * 4) = o;
-        }
-    };
-    auto store = [&](int s) {
-        store1(smem[s][0], r);
-        store1(smem[s][1], r + 4);
     };
 
-    // MFMA: D rows = B tile rows (output columns), D columns = A tile rows
-    // (output rows); wave (wm, wn) owns output rows wm*64 + 16i + 0..15 (i < 4)
-    // and columns wn*128 + 16j + 0..15 (j < 8); lane holds
+    // MFMA: D rows = B columns (output columns), D columns = A columns (output
+    // rows); wave (wm, wn) owns output rows wm*64 + 16i + 0..15 (i < 4) and
+    // columns wn*128 + 16j + 0..15 (j < 8); lane holds
     // C[16-row block + l16][16-column block + 4 gq + 0..3]
+    const int l16 = lane & 15, gq = lane >> 4;
     f32x4_t acc[8][4];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[j][i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // fragment of columns cb..cb+15: lane (gq, l16) names piece l16 of rows
+    // 8gq + l16/4 (+4): columns cb + 4 (l16 % 4) .. +3
+    const int fk = 8 * gq + (l16 >> 2), fc = 4 * (l16 & 3);
+    auto frag = [&](const uint16_t* buf, int cb) {
+        const int s0 = ((cb >> 4) ^ wg_seg(fk)) * 16 + fc;
+        const int s1 = ((cb >> 4) ^ wg_seg(fk + 4)) * 16 + fc;
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(to_lds(buf + fk * BT + s0)));
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(to_lds(buf + (fk + 4) * BT + s1)));
+        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
     auto compute = [&](int st) {
-        const uint16_t* As = smem[st][0];
-        const uint16_t* Bs = smem[st][1];
+        bf16x8_t af[4];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            bf16x8_t af[4];
+        for (int i = 0; i < 4; ++i) af[i] = frag(smem[st][0], wm * 64 + i * 16);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = wm * 64 + i * 16 + l16;
-                af[i] = __builtin_bit_cast(
-                    bf16x8_t, *(const uint4*)(As + row * BBK + wg_chunk(row, 4 * s + gq) * 8));
-            }
+        for (int j = 0; j < 8; ++j) {
+            const bf16x8_t bf = frag(smem[st][1], wn * 128 + j * 16);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int row = wn * 128 + j * 16 + l16;
-                const bf16x8_t bf = __builtin_bit_cast(
-                    bf16x8_t, *(const uint4*)(Bs + row * BBK + wg_chunk(row, 4 * s + gq) * 8));
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf, af[i], acc[j][i], 0, 0, 0);
-            }
+            for (int i = 0; i < 4; ++i)
+                acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf, af[i], acc[j][i], 0, 0, 0);
         }
     };
 
-    // two LDS stages; the global loads of stage kt+1 are in flight while
-    // stage kt is multiplied
-    if (nk > 0) {
-        load(0);
-        store(0);
-    }
-    __syncthreads();
+    // Pipeline: stage kt waits for its copies (each wavefront's later stages
+    // may stay in flight), a barrier makes it visible to all and frees stage
+    // kt-1, whose buffer then takes stage kt+NSTG-1.  lds_barrier, not
+    // __syncthreads: the copies in flight must not be waited for.
+#pragma unroll
+    for (int s = 0; s < NSTG - 1; ++s)
+        if (s < nk) issue(s, s);
     for (int kt = 0; kt < nk; ++kt) {
-        if (kt + 1 < nk) load(kt + 1);
-        compute(kt & 1);
-        if (kt + 1 < nk) store((kt + 1) & 1);
-        __syncthreads();
+        const int after = nk - 1 - kt < NSTG - 2 ? nk - 1 - kt : NSTG - 2;
+        vm_wait_n(after * WG_DMA);
+        lds_barrier();
+        if (kt + NSTG - 1 < nk) issue(kt + NSTG - 1, (kt + NSTG - 1) % NSTG);
+        compute(kt % NSTG);
     }
+    lds_barrier();  // every wave is done with the stage buffers
 
-    // Epilogue through LDS (the stage buffers are free after the loop's last
-    // barrier): the 256 x 256 bf16 tile, 16-byte chunk c of row r at slot
-    // c ^ (r & 15), then whole 512-byte rows to global memory, 16 bytes per
-    // thread, as non-temporal stores (dW is written once and not read back
-    // here; keeping it out of L2 leaves room for the operands; measured
-    // faster).  A group without rows (K = 0) writes zeros.
+    // Epilogue through LDS: the 256 x 256 bf16 tile, 16-byte chunk c of row r
+    // at slot c ^ (r & 15), then whole 512-byte rows to global memory, 16
+    // bytes per thread, as non-temporal stores (dW is written once and not
+    // read back here; keeping it out of L2 leaves room for the operands;
+    // measured faster).  A group without rows (K = 0) writes zeros.
     uint16_t* ot = &smem[0][0][0];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
