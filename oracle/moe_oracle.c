@@ -42,7 +42,17 @@
  *  - FP8 is OCP E4M3FN (largest finite 448); scale = amax/448 as an fp32
  *    divide; x/scale is an fp32 divide, clamped to +-448, then rounded to the
  *    nearest E4M3 value, ties to even; an all-zero tile has scale 0 and all
- *    codes 0.
+ *    codes 0;
+ *  - FP8 backward ("E4M3 for all tensors" read as: every operand of every
+ *    expert GEMM of the backward is E4M3, activations and gradients in tiles
+ *    of 128 along that GEMM's contraction, weights in their 128x128 blocks):
+ *    dh = dY W2 and dX = [da db] [W1; W3] contract over features, so dY and
+ *    [da db] are quantised 1x128 per row; dW2 = dY^T h and dW13 = [da db]^T X
+ *    contract over the expert's rows, so dY, h, [da db] and X are quantised
+ *    in 128x1 tiles along the rows (128 consecutive rows of one expert from
+ *    its first row, the last tile partial), each from its bf16 value; a, b
+ *    come from the FP8 forward (fp32) and are kept in bf16 with
+ *    h = silu(a) b; dh, da, db and every output are rounded to bf16.
  *
  * Build: gcc -O2 -fno-fast-math -ffp-contract=off -fopenmp -shared -fPIC.
  */
@@ -687,4 +697,156 @@ void orc_input_grad(int64_t T, int64_t d, int64_t k, int dtype, const void* dout
             }
             store_elem_from_double(dx, dtype, t * d + c, acc);
         }
+}
+
+/* ---------------------------------------------------------------------- */
+/* FP8 backward of one SwiGLU expert   [P4k] applied to the backward GEMMs */
+/* ---------------------------------------------------------------------- */
+
+/* token-direction tiles: x [M, C] -> codes q [M, C] and scales
+ * [ceil(M/128), C]; tile (u, c) is column c of rows 128u .. min(M, 128u+128)-1,
+ * quantised like an activation tile (scale = amax/448, codes of x/scale) */
+void orc_quant_cols_fp8(int64_t M, int64_t C, int dtype, const void* x, uint8_t* q,
+                        float* scales) {
+    int64_t nb = (M + 127) / 128;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t u = 0; u < nb; ++u)
+        for (int64_t c = 0; c < C; ++c) {
+            int64_t r1 = (u + 1) * 128 < M ? (u + 1) * 128 : M;
+            float amax = 0.0f;
+            for (int64_t r = u * 128; r < r1; ++r) {
+                float a = fabsf(load_elem(x, dtype, r * C + c));
+                if (a > amax) amax = a;
+            }
+            float sc = quant_scale(amax);
+            scales[u * C + c] = sc;
+            for (int64_t r = u * 128; r < r1; ++r)
+                q[r * C + c] = quant_one(load_elem(x, dtype, r * C + c), sc);
+        }
+}
+
+/* Backward of the FP8 SwiGLU expert over its M rows:
+ *  Aq [M,d] codes, As [M,d/128]   the forward's activation tiles (to recompute a, b)
+ *  A  [M,d] bf16                  the same rows before quantisation (for dW13)
+ *  w13q [2I,d], w13s [2I/128,d/128], w2q [d,I], w2s [d/128,I/128]  forward blocks
+ *  dY [M,d] bf16                  gradient of the expert output
+ * out dA [M,d], dw13 [2I,d], dw2 [d,I], all bf16 (gradients of the unquantised
+ * weights: the block quantisation passes the gradient through).
+ *   a, b  = the forward's promoted sums rounded to fp32; kept as bf16 a~, b~;
+ *           h~ = bf16(silu(a) b)
+ *   dh    = bf16( dY W2 )            dY in 1x128 row tiles, W2 in its blocks
+ *   da    = bf16( dh b~ s (1 + a~ (1 - s)) ), db = bf16( dh a~ s ),  s = sig(a~)
+ *   dA    = bf16( [da db] [W1; W3] ) [da db] in 1x128 row tiles
+ *   dw2   = bf16( dY^T h~ )          both in 128x1 row-direction tiles
+ *   dw13  = bf16( [da db]^T A )      both in 128x1 row-direction tiles
+ * Each contraction: sum over its 128-blocks of (product of the two scales)
+ * times the block's exact sum of decoded code products, in double. */
+void orc_swiglu_ffn_backward_fp8(int64_t M, int64_t d, int64_t I, const uint8_t* Aq,
+                                 const float* As, const uint16_t* A, const uint8_t* w13q,
+                                 const float* w13s, const uint8_t* w2q, const float* w2s,
+                                 const uint16_t* dY, uint16_t* dA, uint16_t* dw13,
+                                 uint16_t* dw2) {
+    double lut[256];
+    for (int c = 0; c < 256; ++c) {
+        float v = orc_e4m3_decode((uint8_t)c);
+        lut[c] = isnan(v) ? 0.0 : (double)v;
+    }
+    const int64_t kd = d / 128, ki = I / 128, k2 = 2 * I / 128, nb = (M + 127) / 128;
+    const size_t MI = (size_t)(M * I + 1), M2I = (size_t)(2 * M * I + 1);
+    uint16_t* h = (uint16_t*)malloc(MI * 2);
+    double* ar = (double*)malloc(MI * sizeof(double));
+    double* br = (double*)malloc(MI * sizeof(double));
+    uint16_t* dab = (uint16_t*)malloc(M2I * 2);
+    /* recompute a, b as the FP8 forward does */
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < I; ++n) {
+            double sa = 0.0, sb = 0.0;
+            for (int64_t kb = 0; kb < kd; ++kb) {
+                double pa = block_dot(Aq + m * d + kb * 128, w13q + n * d + kb * 128, lut);
+                double pb = block_dot(Aq + m * d + kb * 128, w13q + (I + n) * d + kb * 128, lut);
+                double xs = (double)As[m * kd + kb];
+                sa += xs * (double)w13s[(n / 128) * kd + kb] * pa;
+                sb += xs * (double)w13s[((I + n) / 128) * kd + kb] * pb;
+            }
+            double a = (double)(float)sa, b = (double)(float)sb;
+            h[m * I + n] = double_to_bf16_bits(a / (1.0 + exp(-a)) * b);
+            ar[m * I + n] = round_dtype(ORC_BF16, a);
+            br[m * I + n] = round_dtype(ORC_BF16, b);
+        }
+    /* dh = dY W2 with dY in row tiles; then da, db */
+    uint8_t* gq = (uint8_t*)malloc((size_t)(M * d + 1));
+    float* gs = (float*)malloc((size_t)(M * kd + 1) * sizeof(float));
+    orc_quant_act_fp8(M, d, ORC_BF16, dY, gq, gs);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < I; ++n) {
+            double acc = 0.0;
+            for (int64_t kb = 0; kb < kd; ++kb) {
+                double p = 0.0;
+                for (int64_t c = kb * 128; c < kb * 128 + 128; ++c)
+                    p += lut[gq[m * d + c]] * lut[w2q[c * I + n]];
+                acc += (double)gs[m * kd + kb] * (double)w2s[kb * ki + n / 128] * p;
+            }
+            const double dh = round_dtype(ORC_BF16, acc);
+            const double a = ar[m * I + n], b = br[m * I + n], sg = sigmoid_d(a);
+            dab[m * 2 * I + n] = double_to_bf16_bits(dh * b * sg * (1.0 + a * (1.0 - sg)));
+            dab[m * 2 * I + I + n] = double_to_bf16_bits(dh * a * sg);
+        }
+    /* dA = [da db] [W1; W3] with [da db] in row tiles */
+    uint8_t* tq = (uint8_t*)malloc(M2I);
+    float* ts = (float*)malloc((size_t)(M * k2 + 1) * sizeof(float));
+    orc_quant_act_fp8(M, 2 * I, ORC_BF16, dab, tq, ts);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (int64_t kb = 0; kb < k2; ++kb) {
+                double p = 0.0;
+                for (int64_t n = kb * 128; n < kb * 128 + 128; ++n)
+                    p += lut[tq[m * 2 * I + n]] * lut[w13q[n * d + c]];
+                acc += (double)ts[m * k2 + kb] * (double)w13s[kb * kd + c / 128] * p;
+            }
+            dA[m * d + c] = double_to_bf16_bits(acc);
+        }
+    /* weight gradients from row-direction tiles */
+    uint8_t* cg = (uint8_t*)malloc((size_t)(M * d + 1));
+    float* cgs = (float*)malloc((size_t)(nb * d + 1) * sizeof(float));
+    uint8_t* ch = (uint8_t*)malloc(MI);
+    float* chs = (float*)malloc((size_t)(nb * I + 1) * sizeof(float));
+    uint8_t* ct = (uint8_t*)malloc(M2I);
+    float* cts = (float*)malloc((size_t)(nb * 2 * I + 1) * sizeof(float));
+    uint8_t* cx = (uint8_t*)malloc((size_t)(M * d + 1));
+    float* cxs = (float*)malloc((size_t)(nb * d + 1) * sizeof(float));
+    orc_quant_cols_fp8(M, d, ORC_BF16, dY, cg, cgs);
+    orc_quant_cols_fp8(M, I, ORC_BF16, h, ch, chs);
+    orc_quant_cols_fp8(M, 2 * I, ORC_BF16, dab, ct, cts);
+    orc_quant_cols_fp8(M, d, ORC_BF16, A, cx, cxs);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t c = 0; c < d; ++c)
+        for (int64_t n = 0; n < I; ++n) {
+            double acc = 0.0;
+            for (int64_t u = 0; u < nb; ++u) {
+                int64_t r1 = (u + 1) * 128 < M ? (u + 1) * 128 : M;
+                double p = 0.0;
+                for (int64_t m = u * 128; m < r1; ++m) p += lut[cg[m * d + c]] * lut[ch[m * I + n]];
+                acc += (double)cgs[u * d + c] * (double)chs[u * I + n] * p;
+            }
+            dw2[c * I + n] = double_to_bf16_bits(acc);
+        }
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t n = 0; n < 2 * I; ++n)
+        for (int64_t c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (int64_t u = 0; u < nb; ++u) {
+                int64_t r1 = (u + 1) * 128 < M ? (u + 1) * 128 : M;
+                double p = 0.0;
+                for (int64_t m = u * 128; m < r1; ++m)
+                    p += lut[ct[m * 2 * I + n]] * lut[cx[m * d + c]];
+                acc += (double)cts[u * 2 * I + n] * (double)cxs[u * d + c] * p;
+            }
+            dw13[n * d + c] = double_to_bf16_bits(acc);
+        }
+    free(h); free(ar); free(br); free(dab); free(gq); free(gs); free(tq); free(ts);
+    free(cg); free(cgs); free(ch); free(chs); free(ct); free(cts); free(cx); free(cxs);
 }

@@ -70,6 +70,8 @@ def _declare(L):
         "orc_route_backward": [I64, I64, I64, P, P, P, P],
         "orc_centroid_grad": [I64, I64, I64, I64, I, P, P, P, P],
         "orc_input_grad": [I64, I64, I64, I, P, P, P, P, P, P, P, P],
+        "orc_quant_cols_fp8": [I64, I64, I, P, P, P],
+        "orc_swiglu_ffn_backward_fp8": [I64, I64, I64] + [P] * 11,
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -243,6 +245,17 @@ def quant_weight_fp8(w):
     return q, s
 
 
+def quant_cols_fp8(x):
+    """128x1 tiles down the rows (blocks of 128 rows from row 0, the last one
+    partial) -> codes [rows, cols], scales [ceil(rows/128), cols]."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty(((rows + 127) // 128, cols), np.float32)
+    lib().orc_quant_cols_fp8(rows, cols, dtype_code(x), _p(x), _p(q), _p(s))
+    return q, s
+
+
 def swiglu_ffn_fp8(Aq, As, w13q, w13s, w2q, w2s):
     Aq = _c(Aq, np.uint8)
     As = _c(As, np.float32)
@@ -379,6 +392,29 @@ def swiglu_ffn_backward(A, w13, w2, dY):
     return dA, dw13, dw2
 
 
+def swiglu_ffn_backward_fp8(Aq, As, A, w13q, w13s, w2q, w2s, dY):
+    """One FP8 expert's backward: (dA [M,d], dw13 [2I,d], dw2 [d,I]) in bf16
+    bits, from the forward's activation tiles (Aq, As), the same rows in bf16
+    (A), the forward's weight blocks and the bf16 output gradient dY."""
+    Aq = _c(Aq, np.uint8)
+    As = _c(As, np.float32)
+    A = _c(A, np.uint16)
+    w13q = _c(w13q, np.uint8)
+    w13s = _c(w13s, np.float32)
+    w2q = _c(w2q, np.uint8)
+    w2s = _c(w2s, np.float32)
+    dY = _c(dY, np.uint16)
+    M, d = Aq.shape
+    I = w13q.shape[0] // 2
+    assert A.shape == (M, d) and dY.shape == (M, d) and w2q.shape == (d, I)
+    dA = np.empty((M, d), np.uint16)
+    dw13 = np.empty((2 * I, d), np.uint16)
+    dw2 = np.empty((d, I), np.uint16)
+    lib().orc_swiglu_ffn_backward_fp8(M, d, I, _p(Aq), _p(As), _p(A), _p(w13q), _p(w13s),
+                                      _p(w2q), _p(w2s), _p(dY), _p(dA), _p(dw13), _p(dw2))
+    return dA, dw13, dw2
+
+
 def route_backward(scores, idx, dgate):
     """dz[t,j]: gradient of the chosen logits from the gate gradient."""
     scores = _c(scores, np.float32)
@@ -424,30 +460,44 @@ def input_grad(dout, dx_shared, dx_perm, dst_row, dz, idx, centroids):
 
 
 def layer_backward(inp, cfg, fwd, dout, residual=True):
-    """Gradients of the layer (bf16 or fp32 storage, no FP8) for the upstream
-    gradient ``dout`` [T,d], given the inputs ``inp`` and the forward's results
-    ``fwd`` (from layer_forward).  Returns dx, dcentroids, dw13 [N,2I,d],
-    dw2 [N,d,I], dws13, dws2 and the intermediates dy_perm, dgate, dz, dx_perm,
-    dx_shared."""
-    assert not cfg.get("fp8", False), "the backward covers bf16 and fp32 storage"
+    """Gradients of the layer for the upstream gradient ``dout`` [T,d], given
+    the inputs ``inp`` and the forward's results ``fwd`` (from layer_forward).
+    bf16 / fp32 layers differentiate the stored-precision experts; FP8 layers
+    run every expert GEMM of the backward in E4M3 (swiglu_ffn_backward_fp8).
+    Returns dx, dcentroids, dw13 [N,2I,d], dw2 [N,d,I], dws13, dws2 and the
+    intermediates dy_perm, dgate, dz, dx_perm, dx_shared."""
+    fp8 = cfg.get("fp8", False)
     N = cfg["N"]
     x = inp["x"]
     T, d = x.shape
     dout = _c(dout, x.dtype)
     offsets = fwd["offsets"]
     dy_perm, dgate = combine_backward(dout, fwd["y_perm"], fwd["gate"], fwd["dst_row"])
-    x_perm = fwd["x_perm"]
+    x_perm = fwd["x_perm"] if not fp8 else gather_rows(x, fwd["src_token"])
     dx_perm = np.empty_like(x_perm)
     dw13 = np.empty_like(inp["w13"])
     dw2 = np.empty_like(inp["w2"])
+    if fp8:
+        w13q, w13s = quant_weight_fp8(inp["w13"])
+        w2q, w2s = quant_weight_fp8(inp["w2"])
     for e in range(N):
         a, b = offsets[e], offsets[e + 1]
-        dA, dw13[e], dw2[e] = swiglu_ffn_backward(x_perm[a:b], inp["w13"][e], inp["w2"][e],
-                                                  dy_perm[a:b])
+        if fp8:
+            dA, dw13[e], dw2[e] = swiglu_ffn_backward_fp8(
+                fwd["x_q_perm"][a:b], fwd["x_s_perm"][a:b], x_perm[a:b], w13q[e], w13s[e],
+                w2q[e], w2s[e], dy_perm[a:b])
+        else:
+            dA, dw13[e], dw2[e] = swiglu_ffn_backward(x_perm[a:b], inp["w13"][e], inp["w2"][e],
+                                                      dy_perm[a:b])
         dx_perm[a:b] = dA
     has_shared = inp.get("ws13") is not None and fwd.get("y_shared") is not None
     dx_shared = dws13 = dws2 = None
-    if has_shared:
+    if has_shared and fp8:
+        ws13q, ws13s = quant_weight_fp8(inp["ws13"])
+        ws2q, ws2s = quant_weight_fp8(inp["ws2"])
+        dx_shared, dws13, dws2 = swiglu_ffn_backward_fp8(fwd["x_q"], fwd["x_s"], x, ws13q, ws13s,
+                                                         ws2q, ws2s, dout)
+    elif has_shared:
         dx_shared, dws13, dws2 = swiglu_ffn_backward(x, inp["ws13"], inp["ws2"], dout)
     dz = route_backward(fwd["scores"], fwd["idx"], dgate)
     dE = centroid_grad(x, fwd["idx"], dz, N)

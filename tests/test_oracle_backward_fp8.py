@@ -1,0 +1,130 @@
+"""Pins for the oracle's FP8 backward of one SwiGLU expert.
+
+The method (DeepSeek-V3 report reading guide, xyznot.com/de, "Kernideen",
+FP8 bullet) runs every tensor of the expert GEMMs in E4M3 with 1x128
+activation tiles and 128x128 weight blocks.  The oracle reads that for the
+backward as: each GEMM operand is quantised along that GEMM's contraction, so
+the weight-gradient GEMMs (which contract over an expert's rows) use 128x1
+tiles running down the rows (oracle/moe_oracle.c, orc_quant_cols_fp8 and
+orc_swiglu_ffn_backward_fp8).  Pinned here against things the oracle does not
+contain:
+  - closed forms of the row-direction tiles: the scale of each tile is its
+    column's amax over the tile's rows / 448, the rows of one tile never
+    reach another, and a value equal to the amax decodes exactly to 448;
+  - float64 reverse-mode differentiation (torch.autograd) of a dense SwiGLU
+    expert on the dequantised forward operands: the FP8 backward must agree
+    within the quantisation error (relative Frobenius error), with block- and
+    row-dependent magnitudes so that a scale taken from the wrong block, a
+    transposed operand or a dropped term is an O(1) error;
+  - exact odd symmetry in the output gradient (the quantisers round
+    symmetrically), and zero output gradient / zero rows giving zeros.
+"""
+import numpy as np
+import pytest
+import torch
+
+
+def _bf16(a):
+    """float64 -> bf16 bits (round to nearest even, through torch)"""
+    t = torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _f64(a):
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def _decode(orc, q):
+    return orc.e4m3_decode(q).astype(np.float64)
+
+
+def test_row_direction_tiles_closed_form(orc):
+    rng = np.random.default_rng(1)
+    M, C = 130, 3
+    x = rng.uniform(-1.0, 1.0, (M, C))
+    x[5, 0] = 3.0           # amax of tile (0, 0)
+    x[127, 1] = -40.0       # amax of tile (0, 1), last row of the first tile
+    x[128, 1] = 0.25        # the second tile holds rows 128 and 129 only
+    x[129, 1] = -0.125
+    x[:, 2] = 0.0           # an all-zero column
+    xb = _bf16(x)
+    xv = _f64(xb)
+    q, s = orc.quant_cols_fp8(xb)
+    assert q.shape == (M, C) and s.shape == (2, C)
+    for u, (r0, r1) in enumerate(((0, 128), (128, 130))):
+        for c in range(C):
+            amax = np.float32(np.abs(xv[r0:r1, c]).max())
+            assert s[u, c] == amax / np.float32(448.0), (u, c)
+    assert s[1, 1] == np.float32(0.25) / np.float32(448.0)   # row 127 does not reach tile 1
+    assert np.all(q[:, 2] == 0) and np.all(s[:, 2] == 0)
+    dec = _decode(orc, q)
+    assert dec[5, 0] == 448.0 and dec[127, 1] == -448.0 and dec[128, 1] == 448.0
+    # every code is the E4M3 value nearest x / scale (3 mantissa bits)
+    for u, (r0, r1) in enumerate(((0, 128), (128, 130))):
+        for c in range(2):
+            t = xv[r0:r1, c] / np.float64(s[u, c])
+            assert np.all(np.abs(dec[r0:r1, c] - t) <= np.abs(t) * 2.0 ** -4 + 2.0 ** -10)
+
+
+def _expert_case(orc, M, d, I, seed):
+    """bf16 rows, weights and output gradient with magnitudes that change per
+    128-block (weights), per 128-column tile (rows) and per row"""
+    rng = np.random.default_rng(seed)
+    blk = lambda r, c: np.kron(2.0 ** rng.integers(-2, 3, (r // 128, c // 128)), np.ones((128, 128)))
+    A = rng.standard_normal((M, d)) * (2.0 ** rng.integers(-1, 2, (M, 1)))
+    A *= np.repeat(2.0 ** rng.integers(-1, 2, (1, d // 128)), 128, axis=1)
+    w13 = rng.standard_normal((2 * I, d)) / np.sqrt(d) * blk(2 * I, d)
+    w2 = rng.standard_normal((d, I)) / np.sqrt(I) * blk(d, I)
+    dY = rng.standard_normal((M, d)) * (2.0 ** rng.integers(-2, 2, (M, 1)))
+    A, w13, w2, dY = _bf16(A), _bf16(w13), _bf16(w2), _bf16(dY)
+    Aq, As = orc.quant_act_fp8(A)
+    w13q, w13s = orc.quant_weight_fp8(w13)
+    w2q, w2s = orc.quant_weight_fp8(w2)
+    return A, dY, Aq, As, w13q, w13s, w2q, w2s
+
+
+def _dequant_rows(orc, q, s):
+    return _decode(orc, q) * np.repeat(s.astype(np.float64), 128, axis=1)
+
+
+def _dequant_blocks(orc, q, s):
+    return _decode(orc, q) * np.kron(s.astype(np.float64), np.ones((128, 128)))
+
+
+@pytest.mark.parametrize("M,d,I,seed", [(200, 256, 256, 0), (77, 384, 128, 1), (300, 128, 256, 2)])
+def test_fp8_backward_against_float64_autograd(orc, M, d, I, seed):
+    A, dY, Aq, As, w13q, w13s, w2q, w2s = _expert_case(orc, M, d, I, seed)
+    dA, dw13, dw2 = orc.swiglu_ffn_backward_fp8(Aq, As, A, w13q, w13s, w2q, w2s, dY)
+    Ad = torch.tensor(_dequant_rows(orc, Aq, As), requires_grad=True)
+    W13 = torch.tensor(_dequant_blocks(orc, w13q, w13s), requires_grad=True)
+    W2 = torch.tensor(_dequant_blocks(orc, w2q, w2s), requires_grad=True)
+    a = Ad @ W13[:I].T
+    b = Ad @ W13[I:].T
+    y = (torch.nn.functional.silu(a) * b) @ W2.T
+    (y * torch.from_numpy(_f64(dY))).sum().backward()
+    for name, got, ref in (("dA", dA, Ad.grad), ("dw13", dw13, W13.grad), ("dw2", dw2, W2.grad)):
+        g, r = _f64(got), ref.numpy()
+        rel = np.linalg.norm(g - r) / np.linalg.norm(r)
+        assert rel < 0.08, (name, rel)
+        # no element far off: within 1.5 times the tensor's RMS
+        assert np.max(np.abs(g - r)) < 1.5 * np.sqrt(np.mean(r ** 2)), name
+
+
+def test_fp8_backward_is_odd_in_the_output_gradient(orc):
+    A, dY, Aq, As, w13q, w13s, w2q, w2s = _expert_case(orc, 150, 256, 128, 3)
+    pos = orc.swiglu_ffn_backward_fp8(Aq, As, A, w13q, w13s, w2q, w2s, dY)
+    neg = orc.swiglu_ffn_backward_fp8(Aq, As, A, w13q, w13s, w2q, w2s, dY ^ np.uint16(0x8000))
+    for p, n in zip(pos, neg):
+        assert np.array_equal(_f64(p), -_f64(n))
+
+
+def test_fp8_backward_zero_gradient_and_zero_rows(orc):
+    A, dY, Aq, As, w13q, w13s, w2q, w2s = _expert_case(orc, 64, 128, 128, 4)
+    z = orc.swiglu_ffn_backward_fp8(Aq, As, A, w13q, w13s, w2q, w2s, np.zeros_like(dY))
+    for t in z:
+        assert not np.any(_f64(t))
+    dA, dw13, dw2 = orc.swiglu_ffn_backward_fp8(Aq[:0], As[:0], A[:0], w13q, w13s, w2q, w2s,
+                                                dY[:0])
+    assert dA.shape == (0, 128) and not np.any(_f64(dw13)) and not np.any(_f64(dw2))
