@@ -167,9 +167,10 @@ int moe_expert_ffn(const moe_cfg* cfg, const void* x_perm, const float* x_perm_s
  * W3 rows.  fp32 layers keep the plain layout (a copy).
  *  which: 0 = routed W13 [N, 2I, d], 1 = routed W2 [N, d, I],
  *         2 = shared W13 [2Is, d],   3 = shared W2 [d, Is];
- *         for moe_expert_ffn_backward (bf16 / fp32 layers), the same stacks
- *         transposed: 4 = routed W13, 5 = routed W2, 6 = shared W13,
- *         7 = shared W2 (tiles of 256 columns of the stored matrix)
+ *         for the backward (moe_expert_ffn_backward, and for FP8 layers
+ *         moe_expert_ffn_backward_fp8), the same stacks transposed:
+ *         4 = routed W13, 5 = routed W2, 6 = shared W13, 7 = shared W2
+ *         (tiles of 256 columns of the stored matrix)
  *  w: act_dtype, row-major (FP8 layers: the E4M3 codes from
  *     moe_quantize_weights_fp8, same shape; their scales are passed to
  *     moe_expert_ffn unchanged); w_packed: moe_packed_weights_size(cfg, which) bytes. */

@@ -1,7 +1,8 @@
 /*
  * moe_backward.h -- C ABI of libmoe, backward pass: the gradients of the layer
  * forward declared in moe.h, for bf16 and fp32 storage (gemm_dtype ==
- * act_dtype; FP8 expert GEMMs have no backward here yet).
+ * act_dtype) and for FP8 expert GEMMs (moe_expert_ffn_backward_fp8 in place
+ * of moe_expert_ffn_backward; the other three calls are the bf16 ones).
  *
  * The layer, from the DeepSeek-V3 report reading guide (xyznot.com/de),
  * "Methode", item 2:
@@ -104,6 +105,47 @@ int moe_expert_ffn_backward(const moe_cfg* cfg, const void* x_perm, const int32_
                             void* dx_perm, void* dx_shared, void* dw13, void* dw2, void* dws13,
                             void* dws2, const void* saved, size_t saved_bytes, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace moe_expert_ffn_backward_fp8 needs (V3 shape: about 5 GB). */
+size_t moe_expert_ffn_backward_fp8_workspace_size(const moe_cfg* cfg);
+
+/* FP8 backward of the grouped SwiGLU experts (gemm_dtype FP8_E4M3, act_dtype
+ * BF16).  Reading guide "Kernideen", FP8 bullet (E4M3 for all tensors, 1x128
+ * activation tiles, 128x128 weight blocks, FP32 promotion every 128) applied
+ * to every GEMM of the backward, each operand quantised along that GEMM's
+ * contraction:
+ *   a, b, h  recomputed on FP8 (as the forward), kept in bf16
+ *   dh = dY W2                    dY in 1x128 row tiles
+ *   da, db as in moe_expert_ffn_backward (bf16), then [da db] in 1x128 tiles
+ *   dX = [da db] [W1; W3]
+ *   dW2 = dY^T h, dW13 = [da db]^T X   with dY, h, [da db] and X (the bf16
+ *        layer input rows) quantised in 128x1 tiles down each expert's rows
+ *        (blocks of 128 rows from the expert's first row, the last partial)
+ *   every weight GEMM operand in the forward's 128x128 blocks (the same codes
+ *   and scales; the gradient passes through the block quantisation)
+ *  x [T, d] bf16 layer input; src_token [T*k], offsets [N+1]: the forward's
+ *  x_perm, x_perm_scale   the forward's routed activation tiles (moe_permute)
+ *  x_q, x_scale           the forward's shared-expert tiles (NULL if Is == 0)
+ *  w13 / w13t             routed gate/up codes packed with which = 0 / 4 (the
+ *                         forward's codes [N, 2I, d] in both cases)
+ *  w13_scale              [N, 2I/128, d/128] the forward's block scales
+ *  w2t, w2_scale          down codes packed with which = 5, [N, d/128, I/128]
+ *  ws13, ws13t, ws13_scale, ws2t, ws2_scale   the shared expert's (2, 6, 7)
+ *  dy_perm [T*k, d], dy_shared [T, d]  bf16 output gradients (dy_shared = dout)
+ *  dx_perm, dx_shared     out, bf16, as moe_expert_ffn_backward
+ *  dw13 [N, 2I, d], dw2 [N, d, I], dws13, dws2   out, bf16; zeros for an
+ *                         expert without rows
+ * Deterministic (no atomics); the common rules of moe.h hold. */
+int moe_expert_ffn_backward_fp8(const moe_cfg* cfg, const void* x, const int32_t* src_token,
+                                const int32_t* offsets, const uint8_t* x_perm,
+                                const float* x_perm_scale, const uint8_t* x_q,
+                                const float* x_scale, const void* w13, const void* w13t,
+                                const float* w13_scale, const void* w2t, const float* w2_scale,
+                                const void* ws13, const void* ws13t, const float* ws13_scale,
+                                const void* ws2t, const float* ws2_scale, const void* dy_perm,
+                                const void* dy_shared, void* dx_perm, void* dx_shared,
+                                void* dw13, void* dw2, void* dws13, void* dws2, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace moe_route_backward needs (T*k fp32). */
 size_t moe_route_backward_workspace_size(const moe_cfg* cfg);

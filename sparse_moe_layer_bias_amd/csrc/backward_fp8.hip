@@ -1,0 +1,605 @@
+// backward_fp8.hip -- FP8 E4M3 backward of the grouped SwiGLU experts.
+//
+// DeepSeek-V3 report reading guide (xyznot.com/de), "Kernideen", FP8 bullet:
+// E4M3 for all tensors, 1x128 activation tiles, 128x128 weight blocks, FP32
+// promotion every 128 accumulation steps.  Applied to the backward GEMMs, each
+// operand is quantised along that GEMM's contraction:
+//   dh  = dY W2            dY in 1x128 row tiles x W2's blocks (transposed pack)
+//   da, db from dh and the recomputed a, b (bf16), then [da db] in 1x128 tiles
+//   dX  = [da db] [W1; W3]  on the forward's FP8 kernel (mode 1, transposed pack)
+//   dW2 = dY^T h,  dW13 = [da db]^T X: contraction over an expert's rows, so
+//         dY, h, [da db] and X are quantised in 128x1 tiles down the rows (128
+//         consecutive rows of one expert from its first, the last partial)
+// a, b and h come from an FP8 gate/up recompute (mode 2), kept in bf16; dh, da,
+// db and every output are rounded to bf16.
+//
+// The row-direction tiles are written transposed: feature f of group g holds
+// its codes at [f][poff[g] + row] (poff = prefix of the groups' row counts
+// rounded up to 128, the shared expert last), so that the weight-gradient
+// GEMM reads both operands as rows along its contraction, like the forward.
+#include "gemm_common.h"
+
+namespace moe {
+
+static int64_t a256(int64_t b) { return (b + 255) & ~int64_t(255); }
+static int64_t r128(int64_t b) { return (b + 127) & ~int64_t(127); }
+
+// ---------------------------------------------------------------- row tiles
+
+// bf16 rows [rows][C] -> E4M3 codes [rows][C] + 1x128 scales [rows][C/128];
+// 16 lanes per tile, 8 values per lane
+__global__ void __launch_bounds__(256) quant_rows_bf16_kernel(const uint4* __restrict__ x,
+                                                              int64_t rows, int64_t C,
+                                                              uint2* __restrict__ q,
+                                                              float* __restrict__ s) {
+    const int64_t tiles = C / 128;
+    const int64_t tile = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const int l = threadIdx.x & 15;
+    const bool valid = tile < rows * tiles;  // uniform over each 16-lane group
+    const int64_t v = (valid ? tile : 0) * 16 + l;  // 8-element vector index
+    const uint4 val = valid ? x[v] : make_uint4(0, 0, 0, 0);
+    const uint32_t w[4] = {val.x, val.y, val.z, val.w};
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(w[i] << 16);
+        f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+    const float scale = amax / 448.0f;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lo |= quant_e4m3(f[i], scale) << (8 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hi |= quant_e4m3(f[4 + i], scale) << (8 * i);
+    if (valid) {
+        q[v] = make_uint2(lo, hi);
+        if (l == 0) s[tile] = scale;
+    }
+}
+
+// SwiGLU backward of rows [rows] with I columns: from dh [rows][I] and the
+// recompute's [a | b] [rows][2I] (bf16), da = dh b s (1 + a (1 - s)) and
+// db = dh a s (s = sigmoid(a)) rounded to bf16 into dab = [da | db]
+// [rows][2I], and the 1x128 tiles of those bf16 values: codes [rows][2I],
+// scales [rows][2I/128].  16 lanes per (row, 128-column block of I): the da
+// tile and the db tile of the same columns.
+__global__ void __launch_bounds__(256) swiglu_bwd_fp8_kernel(
+    const uint4* __restrict__ dh, const uint4* __restrict__ ab, int64_t rows, int64_t I,
+    uint4* __restrict__ dab, uint2* __restrict__ q, float* __restrict__ s) {
+    const int64_t nj = I / 128;
+    const int64_t unit = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const int l = threadIdx.x & 15;
+    const bool valid = unit < rows * nj;
+    const int64_t u = valid ? unit : 0;
+    const int64_t r = u / nj, j = u % nj;
+    const int64_t vh = (r * I + j * 128) / 8 + l;            // dh vector
+    const int64_t va = (r * 2 * I + j * 128) / 8 + l;        // a vector; b at + I/8
+    const uint4 qh = dh[vh], qa = ab[va], qb = ab[va + I / 8];
+    const uint32_t wh[4] = {qh.x, qh.y, qh.z, qh.w};
+    const uint32_t wa[4] = {qa.x, qa.y, qa.z, qa.w};
+    const uint32_t wb[4] = {qb.x, qb.y, qb.z, qb.w};
+    float da[8], db[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int k = i >> 1;
+        const uint32_t sh = (i & 1) ? 0 : 16;
+        const uint32_t mk = 0xffff0000u;
+        const float h = __uint_as_float((wh[k] << sh) & mk);
+        const float a = __uint_as_float((wa[k] << sh) & mk);
+        const float b = __uint_as_float((wb[k] << sh) & mk);
+        const float sg = 1.0f / (1.0f + expf(-a));
+        // rounded to bf16 here: the tiles quantise the stored values
+        da[i] = bf16_to_f32(f32_to_bf16(h * b * sg * (1.0f + a * (1.0f - sg))));
+        db[i] = bf16_to_f32(f32_to_bf16(h * a * sg));
+    }
+    float ma = 0.0f, mb = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        ma = fmaxf(ma, fabsf(da[i]));
+        mb = fmaxf(mb, fabsf(db[i]));
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+        ma = fmaxf(ma, __shfl_xor(ma, m, 64));
+        mb = fmaxf(mb, __shfl_xor(mb, m, 64));
+    }
+    const float sa = ma / 448.0f, sb = mb / 448.0f;
+    uint32_t ca[2] = {0u, 0u}, cb[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        ca[i >> 2] |= quant_e4m3(da[i], sa) << (8 * (i & 3));
+        cb[i >> 2] |= quant_e4m3(db[i], sb) << (8 * (i & 3));
+    }
+    if (valid) {
+        dab[va] = make_uint4(pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3]),
+                             pack_bf16x2(da[4], da[5]), pack_bf16x2(da[6], da[7]));
+        dab[va + I / 8] = make_uint4(pack_bf16x2(db[0], db[1]), pack_bf16x2(db[2], db[3]),
+                                     pack_bf16x2(db[4], db[5]), pack_bf16x2(db[6], db[7]));
+        const int64_t qv = (r * 2 * I + j * 128) / 8 + l;
+        q[qv] = make_uint2(ca[0], ca[1]);
+        q[qv + I / 8] = make_uint2(cb[0], cb[1]);
+        if (l == 0) {
+            s[r * 2 * nj + j] = sa;
+            s[r * 2 * nj + nj + j] = sb;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- row-direction tiles
+
+// poff[g] = sum over g' < g of roundup(M_g', 128), g = 0..N (N = the shared
+// expert with S rows), poff[N+1] = the total
+__global__ void pad_offsets_kernel(const int32_t* __restrict__ offsets, int N, int64_t S,
+                                   int32_t* __restrict__ poff) {
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    int64_t acc = 0;
+    for (int g = 0; g <= N; ++g) {
+        poff[g] = (int32_t)acc;
+        const int64_t M = g < N ? offsets[g + 1] - offsets[g] : S;
+        acc += (M + 127) & ~int64_t(127);
+    }
+    poff[N + 1] = (int32_t)acc;
+}
+
+struct ColQuant {
+    const uint16_t* src_r;     // routed rows [T*k][ld_r] (bf16), or x [T][ld_r] with gather
+    const uint16_t* src_s;     // shared rows [S][ld_s]
+    const int32_t* gather;     // routed row -> source row (nullptr: identity)
+    const int32_t* offsets;
+    const int32_t* poff;
+    int N;
+    int64_t S;                 // shared rows (0: none)
+    int64_t C_r, C_s;          // features (columns) of routed / shared rows
+    int64_t ld_r, ld_s;
+    uint8_t* out;              // [feature][P_ld] codes
+    float* out_s;              // [feature][P_ld/128] scales
+    int64_t P_ld;
+};
+
+// One 128-row block of one group x 64 features: the column amax over the
+// block's real rows, the codes of every real row (padding rows get code 0),
+// written transposed (64 output rows of 128 codes).
+__global__ void __launch_bounds__(256) quant_cols_t_kernel(ColQuant p) {
+    __shared__ float tile[128][65];
+    __shared__ float red[4][64];
+    const int64_t row0 = (int64_t)blockIdx.x * 128;  // position on the padded axis
+    const int32_t total = p.poff[p.N + 1];
+    if (row0 >= total) return;
+    int lo = 0, hi = p.N;  // group g: poff[g] <= row0 < poff[g+1]
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (p.poff[mid] <= row0) lo = mid; else hi = mid - 1;
+    }
+    const int g = lo;
+    const bool routed = g < p.N;
+    const int64_t C = routed ? p.C_r : p.C_s;
+    const int64_t c0 = (int64_t)blockIdx.y * 64;
+    if (c0 >= C) return;
+    const int64_t r0 = row0 - p.poff[g];  // first row of the block within the group
+    const int64_t M = routed ? p.offsets[g + 1] - p.offsets[g] : p.S;
+    const int valid = (int)(M - r0 < 128 ? M - r0 : 128);
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+        const int row = pass * 32 + (t >> 3), cc = (t & 7) * 8;
+        float f[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (row < valid) {
+            const uint16_t* src;
+            if (routed) {
+                const int64_t rr = p.offsets[g] + r0 + row;
+                src = p.src_r + (p.gather ? (int64_t)p.gather[rr] : rr) * p.ld_r;
+            } else {
+                src = p.src_s + (r0 + row) * p.ld_s;
+            }
+            const uint4 v = *(const uint4*)(src + c0 + cc);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f[2 * i] = __uint_as_float(w[i] << 16);
+                f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) tile[row][cc + i] = f[i];
+    }
+    __syncthreads();
+    const int col = t & 63, part = t >> 6;
+    float m = 0.0f;
+    for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(tile[part * 32 + i][col]));
+    red[part][col] = m;
+    __syncthreads();
+    const float amax = fmaxf(fmaxf(red[0][col], red[1][col]), fmaxf(red[2][col], red[3][col]));
+    const float scale = amax / 448.0f;
+    uint32_t code[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        uint32_t wv = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = part * 32 + 4 * k + e;
+            if (row < valid) wv |= quant_e4m3(tile[row][col], scale) << (8 * e);
+        }
+        code[k] = wv;
+    }
+    uint8_t* o = p.out + (c0 + col) * p.P_ld + row0 + part * 32;
+    *(uint4*)o = make_uint4(code[0], code[1], code[2], code[3]);
+    *(uint4*)(o + 16) = make_uint4(code[4], code[5], code[6], code[7]);
+    if (part == 0) p.out_s[(c0 + col) * (p.P_ld / 128) + row0 / 128] = scale;
+}
+
+// ---------------------------------------------------------------- weight gradients
+
+struct WgFp8 {
+    const uint8_t* At;  // [rowsA][P_ld] codes (A^T: output rows along the contraction)
+    const float* AtS;   // [rowsA][P_ld/128]
+    const uint8_t* Bt;  // [rowsB][P_ld]
+    const float* BtS;
+    const int32_t* poff;
+    int64_t P_ld;
+    int N;
+    int has_shared;
+    int64_t rowsA_r, rowsB_r, rowsA_s, rowsB_s;
+    uint16_t* out_r;    // [N][rowsA_r][rowsB_r] bf16
+    uint16_t* out_s;    // [rowsA_s][rowsB_s]
+};
+
+// out[n][c] = sum over the group's 128-row blocks u of
+//   (sA[n,u] sB[c,u]) * sum_{rows of u} qA[n,row] qB[c,row]
+// One workgroup = 128 x 128 outputs of one group, 4 waves of 64 x 64 (2 x 2
+// blocks of 32x32x64 MFMAs).  Per block the two K halves accumulate the code
+// products into a fresh partial (MFMA scale operands 1.0), which is then
+// promoted into the fp32 result with the product of the two fp32 scales.
+__global__ void __launch_bounds__(256) wgrad_fp8_kernel(WgFp8 p) {
+    __shared__ __attribute__((aligned(16))) uint8_t sA[128 * 128];
+    __shared__ __attribute__((aligned(16))) uint8_t sB[128 * 128];
+    __shared__ __attribute__((aligned(16))) float scA[128];
+    __shared__ __attribute__((aligned(16))) float scB[128];
+    const int64_t tr = (p.rowsA_r / 128) * (p.rowsB_r / 128);
+    const int64_t unit = blockIdx.x;
+    int g;
+    int64_t ti, rowsA, rowsB;
+    uint16_t* out;
+    if (unit < (int64_t)p.N * tr) {
+        g = (int)(unit / tr);
+        ti = unit % tr;
+        rowsA = p.rowsA_r;
+        rowsB = p.rowsB_r;
+        out = p.out_r + (int64_t)g * rowsA * rowsB;
+    } else {
+        if (!p.has_shared) return;
+        g = p.N;
+        ti = unit - (int64_t)p.N * tr;
+        rowsA = p.rowsA_s;
+        rowsB = p.rowsB_s;
+        if (ti >= (rowsA / 128) * (rowsB / 128)) return;
+        out = p.out_s;
+    }
+    const int64_t ta = ti / (rowsB / 128), tb = ti % (rowsB / 128);
+    const int64_t P0 = p.poff[g];
+    const int nb = (int)((p.poff[g + 1] - P0) / 128);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wa = wave & 1, wb = wave >> 1, h = lane >> 5;
+    const int64_t sld = p.P_ld / 128;
+
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    const f32x16_t zero = acc[0][0];
+
+    for (int u = 0; u < nb; ++u) {
+        __syncthreads();  // the previous block is read out of LDS
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int idx = threadIdx.x + 256 * k;
+            const int r = idx >> 3, ch = idx & 7;
+            const int64_t col = P0 + (int64_t)u * 128 + ch * 16;
+            const uint4 va = *(const uint4*)(p.At + (ta * 128 + r) * p.P_ld + col);
+            const uint4 vb = *(const uint4*)(p.Bt + (tb * 128 + r) * p.P_ld + col);
+            *(uint4*)(sA + r * 128 + sub_chunk8(r, ch) * 16) = va;
+            *(uint4*)(sB + r * 128 + sub_chunk8(r, ch) * 16) = vb;
+        }
+        if (threadIdx.x < 128)
+            scA[threadIdx.x] = p.AtS[(ta * 128 + threadIdx.x) * sld + P0 / 128 + u];
+        else
+            scB[threadIdx.x - 128] = p.BtS[(tb * 128 + threadIdx.x - 128) * sld + P0 / 128 + u];
+        __syncthreads();
+        f32x16_t part[2][2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            i32x8_t af[2], bf[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int ra = wa * 64 + i * 32 + (lane & 31);
+                const int rb = wb * 64 + i * 32 + (lane & 31);
+                const uint8_t* pa = sA + ra * 128;
+                const uint8_t* pb = sB + rb * 128;
+                const uint4 a0 = *(const uint4*)(pa + sub_chunk8(ra, 4 * q + 2 * h) * 16);
+                const uint4 a1 = *(const uint4*)(pa + sub_chunk8(ra, 4 * q + 2 * h + 1) * 16);
+                const uint4 b0 = *(const uint4*)(pb + sub_chunk8(rb, 4 * q + 2 * h) * 16);
+                const uint4 b1 = *(const uint4*)(pb + sub_chunk8(rb, 4 * q + 2 * h + 1) * 16);
+                af[i] = i32x8_t{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                                (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+                bf[i] = i32x8_t{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                                (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        af[i], bf[j], q == 0 ? zero : part[i][j], 0, 0, 0, 127, 0, 127);
+        }
+        // promotion: lane holds column c = lane%32 of its 32x32 block and rows
+        // 8 (v/4) + 4 (lane/32) + v%4
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const float sb = scB[wb * 64 + j * 32 + (lane & 31)];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const float4 sa = *(const float4*)(scA + wa * 64 + i * 32 + 8 * g4 + 4 * h);
+                    acc[i][j][4 * g4 + 0] += part[i][j][4 * g4 + 0] * (sa.x * sb);
+                    acc[i][j][4 * g4 + 1] += part[i][j][4 * g4 + 1] * (sa.y * sb);
+                    acc[i][j][4 * g4 + 2] += part[i][j][4 * g4 + 2] * (sa.z * sb);
+                    acc[i][j][4 * g4 + 3] += part[i][j][4 * g4 + 3] * (sa.w * sb);
+                }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int64_t c = tb * 128 + wb * 64 + j * 32 + (lane & 31);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t n = ta * 128 + wa * 64 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                out[n * rowsB + c] = f32_to_bf16(acc[i][j][v]);
+            }
+        }
+}
+
+// ---------------------------------------------------------------- driver
+
+struct BwdFp8Ws {
+    int2* tiles;
+    int32_t* counts;
+    int32_t* order;
+    int32_t* keys;
+    int32_t* poff;
+    void *ab_r, *h_r, *ab_s, *h_s;      // recompute (bf16)
+    uint8_t *gq_r, *gq_s;               // dY row tiles
+    float *gs_r, *gs_s;
+    void *dh_r, *dh_s;                  // dh (bf16)
+    void *dab_r, *dab_s;                // [da | db] (bf16)
+    uint8_t *tq_r, *tq_s;               // [da | db] row tiles
+    float *ts_r, *ts_s;
+    uint8_t *gT, *hT, *tT, *xT;         // row-direction tiles, transposed
+    float *gTs, *hTs, *tTs, *xTs;
+    int64_t P_ld;
+};
+
+static int64_t bwd_fp8_max_r(const moe_cfg& c) { return c.tokens * c.top_k / FP8_BM + c.n_experts; }
+static int64_t bwd_fp8_max_s(const moe_cfg& c) { return cdiv(c.tokens, FP8_BM); }
+
+static BwdFp8Ws carve_bwd_fp8(const moe_cfg& c, void* ws, size_t* bytes) {
+    const int64_t R = c.tokens * c.top_k, T = c.tokens, d = c.hidden, I = c.inter;
+    const int64_t Is = c.inter_shared, S = Is > 0 ? T : 0, N = c.n_experts;
+    const int64_t Im = I > Is ? I : Is;
+    BwdFp8Ws w{};
+    w.P_ld = r128(R + 128 * N + S + 128);
+    char* base = (char*)ws;
+    int64_t o = 0;
+    auto take = [&](int64_t n) {
+        char* q = base ? base + o : nullptr;
+        o += a256(n);
+        return q;
+    };
+    w.tiles = (int2*)take((bwd_fp8_max_r(c) + bwd_fp8_max_s(c)) * 8);
+    w.counts = (int32_t*)take(8);
+    w.order = (int32_t*)take(bwd_fp8_max_r(c) * 4);
+    w.keys = (int32_t*)take(bwd_fp8_max_r(c) * 4);
+    w.poff = (int32_t*)take((N + 2) * 4);
+    w.ab_r = take(R * 2 * I * 2);
+    w.h_r = take(R * I * 2);
+    w.ab_s = take(S * 2 * Is * 2);
+    w.h_s = take(S * Is * 2);
+    w.gq_r = (uint8_t*)take(R * d);
+    w.gs_r = (float*)take(R * (d / 128) * 4);
+    w.gq_s = (uint8_t*)take(S * d);
+    w.gs_s = (float*)take(S * (d / 128) * 4);
+    w.dh_r = take(R * I * 2);
+    w.dh_s = take(S * Is * 2);
+    w.dab_r = take(R * 2 * I * 2);
+    w.dab_s = take(S * 2 * Is * 2);
+    w.tq_r = (uint8_t*)take(R * 2 * I);
+    w.ts_r = (float*)take(R * (2 * I / 128) * 4);
+    w.tq_s = (uint8_t*)take(S * 2 * Is);
+    w.ts_s = (float*)take(S * (2 * Is / 128) * 4);
+    const int64_t sl = w.P_ld / 128;
+    w.gT = (uint8_t*)take(d * w.P_ld);
+    w.gTs = (float*)take(d * sl * 4);
+    w.hT = (uint8_t*)take(Im * w.P_ld);
+    w.hTs = (float*)take(Im * sl * 4);
+    w.tT = (uint8_t*)take(2 * Im * w.P_ld);
+    w.tTs = (float*)take(2 * Im * sl * 4);
+    w.xT = (uint8_t*)take(d * w.P_ld);
+    w.xTs = (float*)take(d * sl * 4);
+    if (bytes) *bytes = (size_t)o;
+    return w;
+}
+
+size_t ffn_backward_fp8_workspace_bytes(const moe_cfg& c) {
+    size_t b = 0;
+    carve_bwd_fp8(c, nullptr, &b);
+    return b;
+}
+
+static hipError_t quant_rows(const void* x, int64_t rows, int64_t C, uint8_t* q, float* s,
+                             hipStream_t st) {
+    const int64_t tiles = rows * (C / 128);
+    if (tiles == 0) return hipSuccess;
+    quant_rows_bf16_kernel<<<(unsigned)cdiv(tiles, 16), 256, 0, st>>>((const uint4*)x, rows, C,
+                                                                       (uint2*)q, s);
+    return hipGetLastError();
+}
+
+static hipError_t swiglu_bwd(const void* dh, const void* ab, int64_t rows, int64_t I, void* dab,
+                             uint8_t* q, float* s, hipStream_t st) {
+    const int64_t units = rows * (I / 128);
+    if (units == 0) return hipSuccess;
+    swiglu_bwd_fp8_kernel<<<(unsigned)cdiv(units, 16), 256, 0, st>>>(
+        (const uint4*)dh, (const uint4*)ab, rows, I, (uint4*)dab, (uint2*)q, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_expert_ffn_backward_fp8(const moe_cfg& c, const FfnBwdFp8Args& a, void* ws,
+                                          hipStream_t st) {
+    const int64_t T = c.tokens, R = T * c.top_k, d = c.hidden, I = c.inter;
+    const int64_t Is = c.inter_shared, N = c.n_experts;
+    const bool has_shared = Is > 0 && T > 0;
+    const int64_t S = has_shared ? T : 0;
+    BwdFp8Ws w = carve_bwd_fp8(c, ws, nullptr);
+    const int64_t max_r = bwd_fp8_max_r(c), max_s = has_shared ? bwd_fp8_max_s(c) : 0;
+    hipError_t e;
+    if (R > 0) {
+        launch_tile_map(a.offsets, (int)N, T, has_shared, FP8_BM, w.tiles, w.counts, w.order,
+                        w.keys, st);
+        // 1. a, b, h of every row (FP8 gate/up, as in the forward)
+        Fp8Gemm g{};
+        g.mode = 2;
+        g.K_r = g.K_s = d;
+        g.Nout_r = I;
+        g.Nout_s = Is;
+        g.A_r = a.x_perm_q;
+        g.A_s = a.x_q;
+        g.as_r = a.x_perm_s;
+        g.as_s = a.x_s;
+        g.B_r = a.w13;
+        g.B_s = a.ws13;
+        g.bs_r = a.w13_s;
+        g.bs_s = a.ws13_s;
+        g.C_r = w.h_r;
+        g.C_s = w.h_s;
+        g.E_r = w.ab_r;
+        g.E_s = w.ab_s;
+        if ((e = launch_fp8_gemm(g, w.tiles, w.counts, w.order, a.offsets, (int)N, S, max_r,
+                                 max_s, st)) != hipSuccess)
+            return e;
+        // 2. dY row tiles, dh = dY W2
+        if ((e = quant_rows(a.dy_perm, R, d, w.gq_r, w.gs_r, st)) != hipSuccess) return e;
+        if (has_shared && (e = quant_rows(a.dy_sh, S, d, w.gq_s, w.gs_s, st)) != hipSuccess)
+            return e;
+        g = Fp8Gemm{};
+        g.mode = 1;
+        g.K_r = g.K_s = d;
+        g.Nout_r = I;
+        g.Nout_s = Is;
+        g.A_r = w.gq_r;
+        g.A_s = w.gq_s;
+        g.as_r = w.gs_r;
+        g.as_s = w.gs_s;
+        g.B_r = a.w2t;
+        g.B_s = a.ws2t;
+        g.bs_r = a.w2_s;
+        g.bs_s = a.ws2_s;
+        g.bs_t = 1;
+        g.C_r = w.dh_r;
+        g.C_s = w.dh_s;
+        if ((e = launch_fp8_gemm(g, w.tiles, w.counts, w.order, a.offsets, (int)N, S, max_r,
+                                 max_s, st)) != hipSuccess)
+            return e;
+        // 3. da, db and their row tiles
+        if ((e = swiglu_bwd(w.dh_r, w.ab_r, R, I, w.dab_r, w.tq_r, w.ts_r, st)) != hipSuccess)
+            return e;
+        if (has_shared &&
+            (e = swiglu_bwd(w.dh_s, w.ab_s, S, Is, w.dab_s, w.tq_s, w.ts_s, st)) != hipSuccess)
+            return e;
+        // 4. dX = [da db] [W1; W3]
+        g = Fp8Gemm{};
+        g.mode = 1;
+        g.K_r = 2 * I;
+        g.K_s = 2 * Is;
+        g.Nout_r = g.Nout_s = d;
+        g.A_r = w.tq_r;
+        g.A_s = w.tq_s;
+        g.as_r = w.ts_r;
+        g.as_s = w.ts_s;
+        g.B_r = a.w13t;
+        g.B_s = a.ws13t;
+        g.bs_r = a.w13_s;
+        g.bs_s = a.ws13_s;
+        g.bs_t = 1;
+        g.C_r = a.dx_perm;
+        g.C_s = a.dx_sh;
+        if ((e = launch_fp8_gemm(g, w.tiles, w.counts, w.order, a.offsets, (int)N, S, max_r,
+                                 max_s, st)) != hipSuccess)
+            return e;
+    }
+    // 5. row-direction tiles of dY, h, [da db] and X (empty groups: nothing)
+    pad_offsets_kernel<<<1, 64, 0, st>>>(a.offsets, (int)N, S, w.poff);
+    const unsigned pblocks = (unsigned)(w.P_ld / 128);
+    auto cols = [&](const void* sr, const void* ss, const int32_t* gather, int64_t Cr,
+                    int64_t Cs, int64_t ldr, int64_t lds, uint8_t* out, float* outs) {
+        ColQuant p{};
+        p.src_r = (const uint16_t*)sr;
+        p.src_s = (const uint16_t*)ss;
+        p.gather = gather;
+        p.offsets = a.offsets;
+        p.poff = w.poff;
+        p.N = (int)N;
+        p.S = S;
+        p.C_r = Cr;
+        p.C_s = Cs;
+        p.ld_r = ldr;
+        p.ld_s = lds;
+        p.out = out;
+        p.out_s = outs;
+        p.P_ld = w.P_ld;
+        const int64_t cm = Cr > Cs ? Cr : Cs;
+        quant_cols_t_kernel<<<dim3(pblocks, (unsigned)cdiv(cm, 64)), 256, 0, st>>>(p);
+    };
+    if (R + S > 0) {
+        cols(a.dy_perm, a.dy_sh, nullptr, d, d, d, d, w.gT, w.gTs);
+        cols(w.h_r, w.h_s, nullptr, I, Is, I, Is, w.hT, w.hTs);
+        cols(w.dab_r, w.dab_s, nullptr, 2 * I, 2 * Is, 2 * I, 2 * Is, w.tT, w.tTs);
+        cols(a.x, a.x, a.src_token, d, d, d, d, w.xT, w.xTs);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    // 6. dW2 = dY^T h and dW13 = [da db]^T X for every expert (zeros without rows)
+    auto wgrad = [&](const uint8_t* At, const float* AtS, const uint8_t* Bt, const float* BtS,
+                     int64_t rAr, int64_t rBr, int64_t rAs, int64_t rBs, void* outr, void* outs) {
+        WgFp8 p{};
+        p.At = At;
+        p.AtS = AtS;
+        p.Bt = Bt;
+        p.BtS = BtS;
+        p.poff = w.poff;
+        p.P_ld = w.P_ld;
+        p.N = (int)N;
+        p.has_shared = has_shared ? 1 : 0;
+        p.rowsA_r = rAr;
+        p.rowsB_r = rBr;
+        p.rowsA_s = rAs;
+        p.rowsB_s = rBs;
+        p.out_r = (uint16_t*)outr;
+        p.out_s = (uint16_t*)outs;
+        const int64_t units = N * (rAr / 128) * (rBr / 128) +
+                              (has_shared ? (rAs / 128) * (rBs / 128) : 0);
+        if (units > 0) wgrad_fp8_kernel<<<(unsigned)units, 256, 0, st>>>(p);
+    };
+    wgrad(w.gT, w.gTs, w.hT, w.hTs, d, I, d, Is, a.dw2, a.dws2);
+    wgrad(w.tT, w.tTs, w.xT, w.xTs, 2 * I, d, 2 * Is, d, a.dw13, a.dws13);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -117,7 +117,7 @@ int set_error(int code, const char* msg) {
 
 extern "C" {
 
-int moe_abi_version(void) { return 4; }
+int moe_abi_version(void) { return 5; }
 
 const char* moe_last_error(void) { return g_err; }
 
@@ -289,8 +289,6 @@ int moe_pack_weights(const moe_cfg* cfg, int which, const void* w, void* w_packe
     if (int r = check_cfg(fn, cfg)) return r;
     if (int r = check_ffn_shape(fn, cfg)) return r;
     if (which < 0 || which > 7) return fail(MOE_ERR_ARG, "%s: which must be 0..7", fn);
-    if (which >= 4 && cfg->gemm_dtype == MOE_FP8_E4M3)
-        return fail(MOE_ERR_UNSUPPORTED, "%s: transposed packs are for bf16 / fp32 layers", fn);
     if ((which == 2 || which == 3 || which == 6 || which == 7) && cfg->inter_shared == 0)
         return fail(MOE_ERR_ARG, "%s: no shared expert (inter_shared == 0)", fn);
     REQ_PTR(w);
@@ -440,6 +438,92 @@ int moe_expert_ffn_backward(const moe_cfg* cfg, const void* x_perm, const int32_
                       ws2t,    dy_shared, dx_perm, dx_shared, dw13, dw2,     dws13, dws2};
     return hip_status(fn, moe::launch_expert_ffn_backward(*cfg, a, workspace, (hipStream_t)stream,
                                                           saved));
+}
+
+size_t moe_expert_ffn_backward_fp8_workspace_size(const moe_cfg* cfg) {
+    if (!cfg) return 0;
+    return moe::ffn_backward_fp8_workspace_bytes(*cfg);
+}
+
+int moe_expert_ffn_backward_fp8(const moe_cfg* cfg, const void* x, const int32_t* src_token,
+                                const int32_t* offsets, const uint8_t* x_perm,
+                                const float* x_perm_scale, const uint8_t* x_q,
+                                const float* x_scale, const void* w13, const void* w13t,
+                                const float* w13_scale, const void* w2t, const float* w2_scale,
+                                const void* ws13, const void* ws13t, const float* ws13_scale,
+                                const void* ws2t, const float* ws2_scale, const void* dy_perm,
+                                const void* dy_shared, void* dx_perm, void* dx_shared,
+                                void* dw13, void* dw2, void* dws13, void* dws2, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    const char* fn = "moe_expert_ffn_backward_fp8";
+    if (int r = check_cfg(fn, cfg)) return r;
+    if (int r = check_ffn_shape(fn, cfg)) return r;
+    if (cfg->gemm_dtype != MOE_FP8_E4M3 || cfg->act_dtype != MOE_BF16)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: needs gemm_dtype FP8_E4M3 and act_dtype BF16", fn);
+    const int64_t T = cfg->tokens, R = T * cfg->top_k;
+    if (R + 128 * (cfg->n_experts + 2) + T >= ((int64_t)1 << 31))
+        return fail(MOE_ERR_UNSUPPORTED, "%s: too many rows for the 32-bit row offsets", fn);
+    REQ_PTR(dw13);
+    REQ_PTR(dw2);
+    REQ_PTR(offsets);
+    REQ_PTR(workspace);
+    if (T > 0) {
+        REQ_PTR(x);
+        REQ_PTR(src_token);
+        REQ_PTR(x_perm);
+        REQ_PTR(x_perm_scale);
+        REQ_PTR(w13);
+        REQ_PTR(w13t);
+        REQ_PTR(w13_scale);
+        REQ_PTR(w2t);
+        REQ_PTR(w2_scale);
+        REQ_PTR(dy_perm);
+        REQ_PTR(dx_perm);
+        if (cfg->inter_shared > 0) {
+            REQ_PTR(x_q);
+            REQ_PTR(x_scale);
+            REQ_PTR(ws13);
+            REQ_PTR(ws13t);
+            REQ_PTR(ws13_scale);
+            REQ_PTR(ws2t);
+            REQ_PTR(ws2_scale);
+            REQ_PTR(dy_shared);
+            REQ_PTR(dx_shared);
+            REQ_PTR(dws13);
+            REQ_PTR(dws2);
+        }
+    }
+    if (workspace_bytes < moe_expert_ffn_backward_fp8_workspace_size(cfg))
+        return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes,
+                    moe_expert_ffn_backward_fp8_workspace_size(cfg));
+    moe::FfnBwdFp8Args a{};
+    a.x = x;
+    a.src_token = src_token;
+    a.offsets = offsets;
+    a.x_perm_q = x_perm;
+    a.x_perm_s = x_perm_scale;
+    a.x_q = x_q;
+    a.x_s = x_scale;
+    a.w13 = w13;
+    a.w13t = w13t;
+    a.w13_s = w13_scale;
+    a.w2t = w2t;
+    a.w2_s = w2_scale;
+    a.ws13 = ws13;
+    a.ws13t = ws13t;
+    a.ws13_s = ws13_scale;
+    a.ws2t = ws2t;
+    a.ws2_s = ws2_scale;
+    a.dy_perm = dy_perm;
+    a.dy_sh = dy_shared;
+    a.dx_perm = dx_perm;
+    a.dx_sh = dx_shared;
+    a.dw13 = dw13;
+    a.dw2 = dw2;
+    a.dws13 = dws13;
+    a.dws2 = dws2;
+    return hip_status(fn, moe::launch_expert_ffn_backward_fp8(*cfg, a, workspace,
+                                                              (hipStream_t)stream));
 }
 
 size_t moe_route_backward_workspace_size(const moe_cfg* cfg) {

@@ -29,7 +29,6 @@ namespace moe {
 static int64_t align256(int64_t b) { return (b + 255) & ~int64_t(255); }
 
 constexpr int BF_BM = 320;      // token rows per tile, bf16 MFMA kernel
-constexpr int FP8_BM = 320;     // token rows per tile, FP8 MFMA kernel
 constexpr int F32_BM = 64;      // token rows per tile, fp32 path
 
 // ---------------------------------------------------------------- tile map
@@ -569,7 +568,6 @@ size_t packed_weight_bytes(const moe_cfg& c, int which) {
     const PackShape s = pack_shape(c, which);
     if (c.act_dtype == MOE_F32 && c.gemm_dtype == MOE_F32)
         return (size_t)(s.n_mats * (s.mode == 0 ? 2 * s.Nout : s.Nout) * s.K * 4);
-    if (s.mode == 2 && c.gemm_dtype == MOE_FP8_E4M3) return 0;  // no FP8 backward
     if (c.gemm_dtype == MOE_FP8_E4M3) return packed_weight_bytes_fp8(c, which);
     return (size_t)(s.n_mats * s.ntn * G_WR * s.K * 2);
 }

@@ -56,6 +56,8 @@ struct Fp8Params {
     const float* ws_s;
     float* hs_r;           // gate/up: h tile scales [rows][I/128]
     float* hs_s;
+    int ws_t;              // weight scales indexed [mats][K/128][rows/128] (the
+                           // block grid of the untransposed matrix: dgrad GEMMs)
 };
 
 // Pack FP8 weight codes [n_mats][rows][K] into the kernel's LDS image order:
@@ -124,7 +126,8 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
     const int64_t gi = shared ? 0 : w.g;
     const float* xs = (shared ? P.xs_s : P.xs_r) + (w.rowbase + w.m0) * nkb;
     const float* wsc = shared ? P.ws_s : P.ws_r;
-    const int64_t wrows = MODE == 0 ? 2 * w.Nout : w.Nout;
+    constexpr bool GU = MODE != 1;  // gate/up-shaped tile (modes 0 and 2)
+    const int64_t wrows = GU ? 2 * w.Nout : w.Nout;
     const int64_t wrb = wrows / 128;  // 128-row scale blocks per expert matrix
 
     // Copies go through buffer descriptors (base in SGPRs, 32-bit lane offsets,
@@ -190,11 +193,12 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
     // rows 0..127 and 128..255 (a wave's 64 rows lie in block wg/2).
     float* swl = (float*)(smem + F8_NS * F8_STAGE);
     {
-        const int64_t b0 = MODE == 0 ? w.wt : 2 * w.wt;
-        const int64_t b1 = MODE == 0 ? w.Nout / 128 + w.wt : 2 * w.wt + 1;
+        const int64_t b0 = GU ? w.wt : 2 * w.wt;
+        const int64_t b1 = GU ? w.Nout / 128 + w.wt : 2 * w.wt + 1;
         for (int t = threadIdx.x; t < 2 * nkb; t += F8_THREADS) {
-            const int64_t blk = t < nkb ? b0 : b1;
-            swl[t] = blk < wrb ? wsc[(gi * wrb + blk) * nkb + (t < nkb ? t : t - nkb)] : 0.0f;
+            const int64_t blk = t < nkb ? b0 : b1, kb = t < nkb ? t : t - nkb;
+            swl[t] = blk < wrb ? wsc[P.ws_t ? (gi * nkb + kb) * wrb + blk : (gi * wrb + blk) * nkb + kb]
+                               : 0.0f;
         }
     }
 
@@ -218,7 +222,7 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
                 for (int i = 0; i < 2; ++i) {
                     const int r = (wg * 2 + i) * 32 + (lane & 31);
                     af[i] = ld_frag32(As + r * F8_BK, r, q, h);
-                    if (q == 0) split_scale(swl[(MODE == 0 ? i : wg >> 1) * nkb + kt], ew[i], mw[i]);
+                    if (q == 0) split_scale(swl[(GU ? i : wg >> 1) * nkb + kt], ew[i], mw[i]);
                 }
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
@@ -258,7 +262,38 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
     // epilogue.  32x32 accumulator layout: lane l holds column (token) l%32 and
     // rows (weight rows) 8*(v/4) + 4*(l/32) + v%4, v = 0..15.
     __syncthreads();  // every wave is done with the stage buffers
-    if (MODE == 0) {
+    if (MODE == 2) {
+        // training recompute: a and b rounded to bf16 into E ([rows][2 Nout],
+        // a row is [a | b]) and h = silu(a) * b rounded to bf16 into C
+        // ([rows][Nout]), straight from the accumulators (4 columns per store)
+        if constexpr (NB > 0) {
+            uint16_t* hb = (uint16_t*)(shared ? P.g.C_s : P.g.C_r) + (w.rowbase + w.m0) * w.Nout;
+            uint16_t* eb = (uint16_t*)(shared ? P.g.E_s : P.g.E_r) + (w.rowbase + w.m0) * 2 * w.Nout;
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const int64_t rr = tg * 160 + j * 32 + (lane & 31);
+                if (rr < mc) {
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int64_t col = w.wt * 128 + wg * 32 + 8 * g4 + 4 * (lane >> 5);
+                        float a[4], b[4];
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            a[v] = acc[0][j][4 * g4 + v];
+                            b[v] = acc[1][j][4 * g4 + v];
+                        }
+                        *(uint2*)(eb + rr * 2 * w.Nout + col) =
+                            make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+                        *(uint2*)(eb + rr * 2 * w.Nout + w.Nout + col) =
+                            make_uint2(pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3]));
+                        *(uint2*)(hb + rr * w.Nout + col) = make_uint2(
+                            pack_bf16x2(silu_f(a[0]) * b[0], silu_f(a[1]) * b[1]),
+                            pack_bf16x2(silu_f(a[2]) * b[2], silu_f(a[3]) * b[3]));
+                    }
+                }
+            }
+        }
+    } else if (MODE == 0) {
         // h = silu(a) * b for the tile's 128 columns, then 1x128 quantisation:
         // the tile amax is reduced over the 4 weight-row waves through LDS;
         // codes are staged in LDS and stored as whole 128-byte rows
@@ -366,18 +401,71 @@ __global__ void __launch_bounds__(F8_THREADS, 1) ffn_gemm_fp8_kernel(Fp8Params P
     }
 }
 
+// Pack the TRANSPOSE of FP8 weight codes [n_mats][K][Nout] (the forward's
+// matrix, read column-wise) in the down-projection order of
+// pack_weights_fp8_kernel<1>: packed row r of tile wt is column wt*256 + r.
+// For the data-gradient GEMMs (W2^T: rows I, K = d; [W1; W3]^T: rows d,
+// K = 2I); a one-off preparation, so the 16 codes of a chunk are gathered
+// byte by byte.
+__global__ void __launch_bounds__(256) pack_weights_fp8_t_kernel(const uint8_t* __restrict__ w,
+                                                                 uint4* __restrict__ out,
+                                                                 int64_t n_mats, int64_t Nout,
+                                                                 int64_t K, int64_t ntn) {
+    const int64_t nkt = K / F8_BK;
+    const int64_t per_mat = ntn * nkt * G_WR_PACK * 8;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n_mats * per_mat) return;
+    const int64_t mat = i / per_mat;
+    int64_t rem = i % per_mat;
+    const int64_t wt = rem / (nkt * G_WR_PACK * 8);
+    rem %= nkt * G_WR_PACK * 8;
+    const int64_t kt = rem / (G_WR_PACK * 8);
+    const int slot = (int)(rem % (G_WR_PACK * 8));
+    const int r = slot >> 3, c = sub_chunk8(r, slot & 7);
+    const int64_t src = packed_row_source<1>(wt, r, Nout);
+    uint32_t v[4] = {0u, 0u, 0u, 0u};
+    if (src >= 0) {
+        const uint8_t* col = w + (mat * K + kt * F8_BK + c * 16) * Nout + src;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e >> 2] |= (uint32_t)col[e * Nout] << (8 * (e & 3));
+    }
+    out[i] = make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // ---------------------------------------------------------------- launch
 
-size_t packed_weight_bytes_fp8(const moe_cfg& c, int which) {
-    const bool routed = which == 0 || which == 1;
-    const int64_t n = routed ? c.n_experts : 1;
+// which: 0/2 W13 and 1/3 W2 (routed / shared) for the forward; 4/6 [W1; W3]^T
+// (rows d, K = 2I) and 5/7 W2^T (rows I, K = d) for the backward, packed from
+// the forward's codes
+static void fp8_pack_dims(const moe_cfg& c, int which, int64_t& n, int64_t& Nout, int64_t& K) {
+    const bool routed = which == 0 || which == 1 || which == 4 || which == 5;
+    n = routed ? c.n_experts : 1;
     const int64_t I = routed ? c.inter : c.inter_shared;
-    if (which == 0 || which == 2) return (size_t)(n * cdiv(I, 128) * G_WR_PACK * c.hidden);
-    return (size_t)(n * cdiv(c.hidden, 256) * G_WR_PACK * I);
+    if (which == 0 || which == 2) { Nout = I; K = c.hidden; }
+    else if (which == 1 || which == 3) { Nout = c.hidden; K = I; }
+    else if (which == 4 || which == 6) { Nout = c.hidden; K = 2 * I; }
+    else { Nout = I; K = c.hidden; }
+}
+
+size_t packed_weight_bytes_fp8(const moe_cfg& c, int which) {
+    int64_t n, Nout, K;
+    fp8_pack_dims(c, which, n, Nout, K);
+    if (which == 0 || which == 2) return (size_t)(n * cdiv(Nout, 128) * G_WR_PACK * K);
+    return (size_t)(n * cdiv(Nout, 256) * G_WR_PACK * K);
 }
 
 hipError_t launch_pack_weights_fp8(const moe_cfg& c, int which, const void* w, void* out,
                                    hipStream_t st) {
+    if (which >= 4) {
+        int64_t n, Nout, K;
+        fp8_pack_dims(c, which, n, Nout, K);
+        const int64_t ntn = cdiv(Nout, 256);
+        const int64_t total = n * ntn * (K / F8_BK) * G_WR_PACK * 8;
+        if (total == 0) return hipSuccess;
+        pack_weights_fp8_t_kernel<<<(unsigned)cdiv(total, 256), 256, 0, st>>>(
+            (const uint8_t*)w, (uint4*)out, n, Nout, K, ntn);
+        return hipGetLastError();
+    }
     const bool routed = which == 0 || which == 1;
     const int64_t n = routed ? c.n_experts : 1;
     const int64_t I = routed ? c.inter : c.inter_shared;
@@ -452,6 +540,44 @@ hipError_t launch_expert_ffn_fp8(const moe_cfg& c, const FfnArgs& a, const int2*
     P.g.ntn_s = has_shared ? (int)cdiv(c.hidden, 256) : 0;
     grid = (unsigned)ffn_grid_blocks(max_r, P.g.ntn_r, max_s, P.g.ntn_s);
     ffn_gemm_fp8_kernel<1><<<grid, F8_THREADS, 0, st>>>(P);
+    return hipGetLastError();
+}
+
+hipError_t launch_fp8_gemm(const Fp8Gemm& op, const int2* tiles, const int32_t* counts,
+                           const int32_t* order, const int32_t* offsets, int N, int64_t T_shared,
+                           int64_t max_r, int64_t max_s, hipStream_t st) {
+    Fp8Params P{};
+    P.g.tiles = tiles;
+    P.g.counts = counts;
+    P.g.order = order;
+    P.g.offsets = offsets;
+    P.g.N = N;
+    P.g.T = T_shared;
+    P.g.K_r = op.K_r;
+    P.g.K_s = op.K_s;
+    P.g.Nout_r = op.Nout_r;
+    P.g.Nout_s = op.Nout_s;
+    P.g.A_r = op.A_r;
+    P.g.A_s = op.A_s;
+    P.g.B_r = op.B_r;
+    P.g.B_s = op.B_s;
+    P.g.C_r = op.C_r;
+    P.g.C_s = op.C_s;
+    P.g.E_r = op.E_r;
+    P.g.E_s = op.E_s;
+    P.xs_r = op.as_r;
+    P.xs_s = op.as_s;
+    P.ws_r = op.bs_r;
+    P.ws_s = op.bs_s;
+    P.ws_t = op.bs_t;
+    const int cols = op.mode == 1 ? 256 : 128;
+    P.g.ntn_r = (int)cdiv(op.Nout_r, cols);
+    P.g.ntn_s = T_shared > 0 ? (int)cdiv(op.Nout_s, cols) : 0;
+    const unsigned grid = (unsigned)ffn_grid_blocks(max_r, P.g.ntn_r, max_s, P.g.ntn_s);
+    if (op.mode == 2)
+        ffn_gemm_fp8_kernel<2><<<grid, F8_THREADS, 0, st>>>(P);
+    else
+        ffn_gemm_fp8_kernel<1><<<grid, F8_THREADS, 0, st>>>(P);
     return hipGetLastError();
 }
 

@@ -106,6 +106,65 @@ hipError_t launch_expert_ffn_backward(const moe_cfg& c, const FfnBwdArgs& a, voi
 hipError_t launch_ffn_save_f32(const moe_cfg& c, const void* x_perm, const void* x_sh,
                                const int32_t* offsets, const void* w13, const void* ws13,
                                void* saved, hipStream_t st);
+// One grouped FP8 GEMM launch on the forward's kernel (gemm_fp8.hip) over a
+// tile list from launch_tile_map (row tile FP8_BM): mode 2 = gate/up with a,
+// b and h kept in bf16 (C = h [rows][Nout], E = [a | b] [rows][2 Nout]),
+// mode 1 = plain rows with a bf16 output C [rows][Nout].  A: codes [rows][K]
+// with 1x128 scales as [rows][K/128]; B: packed weight codes; bs: block
+// scales, bs_t = 1 when indexed [mat][K/128][Nout/128].
+struct Fp8Gemm {
+    int mode;
+    int64_t K_r, K_s, Nout_r, Nout_s;
+    const void* A_r;
+    const void* A_s;
+    const float* as_r;
+    const float* as_s;
+    const void* B_r;
+    const void* B_s;
+    const float* bs_r;
+    const float* bs_s;
+    int bs_t;
+    void* C_r;
+    void* C_s;
+    void* E_r;
+    void* E_s;
+};
+hipError_t launch_fp8_gemm(const Fp8Gemm& op, const int2* tiles, const int32_t* counts,
+                           const int32_t* order, const int32_t* offsets, int N, int64_t T_shared,
+                           int64_t max_r, int64_t max_s, hipStream_t st);
+constexpr int FP8_BM = 320;  // FP8 GEMM row tile
+
+// FP8 backward of the experts (backward_fp8.hip)
+struct FfnBwdFp8Args {
+    const void* x;             // [T][d] bf16 layer input
+    const int32_t* src_token;  // [T*k]
+    const int32_t* offsets;    // [N+1]
+    const void* x_perm_q;      // forward's routed activation tiles: codes, scales
+    const float* x_perm_s;
+    const void* x_q;           // forward's shared-expert activation tiles
+    const float* x_s;
+    const void* w13;           // packed which 0 / 4, scales [N][2I/128][d/128]
+    const void* w13t;
+    const float* w13_s;
+    const void* w2t;           // packed which 5, scales [N][d/128][I/128]
+    const float* w2_s;
+    const void* ws13;          // shared: which 2 / 6 / 7
+    const void* ws13t;
+    const float* ws13_s;
+    const void* ws2t;
+    const float* ws2_s;
+    const void* dy_perm;
+    const void* dy_sh;
+    void* dx_perm;
+    void* dx_sh;
+    void* dw13;
+    void* dw2;
+    void* dws13;
+    void* dws2;
+};
+size_t ffn_backward_fp8_workspace_bytes(const moe_cfg& c);
+hipError_t launch_expert_ffn_backward_fp8(const moe_cfg& c, const FfnBwdFp8Args& a, void* ws,
+                                          hipStream_t st);
 hipError_t launch_combine_backward(const moe_cfg& c, const void* dout, const void* y_perm,
                                    const float* gate, const int32_t* dst_row, void* dy_perm,
                                    float* dgate, hipStream_t st);

@@ -3,10 +3,11 @@ the five calls in order on one stream.
 
     route -> permute -> expert_ffn (routed + shared) -> combine -> bias_update
 
-and, for bf16 / fp32 layers built with ``train=True``, the backward calls of
+and, for layers built with ``train=True``, the backward calls of
 include/moe_backward.h:
 
-    combine_backward -> expert_ffn_backward -> route_backward -> input_grad
+    combine_backward -> expert_ffn_backward (FP8 layers: expert_ffn_backward_fp8)
+        -> route_backward -> input_grad
 
 (DeepSeek-V3 report reading guide, xyznot.com/de, "Methode" item 2: the layer
 output h'_t, the biased Topk routing and the end-of-step bias rule.)
@@ -14,7 +15,8 @@ output h'_t, the biased Topk routing and the end-of-step bias rule.)
 import torch
 
 from . import (MoeCfg, cfg_from_dict, moe_bias_update, moe_combine, moe_combine_backward,
-               moe_expert_ffn, moe_expert_ffn_backward, moe_expert_ffn_backward_workspace_size,
+               moe_expert_ffn, moe_expert_ffn_backward, moe_expert_ffn_backward_fp8,
+               moe_expert_ffn_backward_fp8_workspace_size, moe_expert_ffn_backward_workspace_size,
                moe_expert_ffn_saved_size, moe_expert_ffn_train,
                moe_expert_ffn_workspace_size, moe_input_grad, moe_pack_weights,
                moe_packed_weights_size, moe_permute, moe_permute_workspace_size,
@@ -64,17 +66,25 @@ class MoeLayer:
             self.cfg.inter_shared = 0
         if self.fp8:
             # 128x128 block quantisation, then the GEMM's streaming order
+            # (training: also the transposed packs of the same codes for the
+            # backward's data-gradient GEMMs)
             q13, self.w13_s = quantize_weights_fp8(w13)
             q2, self.w2_s = quantize_weights_fp8(w2)
             self.w13 = pack_weights(self.cfg, 0, q13)
             self.w2 = pack_weights(self.cfg, 1, q2)
+            self.w13t_fp8 = pack_weights(self.cfg, 4, q13) if train else None
+            self.w2t_fp8 = pack_weights(self.cfg, 5, q2) if train else None
             del q13, q2
             self.ws13 = self.ws13_s = self.ws2 = self.ws2_s = None
+            self.ws13t_fp8 = self.ws2t_fp8 = None
             if has_shared:
                 qs13, self.ws13_s = quantize_weights_fp8(ws13)
                 qs2, self.ws2_s = quantize_weights_fp8(ws2)
                 self.ws13 = pack_weights(self.cfg, 2, qs13)
                 self.ws2 = pack_weights(self.cfg, 3, qs2)
+                if train:
+                    self.ws13t_fp8 = pack_weights(self.cfg, 6, qs13)
+                    self.ws2t_fp8 = pack_weights(self.cfg, 7, qs2)
         else:
             self.w13 = pack_weights(self.cfg, 0, w13)
             self.w2 = pack_weights(self.cfg, 1, w2)
@@ -110,18 +120,20 @@ class MoeLayer:
                          tuple(ws13.shape) if has_shared else None,
                          tuple(ws2.shape) if has_shared else None)
         self.w13t = self.w2t = self.ws13t = self.ws2t = None
-        if self.train:
-            if self.fp8:
-                raise ValueError("the backward covers bf16 and fp32 layers")
+        if self.train and self.fp8:
+            self.w13t, self.w2t = self.w13t_fp8, self.w2t_fp8
+            self.ws13t, self.ws2t = self.ws13t_fp8, self.ws2t_fp8
+        elif self.train:
             self.w13t = pack_weights(self.cfg, 4, w13)
             self.w2t = pack_weights(self.cfg, 5, w2)
             if has_shared:
                 self.ws13t = pack_weights(self.cfg, 6, ws13)
                 self.ws2t = pack_weights(self.cfg, 7, ws2)
         self.grads = None
-        # a training forward keeps a, b and h for the backward (else recomputed)
+        # a training forward keeps a, b and h for the backward (else recomputed;
+        # FP8 layers always recompute them on FP8)
         self.saved = None
-        if self.train and save_activations:
+        if self.train and save_activations and not self.fp8:
             self.saved = torch.empty((moe_expert_ffn_saved_size(self.cfg),), dtype=torch.uint8,
                                      device=dev)
 
@@ -184,8 +196,9 @@ class MoeLayer:
                  dz=torch.empty((T, k), **f32),
                  dcentroids=torch.empty_like(centroids),
                  dx=torch.empty((T, d), **a))
-        wsb = max(moe_expert_ffn_backward_workspace_size(self.cfg),
-                  moe_route_backward_workspace_size(self.cfg), 256)
+        ffn_ws = (moe_expert_ffn_backward_fp8_workspace_size(self.cfg) if self.fp8 else
+                  moe_expert_ffn_backward_workspace_size(self.cfg))
+        wsb = max(ffn_ws, moe_route_backward_workspace_size(self.cfg), 256)
         g["workspace"] = torch.empty((wsb,), dtype=torch.uint8, device=dev)
         return g
 
@@ -194,6 +207,14 @@ class MoeLayer:
         (dy_perm from its combine backward)."""
         g = self.grads
         shared = self.ws13t is not None
+        if self.fp8:
+            moe_expert_ffn_backward_fp8(
+                self.cfg, x, self.src_token, self.offsets, self.x_perm, self.x_perm_s,
+                self.x_q if shared else None, self.x_s if shared else None, self.w13, self.w13t,
+                self.w13_s, self.w2t, self.w2_s, self.ws13, self.ws13t, self.ws13_s, self.ws2t,
+                self.ws2_s, g["dy_perm"], dout if shared else None, g["dx_perm"], g["dx_shared"],
+                g["dw13"], g["dw2"], g["dws13"], g["dws2"], g["workspace"], stream)
+            return
         moe_expert_ffn_backward(self.cfg, self.x_perm, self.offsets, self.w13, self.w13t,
                                 self.w2t, g["dy_perm"], x if shared else None, self.ws13,
                                 self.ws13t, self.ws2t, dout if shared else None, g["dx_perm"],

@@ -36,11 +36,11 @@ def test_library_exports_every_declared_symbol():
     assert {"moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
             "moe_bias_update"} <= set(names)
     assert {"moe_probe_hbm_read", "moe_probe_mfma"} <= set(names)
-    assert {"moe_combine_backward", "moe_expert_ffn_backward", "moe_route_backward",
-            "moe_input_grad"} <= set(names)
+    assert {"moe_combine_backward", "moe_expert_ffn_backward", "moe_expert_ffn_backward_fp8",
+            "moe_route_backward", "moe_input_grad"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert moe.moe_abi_version() == 4
+    assert moe.moe_abi_version() == 5
 
 
 @host_only
@@ -182,7 +182,7 @@ def _ffn_bwd(cfg, ws_bytes=1 << 40, **over):
 @host_only
 def test_expert_ffn_backward_validation():
     assert _ffn_bwd(_cfg(dtype="bf16", fp8=True, d=256, I=128, Is=128)) == \
-        moe.MOE_ERR_UNSUPPORTED                        # no FP8 backward
+        moe.MOE_ERR_UNSUPPORTED                        # FP8: moe_expert_ffn_backward_fp8
     assert _ffn_bwd(_cfg(dtype="bf16", d=256, I=96, Is=128)) == moe.MOE_ERR_UNSUPPORTED
     assert _ffn_bwd(_cfg(), dw13=0) == moe.MOE_ERR_ARG
     assert _ffn_bwd(_cfg(), dx_shared=0) == moe.MOE_ERR_ARG    # shared expert present
@@ -237,3 +237,28 @@ def test_backward_calls_reject_bad_arguments():
     assert L.moe_input_grad(ctypes.byref(c), P(FAKE), P(FAKE * 2), P(FAKE * 3), P(FAKE * 4),
                             P(FAKE * 5), P(FAKE * 6), P(FAKE * 7), P(FAKE * 3), None) == \
         moe.MOE_ERR_ARG
+
+
+@host_only
+def test_fp8_backward_validation():
+    L = moe.lib()
+    P = ctypes.c_void_p
+    c = _cfg(dtype="bf16", fp8=True, d=256, I=128, Is=128)
+    need = moe.moe_expert_ffn_backward_fp8_workspace_size(c)
+    names = ("x", "src_token", "offsets", "x_perm", "x_perm_scale", "x_q", "x_scale", "w13",
+             "w13t", "w13_scale", "w2t", "w2_scale", "ws13", "ws13t", "ws13_scale", "ws2t",
+             "ws2_scale", "dy_perm", "dy_shared", "dx_perm", "dx_shared", "dw13", "dw2", "dws13",
+             "dws2", "workspace")
+    call = lambda cfg, ws=need, **o: L.moe_expert_ffn_backward_fp8(
+        ctypes.byref(cfg), *(P(o.get(n, FAKE * (i + 1))) if o.get(n, 1) else None
+                             for i, n in enumerate(names)), ws, None)
+    assert call(c, ws=need - 1) == moe.MOE_ERR_WORKSPACE
+    assert moe.lib().moe_last_error().decode().startswith("moe_expert_ffn_backward_fp8")
+    assert call(c, dw13=0) == moe.MOE_ERR_ARG
+    assert call(c, x_q=0) == moe.MOE_ERR_ARG          # the shared expert's tiles
+    assert call(c, w13_scale=0) == moe.MOE_ERR_ARG
+    assert call(_cfg(dtype="bf16", d=256, I=128, Is=128)) == moe.MOE_ERR_UNSUPPORTED  # not FP8
+    assert call(_cfg(dtype="bf16", fp8=True, d=256, I=96, Is=128)) == moe.MOE_ERR_UNSUPPORTED
+    # transposed FP8 packs: rows of 256 columns of the stored matrix
+    assert moe.moe_packed_weights_size(c, 4) == c.n_experts * 1 * 256 * 2 * 128
+    assert moe.moe_packed_weights_size(c, 5) == c.n_experts * 1 * 256 * 256
