@@ -11,11 +11,11 @@ with fused SwiGLU, then down), timed live with HIP events on the stream they
 run on, against the roofline (HBM or MFMA) that bounds its algorithmic work; `cpu_baseline` is the CPU oracle timed on a bounded sample of the same
 workload on this host.
 
---backward measures the layer's backward instead (bf16 / fp32 workloads): a
-step is the four backward calls -- combine backward, expert FFN backward (two
-dgrad and two wgrad GEMMs, reading the a, b, h the training forward kept),
-gate/centroid backward, input gradient -- on the state of one training forward
-step, reported as its own metric.
+--backward measures the layer's backward instead: a step is the four backward
+calls -- combine backward, expert FFN backward (two dgrad and two wgrad GEMMs,
+reading the a, b, h the training forward kept; FP8 workloads recompute them on
+FP8 and quantise every GEMM operand), gate/centroid backward, input gradient --
+on the state of one training forward step, reported as its own metric.
 """
 import argparse
 import json
@@ -65,9 +65,9 @@ def ffn_bytes(c):
 def ffn_bwd_flops(c, recompute=False):
     """dgrad down (2 M d I), dgrad up (4 M d I), wgrad down (2 M d I), wgrad up
     (4 M d I) for M = T*k routed rows, the same for the shared expert over T
-    rows, and with recompute also a, b (4 M d I)"""
+    rows, and with recompute (always on FP8) also a, b (4 M d I)"""
     T, k, d, I, Is = c["T"], c["k"], c["d"], c["I"], c["Is"]
-    f = 16.0 if recompute else 12.0
+    f = 16.0 if (recompute or c.get("fp8")) else 12.0
     return f * T * k * d * I + f * T * d * Is
 
 
@@ -77,6 +77,8 @@ def ffn_bwd_bytes(c, recompute=False):
     W13^T (the dgrads), and W13 with recompute; x_perm, dY, a/b, h, da/db, dX
     and the weight gradients as each GEMM reads or writes them."""
     T, k, d, I, Is, N = c["T"], c["k"], c["d"], c["I"], c["Is"], c["N"]
+    if c.get("fp8"):
+        return ffn_bwd_bytes_fp8(c)
     def one(M, I, n):
         w = 2.0 * n * (d * I + 2 * I * d)                        # W2^T, W13^T read
         rec = 0.0
@@ -88,6 +90,30 @@ def ffn_bwd_bytes(c, recompute=False):
         wgd = 2.0 * (M * d + M * I) + 2.0 * n * d * I            # dY, h in; dW2 out
         wgu = 2.0 * (M * 2 * I + M * d) + 2.0 * n * 2 * I * d    # da/db, x in; dW13 out
         return w + rec + dgd + dgu + wgd + wgu
+    return one(T * k, I, N) + (one(T, Is, 1) if Is > 0 else 0.0)
+
+
+def ffn_bwd_bytes_fp8(c):
+    """Algorithmic HBM bytes of one moe_expert_ffn_backward_fp8 call: each GEMM
+    reads its E4M3 operands (codes, plus 4 bytes of scale per 128 codes) and
+    writes its result once, and each quantised operand is produced once from its
+    bf16 tensor:  recompute (W13, x codes -> a, b, h bf16), dY row tiles, dgrad
+    down (W2^T, dY codes -> dh), SwiGLU' (dh, a, b -> [da db] bf16 and codes),
+    dgrad up (W13^T, [da db] codes -> dX), the row-direction tiles of dY, h,
+    [da db] and x (bf16 in, codes out), and the weight-gradient GEMMs (codes
+    in, dW2 and dW13 bf16 out)."""
+    T, k, d, I, Is, N = c["T"], c["k"], c["d"], c["I"], c["Is"], c["N"]
+    q = 1 + 4.0 / 128  # code + scale share
+    def one(M, I, n):
+        w = n * (2 * I * d + d * I + 2 * I * d) * q                 # W13, W2^T, W13^T codes
+        b = q * M * d + 2.0 * M * 3 * I                             # recompute: x in, a/b/h out
+        b += 2.0 * M * d + q * M * d                                # dY row tiles
+        b += q * M * d + 2.0 * M * I                                # dgrad down
+        b += 2.0 * M * 3 * I + 2.0 * M * 2 * I + q * M * 2 * I      # SwiGLU'
+        b += q * M * 2 * I + 2.0 * M * d                            # dgrad up
+        b += 2.0 * M * (2 * d + 3 * I) + q * M * (2 * d + 3 * I)    # row-direction tiles
+        b += q * M * (2 * d + 3 * I) + 2.0 * n * 3 * I * d          # weight gradients
+        return w + b
     return one(T * k, I, N) + (one(T, Is, 1) if Is > 0 else 0.0)
 
 
@@ -127,7 +153,7 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 def gemm_source_hash(backward=False):
     import hashlib
     h = hashlib.sha256()
-    for f in GEMM_SOURCES + (("gemm_bwd.hip",) if backward else ()):
+    for f in GEMM_SOURCES + (("gemm_bwd.hip", "backward_fp8.hip") if backward else ()):
         with open(os.path.join(ROOT, "sparse_moe_layer_bias_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -185,7 +211,11 @@ def traffic_summary(fetch_csv, write_csv, workload, backward=False):
     lines = []
     # the kernels of one call; each averaged over its last 3 dispatches, the
     # 3 measured calls (the backward's setup also runs forward kernels)
-    if backward:  # with the training forward's saved activations: no recompute (mode 2)
+    if backward and "fp8" in workload:  # every kernel of moe_expert_ffn_backward_fp8
+        ffn = [k for k in fetch if any(n in k for n in (
+            "wgrad_fp8", "ffn_tile_map", "ffn_gemm_fp8_kernel<1>", "ffn_gemm_fp8_kernel<2>",
+            "quant_rows_bf16", "swiglu_bwd_fp8", "pad_offsets", "quant_cols_t"))]
+    elif backward:  # with the training forward's saved activations: no recompute (mode 2)
         ffn = [k for k in fetch if "wgrad" in k or "ffn_tile_map" in k or
                any("ffn_gemm_bf16_kernel<%d," % m in k for m in (1, 3))]
     else:
@@ -410,7 +440,14 @@ def cpu_baseline_backward(cfg, dev, log):
     t0 = time.perf_counter()
     dyp, dg = orc.combine_backward(dout, yp, r["gate"], dst)
     t1 = time.perf_counter()
-    dA, _, _ = orc.swiglu_ffn_backward(xs[:R], w13, w2, dout[:R])
+    if cfg.get("fp8"):
+        xq, xsc = orc.quant_act_fp8(xs[:R])
+        q13, s13 = orc.quant_weight_fp8(w13)
+        q2, s2 = orc.quant_weight_fp8(w2)
+        t1 = time.perf_counter()
+        dA, _, _ = orc.swiglu_ffn_backward_fp8(xq, xsc, xs[:R], q13, s13, q2, s2, dout[:R])
+    else:
+        dA, _, _ = orc.swiglu_ffn_backward(xs[:R], w13, w2, dout[:R])
     t2 = time.perf_counter()
     dz = orc.route_backward(r["scores"], r["idx"], dg)
     orc.centroid_grad(xs, r["idx"], dz, N)
@@ -465,7 +502,7 @@ def run_backward(args, cfg, dev, log):
     nbytes = ffn_bwd_bytes(cfg)
     ffn_s = stage_ms["expert_ffn_backward"] / 1e3
     achieved = flops / ffn_s
-    peak = PEAK["bf16"]
+    peak = PEAK["fp8" if cfg.get("fp8") else "bf16"]
     hbm_bound = nbytes / PEAK["hbm"] > flops / peak
     if hbm_bound:
         roof = {"bound": "hbm", "achieved": nbytes / ffn_s / 1e9, "peak": PEAK["hbm"] / 1e9,
@@ -473,8 +510,11 @@ def run_backward(args, cfg, dev, log):
     else:
         roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12,
                 "unit": "TFLOP/s", "frac": achieved / peak}
-    roof.update({"kernel": "expert FFN backward GEMMs (dgrad down+SwiGLU', dgrad up, wgrad "
-                           "down, wgrad up; a, b, h saved by the training forward)",
+    roof.update({"kernel": ("expert FFN backward, FP8: a, b, h recompute, dgrad down, "
+                            "SwiGLU' + 1x128 tiles, dgrad up, 128x1 row-direction tiles, "
+                            "wgrad down and up" if cfg.get("fp8") else
+                            "expert FFN backward GEMMs (dgrad down+SwiGLU', dgrad up, wgrad "
+                            "down, wgrad up; a, b, h saved by the training forward)"),
                  "traffic": recorded_traffic(args.workload, backward=True),
                  "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
                  "mfma_tflops": achieved / 1e12, "mfma_frac": achieved / peak})
@@ -489,7 +529,7 @@ def run_backward(args, cfg, dev, log):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg["dtype"],
+        "dtype": "fp8" if cfg.get("fp8") else cfg["dtype"],
         "data": "synthetic",
         "config": {"workload": "%s backward: T=%d d=%d, %d routed experts top-%d%s + 1 "
                                "shared, SwiGLU I=%d, %s" %
@@ -543,9 +583,6 @@ def main():
     T = cfg["T"]
     log("generating inputs for", args.workload, cfg)
     dev = moe_inputs.make_layer_inputs(cfg, args.seed, "cuda")
-    if args.backward and cfg.get("fp8"):
-        log("the backward covers bf16 and fp32 layers")
-        sys.exit(2)
     if args.backward and not args.traffic_run:
         run_backward(args, cfg, dev, log)
         return

@@ -99,3 +99,41 @@ def test_fp8_transposed_packs_are_the_transposed_codes():
     direct = pack_weights(c_t, 1, q2.transpose(1, 2).contiguous())
     torch.cuda.synchronize()
     assert torch.equal(layer.w2t, direct)
+
+
+def test_v3_fp8_backward_one_expert_and_sampled_tokens(orc):
+    """DeepSeek-V3-shaped FP8 layer, the launches the benchmark times: the
+    full weight gradients and row gradients of the least-loaded expert, and the
+    shared expert's input gradient of sampled tokens, against the oracle."""
+    cfg = dict(moe_inputs.CONFIGS["v3_fp8"])
+    T, N, k, d = cfg["T"], cfg["N"], cfg["k"], cfg["d"]
+    log("generating V3-shaped FP8 inputs on the GPU")
+    dev = moe_inputs.make_layer_inputs(cfg, 0, "cuda")
+    dout = moe_inputs.make_upstream_grad(cfg, 0, "cuda")
+    layer = MoeLayer(cfg, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"], train=True)
+    layer.forward(dev["x"], dev["centroids"], dev["bias"].clone())
+    g = layer.backward(dout, dev["x"], dev["centroids"])
+    torch.cuda.synchronize()
+    log("V3 FP8 backward done")
+    off = moe_inputs.to_host(layer.offsets).astype(np.int64)
+    counts = np.diff(off)
+    e = int(np.argmin(np.where(counts > 0, counts, 1 << 30)))
+    a, b = int(off[e]), int(off[e + 1])
+    src = moe_inputs.to_host(layer.src_token)[a:b]
+    xh = moe_inputs.to_host(dev["x"])
+    xq = moe_inputs.to_host(layer.x_perm[a:b])
+    xs = moe_inputs.to_host(layer.x_perm_s[a:b])
+    assert np.array_equal(xq, orc.quant_act_fp8(xh[src])[0])   # the forward's tiles
+    dy = moe_inputs.to_host(g["dy_perm"][a:b])
+    q13, s13 = orc.quant_weight_fp8(moe_inputs.to_host(dev["w13"][e]))
+    q2, s2 = orc.quant_weight_fp8(moe_inputs.to_host(dev["w2"][e]))
+    log("oracle FP8 backward of expert", e, "with", b - a, "rows")
+    dA, dw13, dw2 = orc.swiglu_ffn_backward_fp8(xq, xs, xh[src], q13, s13, q2, s2, dy)
+    assert_close_fp8(moe_inputs.to_host(g["dx_perm"][a:b]), dA, "dx_perm rows of expert %d" % e,
+                     elem=3.0)
+    assert_close_fp8_grad(moe_inputs.to_host(g["dw13"][e]), dw13, "dw13 of expert %d" % e)
+    assert_close_fp8_grad(moe_inputs.to_host(g["dw2"][e]), dw2, "dw2 of expert %d" % e)
+    # an expert without rows gets zeros
+    if np.any(counts == 0):
+        z = int(np.nonzero(counts == 0)[0][0])
+        assert not torch.any(g["dw13"][z]) and not torch.any(g["dw2"][z])
