@@ -13,10 +13,11 @@
 // a, b and h come from an FP8 gate/up recompute (mode 2), kept in bf16; dh, da,
 // db and every output are rounded to bf16.
 //
-// The row-direction tiles are written transposed: feature f of group g holds
-// its codes at [f][poff[g] + row] (poff = prefix of the groups' row counts
-// rounded up to 128, the shared expert last), so that the weight-gradient
-// GEMM reads both operands as rows along its contraction, like the forward.
+// The row-direction tiles are written transposed and block-major: the codes of
+// 128-row block pb (blocks numbered along poff = prefix of the groups' row
+// counts rounded up to 128, the shared expert last) are [pb][feature][128], so
+// that the weight-gradient GEMM reads each operand tile of a block as one
+// contiguous run of 128-byte rows along its contraction.
 #include "gemm_common.h"
 
 namespace moe {
@@ -156,9 +157,9 @@ struct ColQuant {
     int64_t S;                 // shared rows (0: none)
     int64_t C_r, C_s;          // features (columns) of routed / shared rows
     int64_t ld_r, ld_s;
-    uint8_t* out;              // [feature][P_ld] codes
-    float* out_s;              // [feature][P_ld/128] scales
-    int64_t P_ld;
+    uint8_t* out;              // [block][F][128] codes
+    float* out_s;              // [block][F] scales
+    int64_t F;                 // features per block in out (>= C_r, C_s)
 };
 
 // One 128-row block of one group x 64 features: the column amax over the
@@ -226,21 +227,21 @@ __global__ void __launch_bounds__(256) quant_cols_t_kernel(ColQuant p) {
         }
         code[k] = wv;
     }
-    uint8_t* o = p.out + (c0 + col) * p.P_ld + row0 + part * 32;
+    uint8_t* o = p.out + ((row0 / 128) * p.F + c0 + col) * 128 + part * 32;
     *(uint4*)o = make_uint4(code[0], code[1], code[2], code[3]);
     *(uint4*)(o + 16) = make_uint4(code[4], code[5], code[6], code[7]);
-    if (part == 0) p.out_s[(c0 + col) * (p.P_ld / 128) + row0 / 128] = scale;
+    if (part == 0) p.out_s[(row0 / 128) * p.F + c0 + col] = scale;
 }
 
 // ---------------------------------------------------------------- weight gradients
 
 struct WgFp8 {
-    const uint8_t* At;  // [rowsA][P_ld] codes (A^T: output rows along the contraction)
-    const float* AtS;   // [rowsA][P_ld/128]
-    const uint8_t* Bt;  // [rowsB][P_ld]
+    const uint8_t* At;  // [block][FA][128] codes (A^T: output rows along the contraction)
+    const float* AtS;   // [block][FA]
+    const uint8_t* Bt;  // [block][FB][128]
     const float* BtS;
     const int32_t* poff;
-    int64_t P_ld;
+    int64_t FA, FB;     // features per block of At, Bt
     int N;
     int has_shared;
     int64_t rowsA_r, rowsB_r, rowsA_s, rowsB_s;
@@ -250,43 +251,111 @@ struct WgFp8 {
 
 // out[n][c] = sum over the group's 128-row blocks u of
 //   (sA[n,u] sB[c,u]) * sum_{rows of u} qA[n,row] qB[c,row]
-// One workgroup = 128 x 128 outputs of one group, 4 waves of 64 x 64 (2 x 2
-// blocks of 32x32x64 MFMAs).  Per block the two K halves accumulate the code
-// products into a fresh partial (MFMA scale operands 1.0), which is then
-// promoted into the fp32 result with the product of the two fp32 scales.
-__global__ void __launch_bounds__(256) wgrad_fp8_kernel(WgFp8 p) {
-    __shared__ __attribute__((aligned(16))) uint8_t sA[128 * 128];
-    __shared__ __attribute__((aligned(16))) uint8_t sB[128 * 128];
-    __shared__ __attribute__((aligned(16))) float scA[128];
-    __shared__ __attribute__((aligned(16))) float scB[128];
-    const int64_t tr = (p.rowsA_r / 128) * (p.rowsB_r / 128);
+// One workgroup (8 waves) = one group and 128 output rows n, sweeping the
+// output columns c in tiles of 256: a flattened loop over steps (column tile,
+// block u).  A step's operands (16 KB of A^T and 32 KB of B^T codes, their
+// scales) are copied global -> LDS by buffer DMA into one of 3 stages, two
+// steps ahead (the swizzle goes through the source addresses; B rows past the
+// end are clamped to the last row -- they only feed output columns that are
+// not stored).  Wave (wa, wb) owns rows wa*64.. and columns wb*64.. of the
+// tile as 2 x 2 blocks of 32x32x64 MFMAs with the B^T rows as the first
+// operand, so that a lane holds one output row n and 4 consecutive columns
+// per register group.  Per block the two K halves accumulate
+// the code products into a fresh partial (MFMA scale operands 1.0), promoted
+// into the fp32 result with the product of the two fp32 scales.  A finished
+// tile is stored at the start of the next step, before that step's copies are
+// issued, so that the newest vector-memory operations in flight at every wait
+// are always copies (loads complete in order among themselves).
+constexpr int WG_THREADS = 512;
+constexpr int WG_TB = 256;                       // output columns per tile
+constexpr int WG_NS = 3;                         // LDS stages
+constexpr int WG_A = 128 * 128, WG_B = WG_TB * 128;
+constexpr int WG_STAGE = WG_A + WG_B + 4 * (128 + WG_TB);
+
+__global__ void __launch_bounds__(WG_THREADS, 1) wgrad_fp8_kernel(WgFp8 p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[WG_NS * WG_STAGE];
+    const int64_t tar = p.rowsA_r / 128;
     const int64_t unit = blockIdx.x;
     int g;
-    int64_t ti, rowsA, rowsB;
+    int64_t ta, rowsA, rowsB;
     uint16_t* out;
-    if (unit < (int64_t)p.N * tr) {
-        g = (int)(unit / tr);
-        ti = unit % tr;
+    if (unit < (int64_t)p.N * tar) {
+        g = (int)(unit / tar);
+        ta = unit % tar;
         rowsA = p.rowsA_r;
         rowsB = p.rowsB_r;
         out = p.out_r + (int64_t)g * rowsA * rowsB;
     } else {
         if (!p.has_shared) return;
         g = p.N;
-        ti = unit - (int64_t)p.N * tr;
+        ta = unit - (int64_t)p.N * tar;
         rowsA = p.rowsA_s;
         rowsB = p.rowsB_s;
-        if (ti >= (rowsA / 128) * (rowsB / 128)) return;
+        if (ta >= rowsA / 128) return;
         out = p.out_s;
     }
-    const int64_t ta = ti / (rowsB / 128), tb = ti % (rowsB / 128);
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wa = wave & 1, wb = wave >> 1, h = lane >> 5;
     const int64_t P0 = p.poff[g];
     const int nb = (int)((p.poff[g + 1] - P0) / 128);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wa = wave & 1, wb = wave >> 1, h = lane >> 5;
-    const int64_t sld = p.P_ld / 128;
+    const int ntb = (int)((rowsB + WG_TB - 1) / WG_TB);
+    const int64_t pb0 = P0 / 128;  // the group's first block
 
-    f32x16_t acc[2][2];
+    if (nb == 0) {  // an expert without rows: zero gradient
+        for (int64_t i = t; i < 128 * rowsB / 8; i += WG_THREADS) {
+            const int64_t r = i / (rowsB / 8), c8 = i % (rowsB / 8);
+            *(uint4*)(out + (ta * 128 + r) * rowsB + c8 * 8) = make_uint4(0, 0, 0, 0);
+        }
+        return;
+    }
+
+    // buffer descriptors over the group's blocks (out-of-range lanes read 0)
+    const i32x4_t rA = make_rsrc(p.At + pb0 * p.FA * 128, (int64_t)nb * p.FA * 128);
+    const i32x4_t rB = make_rsrc(p.Bt + pb0 * p.FB * 128, (int64_t)nb * p.FB * 128);
+    const i32x4_t rAs = make_rsrc(p.AtS + pb0 * p.FA, (int64_t)nb * p.FA * 4);
+    const i32x4_t rBs = make_rsrc(p.BtS + pb0 * p.FB, (int64_t)nb * p.FB * 4);
+    // 1 KB copies: 8 rows of 128 bytes; lane l fills row 8k + l/8, slot l%8
+    // with the logical chunk that the swizzle puts there
+    const int crow = lane >> 3, cslot = lane & 7;
+    const int cnt = 2 + 4 + (wave < 6 ? 1 : 0);  // copies per wave and step
+    auto issue = [&](int s, int buf) {
+        const int tb = s / nb, u = s % nb;
+        uint8_t* st = smem + buf * WG_STAGE;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int k = wave + 8 * j, r = 8 * k + crow;
+            const uint32_t voff = (uint32_t)(((ta * 128 + r) * 128) + sub_chunk8(r, cslot) * 16);
+            dma_to_lds<16>(rA, st + k * 1024, voff, (uint32_t)(u * p.FA * 128));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int k = wave + 8 * j, r = 8 * k + crow;
+            int64_t br = (int64_t)tb * WG_TB + r;
+            br = br < rowsB ? br : rowsB - 1;
+            const uint32_t voff = (uint32_t)(br * 128 + sub_chunk8(r, cslot) * 16);
+            dma_to_lds<16>(rB, st + WG_A + k * 1024, voff, (uint32_t)(u * p.FB * 128));
+        }
+        float* sc = (float*)(st + WG_A + WG_B);
+        if (wave < 2) {
+            const uint32_t voff = (uint32_t)((ta * 128 + wave * 64 + lane) * 4);
+            dma_to_lds<4>(rAs, sc + wave * 64, voff, (uint32_t)(u * p.FA * 4));
+        } else if (wave < 6) {
+            int64_t br = (int64_t)tb * WG_TB + (wave - 2) * 64 + lane;
+            br = br < rowsB ? br : rowsB - 1;
+            dma_to_lds<4>(rBs, sc + 128 + (wave - 2) * 64, (uint32_t)(br * 4),
+                          (uint32_t)(u * p.FB * 4));
+        }
+    };
+    auto frag = [&](const uint8_t* base, int r, int q) {
+        const uint4 lo = *(const uint4*)(base + r * 128 + sub_chunk8(r, 4 * q + 2 * h) * 16);
+        const uint4 hi = *(const uint4*)(base + r * 128 + sub_chunk8(r, 4 * q + 2 * h + 1) * 16);
+        return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
+
+    f32x16_t acc[2][2];  // [A block i][B block j]; lane: row n, 16 columns c
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -294,78 +363,102 @@ __global__ void __launch_bounds__(256) wgrad_fp8_kernel(WgFp8 p) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
     const f32x16_t zero = acc[0][0];
-
-    for (int u = 0; u < nb; ++u) {
-        __syncthreads();  // the previous block is read out of LDS
+    // store the finished column tile tb and restart: staged through the free
+    // LDS stage `buf` in two halves of 128 columns (waves wb < 2, then wb >= 2)
+    // so that every output row leaves as contiguous 256-byte runs (direct
+    // stores from the accumulator layout would write 16-byte pieces of 32
+    // rows per instruction)
+    constexpr int SP = 128 + 8;  // padded staging row (elements)
+    auto flush = [&](int tb, int buf) {
+        uint16_t* stg = (uint16_t*)(smem + buf * WG_STAGE);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int idx = threadIdx.x + 256 * k;
-            const int r = idx >> 3, ch = idx & 7;
-            const int64_t col = P0 + (int64_t)u * 128 + ch * 16;
-            const uint4 va = *(const uint4*)(p.At + (ta * 128 + r) * p.P_ld + col);
-            const uint4 vb = *(const uint4*)(p.Bt + (tb * 128 + r) * p.P_ld + col);
-            *(uint4*)(sA + r * 128 + sub_chunk8(r, ch) * 16) = va;
-            *(uint4*)(sB + r * 128 + sub_chunk8(r, ch) * 16) = vb;
+        for (int half = 0; half < 2; ++half) {
+            if ((wb >> 1) == half) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int row = wa * 64 + i * 32 + (lane & 31);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+#pragma unroll
+                        for (int g4 = 0; g4 < 4; ++g4) {
+                            const int col = (wb & 1) * 64 + j * 32 + 8 * g4 + 4 * h;
+                            *(uint2*)(stg + row * SP + col) = make_uint2(
+                                pack_bf16x2(acc[i][j][4 * g4], acc[i][j][4 * g4 + 1]),
+                                pack_bf16x2(acc[i][j][4 * g4 + 2], acc[i][j][4 * g4 + 3]));
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) acc[i][j][4 * g4 + e] = 0.0f;
+                        }
+                }
+            }
+            lds_barrier();
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int idx = t + WG_THREADS * k, row = idx >> 4, c16 = idx & 15;
+                const int64_t col = (int64_t)tb * WG_TB + half * 128 + c16 * 8;
+                if (col < rowsB)
+                    *(uint4*)(out + (ta * 128 + row) * rowsB + col) =
+                        *(const uint4*)(stg + row * SP + c16 * 8);
+            }
+            lds_barrier();  // the staging rows are read before they are reused
         }
-        if (threadIdx.x < 128)
-            scA[threadIdx.x] = p.AtS[(ta * 128 + threadIdx.x) * sld + P0 / 128 + u];
-        else
-            scB[threadIdx.x - 128] = p.BtS[(tb * 128 + threadIdx.x - 128) * sld + P0 / 128 + u];
-        __syncthreads();
+    };
+
+    const int steps = ntb * nb;
+#pragma unroll
+    for (int s = 0; s < WG_NS - 1; ++s)
+        if (s < steps) issue(s, s);
+    int pend = -1;  // a finished column tile not stored yet
+    for (int s = 0; s < steps; ++s) {
+        const int after = steps - 1 - s < WG_NS - 2 ? steps - 1 - s : WG_NS - 2;
+        vm_wait_n(after * cnt);
+        lds_barrier();  // step s landed for every wave; the stage of s-1 is free
+        if (pend >= 0) {  // the stage of step s-1 is free until this step's copies
+            flush(pend, (s + WG_NS - 1) % WG_NS);
+            pend = -1;
+        }
+        if (s + WG_NS - 1 < steps) issue(s + WG_NS - 1, (s + WG_NS - 1) % WG_NS);
+        const uint8_t* sA = smem + (s % WG_NS) * WG_STAGE;
+        const uint8_t* sB = sA + WG_A;
+        const float* scA = (const float*)(sB + WG_B);
+        const float* scB = scA + 128;
         f32x16_t part[2][2];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             i32x8_t af[2], bf[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const int ra = wa * 64 + i * 32 + (lane & 31);
-                const int rb = wb * 64 + i * 32 + (lane & 31);
-                const uint8_t* pa = sA + ra * 128;
-                const uint8_t* pb = sB + rb * 128;
-                const uint4 a0 = *(const uint4*)(pa + sub_chunk8(ra, 4 * q + 2 * h) * 16);
-                const uint4 a1 = *(const uint4*)(pa + sub_chunk8(ra, 4 * q + 2 * h + 1) * 16);
-                const uint4 b0 = *(const uint4*)(pb + sub_chunk8(rb, 4 * q + 2 * h) * 16);
-                const uint4 b1 = *(const uint4*)(pb + sub_chunk8(rb, 4 * q + 2 * h + 1) * 16);
-                af[i] = i32x8_t{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
-                                (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-                bf[i] = i32x8_t{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
-                                (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+                af[i] = frag(sA, wa * 64 + i * 32 + (lane & 31), q);
+                bf[i] = frag(sB, wb * 64 + i * 32 + (lane & 31), q);
             }
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        af[i], bf[j], q == 0 ? zero : part[i][j], 0, 0, 0, 127, 0, 127);
+                        bf[j], af[i], q == 0 ? zero : part[i][j], 0, 0, 0, 127, 0, 127);
         }
-        // promotion: lane holds column c = lane%32 of its 32x32 block and rows
-        // 8 (v/4) + 4 (lane/32) + v%4
+        // promotion: lane holds output row n = lane%32 of A block i and
+        // columns 8 (v/4) + 4 (lane/32) + v%4 of B block j
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const float sb = scB[wb * 64 + j * 32 + (lane & 31)];
+        for (int i = 0; i < 2; ++i) {
+            const float sa = scA[wa * 64 + i * 32 + (lane & 31)];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
-                    const float4 sa = *(const float4*)(scA + wa * 64 + i * 32 + 8 * g4 + 4 * h);
-                    acc[i][j][4 * g4 + 0] += part[i][j][4 * g4 + 0] * (sa.x * sb);
-                    acc[i][j][4 * g4 + 1] += part[i][j][4 * g4 + 1] * (sa.y * sb);
-                    acc[i][j][4 * g4 + 2] += part[i][j][4 * g4 + 2] * (sa.z * sb);
-                    acc[i][j][4 * g4 + 3] += part[i][j][4 * g4 + 3] * (sa.w * sb);
+                    const float4 sb = *(const float4*)(scB + wb * 64 + j * 32 + 8 * g4 + 4 * h);
+                    acc[i][j][4 * g4 + 0] += part[i][j][4 * g4 + 0] * (sa * sb.x);
+                    acc[i][j][4 * g4 + 1] += part[i][j][4 * g4 + 1] * (sa * sb.y);
+                    acc[i][j][4 * g4 + 2] += part[i][j][4 * g4 + 2] * (sa * sb.z);
+                    acc[i][j][4 * g4 + 3] += part[i][j][4 * g4 + 3] * (sa * sb.w);
                 }
         }
+        if (s % nb == nb - 1) pend = s / nb;
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t c = tb * 128 + wb * 64 + j * 32 + (lane & 31);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t n = ta * 128 + wa * 64 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                out[n * rowsB + c] = f32_to_bf16(acc[i][j][v]);
-            }
-        }
+    if (pend >= 0) {
+        lds_barrier();  // every wave is done with the last step's stage
+        flush(pend, (steps - 1) % WG_NS);
+    }
 }
 
 // ---------------------------------------------------------------- driver
@@ -468,6 +561,7 @@ hipError_t launch_expert_ffn_backward_fp8(const moe_cfg& c, const FfnBwdFp8Args&
     const int64_t Is = c.inter_shared, N = c.n_experts;
     const bool has_shared = Is > 0 && T > 0;
     const int64_t S = has_shared ? T : 0;
+    const int64_t Im = I > Is ? I : Is;
     BwdFp8Ws w = carve_bwd_fp8(c, ws, nullptr);
     const int64_t max_r = bwd_fp8_max_r(c), max_s = has_shared ? bwd_fp8_max_s(c) : 0;
     hipError_t e;
@@ -549,7 +643,8 @@ hipError_t launch_expert_ffn_backward_fp8(const moe_cfg& c, const FfnBwdFp8Args&
     pad_offsets_kernel<<<1, 64, 0, st>>>(a.offsets, (int)N, S, w.poff);
     const unsigned pblocks = (unsigned)(w.P_ld / 128);
     auto cols = [&](const void* sr, const void* ss, const int32_t* gather, int64_t Cr,
-                    int64_t Cs, int64_t ldr, int64_t lds, uint8_t* out, float* outs) {
+                    int64_t Cs, int64_t ldr, int64_t lds, int64_t F, uint8_t* out,
+                    float* outs) {
         ColQuant p{};
         p.src_r = (const uint16_t*)sr;
         p.src_s = (const uint16_t*)ss;
@@ -564,27 +659,29 @@ hipError_t launch_expert_ffn_backward_fp8(const moe_cfg& c, const FfnBwdFp8Args&
         p.ld_s = lds;
         p.out = out;
         p.out_s = outs;
-        p.P_ld = w.P_ld;
+        p.F = F;
         const int64_t cm = Cr > Cs ? Cr : Cs;
         quant_cols_t_kernel<<<dim3(pblocks, (unsigned)cdiv(cm, 64)), 256, 0, st>>>(p);
     };
     if (R + S > 0) {
-        cols(a.dy_perm, a.dy_sh, nullptr, d, d, d, d, w.gT, w.gTs);
-        cols(w.h_r, w.h_s, nullptr, I, Is, I, Is, w.hT, w.hTs);
-        cols(w.dab_r, w.dab_s, nullptr, 2 * I, 2 * Is, 2 * I, 2 * Is, w.tT, w.tTs);
-        cols(a.x, a.x, a.src_token, d, d, d, d, w.xT, w.xTs);
+        cols(a.dy_perm, a.dy_sh, nullptr, d, d, d, d, d, w.gT, w.gTs);
+        cols(w.h_r, w.h_s, nullptr, I, Is, I, Is, Im, w.hT, w.hTs);
+        cols(w.dab_r, w.dab_s, nullptr, 2 * I, 2 * Is, 2 * I, 2 * Is, 2 * Im, w.tT, w.tTs);
+        cols(a.x, a.x, a.src_token, d, d, d, d, d, w.xT, w.xTs);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // 6. dW2 = dY^T h and dW13 = [da db]^T X for every expert (zeros without rows)
-    auto wgrad = [&](const uint8_t* At, const float* AtS, const uint8_t* Bt, const float* BtS,
-                     int64_t rAr, int64_t rBr, int64_t rAs, int64_t rBs, void* outr, void* outs) {
+    auto wgrad = [&](const uint8_t* At, const float* AtS, int64_t FA, const uint8_t* Bt,
+                     const float* BtS, int64_t FB, int64_t rAr, int64_t rBr, int64_t rAs,
+                     int64_t rBs, void* outr, void* outs) {
         WgFp8 p{};
         p.At = At;
         p.AtS = AtS;
         p.Bt = Bt;
         p.BtS = BtS;
         p.poff = w.poff;
-        p.P_ld = w.P_ld;
+        p.FA = FA;
+        p.FB = FB;
         p.N = (int)N;
         p.has_shared = has_shared ? 1 : 0;
         p.rowsA_r = rAr;
@@ -593,12 +690,11 @@ hipError_t launch_expert_ffn_backward_fp8(const moe_cfg& c, const FfnBwdFp8Args&
         p.rowsB_s = rBs;
         p.out_r = (uint16_t*)outr;
         p.out_s = (uint16_t*)outs;
-        const int64_t units = N * (rAr / 128) * (rBr / 128) +
-                              (has_shared ? (rAs / 128) * (rBs / 128) : 0);
-        if (units > 0) wgrad_fp8_kernel<<<(unsigned)units, 256, 0, st>>>(p);
+        const int64_t units = N * (rAr / 128) + (has_shared ? rAs / 128 : 0);
+        if (units > 0) wgrad_fp8_kernel<<<(unsigned)units, WG_THREADS, 0, st>>>(p);
     };
-    wgrad(w.gT, w.gTs, w.hT, w.hTs, d, I, d, Is, a.dw2, a.dws2);
-    wgrad(w.tT, w.tTs, w.xT, w.xTs, 2 * I, d, 2 * Is, d, a.dw13, a.dws13);
+    wgrad(w.gT, w.gTs, d, w.hT, w.hTs, Im, d, I, d, Is, a.dw2, a.dws2);
+    wgrad(w.tT, w.tTs, 2 * Im, w.xT, w.xTs, d, 2 * I, d, 2 * Is, d, a.dw13, a.dws13);
     return hipGetLastError();
 }
 

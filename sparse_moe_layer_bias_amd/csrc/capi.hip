@@ -461,8 +461,15 @@ int moe_expert_ffn_backward_fp8(const moe_cfg* cfg, const void* x, const int32_t
     if (cfg->gemm_dtype != MOE_FP8_E4M3 || cfg->act_dtype != MOE_BF16)
         return fail(MOE_ERR_UNSUPPORTED, "%s: needs gemm_dtype FP8_E4M3 and act_dtype BF16", fn);
     const int64_t T = cfg->tokens, R = T * cfg->top_k;
-    if (R + 128 * (cfg->n_experts + 2) + T >= ((int64_t)1 << 31))
-        return fail(MOE_ERR_UNSUPPORTED, "%s: too many rows for the 32-bit row offsets", fn);
+    {
+        // row-direction tiles: the padded rows times the widest feature count
+        // must stay within the 32-bit offsets of the weight-gradient copies
+        const int64_t P = R + 128 * (cfg->n_experts + 2) + T;
+        const int64_t Im = cfg->inter > cfg->inter_shared ? cfg->inter : cfg->inter_shared;
+        const int64_t F = cfg->hidden > 2 * Im ? cfg->hidden : 2 * Im;
+        if (P >= ((int64_t)1 << 31) || P * F >= ((int64_t)1 << 32))
+            return fail(MOE_ERR_UNSUPPORTED, "%s: too many rows for the 32-bit tile offsets", fn);
+    }
     REQ_PTR(dw13);
     REQ_PTR(dw2);
     REQ_PTR(offsets);
