@@ -367,7 +367,7 @@ __global__ void __launch_bounds__(WG_THREADS, 1) wgrad_fp8_kernel(WgFp8 p) {
     // LDS stage `buf` in two halves of 128 columns (waves wb < 2, then wb >= 2)
     // so that every output row leaves as contiguous 256-byte runs (direct
     // stores from the accumulator layout would write 16-byte pieces of 32
-    // rows per instruction)
+    // rows per instruction); non-temporal: the gradients are not read here
     constexpr int SP = 128 + 8;  // padded staging row (elements)
     auto flush = [&](int tb, int buf) {
         uint16_t* stg = (uint16_t*)(smem + buf * WG_STAGE);
@@ -396,8 +396,8 @@ __global__ void __launch_bounds__(WG_THREADS, 1) wgrad_fp8_kernel(WgFp8 p) {
                 const int idx = t + WG_THREADS * k, row = idx >> 4, c16 = idx & 15;
                 const int64_t col = (int64_t)tb * WG_TB + half * 128 + c16 * 8;
                 if (col < rowsB)
-                    *(uint4*)(out + (ta * 128 + row) * rowsB + col) =
-                        *(const uint4*)(stg + row * SP + c16 * 8);
+                    __builtin_nontemporal_store(*(const u32x4_t*)(stg + row * SP + c16 * 8),
+                                                (u32x4_t*)(out + (ta * 128 + row) * rowsB + col));
             }
             lds_barrier();  // the staging rows are read before they are reused
         }
