@@ -209,13 +209,44 @@ def traffic_summary(fetch_csv, write_csv, workload, backward=False):
     f_scale = COPY_BYTES / cf
     w_scale = COPY_BYTES / cw
     lines = []
+    if backward and "fp8" in workload:
+        # moe_expert_ffn_backward_fp8 launches several kernels more than once:
+        # sum every dispatch of the last measured call (from its tile map to
+        # the calibration copies)
+        def ordered(path, counter):
+            with open(path) as f:
+                rows = [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+            return sorted((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"]))
+                          for r in rows)
+        fo, wo = ordered(fetch_csv, "FETCH_SIZE"), ordered(write_csv, "WRITE_SIZE")
+        wmap = {i: v for i, _, v in wo}
+        starts = [j for j, (_, k, _) in enumerate(fo) if "ffn_tile_map" in k]
+        j0 = starts[-1]
+        j1 = next(j for j in range(j0, len(fo)) if "copybuffer" in fo[j][1].lower())
+        per = collections.OrderedDict()
+        for i, k, v in fo[j0:j1]:
+            if "moe::" not in k:  # the calibration's own buffer fill
+                continue
+            e = per.setdefault(k, [0.0, 0.0, 0])
+            e[0] += v * 1024.0 * f_scale
+            e[1] += wmap.get(i, 0.0) * 1024.0 * w_scale
+            e[2] += 1
+        total = 0.0
+        for k, (fb, wb, n) in per.items():
+            total += fb + wb
+            lines.append("kernel: %s | fetch %.4g B | write %.4g B | dispatches in the call %d" %
+                         (k[:90], fb, wb, n))
+        out = ["workload: %s" % workload,
+               "calibration_copy_kernel: %s" % copy_k[0][:90],
+               "calibration_fetch_scale: %.5f" % f_scale,
+               "calibration_write_scale: %.5f" % w_scale]
+        out += lines
+        out += ["hbm_bytes_per_launch: %.6g" % total,
+                "gemm_source_hash: %s" % gemm_source_hash(backward)]
+        return "\n".join(out)
     # the kernels of one call; each averaged over its last 3 dispatches, the
     # 3 measured calls (the backward's setup also runs forward kernels)
-    if backward and "fp8" in workload:  # every kernel of moe_expert_ffn_backward_fp8
-        ffn = [k for k in fetch if any(n in k for n in (
-            "wgrad_fp8", "ffn_tile_map", "ffn_gemm_fp8_kernel<1>", "ffn_gemm_fp8_kernel<2>",
-            "quant_rows_bf16", "swiglu_bwd_fp8", "pad_offsets", "quant_cols_t"))]
-    elif backward:  # with the training forward's saved activations: no recompute (mode 2)
+    if backward:  # with the training forward's saved activations: no recompute (mode 2)
         ffn = [k for k in fetch if "wgrad" in k or "ffn_tile_map" in k or
                any("ffn_gemm_bf16_kernel<%d," % m in k for m in (1, 3))]
     else:
