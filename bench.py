@@ -13,8 +13,8 @@ workload on this host.
 
 --backward measures the layer's backward instead: a step is the four backward
 calls -- combine backward, expert FFN backward (two dgrad and two wgrad GEMMs,
-reading the a, b, h the training forward kept; FP8 workloads recompute them on
-FP8 and quantise every GEMM operand), gate/centroid backward, input gradient --
+reading the a, b, h the training forward kept; FP8 workloads quantise every
+GEMM operand), gate/centroid backward, input gradient --
 on the state of one training forward step, reported as its own metric.
 """
 import argparse
@@ -67,7 +67,7 @@ def ffn_bwd_flops(c, recompute=False):
     (4 M d I) for M = T*k routed rows, the same for the shared expert over T
     rows, and with recompute (always on FP8) also a, b (4 M d I)"""
     T, k, d, I, Is = c["T"], c["k"], c["d"], c["I"], c["Is"]
-    f = 16.0 if (recompute or c.get("fp8")) else 12.0
+    f = 16.0 if recompute else 12.0
     return f * T * k * d * I + f * T * d * Is
 
 
@@ -78,7 +78,7 @@ def ffn_bwd_bytes(c, recompute=False):
     and the weight gradients as each GEMM reads or writes them."""
     T, k, d, I, Is, N = c["T"], c["k"], c["d"], c["I"], c["Is"], c["N"]
     if c.get("fp8"):
-        return ffn_bwd_bytes_fp8(c)
+        return ffn_bwd_bytes_fp8(c, recompute)
     def one(M, I, n):
         w = 2.0 * n * (d * I + 2 * I * d)                        # W2^T, W13^T read
         rec = 0.0
@@ -93,11 +93,11 @@ def ffn_bwd_bytes(c, recompute=False):
     return one(T * k, I, N) + (one(T, Is, 1) if Is > 0 else 0.0)
 
 
-def ffn_bwd_bytes_fp8(c):
+def ffn_bwd_bytes_fp8(c, recompute=False):
     """Algorithmic HBM bytes of one moe_expert_ffn_backward_fp8 call: each GEMM
     reads its E4M3 operands (codes, plus 4 bytes of scale per 128 codes) and
     writes its result once, and each quantised operand is produced once from its
-    bf16 tensor:  recompute (W13, x codes -> a, b, h bf16), dY row tiles, dgrad
+    bf16 tensor:  with recompute (W13, x codes -> a, b, h bf16), dY row tiles, dgrad
     down (W2^T, dY codes -> dh), SwiGLU' (dh, a, b -> [da db] bf16 and codes),
     dgrad up (W13^T, [da db] codes -> dX), the row-direction tiles of dY, h,
     [da db] and x (bf16 in, codes out), and the weight-gradient GEMMs (codes
@@ -105,8 +105,11 @@ def ffn_bwd_bytes_fp8(c):
     T, k, d, I, Is, N = c["T"], c["k"], c["d"], c["I"], c["Is"], c["N"]
     q = 1 + 4.0 / 128  # code + scale share
     def one(M, I, n):
-        w = n * (2 * I * d + d * I + 2 * I * d) * q                 # W13, W2^T, W13^T codes
-        b = q * M * d + 2.0 * M * 3 * I                             # recompute: x in, a/b/h out
+        w = n * (d * I + 2 * I * d) * q                             # W2^T, W13^T codes
+        b = 0.0
+        if recompute:
+            w += n * 2 * I * d * q                                  # W13 codes
+            b += q * M * d + 2.0 * M * 3 * I                        # x in, a/b/h out
         b += 2.0 * M * d + q * M * d                                # dY row tiles
         b += q * M * d + 2.0 * M * I                                # dgrad down
         b += 2.0 * M * 3 * I + 2.0 * M * 2 * I + q * M * 2 * I      # SwiGLU'
@@ -541,9 +544,10 @@ def run_backward(args, cfg, dev, log):
     else:
         roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12,
                 "unit": "TFLOP/s", "frac": achieved / peak}
-    roof.update({"kernel": ("expert FFN backward, FP8: a, b, h recompute, dgrad down, "
+    roof.update({"kernel": ("expert FFN backward, FP8: dgrad down, "
                             "SwiGLU' + 1x128 tiles, dgrad up, 128x1 row-direction tiles, "
-                            "wgrad down and up" if cfg.get("fp8") else
+                            "wgrad down and up; a, b, h saved by the training forward"
+                            if cfg.get("fp8") else
                             "expert FFN backward GEMMs (dgrad down+SwiGLU', dgrad up, wgrad "
                             "down, wgrad up; a, b, h saved by the training forward)"),
                  "traffic": recorded_traffic(args.workload, backward=True),

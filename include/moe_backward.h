@@ -68,6 +68,19 @@ int moe_expert_ffn_train(const moe_cfg* cfg, const void* x_perm, const int32_t* 
                          size_t saved_bytes, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/* Training forward of FP8 expert GEMMs: the same results as moe_expert_ffn
+ * (bitwise; the arguments as there), and it also stores into `saved`
+ * (moe_expert_ffn_saved_size bytes) a and b (the fp32 sums rounded to bf16)
+ * and h = silu(a) * b in bf16 of every row, for moe_expert_ffn_backward_fp8.
+ * gemm_dtype FP8_E4M3, act_dtype BF16. */
+int moe_expert_ffn_train_fp8(const moe_cfg* cfg, const void* x_perm, const float* x_perm_scale,
+                             const int32_t* offsets, const void* w13, const float* w13_scale,
+                             const void* w2, const float* w2_scale, void* y_perm,
+                             const void* x_sh, const float* x_sh_scale, const void* ws13,
+                             const float* ws13_scale, const void* ws2, const float* ws2_scale,
+                             void* y_shared, void* saved, size_t saved_bytes, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace moe_expert_ffn_backward needs: the recomputed a, b, h and
  * the gradients da, db of every row (bf16 V3 shape: about 1.5 GB). */
 size_t moe_expert_ffn_backward_workspace_size(const moe_cfg* cfg);
@@ -114,7 +127,7 @@ size_t moe_expert_ffn_backward_fp8_workspace_size(const moe_cfg* cfg);
  * activation tiles, 128x128 weight blocks, FP32 promotion every 128) applied
  * to every GEMM of the backward, each operand quantised along that GEMM's
  * contraction:
- *   a, b, h  recomputed on FP8 (as the forward), kept in bf16
+ *   a, b, h  as kept by moe_expert_ffn_train_fp8 (bf16), or recomputed on FP8
  *   dh = dY W2                    dY in 1x128 row tiles
  *   da, db as in moe_expert_ffn_backward (bf16), then [da db] in 1x128 tiles
  *   dX = [da db] [W1; W3]
@@ -135,6 +148,9 @@ size_t moe_expert_ffn_backward_fp8_workspace_size(const moe_cfg* cfg);
  *  dx_perm, dx_shared     out, bf16, as moe_expert_ffn_backward
  *  dw13 [N, 2I, d], dw2 [N, d, I], dws13, dws2   out, bf16; zeros for an
  *                         expert without rows
+ *  saved                  a, b, h kept by moe_expert_ffn_train_fp8 for this step
+ *                         (saved_bytes >= moe_expert_ffn_saved_size), or NULL:
+ *                         recomputed on FP8 (w13, ws13 are read only then)
  * Deterministic (no atomics); the common rules of moe.h hold. */
 int moe_expert_ffn_backward_fp8(const moe_cfg* cfg, const void* x, const int32_t* src_token,
                                 const int32_t* offsets, const uint8_t* x_perm,
@@ -144,8 +160,9 @@ int moe_expert_ffn_backward_fp8(const moe_cfg* cfg, const void* x, const int32_t
                                 const void* ws13, const void* ws13t, const float* ws13_scale,
                                 const void* ws2t, const float* ws2_scale, const void* dy_perm,
                                 const void* dy_shared, void* dx_perm, void* dx_shared,
-                                void* dw13, void* dw2, void* dws13, void* dws2, void* workspace,
-                                size_t workspace_bytes, void* stream);
+                                void* dw13, void* dw2, void* dws13, void* dws2, const void* saved,
+                                size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /* Bytes of workspace moe_route_backward needs (T*k fp32). */
 size_t moe_route_backward_workspace_size(const moe_cfg* cfg);

@@ -9,8 +9,8 @@ missing, importing the functions fails loudly.
 The functions carry the C names: moe_route, moe_permute, moe_expert_ffn,
 moe_combine, moe_bias_update, moe_quantize_weights_fp8, the backward calls of
 include/moe_backward.h (moe_expert_ffn_train, moe_combine_backward,
-moe_expert_ffn_backward, moe_expert_ffn_backward_fp8, moe_route_backward,
-moe_input_grad), plus the workspace size queries.
+moe_expert_ffn_backward, moe_expert_ffn_train_fp8, moe_expert_ffn_backward_fp8,
+moe_route_backward, moe_input_grad), plus the workspace size queries.
 ``MoeLayer`` (in layer.py) strings them together for one step.
 """
 import ctypes
@@ -78,7 +78,8 @@ def lib():
             "moe_expert_ffn_backward_workspace_size": ([C], SZ),
             "moe_expert_ffn_backward": ([C] + [P] * 18 + [SZ, P, SZ, P], ctypes.c_int),
             "moe_expert_ffn_backward_fp8_workspace_size": ([C], SZ),
-            "moe_expert_ffn_backward_fp8": ([C] + [P] * 25 + [P, SZ, P], ctypes.c_int),
+            "moe_expert_ffn_backward_fp8": ([C] + [P] * 26 + [SZ, P, SZ, P], ctypes.c_int),
+            "moe_expert_ffn_train_fp8": ([C] + [P] * 16 + [SZ, P, SZ, P], ctypes.c_int),
             "moe_expert_ffn_saved_size": ([C], SZ),
             "moe_expert_ffn_train": ([C] + [P] * 10 + [SZ, P, SZ, P], ctypes.c_int),
             "moe_route_backward_workspace_size": ([C], SZ),
@@ -221,12 +222,22 @@ def moe_expert_ffn_backward_fp8_workspace_size(cfg):
 def moe_expert_ffn_backward_fp8(cfg, x, src_token, offsets, x_perm, x_perm_scale, x_q, x_scale,
                                 w13, w13t, w13_scale, w2t, w2_scale, ws13, ws13t, ws13_scale,
                                 ws2t, ws2_scale, dy_perm, dy_shared, dx_perm, dx_shared, dw13,
-                                dw2, dws13, dws2, workspace, stream=None):
+                                dw2, dws13, dws2, saved, workspace, stream=None):
     _check(lib().moe_expert_ffn_backward_fp8(
         ctypes.byref(cfg), _p(x), _p(src_token), _p(offsets), _p(x_perm), _p(x_perm_scale),
         _p(x_q), _p(x_scale), _p(w13), _p(w13t), _p(w13_scale), _p(w2t), _p(w2_scale), _p(ws13),
         _p(ws13t), _p(ws13_scale), _p(ws2t), _p(ws2_scale), _p(dy_perm), _p(dy_shared),
-        _p(dx_perm), _p(dx_shared), _p(dw13), _p(dw2), _p(dws13), _p(dws2), _p(workspace),
+        _p(dx_perm), _p(dx_shared), _p(dw13), _p(dw2), _p(dws13), _p(dws2), _p(saved),
+        _nbytes(saved), _p(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def moe_expert_ffn_train_fp8(cfg, x_perm, x_perm_scale, offsets, w13, w13_scale, w2, w2_scale,
+                             y_perm, x_sh, x_sh_scale, ws13, ws13_scale, ws2, ws2_scale,
+                             y_shared, saved, workspace, stream=None):
+    _check(lib().moe_expert_ffn_train_fp8(
+        ctypes.byref(cfg), _p(x_perm), _p(x_perm_scale), _p(offsets), _p(w13), _p(w13_scale),
+        _p(w2), _p(w2_scale), _p(y_perm), _p(x_sh), _p(x_sh_scale), _p(ws13), _p(ws13_scale),
+        _p(ws2), _p(ws2_scale), _p(y_shared), _p(saved), _nbytes(saved), _p(workspace),
         _nbytes(workspace), _stream(stream)))
 
 

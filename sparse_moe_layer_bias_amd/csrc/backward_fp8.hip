@@ -556,19 +556,26 @@ static hipError_t swiglu_bwd(const void* dh, const void* ab, int64_t rows, int64
 }
 
 hipError_t launch_expert_ffn_backward_fp8(const moe_cfg& c, const FfnBwdFp8Args& a, void* ws,
-                                          hipStream_t st) {
+                                          hipStream_t st, const void* saved) {
     const int64_t T = c.tokens, R = T * c.top_k, d = c.hidden, I = c.inter;
     const int64_t Is = c.inter_shared, N = c.n_experts;
     const bool has_shared = Is > 0 && T > 0;
     const int64_t S = has_shared ? T : 0;
     const int64_t Im = I > Is ? I : Is;
     BwdFp8Ws w = carve_bwd_fp8(c, ws, nullptr);
+    if (saved) {  // a, b, h kept by the training forward (moe_expert_ffn_train_fp8)
+        const SavedActs sv = carve_saved(c, const_cast<void*>(saved));
+        w.ab_r = sv.ab_r;
+        w.h_r = sv.h_r;
+        w.ab_s = sv.ab_s;
+        w.h_s = sv.h_s;
+    }
     const int64_t max_r = bwd_fp8_max_r(c), max_s = has_shared ? bwd_fp8_max_s(c) : 0;
     hipError_t e;
     if (R > 0) {
         launch_tile_map(a.offsets, (int)N, T, has_shared, FP8_BM, w.tiles, w.counts, w.order,
                         w.keys, st);
-        // 1. a, b, h of every row (FP8 gate/up, as in the forward)
+        // 1. a, b, h of every row (FP8 gate/up, as in the forward), unless kept
         Fp8Gemm g{};
         g.mode = 2;
         g.K_r = g.K_s = d;
@@ -586,8 +593,8 @@ hipError_t launch_expert_ffn_backward_fp8(const moe_cfg& c, const FfnBwdFp8Args&
         g.C_s = w.h_s;
         g.E_r = w.ab_r;
         g.E_s = w.ab_s;
-        if ((e = launch_fp8_gemm(g, w.tiles, w.counts, w.order, a.offsets, (int)N, S, max_r,
-                                 max_s, st)) != hipSuccess)
+        if (!saved && (e = launch_fp8_gemm(g, w.tiles, w.counts, w.order, a.offsets, (int)N, S,
+                                           max_r, max_s, st)) != hipSuccess)
             return e;
         // 2. dY row tiles, dh = dY W2
         if ((e = quant_rows(a.dy_perm, R, d, w.gq_r, w.gs_r, st)) != hipSuccess) return e;

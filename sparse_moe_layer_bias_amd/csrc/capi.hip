@@ -117,7 +117,7 @@ int set_error(int code, const char* msg) {
 
 extern "C" {
 
-int moe_abi_version(void) { return 5; }
+int moe_abi_version(void) { return 6; }
 
 const char* moe_last_error(void) { return g_err; }
 
@@ -271,6 +271,28 @@ int moe_expert_ffn_train(const moe_cfg* cfg, const void* x_perm, const int32_t* 
     }
     return expert_ffn_impl(fn, cfg, x_perm, nullptr, offsets, w13, nullptr, w2, nullptr, y_perm,
                            x_sh, nullptr, ws13, nullptr, ws2, nullptr, y_shared,
+                           cfg->tokens > 0 ? saved : nullptr, workspace, workspace_bytes, stream);
+}
+
+int moe_expert_ffn_train_fp8(const moe_cfg* cfg, const void* x_perm, const float* x_perm_scale,
+                             const int32_t* offsets, const void* w13, const float* w13_scale,
+                             const void* w2, const float* w2_scale, void* y_perm,
+                             const void* x_sh, const float* x_sh_scale, const void* ws13,
+                             const float* ws13_scale, const void* ws2, const float* ws2_scale,
+                             void* y_shared, void* saved, size_t saved_bytes, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    const char* fn = "moe_expert_ffn_train_fp8";
+    if (int r = check_cfg(fn, cfg)) return r;
+    if (cfg->gemm_dtype != MOE_FP8_E4M3 || cfg->act_dtype != MOE_BF16)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: needs gemm_dtype FP8_E4M3 and act_dtype BF16", fn);
+    if (cfg->tokens > 0) {
+        REQ_PTR(saved);
+        if (saved_bytes < moe_expert_ffn_saved_size(cfg))
+            return fail(MOE_ERR_WORKSPACE, "%s: saved %zu < %zu bytes", fn, saved_bytes,
+                        moe_expert_ffn_saved_size(cfg));
+    }
+    return expert_ffn_impl(fn, cfg, x_perm, x_perm_scale, offsets, w13, w13_scale, w2, w2_scale,
+                           y_perm, x_sh, x_sh_scale, ws13, ws13_scale, ws2, ws2_scale, y_shared,
                            cfg->tokens > 0 ? saved : nullptr, workspace, workspace_bytes, stream);
 }
 
@@ -453,8 +475,9 @@ int moe_expert_ffn_backward_fp8(const moe_cfg* cfg, const void* x, const int32_t
                                 const void* ws13, const void* ws13t, const float* ws13_scale,
                                 const void* ws2t, const float* ws2_scale, const void* dy_perm,
                                 const void* dy_shared, void* dx_perm, void* dx_shared,
-                                void* dw13, void* dw2, void* dws13, void* dws2, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+                                void* dw13, void* dw2, void* dws13, void* dws2, const void* saved,
+                                size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                                void* stream) {
     const char* fn = "moe_expert_ffn_backward_fp8";
     if (int r = check_cfg(fn, cfg)) return r;
     if (int r = check_ffn_shape(fn, cfg)) return r;
@@ -503,6 +526,10 @@ int moe_expert_ffn_backward_fp8(const moe_cfg* cfg, const void* x, const int32_t
     if (workspace_bytes < moe_expert_ffn_backward_fp8_workspace_size(cfg))
         return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes,
                     moe_expert_ffn_backward_fp8_workspace_size(cfg));
+    OPT_PTR(saved);
+    if (saved && saved_bytes < moe_expert_ffn_saved_size(cfg))
+        return fail(MOE_ERR_WORKSPACE, "%s: saved %zu < %zu bytes", fn, saved_bytes,
+                    moe_expert_ffn_saved_size(cfg));
     moe::FfnBwdFp8Args a{};
     a.x = x;
     a.src_token = src_token;
@@ -530,7 +557,7 @@ int moe_expert_ffn_backward_fp8(const moe_cfg* cfg, const void* x, const int32_t
     a.dws13 = dws13;
     a.dws2 = dws2;
     return hip_status(fn, moe::launch_expert_ffn_backward_fp8(*cfg, a, workspace,
-                                                              (hipStream_t)stream));
+                                                              (hipStream_t)stream, saved));
 }
 
 size_t moe_route_backward_workspace_size(const moe_cfg* cfg) {

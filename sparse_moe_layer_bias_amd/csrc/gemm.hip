@@ -602,7 +602,7 @@ void launch_tile_map(const int32_t* offsets, int N, int64_t T, bool has_shared, 
 hipError_t launch_expert_ffn_fp8(const moe_cfg& c, const FfnArgs& a, const int2* tiles,
                                  const int32_t* counts, const int32_t* order, void* h_r,
                                  void* h_s, float* hs_r, float* hs_s, int64_t max_r,
-                                 int64_t max_s, hipStream_t st);
+                                 int64_t max_s, hipStream_t st, const SavedActs* sv);
 
 hipError_t launch_expert_ffn(const moe_cfg& c, const FfnArgs& a, void* ws, hipStream_t st,
                              void* saved) {
@@ -611,7 +611,10 @@ hipError_t launch_expert_ffn(const moe_cfg& c, const FfnArgs& a, void* ws, hipSt
     if (TK == 0) return hipSuccess;
     FfnWs w = carve_ffn(c, ws);
     SavedActs sv{};
-    if (saved) {
+    const bool fp8 = c.gemm_dtype == MOE_FP8_E4M3;
+    if (saved && fp8) {
+        sv = carve_saved(c, saved);  // FP8: the h codes stay in the workspace
+    } else if (saved) {
         // training forward: h lives in the saved activations (with a, b)
         sv = carve_saved(c, saved);
         w.h_r = sv.h_r;
@@ -622,9 +625,9 @@ hipError_t launch_expert_ffn(const moe_cfg& c, const FfnArgs& a, void* ws, hipSt
     const int64_t max_s = has_shared ? ffn_max_shared_tiles(c) : 0;
     launch_tile_map(a.offsets, (int)c.n_experts, T, has_shared, BM, w.tiles, w.counts, w.order,
                     w.keys, st);
-    if (c.gemm_dtype == MOE_FP8_E4M3)
+    if (fp8)
         return launch_expert_ffn_fp8(c, a, w.tiles, w.counts, w.order, w.h_r, w.h_s, w.hs_r, w.hs_s,
-                                     max_r, max_s, st);
+                                     max_r, max_s, st, saved ? &sv : nullptr);
 
     GemmParamsV2 p{};
     p.tiles = w.tiles;

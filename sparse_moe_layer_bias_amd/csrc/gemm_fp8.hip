@@ -58,6 +58,8 @@ struct Fp8Params {
     float* hs_s;
     int ws_t;              // weight scales indexed [mats][K/128][rows/128] (the
                            // block grid of the untransposed matrix: dgrad GEMMs)
+    void* hb_r;            // modes 2 and 4: h in bf16 [rows][Nout]; a, b go to g.E
+    void* hb_s;
 };
 
 // Pack FP8 weight codes [n_mats][rows][K] into the kernel's LDS image order:
@@ -262,12 +264,14 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
     // epilogue.  32x32 accumulator layout: lane l holds column (token) l%32 and
     // rows (weight rows) 8*(v/4) + 4*(l/32) + v%4, v = 0..15.
     __syncthreads();  // every wave is done with the stage buffers
-    if (MODE == 2) {
-        // training recompute: a and b rounded to bf16 into E ([rows][2 Nout],
-        // a row is [a | b]) and h = silu(a) * b rounded to bf16 into C
-        // ([rows][Nout]), straight from the accumulators (4 columns per store)
+    if (MODE == 2 || MODE == 4) {
+        // kept for the backward (mode 2: the backward's recompute; mode 4: the
+        // training forward, which also quantises h below): a and b rounded to
+        // bf16 into E ([rows][2 Nout], a row is [a | b]) and h = silu(a) * b
+        // rounded to bf16 into hb ([rows][Nout]), straight from the
+        // accumulators (4 columns per store)
         if constexpr (NB > 0) {
-            uint16_t* hb = (uint16_t*)(shared ? P.g.C_s : P.g.C_r) + (w.rowbase + w.m0) * w.Nout;
+            uint16_t* hb = (uint16_t*)(shared ? P.hb_s : P.hb_r) + (w.rowbase + w.m0) * w.Nout;
             uint16_t* eb = (uint16_t*)(shared ? P.g.E_s : P.g.E_r) + (w.rowbase + w.m0) * 2 * w.Nout;
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
@@ -293,7 +297,8 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
                 }
             }
         }
-    } else if (MODE == 0) {
+    }
+    if (MODE == 0 || MODE == 4) {
         // h = silu(a) * b for the tile's 128 columns, then 1x128 quantisation:
         // the tile amax is reduced over the 4 weight-row waves through LDS;
         // codes are staged in LDS and stored as whole 128-byte rows
@@ -341,7 +346,7 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
             const int rr = q >> 3, ch = q & 7;
             *(uint4*)(hq + rr * w.Nout + ch * 16) = *(const uint4*)(hcodes + rr * HST + ch * 16);
         }
-    } else {
+    } else if (MODE == 1) {
         // y (bf16) through LDS in two token halves, stored as 16-byte row chunks
         constexpr int OSTR = 256 + 8;  // padded row (elements)
         uint16_t* ot = (uint16_t*)smem;
@@ -486,7 +491,8 @@ hipError_t launch_pack_weights_fp8(const moe_cfg& c, int which, const void* w, v
 
 hipError_t launch_expert_ffn_fp8(const moe_cfg& c, const FfnArgs& a, const int2* tiles,
                                  const int32_t* counts, const int32_t* order, void* h_r, void* h_s, float* hs_r,
-                                 float* hs_s, int64_t max_r, int64_t max_s, hipStream_t st) {
+                                 float* hs_s, int64_t max_r, int64_t max_s, hipStream_t st,
+                                 const SavedActs* sv) {
     const int64_t T = c.tokens;
     const bool has_shared = c.inter_shared > 0 && T > 0;
     Fp8Params P{};
@@ -517,7 +523,16 @@ hipError_t launch_expert_ffn_fp8(const moe_cfg& c, const FfnArgs& a, const int2*
     P.g.ntn_r = (int)(c.inter / 128);
     P.g.ntn_s = has_shared ? (int)(c.inter_shared / 128) : 0;
     unsigned grid = (unsigned)ffn_grid_blocks(max_r, P.g.ntn_r, max_s, P.g.ntn_s);
-    ffn_gemm_fp8_kernel<0><<<grid, F8_THREADS, 0, st>>>(P);
+    if (sv) {  // training forward: also a, b and h in bf16 for the backward
+        P.g.E_r = sv->ab_r;
+        P.g.E_s = sv->ab_s;
+        P.hb_r = sv->h_r;
+        P.hb_s = sv->h_s;
+        ffn_gemm_fp8_kernel<4><<<grid, F8_THREADS, 0, st>>>(P);
+        P.g.E_r = P.g.E_s = P.hb_r = P.hb_s = nullptr;
+    } else {
+        ffn_gemm_fp8_kernel<0><<<grid, F8_THREADS, 0, st>>>(P);
+    }
 
     // down: h codes x W2 codes -> y (bf16)
     P.g.K_r = c.inter;
@@ -574,8 +589,12 @@ hipError_t launch_fp8_gemm(const Fp8Gemm& op, const int2* tiles, const int32_t* 
     P.g.ntn_r = (int)cdiv(op.Nout_r, cols);
     P.g.ntn_s = T_shared > 0 ? (int)cdiv(op.Nout_s, cols) : 0;
     const unsigned grid = (unsigned)ffn_grid_blocks(max_r, P.g.ntn_r, max_s, P.g.ntn_s);
-    if (op.mode == 2)
+    if (op.mode == 2) {
+        P.g.C_r = P.g.C_s = nullptr;
+        P.hb_r = op.C_r;
+        P.hb_s = op.C_s;
         ffn_gemm_fp8_kernel<2><<<grid, F8_THREADS, 0, st>>>(P);
+    }
     else
         ffn_gemm_fp8_kernel<1><<<grid, F8_THREADS, 0, st>>>(P);
     return hipGetLastError();

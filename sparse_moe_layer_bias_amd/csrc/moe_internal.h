@@ -163,8 +163,9 @@ struct FfnBwdFp8Args {
     void* dws2;
 };
 size_t ffn_backward_fp8_workspace_bytes(const moe_cfg& c);
+// saved: the a, b, h a training forward kept (carve_saved), else recomputed
 hipError_t launch_expert_ffn_backward_fp8(const moe_cfg& c, const FfnBwdFp8Args& a, void* ws,
-                                          hipStream_t st);
+                                          hipStream_t st, const void* saved = nullptr);
 hipError_t launch_combine_backward(const moe_cfg& c, const void* dout, const void* y_perm,
                                    const float* gate, const int32_t* dst_row, void* dy_perm,
                                    float* dgate, hipStream_t st);

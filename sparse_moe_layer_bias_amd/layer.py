@@ -17,6 +17,7 @@ import torch
 from . import (MoeCfg, cfg_from_dict, moe_bias_update, moe_combine, moe_combine_backward,
                moe_expert_ffn, moe_expert_ffn_backward, moe_expert_ffn_backward_fp8,
                moe_expert_ffn_backward_fp8_workspace_size, moe_expert_ffn_backward_workspace_size,
+               moe_expert_ffn_train_fp8,
                moe_expert_ffn_saved_size, moe_expert_ffn_train,
                moe_expert_ffn_workspace_size, moe_input_grad, moe_pack_weights,
                moe_packed_weights_size, moe_permute, moe_permute_workspace_size,
@@ -130,10 +131,9 @@ class MoeLayer:
                 self.ws13t = pack_weights(self.cfg, 6, ws13)
                 self.ws2t = pack_weights(self.cfg, 7, ws2)
         self.grads = None
-        # a training forward keeps a, b and h for the backward (else recomputed;
-        # FP8 layers always recompute them on FP8)
+        # a training forward keeps a, b and h for the backward (else recomputed)
         self.saved = None
-        if self.train and save_activations and not self.fp8:
+        if self.train and save_activations:
             self.saved = torch.empty((moe_expert_ffn_saved_size(self.cfg),), dtype=torch.uint8,
                                      device=dev)
 
@@ -147,6 +147,14 @@ class MoeLayer:
                     self.x_perm, self.x_perm_s, self.x_q, self.x_s, self.workspace, stream)
 
     def expert_ffn(self, x, stream=None):
+        if self.saved is not None and self.fp8:
+            shared = self.y_shared is not None
+            moe_expert_ffn_train_fp8(
+                self.cfg, self.x_perm, self.x_perm_s, self.offsets, self.w13, self.w13_s, self.w2,
+                self.w2_s, self.y_perm, self.x_q if shared else None,
+                self.x_s if shared else None, self.ws13, self.ws13_s, self.ws2, self.ws2_s,
+                self.y_shared, self.saved, self.workspace, stream)
+            return
         if self.saved is not None:
             shared = self.y_shared is not None
             moe_expert_ffn_train(self.cfg, self.x_perm, self.offsets, self.w13, self.w2,
@@ -213,7 +221,7 @@ class MoeLayer:
                 self.x_q if shared else None, self.x_s if shared else None, self.w13, self.w13t,
                 self.w13_s, self.w2t, self.w2_s, self.ws13, self.ws13t, self.ws13_s, self.ws2t,
                 self.ws2_s, g["dy_perm"], dout if shared else None, g["dx_perm"], g["dx_shared"],
-                g["dw13"], g["dw2"], g["dws13"], g["dws2"], g["workspace"], stream)
+                g["dw13"], g["dw2"], g["dws13"], g["dws2"], self.saved, g["workspace"], stream)
             return
         moe_expert_ffn_backward(self.cfg, self.x_perm, self.offsets, self.w13, self.w13t,
                                 self.w2t, g["dy_perm"], x if shared else None, self.ws13,

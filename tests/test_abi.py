@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
             "moe_route_backward", "moe_input_grad"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert moe.moe_abi_version() == 5
+    assert moe.moe_abi_version() == 6
 
 
 @host_only
@@ -248,15 +248,24 @@ def test_fp8_backward_validation():
     names = ("x", "src_token", "offsets", "x_perm", "x_perm_scale", "x_q", "x_scale", "w13",
              "w13t", "w13_scale", "w2t", "w2_scale", "ws13", "ws13t", "ws13_scale", "ws2t",
              "ws2_scale", "dy_perm", "dy_shared", "dx_perm", "dx_shared", "dw13", "dw2", "dws13",
-             "dws2", "workspace")
-    call = lambda cfg, ws=need, **o: L.moe_expert_ffn_backward_fp8(
+             "dws2")
+    sv = moe.moe_expert_ffn_saved_size(c)
+    call = lambda cfg, ws=need, saved=0, saved_bytes=0, **o: L.moe_expert_ffn_backward_fp8(
         ctypes.byref(cfg), *(P(o.get(n, FAKE * (i + 1))) if o.get(n, 1) else None
-                             for i, n in enumerate(names)), ws, None)
+                             for i, n in enumerate(names)), P(saved) if saved else None,
+        saved_bytes, P(FAKE * 40), ws, None)
     assert call(c, ws=need - 1) == moe.MOE_ERR_WORKSPACE
     assert moe.lib().moe_last_error().decode().startswith("moe_expert_ffn_backward_fp8")
     assert call(c, dw13=0) == moe.MOE_ERR_ARG
     assert call(c, x_q=0) == moe.MOE_ERR_ARG          # the shared expert's tiles
     assert call(c, w13_scale=0) == moe.MOE_ERR_ARG
+    assert call(c, saved=FAKE * 50, saved_bytes=sv - 1) == moe.MOE_ERR_WORKSPACE
+    # the FP8 training forward: FP8 layers only, saved activations of the full size
+    ws = moe.moe_expert_ffn_workspace_size(c)
+    tr = lambda cfg, saved_bytes: L.moe_expert_ffn_train_fp8(
+        ctypes.byref(cfg), *([P(FAKE)] * 16), saved_bytes, P(FAKE), ws, None)
+    assert tr(c, sv - 1) == moe.MOE_ERR_WORKSPACE
+    assert tr(_cfg(dtype="bf16", d=256, I=128, Is=128), sv) == moe.MOE_ERR_UNSUPPORTED
     assert call(_cfg(dtype="bf16", d=256, I=128, Is=128)) == moe.MOE_ERR_UNSUPPORTED  # not FP8
     assert call(_cfg(dtype="bf16", fp8=True, d=256, I=96, Is=128)) == moe.MOE_ERR_UNSUPPORTED
     # transposed FP8 packs: rows of 256 columns of the stored matrix

@@ -38,14 +38,16 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def _run(orc, seed=0, residual=True, **over):
+def _run(orc, seed=0, residual=True, save=True, **over):
     cfg = dict(moe_inputs.CONFIGS["mid_bf16"], fp8=True)
     T = over.pop("T", None)
     cfg.update(over)
     c, inp, dev = small_layer_inputs(cfg, seed, T)
-    log("fp8 backward case T=%d" % c["T"], over, "seed", seed, "residual", residual)
+    log("fp8 backward case T=%d" % c["T"], over, "seed", seed, "residual", residual,
+        "saved activations" if save else "recompute")
     dout = moe_inputs.make_upstream_grad(c, seed, "cpu")
-    layer = MoeLayer(c, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"], train=True)
+    layer = MoeLayer(c, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"], train=True,
+                     save_activations=save)
     layer.forward(dev["x"], dev["centroids"], dev["bias"].clone(), residual=residual)
     g = layer.backward(dout.cuda(), dev["x"], dev["centroids"], residual=residual)
     torch.cuda.synchronize()
@@ -75,6 +77,31 @@ def test_fp8_backward_parity_small(orc, over):
         assert_close_fp8(moe_inputs.to_host(g[n]), ref[n], n, elem=3.0)
     for n in ("dw13", "dw2", "dws13", "dws2"):
         assert_close_fp8_grad(moe_inputs.to_host(g[n]), ref[n], n)
+
+
+@pytest.mark.parametrize("over", [dict(T=77), dict(T=700, d=384, N=2, k=1, I=256, Is=128)])
+def test_fp8_backward_parity_recompute(orc, over):
+    """Without kept activations the backward recomputes a, b, h on FP8."""
+    c, layer, g, ref = _run(orc, save=False, **dict(over))
+    for n in ("dx_perm", "dx_shared", "dx"):
+        assert_close_fp8(moe_inputs.to_host(g[n]), ref[n], n, elem=3.0)
+    for n in ("dw13", "dw2", "dws13", "dws2"):
+        assert_close_fp8_grad(moe_inputs.to_host(g[n]), ref[n], n)
+
+
+@pytest.mark.parametrize("T", [1, 300])
+def test_fp8_training_forward_is_bitwise_the_inference_forward(T):
+    cfg = dict(moe_inputs.CONFIGS["mid_bf16"], fp8=True)
+    c, inp, dev = small_layer_inputs(cfg, 9, T)
+    outs = []
+    for train in (False, True):
+        layer = MoeLayer(c, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"], train=train)
+        o = layer.forward(dev["x"], dev["centroids"], dev["bias"].clone()).clone()
+        torch.cuda.synchronize()
+        outs.append((moe_inputs.to_host(o), moe_inputs.to_host(layer.y_perm),
+                     moe_inputs.to_host(layer.y_shared)))
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
 def test_fp8_backward_without_residual_and_deterministic(orc):
