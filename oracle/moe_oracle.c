@@ -27,6 +27,8 @@
  *    (index ascending, starting from +0.0f); the pages give only u^T e_i;
  *  - sigmoid is evaluated in double and rounded once to fp32;
  *  - ties in the Topk are broken toward the lower expert index; -0 == +0;
+ *    a NaN key (or a NaN group score) ranks as -inf, so a token whose keys
+ *    are all NaN still gets k valid experts (the lowest eligible indices);
  *  - group-limited routing: G contiguous groups of N/G experts; a group's
  *    score is the fp32 sum of its two largest biased keys; the TG best
  *    groups (ties to the lower group) are kept; the pages do not define it
@@ -161,6 +163,7 @@ static void select_one(int64_t N, int64_t k, int64_t G, int64_t TG, const float*
     for (int64_t i = 0; i < N; ++i) {
         float v = s[i] + b[i];
         if (v == 0.0f) v = 0.0f; /* -0 -> +0 */
+        if (isnan(v)) v = -INFINITY; /* a NaN key ranks below every number */
         r[i] = v;
         allowed[i] = 1;
     }
@@ -181,6 +184,7 @@ static void select_one(int64_t N, int64_t k, int64_t G, int64_t TG, const float*
             }
             float sc = r[i1] + r[i2];
             if (sc == 0.0f) sc = 0.0f;
+            if (isnan(sc)) sc = -INFINITY; /* +inf + -inf: ranks lowest, like a NaN key */
             gscore[g] = sc;
             gkeep[g] = 0;
         }
@@ -434,24 +438,24 @@ static double block_dot(const uint8_t* a, const uint8_t* b, const double* lut) {
     return s;
 }
 
-/* FP8 SwiGLU expert:  A_q [M,d] codes with A_s [M,d/128];  w13_q [2I,d] with
- * w13_s [2I/128, d/128]; w2_q [d,I] with w2_s [d/128, I/128].
- * Each contraction is sum over 128-blocks kb of (s_a[m,kb]*s_w[nb,kb]) times
- * the block's exact code-product sum (the "promotion every 128" of [P4k]).
- * a, b rounded to fp32; h = silu(a)*b rounded to fp32, then quantised per
- * 1x128 tile exactly like the activations; y rounded to bf16. */
-void orc_swiglu_ffn_fp8(int64_t M, int64_t d, int64_t I, const uint8_t* Aq, const float* As,
-                        const uint8_t* w13q, const float* w13s, const uint8_t* w2q,
-                        const float* w2s, uint16_t* y_bf16) {
-    double lut[256];
+static void e4m3_lut(double* lut) {
     for (int c = 0; c < 256; ++c) {
         float v = orc_e4m3_decode((uint8_t)c);
         lut[c] = isnan(v) ? 0.0 : (double)v;
     }
-    int64_t kd = d / 128, ki = I / 128;
-    float* h = (float*)malloc((size_t)(M * I) * sizeof(float));
-    uint8_t* hq = (uint8_t*)malloc((size_t)(M * I));
-    float* hs = (float*)malloc((size_t)(M * ki) * sizeof(float));
+}
+
+/* FP8 gate/up half of the SwiGLU expert:  A_q [M,d] codes with A_s [M,d/128];
+ * w13_q [2I,d] with w13_s [2I/128, d/128] (rows 0..I-1 W1, I..2I-1 W3).
+ * a[m,n] and b[m,n] are sums over the 128-wide contraction blocks kb of
+ * (s_a[m,kb] * s_w[nb,kb]) times the block's exact code-product sum (the
+ * "promotion every 128" of [P4k]), each rounded to fp32;
+ * h[m,n] = silu(a) * b evaluated in double and rounded to fp32. */
+void orc_swiglu_gateup_fp8(int64_t M, int64_t d, int64_t I, const uint8_t* Aq, const float* As,
+                           const uint8_t* w13q, const float* w13s, float* h) {
+    double lut[256];
+    e4m3_lut(lut);
+    int64_t kd = d / 128;
 #pragma omp parallel for collapse(2) schedule(static)
     for (int64_t m = 0; m < M; ++m)
         for (int64_t n = 0; n < I; ++n) {
@@ -467,8 +471,17 @@ void orc_swiglu_ffn_fp8(int64_t M, int64_t d, int64_t I, const uint8_t* Aq, cons
             double a = (double)(float)sa, b = (double)(float)sb;
             h[m * I + n] = (float)(silu_d(a) * b);
         }
-    /* re-quantise h per 1x128 tile, exactly like the activations */
-    orc_quant_act_fp8(M, I, ORC_F32, h, hq, hs);
+}
+
+/* FP8 down half:  h_q [M,I] codes with h_s [M,I/128] (1x128 tiles of h);
+ * w2_q [d,I] with w2_s [d/128, I/128].  y[m,c] = sum over the 128-wide blocks
+ * kb of (s_h[m,kb] * s_w[cb,kb]) times the block's exact code-product sum,
+ * rounded once to bf16. */
+void orc_ffn_down_fp8(int64_t M, int64_t I, int64_t d, const uint8_t* hq, const float* hs,
+                      const uint8_t* w2q, const float* w2s, uint16_t* y_bf16) {
+    double lut[256];
+    e4m3_lut(lut);
+    int64_t ki = I / 128;
 #pragma omp parallel for collapse(2) schedule(static)
     for (int64_t m = 0; m < M; ++m)
         for (int64_t c = 0; c < d; ++c) {
@@ -479,6 +492,21 @@ void orc_swiglu_ffn_fp8(int64_t M, int64_t d, int64_t I, const uint8_t* Aq, cons
             }
             y_bf16[m * d + c] = double_to_bf16_bits(acc);
         }
+}
+
+/* The whole FP8 SwiGLU expert: the gate/up half gives h in fp32; h is
+ * re-quantised per 1x128 tile exactly like the activations ([P4k]: E4M3 for
+ * all tensors); the down half gives y in bf16. */
+void orc_swiglu_ffn_fp8(int64_t M, int64_t d, int64_t I, const uint8_t* Aq, const float* As,
+                        const uint8_t* w13q, const float* w13s, const uint8_t* w2q,
+                        const float* w2s, uint16_t* y_bf16) {
+    int64_t ki = I / 128;
+    float* h = (float*)malloc((size_t)(M * I) * sizeof(float));
+    uint8_t* hq = (uint8_t*)malloc((size_t)(M * I));
+    float* hs = (float*)malloc((size_t)(M * ki) * sizeof(float));
+    orc_swiglu_gateup_fp8(M, d, I, Aq, As, w13q, w13s, h);
+    orc_quant_act_fp8(M, I, ORC_F32, h, hq, hs);
+    orc_ffn_down_fp8(M, I, d, hq, hs, w2q, w2s, y_bf16);
     free(h);
     free(hq);
     free(hs);

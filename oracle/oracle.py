@@ -62,6 +62,8 @@ def _declare(L):
         "orc_quant_act_fp8": [I64, I64, I, P, P, P],
         "orc_quant_weight_fp8": [I64, I64, I64, I, P, P, P],
         "orc_swiglu_ffn_fp8": [I64, I64, I64, P, P, P, P, P, P, P],
+        "orc_swiglu_gateup_fp8": [I64, I64, I64, P, P, P, P, P],
+        "orc_ffn_down_fp8": [I64, I64, I64, P, P, P, P, P],
         "orc_combine": [I64, I64, I64, I, P, P, P, P, P, P],
         "orc_bias_update": [I64, I64, P, F, P],
         "orc_round_to_dtype": [I64, I, P, P],
@@ -268,6 +270,36 @@ def swiglu_ffn_fp8(Aq, As, w13q, w13s, w2q, w2s):
     y = np.empty((M, d), np.uint16)
     lib().orc_swiglu_ffn_fp8(M, d, I, _p(Aq), _p(As), _p(w13q), _p(w13s), _p(w2q), _p(w2s),
                              _p(y))
+    return y
+
+
+def swiglu_gateup_fp8(Aq, As, w13q, w13s):
+    """The gate/up half of the FP8 expert: h = silu(a) * b in fp32 [M, I], from
+    block-scaled sums a, b rounded to fp32."""
+    Aq = _c(Aq, np.uint8)
+    As = _c(As, np.float32)
+    w13q = _c(w13q, np.uint8)
+    w13s = _c(w13s, np.float32)
+    M, d = Aq.shape
+    I = w13q.shape[0] // 2
+    assert w13q.shape == (2 * I, d) and As.shape == (M, d // 128)
+    h = np.empty((M, I), np.float32)
+    lib().orc_swiglu_gateup_fp8(M, d, I, _p(Aq), _p(As), _p(w13q), _p(w13s), _p(h))
+    return h
+
+
+def ffn_down_fp8(hq, hs, w2q, w2s):
+    """The down half of the FP8 expert from h's 1x128 codes and tile scales:
+    y [M, d] as bf16 bits."""
+    hq = _c(hq, np.uint8)
+    hs = _c(hs, np.float32)
+    w2q = _c(w2q, np.uint8)
+    w2s = _c(w2s, np.float32)
+    M, I = hq.shape
+    d = w2q.shape[0]
+    assert w2q.shape == (d, I) and hs.shape == (M, I // 128)
+    y = np.empty((M, d), np.uint16)
+    lib().orc_ffn_down_fp8(M, I, d, _p(hq), _p(hs), _p(w2q), _p(w2s), _p(y))
     return y
 
 

@@ -185,3 +185,77 @@ def test_fp8_promotion_block_boundaries(orc):
     h = a / (1 + math.exp(-a)) * a
     got = float((y[0, 0].astype(np.uint32) << 16).view(np.float32))
     assert abs(got - h) <= h * 2.0 ** -6
+
+
+def _dequant_rows(tab, q, s):
+    return tab[q] * np.repeat(s.astype(np.float64), 128, axis=1)
+
+
+def _dequant_blocks(tab, q, s):
+    return tab[q] * np.kron(s.astype(np.float64), np.ones((128, 128)))
+
+
+def test_fp8_gateup_half_equals_dequantised_fp64(orc):
+    """The gate/up half alone: a, b are the fp64 GEMM of the dequantised
+    operands (the block-scaled exact sums are the same value) rounded to fp32,
+    h = silu(a) * b rounded to fp32.  Block scales differ per 128-row block
+    and per K block, so a transposed scale index changes the result."""
+    rng = np.random.default_rng(31)
+    M, d, I = 9, 384, 256
+    A = rng.standard_normal((M, d)).astype(np.float32)
+    A[:, 128:256] *= 40.0
+    w13 = (rng.standard_normal((2 * I, d)) / 16).astype(np.float32)
+    w13[128:256] *= 0.01
+    w13[:, 256:] *= 7.0
+    Aq, As = orc.quant_act_fp8(A)
+    wq, ws = orc.quant_weight_fp8(w13)
+    assert len(set(ws.ravel().tolist())) == ws.size
+    h = orc.swiglu_gateup_fp8(Aq, As, wq, ws)
+    tab = _torch_decode_all().astype(np.float64)
+    Ad, Wd = _dequant_rows(tab, Aq, As), _dequant_blocks(tab, wq, ws)
+    a = (Ad @ Wd[:I].T).astype(np.float32).astype(np.float64)
+    b = (Ad @ Wd[I:].T).astype(np.float32).astype(np.float64)
+    ref = (a / (1 + np.exp(-a)) * b).astype(np.float32)
+    # fp64 matmul rounding can move a or b across an fp32 rounding boundary
+    # (then by one fp32 ulp); everything else is identical
+    err = np.abs(h.astype(np.float64) - ref) / (np.abs(ref.astype(np.float64)) + 1e-30)
+    assert np.mean(h == ref) > 0.99
+    assert np.all(err <= 2.0 ** -21)
+
+
+def test_fp8_down_half_equals_dequantised_fp64(orc):
+    """The down half alone, from given h codes and 1x128 tile scales: the fp64
+    GEMM of the dequantised operands rounded once to bf16 (at most one bf16
+    step apart where fp64 rounding meets a bf16 midpoint)."""
+    rng = np.random.default_rng(32)
+    M, I, d = 7, 384, 256
+    h = (rng.standard_normal((M, I)) * np.exp(rng.standard_normal((M, 1)))).astype(np.float32)
+    h[:, 256:] *= 1e-3
+    w2 = (rng.standard_normal((d, I)) / 20).astype(np.float32)
+    w2[128:, :128] *= 50.0
+    hq, hs = orc.quant_act_fp8(h)
+    wq, ws = orc.quant_weight_fp8(w2)
+    y = orc.ffn_down_fp8(hq, hs, wq, ws)
+    tab = _torch_decode_all().astype(np.float64)
+    ref = _dequant_rows(tab, hq, hs) @ _dequant_blocks(tab, wq, ws).T
+    got = (y.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ref_bf = torch.from_numpy(ref).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.mean(got == ref_bf) > 0.99
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-300)
+
+
+def test_fp8_expert_is_its_two_halves(orc):
+    """The whole FP8 expert = gate/up half -> 1x128 re-quantisation of h ->
+    down half, bit for bit (the GPU tests feed the GPU's own h to the down
+    half, so the split must not change the composite)."""
+    rng = np.random.default_rng(33)
+    M, d, I = 6, 256, 384
+    A = rng.standard_normal((M, d)).astype(np.float32)
+    w13 = (rng.standard_normal((2 * I, d)) / 16).astype(np.float32)
+    w2 = (rng.standard_normal((d, I)) / 16).astype(np.float32)
+    Aq, As = orc.quant_act_fp8(A)
+    q13, s13 = orc.quant_weight_fp8(w13)
+    q2, s2 = orc.quant_weight_fp8(w2)
+    y = orc.swiglu_ffn_fp8(Aq, As, q13, s13, q2, s2)
+    hq, hs = orc.quant_act_fp8(orc.swiglu_gateup_fp8(Aq, As, q13, s13))
+    assert np.array_equal(y, orc.ffn_down_fp8(hq, hs, q2, s2))

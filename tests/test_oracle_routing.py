@@ -306,3 +306,43 @@ def test_route_shape_errors(orc):
         orc.select(s, b, 2, 5, 2)      # N % G != 0
     with pytest.raises(ValueError):
         orc.select(s, b, 9, 4, 2)      # k > TG * N/G
+
+
+def test_nan_keys_rank_lowest(orc):
+    """NaN is not covered by the pages; the reading: a NaN key (s + b) ranks as
+    -inf, below every number, with the lower index first among equals, so a
+    token always gets k distinct valid experts."""
+    nan = np.float32(np.nan)
+    s = np.array([[nan, 0.5, nan, 0.7, 0.1, nan],
+                  [nan] * 6,
+                  [0.2, nan, 0.9, nan, nan, nan]], np.float32)
+    b = np.zeros(6, np.float32)
+    idx, gate = orc.select(s, b, 4)
+    assert idx[0].tolist() == [3, 1, 4, 0]
+    assert idx[1].tolist() == [0, 1, 2, 3]
+    assert idx[2].tolist() == [2, 0, 1, 3]
+    # gates of a token with a NaN score among its chosen ones are NaN; the others are finite
+    assert np.all(np.isnan(gate[1]))
+    idx2, gate2 = orc.select(s[:, [1, 3, 4]], np.zeros(3, np.float32), 3)
+    assert np.all(np.isfinite(gate2[0]))
+
+
+def test_nan_group_scores_rank_lowest(orc):
+    """Group-limited selection with NaN keys: a group whose two best keys are
+    NaN (or whose score is +inf + -inf from the bias) scores -inf and ranks
+    below every finite group, lower group index first among equals."""
+    nan = np.float32(np.nan)
+    N, G, TG, k = 8, 4, 2, 3
+    s = np.full((2, N), 0.5, np.float32)
+    s[0, 0:2] = nan          # group 0 all NaN
+    s[0, 4:6] = [0.9, 0.8]   # group 2 best
+    s[1, :] = nan            # every key NaN: groups 0, 1 kept, experts 0, 1, 2
+    b = np.zeros(N, np.float32)
+    idx, _ = orc.select(s, b, k, G, TG)
+    assert idx[0].tolist() == [4, 5, 2]
+    assert idx[1].tolist() == [0, 1, 2]
+    # +inf bias on expert 7 and -inf on expert 6: group 3 scores inf + -inf = NaN -> -inf
+    b2 = np.zeros(N, np.float32)
+    b2[6], b2[7] = -np.inf, np.inf
+    idx3, _ = orc.select(np.full((1, N), 0.5, np.float32), b2, 2, G, 1)
+    assert idx3[0].tolist() == [0, 1]
