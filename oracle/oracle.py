@@ -384,7 +384,8 @@ def layer_forward(inp, cfg, residual=True):
     res.update(offsets=offsets, src_token=src, dst_row=dst, x_perm=x_perm, y_perm=y_perm,
                y_shared=y_shared, out=out, new_bias=new_bias)
     if fp8:
-        res.update(x_q=xq, x_s=xs, x_q_perm=xq_perm, x_s_perm=xs_perm)
+        res.update(x_q=xq, x_s=xs, x_q_perm=xq_perm, x_s_perm=xs_perm, w13_q=w13q, w13_s=w13s,
+                   w2_q=w2q, w2_s=w2s, ws13_q=ws13q, ws13_s=ws13s, ws2_q=ws2q, ws2_s=ws2s)
     return res
 
 

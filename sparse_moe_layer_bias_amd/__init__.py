@@ -10,7 +10,8 @@ The functions carry the C names: moe_route, moe_permute, moe_expert_ffn,
 moe_combine, moe_bias_update, moe_quantize_weights_fp8, the backward calls of
 include/moe_backward.h (moe_expert_ffn_train, moe_combine_backward,
 moe_expert_ffn_backward, moe_expert_ffn_train_fp8, moe_expert_ffn_backward_fp8,
-moe_route_backward, moe_input_grad), plus the workspace size queries.
+moe_route_backward, moe_input_grad), the FFN inspection calls of
+include/moe_inspect.h, plus the workspace size queries.
 ``MoeLayer`` (in layer.py) strings them together for one step.
 """
 import ctypes
@@ -85,6 +86,9 @@ def lib():
             "moe_route_backward_workspace_size": ([C], SZ),
             "moe_route_backward": ([C] + [P] * 10 + [SZ, P], ctypes.c_int),
             "moe_input_grad": ([C] + [P] * 8 + [P], ctypes.c_int),
+            "moe_expert_ffn_h_offsets": ([C, ctypes.POINTER(SZ)], ctypes.c_int),
+            "moe_expert_ffn_inspect": ([C] + [P] * 17 + [P, SZ, P], ctypes.c_int),
+            "moe_inspect_e4m3": ([P, I64, F, P, P, P], ctypes.c_int),
             "moe_last_error": ([], ctypes.c_char_p),
             "moe_abi_version": ([], ctypes.c_int),
         }
@@ -156,6 +160,30 @@ def moe_expert_ffn(cfg, x_perm, x_perm_scale, offsets, w13, w13_scale, w2, w2_sc
                                 _p(x_sh), _p(x_sh_scale), _p(ws13), _p(ws13_scale), _p(ws2),
                                 _p(ws2_scale), _p(y_shared), _p(workspace), _nbytes(workspace),
                                 _stream(stream)))
+
+
+def moe_expert_ffn_h_offsets(cfg):
+    """include/moe_inspect.h: byte offsets of h (routed, shared) and of its FP8
+    tile scales (routed, shared; None for other layers) in the FFN workspace."""
+    off = (ctypes.c_size_t * 4)()
+    _check(lib().moe_expert_ffn_h_offsets(ctypes.byref(cfg), off))
+    none = ctypes.c_size_t(-1).value
+    return [None if v == none else int(v) for v in off]
+
+
+def moe_expert_ffn_inspect(cfg, x_perm, x_perm_scale, offsets, w13, w13_scale, w2, w2_scale,
+                           y_perm, x_sh, x_sh_scale, ws13, ws13_scale, ws2, ws2_scale, y_shared,
+                           h_f32, h_f32_shared, workspace=None, stream=None):
+    _check(lib().moe_expert_ffn_inspect(
+        ctypes.byref(cfg), _p(x_perm), _p(x_perm_scale), _p(offsets), _p(w13), _p(w13_scale),
+        _p(w2), _p(w2_scale), _p(y_perm), _p(x_sh), _p(x_sh_scale), _p(ws13), _p(ws13_scale),
+        _p(ws2), _p(ws2_scale), _p(y_shared), _p(h_f32), _p(h_f32_shared), _p(workspace),
+        _nbytes(workspace), _stream(stream)))
+
+
+def moe_inspect_e4m3(v, scale, codes4, codes1, stream=None):
+    _check(lib().moe_inspect_e4m3(_p(v), int(v.numel()), ctypes.c_float(float(scale)),
+                                  _p(codes4), _p(codes1), _stream(stream)))
 
 
 def moe_packed_weights_size(cfg, which):

@@ -8,6 +8,7 @@
 #include <cstring>
 
 #include "moe_backward.h"
+#include "moe_inspect.h"
 #include "moe_internal.h"
 
 namespace {
@@ -199,7 +200,8 @@ static int expert_ffn_impl(const char* fn, const moe_cfg* cfg, const void* x_per
                            void* y_perm, const void* x_sh, const float* x_sh_scale,
                            const void* ws13, const float* ws13_scale, const void* ws2,
                            const float* ws2_scale, void* y_shared, void* saved,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+                           void* workspace, size_t workspace_bytes, void* stream,
+                           float* h_f32 = nullptr, float* h_f32_shared = nullptr) {
     if (int r = check_cfg(fn, cfg)) return r;
     if (int r = check_ffn_shape(fn, cfg)) return r;
     const bool fp8 = cfg->gemm_dtype == MOE_FP8_E4M3;
@@ -232,7 +234,8 @@ static int expert_ffn_impl(const char* fn, const moe_cfg* cfg, const void* x_per
     }
     moe::FfnArgs a{x_perm, x_perm_scale, offsets, w13, w13_scale, w2, w2_scale, y_perm,
                    x_sh,   x_sh_scale,   ws13,    ws13_scale, ws2, ws2_scale, y_shared};
-    return hip_status(fn, moe::launch_expert_ffn(*cfg, a, workspace, (hipStream_t)stream, saved));
+    return hip_status(fn, moe::launch_expert_ffn(*cfg, a, workspace, (hipStream_t)stream, saved,
+                                                 h_f32, h_f32_shared));
 }
 
 extern "C" {
@@ -246,6 +249,49 @@ int moe_expert_ffn(const moe_cfg* cfg, const void* x_perm, const float* x_perm_s
     return expert_ffn_impl("moe_expert_ffn", cfg, x_perm, x_perm_scale, offsets, w13, w13_scale,
                            w2, w2_scale, y_perm, x_sh, x_sh_scale, ws13, ws13_scale, ws2,
                            ws2_scale, y_shared, nullptr, workspace, workspace_bytes, stream);
+}
+
+int moe_expert_ffn_h_offsets(const moe_cfg* cfg, size_t off[4]) {
+    const char* fn = "moe_expert_ffn_h_offsets";
+    if (int r = check_cfg(fn, cfg)) return r;
+    if (!off) return fail(MOE_ERR_ARG, "%s: off is NULL", fn);
+    moe::ffn_h_offsets(*cfg, off);
+    return ok();
+}
+
+int moe_expert_ffn_inspect(const moe_cfg* cfg, const void* x_perm, const float* x_perm_scale,
+                           const int32_t* offsets, const void* w13, const float* w13_scale,
+                           const void* w2, const float* w2_scale, void* y_perm, const void* x_sh,
+                           const float* x_sh_scale, const void* ws13, const float* ws13_scale,
+                           const void* ws2, const float* ws2_scale, void* y_shared,
+                           float* h_f32, float* h_f32_shared, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    const char* fn = "moe_expert_ffn_inspect";
+    if (int r = check_cfg(fn, cfg)) return r;
+    if (cfg->gemm_dtype != MOE_FP8_E4M3)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: FP8 layers only", fn);
+    if (cfg->tokens > 0) {
+        REQ_PTR(h_f32);
+        if (cfg->inter_shared > 0) REQ_PTR(h_f32_shared);
+    }
+    return expert_ffn_impl(fn, cfg, x_perm, x_perm_scale, offsets, w13, w13_scale, w2, w2_scale,
+                           y_perm, x_sh, x_sh_scale, ws13, ws13_scale, ws2, ws2_scale, y_shared,
+                           nullptr, workspace, workspace_bytes, stream, h_f32,
+                           cfg->inter_shared > 0 ? h_f32_shared : nullptr);
+}
+
+int moe_inspect_e4m3(const float* v, int64_t n, float scale, uint8_t* codes4, uint8_t* codes1,
+                     void* stream) {
+    const char* fn = "moe_inspect_e4m3";
+    if (n < 0 || n > ((int64_t)1 << 40)) return fail(MOE_ERR_ARG, "%s: bad n", fn);
+    if (!(scale >= 0.0f) || scale > 3.4e38f)
+        return fail(MOE_ERR_ARG, "%s: scale must be finite and >= 0", fn);
+    if (n > 0) {
+        REQ_PTR(v);
+        if (!codes4 || !codes1) return fail(MOE_ERR_ARG, "%s: codes4 / codes1 is NULL", fn);
+    }
+    return hip_status(fn, moe::launch_e4m3_inspect(v, n, scale, codes4, codes1,
+                                                   (hipStream_t)stream));
 }
 
 size_t moe_expert_ffn_saved_size(const moe_cfg* cfg) {

@@ -602,10 +602,21 @@ void launch_tile_map(const int32_t* offsets, int N, int64_t T, bool has_shared, 
 hipError_t launch_expert_ffn_fp8(const moe_cfg& c, const FfnArgs& a, const int2* tiles,
                                  const int32_t* counts, const int32_t* order, void* h_r,
                                  void* h_s, float* hs_r, float* hs_s, int64_t max_r,
-                                 int64_t max_s, hipStream_t st, const SavedActs* sv);
+                                 int64_t max_s, hipStream_t st, const SavedActs* sv,
+                                 float* hf_r, float* hf_s);
+
+void ffn_h_offsets(const moe_cfg& c, size_t off[4]) {
+    char* base = (char*)(uintptr_t)4096;  // any aligned base: only differences are used
+    const FfnWs w = carve_ffn(c, base);
+    off[0] = (size_t)((char*)w.h_r - base);
+    off[1] = (size_t)((char*)w.h_s - base);
+    const bool fp8 = c.gemm_dtype == MOE_FP8_E4M3;
+    off[2] = fp8 ? (size_t)((char*)w.hs_r - base) : SIZE_MAX;
+    off[3] = fp8 ? (size_t)((char*)w.hs_s - base) : SIZE_MAX;
+}
 
 hipError_t launch_expert_ffn(const moe_cfg& c, const FfnArgs& a, void* ws, hipStream_t st,
-                             void* saved) {
+                             void* saved, float* hf_r, float* hf_s) {
     const int64_t T = c.tokens, TK = T * c.top_k;
     const bool has_shared = c.inter_shared > 0 && T > 0;
     if (TK == 0) return hipSuccess;
@@ -627,7 +638,7 @@ hipError_t launch_expert_ffn(const moe_cfg& c, const FfnArgs& a, void* ws, hipSt
                     w.keys, st);
     if (fp8)
         return launch_expert_ffn_fp8(c, a, w.tiles, w.counts, w.order, w.h_r, w.h_s, w.hs_r, w.hs_s,
-                                     max_r, max_s, st, saved ? &sv : nullptr);
+                                     max_r, max_s, st, saved ? &sv : nullptr, hf_r, hf_s);
 
     GemmParamsV2 p{};
     p.tiles = w.tiles;

@@ -60,6 +60,8 @@ struct Fp8Params {
                            // block grid of the untransposed matrix: dgrad GEMMs)
     void* hb_r;            // modes 2 and 4: h in bf16 [rows][Nout]; a, b go to g.E
     void* hb_s;
+    float* hf_r;           // modes 0 and 4, optional: h in fp32 before quantisation
+    float* hf_s;
 };
 
 // Pack FP8 weight codes [n_mats][rows][K] into the kernel's LDS image order:
@@ -317,6 +319,26 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
             m = fmaxf(m, __shfl_xor(m, 32, 64));
             if (NB > 0 && lane < 32) red[(tg * 160 + j * 32 + lane) * 4 + wg] = m;
         }
+        float* hf = shared ? P.hf_s : P.hf_r;
+        if (hf != nullptr) {
+            // the fp32 h values the quantisation below starts from (for checks
+            // of the codes against an independent quantiser); 4 columns per store
+            if constexpr (NB > 0) {
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    const int64_t rr = tg * 160 + j * 32 + (lane & 31);
+                    if (rr < mc) {
+                        float* hrow = hf + (w.rowbase + w.m0 + rr) * w.Nout + w.wt * 128 + wg * 32 +
+                                      4 * (lane >> 5);
+#pragma unroll
+                        for (int g4 = 0; g4 < 4; ++g4)
+                            *(float4*)(hrow + 8 * g4) =
+                                make_float4(hv[j][4 * g4], hv[j][4 * g4 + 1], hv[j][4 * g4 + 2],
+                                            hv[j][4 * g4 + 3]);
+                    }
+                }
+            }
+        }
         __syncthreads();
         float* hsc = shared ? P.hs_s : P.hs_r;
         const int64_t ntile = w.Nout / 128;
@@ -327,12 +349,13 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
                 const float4 mm = *(const float4*)(red + rr * 4);
                 const float amax = fmaxf(fmaxf(mm.x, mm.y), fmaxf(mm.z, mm.w));
                 const float scale = amax / 448.0f;
-                // codes of h / scale, computed as h * (1 / scale): the quotient
-                // may differ from the division in its last bit
-                const float inv = scale > 0.0f ? 1.0f / scale : 0.0f;
+                // codes of clamp(h / scale) with the IEEE fp32 divide, as for
+                // every other activation tile; an all-zero tile (scale 0) gets
+                // codes 0
                 float t[16];
 #pragma unroll
-                for (int v = 0; v < 16; ++v) t[v] = fminf(fmaxf(hv[j][v] * inv, -448.0f), 448.0f);
+                for (int v = 0; v < 16; ++v)
+                    t[v] = scale > 0.0f ? fminf(fmaxf(hv[j][v] / scale, -448.0f), 448.0f) : 0.0f;
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4)
                     *(uint32_t*)(hcodes + rr * HST + wg * 32 + 8 * g4 + 4 * (lane >> 5)) =
@@ -492,7 +515,7 @@ hipError_t launch_pack_weights_fp8(const moe_cfg& c, int which, const void* w, v
 hipError_t launch_expert_ffn_fp8(const moe_cfg& c, const FfnArgs& a, const int2* tiles,
                                  const int32_t* counts, const int32_t* order, void* h_r, void* h_s, float* hs_r,
                                  float* hs_s, int64_t max_r, int64_t max_s, hipStream_t st,
-                                 const SavedActs* sv) {
+                                 const SavedActs* sv, float* hf_r, float* hf_s) {
     const int64_t T = c.tokens;
     const bool has_shared = c.inter_shared > 0 && T > 0;
     Fp8Params P{};
@@ -520,6 +543,8 @@ hipError_t launch_expert_ffn_fp8(const moe_cfg& c, const FfnArgs& a, const int2*
     P.ws_s = a.ws13_scale;
     P.hs_r = hs_r;
     P.hs_s = hs_s;
+    P.hf_r = hf_r;
+    P.hf_s = has_shared ? hf_s : nullptr;
     P.g.ntn_r = (int)(c.inter / 128);
     P.g.ntn_s = has_shared ? (int)(c.inter_shared / 128) : 0;
     unsigned grid = (unsigned)ffn_grid_blocks(max_r, P.g.ntn_r, max_s, P.g.ntn_s);
@@ -551,6 +576,7 @@ hipError_t launch_expert_ffn_fp8(const moe_cfg& c, const FfnArgs& a, const int2*
     P.ws_s = a.ws2_scale;
     P.hs_r = nullptr;
     P.hs_s = nullptr;
+    P.hf_r = P.hf_s = nullptr;
     P.g.ntn_r = (int)cdiv(c.hidden, 256);
     P.g.ntn_s = has_shared ? (int)cdiv(c.hidden, 256) : 0;
     grid = (unsigned)ffn_grid_blocks(max_r, P.g.ntn_r, max_s, P.g.ntn_s);

@@ -169,6 +169,39 @@ __global__ void __launch_bounds__(256) quant_weight_kernel(const uint4* __restri
     }
 }
 
+// The E4M3 quantisation step on given fp32 values, both ways the kernels
+// perform it: c4 as the FP8 gate/up epilogue does (IEEE quotient v/scale,
+// clamp to +-448, four values per two converter instructions) and c1 as the
+// activation and weight quantisers do (quant_e4m3, one value per converter
+// instruction).  Thread i handles values 4i .. 4i+3 (zero-padded past n).
+__global__ void __launch_bounds__(256) e4m3_inspect_kernel(const float* __restrict__ v, int64_t n,
+                                                           float scale, uint8_t* __restrict__ c4,
+                                                           uint8_t* __restrict__ c1) {
+    const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (i >= n) return;
+    float t[4], x[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        x[j] = i + j < n ? v[i + j] : 0.0f;
+        t[j] = scale > 0.0f ? fminf(fmaxf(x[j] / scale, -448.0f), 448.0f) : 0.0f;
+    }
+    const uint32_t q = e4m3_encode4(t[0], t[1], t[2], t[3]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (i + j < n) {
+            c4[i + j] = (uint8_t)(q >> (8 * j));
+            c1[i + j] = (uint8_t)quant_e4m3(x[j], scale);
+        }
+}
+
+hipError_t launch_e4m3_inspect(const float* v, int64_t n, float scale, uint8_t* c4, uint8_t* c1,
+                               hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    e4m3_inspect_kernel<<<dim3((unsigned)cdiv(cdiv(n, 4), 256)), 256, 0, st>>>(v, n, scale, c4,
+                                                                              c1);
+    return hipGetLastError();
+}
+
 hipError_t launch_quantize_weights(int64_t n_mats, int64_t rows, int64_t cols, const void* w,
                                    uint8_t* q, float* s, hipStream_t st) {
     const int64_t nblk = n_mats * (rows / 128) * (cols / 128);

@@ -62,9 +62,16 @@ struct SavedActs {
 };
 size_t ffn_saved_bytes(const moe_cfg& c);
 SavedActs carve_saved(const moe_cfg& c, void* saved);
-// saved == nullptr: inference forward; else also store a, b and h there
+// saved == nullptr: inference forward; else also store a, b and h there.
+// hf_r / hf_s (FP8 layers, optional): the gate/up epilogue's fp32 h values
+// before quantisation, [T*k][I] and [T][Is]
 hipError_t launch_expert_ffn(const moe_cfg& c, const FfnArgs& a, void* ws, hipStream_t st,
-                             void* saved = nullptr);
+                             void* saved = nullptr, float* hf_r = nullptr,
+                             float* hf_s = nullptr);
+// byte offsets inside the FFN workspace of h as the down GEMM reads it:
+// routed h, shared h, routed tile scales, shared tile scales (FP8 only; the
+// last two are SIZE_MAX for other layers)
+void ffn_h_offsets(const moe_cfg& c, size_t off[4]);
 // device tile list of the grouped GEMMs: routed expert g gets ceil(M_g / BM)
 // tiles (group, first row), then the shared expert's ceil(T / BM); counts[0],
 // counts[1] = their numbers; order = routed tiles by row count, largest first
@@ -186,5 +193,7 @@ hipError_t launch_bias_update(int64_t N, int64_t TK, const int32_t* counts, floa
                               float* bias, hipStream_t st);
 hipError_t launch_quantize_weights(int64_t n_mats, int64_t rows, int64_t cols, const void* w,
                                    uint8_t* q, float* s, hipStream_t st);
+hipError_t launch_e4m3_inspect(const float* v, int64_t n, float scale, uint8_t* c4, uint8_t* c1,
+                               hipStream_t st);
 
 }  // namespace moe

@@ -11,9 +11,10 @@
 //    ascending from +0), so that the chosen indices are reproducible bit for
 //    bit; the chain runs on the VALU (MFMA has no defined summation order).
 //    Epilogue: s = fp32(1 / (1 + exp(-(double)z))).
-//  router_select: one wavefront per token; keys s+b; optional group limit;
-//    k rounds of a wave-wide argmax under the total order (key desc, index
-//    asc); gates in double; per-expert load via integer atomics (order-free).
+//  router_select: one wavefront per token; keys s+b (a NaN key ranks as
+//    -inf); optional group limit; k rounds of a wave-wide argmax under the
+//    total order (key desc, index asc); gates in double; per-expert load via
+//    integer atomics (order-free).
 #include "moe_internal.h"
 
 namespace moe {
@@ -314,6 +315,9 @@ __global__ void __launch_bounds__(256) router_select_kernel(
             sv[r] = st[i];
             float key = sv[r] + bias[i];
             if (key == 0.0f) key = 0.0f;  // -0 -> +0
+            // a NaN key ranks as -inf: it still beats the -inf / 0x7fffffff
+            // start of every argmax below, so the winner is always a real expert
+            if (key != key) key = -__builtin_inff();
             rv[r] = key;
             ok[r] = true;
         } else {
@@ -356,6 +360,7 @@ __global__ void __launch_bounds__(256) router_select_kernel(
             }
             float sc = r1 + r2;
             if (sc == 0.0f) sc = 0.0f;
+            if (sc != sc) sc = -__builtin_inff();  // +inf + -inf ranks like a NaN key
             if (lane == g) my_gscore = sc;
         }
         // keep the TG best groups: TG rounds of argmax over lanes 0..G-1

@@ -17,7 +17,7 @@ import torch
 from . import (MoeCfg, cfg_from_dict, moe_bias_update, moe_combine, moe_combine_backward,
                moe_expert_ffn, moe_expert_ffn_backward, moe_expert_ffn_backward_fp8,
                moe_expert_ffn_backward_fp8_workspace_size, moe_expert_ffn_backward_workspace_size,
-               moe_expert_ffn_train_fp8,
+               moe_expert_ffn_train_fp8, moe_expert_ffn_h_offsets, moe_expert_ffn_inspect,
                moe_expert_ffn_saved_size, moe_expert_ffn_train,
                moe_expert_ffn_workspace_size, moe_input_grad, moe_pack_weights,
                moe_packed_weights_size, moe_permute, moe_permute_workspace_size,
@@ -166,6 +166,41 @@ class MoeLayer:
                        self.w2, self.w2_s, self.y_perm, shared_in if self.y_shared is not None
                        else None, self.x_s if self.y_shared is not None else None, self.ws13,
                        self.ws13_s, self.ws2, self.ws2_s, self.y_shared, self.workspace, stream)
+
+    def expert_ffn_inspect(self, stream=None):
+        """FP8 layers: the expert FFN again through moe_expert_ffn_inspect (same
+        results as expert_ffn) on this step's permuted rows.  Returns a dict:
+        h_f32 / h_f32_shared, the gate/up epilogue's fp32 h before quantisation,
+        and h_q / h_s / h_q_shared / h_s_shared, the E4M3 codes and 1x128 tile
+        scales the down GEMM read (views into the workspace, valid until the
+        next call that uses it)."""
+        if not self.fp8:
+            raise ValueError("expert_ffn_inspect covers FP8 layers")
+        c = self.c
+        T, k, I, Is = c["T"], c["k"], c["I"], self.cfg.inter_shared
+        dev = self.out.device
+        shared = self.y_shared is not None
+        hf = torch.empty((T * k, I), dtype=torch.float32, device=dev)
+        hfs = torch.empty((T, Is), dtype=torch.float32, device=dev) if shared else None
+        moe_expert_ffn_inspect(self.cfg, self.x_perm, self.x_perm_s, self.offsets, self.w13,
+                               self.w13_s, self.w2, self.w2_s, self.y_perm,
+                               self.x_q if shared else None, self.x_s if shared else None,
+                               self.ws13, self.ws13_s, self.ws2, self.ws2_s, self.y_shared, hf,
+                               hfs, self.workspace, stream)
+        off = moe_expert_ffn_h_offsets(self.cfg)
+        ws = self.workspace
+
+        def view(o, n, dtype, shape):
+            b = ws[o:o + n * torch.tensor([], dtype=dtype).element_size()]
+            return b.view(dtype).view(shape)
+
+        out = dict(h_f32=hf, h_f32_shared=hfs,
+                   h_q=view(off[0], T * k * I, torch.uint8, (T * k, I)),
+                   h_s=view(off[2], T * k * (I // 128), torch.float32, (T * k, I // 128)))
+        if shared:
+            out.update(h_q_shared=view(off[1], T * Is, torch.uint8, (T, Is)),
+                       h_s_shared=view(off[3], T * (Is // 128), torch.float32, (T, Is // 128)))
+        return out
 
     def combine(self, x, residual=True, stream=None):
         moe_combine(self.cfg, x if residual else None, self.y_shared, self.y_perm, self.gate,

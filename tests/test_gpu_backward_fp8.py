@@ -2,7 +2,7 @@
 (moe_expert_ffn_backward_fp8 for the experts, through the C ABI) against the
 oracle's FP8 backward on the same seeded inputs and upstream gradient.
 
-Tolerance: the FP8 criterion of parity_util.assert_close_fp8 (rtol 6e-2),
+Tolerance: the FP8 criterion of parity_util.assert_close_fp8_bwd (rtol 6e-2),
 with the elementwise bound at 3 rtol instead of 2.  Both sides re-quantise
 intermediate tensors (h, [da db], the row-direction tiles) from values that
 differ in their last bits (MFMA summation order against exact sums), so a code
@@ -22,7 +22,7 @@ import torch
 
 import moe_inputs
 import sparse_moe_layer_bias_amd as moe
-from parity_util import (assert_close_fp8, assert_close_fp8_grad, host_inputs, log,
+from parity_util import (assert_close_fp8_bwd, assert_close_fp8_grad, host_inputs, log,
                          small_layer_inputs)
 from sparse_moe_layer_bias_amd.layer import MoeLayer
 
@@ -74,7 +74,7 @@ def test_fp8_backward_parity_small(orc, over):
     c, layer, g, ref = _run(orc, **dict(over))
     assert np.array_equal(moe_inputs.to_host(layer.idx), ref["idx"])
     for n in ("dy_perm", "dx_perm", "dx_shared", "dz", "dcentroids", "dx"):
-        assert_close_fp8(moe_inputs.to_host(g[n]), ref[n], n, elem=3.0)
+        assert_close_fp8_bwd(moe_inputs.to_host(g[n]), ref[n], n, elem=3.0)
     for n in ("dw13", "dw2", "dws13", "dws2"):
         assert_close_fp8_grad(moe_inputs.to_host(g[n]), ref[n], n)
 
@@ -84,7 +84,7 @@ def test_fp8_backward_parity_recompute(orc, over):
     """Without kept activations the backward recomputes a, b, h on FP8."""
     c, layer, g, ref = _run(orc, save=False, **dict(over))
     for n in ("dx_perm", "dx_shared", "dx"):
-        assert_close_fp8(moe_inputs.to_host(g[n]), ref[n], n, elem=3.0)
+        assert_close_fp8_bwd(moe_inputs.to_host(g[n]), ref[n], n, elem=3.0)
     for n in ("dw13", "dw2", "dws13", "dws2"):
         assert_close_fp8_grad(moe_inputs.to_host(g[n]), ref[n], n)
 
@@ -106,7 +106,7 @@ def test_fp8_training_forward_is_bitwise_the_inference_forward(T):
 
 def test_fp8_backward_without_residual_and_deterministic(orc):
     c, layer, g, ref = _run(orc, seed=3, residual=False, T=96)
-    assert_close_fp8(moe_inputs.to_host(g["dx"]), ref["dx"], "dx", elem=3.0)
+    assert_close_fp8_bwd(moe_inputs.to_host(g["dx"]), ref["dx"], "dx", elem=3.0)
     first = {n: moe_inputs.to_host(g[n]).copy() for n in ("dx", "dw13", "dw2", "dws13", "dws2")}
     layer.backward(layer.test_dout, layer.test_x, layer.test_centroids, residual=False)
     torch.cuda.synchronize()
@@ -156,7 +156,7 @@ def test_v3_fp8_backward_one_expert_and_sampled_tokens(orc):
     q2, s2 = orc.quant_weight_fp8(moe_inputs.to_host(dev["w2"][e]))
     log("oracle FP8 backward of expert", e, "with", b - a, "rows")
     dA, dw13, dw2 = orc.swiglu_ffn_backward_fp8(xq, xs, xh[src], q13, s13, q2, s2, dy)
-    assert_close_fp8(moe_inputs.to_host(g["dx_perm"][a:b]), dA, "dx_perm rows of expert %d" % e,
+    assert_close_fp8_bwd(moe_inputs.to_host(g["dx_perm"][a:b]), dA, "dx_perm rows of expert %d" % e,
                      elem=3.0)
     assert_close_fp8_grad(moe_inputs.to_host(g["dw13"][e]), dw13, "dw13 of expert %d" % e)
     assert_close_fp8_grad(moe_inputs.to_host(g["dw2"][e]), dw2, "dw2 of expert %d" % e)

@@ -15,8 +15,8 @@ import torch
 
 import moe_inputs
 import sparse_moe_layer_bias_amd as moe
-from parity_util import (RTOL, assert_bits, assert_close, assert_close_fp8, host_inputs, log,
-                         small_layer_inputs)
+from parity_util import (RTOL, assert_bits, assert_close, assert_close_fp8, check_fp8_expert_split,
+                         host_inputs, log, small_layer_inputs)
 from sparse_moe_layer_bias_amd.layer import MoeLayer
 
 pytestmark = pytest.mark.gpu
@@ -31,10 +31,14 @@ def _gpu():
     torch.cuda.synchronize()
 
 
+_last_x = [None]
+
+
 def _run_small(cfg_name, orc, T=None, residual=True, seed=0, **over):
     cfg = dict(moe_inputs.CONFIGS[cfg_name])
     cfg.update(over)
     c, inp, dev = small_layer_inputs(cfg, seed, T)
+    _last_x[0] = inp["x"]
     log("case", cfg_name, "T=%d" % c["T"], over, "seed", seed)
     layer = MoeLayer(c, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"])
     bias = dev["bias"].clone()
@@ -105,15 +109,16 @@ def test_layer_parity_fp8_small(orc, name, over):
     over = dict(over)
     T = over.pop("T", None)
     c, layer, out, bias, ref = _run_small(name, orc, T=T, fp8=True, **over)
-    rtol = RTOL["fp8"]
     assert_bits(moe_inputs.to_host(layer.idx), ref["idx"], "idx")
+    assert_bits(moe_inputs.to_host(layer.gate), ref["gate"], "gate")
     assert_bits(moe_inputs.to_host(layer.x_q), ref["x_q"], "x codes")
     assert_bits(moe_inputs.to_host(layer.x_s).view(np.uint32), ref["x_s"].view(np.uint32),
                 "x scales")
     assert_bits(moe_inputs.to_host(layer.x_perm), ref["x_q_perm"], "permuted codes")
-    assert_close_fp8(moe_inputs.to_host(layer.y_perm), ref["y_perm"], "y_perm")
-    assert_close_fp8(moe_inputs.to_host(layer.y_shared), ref["y_shared"], "y_shared")
-    assert_close_fp8(moe_inputs.to_host(out), ref["out"], "out")
+    assert_bits(moe_inputs.to_host(layer.x_perm_s).view(np.uint32),
+                ref["x_s_perm"].view(np.uint32), "permuted scales")
+    assert_bits(moe_inputs.to_host(layer.dst_row), ref["dst_row"], "dst_row")
+    check_fp8_expert_split(orc, layer, ref, moe_inputs.to_host(_last_x[0]))
     assert_bits(moe_inputs.to_host(bias), ref["new_bias"], "bias after update")
 
 
@@ -153,9 +158,7 @@ def test_fp8_block_scales_far_apart(orc):
     assert np.all(np.isfinite(ref["y_perm"].astype(np.float64))), "oracle overflowed"
     assert_bits(moe_inputs.to_host(layer.idx), ref["idx"], "idx")
     assert_bits(moe_inputs.to_host(layer.x_perm), ref["x_q_perm"], "permuted codes")
-    assert_close_fp8(moe_inputs.to_host(layer.y_perm), ref["y_perm"], "y_perm")
-    assert_close_fp8(moe_inputs.to_host(layer.y_shared), ref["y_shared"], "y_shared")
-    assert_close_fp8(moe_inputs.to_host(out), ref["out"], "out")
+    check_fp8_expert_split(orc, layer, ref, moe_inputs.to_host(inp["x"]))
 
 
 def test_layer_without_residual(orc):
@@ -297,6 +300,65 @@ def test_e4m3_encoder_every_midpoint(orc):
     assert exact.sum() > 100
 
 
+def test_e4m3_encoder_fp32_midpoint_neighbours(orc):
+    """The quantisation step as the kernels apply it (moe_inspect_e4m3: the FP8
+    gate/up epilogue's quotient + four-value conversion, and the activation /
+    weight quantisers' one-value conversion) on fp32 values the bf16 paths
+    cannot carry: every E4M3 midpoint, its fp32 neighbours one ulp either
+    side, the codes themselves, signed zeros, values past +-448 and below the
+    smallest subnormal.  Each 1x128 row's scale comes from the oracle's own
+    quantiser of that row; with an amax of 448 the scale is 1 and the codes are
+    the converter's own.  Rows scaled by 0.37 and 3e-5 exercise the divide."""
+    table = orc.e4m3_decode(np.arange(128, dtype=np.uint8)).astype(np.float64)
+    pos = np.sort(table[np.isfinite(table)])
+    vals = []
+    for a, b in zip(pos[:-1], pos[1:]):
+        m = np.float32((a + b) / 2)
+        vals += [m, np.nextafter(m, np.float32(0)), np.nextafter(m, np.float32(1e9)),
+                 np.float32(a), np.nextafter(np.float32(a), np.float32(1e9))]
+    vals += [0.0, 2.0 ** -11, 2.0 ** -10, 3 * 2.0 ** -11, 448.0]
+    vals = np.array(vals, np.float32)
+    vals = np.concatenate([vals, -vals, np.array([-0.0], np.float32)])
+    n = int(np.ceil(vals.size / 127))
+    flat = np.zeros(n * 127, np.float32)
+    flat[:vals.size] = vals
+    base = np.zeros((n, 128), np.float32)
+    base[:, :127] = np.clip(flat.reshape(n, 127), -448, 448)
+    base[:, 127] = 448.0
+    for f in (1.0, 0.37, 3e-5):
+        rows = (base * np.float32(f)).astype(np.float32)
+        q_ref, s_ref = orc.quant_act_fp8(rows)
+        if f == 1.0:
+            assert np.all(s_ref == 1.0)
+        for r in range(n):
+            v = torch.from_numpy(rows[r]).cuda()
+            c4 = torch.empty(128, dtype=torch.uint8, device="cuda")
+            c1 = torch.empty(128, dtype=torch.uint8, device="cuda")
+            moe.moe_inspect_e4m3(v, float(s_ref[r, 0]), c4, c1)
+            torch.cuda.synchronize()
+            assert_bits(moe_inputs.to_host(c4), q_ref[r], "epilogue codes, row %d, x%g" % (r, f))
+            assert_bits(moe_inputs.to_host(c1), q_ref[r], "quantiser codes, row %d, x%g" % (r, f))
+    # quotients past +-448 are clamped (scale 1: the quotient is the value)
+    big = np.array([448.0, np.nextafter(np.float32(448), 1e9), 449.0, 464.0, 480.0, 1e6, 3e38],
+                   np.float32)
+    big = np.concatenate([big, -big, np.zeros(2, np.float32)])
+    v = torch.from_numpy(big).cuda()
+    c4 = torch.empty(big.size, dtype=torch.uint8, device="cuda")
+    c1 = torch.empty(big.size, dtype=torch.uint8, device="cuda")
+    moe.moe_inspect_e4m3(v, 1.0, c4, c1)
+    torch.cuda.synchronize()
+    ref = orc.e4m3_encode(np.clip(big, -448, 448))
+    assert_bits(moe_inputs.to_host(c4), ref, "clamped (epilogue)")
+    assert_bits(moe_inputs.to_host(c1), ref, "clamped (quantiser)")
+    # an all-zero tile: scale 0, codes 0
+    z = torch.zeros(128, device="cuda")
+    c4 = torch.full((128,), 7, dtype=torch.uint8, device="cuda")
+    c1 = torch.full((128,), 7, dtype=torch.uint8, device="cuda")
+    moe.moe_inspect_e4m3(z, 0.0, c4, c1)
+    torch.cuda.synchronize()
+    assert not moe_inputs.to_host(c4).any() and not moe_inputs.to_host(c1).any()
+
+
 # ------------------------------------------------------------------ bias trajectory
 
 def test_skew_balance_trajectory(orc):
@@ -394,49 +456,99 @@ def v3_fp8_run():
     torch.cuda.empty_cache()
 
 
-def test_v3_fp8_layer_output_sampled_tokens(orc, v3_fp8_run):
+class _ExpertCodes:
+    """The oracle's 128x128 block quantisation of one expert's weights at a time
+    (host copy of the bf16 weights -> oracle quantiser), for ref["w13_q"][e]
+    and the like; the last expert is kept."""
+
+    def __init__(self, orc, w, part):
+        self.orc, self.w, self.part = orc, w, part
+        self.e, self.val = None, None
+
+    def __getitem__(self, e):
+        e = int(e)
+        if self.e != e:
+            self.val = self.orc.quant_weight_fp8(moe_inputs.to_host(self.w[e]))
+            self.e = e
+        return self.val[self.part]
+
+
+def _v3_tokens(cfg, idx, seed, n=64):
+    """n tokens at random plus the first and last, covering all expert groups"""
+    rng = np.random.default_rng(seed)
+    tok = np.unique(np.concatenate([rng.choice(cfg["T"], n, replace=False), [0, cfg["T"] - 1]]))
+    gs = cfg["N"] // cfg["G"]
+    assert len(np.unique(idx[tok] // gs)) == cfg["G"], "sample misses a group"
+    return tok
+
+
+def _check_v3_routing(orc, cfg, dev, layer, bias0, with_scores):
+    """scores (when kept), idx, gates and counts of the whole batch against the
+    oracle, bit for bit; then offsets, src_token and dst_row against the
+    oracle's permutation of the oracle's indices."""
+    xh = moe_inputs.to_host(dev["x"])
+    r = orc.route(xh, moe_inputs.to_host(dev["centroids"]), moe_inputs.to_host(bias0),
+                  cfg["k"], cfg["G"], cfg["TG"], want_scores=with_scores)
+    log("oracle routed the whole batch")
+    if with_scores:
+        assert_bits(moe_inputs.to_host(layer.scores), r["scores"], "scores (all tokens)")
+    assert_bits(moe_inputs.to_host(layer.idx), r["idx"], "idx (all tokens)")
+    assert_bits(moe_inputs.to_host(layer.gate), r["gate"], "gate (all tokens)")
+    assert_bits(moe_inputs.to_host(layer.counts), r["counts"], "counts")
+    off, src, dst = orc.permute(r["idx"], cfg["N"])
+    assert_bits(moe_inputs.to_host(layer.offsets), off, "offsets")
+    assert_bits(moe_inputs.to_host(layer.src_token), src, "src_token")
+    assert_bits(moe_inputs.to_host(layer.dst_row), dst, "dst_row")
+    r.update(offsets=off, src_token=src, dst_row=dst)
+    return xh, r
+
+
+@pytest.mark.timeout(900)
+def test_v3_fp8_layer_parity(orc, v3_fp8_run):
+    """The V3-shaped FP8 layer: routing of all 8192 tokens and the activation
+    codes and scales of every token bit for bit; the expert FFN step by step
+    (fp32 h, h bytes, y, out) on the routed rows of 64+ tokens that cover all
+    8 groups, and every shared-expert row of those tokens."""
     cfg, dev, layer, bias0, bias = v3_fp8_run
-    rng = np.random.default_rng(3)
-    tok = np.unique(np.concatenate([rng.choice(cfg["T"], 6, replace=False), [cfg["T"] - 1]]))
-    ti = torch.from_numpy(tok).cuda()
-    xh = moe_inputs.to_host(dev["x"][ti])
-    r = orc.route(xh, moe_inputs.to_host(dev["centroids"]), moe_inputs.to_host(bias0),
-                  cfg["k"], cfg["G"], cfg["TG"])
-    assert_bits(moe_inputs.to_host(layer.idx)[tok], r["idx"], "idx (sampled)")
+    xh, r = _check_v3_routing(orc, cfg, dev, layer, bias0, with_scores=False)
     xq, xs = orc.quant_act_fp8(xh)
-    assert_bits(moe_inputs.to_host(layer.x_q[ti]), xq, "x codes (sampled)")
-    q13, s13 = orc.quant_weight_fp8(moe_inputs.to_host(dev["ws13"]))
-    q2, s2 = orc.quant_weight_fp8(moe_inputs.to_host(dev["ws2"]))
-    ys = orc.swiglu_ffn_fp8(xq, xs, q13, s13, q2, s2)
-    assert_close_fp8(moe_inputs.to_host(layer.y_shared[ti]), ys, "y_shared (sampled)")
-    yp_ref = np.zeros((len(tok), cfg["k"], cfg["d"]), np.uint16)
-    for e in np.unique(r["idx"]):
-        sel = np.argwhere(r["idx"] == e)
-        q13, s13 = orc.quant_weight_fp8(moe_inputs.to_host(dev["w13"][int(e)]))
-        q2, s2 = orc.quant_weight_fp8(moe_inputs.to_host(dev["w2"][int(e)]))
-        yp_ref[sel[:, 0], sel[:, 1]] = orc.swiglu_ffn_fp8(xq[sel[:, 0]], xs[sel[:, 0]], q13, s13,
-                                                          q2, s2)
-    dst = moe_inputs.to_host(layer.dst_row)[tok]
-    yp_gpu = moe_inputs.to_host(layer.y_perm[torch.from_numpy(dst.ravel()).long().cuda()])
-    assert_close_fp8(yp_gpu.reshape(-1, cfg["d"]), yp_ref.reshape(-1, cfg["d"]),
-                     "y_perm (sampled)")
-    k = cfg["k"]
-    fake_dst = np.arange(len(tok) * k, dtype=np.int32).reshape(len(tok), k)
-    out_ref = orc.combine(xh, ys, yp_ref.reshape(-1, cfg["d"]), r["gate"], fake_dst, "bf16")
-    assert_close_fp8(moe_inputs.to_host(layer.out[ti]), out_ref, "out (sampled)")
+    assert_bits(moe_inputs.to_host(layer.x_q), xq, "x codes (all tokens)")
+    assert_bits(moe_inputs.to_host(layer.x_s).view(np.uint32), xs.view(np.uint32),
+                "x scales (all tokens)")
+    src = r["src_token"]
+    rows = np.random.default_rng(4).choice(cfg["T"] * cfg["k"], 4096, replace=False)
+    rt = torch.from_numpy(rows).cuda()
+    assert_bits(moe_inputs.to_host(layer.x_perm[rt]), xq[src[rows]], "permuted codes (rows)")
+    assert_bits(moe_inputs.to_host(layer.x_perm_s[rt]).view(np.uint32),
+                xs[src[rows]].view(np.uint32), "permuted scales (rows)")
+    tok = _v3_tokens(cfg, r["idx"], 3)
+    rows = np.sort(r["dst_row"][tok].ravel())
+    ref = dict(r, x_q=xq, x_s=xs,
+               w13_q=_ExpertCodes(orc, dev["w13"], 0), w13_s=_ExpertCodes(orc, dev["w13"], 1),
+               w2_q=_ExpertCodes(orc, dev["w2"], 0), w2_s=_ExpertCodes(orc, dev["w2"], 1))
+    ref["x_q_perm"] = _RowsOf(xq, src)
+    ref["x_s_perm"] = _RowsOf(xs, src)
+    ref["ws13_q"], ref["ws13_s"] = orc.quant_weight_fp8(moe_inputs.to_host(dev["ws13"]))
+    ref["ws2_q"], ref["ws2_s"] = orc.quant_weight_fp8(moe_inputs.to_host(dev["ws2"]))
+    log("checking the expert FFN on %d routed rows of %d tokens" % (len(rows), len(tok)))
+    check_fp8_expert_split(orc, layer, ref, xh, rows=rows, what="V3 FP8: ")
+    new_b = orc.bias_update(r["counts"], cfg["T"] * cfg["k"], moe_inputs.to_host(bias0))
+    assert_bits(moe_inputs.to_host(bias).view(np.uint32), new_b.view(np.uint32), "bias update")
 
 
-def test_v3_routing_sampled_tokens(orc, v3_run):
+class _RowsOf:
+    """rows of a host array through an index map (a gather the oracle did)"""
+
+    def __init__(self, a, src):
+        self.a, self.src = a, src
+
+    def __getitem__(self, r):
+        return self.a[self.src[r]]
+
+
+def test_v3_routing_all_tokens(orc, v3_run):
     cfg, dev, layer, bias0, bias = v3_run
-    rng = np.random.default_rng(0)
-    tok = np.sort(rng.choice(cfg["T"], 384, replace=False))
-    tok = np.unique(np.concatenate([tok, [0, cfg["T"] - 1]]))
-    xh = moe_inputs.to_host(dev["x"][torch.from_numpy(tok).cuda()])
-    r = orc.route(xh, moe_inputs.to_host(dev["centroids"]), moe_inputs.to_host(bias0),
-                  cfg["k"], cfg["G"], cfg["TG"], want_scores=True)
-    assert_bits(moe_inputs.to_host(layer.scores)[tok], r["scores"], "scores (sampled)")
-    assert_bits(moe_inputs.to_host(layer.idx)[tok], r["idx"], "idx (sampled)")
-    assert_bits(moe_inputs.to_host(layer.gate)[tok], r["gate"], "gate (sampled)")
+    _check_v3_routing(orc, cfg, dev, layer, bias0, with_scores=True)
 
 
 def test_v3_permutation_properties(orc, v3_run):
@@ -445,17 +557,13 @@ def test_v3_permutation_properties(orc, v3_run):
     idx = moe_inputs.to_host(layer.idx)
     counts = moe_inputs.to_host(layer.counts)
     assert counts.sum() == T * k
-    assert_bits(counts, np.bincount(idx.ravel(), minlength=N).astype(np.int32), "counts")
     for row in idx[:: 97]:
         assert len(set(row)) == k
     # group limit: each token's experts lie in at most TG groups
     gs = N // cfg["G"]
     assert max(len(set(row // gs)) for row in idx) <= cfg["TG"]
-    off, src, dst = orc.permute(idx, N)
-    assert_bits(moe_inputs.to_host(layer.offsets), off, "offsets")
-    assert_bits(moe_inputs.to_host(layer.src_token), src, "src_token")
-    assert_bits(moe_inputs.to_host(layer.dst_row), dst, "dst_row")
-    rows = np.random.default_rng(1).choice(T * k, 2000, replace=False)
+    src = moe_inputs.to_host(layer.src_token)
+    rows = np.random.default_rng(1).choice(T * k, 4000, replace=False)
     xp = moe_inputs.to_host(layer.x_perm[torch.from_numpy(rows).cuda()])
     xs = moe_inputs.to_host(dev["x"][torch.from_numpy(src[rows]).long().cuda()])
     assert_bits(xp, xs, "x_perm rows")
@@ -463,33 +571,96 @@ def test_v3_permutation_properties(orc, v3_run):
     assert_bits(moe_inputs.to_host(bias).view(np.uint32), new_b.view(np.uint32), "bias update")
 
 
+@pytest.mark.timeout(900)
 def test_v3_layer_output_sampled_tokens(orc, v3_run):
+    """Expert outputs and the layer output of 64+ tokens that cover all 8
+    groups (every routed row of those tokens, one expert at a time)."""
     cfg, dev, layer, bias0, bias = v3_run
-    rng = np.random.default_rng(2)
-    tok = np.unique(np.concatenate([rng.choice(cfg["T"], 10, replace=False),
-                                    [0, cfg["T"] - 1]]))
-    h = {"x": moe_inputs.to_host(dev["x"][torch.from_numpy(tok).cuda()])}
-    r = orc.route(h["x"], moe_inputs.to_host(dev["centroids"]), moe_inputs.to_host(bias0),
+    xh_all = moe_inputs.to_host(dev["x"])
+    r = orc.route(xh_all, moe_inputs.to_host(dev["centroids"]), moe_inputs.to_host(bias0),
                   cfg["k"], cfg["G"], cfg["TG"])
+    assert_bits(moe_inputs.to_host(layer.idx), r["idx"], "idx (all tokens)")
+    tok = _v3_tokens(cfg, r["idx"], 2)
+    tt = torch.from_numpy(tok).cuda()
+    xh = xh_all[tok]
     ws13 = moe_inputs.to_host(dev["ws13"])
     ws2 = moe_inputs.to_host(dev["ws2"])
-    ys = orc.swiglu_ffn(h["x"], ws13, ws2)
-    assert_close(moe_inputs.to_host(layer.y_shared[torch.from_numpy(tok).cuda()]), ys,
-                 RTOL["bf16"], "y_shared (sampled)")
+    ys = orc.swiglu_ffn(xh, ws13, ws2)
+    assert_close(moe_inputs.to_host(layer.y_shared[tt]), ys, RTOL["bf16"], "y_shared (sampled)")
     # routed expert outputs for the sampled tokens, one expert at a time
+    idx = r["idx"][tok]
     yp_ref = np.zeros((len(tok), cfg["k"], cfg["d"]), np.uint16)
-    for e in np.unique(r["idx"]):
-        sel = np.argwhere(r["idx"] == e)
-        rows = h["x"][sel[:, 0]]
-        y = orc.swiglu_ffn(rows, moe_inputs.to_host(dev["w13"][int(e)]),
+    experts = np.unique(idx)
+    log("oracle: %d experts for %d tokens" % (len(experts), len(tok)))
+    for n, e in enumerate(experts):
+        sel = np.argwhere(idx == e)
+        y = orc.swiglu_ffn(xh[sel[:, 0]], moe_inputs.to_host(dev["w13"][int(e)]),
                            moe_inputs.to_host(dev["w2"][int(e)]))
         yp_ref[sel[:, 0], sel[:, 1]] = y
+        if n % 32 == 0:
+            log("  expert %d of %d" % (n, len(experts)))
     dst = moe_inputs.to_host(layer.dst_row)[tok]
     yp_gpu = moe_inputs.to_host(layer.y_perm[torch.from_numpy(dst.ravel()).long().cuda()])
     assert_close(yp_gpu.reshape(yp_ref.shape), yp_ref, RTOL["bf16"], "y_perm (sampled)")
     # combine from the oracle's own expert outputs
     k = cfg["k"]
     fake_dst = np.arange(len(tok) * k, dtype=np.int32).reshape(len(tok), k)
-    out_ref = orc.combine(h["x"], ys, yp_ref.reshape(-1, cfg["d"]), r["gate"], fake_dst, "bf16")
-    assert_close(moe_inputs.to_host(layer.out[torch.from_numpy(tok).cuda()]), out_ref,
-                 RTOL["bf16"], "out (sampled)")
+    out_ref = orc.combine(xh, ys, yp_ref.reshape(-1, cfg["d"]), r["gate"][tok], fake_dst, "bf16")
+    assert_close(moe_inputs.to_host(layer.out[tt]), out_ref, RTOL["bf16"], "out (sampled)")
+
+
+@pytest.mark.timeout(900)
+def test_decode_batch_layer_v3_weights(orc, v3_run):
+    """The skewed decode-step workload as a whole layer: T = 128 tokens of the
+    Zipf-skewed router (no group limit) over the V3-shaped experts, with the
+    bias the oracle's own 100 balancing steps reach, so that most experts get
+    1-10 rows (a few rows per 320-row tile).  idx, gates and counts of all
+    tokens bit for bit; routed and shared expert outputs and the layer output
+    of 24 tokens (every routed row of each) within the bf16 tolerance."""
+    cfg5 = dict(moe_inputs.CONFIGS["skew_balance"])
+    _, dev, _, _, _ = v3_run
+    T, N, k = cfg5["T"], cfg5["N"], cfg5["k"]
+    E = moe_inputs.make_skew_centroids(cfg5, 0, "cpu")
+    Eh = moe_inputs.to_host(E)
+    bh = np.zeros(N, np.float32)
+    for step in range(cfg5["steps"]):
+        r = orc.route(moe_inputs.to_host(moe_inputs.make_skew_tokens(cfg5, step, 0, "cpu")), Eh,
+                      bh, k)
+        bh = orc.bias_update(r["counts"], T * k, bh)
+    x = moe_inputs.make_skew_tokens(cfg5, cfg5["steps"], 0, "cpu")
+    xh = moe_inputs.to_host(x)
+    xd = x.cuda()
+    layer = MoeLayer(cfg5, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"])
+    bias = torch.from_numpy(bh.copy()).cuda()
+    out = layer.forward(xd, E.cuda(), bias)
+    torch.cuda.synchronize()
+    r = orc.route(xh, Eh, bh, k)
+    assert_bits(moe_inputs.to_host(layer.idx), r["idx"], "idx")
+    assert_bits(moe_inputs.to_host(layer.gate), r["gate"], "gate")
+    assert_bits(moe_inputs.to_host(layer.counts), r["counts"], "counts")
+    touched = int((r["counts"] > 0).sum())
+    log("decode batch: %d of %d experts touched, max rows %d" % (touched, N, r["counts"].max()))
+    assert touched > N // 2
+    off, src, dst = orc.permute(r["idx"], N)
+    assert_bits(moe_inputs.to_host(layer.dst_row), dst, "dst_row")
+    tok = np.sort(np.random.default_rng(7).choice(T, 24, replace=False))
+    tt = torch.from_numpy(tok).cuda()
+    ys = orc.swiglu_ffn(xh[tok], moe_inputs.to_host(dev["ws13"]), moe_inputs.to_host(dev["ws2"]))
+    assert_close(moe_inputs.to_host(layer.y_shared[tt]), ys, RTOL["bf16"], "y_shared")
+    idx = r["idx"][tok]
+    yp_ref = np.zeros((len(tok), k, cfg5["d"]), np.uint16)
+    for e in np.unique(idx):
+        sel = np.argwhere(idx == e)
+        yp_ref[sel[:, 0], sel[:, 1]] = orc.swiglu_ffn(
+            xh[tok][sel[:, 0]], moe_inputs.to_host(dev["w13"][int(e)]),
+            moe_inputs.to_host(dev["w2"][int(e)]))
+    yp_gpu = moe_inputs.to_host(layer.y_perm[torch.from_numpy(dst[tok].ravel()).long().cuda()])
+    assert_close(yp_gpu.reshape(yp_ref.shape), yp_ref, RTOL["bf16"], "y_perm")
+    fake = np.arange(len(tok) * k, dtype=np.int32).reshape(len(tok), k)
+    out_ref = orc.combine(xh[tok], ys, yp_ref.reshape(-1, cfg5["d"]), r["gate"][tok], fake,
+                          "bf16")
+    assert_close(moe_inputs.to_host(out[tt]), out_ref, RTOL["bf16"], "out")
+    assert_bits(moe_inputs.to_host(bias).view(np.uint32),
+                orc.bias_update(r["counts"], T * k, bh).view(np.uint32), "bias update")
+    del layer
+    torch.cuda.empty_cache()
