@@ -130,6 +130,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time the layer's backward (four calls) instead of the forward step")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="measure the headline workload only (no v3_fp8, skew_balance, "
+                         "tiny_fp32, mid_bf16 block)")
     ap.add_argument("--no-probes", action="store_true",
                     help="skip the measured-peak probes (HBM read, MFMA loop)")
     ap.add_argument("--traffic-run", action="store_true",
@@ -394,9 +397,9 @@ def traffic_run(cfg, layer, dev, backward=False):
     torch.cuda.synchronize()
 
 
-def cpu_baseline(cfg, dev, log):
+def cpu_baseline(cfg, dev, log, rows=4096):
     """Time the oracle (untuned) on a bounded sample of the workload and scale
-    to tokens/s: route, permute and combine on S tokens; the SwiGLU expert on S
+    to tokens/s: route, permute and combine on S tokens; the SwiGLU expert on R
     rows of expert 0, counted k+1 times per token (k routed rows + the shared
     expert row)."""
     import numpy as np
@@ -405,7 +408,7 @@ def cpu_baseline(cfg, dev, log):
     from oracle import oracle as orc
 
     S = cfg["T"]          # every token of the batch for route / permute / combine
-    R = min(4096, S)      # rows through the oracle's SwiGLU expert
+    R = min(rows, S)      # rows through the oracle's SwiGLU expert
     xs = moe_inputs.to_host(dev["x"][:S])
     E = moe_inputs.to_host(dev["centroids"])
     b = moe_inputs.to_host(dev["bias"])
@@ -584,6 +587,196 @@ def run_backward(args, cfg, dev, log):
     print(json.dumps(result), flush=True)
 
 
+STAGES = ["route", "permute", "expert_ffn", "combine", "bias_update"]
+
+
+def load_stats(counts, T, k):
+    """max/mean load and idle experts of one step's per-expert counts"""
+    mean = T * k / len(counts)
+    return {"max_over_mean": float(max(counts)) / mean, "idle_experts": int(sum(c == 0 for c in counts))}
+
+
+def skew_balance(args, dev, log):
+    """The skewed decode-step workload: 100 steps of route + end-of-step bias
+    update over fresh T = 128 batches with Zipf(1.2)-skewed expert popularity
+    (moe_route + moe_bias_update only, timed), the load trajectory (replayed
+    untimed: the same steps give the same bits), the fitted popularity slope at
+    b = 0, and the whole layer at T = 128 with the V3-shaped experts."""
+    import numpy as np
+    import torch
+
+    import moe_inputs
+    import sparse_moe_layer_bias_amd as moe
+    from sparse_moe_layer_bias_amd.layer import MoeLayer
+
+    c5 = dict(moe_inputs.CONFIGS["skew_balance"])
+    T, N, k, steps = c5["T"], c5["N"], c5["k"], c5["steps"]
+    E = moe_inputs.make_skew_centroids(c5, args.seed, "cpu").cuda()
+    xs = [moe_inputs.make_skew_tokens(c5, s, args.seed, "cuda") for s in range(steps + 1)]
+    cfg = moe.cfg_from_dict(c5)
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gate = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    counts = torch.empty((N,), dtype=torch.int32, device="cuda")
+    ws = torch.empty((max(moe.moe_route_workspace_size(cfg), 256),), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def run(record=None):
+        bias = torch.zeros(N, device="cuda")
+        for s in range(steps):
+            moe.moe_route(cfg, xs[s], E, bias, None, idx, gate, counts, ws)
+            if record is not None:
+                record[s].copy_(counts)
+            moe.moe_bias_update(N, T * k, counts, 0.001, bias)
+        if record is not None:  # the routing after the last update
+            moe.moe_route(cfg, xs[steps], E, bias, None, idx, gate, counts, ws)
+            record[steps].copy_(counts)
+        return bias
+
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us_step = e0.elapsed_time(e1) * 1e3 / steps
+    rec = torch.empty((steps + 1, N), dtype=torch.int32, device="cuda")
+    bias_end = run(rec)
+    torch.cuda.synchronize()
+    cnt = rec.cpu().numpy()
+    traj = {str(s): load_stats(cnt[s], T, k) for s in (0, steps // 2, steps)}
+    # popularity at b = 0: top-1 choice of every token of every batch
+    top1 = np.zeros(N, np.int64)
+    zero = torch.zeros(N, device="cuda")
+    for s in range(steps + 1):
+        moe.moe_route(cfg, xs[s], E, zero, None, idx, gate, counts, ws)
+        top1 += np.bincount(idx[:, 0].cpu().numpy(), minlength=N)
+    f = np.sort(top1)[::-1]
+    f = f[f > 0]
+    rank = np.arange(1, len(f) + 1)
+    slope = float(np.polyfit(np.log(rank), np.log(f / f.sum()), 1)[0])
+    log("skew balance: %.1f us/step; load %s; top-1 popularity slope %.2f" %
+        (us_step, json.dumps(traj), slope))
+    # the whole layer at T = 128 over the V3-shaped experts, bias from the trajectory
+    lay = MoeLayer(c5, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"])
+    x = xs[steps]
+    b = bias_end.clone()
+    ms, st = time_forward(lay, x, E, b, 20, 3)
+    touched = int((lay.counts > 0).sum().item())
+    d, I, Is = c5["d"], c5["I"], c5["Is"]
+    wbytes = 2.0 * 3 * d * (touched * I + Is)
+    log("decode layer T=128: %.3f ms/step, %d experts touched, stages %s" %
+        (ms, touched, json.dumps({a: round(v, 4) for a, v in st.items()})))
+    del lay
+    torch.cuda.empty_cache()
+    return {"route_plus_bias_update_us_per_step": us_step,
+            "load": traj, "load_steps": "routing at steps 0, %d and %d (after that many updates)"
+                                        % (steps // 2, steps),
+            "zipf_slope_top1_b0": slope,
+            "layer_T128_v3_experts": {
+                "ms_per_step": ms, "tokens_per_s": T / (ms / 1e3), "stages_ms": st,
+                "experts_touched": touched,
+                "expert_weight_GBps": wbytes / (st["expert_ffn"] / 1e3) / 1e9}}
+
+
+def extra_configs(args, dev, log):
+    """The other four workloads, measured in the same run after the headline
+    one: V3 with FP8 expert GEMMs (its own roofline and oracle time), the
+    skewed decode-step balance workload, and the two small layers."""
+    import torch
+
+    import moe_inputs
+    from sparse_moe_layer_bias_amd.layer import MoeLayer
+
+    out = {}
+    c4 = dict(moe_inputs.CONFIGS["v3_fp8"])
+    lay = MoeLayer(c4, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"])
+    ms, st = time_forward(lay, dev["x"], dev["centroids"], dev["bias"].clone(), 10, 3)
+    del lay
+    torch.cuda.empty_cache()
+    out["v3_fp8"] = {"ms_per_step": ms, "tokens_per_s": c4["T"] / (ms / 1e3), "stages_ms": st,
+                     "roofline": ffn_roofline(c4, st["expert_ffn"] / 1e3, "v3_fp8")}
+    log("v3_fp8: %.3f ms/step, stages %s" % (ms, json.dumps({a: round(v, 4)
+                                                              for a, v in st.items()})))
+    if not args.no_cpu_baseline:
+        try:
+            out["v3_fp8"]["cpu_baseline"] = cpu_baseline(c4, dev, log, rows=512)
+        except Exception as ex:  # report, never hide
+            log("cpu baseline (fp8) failed:", repr(ex))
+            out["v3_fp8"]["cpu_baseline"] = None
+    out["skew_balance"] = skew_balance(args, dev, log)
+    for name in ("tiny_fp32", "mid_bf16"):
+        c = dict(moe_inputs.CONFIGS[name])
+        d2 = moe_inputs.make_layer_inputs(c, args.seed, "cuda")
+        lay = MoeLayer(c, d2["w13"], d2["w2"], d2["ws13"], d2["ws2"])
+        ms, st = time_forward(lay, d2["x"], d2["centroids"], d2["bias"].clone(), 20, 5)
+        out[name] = {"ms_per_step": ms, "tokens_per_s": c["T"] / (ms / 1e3), "stages_ms": st}
+        log("%s: %.4f ms/step" % (name, ms))
+        del lay, d2
+    return out
+
+
+def time_forward(layer, x, E, bias, steps, warmup):
+    """W untimed steps, then K whole steps timed with HIP events on the stream
+    the calls are enqueued on (one event pair around the K steps, and one
+    event between consecutive stages of each step).  Returns ms per step and
+    the mean ms of each stage."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        layer.forward(x, E, bias)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
+          for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for s in range(steps):
+        e = ev[s]
+        e[0].record(stream)
+        layer.route(x, E, bias)
+        e[1].record(stream)
+        layer.permute(x)
+        e[2].record(stream)
+        layer.expert_ffn(x)
+        e[3].record(stream)
+        layer.combine(x)
+        e[4].record(stream)
+        layer.bias_update(bias)
+        e[5].record(stream)
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_stop) / steps
+    stage_ms = {st: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps
+                for i, st in enumerate(STAGES)}
+    return ms_per_step, stage_ms
+
+
+def ffn_roofline(cfg, ffn_s, workload):
+    """The expert FFN call (both grouped GEMM launches and the tile map) against
+    the roofline that bounds its algorithmic work: the larger of the time at
+    the MFMA peak of its dtype and the time at the HBM peak."""
+    fp8 = bool(cfg.get("fp8"))
+    flops = ffn_flops(cfg)
+    achieved = flops / ffn_s
+    peak = PEAK["fp8" if fp8 else "bf16"]
+    nbytes = ffn_bytes(cfg)
+    if nbytes / PEAK["hbm"] > flops / peak:
+        roof = {"bound": "hbm", "achieved": nbytes / ffn_s / 1e9, "peak": PEAK["hbm"] / 1e9,
+                "unit": "GB/s", "frac": nbytes / ffn_s / PEAK["hbm"]}
+    else:
+        roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12,
+                "unit": "TFLOP/s", "frac": achieved / peak}
+    roof.update({"kernel": "grouped expert GEMMs (gate/up+SwiGLU, down)%s" %
+                           (", FP8 E4M3" if fp8 else ""),
+                 "traffic": recorded_traffic(workload),
+                 "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+                 "mfma_tflops": achieved / 1e12, "mfma_frac": achieved / peak})
+    return roof
+
+
 def main():
     args = parse()
     if args.stats_summary:
@@ -635,59 +828,16 @@ def main():
         log("counter run done")
         return
 
-    for _ in range(args.warmup):
-        layer.forward(x, E, bias)
-    torch.cuda.synchronize()
-    log("warmup done")
-
-    # timed region: K whole steps; events bracket each stage on the stream
-    stages = ["route", "permute", "expert_ffn", "combine", "bias_update"]
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
-          for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for s in range(args.steps):
-        e = ev[s]
-        e[0].record(stream)
-        layer.route(x, E, bias)
-        e[1].record(stream)
-        layer.permute(x)
-        e[2].record(stream)
-        layer.expert_ffn(x)
-        e[3].record(stream)
-        layer.combine(x)
-        e[4].record(stream)
-        layer.bias_update(bias)
-        e[5].record(stream)
-    t_stop.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_stop)
-    ms_per_step = total_ms / args.steps
-    stage_ms = {st: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps))
-                / args.steps for i, st in enumerate(stages)}
-    log("stages ms:", json.dumps({k: round(v, 4) for k, v in stage_ms.items()}))
-
+    ms_per_step, stage_ms = time_forward(layer, x, E, bias, args.steps, args.warmup)
+    log("warmup done; stages ms:", json.dumps({k: round(v, 4) for k, v in stage_ms.items()}))
     fp8 = bool(cfg.get("fp8"))
+    roof = ffn_roofline(cfg, stage_ms["expert_ffn"] / 1e3, args.workload)
     flops = ffn_flops(cfg)
-    ffn_s = stage_ms["expert_ffn"] / 1e3
-    achieved = flops / ffn_s
     peak = PEAK["fp8" if fp8 else "bf16"]
     nbytes = ffn_bytes(cfg)
-    # the binding roofline: the larger of time at the MFMA peak and time at
-    # the HBM peak for the call's algorithmic flops and bytes
-    hbm_bound = nbytes / PEAK["hbm"] > flops / peak
-    if hbm_bound:
-        roof = {"bound": "hbm", "achieved": nbytes / ffn_s / 1e9, "peak": PEAK["hbm"] / 1e9,
-                "unit": "GB/s", "frac": nbytes / ffn_s / PEAK["hbm"]}
-    else:
-        roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12,
-                "unit": "TFLOP/s", "frac": achieved / peak}
-    roof.update({"kernel": "grouped expert GEMMs (gate/up+SwiGLU, down)",
-                 "traffic": recorded_traffic(args.workload),
-                 "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
-                 "mfma_tflops": achieved / 1e12, "mfma_frac": achieved / peak})
+    ffn_s = stage_ms["expert_ffn"] / 1e3
+    achieved = flops / ffn_s
+    hbm_bound = roof["bound"] == "hbm"
     if not args.no_probes:
         # the same ceilings measured on this GPU, after the timed region: the
         # HBM read rate of the GEMMs' global -> LDS copies alone, and the rate
@@ -731,6 +881,10 @@ def main():
         except Exception as ex:  # report, never hide
             log("cpu baseline failed:", repr(ex))
             result["cpu_baseline"] = None
+    if args.workload == "v3_bf16" and not args.no_configs:
+        del layer
+        torch.cuda.empty_cache()
+        result["configs"] = extra_configs(args, dev, log)
     print(json.dumps(result), flush=True)
 
 
