@@ -22,7 +22,8 @@
  * Common rules for every call:
  *  - Every pointer argument is a DEVICE pointer owned by the caller, except
  *    `cfg`, which is a host pointer read during the call only.  The library
- *    allocates no memory and keeps no state between calls (it is thread-safe).
+ *    allocates no memory and keeps no state between calls (it is thread-safe);
+ *    the one exception is moe_permute_noalloc's built-in per-GPU scratch.
  *  - Tensors are dense, row-major, contiguous, 16-byte aligned.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *    enqueue work; they never synchronise the host.  Counts and offsets stay
@@ -125,6 +126,23 @@ int moe_permute(const moe_cfg* cfg, const void* x, const int32_t* idx, int32_t* 
                 int32_t* src_token, int32_t* dst_row, void* x_perm, float* x_perm_scale,
                 uint8_t* x_q, float* x_s, void* workspace, size_t workspace_bytes,
                 void* stream);
+
+/* moe_permute for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without the workspace, the same results bit for bit.
+ * Its scratch (the per-(token, slot) ranks and per-64-token-block histograms
+ * moe_permute keeps in the workspace) is a device-resident array built into
+ * the library, one per GPU, held until the process ends; the call allocates
+ * nothing.  Limit: moe_permute_workspace_size(cfg) <= moe_permute_noalloc_max_bytes()
+ * (8 MiB: at N = 256 about 170k tokens of top-8), else MOE_ERR_WORKSPACE
+ * and nothing is enqueued.  Every call on one GPU uses that GPU's array:
+ * calls that overlap on one GPU (concurrent streams, or threads) race; calls
+ * on one stream are ordered and safe.  Errors as moe_permute, plus MOE_ERR_HIP
+ * if the array's device address cannot be obtained. */
+size_t moe_permute_noalloc_max_bytes(void);
+int moe_permute_noalloc(const moe_cfg* cfg, const void* x, const int32_t* idx, int32_t* offsets,
+                        int32_t* src_token, int32_t* dst_row, void* x_perm, float* x_perm_scale,
+                        uint8_t* x_q, float* x_s, void* stream);
 
 /* ------------------------------------------------------------- expert FFN */
 

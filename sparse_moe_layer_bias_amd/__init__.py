@@ -89,6 +89,8 @@ def lib():
             "moe_expert_ffn_h_offsets": ([C, ctypes.POINTER(SZ)], ctypes.c_int),
             "moe_expert_ffn_inspect": ([C] + [P] * 17 + [P, SZ, P], ctypes.c_int),
             "moe_inspect_e4m3": ([P, I64, F, P, P, P], ctypes.c_int),
+            "moe_permute_noalloc_max_bytes": ([], SZ),
+            "moe_permute_noalloc": ([C, P, P, P, P, P, P, P, P, P, P], ctypes.c_int),
             "moe_last_error": ([], ctypes.c_char_p),
             "moe_abi_version": ([], ctypes.c_int),
         }
@@ -146,6 +148,17 @@ def moe_permute(cfg, x, idx, offsets, src_token, dst_row, x_perm, x_perm_scale=N
     _check(lib().moe_permute(ctypes.byref(cfg), _p(x), _p(idx), _p(offsets), _p(src_token),
                              _p(dst_row), _p(x_perm), _p(x_perm_scale), _p(x_q), _p(x_s),
                              _p(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def moe_permute_noalloc_max_bytes():
+    return lib().moe_permute_noalloc_max_bytes()
+
+
+def moe_permute_noalloc(cfg, x, idx, offsets, src_token, dst_row, x_perm, x_perm_scale=None,
+                        x_q=None, x_s=None, stream=None):
+    _check(lib().moe_permute_noalloc(ctypes.byref(cfg), _p(x), _p(idx), _p(offsets),
+                                     _p(src_token), _p(dst_row), _p(x_perm), _p(x_perm_scale),
+                                     _p(x_q), _p(x_s), _stream(stream)))
 
 
 def moe_expert_ffn_workspace_size(cfg):

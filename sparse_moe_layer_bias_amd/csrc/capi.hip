@@ -187,6 +187,43 @@ int moe_permute(const moe_cfg* cfg, const void* x, const int32_t* idx, int32_t* 
                                               (hipStream_t)stream));
 }
 
+size_t moe_permute_noalloc_max_bytes(void) { return moe::PERM_SCRATCH_BYTES; }
+
+int moe_permute_noalloc(const moe_cfg* cfg, const void* x, const int32_t* idx, int32_t* offsets,
+                        int32_t* src_token, int32_t* dst_row, void* x_perm, float* x_perm_scale,
+                        uint8_t* x_q, float* x_s, void* stream) {
+    const char* fn = "moe_permute_noalloc";
+    if (int r = check_cfg(fn, cfg)) return r;
+    REQ_PTR(offsets);
+    if (cfg->tokens > 0) {
+        REQ_PTR(x);
+        REQ_PTR(idx);
+        REQ_PTR(src_token);
+        REQ_PTR(dst_row);
+        REQ_PTR(x_perm);
+        if (cfg->gemm_dtype == MOE_FP8_E4M3) {
+            if (cfg->hidden % 128)
+                return fail(MOE_ERR_UNSUPPORTED, "%s: FP8 needs hidden %% 128 == 0", fn);
+            REQ_PTR(x_perm_scale);
+            REQ_PTR(x_q);
+            REQ_PTR(x_s);
+        }
+    }
+    const size_t need = moe_permute_workspace_size(cfg);
+    if (need > moe::PERM_SCRATCH_BYTES)
+        return fail(MOE_ERR_WORKSPACE,
+                    "%s: this shape needs %zu bytes of scratch, above the built-in %zu "
+                    "(tokens * top_k * 4 + ceil(tokens / 64) * n_experts * 4 + n_experts * 4, "
+                    "each rounded up to 256); use moe_permute with a workspace",
+                    fn, need, moe::PERM_SCRATCH_BYTES);
+    void* ws = nullptr;
+    const hipError_t e = moe::permute_scratch(&ws);
+    if (e != hipSuccess)
+        return fail(MOE_ERR_HIP, "%s: scratch address: %s", fn, hipGetErrorString(e));
+    return hip_status(fn, moe::launch_permute(*cfg, x, idx, offsets, src_token, dst_row, x_perm,
+                                              x_perm_scale, x_q, x_s, ws, (hipStream_t)stream));
+}
+
 size_t moe_expert_ffn_workspace_size(const moe_cfg* cfg) {
     if (!cfg) return 0;
     return moe::ffn_workspace_bytes(*cfg);

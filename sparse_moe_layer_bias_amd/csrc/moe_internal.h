@@ -21,6 +21,10 @@ hipError_t launch_permute(const moe_cfg& c, const void* x, const int32_t* idx,
                           int32_t* offsets, int32_t* src_token, int32_t* dst_row, void* x_perm,
                           float* x_perm_scale, uint8_t* x_q, float* x_s, void* ws,
                           hipStream_t st);
+// moe_permute_noalloc: its device-resident scratch (a file-scope array in
+// permute.hip) and the address of the current device's copy
+constexpr size_t PERM_SCRATCH_BYTES = (size_t)8 << 20;
+hipError_t permute_scratch(void** ptr);
 
 // ---------------------------------------------------------------- expert FFN
 struct FfnArgs {

@@ -15,6 +15,8 @@
 //   4. scatter: dst_row, src_token, and the row copy x[t] -> x_perm[row] for
 //               each of the token's k rows (FP8: quantise the row's 1x128 tiles
 //               first, then copy codes and scales).
+#include <mutex>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -202,6 +204,41 @@ __global__ void __launch_bounds__(1024) perm_scatter_fp8_kernel(
             }
         }
     }
+}
+
+// ---------------------------------------------------------------- no-allocation variant
+//
+// moe_permute_noalloc's scratch: the same ranks and block histograms as the
+// caller's workspace of moe_permute, held in this file-scope device array
+// (every GPU the library runs on holds its own copy until the process ends).
+// In host code `scratch` names a host-side stand-in, not a device address, so
+// the kernels get the address hipGetSymbolAddress returns for the current
+// device, looked up once per device and kept.  Every element the permutation
+// reads is written earlier in the same call, so nothing is cleared; calls that
+// overlap on one GPU (two streams) share the array and race.
+static __device__ __align__(256) uint8_t scratch[PERM_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t permute_scratch(void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_permute(const moe_cfg& c, const void* x, const int32_t* idx,
