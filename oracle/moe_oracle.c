@@ -340,9 +340,11 @@ float orc_e4m3_decode(uint8_t c) {
     return (float)(s ? -v : v);
 }
 
-/* nearest E4M3FN code, ties to even; |v| must be <= 448 (callers clamp) */
+/* nearest E4M3FN code, ties to even; |v| must be <= 448 (callers clamp); a
+ * NaN (which no clamp removes) encodes as the format's NaN, S.1111.111 */
 uint8_t orc_e4m3_encode(float v) {
     uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    if (isnan(v)) return (uint8_t)(sign | 0x7f);
     double a = fabs((double)v);
     if (a < ldexp(1.0, -6)) {
         /* subnormal grid step 2^-9; a result of 8 steps is the smallest

@@ -271,6 +271,74 @@ def assert_bits(got, ref, what=""):
                              (what, neq.sum(), neq.size, tuple(i), g[tuple(i)], r[tuple(i)]))
 
 
+# ------------------------------------------------------------------ canaries
+
+GUARD_BYTES = 4096      # keeps every guarded view 256-byte aligned
+GUARD_PATTERN = 0xA5
+
+
+class Guards:
+    """Device buffers with guard bands: each buffer is a view into an
+    allocation that holds GUARD_BYTES bytes of GUARD_PATTERN before and after
+    it; check() asserts every band is still untouched, so a kernel that writes
+    past either end of an output shows up even when the stray bytes land in
+    memory no other check reads."""
+
+    def __init__(self):
+        self.items = []
+
+    def empty(self, shape, dtype, label, device="cuda"):
+        esz = torch.tensor([], dtype=dtype).element_size()
+        n = int(np.prod(shape)) * esz
+        back = torch.full((n + 2 * GUARD_BYTES,), GUARD_PATTERN, dtype=torch.uint8,
+                          device=device)
+        view = back[GUARD_BYTES:GUARD_BYTES + n].view(dtype).view(shape)
+        self.items.append((label, back, n))
+        return view
+
+    def like(self, t, label, copy=False):
+        if t is None:
+            return None
+        v = self.empty(tuple(t.shape), t.dtype, label, t.device)
+        if copy:
+            v.copy_(t)
+        return v
+
+    def check(self):
+        torch.cuda.synchronize()
+        for label, back, n in self.items:
+            head = back[:GUARD_BYTES]
+            tail = back[GUARD_BYTES + n:]
+            bad_h = int((head != GUARD_PATTERN).sum())
+            bad_t = int((tail != GUARD_PATTERN).sum())
+            assert bad_h == 0 and bad_t == 0, ("%s: %d bytes before and %d bytes after the "
+                                               "buffer were overwritten" % (label, bad_h, bad_t))
+        return len(self.items)
+
+
+LAYER_OUTPUTS = ("scores", "idx", "gate", "counts", "offsets", "src_token", "dst_row", "x_perm",
+                 "x_perm_s", "x_q", "x_s", "y_perm", "y_shared", "out", "workspace", "saved")
+
+
+def guard_layer(layer, guards=None):
+    """Replace every output and scratch buffer of a MoeLayer (and the gradient
+    buffers of its backward) by guarded ones of the same shape."""
+    g = guards or Guards()
+    for name in LAYER_OUTPUTS:
+        t = getattr(layer, name, None)
+        if isinstance(t, torch.Tensor):
+            setattr(layer, name, g.like(t, name))
+    return g
+
+
+def guard_grads(layer, centroids, g):
+    """Pre-allocate the backward's buffers of a training MoeLayer, guarded."""
+    grads = layer._grad_buffers(centroids)
+    layer.grads = {k: (g.like(v, "grad " + k) if isinstance(v, torch.Tensor) else v)
+                   for k, v in grads.items()}
+    return layer.grads
+
+
 def host_inputs(inp):
     """torch dict -> numpy dict in the oracle's conventions"""
     return {k: (to_host(v) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}

@@ -22,8 +22,8 @@ import torch
 
 import moe_inputs
 import sparse_moe_layer_bias_amd as moe
-from parity_util import (assert_close_fp8_bwd, assert_close_fp8_grad, host_inputs, log,
-                         small_layer_inputs)
+from parity_util import (assert_close_fp8_bwd, assert_close_fp8_grad, guard_grads, guard_layer,
+                         host_inputs, log, small_layer_inputs)
 from sparse_moe_layer_bias_amd.layer import MoeLayer
 
 pytestmark = pytest.mark.gpu
@@ -48,9 +48,12 @@ def _run(orc, seed=0, residual=True, save=True, **over):
     dout = moe_inputs.make_upstream_grad(c, seed, "cpu")
     layer = MoeLayer(c, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"], train=True,
                      save_activations=save)
+    guards = guard_layer(layer)
+    guard_grads(layer, dev["centroids"], guards)
     layer.forward(dev["x"], dev["centroids"], dev["bias"].clone(), residual=residual)
     g = layer.backward(dout.cuda(), dev["x"], dev["centroids"], residual=residual)
     torch.cuda.synchronize()
+    guards.check()
     layer.test_dout, layer.test_x, layer.test_centroids = dout.cuda(), dev["x"], dev["centroids"]
     h = host_inputs(inp)
     fwd = orc.layer_forward(h, c, residual=residual)

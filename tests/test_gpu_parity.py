@@ -16,7 +16,7 @@ import torch
 import moe_inputs
 import sparse_moe_layer_bias_amd as moe
 from parity_util import (RTOL, assert_bits, assert_close, assert_close_fp8, check_fp8_expert_split,
-                         host_inputs, log, small_layer_inputs)
+                         guard_layer, host_inputs, log, small_layer_inputs)
 from sparse_moe_layer_bias_amd.layer import MoeLayer
 
 pytestmark = pytest.mark.gpu
@@ -41,9 +41,11 @@ def _run_small(cfg_name, orc, T=None, residual=True, seed=0, **over):
     _last_x[0] = inp["x"]
     log("case", cfg_name, "T=%d" % c["T"], over, "seed", seed)
     layer = MoeLayer(c, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"])
-    bias = dev["bias"].clone()
+    guards = guard_layer(layer)
+    bias = guards.like(dev["bias"], "bias", copy=True)
     out = layer.forward(dev["x"], dev["centroids"], bias, residual=residual)
     torch.cuda.synchronize()
+    guards.check()
     ref = orc.layer_forward(host_inputs(inp), c, residual=residual)
     return c, layer, out, bias, ref
 

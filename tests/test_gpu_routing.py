@@ -16,7 +16,7 @@ import torch
 
 import moe_inputs
 import sparse_moe_layer_bias_amd as moe
-from parity_util import assert_bits, log
+from parity_util import Guards, assert_bits, log
 
 pytestmark = pytest.mark.gpu
 
@@ -38,12 +38,14 @@ def _route_inputs(T, d, N, dtype, seed):
 def _route_gpu(T, d, N, k, G, TG, dtype, inp):
     c = moe.make_cfg(T, d, N, k, G, TG, 0, 0, dtype)
     dev = {n: v.cuda() for n, v in inp.items()}
-    scores = torch.empty((T, N), dtype=torch.float32, device="cuda")
-    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
-    gate = torch.empty((T, k), dtype=torch.float32, device="cuda")
-    counts = torch.empty((N,), dtype=torch.int32, device="cuda")
+    g = Guards()
+    scores = g.empty((T, N), torch.float32, "scores")
+    idx = g.empty((T, k), torch.int32, "idx")
+    gate = g.empty((T, k), torch.float32, "gate")
+    counts = g.empty((N,), torch.int32, "counts")
     moe.moe_route(c, dev["x"], dev["centroids"], dev["bias"], scores, idx, gate, counts)
     torch.cuda.synchronize()
+    g.check()
     return {n: moe_inputs.to_host(v) for n, v in
             dict(scores=scores, idx=idx, gate=gate, counts=counts).items()}
 

@@ -259,3 +259,15 @@ def test_fp8_expert_is_its_two_halves(orc):
     y = orc.swiglu_ffn_fp8(Aq, As, q13, s13, q2, s2)
     hq, hs = orc.quant_act_fp8(orc.swiglu_gateup_fp8(Aq, As, q13, s13))
     assert np.array_equal(y, orc.ffn_down_fp8(hq, hs, q2, s2))
+
+
+def test_encode_nan_is_the_format_nan(orc):
+    """A NaN (outside the layer's finite-input contract, but it must not be
+    undefined behaviour) encodes as E4M3FN's NaN S.1111.111, as PyTorch's cast
+    does; a tile holding a NaN keeps the scale of its finite values."""
+    v = np.array([np.nan, -np.nan], np.float32)
+    assert np.array_equal(orc.e4m3_encode(v), _torch_encode(v))
+    x = np.linspace(-3, 3, 128).astype(np.float32)[None, :].copy()
+    x[0, 5] = np.nan
+    q, s = orc.quant_act_fp8(x)
+    assert s[0, 0] == np.float32(3.0) / np.float32(448) and q[0, 5] in (0x7F, 0xFF)

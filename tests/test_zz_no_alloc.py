@@ -11,7 +11,7 @@ import torch
 
 import moe_inputs
 import sparse_moe_layer_bias_amd as moe
-from parity_util import assert_bits, log
+from parity_util import Guards, assert_bits, log
 
 pytestmark = pytest.mark.gpu
 
@@ -59,9 +59,12 @@ def test_permute_noalloc_matches_permute(fp8):
         moe.moe_permute(cfg, x, idx, ref["offsets"], ref["src_token"], ref["dst_row"],
                         ref["x_perm"], ref["x_perm_scale"], ref["x_q"], ref["x_s"], ws)
         got = _buffers(c, T, d, fp8)
+        g = Guards()
+        got = {n: g.like(v, n, copy=True) for n, v in got.items()}
         moe.moe_permute_noalloc(cfg, x, idx, got["offsets"], got["src_token"], got["dst_row"],
                                 got["x_perm"], got["x_perm_scale"], got["x_q"], got["x_s"])
         torch.cuda.synchronize()
+        g.check()
         for n in ref:
             if ref[n] is None:
                 continue
