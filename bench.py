@@ -133,6 +133,10 @@ def parse():
     ap.add_argument("--no-configs", action="store_true",
                     help="measure the headline workload only (no v3_fp8, skew_balance, "
                          "tiny_fp32, mid_bf16 block)")
+    ap.add_argument("--vendor-calibration", action="store_true",
+                    help="time the vendor GEMM library (torch.bmm / torch._scaled_mm, i.e. "
+                         "hipBLASLt) on the expert FFN's per-expert shapes and on large dense "
+                         "GEMMs, print one JSON line, then exit")
     ap.add_argument("--no-probes", action="store_true",
                     help="skip the measured-peak probes (HBM read, MFMA loop)")
     ap.add_argument("--traffic-run", action="store_true",
@@ -590,6 +594,55 @@ def run_backward(args, cfg, dev, log):
 STAGES = ["route", "permute", "expert_ffn", "combine", "bias_update"]
 
 
+def vendor_calibration(log):
+    """What the vendor GEMM library reaches on this GPU, as context for the
+    grouped expert GEMMs' fractions of the published peaks: bf16 batched GEMMs
+    with the V3 layer's per-expert shapes (256 experts x 256 rows; right
+    operands contiguous), large dense bf16 and FP8 GEMMs (per-tensor scales),
+    each timed with events over several calls."""
+    import torch
+
+    out = {}
+
+    def timeit(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps / 1e3
+
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    for name, B, M, K, N in (("bf16 gate/up 256 x (256x7168 . 7168x4096)", 256, 256, 7168, 4096),
+                             ("bf16 down 256 x (256x2048 . 2048x7168)", 256, 256, 2048, 7168),
+                             ("bf16 dense 16384x7168 . 7168x16384", 1, 16384, 7168, 16384)):
+        X = torch.randn(B, M, K, device="cuda", dtype=torch.bfloat16, generator=g)
+        W = torch.randn(B, K, N, device="cuda", dtype=torch.bfloat16, generator=g).contiguous()
+        t = timeit(lambda: torch.bmm(X, W), 5)
+        fl = 2.0 * B * M * K * N
+        out[name] = {"ms": t * 1e3, "tflops": fl / t / 1e12, "frac_of_peak": fl / t / PEAK["bf16"],
+                     "weight_GBps": 2.0 * B * K * N / t / 1e9}
+        log("vendor %s: %.3f ms, %.0f TFLOP/s" % (name, t * 1e3, fl / t / 1e12))
+        del X, W
+        torch.cuda.empty_cache()
+    f8 = torch.float8_e4m3fn
+    for name, M, K, N in (("fp8 dense 16384x7168 . 7168x16384", 16384, 7168, 16384),):
+        A = torch.randn(M, K, device="cuda", generator=g).to(f8)
+        Bm = torch.randn(N, K, device="cuda", generator=g).to(f8)
+        one = torch.tensor(1.0, device="cuda")
+        t = timeit(lambda: torch._scaled_mm(A, Bm.t(), scale_a=one, scale_b=one,
+                                            out_dtype=torch.bfloat16), 5)
+        fl = 2.0 * M * K * N
+        out[name] = {"ms": t * 1e3, "tflops": fl / t / 1e12, "frac_of_peak": fl / t / PEAK["fp8"]}
+        log("vendor %s: %.3f ms, %.0f TFLOP/s" % (name, t * 1e3, fl / t / 1e12))
+        del A, Bm
+    return out
+
+
 def load_stats(counts, T, k):
     """max/mean load and idle experts of one step's per-expert counts"""
     mean = T * k / len(counts)
@@ -806,6 +859,9 @@ def main():
     if not torch.cuda.is_available():
         log("no GPU visible")
         sys.exit(1)
+    if args.vendor_calibration:
+        print(json.dumps({"vendor_calibration": vendor_calibration(log)}), flush=True)
+        return
     moe.lib()
     cfg = dict(moe_inputs.CONFIGS[args.workload])
     T = cfg["T"]

@@ -125,8 +125,6 @@ constexpr int G_TR = 320;      // token rows per tile
 constexpr int G_WAVES = 8;
 constexpr int G_THREADS = 64 * G_WAVES;
 constexpr int G_WRG = G_WAVES / 2;        // weight-row groups
-constexpr int G_SUB = 64;      // contraction elements per LDS sub-tile (128-byte rows)
-constexpr int G_CPR = G_SUB / 8;  // 16-byte chunks per LDS row
 // contraction step and number of LDS stages in the copy pipeline
 #ifndef MOE_GEMM_BK
 #define MOE_GEMM_BK 64
@@ -134,10 +132,19 @@ constexpr int G_CPR = G_SUB / 8;  // 16-byte chunks per LDS row
 #ifndef MOE_GEMM_NS
 #define MOE_GEMM_NS 2
 #endif
+// contraction elements per LDS sub-tile: one step up to 64 (rows of 2*G_SUB
+// bytes), and the 16-byte chunks per row with their bank-spreading swizzle
+constexpr int G_SUB = MOE_GEMM_BK < 64 ? MOE_GEMM_BK : 64;
+constexpr int G_CPR = G_SUB / 8;
+static_assert(G_CPR == 4 || G_CPR == 8, "LDS rows of 64 or 128 bytes");
+__device__ __forceinline__ int g_swz(int r, int c) {
+    return G_CPR == 8 ? sub_chunk8(r, c) : sub_chunk(r, c);
+}
+constexpr int G_RPB = 1024 / (2 * G_SUB);  // rows per 1 KB copy
 
 // Pack a stack of n_mats expert matrices into the GEMM's LDS image order:
-// out[mat][wt][kc][slot] (16-byte chunks), kc = 64-wide contraction block,
-// slot = r*8 + pc holding logical chunk sub_chunk8(r, pc) of packed row r.
+// out[mat][wt][kc][slot] (16-byte chunks), kc = G_SUB-wide contraction block,
+// slot = r*G_CPR + pc holding logical chunk g_swz(r, pc) of packed row r.
 template <int MODE>
 __global__ void __launch_bounds__(256) pack_weights_kernel(const uint4* __restrict__ w,
                                                            uint4* __restrict__ out,
@@ -153,7 +160,7 @@ __global__ void __launch_bounds__(256) pack_weights_kernel(const uint4* __restri
     rem %= nkc * G_WR * G_CPR;
     const int64_t kc = rem / (G_WR * G_CPR);
     const int slot = (int)(rem % (G_WR * G_CPR));
-    const int r = slot / G_CPR, c = sub_chunk8(r, slot % G_CPR);
+    const int r = slot / G_CPR, c = g_swz(r, slot % G_CPR);
     const int64_t src = packed_row_source<MODE>(wt, r, Nout);
     const int64_t rows = MODE == 0 ? 2 * Nout : Nout;
     uint4 v = make_uint4(0, 0, 0, 0);
@@ -178,7 +185,7 @@ __global__ void __launch_bounds__(256) pack_weights_t_kernel(const uint16_t* __r
     rem %= nkc * G_WR * G_CPR;
     const int64_t kc = rem / (G_WR * G_CPR);
     const int slot = (int)(rem % (G_WR * G_CPR));
-    const int r = slot / G_CPR, c = sub_chunk8(r, slot % G_CPR);
+    const int r = slot / G_CPR, c = g_swz(r, slot % G_CPR);
     const int64_t col = wt * G_WR + r;
     uint32_t v[4] = {0, 0, 0, 0};
     if (col < Nout) {
@@ -212,11 +219,11 @@ __device__ __forceinline__ void gemm_bf16_body(const WorkV2& w, uint16_t* smem) 
     const uint32_t woff = lane * 16;
     const char* xbase = w.X + w.m0 * K * 2;  // the tile's first token row
 
-    // Token copies: block b = 8 rows (rb = b / NSUB) of sub-tile q = b % NSUB,
-    // each row one full 128-byte line; the blocks holding real rows are the
+    // Token copies: block b = G_RPB rows (rb = b / NSUB) of sub-tile q = b % NSUB,
+    // each row one 2*G_SUB-byte line; the blocks holding real rows are the
     // prefix b < nxe.  Rows past the tile's last real row are never copied
     // (their LDS is never stored from).
-    const int nxe = NSUB * (int)((mc + 7) / 8);
+    const int nxe = NSUB * (int)((mc + G_RPB - 1) / G_RPB);
     int cnt = PA;  // copies this wave issues per stage
     uint32_t xoff[PX];
 #pragma unroll
@@ -224,7 +231,7 @@ __device__ __forceinline__ void gemm_bf16_body(const WorkV2& w, uint16_t* smem) 
         const int b = wave + G_WAVES * j;
         if (b < nxe) ++cnt;
         const int q = b % NSUB, rb = b / NSUB;
-        const int r = rb * 8 + (lane >> 3), c = sub_chunk8(r, lane & 7);
+        const int r = rb * G_RPB + (int)((unsigned)lane / G_CPR), c = g_swz(r, (int)((unsigned)lane % G_CPR));
         const int64_t tr = r < mc ? r : mc - 1;  // clamp inside a partial block
         xoff[j] = (uint32_t)((tr * K + q * G_SUB + c * 8) * 2);
     }
@@ -263,7 +270,7 @@ __device__ __forceinline__ void gemm_bf16_body(const WorkV2& w, uint16_t* smem) 
     // rows 16k + l16 share l16's swizzle: chunk offsets are lane constants
     uint32_t coff[G_SUB / 32];
 #pragma unroll
-    for (int s = 0; s < G_SUB / 32; ++s) coff[s] = sub_chunk8(l16, 4 * s + g) * 8;
+    for (int s = 0; s < G_SUB / 32; ++s) coff[s] = g_swz(l16, 4 * s + g) * 8;
 
     auto compute = [&](int sidx) {
         if constexpr (NB > 0) {
