@@ -755,39 +755,18 @@ void orc_quant_cols_fp8(int64_t M, int64_t C, int dtype, const void* x, uint8_t*
         }
 }
 
-/* Backward of the FP8 SwiGLU expert over its M rows:
- *  Aq [M,d] codes, As [M,d/128]   the forward's activation tiles (to recompute a, b)
- *  A  [M,d] bf16                  the same rows before quantisation (for dW13)
- *  w13q [2I,d], w13s [2I/128,d/128], w2q [d,I], w2s [d/128,I/128]  forward blocks
- *  dY [M,d] bf16                  gradient of the expert output
- * out dA [M,d], dw13 [2I,d], dw2 [d,I], all bf16 (gradients of the unquantised
- * weights: the block quantisation passes the gradient through).
- *   a, b  = the forward's promoted sums rounded to fp32; kept as bf16 a~, b~;
- *           h~ = bf16(silu(a) b)
- *   dh    = bf16( dY W2 )            dY in 1x128 row tiles, W2 in its blocks
- *   da    = bf16( dh b~ s (1 + a~ (1 - s)) ), db = bf16( dh a~ s ),  s = sig(a~)
- *   dA    = bf16( [da db] [W1; W3] ) [da db] in 1x128 row tiles
- *   dw2   = bf16( dY^T h~ )          both in 128x1 row-direction tiles
- *   dw13  = bf16( [da db]^T A )      both in 128x1 row-direction tiles
- * Each contraction: sum over its 128-blocks of (product of the two scales)
+/* The FP8 backward's steps, each on given inputs (the composite below chains
+ * them); contractions are sums over 128-blocks of (product of the two scales)
  * times the block's exact sum of decoded code products, in double. */
-void orc_swiglu_ffn_backward_fp8(int64_t M, int64_t d, int64_t I, const uint8_t* Aq,
-                                 const float* As, const uint16_t* A, const uint8_t* w13q,
-                                 const float* w13s, const uint8_t* w2q, const float* w2s,
-                                 const uint16_t* dY, uint16_t* dA, uint16_t* dw13,
-                                 uint16_t* dw2) {
+
+/* a, b of the FP8 forward (its promoted sums rounded to fp32), kept in bf16:
+ * ab [M, 2I] = [a | b] rounded to bf16; h [M, I] = bf16(silu(a) b) of the
+ * fp32 a, b. */
+void orc_fp8_recompute_ab(int64_t M, int64_t d, int64_t I, const uint8_t* Aq, const float* As,
+                          const uint8_t* w13q, const float* w13s, uint16_t* ab, uint16_t* h) {
     double lut[256];
-    for (int c = 0; c < 256; ++c) {
-        float v = orc_e4m3_decode((uint8_t)c);
-        lut[c] = isnan(v) ? 0.0 : (double)v;
-    }
-    const int64_t kd = d / 128, ki = I / 128, k2 = 2 * I / 128, nb = (M + 127) / 128;
-    const size_t MI = (size_t)(M * I + 1), M2I = (size_t)(2 * M * I + 1);
-    uint16_t* h = (uint16_t*)malloc(MI * 2);
-    double* ar = (double*)malloc(MI * sizeof(double));
-    double* br = (double*)malloc(MI * sizeof(double));
-    uint16_t* dab = (uint16_t*)malloc(M2I * 2);
-    /* recompute a, b as the FP8 forward does */
+    e4m3_lut(lut);
+    const int64_t kd = d / 128;
 #pragma omp parallel for collapse(2) schedule(static)
     for (int64_t m = 0; m < M; ++m)
         for (int64_t n = 0; n < I; ++n) {
@@ -801,45 +780,108 @@ void orc_swiglu_ffn_backward_fp8(int64_t M, int64_t d, int64_t I, const uint8_t*
             }
             double a = (double)(float)sa, b = (double)(float)sb;
             h[m * I + n] = double_to_bf16_bits(a / (1.0 + exp(-a)) * b);
-            ar[m * I + n] = round_dtype(ORC_BF16, a);
-            br[m * I + n] = round_dtype(ORC_BF16, b);
+            ab[m * 2 * I + n] = double_to_bf16_bits(a);
+            ab[m * 2 * I + I + n] = double_to_bf16_bits(b);
         }
-    /* dh = dY W2 with dY in row tiles; then da, db */
-    uint8_t* gq = (uint8_t*)malloc((size_t)(M * d + 1));
-    float* gs = (float*)malloc((size_t)(M * kd + 1) * sizeof(float));
-    orc_quant_act_fp8(M, d, ORC_BF16, dY, gq, gs);
+}
+
+/* data gradient through one weight matrix W [K, N] (E4M3 codes, 128x128 block
+ * scales ws [K/128, N/128]) of M gradient rows in 1x128 tiles along K:
+ * out[m, n] = bf16( sum_k g[m, k] W[k, n] ).  dh = dY W2 (K = d, N = I);
+ * dA = [da db] [W1; W3] (K = 2I, N = d). */
+void orc_fp8_dgrad(int64_t M, int64_t K, int64_t N, const uint8_t* gq, const float* gs,
+                   const uint8_t* wq, const float* ws, uint16_t* out) {
+    double lut[256];
+    e4m3_lut(lut);
+    const int64_t kk = K / 128, kn = N / 128;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t kb = 0; kb < kk; ++kb) {
+                double p = 0.0;
+                for (int64_t k = kb * 128; k < kb * 128 + 128; ++k)
+                    p += lut[gq[m * K + k]] * lut[wq[k * N + n]];
+                acc += (double)gs[m * kk + kb] * (double)ws[kb * kn + n / 128] * p;
+            }
+            out[m * N + n] = double_to_bf16_bits(acc);
+        }
+}
+
+/* SwiGLU derivative on stored (bf16) values: from dh [M, I] and [a | b]
+ * [M, 2I], da = bf16(dh b s (1 + a (1 - s))), db = bf16(dh a s), s = sig(a),
+ * into dab [M, 2I] = [da | db]; evaluated in double. */
+void orc_swiglu_bwd_bf16(int64_t M, int64_t I, const uint16_t* dh, const uint16_t* ab,
+                         uint16_t* dab) {
 #pragma omp parallel for collapse(2) schedule(static)
     for (int64_t m = 0; m < M; ++m)
         for (int64_t n = 0; n < I; ++n) {
-            double acc = 0.0;
-            for (int64_t kb = 0; kb < kd; ++kb) {
-                double p = 0.0;
-                for (int64_t c = kb * 128; c < kb * 128 + 128; ++c)
-                    p += lut[gq[m * d + c]] * lut[w2q[c * I + n]];
-                acc += (double)gs[m * kd + kb] * (double)w2s[kb * ki + n / 128] * p;
-            }
-            const double dh = round_dtype(ORC_BF16, acc);
-            const double a = ar[m * I + n], b = br[m * I + n], sg = sigmoid_d(a);
-            dab[m * 2 * I + n] = double_to_bf16_bits(dh * b * sg * (1.0 + a * (1.0 - sg)));
-            dab[m * 2 * I + I + n] = double_to_bf16_bits(dh * a * sg);
+            const double g = (double)bf16_bits_to_float(dh[m * I + n]);
+            const double a = (double)bf16_bits_to_float(ab[m * 2 * I + n]);
+            const double b = (double)bf16_bits_to_float(ab[m * 2 * I + I + n]);
+            const double sg = sigmoid_d(a);
+            dab[m * 2 * I + n] = double_to_bf16_bits(g * b * sg * (1.0 + a * (1.0 - sg)));
+            dab[m * 2 * I + I + n] = double_to_bf16_bits(g * a * sg);
         }
-    /* dA = [da db] [W1; W3] with [da db] in row tiles */
+}
+
+/* weight gradient over M rows in 128x1 row-direction tiles (128 consecutive
+ * rows from row 0, the last partial): A codes [M, FA] with scales
+ * [ceil(M/128), FA], B codes [M, FB] with scales [ceil(M/128), FB];
+ * out[a, b] = bf16( sum_m A[m, a] B[m, b] ).  dW2 = dY^T h; dW13 = [da db]^T X. */
+void orc_fp8_wgrad(int64_t M, int64_t FA, int64_t FB, const uint8_t* Aq, const float* As,
+                   const uint8_t* Bq, const float* Bs, uint16_t* out) {
+    double lut[256];
+    e4m3_lut(lut);
+    const int64_t nb = (M + 127) / 128;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t a = 0; a < FA; ++a)
+        for (int64_t b = 0; b < FB; ++b) {
+            double acc = 0.0;
+            for (int64_t u = 0; u < nb; ++u) {
+                int64_t r1 = (u + 1) * 128 < M ? (u + 1) * 128 : M;
+                double p = 0.0;
+                for (int64_t m = u * 128; m < r1; ++m) p += lut[Aq[m * FA + a]] * lut[Bq[m * FB + b]];
+                acc += (double)As[u * FA + a] * (double)Bs[u * FB + b] * p;
+            }
+            out[a * FB + b] = double_to_bf16_bits(acc);
+        }
+}
+
+/* Backward of the FP8 SwiGLU expert over its M rows:
+ *  Aq [M,d] codes, As [M,d/128]   the forward's activation tiles (to recompute a, b)
+ *  A  [M,d] bf16                  the same rows before quantisation (for dW13)
+ *  w13q [2I,d], w13s [2I/128,d/128], w2q [d,I], w2s [d/128,I/128]  forward blocks
+ *  dY [M,d] bf16                  gradient of the expert output
+ * out dA [M,d], dw13 [2I,d], dw2 [d,I], all bf16 (gradients of the unquantised
+ * weights: the block quantisation passes the gradient through).  The steps:
+ *   a~, b~, h~ = orc_fp8_recompute_ab
+ *   dh    = bf16( dY W2 )            dY in 1x128 row tiles, W2 in its blocks
+ *   da, db = orc_swiglu_bwd_bf16(dh, a~, b~)
+ *   dA    = bf16( [da db] [W1; W3] ) [da db] in 1x128 row tiles
+ *   dw2   = bf16( dY^T h~ )          both in 128x1 row-direction tiles
+ *   dw13  = bf16( [da db]^T A )      both in 128x1 row-direction tiles */
+void orc_swiglu_ffn_backward_fp8(int64_t M, int64_t d, int64_t I, const uint8_t* Aq,
+                                 const float* As, const uint16_t* A, const uint8_t* w13q,
+                                 const float* w13s, const uint8_t* w2q, const float* w2s,
+                                 const uint16_t* dY, uint16_t* dA, uint16_t* dw13,
+                                 uint16_t* dw2) {
+    const int64_t kd = d / 128, k2 = 2 * I / 128, nb = (M + 127) / 128;
+    const size_t MI = (size_t)(M * I + 1), M2I = (size_t)(2 * M * I + 1);
+    uint16_t* h = (uint16_t*)malloc(MI * 2);
+    uint16_t* ab = (uint16_t*)malloc(M2I * 2);
+    uint16_t* dh = (uint16_t*)malloc(MI * 2);
+    uint16_t* dab = (uint16_t*)malloc(M2I * 2);
+    orc_fp8_recompute_ab(M, d, I, Aq, As, w13q, w13s, ab, h);
+    uint8_t* gq = (uint8_t*)malloc((size_t)(M * d + 1));
+    float* gs = (float*)malloc((size_t)(M * kd + 1) * sizeof(float));
+    orc_quant_act_fp8(M, d, ORC_BF16, dY, gq, gs);
+    orc_fp8_dgrad(M, d, I, gq, gs, w2q, w2s, dh);
+    orc_swiglu_bwd_bf16(M, I, dh, ab, dab);
     uint8_t* tq = (uint8_t*)malloc(M2I);
     float* ts = (float*)malloc((size_t)(M * k2 + 1) * sizeof(float));
     orc_quant_act_fp8(M, 2 * I, ORC_BF16, dab, tq, ts);
-#pragma omp parallel for collapse(2) schedule(static)
-    for (int64_t m = 0; m < M; ++m)
-        for (int64_t c = 0; c < d; ++c) {
-            double acc = 0.0;
-            for (int64_t kb = 0; kb < k2; ++kb) {
-                double p = 0.0;
-                for (int64_t n = kb * 128; n < kb * 128 + 128; ++n)
-                    p += lut[tq[m * 2 * I + n]] * lut[w13q[n * d + c]];
-                acc += (double)ts[m * k2 + kb] * (double)w13s[kb * kd + c / 128] * p;
-            }
-            dA[m * d + c] = double_to_bf16_bits(acc);
-        }
-    /* weight gradients from row-direction tiles */
+    orc_fp8_dgrad(M, 2 * I, d, tq, ts, w13q, w13s, dA);
     uint8_t* cg = (uint8_t*)malloc((size_t)(M * d + 1));
     float* cgs = (float*)malloc((size_t)(nb * d + 1) * sizeof(float));
     uint8_t* ch = (uint8_t*)malloc(MI);
@@ -852,31 +894,8 @@ void orc_swiglu_ffn_backward_fp8(int64_t M, int64_t d, int64_t I, const uint8_t*
     orc_quant_cols_fp8(M, I, ORC_BF16, h, ch, chs);
     orc_quant_cols_fp8(M, 2 * I, ORC_BF16, dab, ct, cts);
     orc_quant_cols_fp8(M, d, ORC_BF16, A, cx, cxs);
-#pragma omp parallel for collapse(2) schedule(static)
-    for (int64_t c = 0; c < d; ++c)
-        for (int64_t n = 0; n < I; ++n) {
-            double acc = 0.0;
-            for (int64_t u = 0; u < nb; ++u) {
-                int64_t r1 = (u + 1) * 128 < M ? (u + 1) * 128 : M;
-                double p = 0.0;
-                for (int64_t m = u * 128; m < r1; ++m) p += lut[cg[m * d + c]] * lut[ch[m * I + n]];
-                acc += (double)cgs[u * d + c] * (double)chs[u * I + n] * p;
-            }
-            dw2[c * I + n] = double_to_bf16_bits(acc);
-        }
-#pragma omp parallel for collapse(2) schedule(static)
-    for (int64_t n = 0; n < 2 * I; ++n)
-        for (int64_t c = 0; c < d; ++c) {
-            double acc = 0.0;
-            for (int64_t u = 0; u < nb; ++u) {
-                int64_t r1 = (u + 1) * 128 < M ? (u + 1) * 128 : M;
-                double p = 0.0;
-                for (int64_t m = u * 128; m < r1; ++m)
-                    p += lut[ct[m * 2 * I + n]] * lut[cx[m * d + c]];
-                acc += (double)cts[u * 2 * I + n] * (double)cxs[u * d + c] * p;
-            }
-            dw13[n * d + c] = double_to_bf16_bits(acc);
-        }
-    free(h); free(ar); free(br); free(dab); free(gq); free(gs); free(tq); free(ts);
+    orc_fp8_wgrad(M, d, I, cg, cgs, ch, chs, dw2);
+    orc_fp8_wgrad(M, 2 * I, d, ct, cts, cx, cxs, dw13);
+    free(h); free(ab); free(dh); free(dab); free(gq); free(gs); free(tq); free(ts);
     free(cg); free(cgs); free(ch); free(chs); free(ct); free(cts); free(cx); free(cxs);
 }

@@ -74,6 +74,10 @@ def _declare(L):
         "orc_input_grad": [I64, I64, I64, I, P, P, P, P, P, P, P, P],
         "orc_quant_cols_fp8": [I64, I64, I, P, P, P],
         "orc_swiglu_ffn_backward_fp8": [I64, I64, I64] + [P] * 11,
+        "orc_fp8_recompute_ab": [I64, I64, I64, P, P, P, P, P, P],
+        "orc_fp8_dgrad": [I64, I64, I64, P, P, P, P, P],
+        "orc_swiglu_bwd_bf16": [I64, I64, P, P, P],
+        "orc_fp8_wgrad": [I64, I64, I64, P, P, P, P, P],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -446,6 +450,56 @@ def swiglu_ffn_backward_fp8(Aq, As, A, w13q, w13s, w2q, w2s, dY):
     lib().orc_swiglu_ffn_backward_fp8(M, d, I, _p(Aq), _p(As), _p(A), _p(w13q), _p(w13s),
                                       _p(w2q), _p(w2s), _p(dY), _p(dA), _p(dw13), _p(dw2))
     return dA, dw13, dw2
+
+
+def fp8_recompute_ab(Aq, As, w13q, w13s):
+    """The FP8 forward's a, b kept in bf16 ([M, 2I] = [a | b]) and h = bf16(silu(a) b)."""
+    Aq, As = _c(Aq, np.uint8), _c(As, np.float32)
+    w13q, w13s = _c(w13q, np.uint8), _c(w13s, np.float32)
+    M, d = Aq.shape
+    I = w13q.shape[0] // 2
+    ab = np.empty((M, 2 * I), np.uint16)
+    h = np.empty((M, I), np.uint16)
+    lib().orc_fp8_recompute_ab(M, d, I, _p(Aq), _p(As), _p(w13q), _p(w13s), _p(ab), _p(h))
+    return ab, h
+
+
+def fp8_dgrad(gq, gs, wq, ws):
+    """bf16(g W) for gradient rows g in 1x128 tiles along K (codes [M, K], scales
+    [M, K/128]) and a weight matrix W [K, N] in 128x128 blocks (codes, scales
+    [K/128, N/128])."""
+    gq, gs = _c(gq, np.uint8), _c(gs, np.float32)
+    wq, ws = _c(wq, np.uint8), _c(ws, np.float32)
+    M, K = gq.shape
+    N = wq.shape[1]
+    assert wq.shape == (K, N) and gs.shape == (M, K // 128) and ws.shape == (K // 128, N // 128)
+    out = np.empty((M, N), np.uint16)
+    lib().orc_fp8_dgrad(M, K, N, _p(gq), _p(gs), _p(wq), _p(ws), _p(out))
+    return out
+
+
+def swiglu_bwd_bf16(dh, ab):
+    """[da | db] in bf16 from bf16 dh [M, I] and [a | b] [M, 2I]."""
+    dh, ab = _c(dh, np.uint16), _c(ab, np.uint16)
+    M, I = dh.shape
+    assert ab.shape == (M, 2 * I)
+    dab = np.empty((M, 2 * I), np.uint16)
+    lib().orc_swiglu_bwd_bf16(M, I, _p(dh), _p(ab), _p(dab))
+    return dab
+
+
+def fp8_wgrad(Aq, As, Bq, Bs):
+    """bf16(A^T B) over the M rows, both in 128x1 row-direction tiles (codes
+    [M, F], scales [ceil(M/128), F])."""
+    Aq, As = _c(Aq, np.uint8), _c(As, np.float32)
+    Bq, Bs = _c(Bq, np.uint8), _c(Bs, np.float32)
+    M, FA = Aq.shape
+    FB = Bq.shape[1]
+    nb = (M + 127) // 128
+    assert Bq.shape[0] == M and As.shape == (nb, FA) and Bs.shape == (nb, FB)
+    out = np.empty((FA, FB), np.uint16)
+    lib().orc_fp8_wgrad(M, FA, FB, _p(Aq), _p(As), _p(Bq), _p(Bs), _p(out))
+    return out
 
 
 def route_backward(scores, idx, dgate):

@@ -128,3 +128,126 @@ def test_fp8_backward_zero_gradient_and_zero_rows(orc):
     dA, dw13, dw2 = orc.swiglu_ffn_backward_fp8(Aq[:0], As[:0], A[:0], w13q, w13s, w2q, w2s,
                                                 dY[:0])
     assert dA.shape == (0, 128) and not np.any(_f64(dw13)) and not np.any(_f64(dw2))
+
+
+# ------------------------------------------------------------------ the steps
+
+def _tab():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    t = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    t[np.isnan(t)] = 0.0
+    return t
+
+
+def _bf(x):
+    return (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _f(b):
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _to_bf16(v):
+    return torch.from_numpy(np.asarray(v, np.float64)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def test_fp8_dgrad_step_equals_dequantised_fp64(orc):
+    """bf16(g W) from row-tiled codes and a block-scaled weight: the fp64 GEMM
+    of the dequantised operands rounded once to bf16 (one bf16 step at most
+    where fp64 rounding meets a midpoint); scales differ per block, so a
+    transposed scale index fails."""
+    rng = np.random.default_rng(41)
+    M, K, N = 9, 384, 256
+    g = rng.standard_normal((M, K)).astype(np.float32)
+    g[:, 128:256] *= 30
+    w = (rng.standard_normal((K, N)) / 20).astype(np.float32)
+    w[128:256, :128] *= 0.01
+    gq, gs = orc.quant_act_fp8(g)
+    wq, ws = orc.quant_weight_fp8(w)
+    out = orc.fp8_dgrad(gq, gs, wq, ws)
+    t = _tab()
+    ref = (t[gq] * np.repeat(gs.astype(np.float64), 128, 1)) @ (
+        t[wq] * np.kron(ws.astype(np.float64), np.ones((128, 128))))
+    got = _f(out)
+    assert np.mean(got == _to_bf16(ref)) > 0.99
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-300)
+
+
+def test_fp8_wgrad_step_equals_dequantised_fp64(orc):
+    """bf16(A^T B) over 300 rows in 128x1 tiles (a partial last tile): the
+    fp64 product of the dequantised row-direction tiles."""
+    rng = np.random.default_rng(42)
+    M, FA, FB = 300, 64, 48
+    A = rng.standard_normal((M, FA)).astype(np.float32) * np.exp(rng.standard_normal((M, 1)))
+    B = rng.standard_normal((M, FB)).astype(np.float32)
+    Aq, As = orc.quant_cols_fp8(A.astype(np.float32))
+    Bq, Bs = orc.quant_cols_fp8(B)
+    out = orc.fp8_wgrad(Aq, As, Bq, Bs)
+    t = _tab()
+    rep = lambda s: np.repeat(s.astype(np.float64), 128, 0)[:M]
+    ref = (t[Aq] * rep(As)).T @ (t[Bq] * rep(Bs))
+    got = _f(out)
+    assert np.mean(got == _to_bf16(ref)) > 0.99
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-300)
+
+
+def test_swiglu_bwd_step_matches_autograd(orc):
+    """[da db] from stored bf16 dh, a, b: float64 autograd of silu(a) b, rounded
+    once to bf16 (at most one bf16 step apart where evaluation order meets a
+    midpoint), with a spanning the region where silu' changes sign."""
+    rng = np.random.default_rng(43)
+    M, I = 5, 256
+    a = rng.uniform(-6, 6, (M, I)).astype(np.float32)
+    b = rng.standard_normal((M, I)).astype(np.float32)
+    dh = rng.standard_normal((M, I)).astype(np.float32)
+    ab = np.concatenate([_bf(a), _bf(b)], axis=1)
+    dab = orc.swiglu_bwd_bf16(_bf(dh), ab)
+    at = torch.tensor(_f(ab[:, :I]), requires_grad=True)
+    bt = torch.tensor(_f(ab[:, I:]), requires_grad=True)
+    h = at * torch.sigmoid(at) * bt
+    h.backward(torch.tensor(_f(_bf(dh))))
+    for got, ref in ((dab[:, :I], at.grad.numpy()), (dab[:, I:], bt.grad.numpy())):
+        assert np.all(np.abs(_f(got) - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30)
+
+
+def test_fp8_recompute_step_matches_forward_half(orc):
+    """a, b kept in bf16 are the forward's fp32 sums rounded to bf16 (checked
+    against the fp64 GEMM of the dequantised operands), and h is within one
+    bf16 step of the forward half's fp32 h."""
+    rng = np.random.default_rng(44)
+    M, d, I = 7, 256, 128
+    x = rng.standard_normal((M, d)).astype(np.float32)
+    w13 = (rng.standard_normal((2 * I, d)) / 16).astype(np.float32)
+    xq, xs = orc.quant_act_fp8(x)
+    wq, ws = orc.quant_weight_fp8(w13)
+    ab, h = orc.fp8_recompute_ab(xq, xs, wq, ws)
+    t = _tab()
+    ref = (t[xq] * np.repeat(xs.astype(np.float64), 128, 1)) @ (
+        t[wq] * np.kron(ws.astype(np.float64), np.ones((128, 128)))).T
+    assert np.all(np.abs(_f(ab) - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30)
+    hf = orc.swiglu_gateup_fp8(xq, xs, wq, ws).astype(np.float64)
+    assert np.all(np.abs(_f(h) - hf) <= 2.0 ** -8 * np.abs(hf) + 1e-30)
+
+
+def test_fp8_backward_is_its_steps(orc):
+    """The composite FP8 backward equals its steps chained in order, bit for
+    bit (the GPU checks feed the GPU's own intermediates to the steps)."""
+    rng = np.random.default_rng(45)
+    M, d, I = 130, 256, 128
+    A = _bf(rng.standard_normal((M, d)))
+    dY = _bf(rng.standard_normal((M, d)))
+    w13 = (rng.standard_normal((2 * I, d)) / 16).astype(np.float32)
+    w2 = (rng.standard_normal((d, I)) / 16).astype(np.float32)
+    Aq, As = orc.quant_act_fp8(A)
+    q13, s13 = orc.quant_weight_fp8(w13)
+    q2, s2 = orc.quant_weight_fp8(w2)
+    dA, dw13, dw2 = orc.swiglu_ffn_backward_fp8(Aq, As, A, q13, s13, q2, s2, dY)
+    ab, h = orc.fp8_recompute_ab(Aq, As, q13, s13)
+    gq, gs = orc.quant_act_fp8(dY)
+    dh = orc.fp8_dgrad(gq, gs, q2, s2)
+    dab = orc.swiglu_bwd_bf16(dh, ab)
+    tq, ts = orc.quant_act_fp8(dab)
+    assert np.array_equal(dA, orc.fp8_dgrad(tq, ts, q13, s13))
+    cols = [orc.quant_cols_fp8(v) for v in (dY, h, dab, A)]
+    assert np.array_equal(dw2, orc.fp8_wgrad(*cols[0], *cols[1]))
+    assert np.array_equal(dw13, orc.fp8_wgrad(*cols[2], *cols[3]))
