@@ -48,6 +48,62 @@ int moe_expert_ffn_inspect(const moe_cfg* cfg, const void* x_perm, const float* 
                            float* h_f32, float* h_f32_shared, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/* Where moe_expert_ffn_backward_fp8 keeps its intermediates inside its
+ * workspace (reading guide "Kernideen", FP8 bullet: every operand of every
+ * backward GEMM is E4M3 in tiles along that GEMM's contraction), byte offsets
+ * from the workspace start, for checks of each step against an independent
+ * implementation.  Valid after a call on that workspace until it is reused.
+ * R = T*k routed rows (x_perm order), S = T shared rows (0 without a shared
+ * expert), Ir = I, Is = inter_shared, Im = max(I, Is):
+ *  DY_Q  [R, d] u8,  DY_S  [R, d/128] fp32    dY (dy_perm) in 1x128 row tiles
+ *  DH    [R, I] bf16                          dh = dY W2
+ *  DAB   [R, 2I] bf16                         [da | db]
+ *  DAB_Q [R, 2I] u8, DAB_S [R, 2I/128] fp32   [da db] in 1x128 row tiles
+ *  the same four for the shared expert's S rows (_SH), with Is for I
+ *  COL_*    [P/128][F][128] u8, COL_*_S [P/128][F] fp32: the 128x1 row-direction
+ *           tiles of dY (F = d), h (F = Im), [da db] (F = 2 Im) and x gathered
+ *           through src_token (F = d); 128-row block pb of group g (routed
+ *           experts 0..N-1, then the shared expert) is POFF[g]/128 + its
+ *           block index in the group, codes [pb][feature][row % 128]
+ *  POFF  [N+2] int32: prefix of the groups' row counts, each rounded up to 128
+ *  AB [R, 2I], H [R, I], AB_SH, H_SH bf16: a, b, h when the call recomputes
+ *           them (with saved activations they are in the saved buffer at the
+ *           offsets of moe_expert_ffn_saved_offsets)
+ * Returns MOE_OK, or MOE_ERR_ARG / MOE_ERR_UNSUPPORTED for a bad cfg. */
+#define MOE_BWD8_DY_Q 0
+#define MOE_BWD8_DY_S 1
+#define MOE_BWD8_DY_Q_SH 2
+#define MOE_BWD8_DY_S_SH 3
+#define MOE_BWD8_DH 4
+#define MOE_BWD8_DH_SH 5
+#define MOE_BWD8_DAB 6
+#define MOE_BWD8_DAB_SH 7
+#define MOE_BWD8_DAB_Q 8
+#define MOE_BWD8_DAB_S 9
+#define MOE_BWD8_DAB_Q_SH 10
+#define MOE_BWD8_DAB_S_SH 11
+#define MOE_BWD8_COL_DY 12
+#define MOE_BWD8_COL_DY_S 13
+#define MOE_BWD8_COL_H 14
+#define MOE_BWD8_COL_H_S 15
+#define MOE_BWD8_COL_DAB 16
+#define MOE_BWD8_COL_DAB_S 17
+#define MOE_BWD8_COL_X 18
+#define MOE_BWD8_COL_X_S 19
+#define MOE_BWD8_POFF 20
+#define MOE_BWD8_AB 21
+#define MOE_BWD8_H 22
+#define MOE_BWD8_AB_SH 23
+#define MOE_BWD8_H_SH 24
+#define MOE_BWD8_N 25
+int moe_expert_ffn_backward_fp8_offsets(const moe_cfg* cfg, size_t off[MOE_BWD8_N]);
+
+/* Byte offsets inside the saved-activation buffer of a training forward
+ * (moe_expert_ffn_train / moe_expert_ffn_train_fp8): off[0] routed [a | b]
+ * [T*k, 2I], off[1] routed h [T*k, I], off[2] shared [a | b] [T, 2Is],
+ * off[3] shared h [T, Is], all in act_dtype.  Returns MOE_OK or MOE_ERR_ARG. */
+int moe_expert_ffn_saved_offsets(const moe_cfg* cfg, size_t off[4]);
+
 /* The E4M3 quantisation step the kernels apply, on given fp32 values
  * (reading guide "Kernideen", FP8 bullet; the singularity-lens summary's
  * formula paragraph: code = E4M3(clip(v / S, -448, 448)), nearest, ties to

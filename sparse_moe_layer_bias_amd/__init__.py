@@ -89,6 +89,8 @@ def lib():
             "moe_expert_ffn_h_offsets": ([C, ctypes.POINTER(SZ)], ctypes.c_int),
             "moe_expert_ffn_inspect": ([C] + [P] * 17 + [P, SZ, P], ctypes.c_int),
             "moe_inspect_e4m3": ([P, I64, F, P, P, P], ctypes.c_int),
+            "moe_expert_ffn_backward_fp8_offsets": ([C, ctypes.POINTER(SZ)], ctypes.c_int),
+            "moe_expert_ffn_saved_offsets": ([C, ctypes.POINTER(SZ)], ctypes.c_int),
             "moe_permute_noalloc_max_bytes": ([], SZ),
             "moe_permute_noalloc": ([C, P, P, P, P, P, P, P, P, P, P], ctypes.c_int),
             "moe_last_error": ([], ctypes.c_char_p),
@@ -192,6 +194,25 @@ def moe_expert_ffn_inspect(cfg, x_perm, x_perm_scale, offsets, w13, w13_scale, w
         _p(w2), _p(w2_scale), _p(y_perm), _p(x_sh), _p(x_sh_scale), _p(ws13), _p(ws13_scale),
         _p(ws2), _p(ws2_scale), _p(y_shared), _p(h_f32), _p(h_f32_shared), _p(workspace),
         _nbytes(workspace), _stream(stream)))
+
+
+BWD8_NAMES = ("dy_q", "dy_s", "dy_q_sh", "dy_s_sh", "dh", "dh_sh", "dab", "dab_sh", "dab_q",
+              "dab_s", "dab_q_sh", "dab_s_sh", "col_dy", "col_dy_s", "col_h", "col_h_s",
+              "col_dab", "col_dab_s", "col_x", "col_x_s", "poff", "ab", "h", "ab_sh", "h_sh")
+
+
+def moe_expert_ffn_backward_fp8_offsets(cfg):
+    """include/moe_inspect.h: byte offsets of the FP8 backward's intermediates
+    in its workspace, as a dict keyed by BWD8_NAMES."""
+    off = (ctypes.c_size_t * len(BWD8_NAMES))()
+    _check(lib().moe_expert_ffn_backward_fp8_offsets(ctypes.byref(cfg), off))
+    return {n: int(v) for n, v in zip(BWD8_NAMES, off)}
+
+
+def moe_expert_ffn_saved_offsets(cfg):
+    off = (ctypes.c_size_t * 4)()
+    _check(lib().moe_expert_ffn_saved_offsets(ctypes.byref(cfg), off))
+    return dict(zip(("ab", "h", "ab_sh", "h_sh"), (int(v) for v in off)))
 
 
 def moe_inspect_e4m3(v, scale, codes4, codes1, stream=None):

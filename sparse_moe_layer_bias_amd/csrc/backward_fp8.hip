@@ -531,6 +531,16 @@ static BwdFp8Ws carve_bwd_fp8(const moe_cfg& c, void* ws, size_t* bytes) {
     return w;
 }
 
+void ffn_backward_fp8_offsets(const moe_cfg& c, size_t off[25]) {
+    char* base = (char*)(uintptr_t)4096;  // any aligned base: only differences are used
+    const BwdFp8Ws w = carve_bwd_fp8(c, base, nullptr);
+    auto o = [&](const void* p) { return (size_t)((const char*)p - base); };
+    const void* ptrs[25] = {w.gq_r, w.gs_r, w.gq_s, w.gs_s, w.dh_r, w.dh_s, w.dab_r, w.dab_s,
+                            w.tq_r, w.ts_r, w.tq_s, w.ts_s, w.gT, w.gTs, w.hT, w.hTs, w.tT,
+                            w.tTs, w.xT, w.xTs, w.poff, w.ab_r, w.h_r, w.ab_s, w.h_s};
+    for (int i = 0; i < 25; ++i) off[i] = o(ptrs[i]);
+}
+
 size_t ffn_backward_fp8_workspace_bytes(const moe_cfg& c) {
     size_t b = 0;
     carve_bwd_fp8(c, nullptr, &b);

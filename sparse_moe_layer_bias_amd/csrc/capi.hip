@@ -317,6 +317,31 @@ int moe_expert_ffn_inspect(const moe_cfg* cfg, const void* x_perm, const float* 
                            cfg->inter_shared > 0 ? h_f32_shared : nullptr);
 }
 
+int moe_expert_ffn_backward_fp8_offsets(const moe_cfg* cfg, size_t off[MOE_BWD8_N]) {
+    const char* fn = "moe_expert_ffn_backward_fp8_offsets";
+    if (int r = check_cfg(fn, cfg)) return r;
+    if (int r = check_ffn_shape(fn, cfg)) return r;
+    if (cfg->gemm_dtype != MOE_FP8_E4M3)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: FP8 layers only", fn);
+    if (!off) return fail(MOE_ERR_ARG, "%s: off is NULL", fn);
+    static_assert(MOE_BWD8_N == 25, "one offset per intermediate");
+    moe::ffn_backward_fp8_offsets(*cfg, off);
+    return ok();
+}
+
+int moe_expert_ffn_saved_offsets(const moe_cfg* cfg, size_t off[4]) {
+    const char* fn = "moe_expert_ffn_saved_offsets";
+    if (int r = check_cfg(fn, cfg)) return r;
+    if (!off) return fail(MOE_ERR_ARG, "%s: off is NULL", fn);
+    char* base = (char*)(uintptr_t)4096;
+    const moe::SavedActs s = moe::carve_saved(*cfg, base);
+    off[0] = (size_t)((char*)s.ab_r - base);
+    off[1] = (size_t)((char*)s.h_r - base);
+    off[2] = (size_t)((char*)s.ab_s - base);
+    off[3] = (size_t)((char*)s.h_s - base);
+    return ok();
+}
+
 int moe_inspect_e4m3(const float* v, int64_t n, float scale, uint8_t* codes4, uint8_t* codes1,
                      void* stream) {
     const char* fn = "moe_inspect_e4m3";

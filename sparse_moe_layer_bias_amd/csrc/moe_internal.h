@@ -174,6 +174,9 @@ struct FfnBwdFp8Args {
     void* dws2;
 };
 size_t ffn_backward_fp8_workspace_bytes(const moe_cfg& c);
+// byte offsets of the FP8 backward's intermediates in its workspace, in the
+// order of the MOE_BWD8_* indices of moe_inspect.h
+void ffn_backward_fp8_offsets(const moe_cfg& c, size_t off[25]);
 // saved: the a, b, h a training forward kept (carve_saved), else recomputed
 hipError_t launch_expert_ffn_backward_fp8(const moe_cfg& c, const FfnBwdFp8Args& a, void* ws,
                                           hipStream_t st, const void* saved = nullptr);

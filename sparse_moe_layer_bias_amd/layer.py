@@ -241,8 +241,12 @@ class MoeLayer:
                  dx=torch.empty((T, d), **a))
         ffn_ws = (moe_expert_ffn_backward_fp8_workspace_size(self.cfg) if self.fp8 else
                   moe_expert_ffn_backward_workspace_size(self.cfg))
-        wsb = max(ffn_ws, moe_route_backward_workspace_size(self.cfg), 256)
-        g["workspace"] = torch.empty((wsb,), dtype=torch.uint8, device=dev)
+        # separate workspaces: the expert backward's keeps its intermediates
+        # (readable through moe_expert_ffn_backward_fp8_offsets) until the
+        # next backward call
+        g["workspace"] = torch.empty((max(ffn_ws, 256),), dtype=torch.uint8, device=dev)
+        g["route_workspace"] = torch.empty((max(moe_route_backward_workspace_size(self.cfg), 256),),
+                                           dtype=torch.uint8, device=dev)
         return g
 
     def expert_ffn_backward(self, dout, x, stream=None):
@@ -285,7 +289,7 @@ class MoeLayer:
         mark(2)
         moe_route_backward(self.cfg, x, self.scores, self.idx, g["dgate"], self.offsets,
                            self.src_token, self.dst_row, g["dz"], g["dcentroids"],
-                           g["workspace"], stream)
+                           g["route_workspace"], stream)
         mark(3)
         moe_input_grad(self.cfg, dout if residual else None, g["dx_shared"], g["dx_perm"],
                        self.dst_row, g["dz"], self.idx, centroids, g["dx"], stream)

@@ -203,62 +203,6 @@ def check_fp8_expert_split(orc, layer, ref, x_host, rows=None, residual=True, wh
     return ins
 
 
-def assert_close_fp8_bwd(got, ref, what="", rtol=RTOL["fp8"], elem=3.0):
-    """FP8 backward outputs against the fully independent oracle.  Both sides
-    quantise h, [da db] and the row-direction tiles from bf16 values that can
-    differ in the last bit, so a code at a rounding midpoint can differ and
-    move an element by up to a code step.  Criterion: every element within
-    elem*rtol, at least 99.99% within rtol (elementwise rule as in
-    assert_close), each row's relative L2 error within rtol."""
-    g, r = to_f64(got), to_f64(ref)
-    assert g.shape == r.shape, (what, g.shape, r.shape)
-    if r.size == 0:
-        return
-    r2 = r.reshape(-1, r.shape[-1])
-    g2 = g.reshape(r2.shape)
-    rms = np.sqrt(np.mean(r2 ** 2, axis=1, keepdims=True))
-    den = np.abs(r2) + rms
-    err = np.abs(g2 - r2)
-    rel = np.where(den > 0, err / np.where(den > 0, den, 1.0), np.where(err > 0, np.inf, 0.0))
-    frac_out = float(np.mean(rel > rtol))
-    assert np.all(rel <= elem * rtol), "%s: max elementwise rel err %.3g > %g" % (
-        what, float(rel.max()), elem * rtol)
-    assert frac_out <= 1e-4, "%s: %.2e of elements beyond %g" % (what, frac_out, rtol)
-    row = np.linalg.norm(g2 - r2, axis=1) / np.maximum(np.linalg.norm(r2, axis=1), 1e-30)
-    assert np.all(row <= rtol), "%s: row L2 rel err %.3g > %g" % (what, float(row.max()), rtol)
-
-
-def assert_close_fp8_grad(got, ref, what="", rtol=RTOL["fp8"], elem=3.0):
-    """FP8 weight gradients [experts..., rows, cols].  Criterion as
-    assert_close_fp8_bwd (elem = 3, see the FP8 backward tests), with each
-    element's scale the larger of its row's RMS and its expert matrix's RMS,
-    and the relative L2 error taken per expert matrix.  A weight-gradient row
-    of an expert with few rows is nearly an outer product scaled by one
-    gradient value, which may be a near-cancelling sum: such a row can be far
-    below the matrix's scale, and its own RMS is then no measure of the error
-    (as for the fp32 gradients)."""
-    g, r = to_f64(got), to_f64(ref)
-    assert g.shape == r.shape, (what, g.shape, r.shape)
-    if r.size == 0:
-        return
-    g3 = g.reshape((-1,) + g.shape[-2:])
-    r3 = r.reshape(g3.shape)
-    rms_row = np.sqrt(np.mean(r3 ** 2, axis=2, keepdims=True))
-    rms_mat = np.sqrt(np.mean(r3 ** 2, axis=(1, 2), keepdims=True))
-    den = np.abs(r3) + np.maximum(rms_row, rms_mat)
-    err = np.abs(g3 - r3)
-    rel = np.where(den > 0, err / np.where(den > 0, den, 1.0), np.where(err > 0, np.inf, 0.0))
-    assert np.all(rel <= elem * rtol), "%s: max elementwise rel err %.3g > %g at %s" % (
-        what, float(rel.max()), elem * rtol, np.unravel_index(int(np.argmax(rel)), rel.shape))
-    frac_out = float(np.mean(rel > rtol))
-    assert frac_out <= 1e-4, "%s: %.2e of elements beyond %g" % (what, frac_out, rtol)
-    for i in range(r3.shape[0]):
-        nr = np.linalg.norm(r3[i])
-        ne = np.linalg.norm(g3[i] - r3[i])
-        assert ne <= rtol * nr or (nr == 0 and ne == 0), "%s[%d]: L2 rel err %.3g" % (
-            what, i, ne / max(nr, 1e-300))
-
-
 def assert_bits(got, ref, what=""):
     g, r = np.asarray(got), np.asarray(ref)
     assert g.shape == r.shape, (what, g.shape, r.shape)
@@ -352,3 +296,177 @@ def small_layer_inputs(cfg, seed=0, T=None):
     inp = moe_inputs.make_layer_inputs(c, seed, "cpu")
     dev = {k: v.cuda() for k, v in inp.items()}
     return c, inp, dev
+
+
+class ExpertCodes:
+    """The oracle's 128x128 block quantisation of one expert's weights at a time
+    (host copy of the bf16 weights -> oracle quantiser), for ref["w13_q"][e]
+    and the like; the last expert is kept."""
+
+    def __init__(self, orc, w, part):
+        self.orc, self.w, self.part = orc, w, part
+        self.e, self.val = None, None
+
+    def __getitem__(self, e):
+        e = int(e)
+        if self.e != e:
+            self.val = self.orc.quant_weight_fp8(to_host(self.w[e]))
+            self.e = e
+        return self.val[self.part]
+
+
+class RowsOf:
+    """rows of a host array through an index map (a gather the oracle did)"""
+
+    def __init__(self, a, src):
+        self.a, self.src = a, src
+
+    def __getitem__(self, r):
+        return self.a[self.src[r]]
+
+
+# ------------------------------------------------------------------ FP8 backward, step by step
+
+def _ws_view(ws, off, n, dtype, shape):
+    esz = torch.tensor([], dtype=dtype).element_size()
+    return ws[off:off + n * esz].view(dtype).view(shape)
+
+
+def check_fp8_backward_split(orc, layer, fwd, x_host, dout_host, what="", groups=None):
+    """The FP8 expert backward checked step by step against the oracle's steps
+    fed the GPU's own inputs (moe_expert_ffn_backward_fp8's workspace through
+    moe_expert_ffn_backward_fp8_offsets):
+      bytes, bit for bit: dY, [da db] 1x128 row tiles; the 128x1 row-direction
+        tiles of dY, h, [da db] and x (oracle quantisers on the GPU's bf16 values)
+      dh, dX, dW2, dW13: the oracle's GEMM on those codes, 6e-2 plain rule
+      [da db]: the oracle's SwiGLU derivative of the GPU's dh, a, b, bf16 rule
+      a, b, h (bf16): the oracle's recompute from the same codes, bf16 rule
+    Groups: the routed experts (rows of x_perm) and the shared expert (index
+    N); `groups` limits the check to some (default: all).  `fwd` holds the
+    oracle's offsets, src_token, x_q_perm / x_s_perm (row-indexable), x_q /
+    x_s, and the weight codes (w13_q[e] ..., ws13_q ...)."""
+    import sparse_moe_layer_bias_amd as moe
+    c = layer.c
+    T, k, d, N, I = c["T"], c["k"], c["d"], c["N"], c["I"]
+    Is = layer.cfg.inter_shared
+    R, S = T * k, (T if Is > 0 else 0)
+    Im = max(I, Is)
+    g = layer.grads
+    ws = g["workspace"]
+    off = moe.moe_expert_ffn_backward_fp8_offsets(layer.cfg)
+    Vd = lambda name, n, dt, shape: _ws_view(ws, off[name], n, dt, shape)
+    if layer.saved is not None:
+        so = moe.moe_expert_ffn_saved_offsets(layer.cfg)
+        src, ab_o, h_o, abs_o, hs_o = layer.saved, so["ab"], so["h"], so["ab_sh"], so["h_sh"]
+    else:
+        src, ab_o, h_o, abs_o, hs_o = ws, off["ab"], off["h"], off["ab_sh"], off["h_sh"]
+    dev = dict(
+        ab=_ws_view(src, ab_o, R * 2 * I, torch.bfloat16, (R, 2 * I)),
+        h=_ws_view(src, h_o, R * I, torch.bfloat16, (R, I)),
+        dy=g["dy_perm"],
+        dy_q=Vd("dy_q", R * d, torch.uint8, (R, d)),
+        dy_s=Vd("dy_s", R * d // 128, torch.float32, (R, d // 128)),
+        dh=Vd("dh", R * I, torch.bfloat16, (R, I)),
+        dab=Vd("dab", R * 2 * I, torch.bfloat16, (R, 2 * I)),
+        dab_q=Vd("dab_q", R * 2 * I, torch.uint8, (R, 2 * I)),
+        dab_s=Vd("dab_s", R * 2 * I // 128, torch.float32, (R, 2 * I // 128)),
+        dx=g["dx_perm"])
+    if S:
+        dev_sh = dict(
+            ab=_ws_view(src, abs_o, S * 2 * Is, torch.bfloat16, (S, 2 * Is)),
+            h=_ws_view(src, hs_o, S * Is, torch.bfloat16, (S, Is)),
+            dy_q=Vd("dy_q_sh", S * d, torch.uint8, (S, d)),
+            dy_s=Vd("dy_s_sh", S * d // 128, torch.float32, (S, d // 128)),
+            dh=Vd("dh_sh", S * Is, torch.bfloat16, (S, Is)),
+            dab=Vd("dab_sh", S * 2 * Is, torch.bfloat16, (S, 2 * Is)),
+            dab_q=Vd("dab_q_sh", S * 2 * Is, torch.uint8, (S, 2 * Is)),
+            dab_s=Vd("dab_s_sh", S * 2 * Is // 128, torch.float32, (S, 2 * Is // 128)),
+            dx=g["dx_shared"])
+    poff = to_host(Vd("poff", N + 2, torch.int32, (N + 2,)))
+    offsets = np.asarray(fwd["offsets"], np.int64)
+    M_g = [int(offsets[e + 1] - offsets[e]) for e in range(N)] + [S]
+    assert_bits(poff, np.concatenate([[0], np.cumsum([(m + 127) // 128 * 128 for m in M_g])])
+                .astype(np.int32), what + "padded offsets")
+    P = int(poff[-1])
+    col = {}
+    for name, F in (("col_dy", d), ("col_h", Im), ("col_dab", 2 * Im), ("col_x", d)):
+        col[name] = (Vd(name, P * F, torch.uint8, (P // 128, F, 128)),
+                     Vd(name + "_s", P // 128 * F, torch.float32, (P // 128, F)))
+
+    def cols_of(name, gi, C):
+        q, s = col[name]
+        pb0, M = int(poff[gi]) // 128, M_g[gi]
+        nb = (M + 127) // 128
+        qh = to_host(q[pb0:pb0 + nb, :C, :])
+        codes = qh.transpose(0, 2, 1).reshape(nb * 128, C)[:M]
+        return np.ascontiguousarray(codes), np.ascontiguousarray(to_host(s[pb0:pb0 + nb, :C]))
+
+    def bits(a, b, label):
+        if a.dtype == np.float32:
+            a, b = a.view(np.uint32), b.view(np.uint32)
+        assert_bits(a, b, what + label)
+
+    src_tok = fwd["src_token"]
+    dw2, dw13 = g["dw2"], g["dw13"]
+    err = {"dh": 0.0, "dab": 0.0, "dx": 0.0, "dw2": 0.0, "dw13": 0.0, "ab": 0.0}
+    if groups is None:
+        groups = range(N + (1 if S else 0))
+    for e in groups:
+        shared = e == N
+        M = M_g[e]
+        if M == 0:
+            assert not torch.any(dw2[e]) and not torch.any(dw13[e])
+            continue
+        if shared:
+            Ie, w13q, w13s, w2q, w2s = Is, fwd["ws13_q"], fwd["ws13_s"], fwd["ws2_q"], fwd["ws2_s"]
+            a_in, as_in = fwd["x_q"], fwd["x_s"]
+            G = {n: to_host(v) for n, v in dev_sh.items()}
+            G["dy"] = dout_host
+            x_e = x_host
+            dw2_e, dw13_e = to_host(g["dws2"]), to_host(g["dws13"])
+        else:
+            a0, a1 = int(offsets[e]), int(offsets[e + 1])
+            Ie, w13q, w13s, w2q, w2s = I, fwd["w13_q"][e], fwd["w13_s"][e], fwd["w2_q"][e], \
+                fwd["w2_s"][e]
+            rows = np.arange(a0, a1)
+            a_in, as_in = fwd["x_q_perm"][rows], fwd["x_s_perm"][rows]
+            G = {n: to_host(v[a0:a1]) for n, v in dev.items()}
+            x_e = x_host[src_tok[a0:a1]]
+            dw2_e, dw13_e = to_host(dw2[e]), to_host(dw13[e])
+        label = "(group %d)" % e
+        for vals, codes, scales, nm in ((G["dy"], G["dy_q"], G["dy_s"], "dY"),
+                                        (G["dab"], G["dab_q"], G["dab_s"], "[da db]")):
+            q, s = orc.quant_act_fp8(vals)
+            bits(codes, q, "%s row-tile codes %s" % (nm, label))
+            bits(scales, s, "%s row-tile scales %s" % (nm, label))
+        ab_ref, h_ref = orc.fp8_recompute_ab(a_in, as_in, w13q, w13s)
+        err["ab"] = max(err["ab"], max_rule_err(G["ab"], ab_ref), max_rule_err(G["h"], h_ref))
+        assert_close(G["ab"], ab_ref, RTOL["bf16"], what + "a, b " + label)
+        assert_close(G["h"], h_ref, RTOL["bf16"], what + "h " + label)
+        dh_ref = orc.fp8_dgrad(G["dy_q"], G["dy_s"], w2q, w2s)
+        dab_ref = orc.swiglu_bwd_bf16(G["dh"], G["ab"])
+        dx_ref = orc.fp8_dgrad(G["dab_q"], G["dab_s"], w13q, w13s)
+        for n, (gv, rv) in (("dh", (G["dh"], dh_ref)), ("dab", (G["dab"], dab_ref)),
+                            ("dx", (G["dx"], dx_ref))):
+            err[n] = max(err[n], max_rule_err(gv, rv))
+        assert_close_fp8(G["dh"], dh_ref, what + "dh " + label)
+        assert_close(G["dab"], dab_ref, RTOL["bf16"], what + "[da db] " + label)
+        assert_close_fp8(G["dx"], dx_ref, what + "dX " + label)
+        cdy = cols_of("col_dy", e, d)
+        ch = cols_of("col_h", e, Ie)
+        ct = cols_of("col_dab", e, 2 * Ie)
+        cx = cols_of("col_x", e, d)
+        for (cq, cs), v, nm in ((cdy, G["dy"], "dY"), (ch, G["h"], "h"),
+                                (ct, G["dab"], "[da db]"), (cx, x_e, "x")):
+            q, s = orc.quant_cols_fp8(v)
+            bits(cq, q, "%s row-direction codes %s" % (nm, label))
+            bits(cs, s, "%s row-direction scales %s" % (nm, label))
+        w2_ref = orc.fp8_wgrad(*cdy, *ch)
+        w13_ref = orc.fp8_wgrad(*ct, *cx)
+        err["dw2"] = max(err["dw2"], max_rule_err(dw2_e, w2_ref))
+        err["dw13"] = max(err["dw13"], max_rule_err(dw13_e, w13_ref))
+        assert_close_fp8(dw2_e, w2_ref, what + "dW2 " + label)
+        assert_close_fp8(dw13_e, w13_ref, what + "dW13 " + label)
+    log(what + "FP8 backward steps, max error (row rule): " +
+        ", ".join("%s %.2e" % kv for kv in err.items()))
+    return err

@@ -1,20 +1,23 @@
 """GPU parity of the FP8 backward: libmoe's backward calls for an FP8 layer
 (moe_expert_ffn_backward_fp8 for the experts, through the C ABI) against the
-oracle's FP8 backward on the same seeded inputs and upstream gradient.
+oracle's FP8 backward, step by step.
 
-Tolerance: the FP8 criterion of parity_util.assert_close_fp8_bwd (rtol 6e-2),
-with the elementwise bound at 3 rtol instead of 2.  Both sides re-quantise
-intermediate tensors (h, [da db], the row-direction tiles) from values that
-differ in their last bits (MFMA summation order against exact sums), so a code
-at a rounding midpoint can legitimately differ.  One code step is 2^-3 of its
-value; a weight gradient of an expert with M rows is a sum of M such terms, and
-at the small sizes here (10-30 rows per expert) one term can be ~4x the typical
-one, so a single differing code moves an element by up to ~0.125 * 4 / sqrt(M)
-~ 0.15 of its row's RMS.  The whole tensors agree to ~0.3% (relative L2), and
-both sides are ~5% from the exact gradient of the dequantised operands.  The
-weight gradients take the larger of the row's and the expert matrix's RMS as
-an element's scale (parity_util.assert_close_fp8_grad): with one token an
-expert's dW13 row is da[n] times x, and da[n] can be a near-cancelling sum.
+Each step of the expert FFN backward is compared with the oracle's step fed
+the GPU's own inputs (read from the backward's workspace through
+moe_expert_ffn_backward_fp8_offsets): every E4M3 code and tile scale bit for
+bit (dY in 1x128 row tiles, [da db] in 1x128 row tiles, and the 128x1
+row-direction tiles of dY, h, [da db] and the gathered x), the recomputed a, b
+and h at the bf16 rule, dh, dX, dW2 and dW13 at the plain FP8 rule (6e-2 of the
+row's RMS, elementwise within 2 of it), [da db] at the bf16 rule.  The
+combine, gate, logit, centroid and input gradients are checked the same way
+against the oracle's bf16 steps.
+
+Beside that contract, each gradient is compared with the fully independent
+oracle (its own quantisation of its own intermediates) norm-wise within 6e-2:
+both sides re-quantise intermediates (h, [da db], the row-direction tiles)
+from values that differ in their last bits (MFMA summation order against exact
+sums), so single codes at rounding midpoints can differ, and elementwise bounds
+on the end results would then measure that, not the kernels.
 """
 import numpy as np
 import pytest
@@ -22,8 +25,9 @@ import torch
 
 import moe_inputs
 import sparse_moe_layer_bias_amd as moe
-from parity_util import (assert_close_fp8_bwd, assert_close_fp8_grad, guard_grads, guard_layer,
-                         host_inputs, log, small_layer_inputs)
+from parity_util import (RTOL, ExpertCodes, RowsOf, assert_bits, check_fp8_backward_split,
+                         assert_close, guard_grads, guard_layer, host_inputs, log, row_rel_l2,
+                         small_layer_inputs, to_f64)
 from sparse_moe_layer_bias_amd.layer import MoeLayer
 
 pytestmark = pytest.mark.gpu
@@ -59,7 +63,44 @@ def _run(orc, seed=0, residual=True, save=True, **over):
     fwd = orc.layer_forward(h, c, residual=residual)
     ref = orc.layer_backward(h, c, fwd, moe_inputs.to_host(dout), residual=residual)
     ref["idx"] = fwd["idx"]
+    layer.test_fwd, layer.test_host, layer.test_dout_host = fwd, h, moe_inputs.to_host(dout)
     return c, layer, g, ref
+
+
+def _check_steps(orc, layer, g, ref, residual=True):
+    """Every backward step against the oracle's step fed the GPU's own inputs
+    (expert FFN: check_fp8_backward_split; combine, gate/logit, centroid and
+    input gradients: the oracle's bf16 steps), at the plain rules; then, beside
+    the contract, each gradient against the fully independent oracle,
+    norm-wise within 6e-2 (both sides quantise intermediates that differ in
+    their last bits, so single codes at rounding midpoints can differ)."""
+    fwd, h, dout = layer.test_fwd, layer.test_host, layer.test_dout_host
+    T = layer.c["T"]
+    check_fp8_backward_split(orc, layer, fwd, h["x"], dout)
+    H = moe_inputs.to_host
+    gate, idx, dst = H(layer.gate), H(layer.idx), H(layer.dst_row)
+    assert_bits(gate, fwd["gate"], "gate")
+    assert_bits(dst, fwd["dst_row"], "dst_row")
+    dyp, dg = orc.combine_backward(dout, H(layer.y_perm), gate, dst)
+    assert_close(H(g["dy_perm"]), dyp, RTOL["bf16"], "dy_perm")
+    assert_close(H(g["dgate"]), dg, RTOL["bf16"], "dgate")
+    dz = orc.route_backward(H(layer.scores), idx, H(g["dgate"]))
+    assert_close(H(g["dz"]), dz, RTOL["bf16"], "dz")
+    dE = orc.centroid_grad(h["x"], idx, H(g["dz"]), layer.c["N"])
+    assert_close(H(g["dcentroids"]), dE, RTOL["bf16"], "dcentroids")
+    dx = orc.input_grad(dout if residual else None, H(g["dx_shared"]), H(g["dx_perm"]), dst,
+                        H(g["dz"]), idx, h["centroids"])
+    assert_close(H(g["dx"]), dx, RTOL["bf16"], "dx")
+    for n in ("dx_perm", "dx_shared", "dx"):
+        l2 = row_rel_l2(H(g[n]), ref[n])
+        assert np.all(l2 <= RTOL["fp8"]), "%s vs independent oracle: row L2 %.3g" % (n, l2.max())
+    for n in ("dw13", "dw2", "dws13", "dws2"):
+        a, b = to_f64(H(g[n])), to_f64(ref[n])
+        a3, b3 = a.reshape((-1,) + a.shape[-2:]), b.reshape((-1,) + b.shape[-2:])
+        for i in range(a3.shape[0]):
+            nr, ne = np.linalg.norm(b3[i]), np.linalg.norm(a3[i] - b3[i])
+            assert ne <= RTOL["fp8"] * nr or (nr == 0 and ne == 0), "%s[%d] L2 %.3g" % (
+                n, i, ne / max(nr, 1e-300))
 
 
 FP8_CASES = [
@@ -76,20 +117,14 @@ FP8_CASES = [
 def test_fp8_backward_parity_small(orc, over):
     c, layer, g, ref = _run(orc, **dict(over))
     assert np.array_equal(moe_inputs.to_host(layer.idx), ref["idx"])
-    for n in ("dy_perm", "dx_perm", "dx_shared", "dz", "dcentroids", "dx"):
-        assert_close_fp8_bwd(moe_inputs.to_host(g[n]), ref[n], n, elem=3.0)
-    for n in ("dw13", "dw2", "dws13", "dws2"):
-        assert_close_fp8_grad(moe_inputs.to_host(g[n]), ref[n], n)
+    _check_steps(orc, layer, g, ref)
 
 
 @pytest.mark.parametrize("over", [dict(T=77), dict(T=700, d=384, N=2, k=1, I=256, Is=128)])
 def test_fp8_backward_parity_recompute(orc, over):
     """Without kept activations the backward recomputes a, b, h on FP8."""
     c, layer, g, ref = _run(orc, save=False, **dict(over))
-    for n in ("dx_perm", "dx_shared", "dx"):
-        assert_close_fp8_bwd(moe_inputs.to_host(g[n]), ref[n], n, elem=3.0)
-    for n in ("dw13", "dw2", "dws13", "dws2"):
-        assert_close_fp8_grad(moe_inputs.to_host(g[n]), ref[n], n)
+    _check_steps(orc, layer, g, ref)
 
 
 @pytest.mark.parametrize("T", [1, 300])
@@ -109,7 +144,7 @@ def test_fp8_training_forward_is_bitwise_the_inference_forward(T):
 
 def test_fp8_backward_without_residual_and_deterministic(orc):
     c, layer, g, ref = _run(orc, seed=3, residual=False, T=96)
-    assert_close_fp8_bwd(moe_inputs.to_host(g["dx"]), ref["dx"], "dx", elem=3.0)
+    _check_steps(orc, layer, g, ref, residual=False)
     first = {n: moe_inputs.to_host(g[n]).copy() for n in ("dx", "dw13", "dw2", "dws13", "dws2")}
     layer.backward(layer.test_dout, layer.test_x, layer.test_centroids, residual=False)
     torch.cuda.synchronize()
@@ -131,38 +166,50 @@ def test_fp8_transposed_packs_are_the_transposed_codes():
     assert torch.equal(layer.w2t, direct)
 
 
-def test_v3_fp8_backward_one_expert_and_sampled_tokens(orc):
-    """DeepSeek-V3-shaped FP8 layer, the launches the benchmark times: the
-    full weight gradients and row gradients of the least-loaded expert, and the
-    shared expert's input gradient of sampled tokens, against the oracle."""
+@pytest.mark.timeout(900)
+def test_v3_fp8_backward_one_expert(orc):
+    """DeepSeek-V3-shaped FP8 layer, the launches the benchmark times: every
+    backward step of the least-loaded expert against the oracle's steps fed
+    the GPU's own inputs (bytes bit for bit, values at the plain rules), and
+    its gradients against the fully independent oracle norm-wise; an expert
+    without rows gets zero weight gradients."""
     cfg = dict(moe_inputs.CONFIGS["v3_fp8"])
     T, N, k, d = cfg["T"], cfg["N"], cfg["k"], cfg["d"]
     log("generating V3-shaped FP8 inputs on the GPU")
     dev = moe_inputs.make_layer_inputs(cfg, 0, "cuda")
     dout = moe_inputs.make_upstream_grad(cfg, 0, "cuda")
     layer = MoeLayer(cfg, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"], train=True)
+    bias0 = dev["bias"].clone()
     layer.forward(dev["x"], dev["centroids"], dev["bias"].clone())
     g = layer.backward(dout, dev["x"], dev["centroids"])
     torch.cuda.synchronize()
     log("V3 FP8 backward done")
-    off = moe_inputs.to_host(layer.offsets).astype(np.int64)
-    counts = np.diff(off)
-    e = int(np.argmin(np.where(counts > 0, counts, 1 << 30)))
-    a, b = int(off[e]), int(off[e + 1])
-    src = moe_inputs.to_host(layer.src_token)[a:b]
     xh = moe_inputs.to_host(dev["x"])
-    xq = moe_inputs.to_host(layer.x_perm[a:b])
-    xs = moe_inputs.to_host(layer.x_perm_s[a:b])
-    assert np.array_equal(xq, orc.quant_act_fp8(xh[src])[0])   # the forward's tiles
+    r = orc.route(xh, moe_inputs.to_host(dev["centroids"]), moe_inputs.to_host(bias0), k,
+                  cfg["G"], cfg["TG"])
+    off, src, dst = orc.permute(r["idx"], N)
+    assert_bits(moe_inputs.to_host(layer.offsets), off, "offsets")
+    xq, xs = orc.quant_act_fp8(xh)
+    fwd = dict(offsets=off, src_token=src, x_q_perm=RowsOf(xq, src), x_s_perm=RowsOf(xs, src),
+               x_q=xq, x_s=xs, w13_q=ExpertCodes(orc, dev["w13"], 0),
+               w13_s=ExpertCodes(orc, dev["w13"], 1), w2_q=ExpertCodes(orc, dev["w2"], 0),
+               w2_s=ExpertCodes(orc, dev["w2"], 1))
+    counts = np.diff(off.astype(np.int64))
+    e = int(np.argmin(np.where(counts > 0, counts, 1 << 30)))
+    log("step checks of expert", e, "with", int(counts[e]), "rows")
+    check_fp8_backward_split(orc, layer, fwd, xh, None, what="V3 FP8: ", groups=[e])
+    a, b = int(off[e]), int(off[e + 1])
     dy = moe_inputs.to_host(g["dy_perm"][a:b])
     q13, s13 = orc.quant_weight_fp8(moe_inputs.to_host(dev["w13"][e]))
     q2, s2 = orc.quant_weight_fp8(moe_inputs.to_host(dev["w2"][e]))
-    log("oracle FP8 backward of expert", e, "with", b - a, "rows")
-    dA, dw13, dw2 = orc.swiglu_ffn_backward_fp8(xq, xs, xh[src], q13, s13, q2, s2, dy)
-    assert_close_fp8_bwd(moe_inputs.to_host(g["dx_perm"][a:b]), dA, "dx_perm rows of expert %d" % e,
-                     elem=3.0)
-    assert_close_fp8_grad(moe_inputs.to_host(g["dw13"][e]), dw13, "dw13 of expert %d" % e)
-    assert_close_fp8_grad(moe_inputs.to_host(g["dw2"][e]), dw2, "dw2 of expert %d" % e)
+    dA, dw13, dw2 = orc.swiglu_ffn_backward_fp8(xq[src[a:b]], xs[src[a:b]], xh[src[a:b]], q13,
+                                                s13, q2, s2, dy)
+    l2 = row_rel_l2(moe_inputs.to_host(g["dx_perm"][a:b]), dA)
+    assert np.all(l2 <= RTOL["fp8"]), "dx_perm vs independent oracle: row L2 %.3g" % l2.max()
+    for n, ref in (("dw13", dw13), ("dw2", dw2)):
+        got = to_f64(moe_inputs.to_host(g[n][e]))
+        ne, nr = np.linalg.norm(got - to_f64(ref)), np.linalg.norm(to_f64(ref))
+        assert ne <= RTOL["fp8"] * nr, "%s of expert %d: L2 %.3g" % (n, e, ne / nr)
     # an expert without rows gets zeros
     if np.any(counts == 0):
         z = int(np.nonzero(counts == 0)[0][0])

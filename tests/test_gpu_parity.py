@@ -15,8 +15,8 @@ import torch
 
 import moe_inputs
 import sparse_moe_layer_bias_amd as moe
-from parity_util import (RTOL, assert_bits, assert_close, assert_close_fp8, check_fp8_expert_split,
-                         guard_layer, host_inputs, log, small_layer_inputs)
+from parity_util import (RTOL, ExpertCodes, RowsOf, assert_bits, assert_close, assert_close_fp8,
+                         check_fp8_expert_split, guard_layer, host_inputs, log, small_layer_inputs)
 from sparse_moe_layer_bias_amd.layer import MoeLayer
 
 pytestmark = pytest.mark.gpu
@@ -458,23 +458,6 @@ def v3_fp8_run():
     torch.cuda.empty_cache()
 
 
-class _ExpertCodes:
-    """The oracle's 128x128 block quantisation of one expert's weights at a time
-    (host copy of the bf16 weights -> oracle quantiser), for ref["w13_q"][e]
-    and the like; the last expert is kept."""
-
-    def __init__(self, orc, w, part):
-        self.orc, self.w, self.part = orc, w, part
-        self.e, self.val = None, None
-
-    def __getitem__(self, e):
-        e = int(e)
-        if self.e != e:
-            self.val = self.orc.quant_weight_fp8(moe_inputs.to_host(self.w[e]))
-            self.e = e
-        return self.val[self.part]
-
-
 def _v3_tokens(cfg, idx, seed, n=64):
     """n tokens at random plus the first and last, covering all expert groups"""
     rng = np.random.default_rng(seed)
@@ -526,26 +509,16 @@ def test_v3_fp8_layer_parity(orc, v3_fp8_run):
     tok = _v3_tokens(cfg, r["idx"], 3)
     rows = np.sort(r["dst_row"][tok].ravel())
     ref = dict(r, x_q=xq, x_s=xs,
-               w13_q=_ExpertCodes(orc, dev["w13"], 0), w13_s=_ExpertCodes(orc, dev["w13"], 1),
-               w2_q=_ExpertCodes(orc, dev["w2"], 0), w2_s=_ExpertCodes(orc, dev["w2"], 1))
-    ref["x_q_perm"] = _RowsOf(xq, src)
-    ref["x_s_perm"] = _RowsOf(xs, src)
+               w13_q=ExpertCodes(orc, dev["w13"], 0), w13_s=ExpertCodes(orc, dev["w13"], 1),
+               w2_q=ExpertCodes(orc, dev["w2"], 0), w2_s=ExpertCodes(orc, dev["w2"], 1))
+    ref["x_q_perm"] = RowsOf(xq, src)
+    ref["x_s_perm"] = RowsOf(xs, src)
     ref["ws13_q"], ref["ws13_s"] = orc.quant_weight_fp8(moe_inputs.to_host(dev["ws13"]))
     ref["ws2_q"], ref["ws2_s"] = orc.quant_weight_fp8(moe_inputs.to_host(dev["ws2"]))
     log("checking the expert FFN on %d routed rows of %d tokens" % (len(rows), len(tok)))
     check_fp8_expert_split(orc, layer, ref, xh, rows=rows, what="V3 FP8: ")
     new_b = orc.bias_update(r["counts"], cfg["T"] * cfg["k"], moe_inputs.to_host(bias0))
     assert_bits(moe_inputs.to_host(bias).view(np.uint32), new_b.view(np.uint32), "bias update")
-
-
-class _RowsOf:
-    """rows of a host array through an index map (a gather the oracle did)"""
-
-    def __init__(self, a, src):
-        self.a, self.src = a, src
-
-    def __getitem__(self, r):
-        return self.a[self.src[r]]
 
 
 def test_v3_routing_all_tokens(orc, v3_run):
