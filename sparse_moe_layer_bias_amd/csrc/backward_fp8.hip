@@ -251,213 +251,203 @@ struct WgFp8 {
 
 // out[n][c] = sum over the group's 128-row blocks u of
 //   (sA[n,u] sB[c,u]) * sum_{rows of u} qA[n,row] qB[c,row]
-// One workgroup (8 waves) = one group and 128 output rows n, sweeping the
-// output columns c in tiles of 256: a flattened loop over steps (column tile,
-// block u).  A step's operands (16 KB of A^T and 32 KB of B^T codes, their
-// scales) are copied global -> LDS by buffer DMA into one of 3 stages, two
-// steps ahead (the swizzle goes through the source addresses; B rows past the
-// end are clamped to the last row -- they only feed output columns that are
-// not stored).  Wave (wa, wb) owns rows wa*64.. and columns wb*64.. of the
-// tile as 2 x 2 blocks of 32x32x64 MFMAs with the B^T rows as the first
-// operand, so that a lane holds one output row n and 4 consecutive columns
-// per register group.  Per block the two K halves accumulate
-// the code products into a fresh partial (MFMA scale operands 1.0), promoted
-// into the fp32 result with the product of the two fp32 scales.  A finished
-// tile is stored at the start of the next step, before that step's copies are
-// issued, so that the newest vector-memory operations in flight at every wait
-// are always copies (loads complete in order among themselves).
-constexpr int WG_THREADS = 512;
-constexpr int WG_TB = 256;                       // output columns per tile
-constexpr int WG_NS = 3;                         // LDS stages
-constexpr int WG_A = 128 * 128, WG_B = WG_TB * 128;
-constexpr int WG_STAGE = WG_A + WG_B + 4 * (128 + WG_TB);
+// One workgroup (8 waves) = one 128 x 128 output tile of one group.  The
+// gradients are written once and never read here, so the kernel is bound by
+// those writes: short workgroups that end right after their stores let the
+// next ones start while the stores drain (vmcnt counts loads and stores in
+// issue order, so a workgroup that waited for new copies after a store would
+// wait for the store too), and two of them share a CU.  A block's operands
+// (16 KB of A^T and 16 KB of B^T codes, their scales) are copied global ->
+// LDS by buffer DMA into one of 2 stages, all blocks up front when the group
+// has at most two (the swizzle goes through the source addresses).
+//
+// Wave (wa, wb) owns rows wa*32.. and columns wb*64.. of the tile as 2 x 4
+// blocks of 16x16x128 MFMAs with the B^T rows as the first operand, so that a
+// lane holds one output row n and 4 consecutive columns per block.  One such
+// MFMA takes a whole 128-row block (its code products, scale operands 1.0),
+// whose result is promoted into the fp32 sum right away with the product of
+// the two fp32 scales; no partial sum is carried between instructions, so a
+// wave needs under 128 registers and four waves share a SIMD.  The finished
+// tile is staged through LDS so that every output row leaves as one
+// contiguous 256-byte run: stores straight from the MFMA layout would write
+// 32-byte pieces of 16 rows per instruction, which the non-temporal path
+// writes to HBM as partial lines.
+//
+// Tile order: with N a multiple of 8, routed expert g's tiles go to XCD g % 8
+// (block b runs on XCD b % 8) one expert after another, so the expert's
+// operand tiles are shared in that XCD's L2; the shared expert's tiles come
+// last.  Within a group the tiles go in bands of 8 column tiles, row tile by
+// row tile, so that the ~64 workgroups an XCD holds at once read 8 A^T and 8
+// B^T tiles between them.
+constexpr int WT_THREADS = 512;
+constexpr int WT_A = 128 * 128, WT_B = 128 * 128;
+constexpr int WT_STAGE = WT_A + WT_B + 4 * 256;
+constexpr int WT_BAND = 8;
 
-__global__ void __launch_bounds__(WG_THREADS, 1) wgrad_fp8_kernel(WgFp8 p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[WG_NS * WG_STAGE];
-    const int64_t tar = p.rowsA_r / 128;
-    const int64_t unit = blockIdx.x;
+__global__ void __launch_bounds__(WT_THREADS, 4) wgrad_fp8_kernel(WgFp8 p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * WT_STAGE];
+    const int64_t upg = (p.rowsA_r / 128) * (p.rowsB_r / 128);  // tiles per routed expert
+    const int64_t b = blockIdx.x;
     int g;
-    int64_t ta, rowsA, rowsB;
+    int64_t t, rowsA, rowsB;
     uint16_t* out;
-    if (unit < (int64_t)p.N * tar) {
-        g = (int)(unit / tar);
-        ta = unit % tar;
+    if (b < (int64_t)p.N * upg) {
+        if (p.N % 8 == 0) {
+            const int64_t s = b >> 3;
+            g = (int)((s / upg) * 8 + (b & 7));
+            t = s % upg;
+        } else {
+            g = (int)(b / upg);
+            t = b % upg;
+        }
         rowsA = p.rowsA_r;
         rowsB = p.rowsB_r;
         out = p.out_r + (int64_t)g * rowsA * rowsB;
     } else {
-        if (!p.has_shared) return;
         g = p.N;
-        ta = unit - (int64_t)p.N * tar;
+        t = b - (int64_t)p.N * upg;
         rowsA = p.rowsA_s;
         rowsB = p.rowsB_s;
-        if (ta >= rowsA / 128) return;
+        if (!p.has_shared || t >= (rowsA / 128) * (rowsB / 128)) return;
         out = p.out_s;
     }
-    const int t = threadIdx.x;
-    const int lane = t & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int wa = wave & 1, wb = wave >> 1, h = lane >> 5;
+    // bands of WT_BAND column tiles, row tile by row tile within a band
+    const int64_t nta = rowsA / 128, ntb = rowsB / 128;
+    const int64_t band = t / (nta * WT_BAND), bw = min((int64_t)WT_BAND, ntb - band * WT_BAND);
+    const int64_t in_band = t - band * nta * WT_BAND;
+    const int64_t ta = in_band / bw, tb = band * WT_BAND + in_band % bw;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wa = wave & 3, wb = wave >> 2;
     const int64_t P0 = p.poff[g];
     const int nb = (int)((p.poff[g + 1] - P0) / 128);
-    const int ntb = (int)((rowsB + WG_TB - 1) / WG_TB);
     const int64_t pb0 = P0 / 128;  // the group's first block
+    uint16_t* tile = out + ta * 128 * rowsB + tb * 128;
 
     if (nb == 0) {  // an expert without rows: zero gradient
-        for (int64_t i = t; i < 128 * rowsB / 8; i += WG_THREADS) {
-            const int64_t r = i / (rowsB / 8), c8 = i % (rowsB / 8);
-            *(uint4*)(out + (ta * 128 + r) * rowsB + c8 * 8) = make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int idx = tid + WT_THREADS * k, row = idx >> 4, c16 = idx & 15;
+            *(uint4*)(tile + row * rowsB + c16 * 8) = make_uint4(0, 0, 0, 0);
         }
         return;
     }
 
-    // buffer descriptors over the group's blocks (out-of-range lanes read 0)
+    // buffer descriptors over the group's blocks
     const i32x4_t rA = make_rsrc(p.At + pb0 * p.FA * 128, (int64_t)nb * p.FA * 128);
     const i32x4_t rB = make_rsrc(p.Bt + pb0 * p.FB * 128, (int64_t)nb * p.FB * 128);
     const i32x4_t rAs = make_rsrc(p.AtS + pb0 * p.FA, (int64_t)nb * p.FA * 4);
     const i32x4_t rBs = make_rsrc(p.BtS + pb0 * p.FB, (int64_t)nb * p.FB * 4);
-    // 1 KB copies: 8 rows of 128 bytes; lane l fills row 8k + l/8, slot l%8
-    // with the logical chunk that the swizzle puts there
-    const int crow = lane >> 3, cslot = lane & 7;
-    const int cnt = 2 + 4 + (wave < 6 ? 1 : 0);  // copies per wave and step
-    auto issue = [&](int s, int buf) {
-        const int tb = s / nb, u = s % nb;
-        uint8_t* st = smem + buf * WG_STAGE;
+    const int cnt = 2 + 2 + (wave < 4 ? 1 : 0);  // copies per wave and stage
+    // one block's copies: 1 KB copies of 8 rows of 128 bytes (lane l fills
+    // row 8k + l/8, slot l%8, with the logical chunk that the swizzle puts
+    // there); waves 0-1 also copy the A scales, waves 2-3 the B scales.  The
+    // offsets are recomputed at every call (the empty asm hides that they do
+    // not change): kept live through the loop they would push the MFMA loop's
+    // registers past the 128 of four waves a SIMD.
+    auto issue = [&](int u, int buf) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int crow = ln >> 3, cslot = ln & 7;
+        uint8_t* st = smem + buf * WT_STAGE;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int k = wave + 8 * j, r = 8 * k + crow;
-            const uint32_t voff = (uint32_t)(((ta * 128 + r) * 128) + sub_chunk8(r, cslot) * 16);
+            const uint32_t voff = (uint32_t)((ta * 128 + r) * 128 + sub_chunk8(r, cslot) * 16);
             dma_to_lds<16>(rA, st + k * 1024, voff, (uint32_t)(u * p.FA * 128));
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 2; ++j) {
             const int k = wave + 8 * j, r = 8 * k + crow;
-            int64_t br = (int64_t)tb * WG_TB + r;
-            br = br < rowsB ? br : rowsB - 1;
-            const uint32_t voff = (uint32_t)(br * 128 + sub_chunk8(r, cslot) * 16);
-            dma_to_lds<16>(rB, st + WG_A + k * 1024, voff, (uint32_t)(u * p.FB * 128));
+            const uint32_t voff = (uint32_t)((tb * 128 + r) * 128 + sub_chunk8(r, cslot) * 16);
+            dma_to_lds<16>(rB, st + WT_A + k * 1024, voff, (uint32_t)(u * p.FB * 128));
         }
-        float* sc = (float*)(st + WG_A + WG_B);
-        if (wave < 2) {
-            const uint32_t voff = (uint32_t)((ta * 128 + wave * 64 + lane) * 4);
-            dma_to_lds<4>(rAs, sc + wave * 64, voff, (uint32_t)(u * p.FA * 4));
-        } else if (wave < 6) {
-            int64_t br = (int64_t)tb * WG_TB + (wave - 2) * 64 + lane;
-            br = br < rowsB ? br : rowsB - 1;
-            dma_to_lds<4>(rBs, sc + 128 + (wave - 2) * 64, (uint32_t)(br * 4),
+        float* sc = (float*)(st + WT_A + WT_B);
+        if (wave < 2)
+            dma_to_lds<4>(rAs, sc + wave * 64, (uint32_t)((ta * 128 + wave * 64 + ln) * 4),
+                          (uint32_t)(u * p.FA * 4));
+        else if (wave < 4)
+            dma_to_lds<4>(rBs, sc + 128 + (wave - 2) * 64,
+                          (uint32_t)((tb * 128 + (wave - 2) * 64 + ln) * 4),
                           (uint32_t)(u * p.FB * 4));
-        }
     };
-    auto frag = [&](const uint8_t* base, int r, int q) {
-        const uint4 lo = *(const uint4*)(base + r * 128 + sub_chunk8(r, 4 * q + 2 * h) * 16);
-        const uint4 hi = *(const uint4*)(base + r * 128 + sub_chunk8(r, 4 * q + 2 * h + 1) * 16);
+    // A / B fragment of a 16x16x128 MFMA: lane l holds row r = l%16 of the
+    // operand block and its 32 codes 32 (l/16) .. +31 of the 128-row block
+    auto frag = [&](const uint8_t* base, int r) {
+        const int c = 2 * (lane >> 4);
+        const uint4 lo = *(const uint4*)(base + r * 128 + sub_chunk8(r, c) * 16);
+        const uint4 hi = *(const uint4*)(base + r * 128 + sub_chunk8(r, c + 1) * 16);
         return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                        (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     };
 
-    f32x16_t acc[2][2];  // [A block i][B block j]; lane: row n, 16 columns c
+    f32x4_t acc[2][4];  // [A block i][B block j]; lane: row n, 4 columns c
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-    const f32x16_t zero = acc[0][0];
-    // store the finished column tile tb and restart: staged through the free
-    // LDS stage `buf` in two halves of 128 columns (waves wb < 2, then wb >= 2)
-    // so that every output row leaves as contiguous 256-byte runs (direct
-    // stores from the accumulator layout would write 16-byte pieces of 32
-    // rows per instruction); non-temporal: the gradients are not read here
-    constexpr int SP = 128 + 8;  // padded staging row (elements)
-    auto flush = [&](int tb, int buf) {
-        uint16_t* stg = (uint16_t*)(smem + buf * WG_STAGE);
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            if ((wb >> 1) == half) {
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int row = wa * 64 + i * 32 + (lane & 31);
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-#pragma unroll
-                        for (int g4 = 0; g4 < 4; ++g4) {
-                            const int col = (wb & 1) * 64 + j * 32 + 8 * g4 + 4 * h;
-                            *(uint2*)(stg + row * SP + col) = make_uint2(
-                                pack_bf16x2(acc[i][j][4 * g4], acc[i][j][4 * g4 + 1]),
-                                pack_bf16x2(acc[i][j][4 * g4 + 2], acc[i][j][4 * g4 + 3]));
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) acc[i][j][4 * g4 + e] = 0.0f;
-                        }
-                }
-            }
-            lds_barrier();
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int idx = t + WG_THREADS * k, row = idx >> 4, c16 = idx & 15;
-                const int64_t col = (int64_t)tb * WG_TB + half * 128 + c16 * 8;
-                if (col < rowsB)
-                    __builtin_nontemporal_store(*(const u32x4_t*)(stg + row * SP + c16 * 8),
-                                                (u32x4_t*)(out + (ta * 128 + row) * rowsB + col));
-            }
-            lds_barrier();  // the staging rows are read before they are reused
-        }
-    };
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int steps = ntb * nb;
-#pragma unroll
-    for (int s = 0; s < WG_NS - 1; ++s)
-        if (s < steps) issue(s, s);
-    int pend = -1;  // a finished column tile not stored yet
-    for (int s = 0; s < steps; ++s) {
-        const int after = steps - 1 - s < WG_NS - 2 ? steps - 1 - s : WG_NS - 2;
-        vm_wait_n(after * cnt);
-        lds_barrier();  // step s landed for every wave; the stage of s-1 is free
-        if (pend >= 0) {  // the stage of step s-1 is free until this step's copies
-            flush(pend, (s + WG_NS - 1) % WG_NS);
-            pend = -1;
-        }
-        if (s + WG_NS - 1 < steps) issue(s + WG_NS - 1, (s + WG_NS - 1) % WG_NS);
-        const uint8_t* sA = smem + (s % WG_NS) * WG_STAGE;
-        const uint8_t* sB = sA + WG_A;
-        const float* scA = (const float*)(sB + WG_B);
+    issue(0, 0);
+    if (nb > 1) issue(1, 1);
+    for (int u = 0; u < nb; ++u) {
+        vm_wait_n(u + 1 < nb ? cnt : 0);  // block u landed (u + 1 may be in flight)
+        lds_barrier();
+        const uint8_t* sA = smem + (u & 1) * WT_STAGE;
+        const uint8_t* sB = sA + WT_A;
+        const float* scA = (const float*)(sB + WT_B);
         const float* scB = scA + 128;
-        f32x16_t part[2][2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            i32x8_t af[2], bf[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                af[i] = frag(sA, wa * 64 + i * 32 + (lane & 31), q);
-                bf[i] = frag(sB, wb * 64 + i * 32 + (lane & 31), q);
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        bf[j], af[i], q == 0 ? zero : part[i][j], 0, 0, 0, 127, 0, 127);
-        }
-        // promotion: lane holds output row n = lane%32 of A block i and
-        // columns 8 (v/4) + 4 (lane/32) + v%4 of B block j
+        i32x8_t af[2];
+        float sa[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const float sa = scA[wa * 64 + i * 32 + (lane & 31)];
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const float4 sb = *(const float4*)(scB + wb * 64 + j * 32 + 8 * g4 + 4 * h);
-                    acc[i][j][4 * g4 + 0] += part[i][j][4 * g4 + 0] * (sa * sb.x);
-                    acc[i][j][4 * g4 + 1] += part[i][j][4 * g4 + 1] * (sa * sb.y);
-                    acc[i][j][4 * g4 + 2] += part[i][j][4 * g4 + 2] * (sa * sb.z);
-                    acc[i][j][4 * g4 + 3] += part[i][j][4 * g4 + 3] * (sa * sb.w);
-                }
+            af[i] = frag(sA, wa * 32 + i * 16 + (lane & 15));
+            sa[i] = scA[wa * 32 + i * 16 + (lane & 15)];
         }
-        if (s % nb == nb - 1) pend = s / nb;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const i32x8_t bf = frag(sB, wb * 64 + j * 16 + (lane & 15));
+            const float4 sb = *(const float4*)(scB + wb * 64 + j * 16 + 4 * (lane >> 4));
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                // lane holds output row n = lane%16 of A block i and columns
+                // 4 (lane/16) .. +3 of B block j
+                const f32x4_t part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    bf, af[i], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 127, 0, 127);
+                acc[i][j][0] += part[0] * (sa[i] * sb.x);
+                acc[i][j][1] += part[1] * (sa[i] * sb.y);
+                acc[i][j][2] += part[2] * (sa[i] * sb.z);
+                acc[i][j][3] += part[3] * (sa[i] * sb.w);
+            }
+        }
+        if (u + 2 < nb) {
+            lds_barrier();  // every wave is done with this stage
+            issue(u + 2, u & 1);
+        }
     }
-    if (pend >= 0) {
-        lds_barrier();  // every wave is done with the last step's stage
-        flush(pend, (steps - 1) % WG_NS);
+    // store: staged through the LDS stages as padded bf16 rows, then each
+    // output row leaves as one contiguous 256-byte run; non-temporal: the
+    // gradients are not read here
+    constexpr int SP = 128 + 8;  // padded staging row (elements)
+    static_assert(128 * SP * 2 <= 2 * WT_STAGE, "the staged tile fits in the stages");
+    uint16_t* stg = (uint16_t*)smem;
+    lds_barrier();  // every wave is done with the last stage
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int row = wa * 32 + i * 16 + (lane & 15);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int col = wb * 64 + j * 16 + 4 * (lane >> 4);
+            *(uint2*)(stg + row * SP + col) = make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]),
+                                                         pack_bf16x2(acc[i][j][2], acc[i][j][3]));
+        }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int idx = tid + WT_THREADS * k, row = idx >> 4, c16 = idx & 15;
+        __builtin_nontemporal_store(*(const u32x4_t*)(stg + row * SP + c16 * 8),
+                                    (u32x4_t*)(tile + row * rowsB + c16 * 8));
     }
 }
 
@@ -707,8 +697,9 @@ hipError_t launch_expert_ffn_backward_fp8(const moe_cfg& c, const FfnBwdFp8Args&
         p.rowsB_s = rBs;
         p.out_r = (uint16_t*)outr;
         p.out_s = (uint16_t*)outs;
-        const int64_t units = N * (rAr / 128) + (has_shared ? rAs / 128 : 0);
-        if (units > 0) wgrad_fp8_kernel<<<(unsigned)units, WG_THREADS, 0, st>>>(p);
+        const int64_t units = N * (rAr / 128) * (rBr / 128) +
+                              (has_shared ? (rAs / 128) * (rBs / 128) : 0);
+        if (units > 0) wgrad_fp8_kernel<<<(unsigned)units, WT_THREADS, 0, st>>>(p);
     };
     wgrad(w.gT, w.gTs, d, w.hT, w.hTs, Im, d, I, d, Is, a.dw2, a.dws2);
     wgrad(w.tT, w.tTs, 2 * Im, w.xT, w.xTs, d, 2 * I, d, 2 * Is, d, a.dw13, a.dws13);
