@@ -6,15 +6,19 @@
 // Topk of {s_{j,t} + b_j}, else 0; g = normalised g'.  The bias only decides
 // membership of the Topk.
 //
-// Two kernels:
+// Three kernels:
 //  router_logits: z = x E^T as a fixed-order fp32 FMA chain per output (k
 //    ascending from +0), so that the chosen indices are reproducible bit for
 //    bit; the chain runs on the VALU (MFMA has no defined summation order).
 //    Epilogue: s = fp32(1 / (1 + exp(-(double)z))).
 //  router_select: one wavefront per token; keys s+b (a NaN key ranks as
 //    -inf); optional group limit; k rounds of a wave-wide argmax under the
-//    total order (key desc, index asc); gates in double; per-expert load via
-//    integer atomics (order-free).
+//    total order (key desc, index asc), reduced with DPP lane exchanges;
+//    gates in double.
+//  route_counts: the per-expert load, an LDS histogram of idx (integer, so
+//    order-free); one workgroup for up to 64K (token, slot) pairs writes the
+//    counts directly.  Global atomics straight from the select kernel, 8 per
+//    token on N counters, cost about as much as the whole selection.
 #include "moe_internal.h"
 
 namespace moe {
@@ -294,13 +298,84 @@ __device__ __forceinline__ T shfl_xor(T v, int m) {
     return __shfl_xor(v, m, 64);
 }
 
+// Lane exchanges of a wave reduction, step S pairing disjoint lane sets so
+// that after steps 0..S every aligned block of 2^(S+1) lanes holds the same
+// result: 0, 1 = quad_perm xor 1 / xor 2, 2 = row_half_mirror (lane i <-> 7-i
+// in each 8 lanes), 3 = row_mirror (i <-> 15-i in each row of 16), all DPP
+// (no LDS); 4 = swizzle xor 16 in each 32 lanes; 5 = xor 32.
+template <int S>
+__device__ __forceinline__ int xlane(int v) {
+    if constexpr (S == 0) return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+    else if constexpr (S == 1) return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+    else if constexpr (S == 2) return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+    else if constexpr (S == 3) return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);
+    else if constexpr (S == 4) return __builtin_amdgcn_ds_swizzle(v, 0x401F);
+    else return __shfl_xor(v, 32, 64);
+}
+template <int S>
+__device__ __forceinline__ float xlane(float v) {
+    return __int_as_float(xlane<S>(__float_as_int(v)));
+}
+
+// one step of an argmax of (key v, index i, payload s) under "beats"
+template <int S>
+__device__ __forceinline__ void best_step(float& v, int& i, float& s) {
+    const float ov = xlane<S>(v), os = xlane<S>(s);
+    const int oi = xlane<S>(i);
+    if (beats(ov, oi, v, i)) { v = ov; i = oi; s = os; }
+}
+
+// argmax over the wave: DPP within rows, then the four rows' winners read
+// from lanes 0, 16, 32, 48; every lane gets the result
+__device__ __forceinline__ void wave_best(float& v, int& i, float& s) {
+    best_step<0>(v, i, s);
+    best_step<1>(v, i, s);
+    best_step<2>(v, i, s);
+    best_step<3>(v, i, s);
+    float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    int bi = __builtin_amdgcn_readlane(i, 0);
+    float bs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 0));
+#pragma unroll
+    for (int l = 16; l < 64; l += 16) {
+        const float ov = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+        const int oi = __builtin_amdgcn_readlane(i, l);
+        const float os = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), l));
+        if (beats(ov, oi, bv, bi)) { bv = ov; bi = oi; bs = os; }
+    }
+    v = bv;
+    i = bi;
+    s = bs;
+}
+
+// merge the partner's best two (key, index) pairs into ours (both sorted)
+template <int S>
+__device__ __forceinline__ void top2_step(float& r1, int& i1, float& r2, int& i2) {
+    const float p1 = xlane<S>(r1), p2 = xlane<S>(r2);
+    const int q1 = xlane<S>(i1), q2 = xlane<S>(i2);
+    if (beats(p1, q1, r1, i1)) {
+        // partner's first wins; second is the better of (r1, p2)
+        if (beats(r1, i1, p2, q2)) { r2 = r1; i2 = i1; } else { r2 = p2; i2 = q2; }
+        r1 = p1; i1 = q1;
+    } else if (beats(p1, q1, r2, i2)) {
+        r2 = p1; i2 = q1;
+    }
+}
+
+// group score = sum of the group's two best keys, -0 -> +0, NaN -> -inf
+__device__ __forceinline__ float group_score(float r1, float r2) {
+    float sc = r1 + r2;
+    if (sc == 0.0f) sc = 0.0f;
+    if (sc != sc) sc = -__builtin_inff();  // +inf + -inf ranks like a NaN key
+    return sc;
+}
+
 // Each lane holds up to SEL_RK keys of one token: experts lane + 64*r
-// (SEL_RK = 16 covers N <= 1024).
+// (SEL_RK = 16 covers N <= 1024).  All reductions are exact under the total
+// order "beats", so their pairing order does not change any result.
 template <int SEL_RK>
 __global__ void __launch_bounds__(256) router_select_kernel(
     const float* __restrict__ s, const float* __restrict__ bias, int32_t* __restrict__ idx_out,
-    float* __restrict__ gate_out, int32_t* __restrict__ counts, int64_t T, int N, int k, int G,
-    int TG) {
+    float* __restrict__ gate_out, int64_t T, int N, int k, int G, int TG) {
     const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (t >= T) return;
@@ -328,40 +403,52 @@ __global__ void __launch_bounds__(256) router_select_kernel(
     }
 
     if (G > 1) {
-        // group g = experts [g*gs, (g+1)*gs); score = sum of its two best keys;
-        // lane g ends up holding group g's score
+        // group g = experts [g*gs, (g+1)*gs); score = sum of its two best
+        // keys; lane g ends up holding group g's score
         const int gs = N / G;
         float my_gscore = -__builtin_inff();
-        for (int g = 0; g < G; ++g) {
-            float r1 = -__builtin_inff(), r2 = -__builtin_inff();
-            int i1 = 0x7fffffff, i2 = 0x7fffffff;
+        if (gs <= 64 && (gs & (gs - 1)) == 0) {
+            // a group is an aligned block of gs lanes of one r: reduce the
+            // blocks of every r at once, log2(gs) steps
 #pragma unroll
             for (int r = 0; r < SEL_RK; ++r) {
-                const int i = lane + 64 * r;
-                if (!ok[r] || i / gs != g) continue;
-                if (beats(rv[r], i, r1, i1)) {
-                    r2 = r1; i2 = i1; r1 = rv[r]; i1 = i;
-                } else if (beats(rv[r], i, r2, i2)) {
-                    r2 = rv[r]; i2 = i;
-                }
+                float r1 = ok[r] ? rv[r] : -__builtin_inff(), r2 = -__builtin_inff();
+                int i1 = ok[r] ? lane + 64 * r : 0x7fffffff, i2 = 0x7fffffff;
+                if (gs >= 2) top2_step<0>(r1, i1, r2, i2);
+                if (gs >= 4) top2_step<1>(r1, i1, r2, i2);
+                if (gs >= 8) top2_step<2>(r1, i1, r2, i2);
+                if (gs >= 16) top2_step<3>(r1, i1, r2, i2);
+                if (gs >= 32) top2_step<4>(r1, i1, r2, i2);
+                if (gs >= 64) top2_step<5>(r1, i1, r2, i2);
+                // group g = (64 r + the block's first lane) / gs sits at lane
+                // (g * gs) % 64 of this r
+                const float sc = group_score(r1, r2);
+                const int src = (lane * gs) & 63;
+                const float v = __shfl(sc, src, 64);
+                if (lane < G && (lane * gs) / 64 == r) my_gscore = v;
             }
+        } else {
+            for (int g = 0; g < G; ++g) {
+                float r1 = -__builtin_inff(), r2 = -__builtin_inff();
+                int i1 = 0x7fffffff, i2 = 0x7fffffff;
 #pragma unroll
-            for (int m = 1; m < 64; m <<= 1) {
-                const float p1 = shfl_xor(r1, m), p2 = shfl_xor(r2, m);
-                const int q1 = shfl_xor(i1, m), q2 = shfl_xor(i2, m);
-                // merge two sorted pairs, keep the best two
-                if (beats(p1, q1, r1, i1)) {
-                    // partner's first wins; second is the better of (r1, p2)
-                    if (beats(r1, i1, p2, q2)) { r2 = r1; i2 = i1; } else { r2 = p2; i2 = q2; }
-                    r1 = p1; i1 = q1;
-                } else {
-                    if (beats(p1, q1, r2, i2)) { r2 = p1; i2 = q1; }
+                for (int r = 0; r < SEL_RK; ++r) {
+                    const int i = lane + 64 * r;
+                    if (!ok[r] || i / gs != g) continue;
+                    if (beats(rv[r], i, r1, i1)) {
+                        r2 = r1; i2 = i1; r1 = rv[r]; i1 = i;
+                    } else if (beats(rv[r], i, r2, i2)) {
+                        r2 = rv[r]; i2 = i;
+                    }
                 }
+                top2_step<0>(r1, i1, r2, i2);
+                top2_step<1>(r1, i1, r2, i2);
+                top2_step<2>(r1, i1, r2, i2);
+                top2_step<3>(r1, i1, r2, i2);
+                top2_step<4>(r1, i1, r2, i2);
+                top2_step<5>(r1, i1, r2, i2);
+                if (lane == g) my_gscore = group_score(r1, r2);
             }
-            float sc = r1 + r2;
-            if (sc == 0.0f) sc = 0.0f;
-            if (sc != sc) sc = -__builtin_inff();  // +inf + -inf ranks like a NaN key
-            if (lane == g) my_gscore = sc;
         }
         // keep the TG best groups: TG rounds of argmax over lanes 0..G-1
         bool kept = false;
@@ -369,12 +456,8 @@ __global__ void __launch_bounds__(256) router_select_kernel(
         for (int p = 0; p < TG; ++p) {
             float bv = cand ? my_gscore : -__builtin_inff();
             int bi = cand ? lane : 0x7fffffff;
-#pragma unroll
-            for (int m = 1; m < 64; m <<= 1) {
-                const float ov = shfl_xor(bv, m);
-                const int oi = shfl_xor(bi, m);
-                if (beats(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-            }
+            float unused = 0.0f;
+            wave_best(bv, bi, unused);
             if (lane == bi) { kept = true; cand = false; }
         }
         // experts outside the kept groups are not eligible
@@ -399,13 +482,7 @@ __global__ void __launch_bounds__(256) router_select_kernel(
             const int i = lane + 64 * r;
             if (ok[r] && beats(rv[r], i, bv, bi)) { bv = rv[r]; bi = i; bs = sv[r]; }
         }
-#pragma unroll
-        for (int m = 1; m < 64; m <<= 1) {
-            const float ov = shfl_xor(bv, m);
-            const int oi = shfl_xor(bi, m);
-            const float os = shfl_xor(bs, m);
-            if (beats(ov, oi, bv, bi)) { bv = ov; bi = oi; bs = os; }
-        }
+        wave_best(bv, bi, bs);
         // the owner lane drops the winner from its candidates
 #pragma unroll
         for (int r = 0; r < SEL_RK; ++r)
@@ -418,7 +495,43 @@ __global__ void __launch_bounds__(256) router_select_kernel(
     if (lane < k) {
         idx_out[t * k + lane] = my_idx;
         gate_out[t * k + lane] = (float)((double)my_s / S);
-        atomicAdd(&counts[my_idx], 1);
+    }
+}
+
+// Per-expert load of the step: a histogram of idx [T*k], one workgroup per
+// RC_CHUNK entries, each wave counting into its own LDS copy (fewer lanes
+// contend for one bin), then the copies summed.  A single workgroup writes
+// the counts directly; more add their non-zero bins to counts zeroed
+// beforehand.  Integer counts: the order of the additions does not matter.
+constexpr int RC_CHUNK = 65536, RC_MAXN = 1024, RC_WAVES = 16;
+__global__ void __launch_bounds__(64 * RC_WAVES) route_counts_kernel(
+    const int32_t* __restrict__ idx, int64_t n, int N, int32_t* __restrict__ counts, int direct) {
+    extern __shared__ int32_t h[];  // [RC_WAVES][N]
+    const int wave = threadIdx.x >> 6;
+    for (int i = threadIdx.x; i < RC_WAVES * N; i += blockDim.x) h[i] = 0;
+    __syncthreads();
+    // all of a thread's entries are loaded before the first LDS atomic, so
+    // that the loads overlap instead of each waiting behind an atomic
+    constexpr int PER = RC_CHUNK / (64 * RC_WAVES);
+    const int64_t a = (int64_t)blockIdx.x * RC_CHUNK;
+    const int64_t b = n < a + RC_CHUNK ? n : a + RC_CHUNK;
+    int v[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int64_t i = a + threadIdx.x + (int64_t)j * 64 * RC_WAVES;
+        v[j] = i < b ? idx[i] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+        if (v[j] >= 0) atomicAdd(&h[wave * N + v[j]], 1);
+    __syncthreads();
+    for (int e = threadIdx.x; e < N; e += blockDim.x) {
+        int c = 0;
+        for (int w = 0; w < RC_WAVES; ++w) c += h[w * N + e];
+        if (direct)
+            counts[e] = c;
+        else if (c)
+            atomicAdd(&counts[e], c);
     }
 }
 
@@ -489,20 +602,25 @@ hipError_t launch_route(const moe_cfg& c, const void* x, const float* centroids,
         launch_logits<2>(c.act_dtype, full, x, centroids, scores, T, d, N, st);
     else
         launch_logits<1>(c.act_dtype, full, x, centroids, scores, T, d, N, st);
-    fill_i32_kernel<<<dim3((unsigned)cdiv(N, 256)), 256, 0, st>>>(counts, N, 0);
     const int G = c.n_group > 1 ? (int)c.n_group : 1;
     const dim3 gs((unsigned)cdiv(T, 4));
     const int K = (int)c.top_k, TG = (int)c.topk_group, NN = (int)N;
     if (N <= 64)
-        router_select_kernel<1><<<gs, 256, 0, st>>>(scores, bias, idx, gate, counts, T, NN, K, G, TG);
+        router_select_kernel<1><<<gs, 256, 0, st>>>(scores, bias, idx, gate, T, NN, K, G, TG);
     else if (N <= 128)
-        router_select_kernel<2><<<gs, 256, 0, st>>>(scores, bias, idx, gate, counts, T, NN, K, G, TG);
+        router_select_kernel<2><<<gs, 256, 0, st>>>(scores, bias, idx, gate, T, NN, K, G, TG);
     else if (N <= 256)
-        router_select_kernel<4><<<gs, 256, 0, st>>>(scores, bias, idx, gate, counts, T, NN, K, G, TG);
+        router_select_kernel<4><<<gs, 256, 0, st>>>(scores, bias, idx, gate, T, NN, K, G, TG);
     else if (N <= 512)
-        router_select_kernel<8><<<gs, 256, 0, st>>>(scores, bias, idx, gate, counts, T, NN, K, G, TG);
+        router_select_kernel<8><<<gs, 256, 0, st>>>(scores, bias, idx, gate, T, NN, K, G, TG);
     else
-        router_select_kernel<16><<<gs, 256, 0, st>>>(scores, bias, idx, gate, counts, T, NN, K, G, TG);
+        router_select_kernel<16><<<gs, 256, 0, st>>>(scores, bias, idx, gate, T, NN, K, G, TG);
+    static_assert(RC_MAXN >= 1024, "the ABI allows up to 1024 experts");
+    const int64_t n = T * K;
+    const int64_t blocks = cdiv(n, RC_CHUNK);
+    if (blocks > 1) fill_i32_kernel<<<dim3((unsigned)cdiv(N, 256)), 256, 0, st>>>(counts, N, 0);
+    route_counts_kernel<<<dim3((unsigned)blocks), 64 * RC_WAVES, RC_WAVES * N * 4, st>>>(
+        idx, n, NN, counts, blocks == 1 ? 1 : 0);
     return hipGetLastError();
 }
 

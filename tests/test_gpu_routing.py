@@ -111,3 +111,49 @@ def test_nan_rows_route_to_valid_experts(orc, G, TG):
     assert_bits(got["counts"], r["counts"], "counts")
     _bits_nan_aware(got["scores"], r["scores"], "scores")
     _bits_nan_aware(got["gate"], r["gate"], "gate")
+
+
+# (N, G, TG, k): group sizes gs = N / G that the select kernel reduces as
+# aligned lane blocks (powers of two up to 64) and ones it reduces group by
+# group (gs = 25, 128); N up to 1024 reaches every keys-per-lane instance
+GROUP_CASES = [
+    (128, 64, 16, 8),    # gs 2
+    (256, 64, 8, 8),     # gs 4
+    (64, 8, 3, 6),       # gs 8
+    (256, 16, 4, 8),     # gs 16
+    (96, 3, 2, 8),       # gs 32
+    (192, 3, 2, 6),      # gs 64
+    (256, 2, 1, 8),      # gs 128: group by group
+    (100, 4, 2, 8),      # gs 25: group by group
+    (512, 8, 4, 8),      # gs 64, 8 keys per lane
+    (1024, 64, 8, 8),    # gs 16, 16 keys per lane
+]
+
+
+@pytest.mark.parametrize("N,G,TG,k", GROUP_CASES)
+def test_group_limited_select(orc, N, G, TG, k):
+    T, d = 300, 256
+    log("group select case N=%d G=%d TG=%d k=%d" % (N, G, TG, k))
+    inp = _route_inputs(T, d, N, "bf16", seed=N + G)
+    got = _route_gpu(T, d, N, k, G, TG, "bf16", inp)
+    h = {n: moe_inputs.to_host(v) for n, v in inp.items()}
+    r = orc.route(h["x"], h["centroids"], h["bias"], k, G, TG, want_scores=True)
+    for n in ("scores", "idx", "gate", "counts"):
+        assert_bits(got[n], r[n], n)
+
+
+@pytest.mark.parametrize("G,TG", [(1, 1), (8, 3), (4, 2)])
+def test_select_ties_go_to_lower_indices(orc, G, TG):
+    """x = 0 gives every score Sigmoid(0) = 0.5 exactly; a bias with three
+    distinct values makes keys and group scores tie in many places, so every
+    choice is decided by the lower index (expert, then group)."""
+    T, d, N, k = 128, 256, 64, 8
+    inp = _route_inputs(T, d, N, "bf16", seed=5)
+    inp["x"].zero_()
+    inp["bias"].copy_(torch.tensor([(i % 3) * 0.25 for i in range(N)], dtype=torch.float32))
+    got = _route_gpu(T, d, N, k, G, TG, "bf16", inp)
+    h = {n: moe_inputs.to_host(v) for n, v in inp.items()}
+    r = orc.route(h["x"], h["centroids"], h["bias"], k, G, TG, want_scores=True)
+    assert np.all(got["scores"] == 0.5)
+    for n in ("idx", "gate", "counts"):
+        assert_bits(got[n], r[n], n)
