@@ -183,27 +183,38 @@ __global__ void __launch_bounds__(256) quant_cols_t_kernel(ColQuant p) {
     if (c0 >= C) return;
     const int64_t r0 = row0 - p.poff[g];  // first row of the block within the group
     const int64_t M = routed ? p.offsets[g + 1] - p.offsets[g] : p.S;
-    const int valid = (int)(M - r0 < 128 ? M - r0 : 128);
+    const int valid = (int)(M - r0 < 128 ? M - r0 : 128);  // >= 1: the block holds rows
     const int t = threadIdx.x;
+    // the 4 passes' rows: their source row indices first, then all row loads,
+    // then the transposed LDS stores, so that the memory latencies overlap
+    // (rows past the group's last read its last row and are stored as zeros)
+    int64_t sr[4];
 #pragma unroll
     for (int pass = 0; pass < 4; ++pass) {
-        const int row = pass * 32 + (t >> 3), cc = (t & 7) * 8;
-        float f[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (row < valid) {
-            const uint16_t* src;
-            if (routed) {
-                const int64_t rr = p.offsets[g] + r0 + row;
-                src = p.src_r + (p.gather ? (int64_t)p.gather[rr] : rr) * p.ld_r;
-            } else {
-                src = p.src_s + (r0 + row) * p.ld_s;
-            }
-            const uint4 v = *(const uint4*)(src + c0 + cc);
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        const int row = pass * 32 + (t >> 3);
+        const int64_t rc = r0 + (row < valid ? row : valid - 1);
+        if (routed) {
+            const int64_t rr = p.offsets[g] + rc;
+            sr[pass] = p.gather ? (int64_t)p.gather[rr] : rr;
+        } else {
+            sr[pass] = rc;
+        }
+    }
+    const uint16_t* base = routed ? p.src_r : p.src_s;
+    const int64_t ld = routed ? p.ld_r : p.ld_s;
+    const int cc = (t & 7) * 8;
+    uint4 v[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                f[2 * i] = __uint_as_float(w[i] << 16);
-                f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-            }
+    for (int pass = 0; pass < 4; ++pass) v[pass] = *(const uint4*)(base + sr[pass] * ld + c0 + cc);
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+        const int row = pass * 32 + (t >> 3);
+        const uint32_t w[4] = {v[pass].x, v[pass].y, v[pass].z, v[pass].w};
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = row < valid ? __uint_as_float(w[i] << 16) : 0.0f;
+            f[2 * i + 1] = row < valid ? __uint_as_float(w[i] & 0xffff0000u) : 0.0f;
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) tile[row][cc + i] = f[i];
@@ -216,15 +227,13 @@ __global__ void __launch_bounds__(256) quant_cols_t_kernel(ColQuant p) {
     __syncthreads();
     const float amax = fmaxf(fmaxf(red[0][col], red[1][col]), fmaxf(red[2][col], red[3][col]));
     const float scale = amax / 448.0f;
+    // rows past the group's last hold zeros and encode as code 0
     uint32_t code[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         uint32_t wv = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = part * 32 + 4 * k + e;
-            if (row < valid) wv |= quant_e4m3(tile[row][col], scale) << (8 * e);
-        }
+        for (int e = 0; e < 4; ++e) wv |= quant_e4m3(tile[part * 32 + 4 * k + e][col], scale) << (8 * e);
         code[k] = wv;
     }
     uint8_t* o = p.out + ((row0 / 128) * p.F + c0 + col) * 128 + part * 32;
