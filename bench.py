@@ -1,15 +1,22 @@
 """Benchmark: one DeepSeekMoE layer step at DeepSeek-V3 shape on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v3_bf16|v3_fp8|mid_bf16]
-                    [--no-cpu-baseline] [--backward]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload v3_bf16|v3_fp8|skew_balance|mid_bf16|tiny_fp32]
+                    [--no-cpu-baseline] [--no-configs] [--no-probes] [--backward]
+                    [--vendor-calibration]
 
 A step is the whole hot path on one batch already resident in HBM:
 route -> permute -> expert FFN (routed + shared) -> combine -> bias update.
 Prints ONE JSON line.  `value` is tokens per second of the whole step;
 `roofline` describes the dominant stage, the grouped expert GEMMs (gate/up
 with fused SwiGLU, then down), timed live with HIP events on the stream they
-run on, against the roofline (HBM or MFMA) that bounds its algorithmic work; `cpu_baseline` is the CPU oracle timed on a bounded sample of the same
-workload on this host.
+run on, against the roofline (HBM or MFMA) that bounds its algorithmic work,
+with the HBM traffic the rocprofv3 counter summaries under profiles/ record
+for the same GEMM sources; `cpu_baseline` is the CPU oracle timed on a
+bounded sample of the same workload on this host.  Unless --no-configs, the
+line also carries `configs`: the FP8 workload (with its own roofline and
+oracle time), the decode-sized skewed batch (bias-balancing trajectory and
+the layer at T = 128) and the small workloads, measured after the headline.
 
 --backward measures the layer's backward instead: a step is the four backward
 calls -- combine backward, expert FFN backward (two dgrad and two wgrad GEMMs,
