@@ -462,6 +462,48 @@ def cpu_baseline(cfg, dev, log, rows=4096):
                       % (S, R, cfg["k"] + 1)}
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_layer(cfg, dev, log, single_thread=False):
+    """The oracle's whole layer step (route, permute, every expert, combine)
+    on the whole batch, no sample and no extrapolation -- for the small
+    workloads, where it takes seconds.  With single_thread, also timed on one
+    host thread."""
+    import moe_inputs
+    from oracle import oracle as orc
+
+    h = {n: moe_inputs.to_host(v) for n, v in dev.items()}
+    orc.lib()
+
+    def run():
+        t0 = time.perf_counter()
+        orc.layer_forward(h, cfg)
+        return time.perf_counter() - t0
+
+    cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    dt = run()
+    out = {"value": cfg["T"] / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "sample": "the whole layer step on all %d tokens" % cfg["T"], "cpu": cpu_model()}
+    if single_thread:
+        prev = orc.set_threads(1)
+        try:
+            dt1 = run()
+        finally:
+            orc.set_threads(prev)
+        out["single_thread"] = {"value": cfg["T"] / dt1, "unit": "tokens/s", "cores": 1}
+    log("cpu oracle, whole layer: %d tokens in %.3f s" % (cfg["T"], dt))
+    return out
+
+
 def cpu_baseline_backward(cfg, dev, log):
     """Time the oracle's backward (untuned) on a bounded sample and scale to
     tokens/s: the combine, gate/logit, centroid and input gradients on all T
@@ -773,6 +815,13 @@ def extra_configs(args, dev, log):
         ms, st = time_forward(lay, d2["x"], d2["centroids"], d2["bias"].clone(), 20, 5)
         out[name] = {"ms_per_step": ms, "tokens_per_s": c["T"] / (ms / 1e3), "stages_ms": st}
         log("%s: %.4f ms/step" % (name, ms))
+        if not args.no_cpu_baseline:
+            try:
+                out[name]["cpu_baseline"] = cpu_baseline_layer(c, d2, log,
+                                                               single_thread=name == "tiny_fp32")
+            except Exception as ex:  # report, never hide
+                log("cpu baseline (%s) failed: %r" % (name, ex))
+                out[name]["cpu_baseline"] = None
         del lay, d2
     return out
 

@@ -899,3 +899,20 @@ void orc_swiglu_ffn_backward_fp8(int64_t M, int64_t d, int64_t I, const uint8_t*
     free(h); free(ab); free(dh); free(dab); free(gq); free(gs); free(tq); free(ts);
     free(cg); free(cgs); free(ch); free(chs); free(ct); free(cts); free(cx); free(cxs);
 }
+
+/* Timing support only (the CPU baseline times the oracle with all host
+ * threads and with one): the number of OpenMP threads the next parallel
+ * regions use; returns the previous maximum.  n < 1 leaves it unchanged. */
+#ifdef _OPENMP
+#include <omp.h>
+int orc_set_threads(int n) {
+    const int prev = omp_get_max_threads();
+    if (n >= 1) omp_set_num_threads(n);
+    return prev;
+}
+#else
+int orc_set_threads(int n) {  /* a build without OpenMP runs on one thread */
+    (void)n;
+    return 1;
+}
+#endif

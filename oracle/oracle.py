@@ -43,6 +43,15 @@ def lib():
     return _lib
 
 
+def set_threads(n):
+    """OpenMP threads of the oracle's next calls (timing only); returns the
+    previous maximum."""
+    L = lib()
+    L.orc_set_threads.argtypes = [ctypes.c_int]
+    L.orc_set_threads.restype = ctypes.c_int
+    return int(L.orc_set_threads(int(n)))
+
+
 def _declare(L):
     P = ctypes.c_void_p
     I64 = ctypes.c_int64
