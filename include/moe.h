@@ -113,7 +113,11 @@ size_t moe_permute_workspace_size(const moe_cfg* cfg);
  *  src_token    [T*k]         int32      out, token of each row
  *  dst_row      [T, k]        int32      out, row of each (token, slot)
  *  x_perm       [T*k, d]      out: act_dtype rows (gemm_dtype != FP8) or
- *                             E4M3 codes (gemm_dtype == FP8)
+ *                             E4M3 codes (gemm_dtype == FP8).  May be NULL
+ *                             for bf16 / fp32 layers: then only offsets,
+ *                             src_token and dst_row are written (for
+ *                             moe_expert_ffn_gather, which reads the rows of x
+ *                             through src_token itself)
  *  x_perm_scale [T*k, d/128]  fp32 out, FP8 tile scales (FP8 only, else NULL)
  *  x_q          [T, d]        u8   out, FP8 codes of x for the shared expert (FP8 only)
  *  x_s          [T, d/128]    fp32 out, their tile scales (FP8 only)
@@ -176,6 +180,22 @@ int moe_expert_ffn(const moe_cfg* cfg, const void* x_perm, const float* x_perm_s
                    const float* x_sh_scale, const void* ws13, const float* ws13_scale,
                    const void* ws2, const float* ws2_scale, void* y_shared, void* workspace,
                    size_t workspace_bytes, void* stream);
+
+/* moe_expert_ffn for bf16 layers (act_dtype = gemm_dtype = MOE_BF16) without
+ * the permuted copy of the tokens: routed row r is x[src_token[r]], read by
+ * the gate/up GEMM's own copies ("Methode" item 2: each routed expert sees
+ * the tokens that chose it; the dispatch is the same permutation, its rows
+ * are not materialised).  Results are those of moe_expert_ffn on the x_perm
+ * that moe_permute would have written, bit for bit.
+ *  x          [T, d]   bf16  the layer input
+ *  src_token  [T*k]    int32 from moe_permute (which may skip x_perm for this)
+ *  the other arguments as moe_expert_ffn (x_sh is normally x itself; no
+ *  scales).  Requires T * d * 2 < 2^32 (32-bit row offsets into x), else
+ *  MOE_ERR_UNSUPPORTED; other layers: MOE_ERR_UNSUPPORTED. */
+int moe_expert_ffn_gather(const moe_cfg* cfg, const void* x, const int32_t* src_token,
+                          const int32_t* offsets, const void* w13, const void* w2, void* y_perm,
+                          const void* x_sh, const void* ws13, const void* ws2, void* y_shared,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Weight preparation, off the per-step path (weights are constant across
  * steps).  Rearranges one weight stack into the order the expert GEMM streams

@@ -170,10 +170,10 @@ int moe_permute(const moe_cfg* cfg, const void* x, const int32_t* idx, int32_t* 
         REQ_PTR(idx);
         REQ_PTR(src_token);
         REQ_PTR(dst_row);
-        REQ_PTR(x_perm);
         if (cfg->gemm_dtype == MOE_FP8_E4M3) {
             if (cfg->hidden % 128)
                 return fail(MOE_ERR_UNSUPPORTED, "%s: FP8 needs hidden %% 128 == 0", fn);
+            REQ_PTR(x_perm);  // x_perm may be NULL only for bf16 / fp32 layers
             REQ_PTR(x_perm_scale);
             REQ_PTR(x_q);
             REQ_PTR(x_s);
@@ -200,10 +200,10 @@ int moe_permute_noalloc(const moe_cfg* cfg, const void* x, const int32_t* idx, i
         REQ_PTR(idx);
         REQ_PTR(src_token);
         REQ_PTR(dst_row);
-        REQ_PTR(x_perm);
         if (cfg->gemm_dtype == MOE_FP8_E4M3) {
             if (cfg->hidden % 128)
                 return fail(MOE_ERR_UNSUPPORTED, "%s: FP8 needs hidden %% 128 == 0", fn);
+            REQ_PTR(x_perm);  // x_perm may be NULL only for bf16 / fp32 layers
             REQ_PTR(x_perm_scale);
             REQ_PTR(x_q);
             REQ_PTR(x_s);
@@ -238,7 +238,8 @@ static int expert_ffn_impl(const char* fn, const moe_cfg* cfg, const void* x_per
                            const void* ws13, const float* ws13_scale, const void* ws2,
                            const float* ws2_scale, void* y_shared, void* saved,
                            void* workspace, size_t workspace_bytes, void* stream,
-                           float* h_f32 = nullptr, float* h_f32_shared = nullptr) {
+                           float* h_f32 = nullptr, float* h_f32_shared = nullptr,
+                           const int32_t* gather = nullptr) {
     if (int r = check_cfg(fn, cfg)) return r;
     if (int r = check_ffn_shape(fn, cfg)) return r;
     const bool fp8 = cfg->gemm_dtype == MOE_FP8_E4M3;
@@ -271,8 +272,26 @@ static int expert_ffn_impl(const char* fn, const moe_cfg* cfg, const void* x_per
     }
     moe::FfnArgs a{x_perm, x_perm_scale, offsets, w13, w13_scale, w2, w2_scale, y_perm,
                    x_sh,   x_sh_scale,   ws13,    ws13_scale, ws2, ws2_scale, y_shared};
+    a.gather = gather;
     return hip_status(fn, moe::launch_expert_ffn(*cfg, a, workspace, (hipStream_t)stream, saved,
                                                  h_f32, h_f32_shared));
+}
+
+int moe_expert_ffn_gather(const moe_cfg* cfg, const void* x, const int32_t* src_token,
+                          const int32_t* offsets, const void* w13, const void* w2, void* y_perm,
+                          const void* x_sh, const void* ws13, const void* ws2, void* y_shared,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "moe_expert_ffn_gather";
+    if (int r = check_cfg(fn, cfg)) return r;
+    if (cfg->act_dtype != MOE_BF16 || cfg->gemm_dtype != MOE_BF16)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 layers only (use moe_expert_ffn)", fn);
+    // the token copies address a row of x by a 32-bit byte offset
+    if (cfg->tokens * cfg->hidden * 2 >= ((int64_t)1 << 32))
+        return fail(MOE_ERR_UNSUPPORTED, "%s: tokens * hidden * 2 must stay below 2^32", fn);
+    if (cfg->tokens > 0) REQ_PTR(src_token);
+    return expert_ffn_impl(fn, cfg, x, nullptr, offsets, w13, nullptr, w2, nullptr, y_perm, x_sh,
+                           nullptr, ws13, nullptr, ws2, nullptr, y_shared, nullptr, workspace,
+                           workspace_bytes, stream, nullptr, nullptr, src_token);
 }
 
 extern "C" {

@@ -217,7 +217,9 @@ __device__ __forceinline__ void gemm_bf16_body(const WorkV2& w, uint16_t* smem) 
     // uniform bases + 32-bit per-lane byte offsets (scalar-base addressing)
     const char* wstage0 = w.W + (w.wt * (int64_t)nk * A_EL) * 2;
     const uint32_t woff = lane * 16;
-    const char* xbase = w.X + w.m0 * K * 2;  // the tile's first token row
+    // the tile's first token row; with a gather list the rows come from
+    // anywhere in X and each lane's offset carries its row
+    const char* xbase = w.gather ? w.X : w.X + w.m0 * K * 2;
 
     // Token copies: block b = G_RPB rows (rb = b / NSUB) of sub-tile q = b % NSUB,
     // each row one 2*G_SUB-byte line; the blocks holding real rows are the
@@ -233,7 +235,8 @@ __device__ __forceinline__ void gemm_bf16_body(const WorkV2& w, uint16_t* smem) 
         const int q = b % NSUB, rb = b / NSUB;
         const int r = rb * G_RPB + (int)((unsigned)lane / G_CPR), c = g_swz(r, (int)((unsigned)lane % G_CPR));
         const int64_t tr = r < mc ? r : mc - 1;  // clamp inside a partial block
-        xoff[j] = (uint32_t)((tr * K + q * G_SUB + c * 8) * 2);
+        const int64_t sr = w.gather ? (int64_t)w.gather[w.m0 + tr] : tr;
+        xoff[j] = (uint32_t)((sr * K + q * G_SUB + c * 8) * 2);
     }
 
     auto stage_a = [&](int s) { return smem + s * (A_EL + X_EL); };
@@ -667,6 +670,7 @@ hipError_t launch_expert_ffn(const moe_cfg& c, const FfnArgs& a, void* ws, hipSt
     p.B_s = a.ws13;
     p.C_r = w.h_r;
     p.C_s = w.h_s;
+    p.gather_r = a.gather;  // bf16 inference only (checked by the caller)
     const int cols0 = bf ? 128 : 64;
     p.ntn_r = (int)cdiv(c.inter, cols0);
     p.ntn_s = has_shared ? (int)cdiv(c.inter_shared, cols0) : 0;
@@ -688,6 +692,7 @@ hipError_t launch_expert_ffn(const moe_cfg& c, const FfnArgs& a, void* ws, hipSt
     }
 
     // down: h x W2 -> y  (bf16: 256 output columns per weight tile)
+    p.gather_r = nullptr;
     p.K_r = c.inter;
     p.K_s = c.inter_shared;
     p.Nout_r = c.hidden;

@@ -32,6 +32,9 @@ struct GemmParamsV2 {
     void* E_r;
     void* E_s;
     int c_stride2;         // output rows are 2 Nout wide (down-projection dgrad: da, db)
+    // bf16 gate/up only, optional: routed row r of the token rows is row
+    // gather_r[r] of A_r (the layer input x, src_token), not row r
+    const int32_t* gather_r;
 };
 
 struct WorkV2 {
@@ -42,6 +45,7 @@ struct WorkV2 {
     const char* W;   // weights of the group
     char* C;         // output rows of the group
     char* E;         // side array rows of the group (backward launches)
+    const int32_t* gather;  // the group's source-row indices into X (nullptr: X rows in order)
 };
 
 // Units: routed (tile, wt) tile-major -- the weight tiles of one expert run
@@ -91,7 +95,8 @@ __device__ __forceinline__ bool decode_v2(const GemmParamsV2& p, int mode, WorkV
         w.M = p.offsets[g + 1] - rowbase;
         w.K = p.K_r;
         w.Nout = p.Nout_r;
-        w.X = (const char*)p.A_r + rowbase * w.K * ESZ;
+        w.gather = p.gather_r ? p.gather_r + rowbase : nullptr;
+        w.X = (const char*)p.A_r + (p.gather_r ? 0 : rowbase * w.K * ESZ);
         // weights of one expert: ntn_r packed tiles of G_WR_PACK rows (bf16,
         // FP8 codes) or the plain [rows][K] matrix (fp32)
         const int64_t wrows = ESZ != 4 ? (int64_t)p.ntn_r * G_WR_PACK
@@ -103,6 +108,7 @@ __device__ __forceinline__ bool decode_v2(const GemmParamsV2& p, int mode, WorkV
         w.M = p.T;
         w.K = p.K_s;
         w.Nout = p.Nout_s;
+        w.gather = nullptr;
         w.X = (const char*)p.A_s;
         w.W = (const char*)p.B_s;
         w.C = (char*)p.C_s;

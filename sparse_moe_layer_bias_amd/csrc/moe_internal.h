@@ -43,6 +43,9 @@ struct FfnArgs {
     const void* ws2;
     const float* ws2_scale;
     void* y_shared;
+    // optional (bf16 inference forward): routed row r is x_perm[gather[r]] --
+    // x_perm is then the layer input x and gather the permutation's src_token
+    const int32_t* gather = nullptr;
 };
 size_t ffn_workspace_bytes(const moe_cfg& c);
 // FP8 expert GEMM: contraction blocks of 128 per tile whose weight scales it

@@ -14,7 +14,9 @@
 //   3. offsets: exclusive prefix of the per-expert totals
 //   4. scatter: dst_row, src_token, and the row copy x[t] -> x_perm[row] for
 //               each of the token's k rows (FP8: quantise the row's 1x128 tiles
-//               first, then copy codes and scales).
+//               first, then copy codes and scales).  Without x_perm (bf16 / fp32
+//               layers whose expert GEMM gathers the rows itself through
+//               src_token) only the two index arrays are written.
 #include <mutex>
 
 #include "moe_internal.h"
@@ -144,6 +146,20 @@ __global__ void __launch_bounds__(128) perm_scatter_kernel(
     }
 }
 
+// 4c. indices only (no row copy): one thread per (token, slot) pair
+__global__ void __launch_bounds__(256) perm_index_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ local_rank,
+    const int32_t* __restrict__ blk, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ src_token, int32_t* __restrict__ dst_row, int64_t T, int k, int N) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= T * k) return;
+    const int64_t t = i / k;
+    const int e = idx[i];
+    const int32_t row = offsets[e] + blk[(t / PERM_TB) * N + e] + local_rank[i];
+    dst_row[i] = row;
+    src_token[row] = (int32_t)t;
+}
+
 // 4b. FP8: one 128-thread block per token; 16 lanes per 1x128 tile, 8 values
 // per lane.  scale = amax/448 (fp32 divide); codes are nearest-even E4M3 of
 // clamp(v/scale, +-448); all-zero tile -> scale 0, codes 0.
@@ -256,7 +272,10 @@ hipError_t launch_permute(const moe_cfg& c, const void* x, const int32_t* idx,
     perm_bscan_kernel<<<dim3((unsigned)N), 256, 0, st>>>(w.blk, w.totals, nblk, (int)N);
     perm_offsets_kernel<<<1, 256, 0, st>>>(w.totals, offsets, (int)N);
     if (T > 0) {
-        if (c.gemm_dtype == MOE_FP8_E4M3) {
+        if (x_perm == nullptr) {
+            perm_index_kernel<<<dim3((unsigned)cdiv(T * k, 256)), 256, 0, st>>>(
+                idx, w.local_rank, w.blk, offsets, src_token, dst_row, T, k, (int)N);
+        } else if (c.gemm_dtype == MOE_FP8_E4M3) {
             const int64_t vecs = c.hidden / 8;
             const int threads = (int)(vecs >= 1024 ? 1024 : (vecs + 63) / 64 * 64);
             perm_scatter_fp8_kernel<<<dim3((unsigned)T), threads, 0, st>>>(

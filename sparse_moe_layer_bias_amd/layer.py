@@ -16,6 +16,7 @@ import torch
 
 from . import (MoeCfg, cfg_from_dict, moe_bias_update, moe_combine, moe_combine_backward,
                moe_expert_ffn, moe_expert_ffn_backward, moe_expert_ffn_backward_fp8,
+               moe_expert_ffn_gather,
                moe_expert_ffn_backward_fp8_workspace_size, moe_expert_ffn_backward_workspace_size,
                moe_expert_ffn_train_fp8, moe_expert_ffn_h_offsets, moe_expert_ffn_inspect,
                moe_expert_ffn_saved_size, moe_expert_ffn_train,
@@ -48,10 +49,14 @@ def quantize_weights_fp8(w, stream=None):
 
 class MoeLayer:
     """Holds the expert weights (and their FP8 form when the config asks for it)
-    and every per-step buffer for a batch of T tokens."""
+    and every per-step buffer for a batch of T tokens.
+
+    gather_rows (bf16 inference layers; default on for them): the permutation
+    writes only its indices and the expert GEMM reads the token rows of x
+    through src_token (moe_expert_ffn_gather), so x_perm is not kept."""
 
     def __init__(self, cfg, w13, w2, ws13=None, ws2=None, T=None, device="cuda",
-                 train=False, save_activations=True):
+                 train=False, save_activations=True, gather_rows=None):
         self.c = dict(cfg)
         if T is not None:
             self.c["T"] = T
@@ -101,11 +106,17 @@ class MoeLayer:
         self.offsets = torch.empty((N + 1,), **i32)
         self.src_token = torch.empty((TK,), **i32)
         self.dst_row = torch.empty((T, k), **i32)
+        can_gather = not self.fp8 and c["dtype"] == "bf16" and not train
+        self.gather_rows = can_gather if gather_rows is None else bool(gather_rows)
+        if self.gather_rows and not can_gather:
+            raise ValueError("gather_rows needs a bf16 inference layer")
         if self.fp8:
             self.x_perm = torch.empty((TK, d), dtype=torch.uint8, device=dev)
             self.x_perm_s = torch.empty((TK, d // 128), **f32)
             self.x_q = torch.empty((T, d), dtype=torch.uint8, device=dev)
             self.x_s = torch.empty((T, d // 128), **f32)
+        elif self.gather_rows:
+            self.x_perm = self.x_perm_s = self.x_q = self.x_s = None
         else:
             self.x_perm = torch.empty((TK, d), dtype=act, device=dev)
             self.x_perm_s = self.x_q = self.x_s = None
@@ -160,6 +171,12 @@ class MoeLayer:
             moe_expert_ffn_train(self.cfg, self.x_perm, self.offsets, self.w13, self.w2,
                                  self.y_perm, x if shared else None, self.ws13, self.ws2,
                                  self.y_shared, self.saved, self.workspace, stream)
+            return
+        if self.gather_rows:
+            shared = self.y_shared is not None
+            moe_expert_ffn_gather(self.cfg, x, self.src_token, self.offsets, self.w13, self.w2,
+                                  self.y_perm, x if shared else None, self.ws13, self.ws2,
+                                  self.y_shared, self.workspace, stream)
             return
         shared_in = self.x_q if self.fp8 else x
         moe_expert_ffn(self.cfg, self.x_perm, self.x_perm_s, self.offsets, self.w13, self.w13_s,

@@ -34,13 +34,13 @@ def _gpu():
 _last_x = [None]
 
 
-def _run_small(cfg_name, orc, T=None, residual=True, seed=0, **over):
+def _run_small(cfg_name, orc, T=None, residual=True, seed=0, gather_rows=None, **over):
     cfg = dict(moe_inputs.CONFIGS[cfg_name])
     cfg.update(over)
     c, inp, dev = small_layer_inputs(cfg, seed, T)
     _last_x[0] = inp["x"]
-    log("case", cfg_name, "T=%d" % c["T"], over, "seed", seed)
-    layer = MoeLayer(c, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"])
+    log("case", cfg_name, "T=%d" % c["T"], over, "seed", seed, "gather_rows", gather_rows)
+    layer = MoeLayer(c, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"], gather_rows=gather_rows)
     guards = guard_layer(layer)
     bias = guards.like(dev["bias"], "bias", copy=True)
     out = layer.forward(dev["x"], dev["centroids"], bias, residual=residual)
@@ -84,11 +84,21 @@ def test_layer_parity_small(orc, name, over):
     assert_bits(moe_inputs.to_host(layer.offsets), ref["offsets"], "offsets")
     assert_bits(moe_inputs.to_host(layer.src_token), ref["src_token"], "src_token")
     assert_bits(moe_inputs.to_host(layer.dst_row), ref["dst_row"], "dst_row")
-    assert_bits(moe_inputs.to_host(layer.x_perm), ref["x_perm"], "x_perm")
     assert_close(moe_inputs.to_host(layer.y_perm), ref["y_perm"], rtol, "y_perm")
     assert_close(moe_inputs.to_host(layer.y_shared), ref["y_shared"], rtol, "y_shared")
     assert_close(moe_inputs.to_host(out), ref["out"], rtol, "out")
     assert_bits(moe_inputs.to_host(bias), ref["new_bias"], "bias after update")
+    if layer.gather_rows:
+        # bf16 layers read the token rows through src_token by default: the
+        # same layer with the permuted copy must give x_perm bit for bit and
+        # the very same expert outputs and layer output
+        c2, layer2, out2, _, _ = _run_small(name, orc, T=T, gather_rows=False, **over)
+        assert_bits(moe_inputs.to_host(layer2.x_perm), ref["x_perm"], "x_perm")
+        for n, a, b in (("y_perm", layer.y_perm, layer2.y_perm),
+                        ("y_shared", layer.y_shared, layer2.y_shared), ("out", out, out2)):
+            assert_bits(moe_inputs.to_host(a), moe_inputs.to_host(b), n + ": gathered == permuted")
+    else:
+        assert_bits(moe_inputs.to_host(layer.x_perm), ref["x_perm"], "x_perm")
 
 
 FP8_CASES = [
@@ -521,6 +531,34 @@ def test_v3_fp8_layer_parity(orc, v3_fp8_run):
     assert_bits(moe_inputs.to_host(bias).view(np.uint32), new_b.view(np.uint32), "bias update")
 
 
+def _full_permute(cfg, x, layer):
+    """moe_permute with the permuted copy, on the layer's routing"""
+    T, k, d, N = cfg["T"], cfg["k"], cfg["d"], cfg["N"]
+    i32 = dict(dtype=torch.int32, device="cuda")
+    offs = torch.empty((N + 1,), **i32)
+    src = torch.empty((T * k,), **i32)
+    dst = torch.empty((T, k), **i32)
+    x_perm = torch.empty((T * k, d), dtype=torch.bfloat16, device="cuda")
+    moe.moe_permute(layer.cfg, x, layer.idx, offs, src, dst, x_perm, None, None, None,
+                    layer.workspace)
+    return offs, src, dst, x_perm
+
+
+def test_v3_gathered_rows_equal_permuted_rows(orc, v3_run):
+    """At the V3 shape the expert FFN on the gathered rows (the layer's path)
+    equals moe_expert_ffn on the permuted copy, bit for bit."""
+    cfg, dev, layer, bias0, bias = v3_run
+    assert layer.gather_rows
+    offs, src, dst, x_perm = _full_permute(cfg, dev["x"], layer)
+    y = torch.empty_like(layer.y_perm)
+    ys = torch.empty_like(layer.y_shared)
+    moe.moe_expert_ffn(layer.cfg, x_perm, None, offs, layer.w13, None, layer.w2, None, y,
+                       dev["x"], None, layer.ws13, None, layer.ws2, None, ys, layer.workspace)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), layer.y_perm.view(torch.int16)), "y_perm"
+    assert torch.equal(ys.view(torch.int16), layer.y_shared.view(torch.int16)), "y_shared"
+
+
 def test_v3_routing_all_tokens(orc, v3_run):
     cfg, dev, layer, bias0, bias = v3_run
     _check_v3_routing(orc, cfg, dev, layer, bias0, with_scores=True)
@@ -538,8 +576,14 @@ def test_v3_permutation_properties(orc, v3_run):
     gs = N // cfg["G"]
     assert max(len(set(row // gs)) for row in idx) <= cfg["TG"]
     src = moe_inputs.to_host(layer.src_token)
+    # the layer's permutation wrote indices only (its GEMM gathers the rows):
+    # the full permutation gives the same indices and the rows they name
+    offs, srcf, dstf, x_perm = _full_permute(cfg, dev["x"], layer)
+    assert_bits(moe_inputs.to_host(offs), moe_inputs.to_host(layer.offsets), "offsets")
+    assert_bits(moe_inputs.to_host(srcf), src, "src_token")
+    assert_bits(moe_inputs.to_host(dstf), moe_inputs.to_host(layer.dst_row), "dst_row")
     rows = np.random.default_rng(1).choice(T * k, 4000, replace=False)
-    xp = moe_inputs.to_host(layer.x_perm[torch.from_numpy(rows).cuda()])
+    xp = moe_inputs.to_host(x_perm[torch.from_numpy(rows).cuda()])
     xs = moe_inputs.to_host(dev["x"][torch.from_numpy(src[rows]).long().cuda()])
     assert_bits(xp, xs, "x_perm rows")
     new_b = orc.bias_update(counts, T * k, moe_inputs.to_host(bias0))
