@@ -114,10 +114,11 @@ size_t moe_permute_workspace_size(const moe_cfg* cfg);
  *  dst_row      [T, k]        int32      out, row of each (token, slot)
  *  x_perm       [T*k, d]      out: act_dtype rows (gemm_dtype != FP8) or
  *                             E4M3 codes (gemm_dtype == FP8).  May be NULL
- *                             for bf16 / fp32 layers: then only offsets,
- *                             src_token and dst_row are written (for
- *                             moe_expert_ffn_gather, which reads the rows of x
- *                             through src_token itself)
+ *                             (FP8: with x_perm_scale): then the rows are not
+ *                             copied, only offsets, src_token, dst_row (and
+ *                             for FP8 x_q, x_s) are written, for
+ *                             moe_expert_ffn_gather, which reads the rows
+ *                             through src_token itself
  *  x_perm_scale [T*k, d/128]  fp32 out, FP8 tile scales (FP8 only, else NULL)
  *  x_q          [T, d]        u8   out, FP8 codes of x for the shared expert (FP8 only)
  *  x_s          [T, d/128]    fp32 out, their tile scales (FP8 only)
@@ -181,20 +182,25 @@ int moe_expert_ffn(const moe_cfg* cfg, const void* x_perm, const float* x_perm_s
                    const void* ws2, const float* ws2_scale, void* y_shared, void* workspace,
                    size_t workspace_bytes, void* stream);
 
-/* moe_expert_ffn for bf16 layers (act_dtype = gemm_dtype = MOE_BF16) without
- * the permuted copy of the tokens: routed row r is x[src_token[r]], read by
+/* moe_expert_ffn without the permuted copy of the tokens, for bf16 layers and
+ * FP8 layers (act_dtype bf16): routed row r is row src_token[r] of x, read by
  * the gate/up GEMM's own copies ("Methode" item 2: each routed expert sees
  * the tokens that chose it; the dispatch is the same permutation, its rows
- * are not materialised).  Results are those of moe_expert_ffn on the x_perm
- * that moe_permute would have written, bit for bit.
- *  x          [T, d]   bf16  the layer input
- *  src_token  [T*k]    int32 from moe_permute (which may skip x_perm for this)
- *  the other arguments as moe_expert_ffn (x_sh is normally x itself; no
- *  scales).  Requires T * d * 2 < 2^32 (32-bit row offsets into x), else
- *  MOE_ERR_UNSUPPORTED; other layers: MOE_ERR_UNSUPPORTED. */
-int moe_expert_ffn_gather(const moe_cfg* cfg, const void* x, const int32_t* src_token,
-                          const int32_t* offsets, const void* w13, const void* w2, void* y_perm,
-                          const void* x_sh, const void* ws13, const void* ws2, void* y_shared,
+ * are not materialised).  The shared expert reads the same x.  Results are
+ * those of moe_expert_ffn on the x_perm (x_perm_scale) that moe_permute would
+ * have written, bit for bit.
+ *  x          [T, d]     bf16 layer input, or for FP8 layers its E4M3 codes
+ *                        x_q from moe_permute
+ *  x_scale    [T, d/128] FP8: the tile scales x_s from moe_permute; else NULL
+ *  src_token  [T*k]      int32 from moe_permute (which may skip x_perm for this)
+ *  the weights, scales and outputs as moe_expert_ffn.
+ * Requires x (T * d elements) below 2^32 bytes (32-bit row offsets), else
+ * MOE_ERR_UNSUPPORTED; fp32 layers: MOE_ERR_UNSUPPORTED. */
+int moe_expert_ffn_gather(const moe_cfg* cfg, const void* x, const float* x_scale,
+                          const int32_t* src_token, const int32_t* offsets, const void* w13,
+                          const float* w13_scale, const void* w2, const float* w2_scale,
+                          void* y_perm, const void* ws13, const float* ws13_scale,
+                          const void* ws2, const float* ws2_scale, void* y_shared,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Weight preparation, off the per-step path (weights are constant across

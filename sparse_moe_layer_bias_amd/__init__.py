@@ -70,7 +70,7 @@ def lib():
             "moe_permute": ([C, P, P, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
             "moe_expert_ffn_workspace_size": ([C], SZ),
             "moe_expert_ffn": ([C] + [P] * 15 + [P, SZ, P], ctypes.c_int),
-            "moe_expert_ffn_gather": ([C] + [P] * 10 + [P, SZ, P], ctypes.c_int),
+            "moe_expert_ffn_gather": ([C] + [P] * 14 + [P, SZ, P], ctypes.c_int),
             "moe_combine": ([C, P, P, P, P, P, P, P], ctypes.c_int),
             "moe_packed_weights_size": ([C, ctypes.c_int], SZ),
             "moe_pack_weights": ([C, ctypes.c_int, P, P, P], ctypes.c_int),
@@ -178,12 +178,14 @@ def moe_expert_ffn(cfg, x_perm, x_perm_scale, offsets, w13, w13_scale, w2, w2_sc
                                 _stream(stream)))
 
 
-def moe_expert_ffn_gather(cfg, x, src_token, offsets, w13, w2, y_perm, x_sh, ws13, ws2, y_shared,
-                          workspace=None, stream=None):
-    _check(lib().moe_expert_ffn_gather(ctypes.byref(cfg), _p(x), _p(src_token), _p(offsets),
-                                       _p(w13), _p(w2), _p(y_perm), _p(x_sh), _p(ws13), _p(ws2),
-                                       _p(y_shared), _p(workspace), _nbytes(workspace),
-                                       _stream(stream)))
+def moe_expert_ffn_gather(cfg, x, x_scale, src_token, offsets, w13, w13_scale, w2, w2_scale,
+                          y_perm, ws13, ws13_scale, ws2, ws2_scale, y_shared, workspace=None,
+                          stream=None):
+    _check(lib().moe_expert_ffn_gather(ctypes.byref(cfg), _p(x), _p(x_scale), _p(src_token),
+                                       _p(offsets), _p(w13), _p(w13_scale), _p(w2),
+                                       _p(w2_scale), _p(y_perm), _p(ws13), _p(ws13_scale),
+                                       _p(ws2), _p(ws2_scale), _p(y_shared), _p(workspace),
+                                       _nbytes(workspace), _stream(stream)))
 
 
 def moe_expert_ffn_h_offsets(cfg):

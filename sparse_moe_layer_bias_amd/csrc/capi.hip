@@ -173,8 +173,14 @@ int moe_permute(const moe_cfg* cfg, const void* x, const int32_t* idx, int32_t* 
         if (cfg->gemm_dtype == MOE_FP8_E4M3) {
             if (cfg->hidden % 128)
                 return fail(MOE_ERR_UNSUPPORTED, "%s: FP8 needs hidden %% 128 == 0", fn);
-            REQ_PTR(x_perm);  // x_perm may be NULL only for bf16 / fp32 layers
-            REQ_PTR(x_perm_scale);
+            // x_perm, x_perm_scale: both or neither (without them the expert
+            // GEMM gathers the rows from x_q, x_s through src_token)
+            if ((x_perm == nullptr) != (x_perm_scale == nullptr))
+                return fail(MOE_ERR_ARG, "%s: x_perm and x_perm_scale: both or neither", fn);
+            if (x_perm) {
+                REQ_PTR(x_perm);
+                REQ_PTR(x_perm_scale);
+            }
             REQ_PTR(x_q);
             REQ_PTR(x_s);
         }
@@ -203,8 +209,14 @@ int moe_permute_noalloc(const moe_cfg* cfg, const void* x, const int32_t* idx, i
         if (cfg->gemm_dtype == MOE_FP8_E4M3) {
             if (cfg->hidden % 128)
                 return fail(MOE_ERR_UNSUPPORTED, "%s: FP8 needs hidden %% 128 == 0", fn);
-            REQ_PTR(x_perm);  // x_perm may be NULL only for bf16 / fp32 layers
-            REQ_PTR(x_perm_scale);
+            // x_perm, x_perm_scale: both or neither (without them the expert
+            // GEMM gathers the rows from x_q, x_s through src_token)
+            if ((x_perm == nullptr) != (x_perm_scale == nullptr))
+                return fail(MOE_ERR_ARG, "%s: x_perm and x_perm_scale: both or neither", fn);
+            if (x_perm) {
+                REQ_PTR(x_perm);
+                REQ_PTR(x_perm_scale);
+            }
             REQ_PTR(x_q);
             REQ_PTR(x_s);
         }
@@ -277,21 +289,30 @@ static int expert_ffn_impl(const char* fn, const moe_cfg* cfg, const void* x_per
                                                  h_f32, h_f32_shared));
 }
 
-int moe_expert_ffn_gather(const moe_cfg* cfg, const void* x, const int32_t* src_token,
-                          const int32_t* offsets, const void* w13, const void* w2, void* y_perm,
-                          const void* x_sh, const void* ws13, const void* ws2, void* y_shared,
+int moe_expert_ffn_gather(const moe_cfg* cfg, const void* x, const float* x_scale,
+                          const int32_t* src_token, const int32_t* offsets, const void* w13,
+                          const float* w13_scale, const void* w2, const float* w2_scale,
+                          void* y_perm, const void* ws13, const float* ws13_scale,
+                          const void* ws2, const float* ws2_scale, void* y_shared,
                           void* workspace, size_t workspace_bytes, void* stream) {
     const char* fn = "moe_expert_ffn_gather";
     if (int r = check_cfg(fn, cfg)) return r;
-    if (cfg->act_dtype != MOE_BF16 || cfg->gemm_dtype != MOE_BF16)
-        return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 layers only (use moe_expert_ffn)", fn);
+    const bool fp8 = cfg->gemm_dtype == MOE_FP8_E4M3;
+    if (cfg->act_dtype != MOE_BF16)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 and FP8 layers only (use moe_expert_ffn)", fn);
     // the token copies address a row of x by a 32-bit byte offset
-    if (cfg->tokens * cfg->hidden * 2 >= ((int64_t)1 << 32))
-        return fail(MOE_ERR_UNSUPPORTED, "%s: tokens * hidden * 2 must stay below 2^32", fn);
-    if (cfg->tokens > 0) REQ_PTR(src_token);
-    return expert_ffn_impl(fn, cfg, x, nullptr, offsets, w13, nullptr, w2, nullptr, y_perm, x_sh,
-                           nullptr, ws13, nullptr, ws2, nullptr, y_shared, nullptr, workspace,
-                           workspace_bytes, stream, nullptr, nullptr, src_token);
+    if (cfg->tokens * cfg->hidden * (fp8 ? 1 : 2) >= ((int64_t)1 << 32))
+        return fail(MOE_ERR_UNSUPPORTED, "%s: x must stay below 2^32 bytes", fn);
+    if (cfg->tokens > 0) {
+        REQ_PTR(src_token);
+        if (fp8) REQ_PTR(x_scale);
+    }
+    // the shared expert reads the same rows (x, or its codes and scales)
+    return expert_ffn_impl(fn, cfg, x, x_scale, offsets, w13, w13_scale, w2, w2_scale, y_perm,
+                           cfg->inter_shared > 0 ? x : nullptr,
+                           cfg->inter_shared > 0 ? x_scale : nullptr, ws13, ws13_scale, ws2,
+                           ws2_scale, y_shared, nullptr, workspace, workspace_bytes, stream,
+                           nullptr, nullptr, src_token);
 }
 
 extern "C" {

@@ -62,6 +62,7 @@ struct Fp8Params {
     void* hb_s;
     float* hf_r;           // modes 0 and 4, optional: h in fp32 before quantisation
     float* hf_s;
+    int64_t x_rows;        // rows of the gathered-from codes (g.gather_r set: T)
 };
 
 // Pack FP8 weight codes [n_mats][rows][K] into the kernel's LDS image order:
@@ -128,7 +129,10 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
     const int64_t mc = w.M - w.m0 < F8_TR ? w.M - w.m0 : F8_TR;
     const bool shared = w.g >= P.g.N;
     const int64_t gi = shared ? 0 : w.g;
-    const float* xs = (shared ? P.xs_s : P.xs_r) + (w.rowbase + w.m0) * nkb;
+    // with a gather list (inference forward) the routed rows are rows of the
+    // shared expert's x codes and scales, found through src_token
+    const int32_t* gat = w.gather;
+    const float* xs = gat ? P.xs_r : (shared ? P.xs_s : P.xs_r) + (w.rowbase + w.m0) * nkb;
     const float* wsc = shared ? P.ws_s : P.ws_r;
     constexpr bool GU = MODE != 1;  // gate/up-shaped tile (modes 0 and 2)
     const int64_t wrows = GU ? 2 * w.Nout : w.Nout;
@@ -138,10 +142,10 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
     // out-of-range lanes read as zero): the tile's weight panel, the expert's
     // token rows and their scales.
     const char* wpanel = w.W + w.wt * (int64_t)nk * F8_A;
-    const char* xbase = w.X + w.m0 * K;
+    const char* xbase = gat ? w.X : w.X + w.m0 * K;
     const i32x4_t rw = make_rsrc(wpanel, (int64_t)nk * F8_A);
-    const i32x4_t rx = make_rsrc(xbase, mc * K);
-    const i32x4_t rs = make_rsrc(xs, mc * nkb * 4);
+    const i32x4_t rx = make_rsrc(xbase, gat ? P.x_rows * K : mc * K);
+    const i32x4_t rs = make_rsrc(xs, (gat ? P.x_rows : mc) * nkb * 4);
 
     // token code copies: block b = 8 rows (128-byte lines); the blocks holding
     // real rows are the prefix b < nxe; rows past the last one repeat it
@@ -152,10 +156,12 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
         const int b = wave + F8_WAVES * j;
         const int r = b * 8 + (lane >> 3), c = sub_chunk8(r, lane & 7);
         const int64_t tr = r < mc ? r : mc - 1;
-        xoff[j] = (uint32_t)(tr * K + c * 16);
+        const int64_t sr = gat ? (int64_t)gat[w.m0 + tr] : tr;
+        xoff[j] = (uint32_t)(sr * K + c * 16);
     }
     // token scale copies (dwords): wave s < NSC copies rows s*64 .. +63
-    const int64_t srow = wave * 64 + lane < mc ? wave * 64 + lane : mc - 1;
+    const int64_t srow0 = wave * 64 + lane < mc ? wave * 64 + lane : mc - 1;
+    const int64_t srow = gat ? (int64_t)gat[w.m0 + srow0] : srow0;
     const uint32_t soff = (uint32_t)(srow * nkb * 4);
 
     auto stage = [&](int s) { return smem + s * F8_STAGE; };
@@ -539,6 +545,8 @@ hipError_t launch_expert_ffn_fp8(const moe_cfg& c, const FfnArgs& a, const int2*
     P.g.C_s = h_s;
     P.xs_r = a.x_perm_scale;
     P.xs_s = a.x_sh_scale;
+    P.g.gather_r = a.gather;  // inference forward, optional: routed rows = x_q[src_token]
+    P.x_rows = T;
     P.ws_r = a.w13_scale;
     P.ws_s = a.ws13_scale;
     P.hs_r = hs_r;
@@ -560,6 +568,7 @@ hipError_t launch_expert_ffn_fp8(const moe_cfg& c, const FfnArgs& a, const int2*
     }
 
     // down: h codes x W2 codes -> y (bf16)
+    P.g.gather_r = nullptr;
     P.g.K_r = c.inter;
     P.g.K_s = c.inter_shared;
     P.g.Nout_r = c.hidden;

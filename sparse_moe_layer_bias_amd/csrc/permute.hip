@@ -14,9 +14,9 @@
 //   3. offsets: exclusive prefix of the per-expert totals
 //   4. scatter: dst_row, src_token, and the row copy x[t] -> x_perm[row] for
 //               each of the token's k rows (FP8: quantise the row's 1x128 tiles
-//               first, then copy codes and scales).  Without x_perm (bf16 / fp32
-//               layers whose expert GEMM gathers the rows itself through
-//               src_token) only the two index arrays are written.
+//               into x_q, x_s first, then copy codes and scales).  Without
+//               x_perm (the expert GEMM gathers the rows itself through
+//               src_token) only the indices (and for FP8 x_q, x_s) are written.
 #include <mutex>
 
 #include "moe_internal.h"
@@ -211,12 +211,15 @@ __global__ void __launch_bounds__(1024) perm_scatter_fp8_kernel(
         if (valid) {
             const uint2 q = make_uint2(lo, hi);
             x_q[t * vecs + v] = q;
-            for (int j = 0; j < k; ++j)  // written once, read by the GEMMs later
-                __builtin_nontemporal_store(u32x2_t{lo, hi}, (u32x2_t*)(x_perm + (int64_t)rows[j] * vecs + v));
+            if (x_perm != nullptr)  // (without it the GEMM gathers from x_q)
+                for (int j = 0; j < k; ++j)  // written once, read by the GEMMs later
+                    __builtin_nontemporal_store(u32x2_t{lo, hi},
+                                                (u32x2_t*)(x_perm + (int64_t)rows[j] * vecs + v));
             if ((threadIdx.x & 15) == 0) {
                 const int64_t tile = v / 16;
                 x_s[t * tiles + tile] = scale;
-                for (int j = 0; j < k; ++j) x_perm_scale[(int64_t)rows[j] * tiles + tile] = scale;
+                if (x_perm != nullptr)
+                    for (int j = 0; j < k; ++j) x_perm_scale[(int64_t)rows[j] * tiles + tile] = scale;
             }
         }
     }
@@ -272,7 +275,7 @@ hipError_t launch_permute(const moe_cfg& c, const void* x, const int32_t* idx,
     perm_bscan_kernel<<<dim3((unsigned)N), 256, 0, st>>>(w.blk, w.totals, nblk, (int)N);
     perm_offsets_kernel<<<1, 256, 0, st>>>(w.totals, offsets, (int)N);
     if (T > 0) {
-        if (x_perm == nullptr) {
+        if (x_perm == nullptr && c.gemm_dtype != MOE_FP8_E4M3) {
             perm_index_kernel<<<dim3((unsigned)cdiv(T * k, 256)), 256, 0, st>>>(
                 idx, w.local_rank, w.blk, offsets, src_token, dst_row, T, k, (int)N);
         } else if (c.gemm_dtype == MOE_FP8_E4M3) {

@@ -51,9 +51,10 @@ class MoeLayer:
     """Holds the expert weights (and their FP8 form when the config asks for it)
     and every per-step buffer for a batch of T tokens.
 
-    gather_rows (bf16 inference layers; default on for them): the permutation
-    writes only its indices and the expert GEMM reads the token rows of x
-    through src_token (moe_expert_ffn_gather), so x_perm is not kept."""
+    gather_rows (inference layers with bf16 activations, bf16 or FP8 GEMMs;
+    default on for them): the permutation writes only its indices (FP8: and
+    the codes of x) and the expert GEMM reads the token rows through
+    src_token (moe_expert_ffn_gather), so x_perm is not kept."""
 
     def __init__(self, cfg, w13, w2, ws13=None, ws2=None, T=None, device="cuda",
                  train=False, save_activations=True, gather_rows=None):
@@ -106,13 +107,16 @@ class MoeLayer:
         self.offsets = torch.empty((N + 1,), **i32)
         self.src_token = torch.empty((TK,), **i32)
         self.dst_row = torch.empty((T, k), **i32)
-        can_gather = not self.fp8 and c["dtype"] == "bf16" and not train
+        can_gather = c["dtype"] == "bf16" and not train
         self.gather_rows = can_gather if gather_rows is None else bool(gather_rows)
         if self.gather_rows and not can_gather:
-            raise ValueError("gather_rows needs a bf16 inference layer")
+            raise ValueError("gather_rows needs an inference layer with bf16 activations")
         if self.fp8:
-            self.x_perm = torch.empty((TK, d), dtype=torch.uint8, device=dev)
-            self.x_perm_s = torch.empty((TK, d // 128), **f32)
+            if self.gather_rows:
+                self.x_perm = self.x_perm_s = None
+            else:
+                self.x_perm = torch.empty((TK, d), dtype=torch.uint8, device=dev)
+                self.x_perm_s = torch.empty((TK, d // 128), **f32)
             self.x_q = torch.empty((T, d), dtype=torch.uint8, device=dev)
             self.x_s = torch.empty((T, d // 128), **f32)
         elif self.gather_rows:
@@ -173,10 +177,11 @@ class MoeLayer:
                                  self.y_shared, self.saved, self.workspace, stream)
             return
         if self.gather_rows:
-            shared = self.y_shared is not None
-            moe_expert_ffn_gather(self.cfg, x, self.src_token, self.offsets, self.w13, self.w2,
-                                  self.y_perm, x if shared else None, self.ws13, self.ws2,
-                                  self.y_shared, self.workspace, stream)
+            src = (self.x_q, self.x_s) if self.fp8 else (x, None)
+            moe_expert_ffn_gather(self.cfg, src[0], src[1], self.src_token, self.offsets,
+                                  self.w13, self.w13_s, self.w2, self.w2_s, self.y_perm,
+                                  self.ws13, self.ws13_s, self.ws2, self.ws2_s, self.y_shared,
+                                  self.workspace, stream)
             return
         shared_in = self.x_q if self.fp8 else x
         moe_expert_ffn(self.cfg, self.x_perm, self.x_perm_s, self.offsets, self.w13, self.w13_s,

@@ -275,21 +275,24 @@ def test_fp8_backward_validation():
 
 @host_only
 def test_gathered_rows_validation():
-    """moe_expert_ffn_gather: bf16 layers only, 32-bit row offsets into x, a
-    src_token; moe_permute may skip x_perm for bf16 / fp32 layers only."""
+    """moe_expert_ffn_gather: bf16 activations only, 32-bit row offsets into x,
+    a src_token, FP8 tile scales; moe_permute takes x_perm and x_perm_scale
+    both or neither for FP8 layers."""
     L = moe.lib()
     P = ctypes.c_void_p
     c = _cfg(dtype="bf16", d=256, I=128, Is=128)
     ws = moe.moe_expert_ffn_workspace_size(c)
-    call = lambda cfg, src=FAKE: L.moe_expert_ffn_gather(
-        ctypes.byref(cfg), P(FAKE), P(src), *([P(FAKE)] * 8), P(FAKE), ws, None)
+    call = lambda cfg, src=FAKE, xs=FAKE: L.moe_expert_ffn_gather(
+        ctypes.byref(cfg), P(FAKE), P(xs), P(src), *([P(FAKE)] * 11), P(FAKE), ws, None)
     assert call(_cfg(dtype="f32", d=256, I=128, Is=128)) == moe.MOE_ERR_UNSUPPORTED
-    assert call(_cfg(dtype="bf16", fp8=True, d=256, I=128, Is=128)) == moe.MOE_ERR_UNSUPPORTED
     assert call(c, src=0) == moe.MOE_ERR_ARG
+    assert call(_cfg(dtype="bf16", fp8=True, d=256, I=128, Is=128), xs=0) == moe.MOE_ERR_ARG
     big = _cfg(dtype="bf16", d=65536, I=128, Is=128, T=32768)  # T*d*2 = 2^32
     assert call(big) == moe.MOE_ERR_UNSUPPORTED
-    pws = moe.moe_permute_workspace_size(c)
-    perm = lambda cfg, x_perm: L.moe_permute(
-        ctypes.byref(cfg), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), x_perm, P(FAKE), P(FAKE),
-        P(FAKE), P(FAKE), pws * 4, None)
-    assert perm(_cfg(dtype="bf16", fp8=True, d=256, I=128, Is=128), None) == moe.MOE_ERR_ARG
+    f8 = _cfg(dtype="bf16", fp8=True, d=256, I=128, Is=128)
+    pws = moe.moe_permute_workspace_size(f8)
+    perm = lambda x_perm, x_perm_s: L.moe_permute(
+        ctypes.byref(f8), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), x_perm, x_perm_s,
+        P(FAKE), P(FAKE), P(FAKE), pws * 4, None)
+    assert perm(None, P(FAKE)) == moe.MOE_ERR_ARG
+    assert perm(P(FAKE), None) == moe.MOE_ERR_ARG

@@ -34,11 +34,33 @@ def _gpu():
 _last_x = [None]
 
 
+def _check_gathered_rows(layer):
+    """moe_expert_ffn_gather (token rows read through src_token) on the state
+    of a layer that ran with the permuted copy: y_perm and y_shared bit for
+    bit equal to the layer's"""
+    import sparse_moe_layer_bias_amd as m
+    y = torch.empty_like(layer.y_perm)
+    ys = torch.empty_like(layer.y_shared) if layer.y_shared is not None else None
+    x = layer.x_q if layer.fp8 else _last_dev_x[0]
+    m.moe_expert_ffn_gather(layer.cfg, x, layer.x_s if layer.fp8 else None, layer.src_token,
+                            layer.offsets, layer.w13, layer.w13_s, layer.w2, layer.w2_s, y,
+                            layer.ws13, layer.ws13_s, layer.ws2, layer.ws2_s, ys, layer.workspace)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.uint8), layer.y_perm.view(torch.uint8)), "y_perm (gathered)"
+    if ys is not None:
+        assert torch.equal(ys.view(torch.uint8), layer.y_shared.view(torch.uint8)), \
+            "y_shared (gathered)"
+
+
+_last_dev_x = [None]
+
+
 def _run_small(cfg_name, orc, T=None, residual=True, seed=0, gather_rows=None, **over):
     cfg = dict(moe_inputs.CONFIGS[cfg_name])
     cfg.update(over)
     c, inp, dev = small_layer_inputs(cfg, seed, T)
     _last_x[0] = inp["x"]
+    _last_dev_x[0] = dev["x"]
     log("case", cfg_name, "T=%d" % c["T"], over, "seed", seed, "gather_rows", gather_rows)
     layer = MoeLayer(c, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"], gather_rows=gather_rows)
     guards = guard_layer(layer)
@@ -120,7 +142,8 @@ def test_layer_parity_fp8_small(orc, name, over):
     fp32 promotion per 128-K block) against the oracle's FP8 path."""
     over = dict(over)
     T = over.pop("T", None)
-    c, layer, out, bias, ref = _run_small(name, orc, T=T, fp8=True, **over)
+    c, layer, out, bias, ref = _run_small(name, orc, T=T, fp8=True, gather_rows=False, **over)
+    _check_gathered_rows(layer)
     assert_bits(moe_inputs.to_host(layer.idx), ref["idx"], "idx")
     assert_bits(moe_inputs.to_host(layer.gate), ref["gate"], "gate")
     assert_bits(moe_inputs.to_host(layer.x_q), ref["x_q"], "x codes")
@@ -163,7 +186,7 @@ def test_fp8_block_scales_far_apart(orc):
                ws13=ws13.to(torch.bfloat16), ws2=ws2.to(torch.bfloat16))
     dev = {k: v.cuda() for k, v in inp.items()}
     log("case fp8 far-apart block scales T=%d" % c["T"])
-    layer = MoeLayer(c, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"])
+    layer = MoeLayer(c, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"], gather_rows=False)
     out = layer.forward(dev["x"], dev["centroids"], dev["bias"].clone())
     torch.cuda.synchronize()
     ref = orc.layer_forward(host_inputs(inp), c, residual=True)
@@ -249,7 +272,7 @@ def test_fp8_activation_codes_bit_exact(orc):
     x[3, 128:256] = 0          # an all-zero tile
     x[5, :] *= 1000
     x[6, :] *= 1e-3
-    layer = MoeLayer(c, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"])
+    layer = MoeLayer(c, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"], gather_rows=False)
     layer.route(x, dev["centroids"], dev["bias"])
     layer.permute(x)
     torch.cuda.synchronize()
@@ -457,7 +480,7 @@ def v3_fp8_run():
     cfg = dict(moe_inputs.CONFIGS["v3_fp8"])
     log("generating V3-shaped inputs on the GPU (FP8 layer)")
     dev = moe_inputs.make_layer_inputs(cfg, 0, "cuda")
-    layer = MoeLayer(cfg, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"])
+    layer = MoeLayer(cfg, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"], gather_rows=False)
     bias0 = dev["bias"].clone()
     bias = dev["bias"].clone()
     layer.forward(dev["x"], dev["centroids"], bias)
@@ -557,6 +580,14 @@ def test_v3_gathered_rows_equal_permuted_rows(orc, v3_run):
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), layer.y_perm.view(torch.int16)), "y_perm"
     assert torch.equal(ys.view(torch.int16), layer.y_shared.view(torch.int16)), "y_shared"
+
+
+def test_v3_fp8_gathered_rows_equal_permuted_rows(orc, v3_fp8_run):
+    """The V3-shaped FP8 expert FFN on rows gathered from x_q, x_s through
+    src_token (the inference layer's path) equals the one on the permuted
+    codes, bit for bit."""
+    cfg, dev, layer, bias0, bias = v3_fp8_run
+    _check_gathered_rows(layer)
 
 
 def test_v3_routing_all_tokens(orc, v3_run):
