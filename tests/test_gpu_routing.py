@@ -55,11 +55,13 @@ ROUTE_CASES = [
     (1024, 7168, 256, 8, 8, 4, "bf16"),   # tiled, 1 token per thread
     (2048, 7168, 256, 8, 8, 4, "bf16"),   # tiled, 2 tokens per thread
     (8192, 7176, 256, 8, 8, 4, "bf16"),   # tiled, 4 tokens per thread, d % 32 != 0
+    (6200, 512, 250, 8, 1, 1, "bf16"),    # tiled, 4 tokens per thread, ragged tokens and experts
     (2048, 1000, 256, 8, 1, 1, "bf16"),   # tiled, 2 tokens per thread, d % 32 != 0
     (1024, 1000, 256, 6, 1, 1, "bf16"),   # tiled, 1 token per thread, d % 32 != 0
     (4096, 1000, 64, 8, 1, 1, "f32"),     # fp32 x: tiled, 1 token per thread, d % 32 != 0
     (8192, 512, 64, 8, 1, 1, "f32"),      # fp32 x: tiled, 2 tokens per thread
     (32768, 256, 64, 4, 1, 1, "f32"),     # fp32 x: tiled, 4 tokens per thread
+    (24576, 1000, 64, 8, 1, 1, "f32"),    # fp32 x: tiled, 4 tokens per thread, d % 32 != 0
     (128, 1000, 256, 8, 1, 1, "bf16"),    # one chain per lane, d % 256 != 0
     (100, 7168, 256, 8, 8, 4, "bf16"),    # one chain per lane, ragged tokens
 ]
