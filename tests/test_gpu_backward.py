@@ -76,6 +76,11 @@ BWD_CASES = [
     ("mid_bf16", dict(T=700, d=384, N=2, k=1, I=256, Is=128)),  # several 128-row tiles per expert
     ("mid_bf16", dict(T=130, N=1, k=1)),                 # one expert: gate 1, dz = 0
     ("mid_bf16", dict(T=50, N=16, k=16)),                # k = N
+    # one expert with exactly T rows: the weight gradients' 32-row stages and
+    # the data gradients' 320-row tiles, at and just past an edge
+    ("mid_bf16", dict(T=32, N=1, k=1, d=256, I=256, Is=128)),
+    ("mid_bf16", dict(T=33, N=1, k=1, d=256, I=256, Is=128)),
+    ("mid_bf16", dict(T=321, N=1, k=1, d=256, I=256, Is=128)),
 ]
 
 

@@ -110,6 +110,11 @@ FP8_CASES = [
     dict(T=700, d=384, N=2, k=1, I=256, Is=128),         # several 128-row blocks and row tiles
     dict(T=64, d=256, I=128, Is=256),                    # Is != I
     dict(T=300, G=8, TG=3),                              # group-limited routing
+    # one expert with exactly T rows: a full 128-row block, one more row, and
+    # a second 320-row forward tile of one row
+    dict(T=128, N=1, k=1, d=256, I=256, Is=128),
+    dict(T=129, N=1, k=1, d=256, I=256, Is=128),
+    dict(T=321, N=1, k=1, d=256, I=256, Is=128),
 ]
 
 

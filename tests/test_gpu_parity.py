@@ -89,6 +89,12 @@ LAYER_CASES = [
     ("mid_bf16", dict(T=64, N=100, k=6)),             # N % 64 != 0: a partial router tile
     ("mid_bf16", dict(T=50, N=16, k=16)),             # k = N: every expert chosen
     ("mid_bf16", dict(T=200, N=128, k=8, G=64, TG=4)),  # 64 groups of 2 experts
+    # one expert (and the shared one) with exactly T rows: the edges of a
+    # wave's 160-row token half and of the 320-row tile
+    ("mid_bf16", dict(T=160, N=1, k=1, d=256, I=256, Is=128)),
+    ("mid_bf16", dict(T=161, N=1, k=1, d=256, I=256, Is=128)),
+    ("mid_bf16", dict(T=320, N=1, k=1, d=256, I=256, Is=128)),
+    ("mid_bf16", dict(T=321, N=1, k=1, d=256, I=256, Is=128)),
 ]
 
 
@@ -133,6 +139,8 @@ FP8_CASES = [
     ("mid_bf16", dict(T=1)),                               # one token: 8 one-row tiles
     ("mid_bf16", dict(T=1000, N=2, k=1)),                  # >320 rows/expert: several tiles
     ("mid_bf16", dict(T=40, d=65536, N=2, k=1, I=128, Is=128)),  # K at the FP8 limit: 512 scale blocks
+    ("mid_bf16", dict(T=320, N=1, k=1, d=256, I=256, Is=128)),   # one full 320-row tile
+    ("mid_bf16", dict(T=321, N=1, k=1, d=256, I=256, Is=128)),   # and a second tile of one row
 ]
 
 
