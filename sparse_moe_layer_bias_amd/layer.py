@@ -28,6 +28,19 @@ from . import (MoeCfg, cfg_from_dict, moe_bias_update, moe_combine, moe_combine_
 GAMMA = 0.001  # end-of-step bias step (reading guide, "Methode" item 2)
 
 
+# the gathered-rows expert GEMM addresses a row of x (bf16, or its FP8 codes)
+# by a 32-bit byte offset
+GATHER_MAX_X_BYTES = (1 << 32) - 1
+
+
+def can_gather_rows(c, train):
+    """Whether a layer of config dict c can run its expert GEMM on gathered
+    token rows (moe_expert_ffn_gather): inference with bf16 activations and an
+    x (bf16, or its FP8 codes) below 2^32 bytes."""
+    x_bytes = c["T"] * c["d"] * (1 if c.get("fp8", False) else 2)
+    return c["dtype"] == "bf16" and not train and x_bytes <= GATHER_MAX_X_BYTES
+
+
 def pack_weights(cfg, which, w, stream=None):
     """The expert GEMM's streaming layout of one weight stack (moe_pack_weights)."""
     out = torch.empty((moe_packed_weights_size(cfg, which),), dtype=torch.uint8,
@@ -51,10 +64,11 @@ class MoeLayer:
     """Holds the expert weights (and their FP8 form when the config asks for it)
     and every per-step buffer for a batch of T tokens.
 
-    gather_rows (inference layers with bf16 activations, bf16 or FP8 GEMMs;
-    default on for them): the permutation writes only its indices (FP8: and
-    the codes of x) and the expert GEMM reads the token rows through
-    src_token (moe_expert_ffn_gather), so x_perm is not kept."""
+    gather_rows (inference layers with bf16 activations, bf16 or FP8 GEMMs,
+    whose x stays below 2^32 bytes; default on for them): the permutation
+    writes only its indices (FP8: and the codes of x) and the expert GEMM
+    reads the token rows through src_token (moe_expert_ffn_gather), so x_perm
+    is not kept.  Larger batches use the permuted copy x_perm."""
 
     def __init__(self, cfg, w13, w2, ws13=None, ws2=None, T=None, device="cuda",
                  train=False, save_activations=True, gather_rows=None):
@@ -107,10 +121,11 @@ class MoeLayer:
         self.offsets = torch.empty((N + 1,), **i32)
         self.src_token = torch.empty((TK,), **i32)
         self.dst_row = torch.empty((T, k), **i32)
-        can_gather = c["dtype"] == "bf16" and not train
+        can_gather = can_gather_rows(c, train)
         self.gather_rows = can_gather if gather_rows is None else bool(gather_rows)
         if self.gather_rows and not can_gather:
-            raise ValueError("gather_rows needs an inference layer with bf16 activations")
+            raise ValueError("gather_rows needs an inference layer with bf16 activations "
+                             "and x below 2^32 bytes")
         if self.fp8:
             if self.gather_rows:
                 self.x_perm = self.x_perm_s = None
