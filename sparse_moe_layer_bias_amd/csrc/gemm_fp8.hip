@@ -91,16 +91,8 @@ __global__ void __launch_bounds__(256) pack_weights_fp8_kernel(const uint4* __re
     out[i] = v;
 }
 
-// The 32 codes of a 128-byte LDS row that lane half h (= lane/32) feeds the
-// 32x32x64 MFMA for the K half q: logical chunks 4q + 2h and 4q + 2h + 1
-__device__ __forceinline__ i32x8_t ld_frag32(const uint8_t* rowp, int r, int q, int h) {
-    const uint4 lo = *(const uint4*)(rowp + sub_chunk8(r, 4 * q + 2 * h) * 16);
-    const uint4 hi = *(const uint4*)(rowp + sub_chunk8(r, 4 * q + 2 * h + 1) * 16);
-    i32x8_t v;
-    v[0] = (int)lo.x; v[1] = (int)lo.y; v[2] = (int)lo.z; v[3] = (int)lo.w;
-    v[4] = (int)hi.x; v[5] = (int)hi.y; v[6] = (int)hi.z; v[7] = (int)hi.w;
-    return v;
-}
+// LDS reads of 16-byte MFMA operand pieces by 32-bit LDS address
+typedef __attribute__((address_space(3))) const i32x4_t lds_i32x4_t;
 
 // A non-negative scale s as m * 2^(e8 - 127): e8 is s's biased exponent (the
 // E8M0 code) and m in [1, 2) its significand; for s below 2^-126 (zero or
@@ -212,6 +204,27 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
         }
     }
 
+    // A 32x32x64 operand fragment: lane l holds 32 codes of row l % 32 of a
+    // 32-row block, logical chunks 4q + 2h and 4q + 2h + 1 for K half q, with
+    // h = l / 32.  Fragment rows are a multiple of 32 plus l % 32, so a row's
+    // chunk swizzle (bits 1..3 of the row) is the lane's own: the byte offset
+    // of each chunk is a per-lane constant, and every fragment read is a
+    // stage base plus that offset plus an immediate.
+    const int l32 = lane & 31;
+    uint32_t co[2][2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+            co[q][b] = (uint32_t)(l32 * F8_BK + sub_chunk8(l32, 4 * q + 2 * (lane >> 5) + b) * 16);
+    // p[q][b]: the lane's chunk in the stage's first fragment row block; a
+    // block RB rows further is RB * F8_BK bytes on, an immediate offset
+    auto frag = [&](const uint32_t (&p)[2][2], int q, int rowblk) {
+        const i32x4_t lo = *(lds_i32x4_t*)(uintptr_t)(p[q][0] + rowblk * F8_BK);
+        const i32x4_t hi = *(lds_i32x4_t*)(uintptr_t)(p[q][1] + rowblk * F8_BK);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+
     issue(0, 0);
     for (int kt = 0; kt < nk; ++kt) {
         vm_wait_n(0);
@@ -221,7 +234,19 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
             const uint8_t* As = stage(kt & 1);
             const uint8_t* Xs = As + F8_A;
             const float* Ss = (const float*)(Xs + F8_X);
-            const int h = lane >> 5;
+            // per-lane addresses, opaque to the compiler so that it keeps the
+            // row block in the reads' immediate offsets
+            const uint32_t la = (uint32_t)(uintptr_t)to_lds(As) + (wg * 2) * 32 * F8_BK;
+            const uint32_t lx = (uint32_t)(uintptr_t)to_lds(Xs) + (tg * 160) * F8_BK;
+            uint32_t pa[2][2], px[2][2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    pa[q][b] = la + co[q][b];
+                    px[q][b] = lx + co[q][b];
+                    asm volatile("" : "+v"(pa[q][b]), "+v"(px[q][b]));
+                }
             // the two 64-wide K halves one after the other; the rescale to this
             // block's unit comes before the first half's MFMA
 #pragma unroll
@@ -230,14 +255,13 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
                 float mw[2];
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
-                    const int r = (wg * 2 + i) * 32 + (lane & 31);
-                    af[i] = ld_frag32(As + r * F8_BK, r, q, h);
+                    af[i] = frag(pa, q, i * 32);
                     if (q == 0) split_scale(swl[(GU ? i : wg >> 1) * nkb + kt], ew[i], mw[i]);
                 }
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
-                    const int r = tg * 160 + j * 32 + (lane & 31);
-                    const i32x8_t xf = ld_frag32(Xs + r * F8_BK, r, q, h);
+                    const int r = tg * 160 + j * 32 + l32;
+                    const i32x8_t xf = frag(px, q, j * 32);
                     if (q == 0) {
                         float mx;
                         split_scale(Ss[r], ex[j], mx);
