@@ -162,13 +162,23 @@ struct ColQuant {
     int64_t F;                 // features per block in out (>= C_r, C_s)
 };
 
-// One 128-row block of one group x 64 features: the column amax over the
-// block's real rows, the codes of every real row (padding rows get code 0),
-// written transposed (64 output rows of 128 codes).
+// One 128-row block of one group x QC_CHUNKS * 64 features, 64 at a time: the
+// column amax over the block's real rows, the codes of every real row
+// (padding rows get code 0), written transposed (64 output rows of 128 codes
+// per chunk).  The block's group and source rows are looked up once (a chain
+// of dependent loads: the group search, the group's first row, the gather
+// list) and serve every chunk; the next chunk's rows are loaded while this
+// one is quantised.  The grid is one-dimensional with the feature chunk
+// varying fastest, so consecutive workgroups read neighbouring pieces of the
+// same rows.
+constexpr int QC_CHUNKS = 4;
+
 __global__ void __launch_bounds__(256) quant_cols_t_kernel(ColQuant p) {
     __shared__ float tile[128][65];
     __shared__ float red[4][64];
-    const int64_t row0 = (int64_t)blockIdx.x * 128;  // position on the padded axis
+    const int64_t cm = p.C_r > p.C_s ? p.C_r : p.C_s;
+    const int64_t nfc = (cm + 64 * QC_CHUNKS - 1) / (64 * QC_CHUNKS);  // feature chunks
+    const int64_t row0 = ((int64_t)blockIdx.x / nfc) * 128;  // position on the padded axis
     const int32_t total = p.poff[p.N + 1];
     if (row0 >= total) return;
     int lo = 0, hi = p.N;  // group g: poff[g] <= row0 < poff[g+1]
@@ -178,16 +188,16 @@ __global__ void __launch_bounds__(256) quant_cols_t_kernel(ColQuant p) {
     }
     const int g = lo;
     const bool routed = g < p.N;
-    const int64_t C = routed ? p.C_r : p.C_s;
-    const int64_t c0 = (int64_t)blockIdx.y * 64;
-    if (c0 >= C) return;
+    const int64_t C = routed ? p.C_r : p.C_s;  // a multiple of 64
+    const int64_t cbase = ((int64_t)blockIdx.x % nfc) * 64 * QC_CHUNKS;
+    if (cbase >= C) return;
+    const int nch = (int)((C - cbase) / 64 < QC_CHUNKS ? (C - cbase) / 64 : QC_CHUNKS);
     const int64_t r0 = row0 - p.poff[g];  // first row of the block within the group
     const int64_t M = routed ? p.offsets[g + 1] - p.offsets[g] : p.S;
     const int valid = (int)(M - r0 < 128 ? M - r0 : 128);  // >= 1: the block holds rows
     const int t = threadIdx.x;
-    // the 4 passes' rows: their source row indices first, then all row loads,
-    // then the transposed LDS stores, so that the memory latencies overlap
-    // (rows past the group's last read its last row and are stored as zeros)
+    // the 4 passes' rows (rows past the group's last read its last row and
+    // are stored as zeros)
     int64_t sr[4];
 #pragma unroll
     for (int pass = 0; pass < 4; ++pass) {
@@ -203,43 +213,52 @@ __global__ void __launch_bounds__(256) quant_cols_t_kernel(ColQuant p) {
     const uint16_t* base = routed ? p.src_r : p.src_s;
     const int64_t ld = routed ? p.ld_r : p.ld_s;
     const int cc = (t & 7) * 8;
-    uint4 v[4];
-#pragma unroll
-    for (int pass = 0; pass < 4; ++pass) v[pass] = *(const uint4*)(base + sr[pass] * ld + c0 + cc);
-#pragma unroll
-    for (int pass = 0; pass < 4; ++pass) {
-        const int row = pass * 32 + (t >> 3);
-        const uint32_t w[4] = {v[pass].x, v[pass].y, v[pass].z, v[pass].w};
-        float f[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f[2 * i] = row < valid ? __uint_as_float(w[i] << 16) : 0.0f;
-            f[2 * i + 1] = row < valid ? __uint_as_float(w[i] & 0xffff0000u) : 0.0f;
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) tile[row][cc + i] = f[i];
-    }
-    __syncthreads();
     const int col = t & 63, part = t >> 6;
-    float m = 0.0f;
-    for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(tile[part * 32 + i][col]));
-    red[part][col] = m;
-    __syncthreads();
-    const float amax = fmaxf(fmaxf(red[0][col], red[1][col]), fmaxf(red[2][col], red[3][col]));
-    const float scale = amax / 448.0f;
-    // rows past the group's last hold zeros and encode as code 0
-    uint32_t code[8];
+    auto load = [&](int64_t c0, uint4 (&v)[4]) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        uint32_t wv = 0;
+        for (int pass = 0; pass < 4; ++pass) v[pass] = *(const uint4*)(base + sr[pass] * ld + c0 + cc);
+    };
+    uint4 v[4];
+    load(cbase, v);
+    for (int ch = 0; ch < nch; ++ch) {
+        const int64_t c0 = cbase + (int64_t)ch * 64;
+        if (ch > 0) __syncthreads();  // the previous chunk's tile and red are read
 #pragma unroll
-        for (int e = 0; e < 4; ++e) wv |= quant_e4m3(tile[part * 32 + 4 * k + e][col], scale) << (8 * e);
-        code[k] = wv;
+        for (int pass = 0; pass < 4; ++pass) {
+            const int row = pass * 32 + (t >> 3);
+            const uint32_t w[4] = {v[pass].x, v[pass].y, v[pass].z, v[pass].w};
+            float f[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f[2 * i] = row < valid ? __uint_as_float(w[i] << 16) : 0.0f;
+                f[2 * i + 1] = row < valid ? __uint_as_float(w[i] & 0xffff0000u) : 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) tile[row][cc + i] = f[i];
+        }
+        if (ch + 1 < nch) load(c0 + 64, v);  // in flight while this chunk is quantised
+        __syncthreads();
+        float m = 0.0f;
+        for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(tile[part * 32 + i][col]));
+        red[part][col] = m;
+        __syncthreads();
+        const float amax = fmaxf(fmaxf(red[0][col], red[1][col]), fmaxf(red[2][col], red[3][col]));
+        const float scale = amax / 448.0f;
+        // rows past the group's last hold zeros and encode as code 0
+        uint32_t code[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            uint32_t wv = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                wv |= quant_e4m3(tile[part * 32 + 4 * k + e][col], scale) << (8 * e);
+            code[k] = wv;
+        }
+        uint8_t* o = p.out + ((row0 / 128) * p.F + c0 + col) * 128 + part * 32;
+        *(uint4*)o = make_uint4(code[0], code[1], code[2], code[3]);
+        *(uint4*)(o + 16) = make_uint4(code[4], code[5], code[6], code[7]);
+        if (part == 0) p.out_s[(row0 / 128) * p.F + c0 + col] = scale;
     }
-    uint8_t* o = p.out + ((row0 / 128) * p.F + c0 + col) * 128 + part * 32;
-    *(uint4*)o = make_uint4(code[0], code[1], code[2], code[3]);
-    *(uint4*)(o + 16) = make_uint4(code[4], code[5], code[6], code[7]);
-    if (part == 0) p.out_s[(row0 / 128) * p.F + c0 + col] = scale;
 }
 
 // ---------------------------------------------------------------- weight gradients
@@ -677,7 +696,8 @@ hipError_t launch_expert_ffn_backward_fp8(const moe_cfg& c, const FfnBwdFp8Args&
         p.out_s = outs;
         p.F = F;
         const int64_t cm = Cr > Cs ? Cr : Cs;
-        quant_cols_t_kernel<<<dim3(pblocks, (unsigned)cdiv(cm, 64)), 256, 0, st>>>(p);
+        const int64_t nblk = cdiv(cm, 64 * QC_CHUNKS) * (int64_t)pblocks;
+        if (nblk > 0) quant_cols_t_kernel<<<dim3((unsigned)nblk), 256, 0, st>>>(p);
     };
     if (R + S > 0) {
         cols(a.dy_perm, a.dy_sh, nullptr, d, d, d, d, d, w.gT, w.gTs);
