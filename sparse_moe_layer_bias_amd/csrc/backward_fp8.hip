@@ -134,17 +134,41 @@ __global__ void __launch_bounds__(256) swiglu_bwd_fp8_kernel(
 // ---------------------------------------------------------------- row-direction tiles
 
 // poff[g] = sum over g' < g of roundup(M_g', 128), g = 0..N (N = the shared
-// expert with S rows), poff[N+1] = the total
-__global__ void pad_offsets_kernel(const int32_t* __restrict__ offsets, int N, int64_t S,
-                                   int32_t* __restrict__ poff) {
-    if (threadIdx.x != 0 || blockIdx.x != 0) return;
-    int64_t acc = 0;
-    for (int g = 0; g <= N; ++g) {
-        poff[g] = (int32_t)acc;
-        const int64_t M = g < N ? offsets[g + 1] - offsets[g] : S;
-        acc += (M + 127) & ~int64_t(127);
+// expert with S rows), poff[N+1] = the total.  One workgroup: thread t holds
+// the padded counts of groups PO_E t .. PO_E t + PO_E - 1 (zero past N), and a
+// scan of the per-thread sums gives each thread its starting offset.
+constexpr int PO_T = 256, PO_E = 5;
+static_assert(PO_T * PO_E >= 1024 + 1, "covers the largest expert count and the shared expert");
+__global__ void __launch_bounds__(PO_T) pad_offsets_kernel(const int32_t* __restrict__ offsets,
+                                                           int N, int64_t S,
+                                                           int32_t* __restrict__ poff) {
+    __shared__ int64_t part[PO_T];
+    const int t = threadIdx.x;
+    int64_t v[PO_E];
+    int64_t sum = 0;
+#pragma unroll
+    for (int e = 0; e < PO_E; ++e) {
+        const int g = t * PO_E + e;
+        const int64_t M = g < N ? offsets[g + 1] - offsets[g] : (g == N ? S : 0);
+        v[e] = (M + 127) & ~int64_t(127);
+        sum += v[e];
     }
-    poff[N + 1] = (int32_t)acc;
+    part[t] = sum;
+    __syncthreads();
+    for (int o = 1; o < PO_T; o <<= 1) {  // inclusive scan of the per-thread sums
+        const int64_t add = t >= o ? part[t - o] : 0;
+        __syncthreads();
+        part[t] += add;
+        __syncthreads();
+    }
+    int64_t acc = t > 0 ? part[t - 1] : 0;
+#pragma unroll
+    for (int e = 0; e < PO_E; ++e) {
+        const int g = t * PO_E + e;
+        if (g <= N) poff[g] = (int32_t)acc;
+        acc += v[e];
+    }
+    if (t == PO_T - 1) poff[N + 1] = (int32_t)part[PO_T - 1];
 }
 
 struct ColQuant {
@@ -675,7 +699,7 @@ hipError_t launch_expert_ffn_backward_fp8(const moe_cfg& c, const FfnBwdFp8Args&
             return e;
     }
     // 5. row-direction tiles of dY, h, [da db] and X (empty groups: nothing)
-    pad_offsets_kernel<<<1, 64, 0, st>>>(a.offsets, (int)N, S, w.poff);
+    pad_offsets_kernel<<<1, PO_T, 0, st>>>(a.offsets, (int)N, S, w.poff);
     const unsigned pblocks = (unsigned)(w.P_ld / 128);
     auto cols = [&](const void* sr, const void* ss, const int32_t* gather, int64_t Cr,
                     int64_t Cs, int64_t ldr, int64_t lds, int64_t F, uint8_t* out,
