@@ -154,6 +154,9 @@ def parse():
                          "3 times (for rocprofv3 --pmc passes over the whole step), then exit")
     ap.add_argument("--counter-summary", nargs=3, metavar=("MFMA_CSV", "FETCH_CSV", "WRITE_CSV"),
                     help="per-kernel MFMA busy share and HBM bytes of a --counter-run, then exit")
+    ap.add_argument("--sq-summary", nargs=2, metavar=("PASS_A_CSV", "PASS_B_CSV"),
+                    help="the expert GEMMs' SQ issue and stall counters from two --counter-run "
+                         "passes (the SQ_PASSES counter sets), then exit")
     ap.add_argument("--stats-summary", metavar="KERNEL_STATS_CSV",
                     help="print the per-kernel table of a rocprofv3 --stats run, then exit")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -380,6 +383,51 @@ def counter_summary(mfma_csv, fetch_csv, write_csv, workload):
         out.append("%-58s %5d %10.1f %8.1f%% %10.1f %10.1f %9.0f %6.1f%%" % (
             k.replace("moe::", "")[:58], n, d * 1e6, 100 * bz, rb / 1e6, wb / 1e6, gbs,
             100 * gbs / (PEAK["hbm"] / 1e9)))
+    return "\n".join(out)
+
+
+SQ_PASSES = (
+    ("SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS",
+     "SQ_ACTIVE_INST_VMEM", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VALU", "GRBM_GUI_ACTIVE"),
+    ("SQ_VMEM_TA_ADDR_FIFO_FULL", "SQ_VMEM_TA_CMD_FIFO_FULL", "SQ_LDS_BANK_CONFLICT",
+     "SQ_LDS_DATA_FIFO_FULL", "SQ_LDS_CMD_FIFO_FULL", "SQ_INST_LEVEL_VMEM",
+     "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "GRBM_GUI_ACTIVE"))
+
+
+def sq_summary(csv_a, csv_b, workload):
+    """The expert GEMMs' issue and stall counters of two --counter-run passes
+    (SQ_PASSES): each counter's mean per dispatch, and the shares of wave time
+    spent waiting on a counter (SQ_WAIT_ANY), waiting to issue
+    (SQ_WAIT_INST_ANY), issuing VALU (MFMA included) and LDS instructions, the
+    share of MFMA-busy cycles in which the VALU also ran, and LDS bank
+    conflicts per LDS-active cycle."""
+    import csv
+    import collections
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for tag, path in (("A", csv_a), ("B", csv_b)):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                k = r["Kernel_Name"]
+                if "ffn_gemm" not in k:
+                    continue
+                c = r["Counter_Name"] + ("_" + tag if r["Counter_Name"] == "GRBM_GUI_ACTIVE" else "")
+                per[k.split("(")[0].replace("void ", "").replace("moe::", "")][c].append(
+                    float(r["Counter_Value"]))
+    out = ["workload: %s" % workload]
+    for k, cs in per.items():
+        m = {c: sum(v) / len(v) for c, v in cs.items()}
+        out.append("kernel: %s  (dispatches averaged: %d)" % (k, len(cs["SQ_WAVE_CYCLES"])))
+        out += ["  %-30s %16.0f" % (c, m[c]) for c in sorted(m)]
+        w = m["SQ_WAVE_CYCLES"]
+        for name, num, den in (("wait_any / wave_cycles", "SQ_WAIT_ANY", w),
+                               ("wait_inst_any / wave_cycles", "SQ_WAIT_INST_ANY", w),
+                               ("active_valu / wave_cycles", "SQ_ACTIVE_INST_VALU", w),
+                               ("active_lds / wave_cycles", "SQ_ACTIVE_INST_LDS", w),
+                               ("mfma_coexec / mfma_busy", "SQ_VALU_MFMA_COEXEC_CYCLES",
+                                m["SQ_VALU_MFMA_BUSY_CYCLES"]),
+                               ("lds_bank_conflict / active_lds", "SQ_LDS_BANK_CONFLICT",
+                                m["SQ_ACTIVE_INST_LDS"])):
+            out.append("  %-32s %.3f" % (name, m[num] / den if den else 0.0))
     return "\n".join(out)
 
 
@@ -897,6 +945,9 @@ def main():
         return
     if args.counter_summary:
         print(counter_summary(*args.counter_summary, args.workload))
+        return
+    if args.sq_summary:
+        print(sq_summary(*args.sq_summary, args.workload))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
