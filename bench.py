@@ -16,7 +16,9 @@ for the same GEMM sources; `cpu_baseline` is the CPU oracle timed on a
 bounded sample of the same workload on this host.  Unless --no-configs, the
 line also carries `configs`: the FP8 workload (with its own roofline and
 oracle time), the decode-sized skewed batch (bias-balancing trajectory and
-the layer at T = 128) and the small workloads, measured after the headline.
+the layer at T = 128) and the small workloads, measured after the headline;
+for the launch-bound ones (T = 128 and the small layers) also as one HIP
+graph replay per step (`graph_ms_per_step`).
 
 --backward measures the layer's backward instead: a step is the four backward
 calls -- combine backward, expert FFN backward (two dgrad and two wgrad GEMMs,
@@ -814,10 +816,11 @@ def skew_balance(args, dev, log):
     b = bias_end.clone()
     ms, st = time_forward(lay, x, E, b, 20, 3)
     touched = int((lay.counts > 0).sum().item())
+    gms = time_graph(lay, x, E, bias_end.clone(), 20, 3)
     d, I, Is = c5["d"], c5["I"], c5["Is"]
     wbytes = 2.0 * 3 * d * (touched * I + Is)
-    log("decode layer T=128: %.3f ms/step, %d experts touched, stages %s" %
-        (ms, touched, json.dumps({a: round(v, 4) for a, v in st.items()})))
+    log("decode layer T=128: %.3f ms/step (%.3f as one graph), %d experts touched, stages %s" %
+        (ms, gms, touched, json.dumps({a: round(v, 4) for a, v in st.items()})))
     del lay
     torch.cuda.empty_cache()
     return {"route_plus_bias_update_us_per_step": us_step,
@@ -826,7 +829,7 @@ def skew_balance(args, dev, log):
             "zipf_slope_top1_b0": slope,
             "layer_T128_v3_experts": {
                 "ms_per_step": ms, "tokens_per_s": T / (ms / 1e3), "stages_ms": st,
-                "experts_touched": touched,
+                "graph_ms_per_step": gms, "experts_touched": touched,
                 "expert_weight_GBps": wbytes / (st["expert_ffn"] / 1e3) / 1e9}}
 
 
@@ -861,8 +864,10 @@ def extra_configs(args, dev, log):
         d2 = moe_inputs.make_layer_inputs(c, args.seed, "cuda")
         lay = MoeLayer(c, d2["w13"], d2["w2"], d2["ws13"], d2["ws2"])
         ms, st = time_forward(lay, d2["x"], d2["centroids"], d2["bias"].clone(), 20, 5)
-        out[name] = {"ms_per_step": ms, "tokens_per_s": c["T"] / (ms / 1e3), "stages_ms": st}
-        log("%s: %.4f ms/step" % (name, ms))
+        gms = time_graph(lay, d2["x"], d2["centroids"], d2["bias"].clone(), 20, 5)
+        out[name] = {"ms_per_step": ms, "tokens_per_s": c["T"] / (ms / 1e3), "stages_ms": st,
+                     "graph_ms_per_step": gms, "graph_tokens_per_s": c["T"] / (gms / 1e3)}
+        log("%s: %.4f ms/step, %.4f ms/step as one graph" % (name, ms, gms))
         if not args.no_cpu_baseline:
             try:
                 out[name]["cpu_baseline"] = cpu_baseline_layer(c, d2, log,
@@ -872,6 +877,27 @@ def extra_configs(args, dev, log):
                 out[name]["cpu_baseline"] = None
         del lay, d2
     return out
+
+
+def time_graph(layer, x, E, bias, steps, warmup):
+    """The same step captured once as a HIP graph (MoeLayer.capture_forward:
+    the five calls, no host work in between), W untimed replays, then K
+    replays timed with HIP events on the current stream.  Returns ms per
+    step."""
+    import torch
+    layer.capture_forward(x, E, bias)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        layer.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        layer.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
 
 
 def time_forward(layer, x, E, bias, steps, warmup):

@@ -458,37 +458,62 @@ __global__ void __launch_bounds__(G_THREADS, 1) ffn_gemm_bf16_kernel(GemmParamsV
 }
 
 // ---------------------------------------------------------------- fp32 path
-// Plain VALU kernel for fp32 storage (small layers): 64 token rows x 64 output
-// columns per 256-thread block; thread = (row tid%64, columns (tid/64)*16..+15).
+// VALU kernel for fp32 storage (small layers): 64 token rows x 64 output
+// columns per 256-thread block; thread = (row tid%64, columns (tid/64)*16..+15),
+// each output one fma chain over k ascending from +0.  The block's token rows
+// and weight rows pass through LDS F32_KC contraction elements at a time
+// (coalesced global loads), so the chains read their operands from LDS
+// instead of waiting on a global load per step.
+constexpr int F32_KC = 32;
+
 template <int MODE>
 __global__ void __launch_bounds__(256) ffn_gemm_f32_kernel(GemmParamsV2 p) {
     WorkV2 w;
     if (!decode_v2<4>(p, MODE, w)) return;
+    constexpr int WR = MODE == 0 ? 128 : 64;  // staged weight rows: W1 then W3, or W2
+    __shared__ float xs[64][F32_KC + 1];
+    __shared__ float wsm[WR][F32_KC + 1];
     const int tid = threadIdx.x;
-    const int64_t r = w.m0 + (tid & 63);
-    if (r >= w.M) return;
-    const float* a = (const float*)w.X + r * w.K;
+    const int rl = tid & 63, cg = tid >> 6;
+    const int64_t K = w.K;
+    const int64_t mrows = w.M - w.m0 < 64 ? w.M - w.m0 : 64;
+    const float* X = (const float*)w.X;
     const float* B = (const float*)w.W;
-    float* C = (float*)w.C;
-    const int64_t c0 = w.wt * 64 + (tid >> 6) * 16;
-    for (int jj = 0; jj < 16; ++jj) {
-        const int64_t c = c0 + jj;
-        if (c >= w.Nout) break;
-        if (MODE == 0) {
-            const float* w1 = B + c * w.K;
-            const float* w3 = B + (w.Nout + c) * w.K;
-            float sa = 0.0f, sb = 0.0f;
-            for (int64_t k = 0; k < w.K; ++k) {
-                sa = __builtin_fmaf(a[k], w1[k], sa);
-                sb = __builtin_fmaf(a[k], w3[k], sb);
-            }
-            C[r * w.Nout + c] = sa / (1.0f + expf(-sa)) * sb;
-        } else {
-            const float* w2 = B + c * w.K;
-            float s = 0.0f;
-            for (int64_t k = 0; k < w.K; ++k) s = __builtin_fmaf(a[k], w2[k], s);
-            C[r * w.Nout + c] = s;
+    const int64_t cbase = w.wt * 64;
+    float sa[16], sb[16];
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) sa[jj] = sb[jj] = 0.0f;
+    for (int64_t k0 = 0; k0 < K; k0 += F32_KC) {
+        const int kc = (int)(K - k0 < F32_KC ? K - k0 : F32_KC);
+        __syncthreads();  // the previous chunk has been read
+        for (int i = tid; i < 64 * F32_KC; i += 256) {
+            const int rr = i / F32_KC, kk = i % F32_KC;
+            xs[rr][kk] = rr < mrows && kk < kc ? X[(w.m0 + rr) * K + k0 + kk] : 0.0f;
         }
+        for (int i = tid; i < WR * F32_KC; i += 256) {
+            const int wr = i / F32_KC, kk = i % F32_KC;
+            const int64_t c = cbase + (wr & 63);
+            const int64_t row = MODE == 0 && wr >= 64 ? w.Nout + c : c;
+            wsm[wr][kk] = c < w.Nout && kk < kc ? B[row * K + k0 + kk] : 0.0f;
+        }
+        __syncthreads();
+        for (int kk = 0; kk < kc; ++kk) {
+            const float a = xs[rl][kk];
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) {
+                sa[jj] = __builtin_fmaf(a, wsm[cg * 16 + jj][kk], sa[jj]);
+                if (MODE == 0) sb[jj] = __builtin_fmaf(a, wsm[64 + cg * 16 + jj][kk], sb[jj]);
+            }
+        }
+    }
+    if (rl >= mrows) return;
+    float* C = (float*)w.C;
+    const int64_t r = w.m0 + rl;
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+        const int64_t c = cbase + cg * 16 + jj;
+        if (c < w.Nout)
+            C[r * w.Nout + c] = MODE == 0 ? sa[jj] / (1.0f + expf(-sa[jj])) * sb[jj] : sa[jj];
     }
 }
 

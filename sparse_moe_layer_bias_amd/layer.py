@@ -163,6 +163,7 @@ class MoeLayer:
         self.grads = None
         # a training forward keeps a, b and h for the backward (else recomputed)
         self.saved = None
+        self.graph = None  # capture_forward
         if self.train and save_activations:
             self.saved = torch.empty((moe_expert_ffn_saved_size(self.cfg),), dtype=torch.uint8,
                                      device=dev)
@@ -255,6 +256,35 @@ class MoeLayer:
         self.combine(x, residual, stream)
         if update_bias:
             self.bias_update(bias, stream)
+        return self.out
+
+    # HIP graph ----------------------------------------------------------------
+    def capture_forward(self, x, centroids, bias, residual=True, update_bias=True):
+        """Record one forward step -- the same five calls on the same buffers --
+        into a HIP graph and keep it; ``replay()`` runs it.  Every replay reads
+        x, centroids and bias from the tensors given here (write new values into
+        them in place between replays) and leaves its result in ``self.out``;
+        with ``update_bias`` each replay also updates ``bias`` in place.  None
+        of the calls allocates, synchronises or copies through the host, so a
+        whole step is one graph launch.  One untimed step (without the bias
+        update) runs first on the capture stream."""
+        s = torch.cuda.Stream()  # default priority
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.forward(x, centroids, bias, residual, update_bias=False)
+        s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            self.forward(x, centroids, bias, residual, update_bias)
+        torch.cuda.current_stream().wait_stream(s)
+        self.graph = g
+        return g
+
+    def replay(self):
+        """Run the captured forward step on the current stream."""
+        if self.graph is None:
+            raise RuntimeError("replay() needs capture_forward() first")
+        self.graph.replay()
         return self.out
 
     # the backward ------------------------------------------------------------
