@@ -98,6 +98,21 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const XT* __restrict
     const int64_t t0 = (int64_t)blockIdx.y * TM;
     const int ty = tid >> 4;  // 0..15 -> tokens ty*TY .. +TY-1
     const int tx = tid & 15;  // 0..15 -> experts tx*4 .. +3
+    // LDS chunk swizzle (chunks of 4 floats): in row k of the centroid tile,
+    // chunk c sits at c ^ ((k / 8) << 2); likewise in the token tile when it
+    // is 16 chunks wide (TY = 4, XE = 8).  The threads that stage one column
+    // write rows 8 apart, whose offsets agree modulo the bank count, so
+    // without it 4 of a wave's lanes hit each bank.  A reading wave reads one
+    // row, which the swizzle only permutes; its offset depends on k / 8 alone,
+    // kept per thread for the 4 row groups.
+    constexpr bool XSW = TY == 4;
+    static_assert(!XSW || XE == 8, "the token-tile swizzle assumes rows in groups of 8");
+    int xg[4], eg[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        xg[g] = XSW ? (ty ^ (g << 2)) * 4 : ty * TY;
+        eg[g] = (tx ^ (g << 2)) * 4;
+    }
 
     float acc[TY][4];
 #pragma unroll
@@ -113,10 +128,12 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const XT* __restrict
                 v = __uint_as_float(i & 1 ? r.xw[i / 2] & 0xffff0000u : r.xw[i / 2] << 16);
             else
                 v = __uint_as_float(r.xw[i]);
-            xs[buf][XE * (tid % TPT) + i][tid / TPT] = v;
+            const int q = tid % TPT, t = tid / TPT;
+            xs[buf][XE * q + i][XSW ? (((t >> 2) ^ (q << 2)) << 2) | (t & 3) : t] = v;
         }
+        const int q = tid & 3, n = tid >> 2;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) es[buf][8 * (tid & 3) + i][tid >> 2] = r.e[i];
+        for (int i = 0; i < 8; ++i) es[buf][8 * q + i][(((n >> 2) ^ (q << 2)) << 2) | (n & 3)] = r.e[i];
     };
 
     RlRegs<XT, TY> r;
@@ -139,8 +156,8 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const XT* __restrict
             for (int kk = 0; kk < RL_KG; ++kk) {
                 const int k = g * RL_KG + kk;
 #pragma unroll
-                for (int i = 0; i < TY; ++i) xv[slot][kk][i] = xs[buf][k][ty * TY + i];
-                const float4 eb = *reinterpret_cast<const float4*>(&es[buf][k][tx * 4]);
+                for (int i = 0; i < TY; ++i) xv[slot][kk][i] = xs[buf][k][xg[k >> 3] + i];
+                const float4 eb = *reinterpret_cast<const float4*>(&es[buf][k][eg[k >> 3]]);
                 ev[slot][kk][0] = eb.x; ev[slot][kk][1] = eb.y;
                 ev[slot][kk][2] = eb.z; ev[slot][kk][3] = eb.w;
             }
