@@ -365,17 +365,23 @@ __device__ __forceinline__ void wave_best(float& v, int& i, float& s) {
 }
 
 // merge the partner's best two (key, index) pairs into ours (both sorted)
+// (selects, not branches: the branchy form made the compiler merge the four
+// values through a stack slot, i.e. scratch memory)
 template <int S>
 __device__ __forceinline__ void top2_step(float& r1, int& i1, float& r2, int& i2) {
     const float p1 = xlane<S>(r1), p2 = xlane<S>(r2);
     const int q1 = xlane<S>(i1), q2 = xlane<S>(i2);
-    if (beats(p1, q1, r1, i1)) {
-        // partner's first wins; second is the better of (r1, p2)
-        if (beats(r1, i1, p2, q2)) { r2 = r1; i2 = i1; } else { r2 = p2; i2 = q2; }
-        r1 = p1; i1 = q1;
-    } else if (beats(p1, q1, r2, i2)) {
-        r2 = p1; i2 = q1;
-    }
+    // partner's first wins: the second is the better of (r1, p2); else the
+    // second is the better of (p1, r2)
+    const bool w = beats(p1, q1, r1, i1);
+    const bool a = beats(r1, i1, p2, q2);
+    const bool b = beats(p1, q1, r2, i2);
+    const float n2 = w ? (a ? r1 : p2) : (b ? p1 : r2);
+    const int m2 = w ? (a ? i1 : q2) : (b ? q1 : i2);
+    r1 = w ? p1 : r1;
+    i1 = w ? q1 : i1;
+    r2 = n2;
+    i2 = m2;
 }
 
 // group score = sum of the group's two best keys, -0 -> +0, NaN -> -inf
