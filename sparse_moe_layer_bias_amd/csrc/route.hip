@@ -184,18 +184,26 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const XT* __restrict
         __syncthreads();
     }
 
-    // epilogue: affinity s = Sigmoid(z), evaluated in double, rounded once
-    // (one value at a time: the double-precision exp unrolled over all
-    // outputs would claim registers the main loop then goes without)
-#pragma unroll 1
-    for (int i = 0; i < TY; ++i) {
+    // epilogue: affinity s = Sigmoid(z), evaluated in double, rounded once.
+    // With 4 tokens, one token at a time: the double-precision exp unrolled
+    // over all 16 outputs would claim registers the main loop then goes
+    // without.  With 1 or 2 the loop is unrolled: a loop index into acc
+    // would put the accumulators in scratch memory for the whole main loop.
+    auto emit = [&](int i) {
         const int64_t t = t0 + ty * TY + i;
-        if (t >= T) continue;
+        if (t >= T) return;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int64_t n = n0 + tx * 4 + j;
             if (n < N) s_out[t * N + n] = (float)(1.0 / (1.0 + exp(-(double)acc[i][j])));
         }
+    };
+    if constexpr (TY == 4) {
+#pragma unroll 1
+        for (int i = 0; i < TY; ++i) emit(i);
+    } else {
+#pragma unroll
+        for (int i = 0; i < TY; ++i) emit(i);
     }
 }
 
