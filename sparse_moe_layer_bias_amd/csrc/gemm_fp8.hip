@@ -62,7 +62,6 @@ struct Fp8Params {
     void* hb_s;
     float* hf_r;           // modes 0 and 4, optional: h in fp32 before quantisation
     float* hf_s;
-    int64_t x_rows;        // rows of the gathered-from codes (g.gather_r set: T)
 };
 
 // Pack FP8 weight codes [n_mats][rows][K] into the kernel's LDS image order:
@@ -130,14 +129,15 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
     const int64_t wrows = GU ? 2 * w.Nout : w.Nout;
     const int64_t wrb = wrows / 128;  // 128-row scale blocks per expert matrix
 
-    // Copies go through buffer descriptors (base in SGPRs, 32-bit lane offsets,
-    // out-of-range lanes read as zero): the tile's weight panel, the expert's
-    // token rows and their scales.
+    // Copies: global_load_lds from a wave-uniform base plus 32-bit lane
+    // offsets, every address in bounds (token rows past the tile's last are
+    // clamped to it): the tile's weight panel, the expert's token rows and
+    // their scales.  (The compiler's own waits for these copies stay at the
+    // step boundaries.  The buffer form of the instruction, as a builtin, made
+    // it wait for every copy in flight before the first LDS read; written as
+    // inline asm instead it measured 1% slower than this.)
     const char* wpanel = w.W + w.wt * (int64_t)nk * F8_A;
     const char* xbase = gat ? w.X : w.X + w.m0 * K;
-    const i32x4_t rw = make_rsrc(wpanel, (int64_t)nk * F8_A);
-    const i32x4_t rx = make_rsrc(xbase, gat ? P.x_rows * K : mc * K);
-    const i32x4_t rs = make_rsrc(xs, (gat ? P.x_rows : mc) * nkb * 4);
 
     // token code copies: block b = 8 rows (128-byte lines); the blocks holding
     // real rows are the prefix b < nxe; rows past the last one repeat it
@@ -163,17 +163,24 @@ __device__ __forceinline__ void gemm_fp8_body(const Fp8Params& P, const WorkV2& 
         uint8_t* As = stage(s);
         uint8_t* Xs = As + F8_A;
         uint8_t* Ss = Xs + F8_X;
+        const char* wsrc = wpanel + (int64_t)kt * F8_A;
+        const char* xsrc = xbase + (int64_t)kt * F8_BK;
 #pragma unroll
         for (int c = 0; c < PA; ++c) {
             const int b = wave + F8_WAVES * c;
-            dma_to_lds<16>(rw, As + b * 1024, lane * 16, kt * F8_A + b * 1024);
+            __builtin_amdgcn_global_load_lds((const void*)(wsrc + b * 1024 + lane * 16),
+                                             to_lds(As + b * 1024), 16, 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < PX; ++j) {
             const int b = wave + F8_WAVES * j;
-            if (b < nxe) dma_to_lds<16>(rx, Xs + b * 1024, xoff[j], kt * F8_BK);
+            if (b < nxe)
+                __builtin_amdgcn_global_load_lds((const void*)(xsrc + xoff[j]),
+                                                 to_lds(Xs + b * 1024), 16, 0, 0);
         }
-        if (wave < NSC) dma_to_lds<4>(rs, Ss + wave * 256, soff, kt * 4);
+        if (wave < NSC)
+            __builtin_amdgcn_global_load_lds((const void*)((const char*)xs + soff + kt * 4),
+                                             to_lds(Ss + wave * 256), 4, 0, 0);
     };
 
     f32x16_t acc[2][NBB];
@@ -570,7 +577,6 @@ hipError_t launch_expert_ffn_fp8(const moe_cfg& c, const FfnArgs& a, const int2*
     P.xs_r = a.x_perm_scale;
     P.xs_s = a.x_sh_scale;
     P.g.gather_r = a.gather;  // inference forward, optional: routed rows = x_q[src_token]
-    P.x_rows = T;
     P.ws_r = a.w13_scale;
     P.ws_s = a.ws13_scale;
     P.hs_r = hs_r;
