@@ -722,3 +722,58 @@ def test_decode_batch_layer_v3_weights(orc, v3_run):
                 orc.bias_update(r["counts"], T * k, bh).view(np.uint32), "bias update")
     del layer
     torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_decode_batch_layer_v3_fp8(orc, v3_fp8_run):
+    """The skewed decode-step batch (T = 128, no group limit, the bias of the
+    oracle's own 100 balancing steps) through the FP8 layer with the V3-shaped
+    weights: 1-10 rows in most 320-row FP8 tiles.  idx, gates and counts of all
+    tokens and the activation codes and scales bit for bit; the expert FFN step
+    by step (fp32 h, h bytes, y, out) on every routed row of 24 tokens and
+    their shared-expert rows."""
+    cfg5 = dict(moe_inputs.CONFIGS["skew_balance"], fp8=True)
+    _, dev, _, _, _ = v3_fp8_run
+    T, N, k = cfg5["T"], cfg5["N"], cfg5["k"]
+    E = moe_inputs.make_skew_centroids(cfg5, 0, "cpu")
+    Eh = moe_inputs.to_host(E)
+    bh = np.zeros(N, np.float32)
+    for step in range(cfg5["steps"]):
+        r = orc.route(moe_inputs.to_host(moe_inputs.make_skew_tokens(cfg5, step, 0, "cpu")), Eh,
+                      bh, k)
+        bh = orc.bias_update(r["counts"], T * k, bh)
+    x = moe_inputs.make_skew_tokens(cfg5, cfg5["steps"], 0, "cpu")
+    xh = moe_inputs.to_host(x)
+    layer = MoeLayer(cfg5, dev["w13"], dev["w2"], dev["ws13"], dev["ws2"], gather_rows=False)
+    bias = torch.from_numpy(bh.copy()).cuda()
+    layer.forward(x.cuda(), E.cuda(), bias)
+    torch.cuda.synchronize()
+    r = orc.route(xh, Eh, bh, k)
+    assert_bits(moe_inputs.to_host(layer.idx), r["idx"], "idx")
+    assert_bits(moe_inputs.to_host(layer.gate), r["gate"], "gate")
+    assert_bits(moe_inputs.to_host(layer.counts), r["counts"], "counts")
+    touched = int((r["counts"] > 0).sum())
+    log("FP8 decode batch: %d of %d experts touched, max rows %d" % (touched, N,
+                                                                      r["counts"].max()))
+    assert touched > N // 2
+    off, src, dst = orc.permute(r["idx"], N)
+    assert_bits(moe_inputs.to_host(layer.offsets), off, "offsets")
+    assert_bits(moe_inputs.to_host(layer.dst_row), dst, "dst_row")
+    xq, xs = orc.quant_act_fp8(xh)
+    assert_bits(moe_inputs.to_host(layer.x_q), xq, "x codes")
+    assert_bits(moe_inputs.to_host(layer.x_s).view(np.uint32), xs.view(np.uint32), "x scales")
+    tok = np.sort(np.random.default_rng(9).choice(T, 24, replace=False))
+    rows = np.sort(dst[tok].ravel())
+    ref = dict(r, offsets=off, src_token=src, dst_row=dst, x_q=xq, x_s=xs,
+               w13_q=ExpertCodes(orc, dev["w13"], 0), w13_s=ExpertCodes(orc, dev["w13"], 1),
+               w2_q=ExpertCodes(orc, dev["w2"], 0), w2_s=ExpertCodes(orc, dev["w2"], 1))
+    ref["x_q_perm"] = RowsOf(xq, src)
+    ref["x_s_perm"] = RowsOf(xs, src)
+    ref["ws13_q"], ref["ws13_s"] = orc.quant_weight_fp8(moe_inputs.to_host(dev["ws13"]))
+    ref["ws2_q"], ref["ws2_s"] = orc.quant_weight_fp8(moe_inputs.to_host(dev["ws2"]))
+    log("checking the FP8 expert FFN on %d routed rows of %d tokens" % (len(rows), len(tok)))
+    check_fp8_expert_split(orc, layer, ref, xh, rows=rows, what="FP8 decode: ")
+    assert_bits(moe_inputs.to_host(bias).view(np.uint32),
+                orc.bias_update(r["counts"], T * k, bh).view(np.uint32), "bias update")
+    del layer
+    torch.cuda.empty_cache()
