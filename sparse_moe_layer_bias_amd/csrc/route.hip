@@ -9,7 +9,9 @@
 // Three kernels:
 //  router_logits: z = x E^T as a fixed-order fp32 FMA chain per output (k
 //    ascending from +0), so that the chosen indices are reproducible bit for
-//    bit; the chain runs on the VALU (MFMA has no defined summation order).
+//    bit; for large batches the chain runs on the matrix cores as one
+//    contraction-1 MFMA per k (each a single fused multiply-add, the same
+//    bits as the VALU fma), for smaller ones on the VALU.
 //    Epilogue: s = fp32(1 / (1 + exp(-(double)z))).
 //  router_select: one wavefront per token; keys s+b (a NaN key ranks as
 //    -inf); optional group limit; k rounds of a wave-wide argmax under the
@@ -204,6 +206,116 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const XT* __restrict
     } else {
 #pragma unroll
         for (int i = 0; i < TY; ++i) emit(i);
+    }
+}
+
+// Large batches: the same chains on the matrix cores.  An fp32 MFMA with a
+// contraction of 1 (v_mfma_f32_16x16x1_4b_f32) computes each output as one
+// fused multiply-add, d = RN(c + a*b), bit for bit the VALU fma (checked on
+// gfx950 against __builtin_fmaf over random, wide-exponent, cancelling and
+// subnormal operands), at twice the VALU's fp32 fma rate.  Issued for k = 0,
+// 1, 2, ... on one accumulator it is the fixed-order chain of the VALU
+// kernels, so the logits are the same bits.
+// Tile: 64 tokens x 64 experts per 256-thread workgroup.  Wave w owns tokens
+// (w >> 1) * 32 .. +31 and experts (w & 1) * 32 .. +31 as the four 16 x 16
+// blocks of one instruction: block b holds tokens (b >> 1) * 16 and experts
+// (b & 1) * 16 .. +15; lane 16b + r supplies token r's and expert r's element
+// k of block b, and the result of block b sits in accumulator registers
+// 4b .. 4b+3 (the lane/register layout measured on gfx950, see the epilogue).  Operands are staged through LDS
+// token- and expert-major ([row][k], rows padded by 4 floats so the 16 rows a
+// block reads with one ds_read_b128 hit distinct banks) in stages of RM_BK,
+// double buffered; a partial last stage is padded with zeros, which leave a
+// chain unchanged (it starts at +0 and never holds -0).
+constexpr int RM_BK = 32, RM_PAD = RM_BK + 4;
+
+template <typename XT, bool FULL>
+__global__ void __launch_bounds__(256) router_logits_mfma_kernel(const XT* __restrict__ x,
+                                                                 const float* __restrict__ E,
+                                                                 float* __restrict__ s_out,
+                                                                 int64_t T, int64_t d, int64_t N) {
+    __shared__ __attribute__((aligned(16))) float xs[2][64][RM_PAD];
+    __shared__ __attribute__((aligned(16))) float es[2][64][RM_PAD];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t n0 = (int64_t)blockIdx.x * 64, t0 = (int64_t)blockIdx.y * 64;
+    // staging: thread tid copies row tid / 4, elements (tid % 4) * 8 .. +7
+    const int srow = tid >> 2, sk = (tid & 3) * 8;
+    const int64_t st = t0 + srow < T ? t0 + srow : T - 1;  // clamped: never stored
+    const int64_t sn = n0 + srow < N ? n0 + srow : N - 1;
+    constexpr int XW = 8 * (int)sizeof(XT) / 4;
+    uint32_t xw[XW];
+    float ev[8];
+    auto load = [&](int64_t k0) {
+        const int64_t k = k0 + sk;
+        const XT* xr = x + st * d + k;
+        const float* er = E + sn * d + k;
+        if (FULL) {
+            __builtin_memcpy(xw, xr, sizeof(xw));
+            const float4 a = *(const float4*)er;
+            const float4 b = *(const float4*)(er + 4);
+            ev[0] = a.x; ev[1] = a.y; ev[2] = a.z; ev[3] = a.w;
+            ev[4] = b.x; ev[5] = b.y; ev[6] = b.z; ev[7] = b.w;
+        } else {
+            XT v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                v[i] = k + i < d ? xr[i] : XT(0);
+                ev[i] = k + i < d ? er[i] : 0.0f;
+            }
+            __builtin_memcpy(xw, v, sizeof(xw));
+        }
+    };
+    auto store = [&](int buf) {
+        float xv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if constexpr (sizeof(XT) == 2)
+                xv[i] = __uint_as_float(i & 1 ? xw[i / 2] & 0xffff0000u : xw[i / 2] << 16);
+            else
+                xv[i] = __uint_as_float(xw[i]);
+        }
+        *(float4*)&xs[buf][srow][sk] = make_float4(xv[0], xv[1], xv[2], xv[3]);
+        *(float4*)&xs[buf][srow][sk + 4] = make_float4(xv[4], xv[5], xv[6], xv[7]);
+        *(float4*)&es[buf][srow][sk] = make_float4(ev[0], ev[1], ev[2], ev[3]);
+        *(float4*)&es[buf][srow][sk + 4] = make_float4(ev[4], ev[5], ev[6], ev[7]);
+    };
+
+    const int b = lane >> 4, r = lane & 15;
+    const int xrow = (wave >> 1) * 32 + (b >> 1) * 16 + r;  // token row this lane supplies
+    const int erow = (wave & 1) * 32 + (b & 1) * 16 + r;    // expert row this lane supplies
+    f32x16_t acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+
+    const int64_t nk = cdiv(d, RM_BK);
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int64_t kb = 0; kb < nk; ++kb) {
+        const int buf = kb & 1;
+        const bool more = kb + 1 < nk;
+        if (more) load((kb + 1) * RM_BK);
+#pragma unroll
+        for (int kk = 0; kk < RM_BK; kk += 4) {
+            const float4 a = *(const float4*)&xs[buf][xrow][kk];
+            const float4 e = *(const float4*)&es[buf][erow][kk];
+            acc = __builtin_amdgcn_mfma_f32_16x16x1f32(a.x, e.x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x1f32(a.y, e.y, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x1f32(a.z, e.z, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x1f32(a.w, e.w, acc, 0, 0, 0);
+        }
+        if (more) store(buf ^ 1);
+        __syncthreads();
+    }
+
+    // epilogue: s = Sigmoid(z) in double, rounded once.  Accumulator
+    // register q holds block q / 4, row (token) 4 * (lane / 16) + q % 4,
+    // column (expert) lane % 16.
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int qb = q >> 2;
+        const int64_t t = t0 + (wave >> 1) * 32 + (qb >> 1) * 16 + 4 * (lane >> 4) + (q & 3);
+        const int64_t n = n0 + (wave & 1) * 32 + (qb & 1) * 16 + (lane & 15);
+        if (t < T && n < N) s_out[t * N + n] = (float)(1.0 / (1.0 + exp(-(double)acc[q])));
     }
 }
 
@@ -627,8 +739,24 @@ hipError_t launch_route(const moe_cfg& c, const void* x, const float* centroids,
                 router_logits_rows_kernel<float, false><<<g1, 512, 0, st>>>(
                     (const float*)x, centroids, scores, T, d, N);
         }
-    } else if (cdiv(N, RL_TN) * cdiv(T, 16 * 4) >= 384)
-        launch_logits<4>(c.act_dtype, full, x, centroids, scores, T, d, N, st);
+    } else if (cdiv(N, RL_TN) * cdiv(T, 16 * 4) >= 384) {
+        const dim3 gm((unsigned)cdiv(N, 64), (unsigned)cdiv(T, 64));
+        if (c.act_dtype == MOE_BF16) {
+            if (full)
+                router_logits_mfma_kernel<uint16_t, true><<<gm, 256, 0, st>>>(
+                    (const uint16_t*)x, centroids, scores, T, d, N);
+            else
+                router_logits_mfma_kernel<uint16_t, false><<<gm, 256, 0, st>>>(
+                    (const uint16_t*)x, centroids, scores, T, d, N);
+        } else {
+            if (full)
+                router_logits_mfma_kernel<float, true><<<gm, 256, 0, st>>>(
+                    (const float*)x, centroids, scores, T, d, N);
+            else
+                router_logits_mfma_kernel<float, false><<<gm, 256, 0, st>>>(
+                    (const float*)x, centroids, scores, T, d, N);
+        }
+    }
     else if (cdiv(N, RL_TN) * cdiv(T, 16 * 2) >= 192)
         launch_logits<2>(c.act_dtype, full, x, centroids, scores, T, d, N, st);
     else

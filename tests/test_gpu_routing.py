@@ -4,11 +4,12 @@ whose keys are NaN.
 
 The launcher picks the logits kernel by batch size (a serial fp32 chain per
 (token, expert) pair, so the tile per thread trades chains against
-workgroups): one chain per lane when cdiv(N,64)*cdiv(T,64) < 64, else 4, 2 or
-1 token(s) per thread (TY) by the number of workgroups each gives; FULL
-instances need d % 32 == 0 (tiled) or d % 256 == 0 (one chain per lane), the
-others pad the last stage.  Scores, indices, gates and counts must match bit
-for bit.
+workgroups): one chain per lane when cdiv(N,64)*cdiv(T,64) < 64, the
+matrix-core kernel (one contraction-1 MFMA per k) from 384 64x64 tiles on,
+else 2 or 1 token(s) per thread (TY) on the VALU by the number of workgroups
+each gives; FULL instances need d % 32 == 0 (tiled) or d % 256 == 0 (one
+chain per lane), the others pad the last stage.  Scores, indices, gates and
+counts must match bit for bit.
 """
 import numpy as np
 import pytest
@@ -54,14 +55,14 @@ def _route_gpu(T, d, N, k, G, TG, dtype, inp):
 ROUTE_CASES = [
     (1024, 7168, 256, 8, 8, 4, "bf16"),   # tiled, 1 token per thread
     (2048, 7168, 256, 8, 8, 4, "bf16"),   # tiled, 2 tokens per thread
-    (8192, 7176, 256, 8, 8, 4, "bf16"),   # tiled, 4 tokens per thread, d % 32 != 0
-    (6200, 512, 250, 8, 1, 1, "bf16"),    # tiled, 4 tokens per thread, ragged tokens and experts
+    (8192, 7176, 256, 8, 8, 4, "bf16"),   # matrix cores, d % 32 != 0
+    (6200, 512, 250, 8, 1, 1, "bf16"),    # matrix cores, ragged tokens and experts
     (2048, 1000, 256, 8, 1, 1, "bf16"),   # tiled, 2 tokens per thread, d % 32 != 0
     (1024, 1000, 256, 6, 1, 1, "bf16"),   # tiled, 1 token per thread, d % 32 != 0
     (4096, 1000, 64, 8, 1, 1, "f32"),     # fp32 x: tiled, 1 token per thread, d % 32 != 0
     (8192, 512, 64, 8, 1, 1, "f32"),      # fp32 x: tiled, 2 tokens per thread
-    (32768, 256, 64, 4, 1, 1, "f32"),     # fp32 x: tiled, 4 tokens per thread
-    (24576, 1000, 64, 8, 1, 1, "f32"),    # fp32 x: tiled, 4 tokens per thread, d % 32 != 0
+    (32768, 256, 64, 4, 1, 1, "f32"),     # fp32 x: matrix cores
+    (24576, 1000, 64, 8, 1, 1, "f32"),    # fp32 x: matrix cores, d % 32 != 0
     (128, 1000, 256, 8, 1, 1, "bf16"),    # one chain per lane, d % 256 != 0
     (100, 7168, 256, 8, 8, 4, "bf16"),    # one chain per lane, ragged tokens
 ]
@@ -87,12 +88,13 @@ def _bits_nan_aware(got, ref, what):
     assert_bits(g[~nan], r[~nan], what)
 
 
-@pytest.mark.parametrize("G,TG", [(1, 1), (8, 3)])
-def test_nan_rows_route_to_valid_experts(orc, G, TG):
+@pytest.mark.parametrize("T,d,N,G,TG", [(256, 1024, 64, 1, 1), (256, 1024, 64, 8, 3),
+                                        (8192, 512, 256, 8, 3)])  # the last on the matrix cores
+def test_nan_rows_route_to_valid_experts(orc, T, d, N, G, TG):
     """Rows of x holding NaN or inf give NaN (or extreme) scores; every token
     must still get k distinct experts in [0, N), counts must sum to T*k, and
     idx must equal the oracle's (a NaN key ranks as -inf, lower index first)."""
-    T, d, N, k = 256, 1024, 64, 6
+    k = 6
     inp = _route_inputs(T, d, N, "bf16", seed=41)
     x = inp["x"]
     x[5, :] = float("nan")
