@@ -27,8 +27,9 @@ namespace moe {
 
 // ------------------------------------------------------------------ logits
 
-// Tile: TM = 16*TY tokens x 64 experts per 256-thread workgroup; each thread
-// owns TY tokens x 4 experts (4*TY independent FMA chains).  BK = 32 hidden
+// VALU tile for mid-sized batches: TM = 16*TY tokens (TY = 1 or 2) x 64
+// experts per 256-thread workgroup; each thread owns TY tokens x 4 experts
+// (4*TY independent FMA chains).  BK = 32 hidden
 // elements per LDS stage, double buffered, held transposed ([k][token],
 // [k][expert]) so each thread reads its tokens and experts as float4s.
 // Global loads are 16-byte vectors; FULL = (d % BK == 0) drops every
@@ -100,21 +101,17 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const XT* __restrict
     const int64_t t0 = (int64_t)blockIdx.y * TM;
     const int ty = tid >> 4;  // 0..15 -> tokens ty*TY .. +TY-1
     const int tx = tid & 15;  // 0..15 -> experts tx*4 .. +3
-    // LDS chunk swizzle (chunks of 4 floats): in row k of the centroid tile,
-    // chunk c sits at c ^ ((k / 8) << 2); likewise in the token tile when it
-    // is 16 chunks wide (TY = 4, XE = 8).  The threads that stage one column
+    // LDS chunk swizzle of the centroid tile (chunks of 4 floats): in row k,
+    // chunk c sits at c ^ ((k / 8) << 2).  The threads that stage one column
     // write rows 8 apart, whose offsets agree modulo the bank count, so
     // without it 4 of a wave's lanes hit each bank.  A reading wave reads one
     // row, which the swizzle only permutes; its offset depends on k / 8 alone,
     // kept per thread for the 4 row groups.
-    constexpr bool XSW = TY == 4;
-    static_assert(!XSW || XE == 8, "the token-tile swizzle assumes rows in groups of 8");
-    int xg[4], eg[4];
+    static_assert(TY == 1 || TY == 2, "1 or 2 tokens per thread");
+    int eg[4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        xg[g] = XSW ? (ty ^ (g << 2)) * 4 : ty * TY;
-        eg[g] = (tx ^ (g << 2)) * 4;
-    }
+    for (int g = 0; g < 4; ++g) eg[g] = (tx ^ (g << 2)) * 4;
+    const int xg = ty * TY;
 
     float acc[TY][4];
 #pragma unroll
@@ -131,7 +128,7 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const XT* __restrict
             else
                 v = __uint_as_float(r.xw[i]);
             const int q = tid % TPT, t = tid / TPT;
-            xs[buf][XE * q + i][XSW ? (((t >> 2) ^ (q << 2)) << 2) | (t & 3) : t] = v;
+            xs[buf][XE * q + i][t] = v;
         }
         const int q = tid & 3, n = tid >> 2;
 #pragma unroll
@@ -158,7 +155,7 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const XT* __restrict
             for (int kk = 0; kk < RL_KG; ++kk) {
                 const int k = g * RL_KG + kk;
 #pragma unroll
-                for (int i = 0; i < TY; ++i) xv[slot][kk][i] = xs[buf][k][xg[k >> 3] + i];
+                for (int i = 0; i < TY; ++i) xv[slot][kk][i] = xs[buf][k][xg + i];
                 const float4 eb = *reinterpret_cast<const float4*>(&es[buf][k][eg[k >> 3]]);
                 ev[slot][kk][0] = eb.x; ev[slot][kk][1] = eb.y;
                 ev[slot][kk][2] = eb.z; ev[slot][kk][3] = eb.w;
@@ -187,10 +184,8 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const XT* __restrict
     }
 
     // epilogue: affinity s = Sigmoid(z), evaluated in double, rounded once.
-    // With 4 tokens, one token at a time: the double-precision exp unrolled
-    // over all 16 outputs would claim registers the main loop then goes
-    // without.  With 1 or 2 the loop is unrolled: a loop index into acc
-    // would put the accumulators in scratch memory for the whole main loop.
+    // The loop is unrolled: a loop index into acc would put the accumulators
+    // in scratch memory for the whole main loop.
     auto emit = [&](int i) {
         const int64_t t = t0 + ty * TY + i;
         if (t >= T) return;
@@ -200,13 +195,8 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const XT* __restrict
             if (n < N) s_out[t * N + n] = (float)(1.0 / (1.0 + exp(-(double)acc[i][j])));
         }
     };
-    if constexpr (TY == 4) {
-#pragma unroll 1
-        for (int i = 0; i < TY; ++i) emit(i);
-    } else {
 #pragma unroll
-        for (int i = 0; i < TY; ++i) emit(i);
-    }
+    for (int i = 0; i < TY; ++i) emit(i);
 }
 
 // Large batches: the same chains on the matrix cores.  An fp32 MFMA with a
@@ -216,7 +206,9 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const XT* __restrict
 // subnormal operands), at twice the VALU's fp32 fma rate.  Issued for k = 0,
 // 1, 2, ... on one accumulator it is the fixed-order chain of the VALU
 // kernels, so the logits are the same bits.
-// Tile: 64 tokens x 64 experts per 256-thread workgroup.  Wave w owns tokens
+// Tile: TM tokens (64 or 128) x 64 experts per workgroup of TM / 16 waves
+// (the 128-token tile halves the centroid traffic per multiply; the launcher
+// takes it while it still gives every CU a workgroup).  Wave w owns tokens
 // (w >> 1) * 32 .. +31 and experts (w & 1) * 32 .. +31 as the four 16 x 16
 // blocks of one instruction: block b holds tokens (b >> 1) * 16 and experts
 // (b & 1) * 16 .. +15; lane 16b + r supplies token r's and expert r's element
@@ -228,19 +220,22 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const XT* __restrict
 // chain unchanged (it starts at +0 and never holds -0).
 constexpr int RM_BK = 32, RM_PAD = RM_BK + 4;
 
-template <typename XT, bool FULL>
-__global__ void __launch_bounds__(256) router_logits_mfma_kernel(const XT* __restrict__ x,
-                                                                 const float* __restrict__ E,
-                                                                 float* __restrict__ s_out,
-                                                                 int64_t T, int64_t d, int64_t N) {
-    __shared__ __attribute__((aligned(16))) float xs[2][64][RM_PAD];
+template <typename XT, bool FULL, int TM>
+__global__ void __launch_bounds__(TM * 4) router_logits_mfma_kernel(const XT* __restrict__ x,
+                                                                    const float* __restrict__ E,
+                                                                    float* __restrict__ s_out,
+                                                                    int64_t T, int64_t d, int64_t N) {
+    static_assert(TM == 64 || TM == 128, "64 or 128 tokens per workgroup");
+    __shared__ __attribute__((aligned(16))) float xs[2][TM][RM_PAD];
     __shared__ __attribute__((aligned(16))) float es[2][64][RM_PAD];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t n0 = (int64_t)blockIdx.x * 64, t0 = (int64_t)blockIdx.y * 64;
-    // staging: thread tid copies row tid / 4, elements (tid % 4) * 8 .. +7
+    const int64_t n0 = (int64_t)blockIdx.x * 64, t0 = (int64_t)blockIdx.y * TM;
+    // staging: thread tid copies token row tid / 4 and, in waves 0-3, expert
+    // row tid / 4, elements (tid % 4) * 8 .. +7
+    const bool stage_e = tid < 256;
     const int srow = tid >> 2, sk = (tid & 3) * 8;
     const int64_t st = t0 + srow < T ? t0 + srow : T - 1;  // clamped: never stored
-    const int64_t sn = n0 + srow < N ? n0 + srow : N - 1;
+    const int64_t sn = n0 + (srow & 63) < N ? n0 + (srow & 63) : N - 1;
     constexpr int XW = 8 * (int)sizeof(XT) / 4;
     uint32_t xw[XW];
     float ev[8];
@@ -250,16 +245,18 @@ __global__ void __launch_bounds__(256) router_logits_mfma_kernel(const XT* __res
         const float* er = E + sn * d + k;
         if (FULL) {
             __builtin_memcpy(xw, xr, sizeof(xw));
-            const float4 a = *(const float4*)er;
-            const float4 b = *(const float4*)(er + 4);
-            ev[0] = a.x; ev[1] = a.y; ev[2] = a.z; ev[3] = a.w;
-            ev[4] = b.x; ev[5] = b.y; ev[6] = b.z; ev[7] = b.w;
+            if (stage_e) {
+                const float4 a = *(const float4*)er;
+                const float4 b = *(const float4*)(er + 4);
+                ev[0] = a.x; ev[1] = a.y; ev[2] = a.z; ev[3] = a.w;
+                ev[4] = b.x; ev[5] = b.y; ev[6] = b.z; ev[7] = b.w;
+            }
         } else {
             XT v[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 v[i] = k + i < d ? xr[i] : XT(0);
-                ev[i] = k + i < d ? er[i] : 0.0f;
+                if (stage_e) ev[i] = k + i < d ? er[i] : 0.0f;
             }
             __builtin_memcpy(xw, v, sizeof(xw));
         }
@@ -275,8 +272,10 @@ __global__ void __launch_bounds__(256) router_logits_mfma_kernel(const XT* __res
         }
         *(float4*)&xs[buf][srow][sk] = make_float4(xv[0], xv[1], xv[2], xv[3]);
         *(float4*)&xs[buf][srow][sk + 4] = make_float4(xv[4], xv[5], xv[6], xv[7]);
-        *(float4*)&es[buf][srow][sk] = make_float4(ev[0], ev[1], ev[2], ev[3]);
-        *(float4*)&es[buf][srow][sk + 4] = make_float4(ev[4], ev[5], ev[6], ev[7]);
+        if (stage_e) {
+            *(float4*)&es[buf][srow][sk] = make_float4(ev[0], ev[1], ev[2], ev[3]);
+            *(float4*)&es[buf][srow][sk + 4] = make_float4(ev[4], ev[5], ev[6], ev[7]);
+        }
     };
 
     const int b = lane >> 4, r = lane & 15;
@@ -706,6 +705,27 @@ static void launch_logits(int32_t act_dtype, bool full, const void* x, const flo
     }
 }
 
+template <int TM>
+static void launch_logits_mfma(int32_t act_dtype, bool full, const void* x, const float* centroids,
+                               float* scores, int64_t T, int64_t d, int64_t N, hipStream_t st) {
+    const dim3 g((unsigned)cdiv(N, 64), (unsigned)cdiv(T, TM));
+    if (act_dtype == MOE_BF16) {
+        if (full)
+            router_logits_mfma_kernel<uint16_t, true, TM><<<g, TM * 4, 0, st>>>(
+                (const uint16_t*)x, centroids, scores, T, d, N);
+        else
+            router_logits_mfma_kernel<uint16_t, false, TM><<<g, TM * 4, 0, st>>>(
+                (const uint16_t*)x, centroids, scores, T, d, N);
+    } else {
+        if (full)
+            router_logits_mfma_kernel<float, true, TM><<<g, TM * 4, 0, st>>>(
+                (const float*)x, centroids, scores, T, d, N);
+        else
+            router_logits_mfma_kernel<float, false, TM><<<g, TM * 4, 0, st>>>(
+                (const float*)x, centroids, scores, T, d, N);
+    }
+}
+
 hipError_t launch_route(const moe_cfg& c, const void* x, const float* centroids,
                         const float* bias, float* scores, int32_t* idx, float* gate,
                         int32_t* counts, hipStream_t st) {
@@ -714,11 +734,11 @@ hipError_t launch_route(const moe_cfg& c, const void* x, const float* centroids,
         fill_i32_kernel<<<dim3((unsigned)cdiv(N, 256)), 256, 0, st>>>(counts, N, 0);
         return hipGetLastError();
     }
-    // Each (token, expert) logit is one serial chain over d, so the tile per
-    // thread trades chains (latency hiding) against workgroups (parallelism):
-    // 4 tokens per thread for large batches (two workgroups per CU at
-    // 8192 x 256), fewer for smaller ones, and one chain per lane for
-    // decode-sized batches.
+    // Each (token, expert) logit is one serial chain over d, so the tile
+    // trades chains (latency hiding) against workgroups (parallelism): the
+    // matrix-core kernel for large batches (its instruction advances 1024
+    // chains by one step), 2 or 1 token(s) per thread on the VALU for
+    // mid-sized ones, and one chain per lane for decode-sized batches.
     const bool full = d % RL_BK == 0;
     if (cdiv(N, RL_TN) * cdiv(T, 64) < 64) {
         // decode-sized batch: one chain per lane
@@ -740,22 +760,10 @@ hipError_t launch_route(const moe_cfg& c, const void* x, const float* centroids,
                     (const float*)x, centroids, scores, T, d, N);
         }
     } else if (cdiv(N, RL_TN) * cdiv(T, 16 * 4) >= 384) {
-        const dim3 gm((unsigned)cdiv(N, 64), (unsigned)cdiv(T, 64));
-        if (c.act_dtype == MOE_BF16) {
-            if (full)
-                router_logits_mfma_kernel<uint16_t, true><<<gm, 256, 0, st>>>(
-                    (const uint16_t*)x, centroids, scores, T, d, N);
-            else
-                router_logits_mfma_kernel<uint16_t, false><<<gm, 256, 0, st>>>(
-                    (const uint16_t*)x, centroids, scores, T, d, N);
-        } else {
-            if (full)
-                router_logits_mfma_kernel<float, true><<<gm, 256, 0, st>>>(
-                    (const float*)x, centroids, scores, T, d, N);
-            else
-                router_logits_mfma_kernel<float, false><<<gm, 256, 0, st>>>(
-                    (const float*)x, centroids, scores, T, d, N);
-        }
+        if (cdiv(N, 64) * cdiv(T, 128) >= 256)
+            launch_logits_mfma<128>(c.act_dtype, full, x, centroids, scores, T, d, N, st);
+        else
+            launch_logits_mfma<64>(c.act_dtype, full, x, centroids, scores, T, d, N, st);
     }
     else if (cdiv(N, RL_TN) * cdiv(T, 16 * 2) >= 192)
         launch_logits<2>(c.act_dtype, full, x, centroids, scores, T, d, N, st);

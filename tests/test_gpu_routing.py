@@ -5,7 +5,8 @@ whose keys are NaN.
 The launcher picks the logits kernel by batch size (a serial fp32 chain per
 (token, expert) pair, so the tile per thread trades chains against
 workgroups): one chain per lane when cdiv(N,64)*cdiv(T,64) < 64, the
-matrix-core kernel (one contraction-1 MFMA per k) from 384 64x64 tiles on,
+matrix-core kernel (one contraction-1 MFMA per k) from 384 64x64 tiles on
+(128-token tiles while they still number 256 or more),
 else 2 or 1 token(s) per thread (TY) on the VALU by the number of workgroups
 each gives; FULL instances need d % 32 == 0 (tiled) or d % 256 == 0 (one
 chain per lane), the others pad the last stage.  Scores, indices, gates and
@@ -55,14 +56,16 @@ def _route_gpu(T, d, N, k, G, TG, dtype, inp):
 ROUTE_CASES = [
     (1024, 7168, 256, 8, 8, 4, "bf16"),   # tiled, 1 token per thread
     (2048, 7168, 256, 8, 8, 4, "bf16"),   # tiled, 2 tokens per thread
-    (8192, 7176, 256, 8, 8, 4, "bf16"),   # matrix cores, d % 32 != 0
-    (6200, 512, 250, 8, 1, 1, "bf16"),    # matrix cores, ragged tokens and experts
+    (8192, 7176, 256, 8, 8, 4, "bf16"),   # matrix cores, 128-token tile, d % 32 != 0
+    (6200, 512, 250, 8, 1, 1, "bf16"),    # matrix cores, 64-token tile, ragged tokens and experts
     (2048, 1000, 256, 8, 1, 1, "bf16"),   # tiled, 2 tokens per thread, d % 32 != 0
     (1024, 1000, 256, 6, 1, 1, "bf16"),   # tiled, 1 token per thread, d % 32 != 0
     (4096, 1000, 64, 8, 1, 1, "f32"),     # fp32 x: tiled, 1 token per thread, d % 32 != 0
     (8192, 512, 64, 8, 1, 1, "f32"),      # fp32 x: tiled, 2 tokens per thread
-    (32768, 256, 64, 4, 1, 1, "f32"),     # fp32 x: matrix cores
-    (24576, 1000, 64, 8, 1, 1, "f32"),    # fp32 x: matrix cores, d % 32 != 0
+    (32768, 256, 64, 4, 1, 1, "f32"),     # fp32 x: matrix cores, 128-token tile
+    (32768, 1000, 64, 4, 1, 1, "f32"),    # fp32 x: matrix cores, 128-token tile, d % 32 != 0
+    (24576, 1000, 64, 8, 1, 1, "f32"),    # fp32 x: matrix cores, 64-token tile, d % 32 != 0
+    (24576, 512, 64, 8, 1, 1, "f32"),     # fp32 x: matrix cores, 64-token tile
     (128, 1000, 256, 8, 1, 1, "bf16"),    # one chain per lane, d % 256 != 0
     (100, 7168, 256, 8, 8, 4, "bf16"),    # one chain per lane, ragged tokens
 ]
