@@ -132,6 +132,10 @@ constexpr int G_WRG = G_WAVES / 2;        // weight-row groups
 #ifndef MOE_GEMM_NS
 #define MOE_GEMM_NS 2
 #endif
+// token fragments read ahead of their MFMAs in the scheduled step sequence
+#ifndef MOE_GEMM_LA
+#define MOE_GEMM_LA 5
+#endif
 // contraction elements per LDS sub-tile: one step up to 64 (rows of 2*G_SUB
 // bytes), and the 16-byte chunks per row with their bank-spreading swizzle
 constexpr int G_SUB = MOE_GEMM_BK < 64 ? MOE_GEMM_BK : 64;
@@ -197,6 +201,19 @@ __global__ void __launch_bounds__(256) pack_weights_t_kernel(const uint16_t* __r
     out[i] = make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// 16-byte-per-lane global -> LDS copy (lane i's bytes land at lds + 16 i).
+// Written as asm so that the compiler's waitcnt bookkeeping does not see it:
+// a pending builtin LDS-DMA copy counts there as an LDS access of unknown
+// order, after which every wait for an LDS fragment read becomes lgkmcnt(0),
+// i.e. for all reads in flight, and reads cannot run ahead of the MFMAs.
+// The caller waits for the copies itself (vmcnt), also before the LDS is
+// reused.  Five wait states first: the M0 and address set-up just before may
+// come from VALU-written SGPRs.
+__device__ __forceinline__ void copy16_to_lds(const void* g, const void* lds) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)lds;
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0) : "memory");
+}
+
 template <int MODE, int BK, int NS, int NB>
 __device__ __forceinline__ void gemm_bf16_body(const WorkV2& w, uint16_t* smem) {
     constexpr int NSUB = BK / G_SUB;
@@ -249,16 +266,14 @@ __device__ __forceinline__ void gemm_bf16_body(const WorkV2& w, uint16_t* smem) 
 #pragma unroll
         for (int j = 0; j < PA; ++j) {
             const int b = wave + G_WAVES * j;
-            __builtin_amdgcn_global_load_lds((const void*)(wsrc + b * 1024 + woff),
-                                             to_lds(As + b * 512), 16, 0, 0);
+            copy16_to_lds((const void*)(wsrc + b * 1024 + woff), As + b * 512);
         }
 #pragma unroll
         for (int j = 0; j < PX; ++j) {
             const int b = wave + G_WAVES * j;
             if (b < nxe)
-                __builtin_amdgcn_global_load_lds(
-                    (const void*)(xsrc + xoff[j]),
-                    to_lds(Xs + (b % NSUB) * G_TR * G_SUB + (b / NSUB) * 512), 16, 0, 0);
+                copy16_to_lds((const void*)(xsrc + xoff[j]),
+                              Xs + (b % NSUB) * G_TR * G_SUB + (b / NSUB) * 512);
         }
     };
 
@@ -275,8 +290,75 @@ __device__ __forceinline__ void gemm_bf16_body(const WorkV2& w, uint16_t* smem) 
 #pragma unroll
     for (int s = 0; s < G_SUB / 32; ++s) coff[s] = g_swz(l16, 4 * s + g) * 8;
 
+    // One step as one scheduled sequence, weight-fragment-major: pass i of a
+    // 32-wide substep multiplies weight fragment i with all NB token
+    // fragments, so the first MFMA of a substep waits for two reads, not five.
+    // Reads are held (sched_group_barrier) to [A0, X0..X(L-1), A1] up front,
+    // then one per MFMA of pass 0 (X(L).., A2, A3); pass 3 of a substep
+    // issues the next substep's first reads into the registers its own MFMAs
+    // have just freed.  Each MFMA then waits only for the reads it uses
+    // (partial lgkmcnt waits), and the other wave of the SIMD fills the rest.
+    // The products and their order per accumulator are those of the plain
+    // loop below (k ascending), so the results are the same bits.
+    constexpr int LA = MOE_GEMM_LA;
+    auto compute_seq = [&](auto sidx) {  // generic: instantiated only when NB >= LA
+        constexpr int SUBS = BK / 32;
+        const uint16_t* As = stage_a(sidx);
+        const uint16_t* Xs = stage_x(sidx);
+        bf16x8_t af[SUBS][4], xf[SUBS][NBB];
+        auto rda = [&](int s, int i) {
+            const int q = s / (G_SUB / 32);
+            return __builtin_bit_cast(bf16x8_t, *(const uint4*)(As + q * G_WR * G_SUB +
+                (wr * 64 + i * 16 + l16) * G_SUB + coff[s % (G_SUB / 32)]));
+        };
+        auto rdx = [&](int s, int j) {
+            const int q = s / (G_SUB / 32);
+            return __builtin_bit_cast(bf16x8_t, *(const uint4*)(Xs + q * G_TR * G_SUB +
+                (tg * 160 + j * 16 + l16) * G_SUB + coff[s % (G_SUB / 32)]));
+        };
+#pragma unroll
+        for (int s = 0; s < SUBS; ++s) {
+            af[s][0] = rda(s, 0);
+#pragma unroll
+            for (int j = 0; j < LA; ++j) xf[s][j] = rdx(s, j);
+            af[s][1] = rda(s, 1);
+#pragma unroll
+            for (int j = LA; j < NB; ++j) xf[s][j] = rdx(s, j);
+            af[s][2] = rda(s, 2);
+            af[s][3] = rda(s, 3);
+        }
+#pragma unroll
+        for (int s = 0; s < SUBS; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s][i], xf[s][j], acc[i][j], 0, 0, 0);
+        constexpr int R0 = LA + 2;       // reads before the first MFMA of a substep
+        constexpr int RP = NB - LA + 2;  // reads of a substep during its pass 0
+        __builtin_amdgcn_sched_group_barrier(0x100, R0, 0);  // 0x100: LDS reads
+#pragma unroll
+        for (int s = 0; s < SUBS; ++s) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 0x008: MFMA
+                if (j < RP) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            if constexpr (RP > NB) __builtin_amdgcn_sched_group_barrier(0x100, RP - NB, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * NB, 0);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (s + 1 < SUBS && j < R0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            if constexpr (R0 > NB)
+                if (s + 1 < SUBS) __builtin_amdgcn_sched_group_barrier(0x100, R0 - NB, 0);
+        }
+    };
     auto compute = [&](int sidx) {
-        if constexpr (NB > 0) {
+        if constexpr (NB >= LA) {
+            compute_seq(sidx);
+        } else if constexpr (NB > 0) {
             const uint16_t* As = stage_a(sidx);
             const uint16_t* Xs = stage_x(sidx);
 #pragma unroll
@@ -308,7 +390,9 @@ __device__ __forceinline__ void gemm_bf16_body(const WorkV2& w, uint16_t* smem) 
         // later stages, cnt each
         const int after = nk - 1 - kt < NS - 2 ? nk - 1 - kt : NS - 2;
         vm_wait_n(after * cnt);
-        __syncthreads();  // stage kt landed for every wave; stage kt-1 is free
+        // this wave's copies of stage kt have landed (its own vmcnt); the
+        // barrier makes that true for every wave, and stage kt-1 is free
+        lds_barrier();
         if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
         compute(kt % NS);
     }
@@ -318,6 +402,7 @@ __device__ __forceinline__ void gemm_bf16_body(const WorkV2& w, uint16_t* smem) 
     // once; down writes 256 y columns in two passes (token halves).  LDS rows
     // are padded by 16 bytes so the 16 rows written by a lane group hit
     // distinct banks.
+    vm_wait<0>();     // no copy of this wave in flight (the asm copies are not tracked)
     __syncthreads();  // every wave is done with the stage buffers
     constexpr bool GU = MODE == 0 || MODE == 2;  // gate/up-shaped tile
     constexpr int OCOLS = GU ? 128 : 256;
