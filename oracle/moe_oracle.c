@@ -553,6 +553,51 @@ void orc_bias_update(int64_t N, int64_t TK, const int32_t* counts, float gamma, 
     }
 }
 
+/* ---------------------------------------------------------------------- */
+/* sequence-wise balance loss   [P4] "Methode" item 2, last sentence        */
+/* ---------------------------------------------------------------------- */
+
+/* The pages name a minimal sequence-wise balance loss (alpha = 0.0001) that
+ * complements the bias rule by keeping any single sequence away from extreme
+ * imbalance, and the issoh.co.jp page describes the conventional auxiliary
+ * loss as a penalty on inputs crowding onto particular experts; neither
+ * prints a formula.  Reading (parity unpinned by the pages): the batch is
+ * T / S sequences of S consecutive tokens, and for sequence b
+ *   f_i = N / (k S) * #{(t, j) : t in b, idx[t][j] = i}   (load relative to
+ *         the uniform share k S / N, the same load the bias rule compares)
+ *   P_i = (1 / S) * sum_{t in b} s_{i,t} / sum_{j<N} s_{j,t}   (mean affinity
+ *         of expert i, normalised over all N experts per token)
+ *   loss[b] = alpha * sum_i f_i P_i.
+ * Every sum in double, in index order; loss[b] rounded once to fp32.  With
+ * equal affinities the loss is alpha whatever the routing; with every token
+ * on the same k experts holding all of its affinity it is alpha * N / k. */
+void orc_seq_balance_loss(int64_t T, int64_t N, int64_t k, int64_t S, float alpha,
+                          const float* scores, const int32_t* idx, float* loss) {
+    int64_t B = T / S;
+    double* P = (double*)malloc((size_t)N * sizeof(double));
+    int64_t* cnt = (int64_t*)malloc((size_t)N * sizeof(int64_t));
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t i = 0; i < N; ++i) {
+            P[i] = 0.0;
+            cnt[i] = 0;
+        }
+        for (int64_t t = b * S; t < (b + 1) * S; ++t) {
+            double row = 0.0;
+            for (int64_t i = 0; i < N; ++i) row += (double)scores[t * N + i];
+            for (int64_t i = 0; i < N; ++i) P[i] += (double)scores[t * N + i] / row;
+            for (int64_t j = 0; j < k; ++j) cnt[idx[t * k + j]] += 1;
+        }
+        double sum = 0.0;
+        for (int64_t i = 0; i < N; ++i) {
+            double f = (double)N / ((double)k * (double)S) * (double)cnt[i];
+            sum += f * (P[i] / (double)S);
+        }
+        loss[b] = (float)((double)alpha * sum);
+    }
+    free(P);
+    free(cnt);
+}
+
 /* ====================================================================== */
 /* backward pass of the layer                                              */
 /* ====================================================================== */

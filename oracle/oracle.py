@@ -75,6 +75,7 @@ def _declare(L):
         "orc_ffn_down_fp8": [I64, I64, I64, P, P, P, P, P],
         "orc_combine": [I64, I64, I64, I, P, P, P, P, P, P],
         "orc_bias_update": [I64, I64, P, F, P],
+        "orc_seq_balance_loss": [I64, I64, I64, I64, F, P, P, P],
         "orc_round_to_dtype": [I64, I, P, P],
         "orc_combine_backward": [I64, I64, I64, I, P, P, P, P, P, P],
         "orc_swiglu_ffn_backward": [I64, I64, I64, I, P, P, P, P, P, P, P],
@@ -343,6 +344,21 @@ def bias_update(counts, tokens_times_k, bias, gamma=GAMMA):
     lib().orc_bias_update(counts.size, int(tokens_times_k), _p(counts),
                           ctypes.c_float(float(gamma)), _p(b))
     return b
+
+
+def seq_balance_loss(scores, idx, seq_len, alpha=1e-4):
+    """Per-sequence balance loss [T / seq_len] fp32 of moe_oracle.c's reading
+    (sequences of seq_len consecutive tokens; alpha taken as fp32)."""
+    scores = _c(scores, np.float32)
+    idx = _c(idx, np.int32)
+    T, N = scores.shape
+    k = idx.shape[1]
+    if seq_len < 1 or T % seq_len:
+        raise ValueError("T must be a multiple of seq_len")
+    out = np.empty(T // seq_len, np.float32)
+    lib().orc_seq_balance_loss(T, N, k, int(seq_len), ctypes.c_float(float(alpha)),
+                               _p(scores), _p(idx), _p(out))
+    return out
 
 
 def round_to_dtype(v, dtype):

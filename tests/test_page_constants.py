@@ -44,3 +44,10 @@ def test_v3_shape_matches_pages():
     c = moe_inputs.CONFIGS["v3_bf16"]
     assert c["N"] == g["n_routed"]["value"] and c["k"] == g["n_active"]["value"]
     assert moe_inputs.CONFIGS["v3_fp8"]["N"] == g["n_routed"]["value"]
+
+
+def test_seq_balance_alpha(orc):
+    # the default coefficient of the sequence-wise balance loss is the pages' alpha
+    import inspect
+    a = inspect.signature(orc.seq_balance_loss).parameters["alpha"].default
+    assert a == _g()["seq_balance_alpha"]["value"]
