@@ -245,6 +245,28 @@ int moe_combine(const moe_cfg* cfg, const void* x_residual, const void* y_shared
 int moe_bias_update(int64_t n_experts, int64_t tokens_times_k, const int32_t* counts,
                     float gamma, float* bias, void* stream);
 
+/* -------------------------------------------------- sequence-wise balance loss */
+
+/* The minimal sequence-wise balance loss (alpha = 0.0001) that the reading
+ * guide's "Methode" item 2 names, in its last sentence, as a complement to
+ * the bias rule, evaluated as a forward statistic.  The pages print no
+ * formula; the reading taken: the batch is tokens / seq_len sequences of
+ * seq_len consecutive tokens, and for sequence b
+ *   loss[b] = alpha * sum_i f_i P_i,
+ *   f_i = N / (top_k seq_len) * (number of the sequence's idx entries == i),
+ *   P_i = (1 / seq_len) * sum_t scores[t][i] / sum_j scores[t][j].
+ * scores [T, N] fp32: the affinities s_{i,t} (moe_route's scores output);
+ * idx [T, top_k] int32 from moe_route (entries outside 0..N-1 are not
+ * counted); loss [T / seq_len] fp32 out.  Sums in double in a fixed order,
+ * one rounding to fp32, the same bits on every run.  Uses tokens, n_experts
+ * and top_k of cfg.  Errors: MOE_ERR_ARG when seq_len < 1, tokens is not a
+ * multiple of seq_len or alpha is NaN; MOE_ERR_WORKSPACE when workspace_bytes
+ * is below moe_seq_balance_loss_workspace_size(cfg, seq_len). */
+size_t moe_seq_balance_loss_workspace_size(const moe_cfg* cfg, int64_t seq_len);
+int moe_seq_balance_loss(const moe_cfg* cfg, int64_t seq_len, float alpha, const float* scores,
+                         const int32_t* idx, float* loss, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 /* ----------------------------------------------------------- preparation */
 
 /* Off the per-step path: 128x128 block quantisation of n_mats bf16 matrices

@@ -7,7 +7,8 @@ for device memory and streams only.  There is no fallback: if ``libmoe.so`` is
 missing, importing the functions fails loudly.
 
 The functions carry the C names: moe_route, moe_permute, moe_expert_ffn,
-moe_combine, moe_bias_update, moe_quantize_weights_fp8, the backward calls of
+moe_combine, moe_bias_update, moe_seq_balance_loss, moe_quantize_weights_fp8,
+the backward calls of
 include/moe_backward.h (moe_expert_ffn_train, moe_combine_backward,
 moe_expert_ffn_backward, moe_expert_ffn_train_fp8, moe_expert_ffn_backward_fp8,
 moe_route_backward, moe_input_grad), the FFN inspection calls of
@@ -75,6 +76,8 @@ def lib():
             "moe_packed_weights_size": ([C, ctypes.c_int], SZ),
             "moe_pack_weights": ([C, ctypes.c_int, P, P, P], ctypes.c_int),
             "moe_bias_update": ([I64, I64, P, F, P, P], ctypes.c_int),
+            "moe_seq_balance_loss_workspace_size": ([C, I64], SZ),
+            "moe_seq_balance_loss": ([C, I64, F, P, P, P, P, SZ, P], ctypes.c_int),
             "moe_quantize_weights_fp8": ([I64, I64, I64, P, P, P, P], ctypes.c_int),
             "moe_combine_backward": ([C, P, P, P, P, P, P, P], ctypes.c_int),
             "moe_expert_ffn_backward_workspace_size": ([C], SZ),
@@ -248,6 +251,16 @@ def moe_combine(cfg, x_residual, y_shared, y_perm, gate, dst_row, out, stream=No
 def moe_bias_update(n_experts, tokens_times_k, counts, gamma, bias, stream=None):
     _check(lib().moe_bias_update(int(n_experts), int(tokens_times_k), _p(counts),
                                  ctypes.c_float(float(gamma)), _p(bias), _stream(stream)))
+
+
+def moe_seq_balance_loss_workspace_size(cfg, seq_len):
+    return int(lib().moe_seq_balance_loss_workspace_size(ctypes.byref(cfg), int(seq_len)))
+
+
+def moe_seq_balance_loss(cfg, seq_len, alpha, scores, idx, loss, workspace=None, stream=None):
+    _check(lib().moe_seq_balance_loss(ctypes.byref(cfg), int(seq_len), ctypes.c_float(float(alpha)),
+                                      _p(scores), _p(idx), _p(loss), _p(workspace),
+                                      _nbytes(workspace), _stream(stream)))
 
 
 def moe_quantize_weights_fp8(n_mats, rows, cols, w_bf16, w_q, w_scale, stream=None):

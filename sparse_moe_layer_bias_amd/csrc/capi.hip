@@ -118,7 +118,7 @@ int set_error(int code, const char* msg) {
 
 extern "C" {
 
-int moe_abi_version(void) { return 6; }
+int moe_abi_version(void) { return 7; }
 
 const char* moe_last_error(void) { return g_err; }
 
@@ -497,6 +497,35 @@ int moe_bias_update(int64_t n_experts, int64_t tokens_times_k, const int32_t* co
     REQ_PTR(bias);
     return hip_status(fn, moe::launch_bias_update(n_experts, tokens_times_k, counts, gamma, bias,
                                                   (hipStream_t)stream));
+}
+
+size_t moe_seq_balance_loss_workspace_size(const moe_cfg* cfg, int64_t seq_len) {
+    if (!cfg) return 0;
+    return moe::seq_balance_workspace_bytes(cfg->tokens, cfg->n_experts, seq_len);
+}
+
+int moe_seq_balance_loss(const moe_cfg* cfg, int64_t seq_len, float alpha, const float* scores,
+                         const int32_t* idx, float* loss, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    const char* fn = "moe_seq_balance_loss";
+    if (int r = check_cfg(fn, cfg)) return r;
+    if (seq_len < 1) return fail(MOE_ERR_ARG, "%s: seq_len must be >= 1", fn);
+    if (cfg->tokens % seq_len)
+        return fail(MOE_ERR_ARG, "%s: tokens=%lld is not a multiple of seq_len=%lld", fn,
+                    (long long)cfg->tokens, (long long)seq_len);
+    if (!(alpha == alpha)) return fail(MOE_ERR_ARG, "%s: alpha is NaN", fn);
+    if (cfg->tokens == 0) return ok();
+    REQ_PTR(scores);
+    REQ_PTR(idx);
+    REQ_PTR(loss);
+    REQ_PTR(workspace);
+    const size_t need = moe_seq_balance_loss_workspace_size(cfg, seq_len);
+    if (workspace_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, workspace_bytes,
+                    need);
+    return hip_status(fn, moe::launch_seq_balance_loss(cfg->tokens, cfg->n_experts, cfg->top_k,
+                                                       seq_len, alpha, scores, idx, loss,
+                                                       workspace, (hipStream_t)stream));
 }
 
 int moe_quantize_weights_fp8(int64_t n_mats, int64_t rows, int64_t cols, const void* w_bf16,

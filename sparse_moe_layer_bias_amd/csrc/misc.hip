@@ -1,5 +1,6 @@
-// misc.hip -- combine (un-permute), end-of-step bias update, and the FP8
-// weight block quantiser used as preparation.
+// misc.hip -- combine (un-permute), end-of-step bias update, the
+// sequence-wise balance loss, and the FP8 weight block quantiser used as
+// preparation.
 #include "moe_internal.h"
 
 namespace moe {
@@ -112,6 +113,112 @@ __global__ void bias_update_kernel(const int32_t* __restrict__ counts, float gam
 hipError_t launch_bias_update(int64_t N, int64_t TK, const int32_t* counts, float gamma,
                               float* bias, hipStream_t st) {
     bias_update_kernel<<<dim3((unsigned)cdiv(N, 256)), 256, 0, st>>>(counts, gamma, bias, N, TK);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- balance loss
+// Sequence-wise balance loss (reading guide "Methode" item 2, last sentence:
+// a minimal sequence-wise balance loss, alpha = 0.0001, beside the bias rule;
+// no formula on the pages).  Reading: per sequence b of S consecutive tokens,
+//   loss[b] = alpha * sum_i f_i P_i,  f_i = N/(kS) * load_i,
+//   P_i = 1/S * sum_t s_{i,t} / sum_j s_{j,t}.
+// Two launches, no atomics on floating values, so the result is the same bits
+// on every run:
+//   partial: block (b, c) takes tokens c*64 .. c*64+63 of sequence b; each
+//     wave walks every 4th of them, lane l holding experts l, l+64, ...; the
+//     token's row sum is a butterfly over the wave (every lane ends with the
+//     same double); the four waves' sums of s/row are added in wave order and
+//     stored as partial[b][c][i] (double);
+//   final: one block per sequence: load_i by an LDS integer histogram of the
+//     sequence's idx, P_i by summing the chunks in order, then a fixed-shape
+//     tree over the block.  Everything in double; one rounding to fp32.
+constexpr int SBL_CH = 64;   // tokens per partial block
+constexpr int SBL_MAXN = 1024;
+
+__global__ void __launch_bounds__(256) seq_balance_partial_kernel(const float* __restrict__ s,
+                                                                  int64_t N, int64_t S, int cps,
+                                                                  double* __restrict__ part) {
+    __shared__ double wsum[4][SBL_MAXN];
+    const int64_t b = blockIdx.x / cps;
+    const int c = blockIdx.x % cps;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t t_end = S < (int64_t)(c + 1) * SBL_CH ? S : (int64_t)(c + 1) * SBL_CH;
+    constexpr int Q = SBL_MAXN / 64;
+    double p[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) p[q] = 0.0;
+    for (int64_t tl = (int64_t)c * SBL_CH + wave; tl < t_end; tl += 4) {
+        const float* row = s + (b * S + tl) * N;
+        float v[Q];
+        double r = 0.0;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int64_t i = q * 64 + lane;
+            v[q] = i < N ? row[i] : 0.0f;
+            r += (double)v[q];
+        }
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) r += __shfl_xor(r, m, 64);
+#pragma unroll
+        for (int q = 0; q < Q; ++q)
+            if (q * 64 + lane < N) p[q] += (double)v[q] / r;
+    }
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+        if (q * 64 + lane < N) wsum[wave][q * 64 + lane] = p[q];
+    __syncthreads();
+    for (int64_t i = threadIdx.x; i < N; i += 256)
+        part[(int64_t)blockIdx.x * N + i] =
+            ((wsum[0][i] + wsum[1][i]) + wsum[2][i]) + wsum[3][i];
+}
+
+__global__ void __launch_bounds__(256) seq_balance_final_kernel(const double* __restrict__ part,
+                                                                const int32_t* __restrict__ idx,
+                                                                int64_t N, int64_t k, int64_t S,
+                                                                int cps, float alpha,
+                                                                float* __restrict__ loss) {
+    __shared__ int32_t cnt[SBL_MAXN];
+    __shared__ double red[256];
+    const int64_t b = blockIdx.x;
+    for (int64_t i = threadIdx.x; i < N; i += 256) cnt[i] = 0;
+    __syncthreads();
+    const int32_t* ib = idx + b * S * k;
+    for (int64_t p = threadIdx.x; p < S * k; p += 256) {
+        const int32_t e = ib[p];
+        if (e >= 0 && e < N) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+    const double fscale = (double)N / ((double)k * (double)S);
+    double acc = 0.0;
+    for (int64_t i = threadIdx.x; i < N; i += 256) {
+        double P = 0.0;
+        for (int c = 0; c < cps; ++c) P += part[(b * cps + c) * N + i];
+        acc += fscale * (double)cnt[i] * (P / (double)S);
+    }
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) loss[b] = (float)((double)alpha * red[0]);
+}
+
+size_t seq_balance_workspace_bytes(int64_t T, int64_t N, int64_t S) {
+    if (S <= 0 || T <= 0) return 0;
+    return (size_t)((T / S) * cdiv(S, SBL_CH) * N * 8);
+}
+
+hipError_t launch_seq_balance_loss(int64_t T, int64_t N, int64_t k, int64_t S, float alpha,
+                                   const float* scores, const int32_t* idx, float* loss,
+                                   void* ws, hipStream_t st) {
+    const int64_t B = T / S;
+    const int cps = (int)cdiv(S, SBL_CH);
+    double* part = (double*)ws;
+    seq_balance_partial_kernel<<<dim3((unsigned)(B * cps)), 256, 0, st>>>(scores, N, S, cps,
+                                                                         part);
+    seq_balance_final_kernel<<<dim3((unsigned)B), 256, 0, st>>>(part, idx, N, k, S, cps, alpha,
+                                                               loss);
     return hipGetLastError();
 }
 

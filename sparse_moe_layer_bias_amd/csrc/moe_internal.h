@@ -201,6 +201,10 @@ hipError_t launch_combine(const moe_cfg& c, const void* x, const void* y_shared,
                           void* out, hipStream_t st);
 hipError_t launch_bias_update(int64_t N, int64_t TK, const int32_t* counts, float gamma,
                               float* bias, hipStream_t st);
+size_t seq_balance_workspace_bytes(int64_t T, int64_t N, int64_t S);
+hipError_t launch_seq_balance_loss(int64_t T, int64_t N, int64_t k, int64_t S, float alpha,
+                                   const float* scores, const int32_t* idx, float* loss,
+                                   void* ws, hipStream_t st);
 hipError_t launch_quantize_weights(int64_t n_mats, int64_t rows, int64_t cols, const void* w,
                                    uint8_t* q, float* s, hipStream_t st);
 hipError_t launch_e4m3_inspect(const float* v, int64_t n, float scale, uint8_t* c4, uint8_t* c1,

@@ -23,7 +23,8 @@ from . import (MoeCfg, cfg_from_dict, moe_bias_update, moe_combine, moe_combine_
                moe_expert_ffn_workspace_size, moe_input_grad, moe_pack_weights,
                moe_packed_weights_size, moe_permute, moe_permute_workspace_size,
                moe_quantize_weights_fp8, moe_route, moe_route_backward,
-               moe_route_backward_workspace_size, moe_route_workspace_size)
+               moe_route_backward_workspace_size, moe_route_workspace_size,
+               moe_seq_balance_loss, moe_seq_balance_loss_workspace_size)
 
 GAMMA = 0.001  # end-of-step bias step (reading guide, "Methode" item 2)
 
@@ -172,6 +173,18 @@ class MoeLayer:
     def route(self, x, centroids, bias, stream=None):
         moe_route(self.cfg, x, centroids, bias, self.scores, self.idx, self.gate, self.counts,
                   None, stream)
+
+    def seq_balance_loss(self, seq_len, alpha=1e-4, stream=None):
+        """The sequence-wise balance loss of this step's routing (moe_seq_balance_loss:
+        one fp32 value per sequence of seq_len consecutive tokens), from the
+        affinities and indices of the last route()."""
+        T = self.c["T"]
+        loss = torch.empty(T // seq_len if seq_len > 0 else 0, dtype=torch.float32,
+                           device=self.scores.device)
+        ws = torch.empty(max(moe_seq_balance_loss_workspace_size(self.cfg, seq_len), 16),
+                         dtype=torch.uint8, device=self.scores.device)
+        moe_seq_balance_loss(self.cfg, seq_len, alpha, self.scores, self.idx, loss, ws, stream)
+        return loss
 
     def permute(self, x, stream=None):
         moe_permute(self.cfg, x, self.idx, self.offsets, self.src_token, self.dst_row,

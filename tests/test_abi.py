@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
             "moe_route_backward", "moe_input_grad"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert moe.moe_abi_version() == 6
+    assert moe.moe_abi_version() == 7
 
 
 @host_only
@@ -163,6 +163,28 @@ def test_bias_update_and_quantize_validation():
         moe.MOE_ERR_ARG
     assert L.moe_quantize_weights_fp8(1, 100, 128, P(FAKE), P(FAKE), P(FAKE), None) == \
         moe.MOE_ERR_ARG
+
+
+@host_only
+def test_seq_balance_loss_validation():
+    L = moe.lib()
+    P = ctypes.c_void_p
+    cfg = _cfg(T=64, N=16, k=2)
+    need = moe.moe_seq_balance_loss_workspace_size(cfg, 16)
+    # 4 sequences x 1 chunk of up to 64 tokens x 16 experts, doubles
+    assert need == 4 * 16 * 8
+
+    def call(seq_len, alpha=1e-4, ws_bytes=need, scores=FAKE, c=cfg):
+        return L.moe_seq_balance_loss(ctypes.byref(c), seq_len, ctypes.c_float(alpha),
+                                      P(scores) if scores else None, P(FAKE), P(FAKE), P(FAKE),
+                                      ws_bytes, None)
+    assert call(0) == moe.MOE_ERR_ARG                  # seq_len < 1
+    assert call(10) == moe.MOE_ERR_ARG                 # 64 tokens are not whole sequences of 10
+    assert call(16, alpha=float("nan")) == moe.MOE_ERR_ARG
+    assert call(16, scores=0) == moe.MOE_ERR_ARG       # NULL scores
+    assert call(16, scores=FAKE + 4) == moe.MOE_ERR_ARG  # misaligned
+    assert call(16, ws_bytes=need - 1) == moe.MOE_ERR_WORKSPACE
+    assert call(16, c=_cfg(T=0, N=16, k=2)) == moe.MOE_OK  # nothing to do
 
 
 # ------------------------------------------------------------------ backward
