@@ -937,6 +937,35 @@ def time_forward(layer, x, E, bias, steps, warmup):
     return ms_per_step, stage_ms
 
 
+def time_seq_balance_loss(layer, seq_len, reps=20):
+    """The sequence-wise balance loss of the last routed step (moe_seq_balance_loss),
+    timed with HIP events over `reps` calls on the stream it runs on."""
+    import torch
+    from sparse_moe_layer_bias_amd import (moe_seq_balance_loss,
+                                           moe_seq_balance_loss_workspace_size)
+    T, N, k = layer.c["T"], layer.c["N"], layer.c["k"]
+    if T % seq_len:
+        return None
+    dev = layer.scores.device
+    loss = torch.empty(T // seq_len, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(moe_seq_balance_loss_workspace_size(layer.cfg, seq_len), 16),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    moe_seq_balance_loss(layer.cfg, seq_len, 1e-4, layer.scores, layer.idx, loss, ws)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        moe_seq_balance_loss(layer.cfg, seq_len, 1e-4, layer.scores, layer.idx, loss, ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    nbytes = T * N * 4 + T * k * 4
+    return {"seq_len": seq_len, "alpha": 1e-4, "us_per_call": us,
+            "read_GBps": nbytes / (us * 1e-6) / 1e9, "loss": [float(v) for v in loss.cpu()]}
+
+
 def ffn_roofline(cfg, ffn_s, workload):
     """The expert FFN call (both grouped GEMM launches and the tile map) against
     the roofline that bounds its algorithmic work: the larger of the time at
@@ -1064,6 +1093,9 @@ def main():
         "stages_ms": stage_ms,
         "layer_tflops": (flops + 2.0 * T * cfg["d"] * cfg["N"]) / (ms_per_step / 1e3) / 1e12,
     }
+    # the sequence-wise balance loss of the step's routing (sequences of 4096
+    # tokens), a statistic beside the step, not part of its time
+    result["seq_balance_loss"] = time_seq_balance_loss(layer, min(4096, T))
     if not args.no_cpu_baseline:
         try:
             result["cpu_baseline"] = cpu_baseline(cfg, dev, log)

@@ -125,77 +125,122 @@ hipError_t launch_bias_update(int64_t N, int64_t TK, const int32_t* counts, floa
 // Two launches, no atomics on floating values, so the result is the same bits
 // on every run:
 //   partial: block (b, c) takes tokens c*64 .. c*64+63 of sequence b; each
-//     wave walks every 4th of them, lane l holding experts l, l+64, ...; the
-//     token's row sum is a butterfly over the wave (every lane ends with the
-//     same double); the four waves' sums of s/row are added in wave order and
-//     stored as partial[b][c][i] (double);
-//   final: one block per sequence: load_i by an LDS integer histogram of the
-//     sequence's idx, P_i by summing the chunks in order, then a fixed-shape
-//     tree over the block.  Everything in double; one rounding to fp32.
+//     wave walks 16 of them, four at a time (all four rows' loads in flight
+//     together), lane l holding experts l, l+64, ...; a token's row sum is a
+//     butterfly over the wave (every lane ends with the same double); the four
+//     waves' sums of s/row are added in wave order and stored as
+//     part[b][c][i] (double), the chunk's load of each expert (an LDS integer
+//     histogram of its idx entries) as cnt[b][c][i];
+//   final: one block of 1024 threads per sequence; thread (g, i) adds the
+//     chunks c = g, g+4, ... of expert i, the four groups are added in group
+//     order, then f_i P_i goes through a fixed-shape tree.  Everything in
+//     double; one rounding to fp32.
 constexpr int SBL_CH = 64;   // tokens per partial block
+constexpr int SBL_TB = 4;    // tokens per wave in flight together
 constexpr int SBL_MAXN = 1024;
 
+template <int Q>  // Q = cdiv(N, 64) expert slots per lane
 __global__ void __launch_bounds__(256) seq_balance_partial_kernel(const float* __restrict__ s,
-                                                                  int64_t N, int64_t S, int cps,
-                                                                  double* __restrict__ part) {
+                                                                  const int32_t* __restrict__ idx,
+                                                                  int64_t N, int64_t k, int64_t S,
+                                                                  int cps, double* __restrict__ part,
+                                                                  int32_t* __restrict__ cnt) {
     __shared__ double wsum[4][SBL_MAXN];
+    __shared__ int32_t hist[SBL_MAXN];
     const int64_t b = blockIdx.x / cps;
     const int c = blockIdx.x % cps;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t t_end = S < (int64_t)(c + 1) * SBL_CH ? S : (int64_t)(c + 1) * SBL_CH;
-    constexpr int Q = SBL_MAXN / 64;
+    const int64_t t0 = (int64_t)c * SBL_CH;
+    const int64_t t_end = S < t0 + SBL_CH ? S : t0 + SBL_CH;
+    for (int64_t i = threadIdx.x; i < N; i += 256) hist[i] = 0;
+    __syncthreads();
+    // the chunk's idx entries (token-major, so the chunk is one contiguous run)
+    const int32_t* ib = idx + (b * S + t0) * k;
+    for (int64_t p = threadIdx.x; p < (t_end - t0) * k; p += 256) {
+        const int32_t e = ib[p];
+        if (e >= 0 && e < N) atomicAdd(&hist[e], 1);
+    }
     double p[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) p[q] = 0.0;
-    for (int64_t tl = (int64_t)c * SBL_CH + wave; tl < t_end; tl += 4) {
-        const float* row = s + (b * S + tl) * N;
-        float v[Q];
-        double r = 0.0;
+    // wave w takes tokens t0 + 16w .. t0 + 16w + 15, four at a time
+    for (int64_t tb = t0 + wave * (SBL_CH / 4); tb < t0 + (wave + 1) * (SBL_CH / 4) && tb < t_end;
+         tb += SBL_TB) {
+        float v[SBL_TB][Q];
+        double r[SBL_TB];
 #pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            const int64_t i = q * 64 + lane;
-            v[q] = i < N ? row[i] : 0.0f;
-            r += (double)v[q];
+        for (int u = 0; u < SBL_TB; ++u) {
+            const float* row = s + (b * S + tb + u) * N;
+            const bool tok = tb + u < t_end;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                const int64_t i = q * 64 + lane;
+                v[u][q] = tok && i < N ? row[i] : 0.0f;
+            }
         }
 #pragma unroll
-        for (int m = 1; m < 64; m <<= 1) r += __shfl_xor(r, m, 64);
+        for (int u = 0; u < SBL_TB; ++u) {
+            r[u] = 0.0;
 #pragma unroll
-        for (int q = 0; q < Q; ++q)
-            if (q * 64 + lane < N) p[q] += (double)v[q] / r;
+            for (int q = 0; q < Q; ++q) r[u] += (double)v[u][q];
+        }
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1)
+#pragma unroll
+            for (int u = 0; u < SBL_TB; ++u) r[u] += __shfl_xor(r[u], m, 64);
+#pragma unroll
+        for (int u = 0; u < SBL_TB; ++u)
+            if (tb + u < t_end)
+#pragma unroll
+                for (int q = 0; q < Q; ++q)
+                    if (q * 64 + lane < N) p[q] += (double)v[u][q] / r[u];
     }
 #pragma unroll
     for (int q = 0; q < Q; ++q)
         if (q * 64 + lane < N) wsum[wave][q * 64 + lane] = p[q];
     __syncthreads();
-    for (int64_t i = threadIdx.x; i < N; i += 256)
-        part[(int64_t)blockIdx.x * N + i] =
-            ((wsum[0][i] + wsum[1][i]) + wsum[2][i]) + wsum[3][i];
+    for (int64_t i = threadIdx.x; i < N; i += 256) {
+        part[(int64_t)blockIdx.x * N + i] = ((wsum[0][i] + wsum[1][i]) + wsum[2][i]) + wsum[3][i];
+        cnt[(int64_t)blockIdx.x * N + i] = hist[i];
+    }
 }
 
-__global__ void __launch_bounds__(256) seq_balance_final_kernel(const double* __restrict__ part,
-                                                                const int32_t* __restrict__ idx,
-                                                                int64_t N, int64_t k, int64_t S,
-                                                                int cps, float alpha,
-                                                                float* __restrict__ loss) {
-    __shared__ int32_t cnt[SBL_MAXN];
+__global__ void __launch_bounds__(1024) seq_balance_final_kernel(const double* __restrict__ part,
+                                                                 const int32_t* __restrict__ cnt,
+                                                                 int64_t N, int64_t k, int64_t S,
+                                                                 int cps, float alpha,
+                                                                 float* __restrict__ loss) {
+    __shared__ double gp[4][256];
+    __shared__ int64_t gc[4][256];
     __shared__ double red[256];
     const int64_t b = blockIdx.x;
-    for (int64_t i = threadIdx.x; i < N; i += 256) cnt[i] = 0;
-    __syncthreads();
-    const int32_t* ib = idx + b * S * k;
-    for (int64_t p = threadIdx.x; p < S * k; p += 256) {
-        const int32_t e = ib[p];
-        if (e >= 0 && e < N) atomicAdd(&cnt[e], 1);
-    }
-    __syncthreads();
+    const int g = threadIdx.x >> 8, il = threadIdx.x & 255;
     const double fscale = (double)N / ((double)k * (double)S);
-    double acc = 0.0;
-    for (int64_t i = threadIdx.x; i < N; i += 256) {
+    double acc = 0.0;  // threads of group 0: f_i P_i over their experts
+    for (int64_t i0 = 0; i0 < N; i0 += 256) {
+        const int64_t i = i0 + il;
         double P = 0.0;
-        for (int c = 0; c < cps; ++c) P += part[(b * cps + c) * N + i];
-        acc += fscale * (double)cnt[i] * (P / (double)S);
+        int64_t n = 0;
+        if (i < N) {
+            const double* pp = part + b * cps * N + i;
+            const int32_t* cp = cnt + b * cps * N + i;
+#pragma unroll 4
+            for (int c = g; c < cps; c += 4) {
+                P += pp[(int64_t)c * N];
+                n += cp[(int64_t)c * N];
+            }
+        }
+        gp[g][il] = P;
+        gc[g][il] = n;
+        __syncthreads();
+        if (g == 0 && i < N) {
+            const double Pi = ((gp[0][il] + gp[1][il]) + gp[2][il]) + gp[3][il];
+            const int64_t ni = gc[0][il] + gc[1][il] + gc[2][il] + gc[3][il];
+            acc += fscale * (double)ni * (Pi / (double)S);
+        }
+        __syncthreads();
     }
-    red[threadIdx.x] = acc;
+    if (g == 0) red[il] = acc;
     __syncthreads();
     for (int w = 128; w > 0; w >>= 1) {
         if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
@@ -206,7 +251,8 @@ __global__ void __launch_bounds__(256) seq_balance_final_kernel(const double* __
 
 size_t seq_balance_workspace_bytes(int64_t T, int64_t N, int64_t S) {
     if (S <= 0 || T <= 0) return 0;
-    return (size_t)((T / S) * cdiv(S, SBL_CH) * N * 8);
+    const int64_t n = (T / S) * cdiv(S, SBL_CH) * N;
+    return (size_t)(n * 8 + ((n * 4 + 255) & ~(int64_t)255));
 }
 
 hipError_t launch_seq_balance_loss(int64_t T, int64_t N, int64_t k, int64_t S, float alpha,
@@ -215,10 +261,21 @@ hipError_t launch_seq_balance_loss(int64_t T, int64_t N, int64_t k, int64_t S, f
     const int64_t B = T / S;
     const int cps = (int)cdiv(S, SBL_CH);
     double* part = (double*)ws;
-    seq_balance_partial_kernel<<<dim3((unsigned)(B * cps)), 256, 0, st>>>(scores, N, S, cps,
-                                                                         part);
-    seq_balance_final_kernel<<<dim3((unsigned)B), 256, 0, st>>>(part, idx, N, k, S, cps, alpha,
-                                                               loss);
+    int32_t* cnt = (int32_t*)(part + B * cps * N);
+    const dim3 grid((unsigned)(B * cps));
+    const int q = (int)cdiv(N, 64);
+    if (q <= 1)
+        seq_balance_partial_kernel<1><<<grid, 256, 0, st>>>(scores, idx, N, k, S, cps, part, cnt);
+    else if (q <= 2)
+        seq_balance_partial_kernel<2><<<grid, 256, 0, st>>>(scores, idx, N, k, S, cps, part, cnt);
+    else if (q <= 4)
+        seq_balance_partial_kernel<4><<<grid, 256, 0, st>>>(scores, idx, N, k, S, cps, part, cnt);
+    else if (q <= 8)
+        seq_balance_partial_kernel<8><<<grid, 256, 0, st>>>(scores, idx, N, k, S, cps, part, cnt);
+    else
+        seq_balance_partial_kernel<16><<<grid, 256, 0, st>>>(scores, idx, N, k, S, cps, part, cnt);
+    seq_balance_final_kernel<<<dim3((unsigned)B), 1024, 0, st>>>(part, cnt, N, k, S, cps, alpha,
+                                                                loss);
     return hipGetLastError();
 }
 
