@@ -38,6 +38,11 @@
  *  - the FFN is SwiGLU without biases: W2 (silu(W1 u) * (W3 u)); the pages
  *    only write FFN_i (parity unpinned by the pages; pinned by the dense
  *    textbook reduction against an independent library matmul);
+ *  - the sequence-wise balance loss (named, with alpha = 0.0001, in [P4]'s
+ *    last sentence of "Methode" item 2, without a formula) is read as
+ *    alpha * sum_i f_i P_i per sequence, see orc_seq_balance_loss (parity
+ *    unpinned by the pages; pinned by closed forms and invariances of that
+ *    reading);
  *  - permutation: stable counting sort of (token, slot) pairs by expert;
  *  - the bias update compares load_i * N with T*k exactly in integers;
  *    gamma is the fp32 value nearest 0.001; sign(0) = 0;
