@@ -179,7 +179,9 @@ __global__ void __launch_bounds__(1024) perm_scatter_fp8_kernel(
         dst_row[t * k + j] = row;
         src_token[row] = (int32_t)t;
     }
-    __syncthreads();
+    // the token's rows are needed only to scatter into x_perm; the codes of x
+    // itself do not wait for the index loads
+    if (x_perm != nullptr) __syncthreads();
     const int64_t vecs = d / 8;     // 8 bf16 per 16-byte vector
     const int64_t tiles = d / 128;
     const uint4* src = x + t * vecs;
