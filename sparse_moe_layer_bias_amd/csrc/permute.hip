@@ -160,6 +160,12 @@ __global__ void __launch_bounds__(256) perm_index_kernel(
     src_token[row] = (int32_t)t;
 }
 
+// threads per token block of the FP8 scatter (up to 2 row vectors each: more
+// blocks resident than with one 896-thread block per V3 token, 69 -> 62 us
+// per permute call)
+#ifndef MOE_F8SC_T
+#define MOE_F8SC_T 512
+#endif
 // 4b. FP8: one 128-thread block per token; 16 lanes per 1x128 tile, 8 values
 // per lane.  scale = amax/448 (fp32 divide); codes are nearest-even E4M3 of
 // clamp(v/scale, +-448); all-zero tile -> scale 0, codes 0.
@@ -188,6 +194,7 @@ __global__ void __launch_bounds__(1024) perm_scatter_fp8_kernel(
     // blockDim.x (a multiple of 64) threads = blockDim.x/16 tiles per pass;
     // every lane of a 16-lane group belongs to the same tile, and a pass is
     // entered by the whole block (uniform trip count)
+#pragma unroll 4
     for (int64_t v0 = 0; v0 < vecs; v0 += blockDim.x) {
         const int64_t v = v0 + threadIdx.x;
         const bool valid = v < vecs;
@@ -282,7 +289,7 @@ hipError_t launch_permute(const moe_cfg& c, const void* x, const int32_t* idx,
                 idx, w.local_rank, w.blk, offsets, src_token, dst_row, T, k, (int)N);
         } else if (c.gemm_dtype == MOE_FP8_E4M3) {
             const int64_t vecs = c.hidden / 8;
-            const int threads = (int)(vecs >= 1024 ? 1024 : (vecs + 63) / 64 * 64);
+            const int threads = (int)(vecs >= MOE_F8SC_T ? MOE_F8SC_T : (vecs + 63) / 64 * 64);
             perm_scatter_fp8_kernel<<<dim3((unsigned)T), threads, 0, st>>>(
                 (const uint4*)x, idx, w.local_rank, w.blk, offsets, src_token, dst_row,
                 (uint2*)x_perm, x_perm_scale, (uint2*)x_q, x_s, k, (int)N, c.hidden);
